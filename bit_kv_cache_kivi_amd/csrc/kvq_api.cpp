@@ -1,0 +1,208 @@
+// kvq_api.cpp -- host side of libkvq.so: validation, launch geometry and
+// workspace sizing behind the C ABI of include/kvq.h.  Never allocates, frees
+// or synchronizes device memory.
+#include <string.h>
+
+#include "kvq.h"
+#include "kvq_common.hpp"
+#include "kvq_kernels.hpp"
+
+namespace {
+
+constexpr int32_t MAGIC = 0x4b565131;   // "KVQ1"
+
+bool aligned(const void *p, uintptr_t a) { return ((uintptr_t)p % a) == 0; }
+
+int validate_layout(const kvq_layout_t *L) {
+    if (L->head_dim != kvq::D) return KVQ_EINVAL;
+    if (L->n_kv_heads < 1 || L->n_kv_heads > 65535) return KVQ_EINVAL;
+    if (L->n_q_heads < L->n_kv_heads || L->n_q_heads % L->n_kv_heads != 0) return KVQ_EINVAL;
+    const int qpk = L->n_q_heads / L->n_kv_heads;
+    if (qpk > 8) return KVQ_EINVAL;
+    if (L->batch < 1 || L->batch > 65535) return KVQ_EINVAL;
+    if (L->max_pages < 1 || L->n_pages < 1) return KVQ_EINVAL;
+    if (L->split_pages < 0) return KVQ_EINVAL;
+    switch (L->scheme) {
+        case KVQ_SCHEME_KIVI2:
+        case KVQ_SCHEME_KITTY:
+            if (L->group != 32 || L->value_group != 32) return KVQ_EINVAL;
+            // the key residual is quantized in whole groups: R % G == 0, and
+            // the flush writes whole 64-token pages
+            if (L->residual % L->group != 0 || L->residual % kvq::PT != 0) return KVQ_EINVAL;
+            if (L->residual < kvq::PT || L->residual > 256) return KVQ_EINVAL;
+            if (L->scheme == KVQ_SCHEME_KITTY ? L->n_boost != kvq::NB : L->n_boost != 0)
+                return KVQ_EINVAL;
+            break;
+        case KVQ_SCHEME_WITCERT:
+            if (L->block != kvq::WPT) return KVQ_EINVAL;
+            if (L->layer >= 65536u) return KVQ_EINVAL;
+            if (qpk != 1 && qpk != 2 && qpk != 4 && qpk != 8) return KVQ_EINVAL;
+            break;
+        default:
+            return KVQ_EINVAL;
+    }
+    return KVQ_OK;
+}
+
+kvq::KParams params(const kvq_cache_t *C) {
+    kvq::KParams P;
+    const kvq_layout_t &L = C->layout;
+    P.pool = (uint8_t *)C->bufs.pool;
+    P.table = C->bufs.page_table;
+    P.state = C->bufs.state;
+    P.res_k = C->bufs.res_k;
+    P.res_v = C->bufs.res_v;
+    P.boost_idx = C->bufs.boost_idx;
+    P.status = C->bufs.status;
+    P.B = L.batch;
+    P.Hq = L.n_q_heads;
+    P.Hkv = L.n_kv_heads;
+    P.R = L.scheme == KVQ_SCHEME_WITCERT ? kvq::WPT : L.residual;
+    P.max_pages = L.max_pages;
+    P.n_pages = L.n_pages;
+    P.page_bytes = (int)C->page_bytes;
+    P.scheme = L.scheme;
+    P.qpk = L.n_q_heads / L.n_kv_heads;
+    P.split_pages = C->split_pages;
+    P.layer = L.layer;
+    P.seed = L.seed;
+    return P;
+}
+
+int check_cache(const kvq_cache_t *C) {
+    if (!C) return KVQ_ENULL;
+    if (C->magic != MAGIC) return KVQ_ENOLAYOUT;
+    return KVQ_OK;
+}
+
+int max_splits(const kvq_cache_t *C) {
+    return (C->layout.max_pages + C->split_pages - 1) / C->split_pages;
+}
+
+}  // namespace
+
+extern "C" {
+
+int64_t kvq_page_bytes(const kvq_layout_t *L) {
+    if (!L) return 0;
+    if (L->scheme < KVQ_SCHEME_KIVI2 || L->scheme > KVQ_SCHEME_WITCERT) return 0;
+    return kvq::geom(L->scheme).bytes;
+}
+
+int32_t kvq_page_tokens(const kvq_layout_t *L) {
+    if (!L) return 0;
+    if (L->scheme < KVQ_SCHEME_KIVI2 || L->scheme > KVQ_SCHEME_WITCERT) return 0;
+    return kvq::geom(L->scheme).tokens;
+}
+
+double kvq_bytes_per_token(const kvq_layout_t *L) {
+    const int32_t t = kvq_page_tokens(L);
+    return t ? (double)kvq_page_bytes(L) / (double)t : 0.0;
+}
+
+int kvq_set_layout(kvq_cache_t *cache, const kvq_layout_t *layout, const kvq_buffers_t *bufs) {
+    if (!cache || !layout || !bufs) return KVQ_ENULL;
+    int rc = validate_layout(layout);
+    if (rc != KVQ_OK) return rc;
+    if (!bufs->pool || !bufs->page_table || !bufs->state || !bufs->res_k || !bufs->res_v ||
+        !bufs->status)
+        return KVQ_ENULL;
+    if (layout->scheme == KVQ_SCHEME_KITTY && !bufs->boost_idx) return KVQ_ENULL;
+    if (!aligned(bufs->pool, 256) || !aligned(bufs->page_table, 16) || !aligned(bufs->state, 16) ||
+        !aligned(bufs->res_k, 16) || !aligned(bufs->res_v, 16) || !aligned(bufs->status, 4))
+        return KVQ_EALIGN;
+    memset(cache, 0, sizeof(*cache));
+    cache->layout = *layout;
+    cache->bufs = *bufs;
+    const kvq::Geom G = kvq::geom(layout->scheme);
+    cache->page_tokens = G.tokens;
+    cache->page_bytes = G.bytes;
+    int sp = layout->split_pages;
+    if (sp == 0) sp = layout->scheme == KVQ_SCHEME_WITCERT ? 1 : 16;
+    cache->split_pages = sp;
+    cache->magic = MAGIC;
+    return KVQ_OK;
+}
+
+size_t kvq_workspace_bytes(const kvq_cache_t *cache) {
+    if (check_cache(cache) != KVQ_OK) return 0;
+    const size_t rows = (size_t)cache->layout.batch * cache->layout.n_q_heads * max_splits(cache);
+    return rows * kvq::D * sizeof(float) + rows * sizeof(float2) + 256;
+}
+
+int kvq_append_token(const kvq_cache_t *cache, const uint16_t *k_new, const uint16_t *v_new,
+                     hipStream_t stream) {
+    int rc = check_cache(cache);
+    if (rc != KVQ_OK) return rc;
+    if (!k_new || !v_new) return KVQ_ENULL;
+    if (!aligned(k_new, 16) || !aligned(v_new, 16)) return KVQ_EALIGN;
+    return kvq::launch_append(params(cache), k_new, v_new, stream) == hipSuccess ? KVQ_OK
+                                                                                 : KVQ_ELAUNCH;
+}
+
+int kvq_flush_key_group(const kvq_cache_t *cache, hipStream_t stream) {
+    int rc = check_cache(cache);
+    if (rc != KVQ_OK) return rc;
+    return kvq::launch_flush(params(cache), stream) == hipSuccess ? KVQ_OK : KVQ_ELAUNCH;
+}
+
+int kvq_decode_attention(const kvq_cache_t *cache, const uint16_t *q, float *out, float *cert,
+                         float sm_scale, float kappa, void *workspace, size_t ws_bytes,
+                         hipStream_t stream) {
+    int rc = check_cache(cache);
+    if (rc != KVQ_OK) return rc;
+    if (!q || !out || !workspace) return KVQ_ENULL;
+    if (!aligned(q, 16) || !aligned(out, 16) || !aligned(workspace, 256) ||
+        (cert && !aligned(cert, 4)))
+        return KVQ_EALIGN;
+    if (ws_bytes < kvq_workspace_bytes(cache)) return KVQ_EWORKSPACE;
+    kvq::Workspace W;
+    W.max_splits = max_splits(cache);
+    const size_t rows = (size_t)cache->layout.batch * cache->layout.n_q_heads * W.max_splits;
+    W.o = (float *)workspace;
+    W.ml = (float2 *)((char *)workspace + rows * kvq::D * sizeof(float));
+    return kvq::launch_decode(params(cache), q, out, cert, sm_scale, kappa, W, stream) == hipSuccess
+               ? KVQ_OK
+               : KVQ_ELAUNCH;
+}
+
+int kvq_prefill(const kvq_cache_t *cache, int32_t req0, int32_t n_req, const uint16_t *K,
+                const uint16_t *V, int64_t ld_tokens, const int32_t *lengths, hipStream_t stream) {
+    int rc = check_cache(cache);
+    if (rc != KVQ_OK) return rc;
+    if (!K || !V || !lengths) return KVQ_ENULL;
+    if (req0 < 0 || n_req < 1 || req0 + n_req > cache->layout.batch || ld_tokens < 1)
+        return KVQ_EINVAL;
+    if (!aligned(K, 16) || !aligned(V, 16) || !aligned(lengths, 4)) return KVQ_EALIGN;
+    return kvq::launch_prefill(params(cache), req0, n_req, K, V, (long long)ld_tokens, lengths,
+                               stream) == hipSuccess
+               ? KVQ_OK
+               : KVQ_ELAUNCH;
+}
+
+int kvq_kitty_calibrate(const kvq_cache_t *cache, const uint16_t *calib, int32_t n_tokens,
+                        uint8_t *idx_out, hipStream_t stream) {
+    int rc = check_cache(cache);
+    if (rc != KVQ_OK) return rc;
+    if (cache->layout.scheme != KVQ_SCHEME_KITTY) return KVQ_EINVAL;
+    if (!calib || !idx_out) return KVQ_ENULL;
+    if (n_tokens < 1) return KVQ_EINVAL;
+    return kvq::launch_kitty_calibrate(params(cache), calib, n_tokens, idx_out, stream) == hipSuccess
+               ? KVQ_OK
+               : KVQ_ELAUNCH;
+}
+
+const char *kvq_strerror(int code) {
+    switch (code) {
+        case KVQ_OK: return "ok";
+        case KVQ_EINVAL: return "invalid layout or argument";
+        case KVQ_ENULL: return "required pointer is NULL";
+        case KVQ_EALIGN: return "device pointer misaligned";
+        case KVQ_ENOLAYOUT: return "cache not initialised by kvq_set_layout";
+        case KVQ_EWORKSPACE: return "workspace too small";
+        case KVQ_ELAUNCH: return "kernel launch failed";
+        default: return "unknown";
+    }
+}
+
+}  // extern "C"

@@ -1,0 +1,180 @@
+// kvq_common.hpp -- device-side layout and arithmetic shared by the kernels of
+// libkvq.so (gfx950).  Host code includes it for the page geometry only.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "kvq.h"
+
+namespace kvq {
+
+constexpr int D = 128;          // head dim
+constexpr int PT = 64;          // tokens per KIVI2/KITTY page
+constexpr int WPT = 256;        // tokens per WITCERT page (= one block)
+constexpr int NB = 16;          // Kitty boosted channels per KV head
+
+// ---------------------------------------------------------------------------
+// Page geometry.  One (page, KV head) block; the pool is
+// [n_pages][n_kv_heads][page_bytes].
+//
+// KIVI2 / KITTY, 64 tokens:
+//   KC  2048 B  low 2-bit key codes, token-major, arranged as the B operand of
+//               a 16x16x32 f16 matrix-core product (see key_code_pos)
+//   KH   256 B  KITTY only: high 2-bit plane of the 16 boosted channels
+//   KS  1024 B  key {scale, zero} fp16 pairs, [2 groups][128 channel slots]
+//   VC  2048 B  value codes, channel-major (see value_code_pos)
+//   VS  1024 B  value {scale, zero} fp16 pairs, [64 tokens][4 groups]
+// WITCERT, 256 tokens (one block):
+//   KC 32768 B int8 [256][128];  KS 256 B fp16 [128];
+//   VC 32768 B int8 [256][128];  VS 256 B fp16 [128]
+// ---------------------------------------------------------------------------
+struct Geom {
+    int kc, kh, ks, vc, vs, bytes, tokens;
+};
+
+__host__ __device__ inline Geom geom(int scheme) {
+    Geom g{};
+    if (scheme == KVQ_SCHEME_WITCERT) {
+        g.kc = 0; g.kh = 0; g.ks = 32768; g.vc = 33024; g.vs = 65792; g.bytes = 66048;
+        g.tokens = WPT;
+    } else if (scheme == KVQ_SCHEME_KITTY) {
+        g.kc = 0; g.kh = 2048; g.ks = 2304; g.vc = 3328; g.vs = 5376; g.bytes = 6400;
+        g.tokens = PT;
+    } else {
+        g.kc = 0; g.kh = 0; g.ks = 2048; g.vc = 3072; g.vs = 5120; g.bytes = 6144;
+        g.tokens = PT;
+    }
+    return g;
+}
+
+// Key code of (token t in page, channel c): dword index into KC and bit shift.
+// Lane L = 16*((c>>3)&3) + (t&15) of a wave loads dwords {256*p + 4*L + i},
+// i.e. 16 contiguous bytes per lane per 1 KB; dword d = 4p + i holds the 16
+// codes of token 16*(d>>1) + (t&15), channels 32*kc + 8*((c>>3)&3) + j with
+// kc = 2*(d&1) + h, at bit 4j + 2h.  Masking with 0x33333333 (h = 0) or
+// (x >> 2) & 0x33333333 (h = 1) leaves eight codes in nibble j, ready for the
+// packed fp4 -> f16 / f32 converters.
+__host__ __device__ inline void key_code_pos(int t, int c, int &dword, int &shift) {
+    int n = t >> 4, r = t & 15, kc = c >> 5, g = (c >> 3) & 3, j = c & 7;
+    int lane = 16 * g + r;
+    int d = 2 * n + (kc >> 1), h = kc & 1;
+    dword = (d >> 2) * 256 + lane * 4 + (d & 3);
+    shift = 4 * j + 2 * h;
+}
+
+// Value code of (token t in page, channel c).  Lane L = 16*((t>>3)&3) + (c&15)
+// holds dword d = c >> 4 (channel 16d + (c&15)) with the 16 codes of tokens
+// 32*ks + 8*((t>>3)&3) + j at bit 4j + 2ks.
+__host__ __device__ inline void value_code_pos(int t, int c, int &dword, int &shift) {
+    int nt = c >> 4, r = c & 15, ks = t >> 5, g = (t >> 3) & 3, j = t & 7;
+    int lane = 16 * g + r;
+    dword = (nt >> 2) * 256 + lane * 4 + (nt & 3);
+    shift = 4 * j + 2 * ks;
+}
+
+// Kitty high plane: (token t in page, boosted offset o in [0,16)).
+// Dword 16*(o>>2) + (t&15) (the lane whose KC data holds token t), bit
+// 4*(4*(n&1) + (o&3)) + 2*(n>>1) with n = t >> 4.
+__host__ __device__ inline void high_code_pos(int t, int o, int &dword, int &shift) {
+    int n = t >> 4, r = t & 15, g = o >> 2, i = o & 3;
+    dword = 16 * g + r;
+    shift = 4 * (4 * (n & 1) + i) + 2 * (n >> 1);
+}
+
+// Key statistic slot of channel c inside a group: lanes with the same
+// (c>>3)&3 read 32 contiguous slots.
+__host__ __device__ inline int key_stat_slot(int c) {
+    return 32 * ((c >> 3) & 3) + 8 * (c >> 5) + (c & 7);
+}
+
+// ---------------------------------------------------------------------------
+// binary16 helpers (bit patterns in uint16_t)
+// ---------------------------------------------------------------------------
+__device__ inline float h2f(uint16_t b) {
+    return (float)__builtin_bit_cast(_Float16, b);
+}
+__device__ inline uint16_t f2h(float x) {          // round to nearest even
+    return __builtin_bit_cast(uint16_t, (_Float16)x);
+}
+
+// ---------------------------------------------------------------------------
+// Asymmetric RTN group quantizer ("Kitty" summary, Observation 1 and the
+// quantization step: x_q = round((x - z)/s) clamped to [0, 2^b-1]):
+//   z = min (canonical +0), s = fp16(fl32(fl32(max - min)/(2^b - 1))),
+//   s raised one fp16 step when (2^b - 1/2) s < max - min (fp16-subnormal s
+//   only), s = 0 for a constant group; code = clamp(rint(fl32(x - z)/s)).
+// Every operation is a single IEEE binary32 operation (no contraction).
+// ---------------------------------------------------------------------------
+struct AsymParams {
+    float s, z;
+    uint16_t s16, z16;
+};
+
+__device__ inline AsymParams asym_params(float mn, float mx, float lmax) {
+#pragma clang fp contract(off)
+    AsymParams p;
+    p.z = mn + 0.0f;
+    float d = mx - mn;
+    uint16_t s16 = 0;
+    if (d > 0.0f) {
+        s16 = f2h(d / lmax);
+        if ((lmax + 0.5f) * h2f(s16) < d) s16 = (uint16_t)(s16 + 1);
+    }
+    p.s16 = s16;
+    p.s = h2f(s16);
+    p.z16 = f2h(p.z);
+    return p;
+}
+
+__device__ inline uint32_t asym_code(float x, const AsymParams &p, float lmax) {
+#pragma clang fp contract(off)
+    if (p.s16 == 0) return 0u;
+    float t = x - p.z;
+    float c = rintf(t / p.s);
+    c = fminf(fmaxf(c, 0.0f), lmax);
+    return (uint32_t)c;
+}
+
+// ---------------------------------------------------------------------------
+// Philox4x32-10 (Salmon et al., SC'11) and the WitCert dither
+// (counter = (token, channel>>2, layer<<16 | kv_head, request),
+//  key = (seed_lo, seed_hi ^ side), word = channel & 3,
+//  xi = fl32((u >> 8) * 2^-24) - 1/2).
+// ---------------------------------------------------------------------------
+struct U4 {
+    uint32_t x, y, z, w;
+};
+
+__device__ inline U4 philox4x32_10(U4 c, uint32_t k0, uint32_t k1) {
+#pragma unroll
+    for (int r = 0; r < 10; r++) {
+        if (r > 0) {
+            k0 += 0x9E3779B9u;
+            k1 += 0xBB67AE85u;
+        }
+        uint32_t lo0 = 0xD2511F53u * c.x;
+        uint32_t hi0 = __umulhi(0xD2511F53u, c.x);
+        uint32_t lo1 = 0xCD9E8D57u * c.z;
+        uint32_t hi1 = __umulhi(0xCD9E8D57u, c.z);
+        U4 n;
+        n.x = hi1 ^ c.y ^ k0;
+        n.y = lo1;
+        n.z = hi0 ^ c.w ^ k1;
+        n.w = lo0;
+        c = n;
+    }
+    return c;
+}
+
+__device__ inline float dither_from_word(uint32_t u) {
+#pragma clang fp contract(off)
+    return (float)(u >> 8) * 0x1p-24f - 0.5f;
+}
+
+// ---------------------------------------------------------------------------
+// wave64 cross-lane helpers
+// ---------------------------------------------------------------------------
+__device__ inline float shfl_xor(float v, int m) { return __shfl_xor(v, m, 64); }
+
+}  // namespace kvq

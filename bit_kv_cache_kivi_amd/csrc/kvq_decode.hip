@@ -1,0 +1,555 @@
+// kvq_decode.hip -- read path: split-KV stage 1 over the quantized prefix and
+// stage 2 (fp16 window + log-sum-exp merge).
+//
+// Attention for query head h of KV head g: z_t = sm_scale q.k~_t over every
+// token, p = softmax(z), o = sum_t p_t v~_t, with k~, v~ the dequantized or
+// fp16 tokens ("KIVI" explainer eq. 3).  Stage 1 takes the prefix [0, n_vq)
+// whose keys and values are both quantized, split into runs of pages, and
+// emits per split (acc / l_s, lse_s, A_s); stage 2 attends to the fp16 window
+// (keys of [n_vq, n_kq) still 2-bit) and merges every partial with
+// log-sum-exp weights; the certificate A_s merges with the same weights
+// ("WitCert" Key structure).  Scores are kept in log2 units: z2 = z log2(e).
+//
+// Folding: for a key group, q.k~ = sum_c (q_c s_c) code_c + sum_c q_c z_c;
+// for a value group, sum_t p_t v~_t = sum_t (p_t s_t) code_t + sum_t p_t z_t.
+// Only small integer codes are touched per element.
+#include "kvq_common.hpp"
+#include "kvq_kernels.hpp"
+
+namespace kvq {
+
+typedef float float2v __attribute__((ext_vector_type(2)));
+
+__device__ inline const uint8_t *cpage(const KParams &P, int pid, int h) {
+    return P.pool + ((size_t)pid * P.Hkv + h) * (size_t)P.page_bytes;
+}
+
+// Two codes (nibbles 2*sel, 2*sel+1 of a masked dword) as exact floats: a
+// 2-bit code c in the low bits of a nibble is the fp4 (e2m1) value c/2.
+__device__ inline float2v cvt2(uint32_t x, int sel) {
+    switch (sel) {
+        case 0: return __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(x, 2.0f, 0);
+        case 1: return __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(x, 2.0f, 1);
+        case 2: return __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(x, 2.0f, 2);
+        default: return __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(x, 2.0f, 3);
+    }
+}
+#define CVT2(x, sel) cvt2((x), (sel))
+
+// ---------------------------------------------------------------------------
+// Stage 1, KIVI2 / KITTY, one query head per wave (VALU).
+// Lane L = 16 g + r.  Key side: the lane's dwords hold tokens 16n + r
+// (n = 0..3) for its 32 channels 32kc + 8g + j; partial scores are summed
+// over g.  Value side: channels 16d + r (d = 0..7) over tokens 32ks + 8g + j;
+// partial outputs are summed over g at the end.
+// ---------------------------------------------------------------------------
+template <bool KITTY>
+__global__ __launch_bounds__(64) void stage1_valu_kernel(KParams P, const uint16_t *__restrict__ q,
+                                                         Workspace W, float qscale) {
+    const int s = blockIdx.x, hq = blockIdx.y, b = blockIdx.z;
+    const int lane = threadIdx.x, g = lane >> 4, r = lane & 15;
+    const int h = hq / P.qpk;
+    const Geom G = geom(P.scheme);
+    const size_t bh = (size_t)b * P.Hkv + h;
+    const int l = P.state[bh * 4];
+    const int nvq = l > P.R ? l - P.R : 0;
+    const int npages = (nvq + PT - 1) / PT;
+    const int p0 = s * P.split_pages;
+    const int p1 = min(p0 + P.split_pages, npages);
+    if (p0 >= p1) return;
+
+    __shared__ uint32_t kss[256];
+    __shared__ float4 wsh[PT];
+    __shared__ int inv[NB];
+
+    const uint16_t *qh = q + ((size_t)b * P.Hq + hq) * D;
+    float qv[32];
+#pragma unroll
+    for (int kc = 0; kc < 4; kc++) {
+        const uint4 raw = *(const uint4 *)(qh + 32 * kc + 8 * g);
+        const uint32_t w4[4] = {raw.x, raw.y, raw.z, raw.w};
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+            qv[8 * kc + 2 * i] = h2f((uint16_t)(w4[i] & 0xffff));
+            qv[8 * kc + 2 * i + 1] = h2f((uint16_t)(w4[i] >> 16));
+        }
+    }
+    float qb[4] = {0.f, 0.f, 0.f, 0.f};
+    int slotb[4] = {0, 0, 0, 0};
+    if (KITTY) {
+        if (lane < NB) inv[lane] = 0;
+        __syncthreads();
+        for (int c = lane; c < D; c += 64) {
+            const int o = P.boost_idx[(size_t)h * D + c];
+            if (o < NB) inv[o] = c;
+        }
+        __syncthreads();
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+            const int c = inv[4 * g + i];
+            qb[i] = h2f(qh[c]);
+            slotb[i] = key_stat_slot(c);
+        }
+    }
+
+    float m = -INFINITY;           // running max (log2 units)
+    float lpart = 0.f;             // this lane's share of sum p (token = lane)
+    float o[8];                    // channels 16d + r, tokens of lane group g
+    float zacc[4] = {0.f, 0.f, 0.f, 0.f};   // sum_t p_t z_{t,jv}, token = lane
+#pragma unroll
+    for (int d = 0; d < 8; d++) o[d] = 0.f;
+
+    for (int p = p0; p < p1; p++) {
+        const int pid = P.table[(size_t)b * P.max_pages + p];
+        if (pid < 0 || pid >= P.n_pages) {
+            if (lane == 0) atomicOr(P.status, (uint32_t)KVQ_STATUS_UNMAPPED_PAGE);
+            continue;
+        }
+        const uint8_t *page = cpage(P, pid, h);
+        const uint4 *kc4 = (const uint4 *)(page + G.kc);
+        const uint4 *vc4 = (const uint4 *)(page + G.vc);
+        const uint4 ka = kc4[lane], kb = kc4[64 + lane];
+        const uint4 va = vc4[lane], vb = vc4[64 + lane];
+        const uint4 vsz = ((const uint4 *)(page + G.vs))[lane];
+        const uint4 ksz = ((const uint4 *)(page + G.ks))[lane];
+        uint32_t khw = 0;
+        if (KITTY) khw = ((const uint32_t *)(page + G.kh))[lane];
+        __syncthreads();                                 // previous page's LDS reads done
+        ((uint4 *)kss)[lane] = ksz;
+        __syncthreads();
+
+        // ---- scores --------------------------------------------------------
+        const uint32_t kd[8] = {ka.x, ka.y, ka.z, ka.w, kb.x, kb.y, kb.z, kb.w};
+        float part[4];
+#pragma unroll
+        for (int gi = 0; gi < 2; gi++) {
+            float a[32];
+            float bias = 0.f;
+#pragma unroll
+            for (int i = 0; i < 32; i++) {
+                const uint32_t sz = kss[128 * gi + 32 * g + i];
+                const float sc = h2f((uint16_t)(sz & 0xffff));
+                const float ze = h2f((uint16_t)(sz >> 16));
+                a[i] = qv[i] * sc;
+                bias = fmaf(qv[i], ze, bias);
+            }
+            float ab[4] = {0.f, 0.f, 0.f, 0.f};
+            if (KITTY) {
+#pragma unroll
+                for (int i = 0; i < 4; i++) {
+                    const uint32_t sz = kss[128 * gi + slotb[i]];
+                    ab[i] = 4.0f * qb[i] * h2f((uint16_t)(sz & 0xffff));
+                }
+            }
+#pragma unroll
+            for (int nn = 0; nn < 2; nn++) {
+                const int n = 2 * gi + nn;
+                float acc = bias;
+#pragma unroll
+                for (int dd = 0; dd < 2; dd++) {             // d = 2n + dd: kc = 2dd + h
+                    const uint32_t x = kd[2 * n + dd];
+                    const uint32_t x0 = x & 0x33333333u, x1 = (x >> 2) & 0x33333333u;
+#pragma unroll
+                    for (int sel = 0; sel < 4; sel++) {
+                        const float2v c0 = CVT2(x0, sel), c1 = CVT2(x1, sel);
+                        const int kcl = 2 * dd, kch = 2 * dd + 1;
+                        acc = fmaf(a[8 * kcl + 2 * sel], c0.x, acc);
+                        acc = fmaf(a[8 * kcl + 2 * sel + 1], c0.y, acc);
+                        acc = fmaf(a[8 * kch + 2 * sel], c1.x, acc);
+                        acc = fmaf(a[8 * kch + 2 * sel + 1], c1.y, acc);
+                    }
+                }
+                if (KITTY) {
+                    // high plane: n&1 selects nibble block, n>>1 the 2-bit half
+                    const uint32_t hx = ((n >> 1) ? (khw >> 2) : khw) & 0x33333333u;
+                    const int sb = 2 * (n & 1);
+                    const float2v h0 = CVT2(hx, sb), h1 = CVT2(hx, sb + 1);
+                    acc = fmaf(ab[0], h0.x, acc);
+                    acc = fmaf(ab[1], h0.y, acc);
+                    acc = fmaf(ab[2], h1.x, acc);
+                    acc = fmaf(ab[3], h1.y, acc);
+                }
+                part[n] = acc;
+            }
+        }
+#pragma unroll
+        for (int n = 0; n < 4; n++) {
+            part[n] += shfl_xor(part[n], 16);
+            part[n] += shfl_xor(part[n], 32);
+        }
+        // ---- online softmax --------------------------------------------------
+        const int tbase = p * PT;
+        float z2[4];
+        float mloc = -INFINITY;
+#pragma unroll
+        for (int n = 0; n < 4; n++) {
+            const bool valid = tbase + 16 * n + r < nvq;
+            z2[n] = valid ? part[n] * qscale : -INFINITY;
+            mloc = fmaxf(mloc, z2[n]);
+        }
+#pragma unroll
+        for (int msk = 1; msk < 16; msk <<= 1) mloc = fmaxf(mloc, shfl_xor(mloc, msk));
+        const float mnew = fmaxf(m, mloc);
+        const float alpha = exp2f(m - mnew);
+        m = mnew;
+        float pn[4];
+#pragma unroll
+        for (int n = 0; n < 4; n++) pn[n] = exp2f(z2[n] - mnew);     // -inf -> 0
+        const float pt = g == 0 ? pn[0] : g == 1 ? pn[1] : g == 2 ? pn[2] : pn[3];
+        const bool tvalid = tbase + lane < nvq;                    // token = lane
+        lpart = lpart * alpha + pt;
+        const uint32_t vw[4] = {vsz.x, vsz.y, vsz.z, vsz.w};
+        float4 wv;
+        float wtmp[4];
+#pragma unroll
+        for (int jv = 0; jv < 4; jv++) {
+            const float sv = h2f((uint16_t)(vw[jv] & 0xffff));
+            const float zv = h2f((uint16_t)(vw[jv] >> 16));
+            wtmp[jv] = tvalid ? pt * sv : 0.f;
+            zacc[jv] = zacc[jv] * alpha + (tvalid ? pt * zv : 0.f);
+        }
+        wv.x = wtmp[0]; wv.y = wtmp[1]; wv.z = wtmp[2]; wv.w = wtmp[3];
+        wsh[lane] = wv;
+#pragma unroll
+        for (int d = 0; d < 8; d++) o[d] *= alpha;
+        __syncthreads();
+
+        // ---- P.V -------------------------------------------------------------
+        float4 wt[16];
+#pragma unroll
+        for (int ks = 0; ks < 2; ks++)
+#pragma unroll
+            for (int j = 0; j < 8; j++) wt[8 * ks + j] = wsh[32 * ks + 8 * g + j];
+        const uint32_t vd[8] = {va.x, va.y, va.z, va.w, vb.x, vb.y, vb.z, vb.w};
+#pragma unroll
+        for (int d = 0; d < 8; d++) {
+            const int jv = d >> 1;
+            const uint32_t x = vd[d];
+            const uint32_t x0 = x & 0x33333333u, x1 = (x >> 2) & 0x33333333u;
+            float acc = o[d];
+#pragma unroll
+            for (int sel = 0; sel < 4; sel++) {
+                const float2v c0 = CVT2(x0, sel), c1 = CVT2(x1, sel);
+                const float4 w0 = wt[2 * sel], w1 = wt[2 * sel + 1];
+                const float4 w2 = wt[8 + 2 * sel], w3 = wt[8 + 2 * sel + 1];
+                const float f0 = jv == 0 ? w0.x : jv == 1 ? w0.y : jv == 2 ? w0.z : w0.w;
+                const float f1 = jv == 0 ? w1.x : jv == 1 ? w1.y : jv == 2 ? w1.z : w1.w;
+                const float f2 = jv == 0 ? w2.x : jv == 1 ? w2.y : jv == 2 ? w2.z : w2.w;
+                const float f3 = jv == 0 ? w3.x : jv == 1 ? w3.y : jv == 2 ? w3.z : w3.w;
+                acc = fmaf(f0, c0.x, acc);
+                acc = fmaf(f1, c0.y, acc);
+                acc = fmaf(f2, c1.x, acc);
+                acc = fmaf(f3, c1.y, acc);
+            }
+            o[d] = acc;
+        }
+    }
+
+    // ---- reduce and write the split's partial ----------------------------------
+#pragma unroll
+    for (int d = 0; d < 8; d++) {
+        o[d] += shfl_xor(o[d], 16);
+        o[d] += shfl_xor(o[d], 32);
+    }
+#pragma unroll
+    for (int msk = 1; msk < 64; msk <<= 1) {
+        lpart += shfl_xor(lpart, msk);
+#pragma unroll
+        for (int jv = 0; jv < 4; jv++) zacc[jv] += shfl_xor(zacc[jv], msk);
+    }
+    const float inv_l = 1.0f / lpart;
+    const size_t row = ((size_t)b * P.Hq + hq) * W.max_splits + s;
+    if (g == 0) {
+#pragma unroll
+        for (int d = 0; d < 8; d++) W.o[row * D + 16 * d + r] = (o[d] + zacc[d >> 1]) * inv_l;
+    }
+    if (lane == 0) W.ml[row] = make_float2(m + log2f(lpart), 1.0f);
+}
+
+// ---------------------------------------------------------------------------
+// Stage 1, WITCERT: INT8 codes with the Philox dither regenerated in the
+// kernel, and the certificate accumulated next to the output.  One wave per
+// (split, KV head, request) serves all QPK query heads of the KV head, so each
+// dither draw is shared by the group.  Lane L: channel quad cq = L & 31 (one
+// Philox4x32-10 block gives the four dither words of channels 4cq..4cq+3)
+// and token phase tp = L >> 5.
+// ---------------------------------------------------------------------------
+template <int QPK>
+__global__ __launch_bounds__(64) void stage1_witcert_kernel(KParams P, const uint16_t *__restrict__ q,
+                                                            Workspace W, float qscale, float sm_scale,
+                                                            float kappa) {
+    const int s = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+    const int lane = threadIdx.x, cq = lane & 31, tp = lane >> 5;
+    const Geom G = geom(P.scheme);
+    const size_t bh = (size_t)b * P.Hkv + h;
+    const int nq = P.state[bh * 4 + 1];
+    const int npages = nq / WPT;
+    const int p0 = s * P.split_pages;
+    const int p1 = min(p0 + P.split_pages, npages);
+    if (p0 >= p1) return;
+
+    float qv[QPK][4];
+#pragma unroll
+    for (int hh = 0; hh < QPK; hh++) {
+        const uint2 raw = *(const uint2 *)(q + ((size_t)b * P.Hq + h * QPK + hh) * D + 4 * cq);
+        qv[hh][0] = h2f((uint16_t)(raw.x & 0xffff));
+        qv[hh][1] = h2f((uint16_t)(raw.x >> 16));
+        qv[hh][2] = h2f((uint16_t)(raw.y & 0xffff));
+        qv[hh][3] = h2f((uint16_t)(raw.y >> 16));
+    }
+    float m[QPK], lp[QPK], ap[QPK], o[QPK][4];
+#pragma unroll
+    for (int hh = 0; hh < QPK; hh++) {
+        m[hh] = -INFINITY; lp[hh] = 0.f; ap[hh] = 0.f;
+        o[hh][0] = o[hh][1] = o[hh][2] = o[hh][3] = 0.f;
+    }
+    const uint32_t k0 = (uint32_t)P.seed;
+    const uint32_t k1 = (uint32_t)(P.seed >> 32);
+    const uint32_t c2 = (P.layer << 16) | (uint32_t)h;
+    const float LOG2E = 1.4426950408889634f;
+
+    for (int p = p0; p < p1; p++) {
+        const int pid = P.table[(size_t)b * P.max_pages + p];
+        if (pid < 0 || pid >= P.n_pages) {
+            if (lane == 0) atomicOr(P.status, (uint32_t)KVQ_STATUS_UNMAPPED_PAGE);
+            continue;
+        }
+        const uint8_t *page = cpage(P, pid, h);
+        const int8_t *kcod = (const int8_t *)(page + G.kc);
+        const int8_t *vcod = (const int8_t *)(page + G.vc);
+        const uint2 ksr = *(const uint2 *)(page + G.ks + 8 * cq);
+        const uint2 vsr = *(const uint2 *)(page + G.vs + 8 * cq);
+        const float ks[4] = {h2f((uint16_t)(ksr.x & 0xffff)), h2f((uint16_t)(ksr.x >> 16)),
+                             h2f((uint16_t)(ksr.y & 0xffff)), h2f((uint16_t)(ksr.y >> 16))};
+        const float vs[4] = {h2f((uint16_t)(vsr.x & 0xffff)), h2f((uint16_t)(vsr.x >> 16)),
+                             h2f((uint16_t)(vsr.y & 0xffff)), h2f((uint16_t)(vsr.y >> 16))};
+        // certificate: varsigma^2 = (sm^2/12) sum_c q_c^2 s_c^2 for this block,
+        // u = kappa sqrt(varsigma^2); e^u folded into the A accumulator
+        float eu[QPK];
+#pragma unroll
+        for (int hh = 0; hh < QPK; hh++) {
+            float v2 = 0.f;
+#pragma unroll
+            for (int e = 0; e < 4; e++) v2 = fmaf(qv[hh][e] * qv[hh][e], ks[e] * ks[e], v2);
+#pragma unroll
+            for (int msk = 1; msk < 32; msk <<= 1) v2 += shfl_xor(v2, msk);
+            v2 *= sm_scale * sm_scale * (1.0f / 12.0f);
+            eu[hh] = exp2f(kappa * sqrtf(v2) * LOG2E);
+        }
+        for (int i = 0; i < WPT / 2; i++) {
+            const int t = 2 * i + tp;
+            const uint32_t tok = (uint32_t)(p * WPT + t);
+            const U4 uk = philox4x32_10(U4{tok, (uint32_t)cq, c2, (uint32_t)b}, k0, k1);
+            const U4 uv = philox4x32_10(U4{tok, (uint32_t)cq, c2, (uint32_t)b}, k0, k1 ^ 1u);
+            const uint32_t kw = *(const uint32_t *)(kcod + (size_t)t * D + 4 * cq);
+            const uint32_t vw = *(const uint32_t *)(vcod + (size_t)t * D + 4 * cq);
+            const uint32_t ukw[4] = {uk.x, uk.y, uk.z, uk.w};
+            const uint32_t uvw[4] = {uv.x, uv.y, uv.z, uv.w};
+            float kx[4], vx[4];
+#pragma unroll
+            for (int e = 0; e < 4; e++) {
+#pragma clang fp contract(off)
+                const float kcode = (float)(int8_t)((kw >> (8 * e)) & 0xff);
+                const float vcode = (float)(int8_t)((vw >> (8 * e)) & 0xff);
+                kx[e] = ks[e] * (kcode - dither_from_word(ukw[e]));
+                vx[e] = vs[e] * (vcode - dither_from_word(uvw[e]));
+            }
+#pragma unroll
+            for (int hh = 0; hh < QPK; hh++) {
+                float part = 0.f;
+#pragma unroll
+                for (int e = 0; e < 4; e++) part = fmaf(qv[hh][e], kx[e], part);
+#pragma unroll
+                for (int msk = 1; msk < 32; msk <<= 1) part += shfl_xor(part, msk);
+                const float z2 = part * qscale;
+                // per token phase: each half-wave sees its own token stream
+                const float mnew = fmaxf(m[hh], z2);
+                const float alpha = exp2f(m[hh] - mnew);
+                const float pr = exp2f(z2 - mnew);
+                m[hh] = mnew;
+                lp[hh] = lp[hh] * alpha + pr;
+                ap[hh] = ap[hh] * alpha + pr * eu[hh];
+#pragma unroll
+                for (int e = 0; e < 4; e++) o[hh][e] = fmaf(pr, vx[e], o[hh][e] * alpha);
+            }
+        }
+    }
+    // combine the two token phases (lanes L and L ^ 32)
+    const float4 zero4 = make_float4(0.f, 0.f, 0.f, 0.f);
+    (void)zero4;
+#pragma unroll
+    for (int hh = 0; hh < QPK; hh++) {
+        const float mo = shfl_xor(m[hh], 32);
+        const float mt = fmaxf(m[hh], mo);
+        const float sa = exp2f(m[hh] - mt);
+        const float lo = shfl_xor(lp[hh] * sa, 32);
+        const float ao = shfl_xor(ap[hh] * sa, 32);
+        const float lt = lp[hh] * sa + lo;
+        const float at = ap[hh] * sa + ao;
+        float oo[4];
+#pragma unroll
+        for (int e = 0; e < 4; e++) {
+            const float mine = o[hh][e] * sa;
+            oo[e] = mine + shfl_xor(mine, 32);
+        }
+        const size_t row = ((size_t)b * P.Hq + h * QPK + hh) * W.max_splits + s;
+        if (tp == 0) {
+            const float il = 1.0f / lt;
+            *(float4 *)(W.o + row * D + 4 * cq) = make_float4(oo[0] * il, oo[1] * il, oo[2] * il, oo[3] * il);
+        }
+        if (lane == 0) W.ml[row] = make_float2(mt + log2f(lt), at / lt);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Stage 2: fp16 window (and 2-bit keys of [n_vq, n_kq)) + LSE merge.
+// One 256-thread block per (KV head, request), all query heads of the group.
+// ---------------------------------------------------------------------------
+constexpr int S2_MAXQ = 8;
+constexpr int S2_MAXW = 256;
+
+__device__ inline float key_tilde_page(const KParams &P, const Geom &G, const uint8_t *page,
+                                       int tp, int c, int h) {
+    int dw, sh;
+    key_code_pos(tp, c, dw, sh);
+    uint32_t code = (((const uint32_t *)(page + G.kc))[dw] >> sh) & 3u;
+    const uint32_t sz = ((const uint32_t *)(page + G.ks))[128 * (tp >> 5) + key_stat_slot(c)];
+    if (P.scheme == KVQ_SCHEME_KITTY) {
+        const int o = P.boost_idx[(size_t)h * D + c];
+        if (o < NB) {
+            int dh, shh;
+            high_code_pos(tp, o, dh, shh);
+            code |= ((((const uint32_t *)(page + G.kh))[dh] >> shh) & 3u) << 2;
+        }
+    }
+    const float cs = (float)code * h2f((uint16_t)(sz & 0xffff));
+    return cs + h2f((uint16_t)(sz >> 16));
+}
+
+__global__ __launch_bounds__(256) void stage2_kernel(KParams P, const uint16_t *__restrict__ q,
+                                                    float *__restrict__ out, float *__restrict__ cert,
+                                                    Workspace W, float qscale) {
+    const int h = blockIdx.x, b = blockIdx.y;
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int QPK = P.qpk;
+    const Geom G = geom(P.scheme);
+    const bool wit = P.scheme == KVQ_SCHEME_WITCERT;
+    const size_t bh = (size_t)b * P.Hkv + h;
+    const int l = P.state[bh * 4], nkq = P.state[bh * 4 + 1];
+    const int W0 = wit ? nkq : (l > P.R ? l - P.R : 0);        // first fp16-value token
+    const int nr = l - W0;
+    const int win = wit ? WPT : P.R;
+    const int npages = wit ? nkq / WPT : (W0 + PT - 1) / PT;
+    const int nsplit = (npages + P.split_pages - 1) / P.split_pages;
+
+    __shared__ float qs[S2_MAXQ][D];
+    __shared__ float sc[S2_MAXQ][S2_MAXW];
+    __shared__ float mr[S2_MAXQ], lr[S2_MAXQ];
+    for (int i = tid; i < QPK * D; i += 256)
+        qs[i / D][i % D] = h2f(q[((size_t)b * P.Hq + (size_t)h * QPK + i / D) * D + i % D]);
+    __syncthreads();
+
+    // scores of the window: one wave per token, lane = channels 2L, 2L+1
+    for (int i = wave; i < nr; i += 4) {
+        const int t = W0 + i;
+        float k0, k1;
+        if (!wit && t < nkq) {
+            const int pid = P.table[(size_t)b * P.max_pages + t / PT];
+            if (pid < 0 || pid >= P.n_pages) {
+                if (lane == 0) atomicOr(P.status, (uint32_t)KVQ_STATUS_UNMAPPED_PAGE);
+                k0 = k1 = 0.f;
+            } else {
+                const uint8_t *page = cpage(P, pid, h);
+                k0 = key_tilde_page(P, G, page, t % PT, 2 * lane, h);
+                k1 = key_tilde_page(P, G, page, t % PT, 2 * lane + 1, h);
+            }
+        } else {
+            const uint32_t kk = ((const uint32_t *)P.res_k)[(bh * win + (size_t)(t - nkq)) * (D / 2) + lane];
+            k0 = h2f((uint16_t)(kk & 0xffff));
+            k1 = h2f((uint16_t)(kk >> 16));
+        }
+        for (int hh = 0; hh < QPK; hh++) {
+            float part = fmaf(qs[hh][2 * lane + 1], k1, qs[hh][2 * lane] * k0);
+#pragma unroll
+            for (int msk = 1; msk < 64; msk <<= 1) part += shfl_xor(part, msk);
+            if (lane == 0) sc[hh][i] = part * qscale;
+        }
+    }
+    __syncthreads();
+    // softmax statistics of the window per query head
+    for (int hh = wave; hh < QPK; hh += 4) {
+        float mx = -INFINITY;
+        for (int i = lane; i < nr; i += 64) mx = fmaxf(mx, sc[hh][i]);
+#pragma unroll
+        for (int msk = 1; msk < 64; msk <<= 1) mx = fmaxf(mx, shfl_xor(mx, msk));
+        float sum = 0.f;
+        for (int i = lane; i < nr; i += 64) {
+            const float pv = exp2f(sc[hh][i] - mx);
+            sc[hh][i] = pv;
+            sum += pv;
+        }
+#pragma unroll
+        for (int msk = 1; msk < 64; msk <<= 1) sum += shfl_xor(sum, msk);
+        if (lane == 0) { mr[hh] = mx; lr[hh] = sum; }
+    }
+    __syncthreads();
+    // window output and merge, thread = (query head, channel)
+    for (int i = tid; i < QPK * D; i += 256) {
+        const int hh = i / D, c = i % D;
+        const int hq = h * QPK + hh;
+        float acc = 0.f;
+        for (int j = 0; j < nr; j++) {
+            const int t = W0 + j;
+            const size_t slot = wit ? (size_t)(t - nkq) : (size_t)(t % P.R);
+            acc = fmaf(sc[hh][j], h2f(P.res_v[(bh * win + slot) * D + c]), acc);
+        }
+        const size_t row0 = ((size_t)b * P.Hq + hq) * W.max_splits;
+        float M = nr > 0 ? mr[hh] + log2f(lr[hh]) : -INFINITY;
+        for (int sp = 0; sp < nsplit; sp++) M = fmaxf(M, W.ml[row0 + sp].x);
+        float wsum = 0.f, num = 0.f, anum = 0.f;
+        if (nr > 0) {
+            const float wr = exp2f(mr[hh] + log2f(lr[hh]) - M);
+            wsum += wr;
+            num += wr * (acc / lr[hh]);
+            anum += wr;                                  // fp16 tokens: u = 0
+        }
+        for (int sp = 0; sp < nsplit; sp++) {
+            const float2 ml = W.ml[row0 + sp];
+            const float ws = exp2f(ml.x - M);
+            wsum += ws;
+            num = fmaf(ws, W.o[(row0 + sp) * D + c], num);
+            anum = fmaf(ws, ml.y, anum);
+        }
+        const bool any = wsum > 0.f;
+        out[((size_t)b * P.Hq + hq) * D + c] = any ? num / wsum : 0.f;
+        if (cert && c == 0) cert[(size_t)b * P.Hq + hq] = any ? anum / wsum : 0.f;
+    }
+}
+
+// ---------------------------------------------------------------------------
+hipError_t launch_decode(const KParams &P, const uint16_t *q, float *out, float *cert,
+                         float sm_scale, float kappa, const Workspace &W, hipStream_t s) {
+    const float qscale = sm_scale * 1.4426950408889634f;
+    if (P.scheme == KVQ_SCHEME_WITCERT) {
+        dim3 g1(W.max_splits, P.Hkv, P.B);
+        switch (P.qpk) {
+            case 1: stage1_witcert_kernel<1><<<g1, 64, 0, s>>>(P, q, W, qscale, sm_scale, kappa); break;
+            case 2: stage1_witcert_kernel<2><<<g1, 64, 0, s>>>(P, q, W, qscale, sm_scale, kappa); break;
+            case 4: stage1_witcert_kernel<4><<<g1, 64, 0, s>>>(P, q, W, qscale, sm_scale, kappa); break;
+            case 8: stage1_witcert_kernel<8><<<g1, 64, 0, s>>>(P, q, W, qscale, sm_scale, kappa); break;
+            default: return hipErrorInvalidValue;
+        }
+    } else {
+        dim3 g1(W.max_splits, P.Hq, P.B);
+        if (P.scheme == KVQ_SCHEME_KITTY)
+            stage1_valu_kernel<true><<<g1, 64, 0, s>>>(P, q, W, qscale);
+        else
+            stage1_valu_kernel<false><<<g1, 64, 0, s>>>(P, q, W, qscale);
+    }
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    stage2_kernel<<<dim3(P.Hkv, P.B), 256, 0, s>>>(P, q, out, cert, W, qscale);
+    return hipGetLastError();
+}
+
+}  // namespace kvq

@@ -1,0 +1,44 @@
+// kvq_kernels.hpp -- kernel parameter block and launch declarations shared by
+// the host API (kvq_api.cpp) and the kernel translation units.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace kvq {
+
+struct KParams {
+    uint8_t *pool;
+    const int32_t *table;
+    int32_t *state;
+    uint16_t *res_k;
+    uint16_t *res_v;
+    const uint8_t *boost_idx;
+    uint32_t *status;
+    int B, Hq, Hkv, R, max_pages, n_pages, page_bytes, scheme, qpk, split_pages;
+    uint32_t layer;
+    uint64_t seed;
+};
+
+// Stage-1 partial results: per (request, query head, split):
+//   o[128] fp32 (acc / l_s), then {lse_s, A_s} fp32 pairs.
+struct Workspace {
+    float *o;        // [B][Hq][max_splits][128]
+    float2 *ml;      // [B][Hq][max_splits]  (lse in log2 units, A)
+    int max_splits;
+};
+
+// write path (kvq_write.hip)
+hipError_t launch_append(const KParams &P, const uint16_t *k, const uint16_t *v, hipStream_t s);
+hipError_t launch_flush(const KParams &P, hipStream_t s);
+hipError_t launch_prefill(const KParams &P, int req0, int n_req, const uint16_t *K,
+                          const uint16_t *V, long long ld, const int32_t *lengths,
+                          hipStream_t s);
+hipError_t launch_kitty_calibrate(const KParams &P, const uint16_t *calib, int n_tokens,
+                                  uint8_t *idx_out, hipStream_t s);
+
+// read path (kvq_decode.hip)
+hipError_t launch_decode(const KParams &P, const uint16_t *q, float *out, float *cert,
+                         float sm_scale, float kappa, const Workspace &W, hipStream_t s);
+
+}  // namespace kvq

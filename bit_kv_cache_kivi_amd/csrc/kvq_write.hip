@@ -1,0 +1,525 @@
+// kvq_write.hip -- write path: token append (value FIFO pack), key group
+// flush, bulk prefill and Kitty calibration for KIVI2 / KITTY; active-block
+// append, block flush and prefill for WITCERT.
+//
+// KIVI2: keys gather in an fp16 residual and are quantized per channel in
+// groups of 32 tokens once R have gathered; values leave an R-token fp16 FIFO
+// one at a time and are quantized per token in groups of 32 channels ("KIVI"
+// explainer 3.3).  KITTY boosts 16 key channels to 4 bits and stores their
+// high 2 bits in a separate plane ("Kitty" summary, Dense-Sparse
+// Decomposition).  WITCERT quantizes whole 256-token blocks per channel with
+// Philox dither ("WitCert" write-kernel paragraph).
+#include "kvq_common.hpp"
+#include "kvq_kernels.hpp"
+
+namespace kvq {
+
+__device__ inline uint8_t *page_ptr(const KParams &P, int pid, int h) {
+    return P.pool + ((size_t)pid * P.Hkv + h) * (size_t)P.page_bytes;
+}
+
+__device__ inline bool page_ok(const KParams &P, int pid) {
+    return pid >= 0 && pid < P.n_pages;
+}
+
+// ---------------------------------------------------------------------------
+// KIVI2 / KITTY: quantize the keys of one 64-token page from fp16 rows
+// src[t * D + c] (t in [0, 64)).  256 threads: thread (c = tid & 127,
+// half = tid >> 7) takes the two 32-token groups half, half + 2 ... of its
+// channel.  codes: LDS scratch [64][128].
+// ---------------------------------------------------------------------------
+__device__ void quant_key_page(const KParams &P, const Geom &G, const uint16_t *src,
+                               uint8_t *page, const int *inv, const uint8_t *bits4,
+                               uint8_t (*codes)[D]) {
+    const int tid = threadIdx.x;
+    const int c = tid & 127;
+    const int gi = tid >> 7;                         // group 0 or 1 of the page
+    const float lmax = bits4[c] ? 15.0f : 3.0f;
+    float xs[32];
+    float mn = 0.f, mx = 0.f;
+#pragma unroll
+    for (int i = 0; i < 32; i++) {
+        xs[i] = h2f(src[(size_t)(32 * gi + i) * D + c]);
+        if (i == 0) { mn = xs[0]; mx = xs[0]; }
+        else { mn = fminf(mn, xs[i]); mx = fmaxf(mx, xs[i]); }
+    }
+    AsymParams ap = asym_params(mn, mx, lmax);
+#pragma unroll
+    for (int i = 0; i < 32; i++) codes[32 * gi + i][c] = (uint8_t)asym_code(xs[i], ap, lmax);
+    uint32_t *ks = (uint32_t *)(page + G.ks);
+    ks[128 * gi + key_stat_slot(c)] = (uint32_t)ap.s16 | ((uint32_t)ap.z16 << 16);
+    __syncthreads();
+    uint32_t *kc = (uint32_t *)(page + G.kc);
+    for (int w = tid; w < 512; w += 256) {
+        int d = 4 * (w >> 8) + (w & 3);
+        int L = (w >> 2) & 63;
+        int g = L >> 4, r = L & 15;
+        int t = 16 * (d >> 1) + r;
+        int kcb = 2 * (d & 1);
+        uint32_t val = 0;
+#pragma unroll
+        for (int hh = 0; hh < 2; hh++)
+#pragma unroll
+            for (int j = 0; j < 8; j++) {
+                int cc = 32 * (kcb + hh) + 8 * g + j;
+                val |= (uint32_t)(codes[t][cc] & 3) << (4 * j + 2 * hh);
+            }
+        kc[w] = val;
+    }
+    if (P.scheme == KVQ_SCHEME_KITTY && tid < 64) {
+        uint32_t *kh = (uint32_t *)(page + G.kh);
+        int g = tid >> 4, r = tid & 15;
+        uint32_t val = 0;
+        for (int n = 0; n < 4; n++)
+            for (int i = 0; i < 4; i++) {
+                int o = 4 * g + i;
+                int cc = inv[o];
+                uint32_t hi = (uint32_t)(codes[16 * n + r][cc] >> 2);
+                val |= hi << (4 * (4 * (n & 1) + i) + 2 * (n >> 1));
+            }
+        kh[tid] = val;
+    }
+    __syncthreads();
+}
+
+// Kitty boost tables of KV head h in LDS: bits4[c] (channel takes 16 levels)
+// and inv[o] (channel of high-plane offset o).
+__device__ void load_boost(const KParams &P, int h, int *inv, uint8_t *bits4) {
+    const int tid = threadIdx.x;
+    if (tid < NB) inv[tid] = 0;
+    __syncthreads();
+    if (tid < D) {
+        bits4[tid] = 0;
+        if (P.scheme == KVQ_SCHEME_KITTY) {
+            int o = P.boost_idx[(size_t)h * D + tid];
+            if (o < NB) {
+                bits4[tid] = 1;
+                inv[o] = tid;
+            }
+        }
+    }
+    __syncthreads();
+}
+
+// ---------------------------------------------------------------------------
+// append (KIVI2 / KITTY): one wave per (KV head, request)
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(64) void append_kivi_kernel(KParams P, const uint16_t *__restrict__ kn,
+                                                         const uint16_t *__restrict__ vn) {
+    const int h = blockIdx.x, b = blockIdx.y, lane = threadIdx.x;
+    const Geom G = geom(P.scheme);
+    const size_t bh = (size_t)b * P.Hkv + h;
+    int32_t *st = P.state + bh * 4;
+    const int l = st[0], nkq = st[1];
+    const int R = P.R;
+    if (l - nkq >= R) {
+        if (lane == 0) atomicOr(P.status, (uint32_t)KVQ_STATUS_RESIDUAL_FULL);
+        return;
+    }
+    if (l >= P.max_pages * PT) {
+        if (lane == 0) atomicOr(P.status, (uint32_t)KVQ_STATUS_CAPACITY);
+        return;
+    }
+    const uint32_t *kin = (const uint32_t *)(kn + bh * D);
+    const uint32_t *vin = (const uint32_t *)(vn + bh * D);
+    uint32_t *rk = (uint32_t *)(P.res_k + (bh * R + (size_t)(l - nkq)) * D);
+    uint32_t *rv = (uint32_t *)(P.res_v + (bh * R + (size_t)(l % R)) * D);
+    if (l >= R) {
+        // the token leaving the fp16 value window is quantized per token
+        const int t = l - R;
+        const int pid = P.table[(size_t)b * P.max_pages + t / PT];
+        if (!page_ok(P, pid)) {
+            if (lane == 0) atomicOr(P.status, (uint32_t)KVQ_STATUS_UNMAPPED_PAGE);
+            return;
+        }
+        uint8_t *page = page_ptr(P, pid, h);
+        const uint32_t old = rv[lane];               // channels 2*lane, 2*lane+1
+        const float x0 = h2f((uint16_t)(old & 0xffffu)), x1 = h2f((uint16_t)(old >> 16));
+        float mn = fminf(x0, x1), mx = fmaxf(x0, x1);
+#pragma unroll
+        for (int m = 8; m >= 1; m >>= 1) {           // 16 lanes = one 32-channel group
+            mn = fminf(mn, shfl_xor(mn, m));
+            mx = fmaxf(mx, shfl_xor(mx, m));
+        }
+        const AsymParams ap = asym_params(mn, mx, 3.0f);
+        const uint32_t code[2] = {asym_code(x0, ap, 3.0f), asym_code(x1, ap, 3.0f)};
+        const int tp = t % PT;
+        uint32_t *vc = (uint32_t *)(page + G.vc);
+#pragma unroll
+        for (int e = 0; e < 2; e++) {
+            int dw, sh;
+            value_code_pos(tp, 2 * lane + e, dw, sh);
+            uint32_t w = vc[dw];
+            w = (w & ~(3u << sh)) | (code[e] << sh);
+            vc[dw] = w;
+        }
+        if ((lane & 15) == 0) {
+            uint32_t *vs = (uint32_t *)(page + G.vs);
+            vs[tp * 4 + (lane >> 4)] = (uint32_t)ap.s16 | ((uint32_t)ap.z16 << 16);
+        }
+    }
+    rk[lane] = kin[lane];
+    rv[lane] = vin[lane];
+    if (lane == 0) st[0] = l + 1;
+}
+
+// ---------------------------------------------------------------------------
+// flush (KIVI2 / KITTY): 256 threads per (KV head, request)
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void flush_kivi_kernel(KParams P) {
+    const int h = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
+    const Geom G = geom(P.scheme);
+    const size_t bh = (size_t)b * P.Hkv + h;
+    int32_t *st = P.state + bh * 4;
+    const int l = st[0], nkq = st[1];
+    if (l - nkq != P.R) return;
+    __shared__ uint8_t codes[PT][D];
+    __shared__ int inv[NB];
+    __shared__ uint8_t bits4[D];
+    __shared__ int bad;
+    const int np = P.R / PT;
+    if (tid == 0) {
+        bad = 0;
+        for (int p = 0; p < np; p++)
+            if (!page_ok(P, P.table[(size_t)b * P.max_pages + nkq / PT + p])) bad = 1;
+    }
+    load_boost(P, h, inv, bits4);                    // contains __syncthreads
+    if (bad) {
+        if (tid == 0) atomicOr(P.status, (uint32_t)KVQ_STATUS_UNMAPPED_PAGE);
+        return;
+    }
+    for (int p = 0; p < np; p++) {
+        const int pid = P.table[(size_t)b * P.max_pages + nkq / PT + p];
+        quant_key_page(P, G, P.res_k + (bh * P.R + (size_t)p * PT) * D, page_ptr(P, pid, h),
+                       inv, bits4, codes);
+    }
+    if (tid == 0) st[1] = nkq + P.R;
+}
+
+// ---------------------------------------------------------------------------
+// prefill (KIVI2 / KITTY): one 256-thread block per (page, KV head, request)
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void prefill_kivi_kernel(KParams P, int req0,
+                                                          const uint16_t *__restrict__ K,
+                                                          const uint16_t *__restrict__ V,
+                                                          long long ld,
+                                                          const int32_t *__restrict__ lengths) {
+    const int p = blockIdx.x, h = blockIdx.y, rr = blockIdx.z, b = req0 + rr;
+    const int tid = threadIdx.x;
+    const Geom G = geom(P.scheme);
+    const int R = P.R;
+    const int len = lengths[rr];
+    if (len < 0 || len > P.max_pages * PT || (long long)len > ld) {
+        if (p == 0 && tid == 0) atomicOr(P.status, (uint32_t)KVQ_STATUS_BAD_LENGTH);
+        return;
+    }
+    const int rk = len ? ((len - 1) % R) + 1 : 0;
+    const int nkq = len - rk;
+    const int nvq = len > R ? len - R : 0;
+    const size_t bh = (size_t)b * P.Hkv + h;
+    if (p == 0 && tid == 0) {
+        P.state[bh * 4 + 0] = len;
+        P.state[bh * 4 + 1] = nkq;
+        P.state[bh * 4 + 2] = 0;
+        P.state[bh * 4 + 3] = 0;
+    }
+    const int t0 = p * PT;
+    if (t0 >= len) return;
+    const uint16_t *Ks = K + ((size_t)rr * P.Hkv + h) * (size_t)ld * D;
+    const uint16_t *Vs = V + ((size_t)rr * P.Hkv + h) * (size_t)ld * D;
+    // fp16 windows: keys [nkq, len) and values [nvq, len) of this page
+    for (int i = tid; i < PT * (D / 2); i += 256) {
+        const int t = t0 + i / (D / 2), w = i % (D / 2);
+        if (t >= len) break;
+        if (t >= nkq)
+            ((uint32_t *)P.res_k)[(bh * R + (size_t)(t - nkq)) * (D / 2) + w] =
+                ((const uint32_t *)Ks)[(size_t)t * (D / 2) + w];
+        if (t >= nvq)
+            ((uint32_t *)P.res_v)[(bh * R + (size_t)(t % R)) * (D / 2) + w] =
+                ((const uint32_t *)Vs)[(size_t)t * (D / 2) + w];
+    }
+    if (t0 >= nkq && t0 >= nvq) return;
+    const int pid = P.table[(size_t)b * P.max_pages + p];
+    if (!page_ok(P, pid)) {
+        if (tid == 0) atomicOr(P.status, (uint32_t)KVQ_STATUS_UNMAPPED_PAGE);
+        return;
+    }
+    uint8_t *page = page_ptr(P, pid, h);
+    __shared__ uint8_t codes[PT][D];
+    __shared__ int inv[NB];
+    __shared__ uint8_t bits4[D];
+    load_boost(P, h, inv, bits4);
+    if (t0 < nkq)                                    // nkq is a multiple of 128: whole page
+        quant_key_page(P, G, Ks + (size_t)t0 * D, page, inv, bits4, codes);
+    if (t0 < nvq) {
+        // values, per token, groups of 32 channels: thread (token tl, group jv)
+        const int tl = tid >> 2, jv = tid & 3;
+        const int t = t0 + tl;
+        if (t < nvq) {
+            float xs[32];
+            float mn = 0.f, mx = 0.f;
+#pragma unroll
+            for (int i = 0; i < 32; i++) {
+                xs[i] = h2f(Vs[(size_t)t * D + 32 * jv + i]);
+                if (i == 0) { mn = xs[0]; mx = xs[0]; }
+                else { mn = fminf(mn, xs[i]); mx = fmaxf(mx, xs[i]); }
+            }
+            AsymParams ap = asym_params(mn, mx, 3.0f);
+#pragma unroll
+            for (int i = 0; i < 32; i++) codes[tl][32 * jv + i] = (uint8_t)asym_code(xs[i], ap, 3.0f);
+            ((uint32_t *)(page + G.vs))[tl * 4 + jv] = (uint32_t)ap.s16 | ((uint32_t)ap.z16 << 16);
+        } else {
+#pragma unroll
+            for (int i = 0; i < 32; i++) codes[tl][32 * jv + i] = 0;
+        }
+        __syncthreads();
+        uint32_t *vc = (uint32_t *)(page + G.vc);
+        for (int w = tid; w < 512; w += 256) {
+            const int nt = 4 * (w >> 8) + (w & 3);
+            const int L = (w >> 2) & 63;
+            const int g = L >> 4, r = L & 15;
+            const int c = 16 * nt + r;
+            uint32_t val = 0;
+#pragma unroll
+            for (int ks = 0; ks < 2; ks++)
+#pragma unroll
+                for (int j = 0; j < 8; j++)
+                    val |= (uint32_t)codes[32 * ks + 8 * g + j][c] << (4 * j + 2 * ks);
+            vc[w] = val;
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Kitty calibration: static boost set per KV head from a calibration slice
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(128) void kitty_calibrate_kernel(const uint16_t *__restrict__ calib,
+                                                             int T, uint8_t *__restrict__ idx_out) {
+    const int h = blockIdx.x, c = threadIdx.x;
+    __shared__ float am[D];
+    __shared__ uint8_t chosen[D];
+    float a = 0.0f;
+    for (int t = 0; t < T; t++) a = fmaxf(a, fabsf(h2f(calib[((size_t)h * T + t) * D + c])));
+    am[c] = a;
+    chosen[c] = 0;
+    __syncthreads();
+    if (c == 0) {
+        for (int j = 0; j < NB; j++) {
+            int best = -1;
+            for (int cc = 0; cc < D; cc++)
+                if (!chosen[cc] && (best < 0 || am[cc] > am[best])) best = cc;
+            chosen[best] = 1;
+        }
+        int off = 0;
+        for (int cc = 0; cc < D; cc++)
+            idx_out[(size_t)h * D + cc] = chosen[cc] ? (uint8_t)(off++) : (uint8_t)(NB + 1);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// WITCERT
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(64) void append_witcert_kernel(KParams P, const uint16_t *__restrict__ kn,
+                                                            const uint16_t *__restrict__ vn) {
+    const int h = blockIdx.x, b = blockIdx.y, lane = threadIdx.x;
+    const size_t bh = (size_t)b * P.Hkv + h;
+    int32_t *st = P.state + bh * 4;
+    const int l = st[0], nq = st[1];
+    if (l - nq >= WPT) {
+        if (lane == 0) atomicOr(P.status, (uint32_t)KVQ_STATUS_RESIDUAL_FULL);
+        return;
+    }
+    if (l >= P.max_pages * WPT) {
+        if (lane == 0) atomicOr(P.status, (uint32_t)KVQ_STATUS_CAPACITY);
+        return;
+    }
+    const size_t row = (bh * WPT + (size_t)(l - nq)) * (D / 2);
+    ((uint32_t *)P.res_k)[row + lane] = ((const uint32_t *)kn)[bh * (D / 2) + lane];
+    ((uint32_t *)P.res_v)[row + lane] = ((const uint32_t *)vn)[bh * (D / 2) + lane];
+    if (lane == 0) st[0] = l + 1;
+}
+
+// Quantize one 256-token block (keys or values) of KV head h, request b from
+// fp16 rows src[t * D + c].  256 threads.  Pass 1: amax per channel (thread
+// (c, half) over 128 tokens, combined in LDS).  Pass 2: thread (channel quad
+// cq = tid & 31, token phase tp = tid >> 5) draws one Philox4x32-10 block per
+// token and uses all four words for channels 4cq .. 4cq+3.
+__device__ void quant_witcert_block(const KParams &P, int b, int h, int blk, int side,
+                                    const uint16_t *src, int8_t *codes, uint16_t *scales,
+                                    float *amax_s) {
+    const int tid = threadIdx.x;
+    {
+        const int c = tid & 127, half = tid >> 7;
+        float a = 0.0f;
+        for (int i = 0; i < 128; i++)
+            a = fmaxf(a, fabsf(h2f(src[(size_t)(128 * half + i) * D + c])));
+        amax_s[tid] = a;
+    }
+    __syncthreads();
+    if (tid < D) {
+#pragma clang fp contract(off)
+        const float a = fmaxf(amax_s[tid], amax_s[tid + 128]);
+        uint16_t s16 = 0;
+        if (a > 0.0f) {
+            s16 = f2h(a / 126.5f);
+            if (127.0f * h2f(s16) <= a) s16 = (uint16_t)(s16 + 1);
+        }
+        scales[tid] = s16;
+    }
+    __syncthreads();
+    const int cq = tid & 31, tp = tid >> 5;
+    float s[4];
+    bool nz[4];
+#pragma unroll
+    for (int e = 0; e < 4; e++) {
+        const uint16_t s16 = scales[4 * cq + e];
+        s[e] = h2f(s16);
+        nz[e] = s16 != 0;
+    }
+    const uint32_t k0 = (uint32_t)P.seed;
+    const uint32_t k1 = (uint32_t)(P.seed >> 32) ^ (uint32_t)side;
+    for (int i = 0; i < WPT / 8; i++) {
+        const int t = tp + 8 * i;
+        const uint32_t tok = (uint32_t)(blk * WPT + t);
+        U4 ctr{tok, (uint32_t)cq, (P.layer << 16) | (uint32_t)h, (uint32_t)b};
+        U4 u = philox4x32_10(ctr, k0, k1);
+        const uint32_t wv[4] = {u.x, u.y, u.z, u.w};
+        const uint2 xin = *(const uint2 *)(src + (size_t)t * D + 4 * cq);
+        const uint16_t xb[4] = {(uint16_t)(xin.x & 0xffff), (uint16_t)(xin.x >> 16),
+                                (uint16_t)(xin.y & 0xffff), (uint16_t)(xin.y >> 16)};
+        uint32_t packed = 0;
+#pragma unroll
+        for (int e = 0; e < 4; e++) {
+#pragma clang fp contract(off)
+            float c = 0.0f;
+            if (nz[e]) {
+                const float xi = dither_from_word(wv[e]);
+                const float q = h2f(xb[e]) / s[e];
+                c = rintf(q + xi);
+                c = fminf(fmaxf(c, -127.0f), 127.0f);
+            }
+            packed |= ((uint32_t)(uint8_t)(int8_t)(int)c) << (8 * e);
+        }
+        *(uint32_t *)(codes + (size_t)t * D + 4 * cq) = packed;
+    }
+    __syncthreads();
+}
+
+__global__ __launch_bounds__(256) void flush_witcert_kernel(KParams P) {
+    const int h = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
+    const Geom G = geom(P.scheme);
+    const size_t bh = (size_t)b * P.Hkv + h;
+    int32_t *st = P.state + bh * 4;
+    const int l = st[0], nq = st[1];
+    if (l - nq != WPT) return;
+    const int blk = nq / WPT;
+    const int pid = P.table[(size_t)b * P.max_pages + blk];
+    if (!page_ok(P, pid)) {
+        if (tid == 0) atomicOr(P.status, (uint32_t)KVQ_STATUS_UNMAPPED_PAGE);
+        return;
+    }
+    __shared__ float amax_s[256];
+    __shared__ uint16_t scales[D];
+    uint8_t *page = page_ptr(P, pid, h);
+    for (int side = 0; side < 2; side++) {
+        const uint16_t *src = (side ? P.res_v : P.res_k) + bh * WPT * D;
+        quant_witcert_block(P, b, h, blk, side, src, (int8_t *)(page + (side ? G.vc : G.kc)),
+                            scales, amax_s);
+        if (tid < D) ((uint16_t *)(page + (side ? G.vs : G.ks)))[tid] = scales[tid];
+        __syncthreads();
+    }
+    if (tid == 0) st[1] = nq + WPT;
+}
+
+__global__ __launch_bounds__(256) void prefill_witcert_kernel(KParams P, int req0,
+                                                             const uint16_t *__restrict__ K,
+                                                             const uint16_t *__restrict__ V,
+                                                             long long ld,
+                                                             const int32_t *__restrict__ lengths) {
+    const int p = blockIdx.x, h = blockIdx.y, rr = blockIdx.z, b = req0 + rr;
+    const int tid = threadIdx.x;
+    const Geom G = geom(P.scheme);
+    const int len = lengths[rr];
+    if (len < 0 || len > P.max_pages * WPT || (long long)len > ld) {
+        if (p == 0 && tid == 0) atomicOr(P.status, (uint32_t)KVQ_STATUS_BAD_LENGTH);
+        return;
+    }
+    const int r = len ? ((len - 1) % WPT) + 1 : 0;
+    const int nq = len - r;
+    const size_t bh = (size_t)b * P.Hkv + h;
+    if (p == 0 && tid == 0) {
+        P.state[bh * 4 + 0] = len;
+        P.state[bh * 4 + 1] = nq;
+        P.state[bh * 4 + 2] = 0;
+        P.state[bh * 4 + 3] = 0;
+    }
+    const int t0 = p * WPT;
+    if (t0 >= len) return;
+    const uint16_t *Ks = K + ((size_t)rr * P.Hkv + h) * (size_t)ld * D;
+    const uint16_t *Vs = V + ((size_t)rr * P.Hkv + h) * (size_t)ld * D;
+    if (t0 >= nq) {                                  // the active block: copy to fp16
+        for (int i = tid; i < WPT * (D / 2); i += 256) {
+            const int t = t0 + i / (D / 2), w = i % (D / 2);
+            if (t >= len) break;
+            const size_t dst = (bh * WPT + (size_t)(t - nq)) * (D / 2) + w;
+            ((uint32_t *)P.res_k)[dst] = ((const uint32_t *)Ks)[(size_t)t * (D / 2) + w];
+            ((uint32_t *)P.res_v)[dst] = ((const uint32_t *)Vs)[(size_t)t * (D / 2) + w];
+        }
+        return;
+    }
+    const int pid = P.table[(size_t)b * P.max_pages + p];
+    if (!page_ok(P, pid)) {
+        if (tid == 0) atomicOr(P.status, (uint32_t)KVQ_STATUS_UNMAPPED_PAGE);
+        return;
+    }
+    __shared__ float amax_s[256];
+    __shared__ uint16_t scales[D];
+    uint8_t *page = page_ptr(P, pid, h);
+    for (int side = 0; side < 2; side++) {
+        const uint16_t *src = (side ? Vs : Ks) + (size_t)t0 * D;
+        quant_witcert_block(P, b, h, p, side, src, (int8_t *)(page + (side ? G.vc : G.kc)),
+                            scales, amax_s);
+        if (tid < D) ((uint16_t *)(page + (side ? G.vs : G.ks)))[tid] = scales[tid];
+        __syncthreads();
+    }
+}
+
+// ---------------------------------------------------------------------------
+// launchers
+// ---------------------------------------------------------------------------
+hipError_t launch_append(const KParams &P, const uint16_t *k, const uint16_t *v, hipStream_t s) {
+    dim3 grid(P.Hkv, P.B);
+    if (P.scheme == KVQ_SCHEME_WITCERT)
+        append_witcert_kernel<<<grid, 64, 0, s>>>(P, k, v);
+    else
+        append_kivi_kernel<<<grid, 64, 0, s>>>(P, k, v);
+    return hipGetLastError();
+}
+
+hipError_t launch_flush(const KParams &P, hipStream_t s) {
+    dim3 grid(P.Hkv, P.B);
+    if (P.scheme == KVQ_SCHEME_WITCERT)
+        flush_witcert_kernel<<<grid, 256, 0, s>>>(P);
+    else
+        flush_kivi_kernel<<<grid, 256, 0, s>>>(P);
+    return hipGetLastError();
+}
+
+hipError_t launch_prefill(const KParams &P, int req0, int n_req, const uint16_t *K,
+                          const uint16_t *V, long long ld, const int32_t *lengths,
+                          hipStream_t s) {
+    dim3 grid(P.max_pages, P.Hkv, n_req);
+    if (P.scheme == KVQ_SCHEME_WITCERT)
+        prefill_witcert_kernel<<<grid, 256, 0, s>>>(P, req0, K, V, ld, lengths);
+    else
+        prefill_kivi_kernel<<<grid, 256, 0, s>>>(P, req0, K, V, ld, lengths);
+    return hipGetLastError();
+}
+
+hipError_t launch_kitty_calibrate(const KParams &P, const uint16_t *calib, int n_tokens,
+                                  uint8_t *idx_out, hipStream_t s) {
+    kitty_calibrate_kernel<<<P.Hkv, 128, 0, s>>>(calib, n_tokens, idx_out);
+    return hipGetLastError();
+}
+
+}  // namespace kvq

@@ -1,0 +1,211 @@
+/*
+ * kvq.h -- C ABI of libkvq.so: low-bit KV-cache quantization on write and
+ * single-query decode attention with dequantization fused into the read, for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * Schemes
+ *   KVQ_SCHEME_KIVI2   keys: 2-bit asymmetric, one group = one channel x G=32
+ *                      consecutive tokens; values: 2-bit asymmetric, one group
+ *                      = one token x 32 consecutive channels; fp16 scale and
+ *                      zero point per group; the newest keys (1..R) and values
+ *                      (R) stay fp16.  ("KIVI" explainer, sections 3.1-3.3
+ *                      and section 4 steps 2-5.)
+ *   KVQ_SCHEME_KITTY   KIVI2 with n_boost key channels per KV head stored at
+ *                      4 bits, split into a dense low 2-bit plane (all
+ *                      channels) and a structured high 2-bit plane (boosted
+ *                      channels only); code = low | high << 2.  ("Kitty"
+ *                      summary: Channel-Wise Precision Boost Mechanism;
+ *                      Page-Centric Memory Layout and Dense-Sparse
+ *                      Decomposition; Algorithm 1.)
+ *   KVQ_SCHEME_WITCERT INT8 keys and values with subtractive dither:
+ *                      x_hat = s (round(x/s + xi) - xi), s = amax/126.5 per
+ *                      (256-token block, channel) stored fp16 and used for
+ *                      quantization, xi from Philox4x32-10 keyed by (request,
+ *                      layer, KV head, token, channel); the active block stays
+ *                      fp16; a per-query certificate A = sum_t p_t exp(u_t) is
+ *                      accumulated in the attention pass.  ("WitCert" page:
+ *                      write-kernel paragraph, "Key structure", quantised-path
+ *                      certificate paragraph.)
+ *
+ * Step order per decode step (all calls asynchronous on the caller's stream,
+ * none synchronizes, allocates or frees, so a step can be captured in a HIP
+ * graph):  kvq_flush_key_group -> kvq_append_token -> kvq_decode_attention.
+ * The flush quantizes the key residual once it holds R tokens (the pipeline
+ * order of the "Kitty" summary: attention runs on the fp16 group, the group is
+ * quantized once it has gathered).
+ *
+ * Memory ownership: every device buffer is allocated and freed by the caller;
+ * the library keeps only the pointers copied into kvq_cache_t.  Device
+ * pointers must be 256-byte aligned (pool) or 16-byte aligned (all others).
+ *
+ * Errors: host-side checks return a negative KVQ_E* code and launch nothing.
+ * Conditions only the device can see set sticky bits in the caller's status
+ * word (KVQ_STATUS_*), read by the caller after its own synchronization; the
+ * affected (request, KV head) is then left unmodified.
+ *
+ * fp16 values cross the ABI as uint16_t bit patterns.
+ */
+#ifndef KVQ_H
+#define KVQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+    KVQ_SCHEME_KIVI2 = 0,
+    KVQ_SCHEME_KITTY = 1,
+    KVQ_SCHEME_WITCERT = 2
+};
+
+/* host-side return codes */
+enum {
+    KVQ_OK = 0,
+    KVQ_EINVAL = -1,      /* a layout field is out of range (see kvq_set_layout) */
+    KVQ_ENULL = -2,       /* a required pointer is NULL */
+    KVQ_EALIGN = -3,      /* a device pointer is misaligned */
+    KVQ_ENOLAYOUT = -4,   /* cache was not filled by kvq_set_layout */
+    KVQ_EWORKSPACE = -5,  /* workspace smaller than kvq_workspace_bytes() */
+    KVQ_ELAUNCH = -6      /* a kernel launch failed (hipGetLastError) */
+};
+
+/* device status bits (sticky, OR-ed into *status) */
+enum {
+    KVQ_STATUS_RESIDUAL_FULL = 1u,  /* append found the key residual / active
+                                       block full: flush was skipped */
+    KVQ_STATUS_CAPACITY = 2u,       /* append beyond max_pages * page_tokens */
+    KVQ_STATUS_UNMAPPED_PAGE = 4u,  /* page-table entry outside [0, n_pages) */
+    KVQ_STATUS_BAD_LENGTH = 8u      /* prefill length outside [0, capacity] */
+};
+
+/* Layout.  Fields the caller fills before kvq_set_layout. */
+typedef struct kvq_layout {
+    int32_t scheme;          /* KVQ_SCHEME_* */
+    int32_t head_dim;        /* D; must be 128 */
+    int32_t n_q_heads;       /* Hq; multiple of n_kv_heads */
+    int32_t n_kv_heads;      /* Hkv; 1 .. 65535 */
+    int32_t batch;           /* B, requests; 1 .. 65535 */
+    int32_t group;           /* G, key group tokens; must be 32 (KIVI2/KITTY) */
+    int32_t value_group;     /* value group channels; must be 32 (KIVI2/KITTY) */
+    int32_t residual;        /* R, key/value fp16 window; multiple of 64 (so of
+                                G), 64 .. 1024 (KIVI2/KITTY) */
+    int32_t block;           /* WitCert block tokens; must be 256 (WITCERT) */
+    int32_t n_boost;         /* KITTY boosted key channels: 16 (0 for others) */
+    int32_t max_pages;       /* page-table row length per request */
+    int32_t n_pages;         /* pages in the pool */
+    int32_t split_pages;     /* stage-1 split size in pages (0: default) */
+    uint32_t layer;          /* WITCERT dither counter field; < 65536 */
+    uint64_t seed;           /* WITCERT dither key */
+} kvq_layout_t;
+
+/* Caller-owned device buffers. */
+typedef struct kvq_buffers {
+    void *pool;               /* n_pages * n_kv_heads * kvq_page_bytes() bytes */
+    const int32_t *page_table;/* [batch][max_pages] physical page ids; a page
+                                 holds page_tokens consecutive tokens */
+    int32_t *state;           /* [batch][n_kv_heads][4]: {l, n_kq, 0, 0}:
+                                 tokens appended, keys (WitCert: both sides)
+                                 quantized */
+    uint16_t *res_k;          /* [batch][n_kv_heads][W][D] fp16 key residual;
+                                 W = residual (KIVI2/KITTY) or block (WITCERT) */
+    uint16_t *res_v;          /* [batch][n_kv_heads][W][D] fp16 value window:
+                                 ring by token index (KIVI2/KITTY) or active
+                                 block (WITCERT) */
+    const uint8_t *boost_idx; /* KITTY: [n_kv_heads][D] offset of each channel
+                                 in the high plane, or n_boost + 1 */
+    uint32_t *status;         /* one uint32 of sticky KVQ_STATUS_* bits */
+} kvq_buffers_t;
+
+/* Filled by kvq_set_layout; plain data, copyable. */
+typedef struct kvq_cache {
+    kvq_layout_t layout;
+    kvq_buffers_t bufs;
+    int32_t page_tokens;      /* 64 (KIVI2/KITTY) or 256 (WITCERT) */
+    int32_t split_pages;      /* resolved stage-1 split, pages */
+    int64_t page_bytes;       /* bytes of one (page, KV head) block */
+    int32_t magic;            /* set by kvq_set_layout */
+    int32_t reserved;
+} kvq_cache_t;
+
+/* Validate `layout` and `bufs` and fill `cache`.  Host only, synchronous, no
+ * device work.  Returns KVQ_OK, KVQ_EINVAL (head_dim != 128; Hq % Hkv != 0;
+ * group or value_group != 32; residual % 64 != 0 or outside [64, 1024];
+ * block != 256; n_boost not in {0..32} for KITTY; Hkv or layer >= 65536;
+ * batch or max_pages or n_pages < 1), KVQ_ENULL or KVQ_EALIGN.
+ * The residual must be divisible by the key group ("KIVI" explainer 3.3). */
+int kvq_set_layout(kvq_cache_t *cache, const kvq_layout_t *layout,
+                   const kvq_buffers_t *bufs);
+
+/* Append one token per (request, KV head).  k_new, v_new: device fp16
+ * [batch][n_kv_heads][D].  KIVI2/KITTY: the key goes to residual slot
+ * l - n_kq; the value goes to ring slot l mod R after the token leaving the
+ * window (l - R, when l >= R) is quantized per token into the pages ("KIVI"
+ * explainer 3.3 value FIFO).  WITCERT: key and value go to the active block.
+ * Then l += 1.  Device errors: RESIDUAL_FULL, CAPACITY, UNMAPPED_PAGE. */
+int kvq_append_token(const kvq_cache_t *cache, const uint16_t *k_new,
+                     const uint16_t *v_new, hipStream_t stream);
+
+/* Quantize every (request, KV head) whose key residual holds R tokens
+ * (KIVI2/KITTY: per channel, R/G groups of G tokens, written to the pages;
+ * "KIVI" explainer 3.3) or whose active block holds 256 tokens (WITCERT:
+ * keys and values, per channel).  A no-op elsewhere, so it may be called every
+ * step. */
+int kvq_flush_key_group(const kvq_cache_t *cache, hipStream_t stream);
+
+/* Decode attention for one query token per request over the current state.
+ * q: device fp16 [batch][n_q_heads][D]; out: device fp32 [batch][n_q_heads][D];
+ * cert: device fp32 [batch][n_q_heads] (WITCERT certificate, may be NULL;
+ * +inf is a valid value); sm_scale multiplies q.k; kappa multiplies the
+ * certificate's per-block standard deviation.  Query head h reads KV head
+ * h / (n_q_heads / n_kv_heads).  workspace: device, >= kvq_workspace_bytes().
+ * Stage 1 splits the tokens whose key and value are both quantized; stage 2
+ * attends to the fp16 window and merges all partials with log-sum-exp
+ * weights ("WitCert" Key structure).  Returns KVQ_EWORKSPACE if ws_bytes is too
+ * small. */
+int kvq_decode_attention(const kvq_cache_t *cache, const uint16_t *q, float *out,
+                         float *cert, float sm_scale, float kappa,
+                         void *workspace, size_t ws_bytes, hipStream_t stream);
+
+/* ---- helpers ---------------------------------------------------------- */
+
+/* Bytes of one (page, KV head) block for a layout (0 if invalid). */
+int64_t kvq_page_bytes(const kvq_layout_t *layout);
+
+/* Tokens per page for a layout (64 or 256; 0 if invalid). */
+int32_t kvq_page_tokens(const kvq_layout_t *layout);
+
+/* Quantized bytes per token per KV head, keys and values together, statistics
+ * included (96 for KIVI2, 100 for KITTY with 16 boosted, 258 for WITCERT). */
+double kvq_bytes_per_token(const kvq_layout_t *layout);
+
+/* Workspace bytes kvq_decode_attention needs for this cache. */
+size_t kvq_workspace_bytes(const kvq_cache_t *cache);
+
+/* Bulk state for a context ("KIVI" explainer 3.3 prefill split): for requests
+ * [req0, req0 + n_req), K, V: device fp16 [n_req][n_kv_heads][ld_tokens][D],
+ * lengths: device int32 [n_req].  Leaves each (request, KV head) exactly as
+ * streaming its tokens through flush/append would: r_k = ((l-1) mod R) + 1 keys
+ * (WITCERT: ((l-1) mod 256) + 1 tokens) stay fp16, values keep the newest R. */
+int kvq_prefill(const kvq_cache_t *cache, int32_t req0, int32_t n_req,
+                const uint16_t *K, const uint16_t *V, int64_t ld_tokens,
+                const int32_t *lengths, hipStream_t stream);
+
+/* KITTY static boost set from a calibration slice: calib: device fp16
+ * [n_kv_heads][n_tokens][D]; idx_out: device uint8 [n_kv_heads][D].  The
+ * n_boost channels with the largest max|x| are boosted (ties to the lower
+ * channel), offsets in ascending channel order, others n_boost + 1
+ * ("Kitty" summary: Selecting the Top-K Channels; The Boost Index Tensor). */
+int kvq_kitty_calibrate(const kvq_cache_t *cache, const uint16_t *calib,
+                        int32_t n_tokens, uint8_t *idx_out, hipStream_t stream);
+
+/* Static description of a return code or status bit set. */
+const char *kvq_strerror(int code);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* KVQ_H */

@@ -1,0 +1,144 @@
+"""GPU parity of the HIP path (through the C ABI) against the CPU oracle.
+
+Codes, statistics, fp16 windows and state: bit-exact.  Attention output:
+max |delta o| <= 1e-5 absolute; certificate: relative 1e-5 (+inf equal).
+Pools are filled with 0xFF (NaN statistics) so a read of unwritten memory
+poisons the output."""
+import numpy as np
+import pytest
+
+from bit_kv_cache_kivi_amd import inputs
+
+pytestmark = pytest.mark.gpu
+
+TOL_O = 1e-5
+TOL_CERT = 1e-5
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    torch = pytest.importorskip("torch")
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from bit_kv_cache_kivi_amd import kvq
+    kvq.lib()          # the HIP library must load: no fallback
+
+
+def _case(*a, **k):
+    from gpu_harness import Case
+    return Case(*a, **k)
+
+
+def _check_decode(case, out, cert, q, kappa=0.0, cert_check=False):
+    w = case.w
+    g = w.group
+    o = out.cpu().numpy()
+    c = cert.cpu().numpy()
+    worst = 0.0
+    for (b, h) in case.streams:
+        ref, rc = case.oracle_decode(q, b, h, kappa)
+        got = o[b, h * g:(h + 1) * g]
+        assert np.all(np.isfinite(got)), (b, h)
+        err = np.abs(got.astype(np.float64) - ref).max()
+        worst = max(worst, err)
+        assert err <= TOL_O, (b, h, err)
+        if cert_check:
+            gc = c[b, h * g:(h + 1) * g].astype(np.float64)
+            both_inf = np.isinf(gc) & np.isinf(rc)
+            rel = np.abs(gc - rc) / np.maximum(np.abs(rc), 1e-30)
+            assert np.all(both_inf | (rel <= TOL_CERT)), (b, h, gc, rc)
+    return worst
+
+
+@pytest.mark.parametrize("Hq,Hkv", [(2, 2), (8, 2)])
+def test_kivi_prefill_decode_small(Hq, Hkv):
+    w = inputs.workload(3, B=3, Hq=Hq, Hkv=Hkv, ctx=(700, 1301, 2113), steps=3)
+    case = _case(w, extra_tokens=300, split_pages=4)
+    case.check_status()
+    case.check_state()
+    case.check_store()
+    out, cert, q = case.decode_now(99)
+    _check_decode(case, out, cert, q)
+
+
+def test_kivi_streaming_crosses_flush_and_pages():
+    w = inputs.workload(2, B=2, Hq=4, Hkv=4, ctx=(250, 383))
+    case = _case(w, extra_tokens=300, split_pages=2)
+    for i in range(140):                 # crosses a flush on both requests
+        out, cert, q = case.step(decode=(i % 35 == 34 or i in (0, 1, 127, 128, 129)))
+        if out is not None:
+            _check_decode(case, out, cert, q)
+    case.check_status()
+    case.check_state()
+    case.check_store()
+
+
+def test_workload1_exact_config():
+    w = inputs.workload(1)
+    case = _case(w, extra_tokens=64)
+    case.check_state()
+    case.check_store()
+    out, cert, q = case.decode_now(0)
+    err = _check_decode(case, out, cert, q)
+    print(f"workload 1 max|do| = {err:.3e}")
+
+
+@pytest.mark.parametrize("ctx", [(1,), (64,), (128,), (129,), (191,), (192,), (257,)])
+def test_kivi_short_contexts(ctx):
+    w = inputs.workload(2, B=1, Hq=4, Hkv=1, ctx=ctx)
+    case = _case(w, extra_tokens=200, split_pages=1)
+    case.check_state()
+    case.check_store()
+    out, cert, q = case.decode_now(5)
+    _check_decode(case, out, cert, q)
+    for i in range(3):
+        out, cert, q = case.step()
+        _check_decode(case, out, cert, q)
+    case.check_store()
+
+
+def test_kitty_calibrate_store_decode():
+    w = inputs.workload(4, B=2, Hq=2, Hkv=2, ctx=(1100, 1500))
+    case = _case(w, extra_tokens=200, split_pages=3)
+    idx_gpu = case.cache.boost_idx.cpu().numpy()
+    assert np.array_equal(idx_gpu, case.idx)
+    case.check_state()
+    case.check_store()
+    out, cert, q = case.decode_now(1)
+    _check_decode(case, out, cert, q)
+    for i in range(130):
+        out, cert, q = case.step(decode=(i % 64 == 63))
+        if out is not None:
+            _check_decode(case, out, cert, q)
+    case.check_store()
+
+
+@pytest.mark.parametrize("Hq,Hkv", [(8, 2), (2, 2)])
+def test_witcert_store_decode_certificate(Hq, Hkv):
+    w = inputs.workload(5, B=2, Hq=Hq, Hkv=Hkv, ctx=(700, 1024))
+    case = _case(w, extra_tokens=300)
+    case.check_state()
+    case.check_store()
+    for kappa in (0.0, 1.7):
+        out, cert, q = case.decode_now(3, kappa=kappa)
+        _check_decode(case, out, cert, q, kappa=kappa, cert_check=True)
+    for i in range(260):                 # crosses a block flush
+        out, cert, q = case.step(decode=(i % 100 == 99), kappa=2.0)
+        if out is not None:
+            _check_decode(case, out, cert, q, kappa=2.0, cert_check=True)
+    case.check_status()
+    case.check_state()
+    case.check_store()
+
+
+def test_append_refuses_full_residual_and_flags():
+    import torch
+    w = inputs.workload(2, B=1, Hq=1, Hkv=1, ctx=(256,))
+    case = _case(w, extra_tokens=64, poison=False)
+    k, v = inputs.step_kv(w, 0)
+    st0 = case.cache.state.clone()
+    case.cache.append(torch.from_numpy(k.view(np.float16)).cuda(),
+                      torch.from_numpy(v.view(np.float16)).cuda())
+    torch.cuda.synchronize()
+    assert int(case.cache.status[0].item()) & 1
+    assert torch.equal(case.cache.state, st0)
