@@ -1,0 +1,353 @@
+#!/usr/bin/env python3
+"""Quantized-KV decode attention benchmark on one MI355X.
+
+One step = kvq_flush_key_group -> kvq_append_token -> kvq_decode_attention for
+one attention layer of a whole decode batch (every request appends one token
+and attends once).  Inputs are seeded synthetic fp16 tensors shaped like the
+pages' workloads (bit_kv_cache_kivi_amd/inputs.py); the cache is prefilled
+and every step's q/k/v is resident in HBM before the timed region.
+
+Prints ONE JSON line: effective KV GB/s (algorithmic bytes of the step / step
+time) as `value`, with tokens/s, the stage-1 kernel's roofline (HIP events
+around it inside the timed steps) and the CPU oracle timed on a bounded
+sample of the same workload on the host cores.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 1..5]
+"""
+from __future__ import annotations
+
+import argparse
+import concurrent.futures as cf
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+from bit_kv_cache_kivi_amd import inputs  # noqa: E402
+
+METRIC = "quantized-KV decode attn: effective KV GB/s (% of HBM peak) + tokens/s, 1 GPU"
+HBM_PEAK_GBS = 8000.0
+PROFILES = os.path.join(ROOT, "profiles")
+KERNEL_SOURCES = ["bit_kv_cache_kivi_amd/csrc/kvq_decode.hip",
+                  "bit_kv_cache_kivi_amd/csrc/kvq_common.hpp"]
+
+
+def log(msg: str):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+# ---------------------------------------------------------------------------
+# algorithmic byte accounts (per (request, KV head) at decode time)
+# ---------------------------------------------------------------------------
+
+def kivi_bytes(l: int, n_kq: int, R: int, qpk: int, kitty: bool) -> dict:
+    n_vq = max(0, l - R)
+    kq = 52 if kitty else 48          # codes (+ Kitty high plane) + stats per token
+    stage1 = n_vq * (kq + 48)
+    window = (n_kq - n_vq) * kq + (l - n_kq) * 256 + (l - n_vq) * 256
+    qo = qpk * (256 + 512)
+    table = ((l + 63) // 64) * 4
+    return dict(stage1=stage1, decode=stage1 + window + qo + table)
+
+
+def witcert_bytes(l: int, n_q: int, qpk: int) -> dict:
+    stage1 = n_q * 258
+    window = (l - n_q) * 512
+    qo = qpk * (256 + 512 + 4)
+    table = ((l + 255) // 256) * 4
+    return dict(stage1=stage1, decode=stage1 + window + qo + table)
+
+
+def write_bytes(w: inputs.Workload, l_before: int, n_kq_before: int) -> int:
+    """Append (+ value pack) and flush-if-due bytes of one (request, KV head)."""
+    b = 512 + 512                      # new k, v in; fp16 windows out
+    if w.scheme == "witcert":
+        if l_before - n_kq_before == w.BLK:
+            b += 2 * w.BLK * 256 + 2 * (w.BLK * 128 + 256)
+        return b
+    if l_before >= w.R:
+        b += 256 + 48                  # value leaving the window, its codes + stats
+    if l_before - n_kq_before == w.R:
+        b += w.R * 256 + w.R * (52 if w.scheme == "kitty" else 48)
+    return b
+
+
+def state_after_prefill(w: inputs.Workload, l0: int):
+    W = w.BLK if w.scheme == "witcert" else w.R
+    r = ((l0 - 1) % W) + 1 if l0 else 0
+    return l0, l0 - r
+
+
+def step_state(w: inputs.Workload, l: int, n_kq: int):
+    W = w.BLK if w.scheme == "witcert" else w.R
+    if l - n_kq == W:
+        n_kq += W
+    return l + 1, n_kq
+
+
+def step_bytes(w: inputs.Workload, states):
+    """states: list over requests of (l, n_kq) before the step.  Returns
+    (total algorithmic bytes of the step, stage-1 bytes, new states)."""
+    tot = 0
+    s1 = 0
+    new = []
+    for (l, n_kq) in states:
+        wb = write_bytes(w, l, n_kq)
+        l2, k2 = step_state(w, l, n_kq)
+        if w.scheme == "witcert":
+            d = witcert_bytes(l2, k2, w.group)
+        else:
+            d = kivi_bytes(l2, k2, w.R, w.group, w.scheme == "kitty")
+        tot += w.Hkv * (wb + d["decode"])
+        s1 += w.Hkv * d["stage1"]
+        new.append((l2, k2))
+    return tot, s1, new
+
+
+# ---------------------------------------------------------------------------
+# GPU side
+# ---------------------------------------------------------------------------
+
+def gen_request(w: inputs.Workload, b: int):
+    K = np.stack([inputs.context_kv(w, b, h)[0] for h in range(w.Hkv)])
+    V = np.stack([inputs.context_kv(w, b, h)[1] for h in range(w.Hkv)])
+    return K, V
+
+
+def setup_gpu(w: inputs.Workload, extra: int, split_pages: int):
+    import torch
+    from bit_kv_cache_kivi_amd import kvq
+    from oracle import oracle as O  # noqa: F401  (only for the Kitty boost check below)
+    pt = 256 if w.scheme == "witcert" else 64
+    cap = max(w.ctx) + extra
+    max_pages = (cap + pt - 1) // pt
+    n_pages = w.B * max_pages
+    table = inputs.page_permutation(w, n_pages).reshape(w.B, max_pages)
+    layout = kvq.make_layout(w.scheme, w.B, w.Hq, w.Hkv, max_pages, n_pages, R=w.R,
+                             seed=0x5EED_0000_0000_0000 | w.seed, split_pages=split_pages)
+    cache = kvq.KVCache(layout, table)
+    if w.scheme == "kitty":
+        calib = np.stack([inputs.kitty_calibration(w, h) for h in range(w.Hkv)])
+        cache.kitty_calibrate(torch.from_numpy(calib.view(np.float16)).cuda())
+    threads = min(16, os.cpu_count() or 1)
+    t0 = time.time()
+    with cf.ThreadPoolExecutor(threads) as ex:
+        futs = {b: ex.submit(gen_request, w, b) for b in range(min(w.B, threads))}
+        nxt = len(futs)
+        for b in range(w.B):
+            K, V = futs.pop(b).result()
+            if nxt < w.B:
+                futs[nxt] = ex.submit(gen_request, w, nxt)
+                nxt += 1
+            Kt = torch.from_numpy(K.view(np.float16)).cuda(non_blocking=False)[None]
+            Vt = torch.from_numpy(V.view(np.float16)).cuda(non_blocking=False)[None]
+            lens = torch.tensor([w.ctx[b]], dtype=torch.int32, device="cuda")
+            cache.prefill(b, Kt.contiguous(), Vt.contiguous(), lens)
+    torch.cuda.synchronize()
+    if cache.status_word() != 0:
+        raise RuntimeError(f"prefill status {cache.status_word():#x}")
+    log(f"prefill of {w.B} requests x {w.Hkv} KV heads done in {time.time() - t0:.1f}s")
+    return cache
+
+
+def run_gpu(w: inputs.Workload, steps: int, warmup: int, split_pages: int):
+    import torch
+    from bit_kv_cache_kivi_amd import kvq
+    cache = setup_gpu(w, extra=steps + warmup + 8, split_pages=split_pages)
+    n = steps + warmup
+    # every step's inputs resident in HBM before timing
+    ks, vs, qs = [], [], []
+    for i in range(n):
+        k, v = inputs.step_kv(w, i)
+        ks.append(torch.from_numpy(k.view(np.float16)).cuda())
+        vs.append(torch.from_numpy(v.view(np.float16)).cuda())
+        qs.append(torch.from_numpy(inputs.step_q(w, i).view(np.float16)).cuda())
+    out = torch.empty((w.B, w.Hq, 128), dtype=torch.float32, device="cuda")
+    cert = torch.empty((w.B, w.Hq), dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream()
+    ev1 = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(steps)]
+    kappa = 1.0 if w.scheme == "witcert" else 0.0
+    for a, b in ev1:            # torch creates the HIP event at its first record
+        a.record()
+        b.record()
+    torch.cuda.synchronize()
+    assert all(a.cuda_event and b.cuda_event for a, b in ev1)
+
+    def one(i, evs=None):
+        if evs is not None:
+            kvq.kvq_set_stage1_events(cache.cache, evs[0].cuda_event, evs[1].cuda_event)
+        else:
+            kvq.kvq_set_stage1_events(cache.cache, None, None)
+        cache.flush()
+        cache.append(ks[i], vs[i])
+        cache.decode(qs[i], out, cert, sm_scale=w.sm_scale, kappa=kappa)
+
+    for i in range(warmup):
+        one(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for j in range(steps):
+        one(warmup + j, ev1[j])
+    torch.cuda.synchronize()
+    dt = time.perf_counter() - t0
+    kvq.kvq_set_stage1_events(cache.cache, None, None)
+    st = cache.status_word()
+    if st != 0:
+        raise RuntimeError(f"device status {st:#x}")
+    if not torch.isfinite(out).all():
+        raise RuntimeError("non-finite output")
+    s1_ms = [a.elapsed_time(b) for a, b in ev1]
+    del stream
+    return dt, s1_ms
+
+
+# ---------------------------------------------------------------------------
+# CPU oracle baseline (bounded sample of the same workload)
+# ---------------------------------------------------------------------------
+
+def cpu_baseline(w: inputs.Workload, warmup: int, target_s: float = 15.0):
+    from oracle import oracle as O
+    sid = {"kivi2": O.KIVI, "kitty": O.KITTY, "witcert": O.WITCERT}[w.scheme]
+    threads = max(1, min(16, len(os.sched_getaffinity(0))))
+    idx = None
+    if w.scheme == "kitty":
+        idx = [O.kitty_select(inputs.kitty_calibration(w, h), w.nb) for h in range(w.Hkv)]
+    pairs = [(b, b % w.Hkv) for b in range(w.B)]
+    seed = 0x5EED_0000_0000_0000 | w.seed
+
+    def make(pair):
+        b, h = pair
+        s = O.Stream(sid, w.ctx[b] + warmup + 210, G=w.G, R=w.R, VG=w.VG, BLK=w.BLK, nb=w.nb,
+                     idx=None if idx is None else idx[h], seed=seed, req=b, kvh=h)
+        K, V = inputs.context_kv(w, b, h)
+        s.prefill(K, V)
+        return s, b, h
+
+    def run(item, k, v, q):
+        s, b, h = item
+        s.flush()
+        s.append(k[b, h], v[b, h])
+        s.decode(q[b, h * w.group:(h + 1) * w.group], w.sm_scale,
+                 1.0 if w.scheme == "witcert" else 0.0)
+
+    # rounds of one flush/append/decode step on every sampled pair, until the
+    # timed work reaches about target_s (bounded by max_rounds)
+    max_rounds = 200
+    with cf.ThreadPoolExecutor(threads) as ex:
+        items = list(ex.map(make, pairs))
+        states = [state_after_prefill(w, w.ctx[b]) for (b, h) in pairs]
+        total_t = 0.0
+        done_bytes = 0
+        rounds = 0
+        while rounds < max_rounds and total_t < target_s:
+            k, v = inputs.step_kv(w, warmup + rounds)
+            q = inputs.step_q(w, warmup + rounds)
+            t0 = time.perf_counter()
+            list(ex.map(lambda it: run(it, k, v, q), items))
+            total_t += time.perf_counter() - t0
+            for i, (l, n_kq) in enumerate(states):
+                wb = write_bytes(w, l, n_kq)
+                l2, k2 = step_state(w, l, n_kq)
+                d = (witcert_bytes(l2, k2, w.group) if w.scheme == "witcert"
+                     else kivi_bytes(l2, k2, w.R, w.group, w.scheme == "kitty"))
+                done_bytes += wb + d["decode"]
+                states[i] = (l2, k2)
+            rounds += 1
+    done_pairs = len(pairs) * rounds
+    gbs = done_bytes / total_t / 1e9
+    return {"value": gbs, "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "sample": f"{len(pairs)} (request, KV head) pairs of the workload (one per request) "
+                      f"x {rounds} flush/append/decode steps ({done_bytes / 1e6:.1f} MB "
+                      f"algorithmic), {total_t:.1f}s on {threads} host threads",
+            "tokens_per_s_equiv": done_pairs / w.Hkv / total_t}
+
+
+# ---------------------------------------------------------------------------
+
+def source_sha() -> str:
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_entry(kernel: str, workload: str):
+    path = os.path.join(PROFILES, "traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        data = json.load(f)
+    e = data.get(f"{kernel}@{workload}")
+    if not e or e.get("source_sha") != source_sha():
+        return None
+    return e.get("bytes_per_launch")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", type=int, default=3)
+    ap.add_argument("--split-pages", type=int, default=0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(--gpus must be 1)", file=sys.stderr)
+        sys.exit(2)
+    w = inputs.workload(args.workload)
+    log(f"workload {w.name}: B={w.B} Hq={w.Hq} Hkv={w.Hkv} ctx mean "
+        f"{np.mean(w.ctx):.0f}, steps={args.steps} warmup={args.warmup}")
+    dt, s1_ms = run_gpu(w, args.steps, args.warmup, args.split_pages)
+
+    # algorithmic bytes of the timed steps
+    states = [state_after_prefill(w, l) for l in w.ctx]
+    for _ in range(args.warmup):
+        _, _, states = step_bytes(w, states)
+    tot = 0
+    s1_bytes = []
+    for _ in range(args.steps):
+        b, s1, states = step_bytes(w, states)
+        tot += b
+        s1_bytes.append(s1)
+    gbs = tot / dt / 1e9
+    ms_step = dt / args.steps * 1e3
+    s1_avg_ms = float(np.mean(s1_ms))
+    s1_gbs = float(np.mean(s1_bytes)) / (s1_avg_ms * 1e-3) / 1e9
+    kernel = "stage1_witcert" if w.scheme == "witcert" else "stage1_valu"
+    roof = {"kernel": kernel, "bound": "alu" if w.scheme == "witcert" else "hbm",
+            "achieved": round(s1_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(s1_gbs / HBM_PEAK_GBS, 4),
+            "traffic": traffic_entry(kernel, w.name),
+            "avg_launch_us": round(s1_avg_ms * 1e3, 2),
+            "algorithmic_bytes_per_launch": int(np.mean(s1_bytes))}
+    rec = {"metric": METRIC, "value": round(gbs, 1), "unit": "GB/s", "n_gpus": 1,
+           "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
+           "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+           "dtype": "u2+f32" if w.scheme != "witcert" else "i8+f32", "data": "synthetic",
+           "config": {"workload": w.name, "batch": w.B, "q_heads": w.Hq, "kv_heads": w.Hkv,
+                      "head_dim": w.D, "ctx_mean": float(np.mean(w.ctx)),
+                      "ctx_min": int(min(w.ctx)), "ctx_max": int(max(w.ctx)),
+                      "page_tokens": 256 if w.scheme == "witcert" else 64,
+                      "G": w.G, "R": w.R, "layers": 1},
+           "tokens_per_s": round(w.B / (ms_step * 1e-3), 1),
+           "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
+           "roofline": roof}
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle on a bounded sample ...")
+        rec["cpu_baseline"] = cpu_baseline(w, args.warmup, args.cpu_seconds)
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

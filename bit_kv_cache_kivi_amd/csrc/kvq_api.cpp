@@ -161,6 +161,8 @@ int kvq_decode_attention(const kvq_cache_t *cache, const uint16_t *q, float *out
     const size_t rows = (size_t)cache->layout.batch * cache->layout.n_q_heads * W.max_splits;
     W.o = (float *)workspace;
     W.ml = (float2 *)((char *)workspace + rows * kvq::D * sizeof(float));
+    W.ev_begin = cache->ev_stage1_begin;
+    W.ev_end = cache->ev_stage1_end;
     return kvq::launch_decode(params(cache), q, out, cert, sm_scale, kappa, W, stream) == hipSuccess
                ? KVQ_OK
                : KVQ_ELAUNCH;
@@ -190,6 +192,15 @@ int kvq_kitty_calibrate(const kvq_cache_t *cache, const uint16_t *calib, int32_t
     return kvq::launch_kitty_calibrate(params(cache), calib, n_tokens, idx_out, stream) == hipSuccess
                ? KVQ_OK
                : KVQ_ELAUNCH;
+}
+
+int kvq_set_stage1_events(kvq_cache_t *cache, hipEvent_t begin, hipEvent_t end) {
+    int rc = check_cache(cache);
+    if (rc != KVQ_OK) return rc;
+    if ((begin == nullptr) != (end == nullptr)) return KVQ_ENULL;
+    cache->ev_stage1_begin = begin;
+    cache->ev_stage1_end = end;
+    return KVQ_OK;
 }
 
 const char *kvq_strerror(int code) {

@@ -530,6 +530,10 @@ __global__ __launch_bounds__(256) void stage2_kernel(KParams P, const uint16_t *
 hipError_t launch_decode(const KParams &P, const uint16_t *q, float *out, float *cert,
                          float sm_scale, float kappa, const Workspace &W, hipStream_t s) {
     const float qscale = sm_scale * 1.4426950408889634f;
+    if (W.ev_begin) {
+        hipError_t e = hipEventRecord(W.ev_begin, s);
+        if (e != hipSuccess) return e;
+    }
     if (P.scheme == KVQ_SCHEME_WITCERT) {
         dim3 g1(W.max_splits, P.Hkv, P.B);
         switch (P.qpk) {
@@ -548,6 +552,10 @@ hipError_t launch_decode(const KParams &P, const uint16_t *q, float *out, float 
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
+    if (W.ev_end) {
+        e = hipEventRecord(W.ev_end, s);
+        if (e != hipSuccess) return e;
+    }
     stage2_kernel<<<dim3(P.Hkv, P.B), 256, 0, s>>>(P, q, out, cert, W, qscale);
     return hipGetLastError();
 }

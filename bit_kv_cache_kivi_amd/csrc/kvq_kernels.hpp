@@ -26,6 +26,7 @@ struct Workspace {
     float *o;        // [B][Hq][max_splits][128]
     float2 *ml;      // [B][Hq][max_splits]  (lse in log2 units, A)
     int max_splits;
+    hipEvent_t ev_begin, ev_end;   // optional stage-1 timing events
 };
 
 // write path (kvq_write.hip)

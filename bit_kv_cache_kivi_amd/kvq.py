@@ -28,7 +28,7 @@ STATUS_RESIDUAL_FULL, STATUS_CAPACITY, STATUS_UNMAPPED_PAGE, STATUS_BAD_LENGTH =
 EXPORTS = ("kvq_set_layout", "kvq_append_token", "kvq_flush_key_group",
            "kvq_decode_attention", "kvq_page_bytes", "kvq_page_tokens",
            "kvq_bytes_per_token", "kvq_workspace_bytes", "kvq_prefill",
-           "kvq_kitty_calibrate", "kvq_strerror")
+           "kvq_kitty_calibrate", "kvq_set_stage1_events", "kvq_strerror")
 
 
 class kvq_layout_t(C.Structure):
@@ -48,7 +48,8 @@ class kvq_buffers_t(C.Structure):
 class kvq_cache_t(C.Structure):
     _fields_ = [("layout", kvq_layout_t), ("bufs", kvq_buffers_t), ("page_tokens", C.c_int32),
                 ("split_pages", C.c_int32), ("page_bytes", C.c_int64), ("magic", C.c_int32),
-                ("reserved", C.c_int32)]
+                ("reserved", C.c_int32), ("ev_stage1_begin", C.c_void_p),
+                ("ev_stage1_end", C.c_void_p)]
 
 
 _lib = None
@@ -79,6 +80,7 @@ def lib():
         L.kvq_prefill.argtypes = [C.POINTER(kvq_cache_t), C.c_int32, C.c_int32, P, P,
                                   C.c_int64, P, S]
         L.kvq_kitty_calibrate.argtypes = [C.POINTER(kvq_cache_t), P, C.c_int32, P, S]
+        L.kvq_set_stage1_events.argtypes = [C.POINTER(kvq_cache_t), P, P]
         L.kvq_strerror.argtypes = [C.c_int]
         L.kvq_strerror.restype = C.c_char_p
         _lib = L
@@ -128,6 +130,10 @@ def kvq_kitty_calibrate(cache: kvq_cache_t, calib_ptr: int, n_tokens: int, idx_p
                         stream: int):
     _check(lib().kvq_kitty_calibrate(C.byref(cache), calib_ptr, n_tokens, idx_ptr, stream),
            "kvq_kitty_calibrate")
+
+
+def kvq_set_stage1_events(cache: kvq_cache_t, begin: int | None, end: int | None):
+    _check(lib().kvq_set_stage1_events(C.byref(cache), begin, end), "kvq_set_stage1_events")
 
 
 def kvq_workspace_bytes(cache: kvq_cache_t) -> int:

@@ -129,6 +129,8 @@ typedef struct kvq_cache {
     int64_t page_bytes;       /* bytes of one (page, KV head) block */
     int32_t magic;            /* set by kvq_set_layout */
     int32_t reserved;
+    hipEvent_t ev_stage1_begin; /* optional, see kvq_set_stage1_events */
+    hipEvent_t ev_stage1_end;
 } kvq_cache_t;
 
 /* Validate `layout` and `bufs` and fill `cache`.  Host only, synchronous, no
@@ -201,6 +203,11 @@ int kvq_prefill(const kvq_cache_t *cache, int32_t req0, int32_t n_req,
  * ("Kitty" summary: Selecting the Top-K Channels; The Boost Index Tensor). */
 int kvq_kitty_calibrate(const kvq_cache_t *cache, const uint16_t *calib,
                         int32_t n_tokens, uint8_t *idx_out, hipStream_t stream);
+
+/* Optional timing hook: when both events are non-NULL, kvq_decode_attention
+ * records `begin` on its stream right before the stage-1 kernel and `end`
+ * right after it (caller-owned events; NULL, NULL turns the hook off). */
+int kvq_set_stage1_events(kvq_cache_t *cache, hipEvent_t begin, hipEvent_t end);
 
 /* Static description of a return code or status bit set. */
 const char *kvq_strerror(int code);
