@@ -324,7 +324,8 @@ def main():
     ms_step = dt / args.steps * 1e3
     s1_avg_ms = float(np.mean(s1_ms))
     s1_gbs = float(np.mean(s1_bytes)) / (s1_avg_ms * 1e-3) / 1e9
-    kernel = "stage1_witcert" if w.scheme == "witcert" else "stage1_valu"
+    kernel = ("stage1_witcert" if w.scheme == "witcert" else
+              "stage1_gqa4_mfma" if (w.scheme == "kivi2" and w.group == 4) else "stage1_valu")
     roof = {"kernel": kernel, "bound": "alu" if w.scheme == "witcert" else "hbm",
             "achieved": round(s1_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(s1_gbs / HBM_PEAK_GBS, 4),

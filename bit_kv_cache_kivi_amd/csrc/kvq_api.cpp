@@ -21,7 +21,8 @@ int validate_layout(const kvq_layout_t *L) {
     if (qpk > 8) return KVQ_EINVAL;
     if (L->batch < 1 || L->batch > 65535) return KVQ_EINVAL;
     if (L->max_pages < 1 || L->n_pages < 1) return KVQ_EINVAL;
-    if (L->split_pages < 0) return KVQ_EINVAL;
+    if (L->split_pages < 0 || L->split_pages > 64) return KVQ_EINVAL;
+    if (L->flags & ~KVQ_FLAG_GENERIC_STAGE1) return KVQ_EINVAL;
     switch (L->scheme) {
         case KVQ_SCHEME_KIVI2:
         case KVQ_SCHEME_KITTY:
@@ -64,6 +65,7 @@ kvq::KParams params(const kvq_cache_t *C) {
     P.scheme = L.scheme;
     P.qpk = L.n_q_heads / L.n_kv_heads;
     P.split_pages = C->split_pages;
+    P.force_generic = (L.flags & KVQ_FLAG_GENERIC_STAGE1) ? 1 : 0;
     P.layer = L.layer;
     P.seed = L.seed;
     return P;

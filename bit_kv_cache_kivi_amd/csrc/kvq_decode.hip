@@ -267,6 +267,351 @@ __global__ __launch_bounds__(64) void stage1_valu_kernel(KParams P, const uint16
 }
 
 // ---------------------------------------------------------------------------
+// Stage 1, KIVI2, GQA group of 4 query heads per KV head, on the matrix cores.
+// One wave per (split, KV head, request) streams each page once for all four
+// query heads.
+//
+// Scores, C[m][t] = sum_c A[m][c] code_{t,c} with 16x16x32 f16 products:
+//   rows m = 0..3 hold hi(q_h s_c), rows 4..7 lo(q_h s_c) = f16 remainder
+//   (hi + lo carries the binary32 product to within 2^-22), rows 8..15 zero;
+//   B is the page's key codes, exact in f16 (2-bit code c in a nibble is the
+//   fp4 value c/2, scaled by 2 on conversion).  The accumulator starts at
+//   sum_c q_h z_c; rows h and h+4 are added afterwards.
+// P.V, transposed: O^T[c][(h,j)] = sum_t code_{t,c} (p_{h,t} s_{t,j}), A =
+//   value codes (channel rows, token columns), B columns = (query h, value
+//   group j): all 16 columns carry data; hi and lo parts of p s are two
+//   products into one accumulator; column (h, j) is kept for channels of
+//   group j.  sum_t p_{h,t} z_{t,j} is accumulated on the side.
+// Online softmax with lazy rescaling: the running maximum m moves only when a
+// score exceeds m + 8 (log2 units), so p <= 256 and the rescale is rare; the
+// split's lse = m + log2(l) stays exact.
+// ---------------------------------------------------------------------------
+typedef _Float16 h8v __attribute__((ext_vector_type(8)));
+typedef _Float16 h2v __attribute__((ext_vector_type(2)));
+typedef float f4v __attribute__((ext_vector_type(4)));
+
+__device__ inline h2v cvth(uint32_t x, int sel) {
+    switch (sel) {
+        case 0: return __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(x, 2.0f, 0);
+        case 1: return __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(x, 2.0f, 1);
+        case 2: return __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(x, 2.0f, 2);
+        default: return __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(x, 2.0f, 3);
+    }
+}
+
+// eight codes held in the nibbles of a masked dword -> f16 fragment (k = nibble)
+__device__ inline h8v frag8(uint32_t m) {
+    const h2v a = cvth(m, 0), b = cvth(m, 1), c = cvth(m, 2), d = cvth(m, 3);
+    return h8v{a.x, a.y, b.x, b.y, c.x, c.y, d.x, d.y};
+}
+
+__device__ inline float lo16f(uint32_t v) { return h2f((uint16_t)(v & 0xffffu)); }
+__device__ inline float hi16f(uint32_t v) { return h2f((uint16_t)(v >> 16)); }
+
+constexpr float LAZY_TAU = 8.0f;
+
+// a = fl32(x * y) for two pairs, each split into f16 hi + lo with hi + lo = a
+// to within half an ulp of lo.  hi is cut by round-toward-zero in one opaque
+// packed conversion, and lo is the exact binary32 remainder a - hi rounded to
+// f16, so both parts come from the same rounded a whatever the compiler does
+// with the product (a remainder formed by an FMA against a separately rounded
+// hi can miss by one f16 ulp of hi).
+__device__ inline void mul_split2(float x0, float y0, float x1, float y1, h2v &hi, h2v &lo) {
+#pragma clang fp contract(off)
+    const float a0 = x0 * y0;
+    const float a1 = x1 * y1;
+    const h2v h = __builtin_bit_cast(h2v, __builtin_amdgcn_cvt_pkrtz(a0, a1));
+    hi = h;
+    lo = h2v{(_Float16)(a0 - (float)h.x), (_Float16)(a1 - (float)h.y)};
+}
+
+struct PageRegs {
+    uint4 ka, kb, va, vb, ks, vs;
+};
+
+__device__ inline PageRegs load_page(const uint8_t *page, const Geom &G, int lane) {
+    PageRegs R;
+    R.ka = ((const uint4 *)(page + G.kc))[lane];
+    R.kb = ((const uint4 *)(page + G.kc))[64 + lane];
+    R.va = ((const uint4 *)(page + G.vc))[lane];
+    R.vb = ((const uint4 *)(page + G.vc))[64 + lane];
+    R.ks = ((const uint4 *)(page + G.ks))[lane];
+    R.vs = ((const uint4 *)(page + G.vs))[lane];
+    return R;
+}
+
+// sum over the 16 lanes of a row; the total lands in the row's lane 15
+__device__ inline float row_sum16(float v) {
+    v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0u, __builtin_bit_cast(uint32_t, v), 0x111, 0xf, 0xf, true));
+    v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0u, __builtin_bit_cast(uint32_t, v), 0x112, 0xf, 0xf, true));
+    v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0u, __builtin_bit_cast(uint32_t, v), 0x114, 0xf, 0xf, true));
+    v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0u, __builtin_bit_cast(uint32_t, v), 0x118, 0xf, 0xf, true));
+    return v;
+}
+
+struct Gqa4State {
+    float m[4];
+    float lsum[4];
+    float zacc;
+    f4v acc[8];
+};
+
+struct Gqa4Smem {
+    f4v zsh[PT];            // scores [token][query]
+    float psh[4][PT];       // p [query][token]
+    uint32_t vsT[4][PT];    // value {s, z} [group][token]
+    uint32_t kss[256];      // key {s, z} [group][slot]
+    h8v As[2][9][16];       // score A: [key group][row 0..7, 8 = zero][channel octet]
+};
+
+// One 64-token page.  nvalid < 64 only on the last page of the prefix.
+template <bool MASK>
+__device__ inline void gqa4_page(const PageRegs &R, Gqa4State &S, Gqa4Smem &sm, const float *qc,
+                                 int slot0, int lane, int nvalid, float qscale) {
+    const int g = lane >> 4, r = lane & 15;
+    const int hq = g, c8 = r;
+    const int hp = r >> 2, jp = r & 3;
+    const uint32_t MSK = 0x33333333u;
+
+    __syncthreads();                            // previous page done with the LDS
+    ((uint4 *)sm.kss)[lane] = R.ks;
+    sm.vsT[0][lane] = R.vs.x;
+    sm.vsT[1][lane] = R.vs.y;
+    sm.vsT[2][lane] = R.vs.z;
+    sm.vsT[3][lane] = R.vs.w;
+    __syncthreads();
+
+    // ---- score operand: hi/lo of q_h * s_c, zero-point bias ----
+    float bq[2][4];
+#pragma unroll
+    for (int gi = 0; gi < 2; gi++) {
+        const uint4 s0 = *(const uint4 *)&sm.kss[128 * gi + slot0];
+        const uint4 s1 = *(const uint4 *)&sm.kss[128 * gi + slot0 + 4];
+        const uint32_t sz[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
+        h8v hi, lo;
+        float bias = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; e += 2) {
+            h2v hh, ll;
+            mul_split2(qc[e], lo16f(sz[e]), qc[e + 1], lo16f(sz[e + 1]), hh, ll);
+            hi[e] = hh.x; hi[e + 1] = hh.y;
+            lo[e] = ll.x; lo[e + 1] = ll.y;
+            bias = fmaf(qc[e], hi16f(sz[e]), bias);
+            bias = fmaf(qc[e + 1], hi16f(sz[e + 1]), bias);
+        }
+        sm.As[gi][hq][c8] = hi;
+        sm.As[gi][4 + hq][c8] = lo;
+        bias = row_sum16(bias);
+#pragma unroll
+        for (int i = 0; i < 4; i++)
+            bq[gi][i] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, bias), 16 * i + 15));
+    }
+    __syncthreads();
+
+    // ---- scores on the matrix cores ----
+    const uint32_t kd[8] = {R.ka.x, R.ka.y, R.ka.z, R.ka.w, R.kb.x, R.kb.y, R.kb.z, R.kb.w};
+    f4v sc[4];
+#pragma unroll
+    for (int gi = 0; gi < 2; gi++) {
+        const f4v init = lane < 16 ? f4v{bq[gi][0], bq[gi][1], bq[gi][2], bq[gi][3]}
+                                   : f4v{0.f, 0.f, 0.f, 0.f};
+        sc[2 * gi] = init;
+        sc[2 * gi + 1] = init;
+#pragma unroll
+        for (int kc = 0; kc < 4; kc++) {
+            const h8v af = sm.As[gi][r < 8 ? r : 8][r < 8 ? 4 * kc + g : 0];
+#pragma unroll
+            for (int nn = 0; nn < 2; nn++) {
+                const int n = 2 * gi + nn;
+                const uint32_t x = kd[2 * n + (kc >> 1)];
+                const uint32_t mx = (kc & 1) ? ((x >> 2) & MSK) : (x & MSK);
+                sc[n] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af, frag8(mx), sc[n], 0, 0, 0);
+            }
+        }
+    }
+    // rows h (lanes 0..15) + rows h+4 (lanes 16..31)
+#pragma unroll
+    for (int n = 0; n < 4; n++)
+#pragma unroll
+        for (int i = 0; i < 4; i++) sc[n][i] += shfl_xor(sc[n][i], 16);
+    if (lane < 16) {
+#pragma unroll
+        for (int n = 0; n < 4; n++) sm.zsh[16 * n + r] = sc[n];
+    }
+    __syncthreads();
+
+    // ---- online softmax, lane = token ----
+    const f4v z = sm.zsh[lane] * qscale;       // log2 units
+    float zz[4] = {z[0], z[1], z[2], z[3]};
+    bool exceed = false;
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+        if (MASK && lane >= nvalid) zz[i] = -INFINITY;
+        exceed |= zz[i] > S.m[i] + LAZY_TAU;
+    }
+    if (__any(exceed)) {
+        float alpha[4];
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+            float mt = zz[i];
+#pragma unroll
+            for (int msk = 1; msk < 64; msk <<= 1) mt = fmaxf(mt, shfl_xor(mt, msk));
+            const float mn = fmaxf(S.m[i], mt);
+            alpha[i] = __builtin_amdgcn_exp2f(S.m[i] - mn);
+            S.m[i] = mn;
+            S.lsum[i] *= alpha[i];
+        }
+        const float ap = hp == 0 ? alpha[0] : hp == 1 ? alpha[1] : hp == 2 ? alpha[2] : alpha[3];
+        S.zacc *= ap;
+#pragma unroll
+        for (int nt = 0; nt < 8; nt++) S.acc[nt] *= ap;
+    }
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+        const float pv = __builtin_amdgcn_exp2f(zz[i] - S.m[i]);
+        S.lsum[i] += pv;
+        sm.psh[i][lane] = pv;
+    }
+    __syncthreads();
+
+    // ---- P.V on the matrix cores ----
+    const uint32_t vd[8] = {R.va.x, R.va.y, R.va.z, R.va.w, R.vb.x, R.vb.y, R.vb.z, R.vb.w};
+#pragma unroll
+    for (int ks = 0; ks < 2; ks++) {
+        const int t0 = 32 * ks + 8 * g;
+        const float4 pa = *(const float4 *)&sm.psh[hp][t0];
+        const float4 pb = *(const float4 *)&sm.psh[hp][t0 + 4];
+        const uint4 za = *(const uint4 *)&sm.vsT[jp][t0];
+        const uint4 zb = *(const uint4 *)&sm.vsT[jp][t0 + 4];
+        const float pe[8] = {pa.x, pa.y, pa.z, pa.w, pb.x, pb.y, pb.z, pb.w};
+        const uint32_t se[8] = {za.x, za.y, za.z, za.w, zb.x, zb.y, zb.z, zb.w};
+        h8v bhi, blo;
+        float pv[8], sv[8];
+#pragma unroll
+        for (int e = 0; e < 8; e++) {
+            pv[e] = pe[e];
+            sv[e] = lo16f(se[e]);
+            float zv = hi16f(se[e]);
+            if (MASK) {
+                const bool tv = t0 + e < nvalid;     // statistics past nvalid are not written yet
+                pv[e] = tv ? pv[e] : 0.f;
+                sv[e] = tv ? sv[e] : 0.f;
+                zv = tv ? zv : 0.f;
+            }
+            S.zacc = fmaf(pv[e], zv, S.zacc);
+        }
+#pragma unroll
+        for (int e = 0; e < 8; e += 2) {
+            h2v hh, ll;
+            mul_split2(pv[e], sv[e], pv[e + 1], sv[e + 1], hh, ll);
+            bhi[e] = hh.x; bhi[e + 1] = hh.y;
+            blo[e] = ll.x; blo[e + 1] = ll.y;
+        }
+#pragma unroll
+        for (int nt = 0; nt < 8; nt++) {
+            const uint32_t x = vd[nt];
+            const h8v af = frag8(ks ? ((x >> 2) & MSK) : (x & MSK));
+            S.acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af, bhi, S.acc[nt], 0, 0, 0);
+            S.acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af, blo, S.acc[nt], 0, 0, 0);
+        }
+    }
+}
+
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 8))) void stage1_gqa4_mfma_kernel(KParams P, const uint16_t *__restrict__ q,
+                                                              Workspace W, float qscale) {
+    const int s = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+    const int lane = threadIdx.x, g = lane >> 4, r = lane & 15;
+    const Geom G = geom(P.scheme);
+    const size_t bh = (size_t)b * P.Hkv + h;
+    const int l = P.state[bh * 4];
+    const int nvq = l > P.R ? l - P.R : 0;
+    const int npages = (nvq + PT - 1) / PT;
+    const int p0 = s * P.split_pages;
+    const int p1 = min(p0 + P.split_pages, npages);
+    if (p0 >= p1) return;
+    const int np = p1 - p0;                      // <= split_pages <= 64
+
+    __shared__ Gqa4Smem sm;
+
+    // page ids of this split, one per lane
+    int pid_l = lane < np ? P.table[(size_t)b * P.max_pages + p0 + lane] : 0;
+    const bool bad = lane < np && (pid_l < 0 || pid_l >= P.n_pages);
+    if (__any(bad)) {
+        if (lane == 0) atomicOr(P.status, (uint32_t)KVQ_STATUS_UNMAPPED_PAGE);
+        pid_l = bad ? 0 : pid_l;                 // read page 0 instead; the result is flagged
+    }
+
+    // query for this lane's score-operand role (unscaled: keeps q s in the
+    // range where the f16 remainder is a normal number)
+    const int hq = g, c8 = r;
+    float qc[8];
+    {
+        const uint4 raw = *(const uint4 *)(q + ((size_t)b * P.Hq + (size_t)h * 4 + hq) * D + 8 * c8);
+        const uint32_t w4[4] = {raw.x, raw.y, raw.z, raw.w};
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+            qc[2 * i] = lo16f(w4[i]);
+            qc[2 * i + 1] = hi16f(w4[i]);
+        }
+    }
+    const int slot0 = 32 * (c8 & 3) + 8 * (c8 >> 2);      // key_stat_slot(8 * c8)
+    if (lane < 16) {
+        sm.As[0][8][lane] = h8v{0, 0, 0, 0, 0, 0, 0, 0};
+        sm.As[1][8][lane] = h8v{0, 0, 0, 0, 0, 0, 0, 0};
+    }
+
+    Gqa4State S;
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+        S.m[i] = -INFINITY;
+        S.lsum[i] = 0.f;
+    }
+    S.zacc = 0.f;
+#pragma unroll
+    for (int nt = 0; nt < 8; nt++) S.acc[nt] = f4v{0.f, 0.f, 0.f, 0.f};
+
+    const uint8_t *base = P.pool + (size_t)h * P.page_bytes;
+    const size_t pstride = (size_t)P.Hkv * P.page_bytes;
+    PageRegs cur = load_page(base + (size_t)__builtin_amdgcn_readlane(pid_l, 0) * pstride, G, lane);
+    for (int i = 0; i < np; i++) {
+        PageRegs nxt;
+        if (i + 1 < np)                          // prefetch the next page
+            nxt = load_page(base + (size_t)__builtin_amdgcn_readlane(pid_l, i + 1) * pstride, G, lane);
+        const int nvalid = nvq - (p0 + i) * PT;
+        if (nvalid >= PT)
+            gqa4_page<false>(cur, S, sm, qc, slot0, lane, PT, qscale);
+        else
+            gqa4_page<true>(cur, S, sm, qc, slot0, lane, nvalid, qscale);
+        if (i + 1 < np) cur = nxt;
+    }
+
+    // ---- reduce and write the split's partial ----
+    const int hp = r >> 2, jp = r & 3;
+#pragma unroll
+    for (int i = 0; i < 4; i++)
+#pragma unroll
+        for (int msk = 1; msk < 64; msk <<= 1) S.lsum[i] += shfl_xor(S.lsum[i], msk);
+    S.zacc += shfl_xor(S.zacc, 16);
+    S.zacc += shfl_xor(S.zacc, 32);
+    const float lh = hp == 0 ? S.lsum[0] : hp == 1 ? S.lsum[1] : hp == 2 ? S.lsum[2] : S.lsum[3];
+    const float il = 1.0f / lh;
+    const size_t row = ((size_t)b * P.Hq + (size_t)h * 4 + hp) * W.max_splits + s;
+#pragma unroll
+    for (int nt = 0; nt < 8; nt++) {
+        if (jp == (nt >> 1)) {
+            const f4v o = (S.acc[nt] + S.zacc) * il;
+            *(float4 *)(W.o + row * D + 16 * nt + 4 * g) = make_float4(o[0], o[1], o[2], o[3]);
+        }
+    }
+    if (lane < 4) {
+        const float li = lane == 0 ? S.lsum[0] : lane == 1 ? S.lsum[1] : lane == 2 ? S.lsum[2] : S.lsum[3];
+        const float mi = lane == 0 ? S.m[0] : lane == 1 ? S.m[1] : lane == 2 ? S.m[2] : S.m[3];
+        const size_t row_i = ((size_t)b * P.Hq + (size_t)h * 4 + lane) * W.max_splits + s;
+        W.ml[row_i] = make_float2(mi + log2f(li), 1.0f);
+    }
+}
+
+// ---------------------------------------------------------------------------
 // Stage 1, WITCERT: INT8 codes with the Philox dither regenerated in the
 // kernel, and the certificate accumulated next to the output.  One wave per
 // (split, KV head, request) serves all QPK query heads of the KV head, so each
@@ -543,6 +888,9 @@ hipError_t launch_decode(const KParams &P, const uint16_t *q, float *out, float 
             case 8: stage1_witcert_kernel<8><<<g1, 64, 0, s>>>(P, q, W, qscale, sm_scale, kappa); break;
             default: return hipErrorInvalidValue;
         }
+    } else if (P.scheme == KVQ_SCHEME_KIVI2 && P.qpk == 4 && !P.force_generic) {
+        dim3 g1(W.max_splits, P.Hkv, P.B);
+        stage1_gqa4_mfma_kernel<<<g1, 64, 0, s>>>(P, q, W, qscale);
     } else {
         dim3 g1(W.max_splits, P.Hq, P.B);
         if (P.scheme == KVQ_SCHEME_KITTY)

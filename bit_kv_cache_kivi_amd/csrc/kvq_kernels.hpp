@@ -16,6 +16,7 @@ struct KParams {
     const uint8_t *boost_idx;
     uint32_t *status;
     int B, Hq, Hkv, R, max_pages, n_pages, page_bytes, scheme, qpk, split_pages;
+    int force_generic;            // 1: use the per-query-head VALU stage 1
     uint32_t layer;
     uint64_t seed;
 };

@@ -24,6 +24,7 @@ SCHEMES = {"kivi2": KVQ_SCHEME_KIVI2, "kitty": KVQ_SCHEME_KITTY, "witcert": KVQ_
 KVQ_OK, KVQ_EINVAL, KVQ_ENULL, KVQ_EALIGN, KVQ_ENOLAYOUT, KVQ_EWORKSPACE, KVQ_ELAUNCH = \
     0, -1, -2, -3, -4, -5, -6
 STATUS_RESIDUAL_FULL, STATUS_CAPACITY, STATUS_UNMAPPED_PAGE, STATUS_BAD_LENGTH = 1, 2, 4, 8
+FLAG_GENERIC_STAGE1 = 1
 
 EXPORTS = ("kvq_set_layout", "kvq_append_token", "kvq_flush_key_group",
            "kvq_decode_attention", "kvq_page_bytes", "kvq_page_tokens",
@@ -36,7 +37,8 @@ class kvq_layout_t(C.Structure):
                 ("n_kv_heads", C.c_int32), ("batch", C.c_int32), ("group", C.c_int32),
                 ("value_group", C.c_int32), ("residual", C.c_int32), ("block", C.c_int32),
                 ("n_boost", C.c_int32), ("max_pages", C.c_int32), ("n_pages", C.c_int32),
-                ("split_pages", C.c_int32), ("layer", C.c_uint32), ("seed", C.c_uint64)]
+                ("split_pages", C.c_int32), ("flags", C.c_int32), ("layer", C.c_uint32),
+                ("seed", C.c_uint64)]
 
 
 class kvq_buffers_t(C.Structure):
@@ -142,13 +144,13 @@ def kvq_workspace_bytes(cache: kvq_cache_t) -> int:
 
 def make_layout(scheme: str, B: int, Hq: int, Hkv: int, max_pages: int, n_pages: int,
                 R: int = 128, seed: int = 0, layer: int = 0, split_pages: int = 0,
-                nb: int | None = None) -> kvq_layout_t:
+                nb: int | None = None, flags: int = 0) -> kvq_layout_t:
     s = SCHEMES[scheme]
     return kvq_layout_t(scheme=s, head_dim=128, n_q_heads=Hq, n_kv_heads=Hkv, batch=B, group=32,
                         value_group=32, residual=R, block=256,
                         n_boost=(16 if s == KVQ_SCHEME_KITTY else 0) if nb is None else nb,
                         max_pages=max_pages, n_pages=n_pages, split_pages=split_pages,
-                        layer=layer, seed=seed)
+                        flags=flags, layer=layer, seed=seed)
 
 
 def page_bytes(layout: kvq_layout_t) -> int:

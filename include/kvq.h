@@ -62,6 +62,12 @@ enum {
     KVQ_SCHEME_WITCERT = 2
 };
 
+/* layout flags */
+enum {
+    KVQ_FLAG_GENERIC_STAGE1 = 1  /* run the per-query-head VALU stage 1 even where
+                                    a matrix-core stage 1 exists (comparison) */
+};
+
 /* host-side return codes */
 enum {
     KVQ_OK = 0,
@@ -98,6 +104,7 @@ typedef struct kvq_layout {
     int32_t max_pages;       /* page-table row length per request */
     int32_t n_pages;         /* pages in the pool */
     int32_t split_pages;     /* stage-1 split size in pages (0: default) */
+    int32_t flags;           /* KVQ_FLAG_* */
     uint32_t layer;          /* WITCERT dither counter field; < 65536 */
     uint64_t seed;           /* WITCERT dither key */
 } kvq_layout_t;

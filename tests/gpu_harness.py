@@ -14,7 +14,7 @@ class Case:
     """One workload on the GPU plus its oracle streams."""
 
     def __init__(self, w: inputs.Workload, extra_tokens: int = 0, split_pages: int = 0,
-                 poison: bool = True, sample=None):
+                 poison: bool = True, sample=None, flags: int = 0):
         import torch
         from bit_kv_cache_kivi_amd import kvq
         from oracle import oracle as O
@@ -35,7 +35,7 @@ class Case:
             self.idx = np.stack([O.kitty_select(inputs.kitty_calibration(w, h), w.nb)
                                  for h in range(w.Hkv)])
         layout = kvq.make_layout(w.scheme, w.B, w.Hq, w.Hkv, self.max_pages, self.n_pages,
-                                 R=w.R, seed=self.seed, split_pages=split_pages)
+                                 R=w.R, seed=self.seed, split_pages=split_pages, flags=flags)
         self.cache = kvq.KVCache(layout, self.table, poison=poison)
         if w.scheme == "kitty":
             calib = np.stack([inputs.kitty_calibration(w, h) for h in range(w.Hkv)])

@@ -50,10 +50,11 @@ def _check_decode(case, out, cert, q, kappa=0.0, cert_check=False):
     return worst
 
 
-@pytest.mark.parametrize("Hq,Hkv", [(2, 2), (8, 2)])
-def test_kivi_prefill_decode_small(Hq, Hkv):
+@pytest.mark.parametrize("Hq,Hkv,flags", [(2, 2, 0), (8, 2, 0), (8, 2, 1), (16, 4, 0)])
+def test_kivi_prefill_decode_small(Hq, Hkv, flags):
+    # (8, 2, 0): matrix-core GQA stage 1; (8, 2, 1): the generic VALU stage 1
     w = inputs.workload(3, B=3, Hq=Hq, Hkv=Hkv, ctx=(700, 1301, 2113), steps=3)
-    case = _case(w, extra_tokens=300, split_pages=4)
+    case = _case(w, extra_tokens=300, split_pages=4, flags=flags)
     case.check_status()
     case.check_state()
     case.check_store()
@@ -61,8 +62,9 @@ def test_kivi_prefill_decode_small(Hq, Hkv):
     _check_decode(case, out, cert, q)
 
 
-def test_kivi_streaming_crosses_flush_and_pages():
-    w = inputs.workload(2, B=2, Hq=4, Hkv=4, ctx=(250, 383))
+@pytest.mark.parametrize("Hq,Hkv", [(4, 4), (8, 2)])
+def test_kivi_streaming_crosses_flush_and_pages(Hq, Hkv):
+    w = inputs.workload(2, B=2, Hq=Hq, Hkv=Hkv, ctx=(250, 383))
     case = _case(w, extra_tokens=300, split_pages=2)
     for i in range(140):                 # crosses a flush on both requests
         out, cert, q = case.step(decode=(i % 35 == 34 or i in (0, 1, 127, 128, 129)))
@@ -83,7 +85,7 @@ def test_workload1_exact_config():
     print(f"workload 1 max|do| = {err:.3e}")
 
 
-@pytest.mark.parametrize("ctx", [(1,), (64,), (128,), (129,), (191,), (192,), (257,)])
+@pytest.mark.parametrize("ctx", [(1,), (64,), (128,), (129,), (191,), (192,), (257,), (1000,)])
 def test_kivi_short_contexts(ctx):
     w = inputs.workload(2, B=1, Hq=4, Hkv=1, ctx=ctx)
     case = _case(w, extra_tokens=200, split_pages=1)
