@@ -120,7 +120,10 @@ int kvq_set_layout(kvq_cache_t *cache, const kvq_layout_t *layout, const kvq_buf
     cache->page_tokens = G.tokens;
     cache->page_bytes = G.bytes;
     int sp = layout->split_pages;
-    if (sp == 0) sp = layout->scheme == KVQ_SCHEME_WITCERT ? 1 : 16;
+    if (sp == 0) sp = layout->scheme == KVQ_SCHEME_WITCERT ? 1 : 8;
+    // stage 2 merges at most 256 splits per query head
+    while ((layout->max_pages + sp - 1) / sp > 256) sp *= 2;
+    if (sp > 64) return KVQ_EINVAL;
     cache->split_pages = sp;
     cache->magic = MAGIC;
     return KVQ_OK;

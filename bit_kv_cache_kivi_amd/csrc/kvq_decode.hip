@@ -752,6 +752,7 @@ __global__ __launch_bounds__(64) void stage1_witcert_kernel(KParams P, const uin
 // ---------------------------------------------------------------------------
 constexpr int S2_MAXQ = 8;
 constexpr int S2_MAXW = 256;
+constexpr int S2_MAXSPLIT = 256;
 
 __device__ inline float key_tilde_page(const KParams &P, const Geom &G, const uint8_t *page,
                                        int tp, int c, int h) {
@@ -771,6 +772,8 @@ __device__ inline float key_tilde_page(const KParams &P, const Geom &G, const ui
     return cs + h2f((uint16_t)(sz >> 16));
 }
 
+constexpr int S2_CH = 64;      // window tokens staged per chunk
+
 __global__ __launch_bounds__(256) void stage2_kernel(KParams P, const uint16_t *__restrict__ q,
                                                     float *__restrict__ out, float *__restrict__ cert,
                                                     Workspace W, float qscale) {
@@ -788,86 +791,194 @@ __global__ __launch_bounds__(256) void stage2_kernel(KParams P, const uint16_t *
     const int nsplit = (npages + P.split_pages - 1) / P.split_pages;
 
     __shared__ float qs[S2_MAXQ][D];
-    __shared__ float sc[S2_MAXQ][S2_MAXW];
-    __shared__ float mr[S2_MAXQ], lr[S2_MAXQ];
+    __shared__ float kt[S2_CH][D + 1];      // padded: row reads by different lanes hit different banks
+    __shared__ uint16_t vt[S2_CH][D];
+    __shared__ float ps[S2_MAXQ][S2_CH];
+    __shared__ float run_m[S2_MAXQ], run_l[S2_MAXQ], run_a[S2_MAXQ];
+    __shared__ int wpid[8];                 // pages of the 2-bit-key part of the window
+    const int wp0 = W0 / PT;
+    if (tid < 8) {
+        int pid = -1;
+        if (!wit && (wp0 + tid) * PT < nkq) {
+            pid = P.table[(size_t)b * P.max_pages + wp0 + tid];
+            if (pid < 0 || pid >= P.n_pages) {
+                atomicOr(P.status, (uint32_t)KVQ_STATUS_UNMAPPED_PAGE);
+                pid = 0;                         // read page 0 instead; the result is flagged
+            }
+        }
+        wpid[tid] = pid;
+    }
     for (int i = tid; i < QPK * D; i += 256)
         qs[i / D][i % D] = h2f(q[((size_t)b * P.Hq + (size_t)h * QPK + i / D) * D + i % D]);
+    if (tid < S2_MAXQ) {
+        run_m[tid] = -INFINITY;
+        run_l[tid] = 0.f;
+        run_a[tid] = 0.f;
+    }
+    float acc[S2_MAXQ * D / 256];           // this thread's (query, channel) window outputs
+#pragma unroll
+    for (int k = 0; k < S2_MAXQ * D / 256; k++) acc[k] = 0.f;
     __syncthreads();
 
-    // scores of the window: one wave per token, lane = channels 2L, 2L+1
-    for (int i = wave; i < nr; i += 4) {
-        const int t = W0 + i;
-        float k0, k1;
-        if (!wit && t < nkq) {
-            const int pid = P.table[(size_t)b * P.max_pages + t / PT];
-            if (pid < 0 || pid >= P.n_pages) {
-                if (lane == 0) atomicOr(P.status, (uint32_t)KVQ_STATUS_UNMAPPED_PAGE);
-                k0 = k1 = 0.f;
-            } else {
-                const uint8_t *page = cpage(P, pid, h);
-                k0 = key_tilde_page(P, G, page, t % PT, 2 * lane, h);
-                k1 = key_tilde_page(P, G, page, t % PT, 2 * lane + 1, h);
+    for (int c0 = 0; c0 < nr; c0 += S2_CH) {
+        const int n = min(S2_CH, nr - c0);
+        // stage values (fp16 rows, 16 B per load) and keys (binary32; dequantized
+        // where still 2-bit) of the chunk
+#pragma unroll
+        for (int k = 0; k < S2_CH * D / 8 / 256; k++) {
+            const int i = tid + 256 * k;
+            const int tt = i / (D / 8), c8 = i % (D / 8);
+            if (tt < n) {
+                const int t = W0 + c0 + tt;
+                const size_t vslot = wit ? (size_t)(t - nkq) : (size_t)(t % P.R);
+                *(uint4 *)&vt[tt][8 * c8] = *(const uint4 *)&P.res_v[(bh * win + vslot) * D + 8 * c8];
+                if (wit || t >= nkq) {
+                    const uint4 kr = *(const uint4 *)&P.res_k[(bh * win + (size_t)(t - nkq)) * D + 8 * c8];
+                    const uint32_t kw[4] = {kr.x, kr.y, kr.z, kr.w};
+#pragma unroll
+                    for (int e = 0; e < 4; e++) {
+                        kt[tt][8 * c8 + 2 * e] = lo16f(kw[e]);
+                        kt[tt][8 * c8 + 2 * e + 1] = hi16f(kw[e]);
+                    }
+                } else {
+                    const uint8_t *page = cpage(P, wpid[t / PT - wp0], h);
+#pragma unroll
+                    for (int e = 0; e < 8; e++)
+                        kt[tt][8 * c8 + e] = key_tilde_page(P, G, page, t % PT, 8 * c8 + e, h);
+                }
             }
-        } else {
-            const uint32_t kk = ((const uint32_t *)P.res_k)[(bh * win + (size_t)(t - nkq)) * (D / 2) + lane];
-            k0 = h2f((uint16_t)(kk & 0xffff));
-            k1 = h2f((uint16_t)(kk >> 16));
         }
-        for (int hh = 0; hh < QPK; hh++) {
-            float part = fmaf(qs[hh][2 * lane + 1], k1, qs[hh][2 * lane] * k0);
+        __syncthreads();
+        // scores, thread = (query, token); a wave shares one query
+        for (int i = tid; i < QPK * S2_CH; i += 256) {
+            const int hh = i / S2_CH, tt = i % S2_CH;
+            if (tt < n) {
+                float dot = 0.f;
+#pragma unroll 16
+                for (int c = 0; c < D; c++) dot = fmaf(qs[hh][c], kt[tt][c], dot);
+                ps[hh][tt] = dot * qscale;
+            }
+        }
+        __syncthreads();
+        // online softmax over the window, one wave per query
+        for (int hh = wave; hh < QPK; hh += 4) {
+            const float zv = lane < n ? ps[hh][lane] : -INFINITY;
+            float mx = zv;
 #pragma unroll
-            for (int msk = 1; msk < 64; msk <<= 1) part += shfl_xor(part, msk);
-            if (lane == 0) sc[hh][i] = part * qscale;
+            for (int msk = 1; msk < 64; msk <<= 1) mx = fmaxf(mx, shfl_xor(mx, msk));
+            const float mo = run_m[hh];
+            const float mn = fmaxf(mo, mx);
+            const float pv = lane < n ? exp2f(zv - mn) : 0.f;
+            if (lane < n) ps[hh][lane] = pv;
+            float sum = pv;
+#pragma unroll
+            for (int msk = 1; msk < 64; msk <<= 1) sum += shfl_xor(sum, msk);
+            if (lane == 0) {
+                const float al = exp2f(mo - mn);
+                run_a[hh] = al;
+                run_l[hh] = run_l[hh] * al + sum;
+                run_m[hh] = mn;
+            }
         }
+        __syncthreads();
+        // window P.V, thread = (query, channel)
+#pragma unroll
+        for (int k = 0; k < S2_MAXQ * D / 256; k++) {
+            const int i = tid + 256 * k;
+            if (i < QPK * D) {
+                const int hh = i / D, c = i % D;
+                float a = acc[k] * run_a[hh];
+#pragma unroll 16
+                for (int tt = 0; tt < n; tt++) a = fmaf(ps[hh][tt], h2f(vt[tt][c]), a);
+                acc[k] = a;
+            }
+        }
+        __syncthreads();
+    }
+
+    // merge the window with the stage-1 splits: log-sum-exp weights once per
+    // (query, split) in shared memory
+    __shared__ float sw[S2_MAXQ][S2_MAXSPLIT];
+    __shared__ float wr_s[S2_MAXQ], wsum_s[S2_MAXQ], anum_s[S2_MAXQ];
+    __shared__ float4 red[256];
+    for (int i = tid; i < QPK * nsplit; i += 256) {
+        const int hh = i / nsplit, sp = i % nsplit;
+        sw[hh][sp] = W.ml[((size_t)b * P.Hq + h * QPK + hh) * W.max_splits + sp].x;
     }
     __syncthreads();
-    // softmax statistics of the window per query head
     for (int hh = wave; hh < QPK; hh += 4) {
-        float mx = -INFINITY;
-        for (int i = lane; i < nr; i += 64) mx = fmaxf(mx, sc[hh][i]);
+        const size_t row0 = ((size_t)b * P.Hq + h * QPK + hh) * W.max_splits;
+        const float lr = run_l[hh], mr = run_m[hh];
+        const float lse_r = nr > 0 ? mr + log2f(lr) : -INFINITY;
+        float M = lse_r;
+        for (int sp = lane; sp < nsplit; sp += 64) M = fmaxf(M, sw[hh][sp]);
 #pragma unroll
-        for (int msk = 1; msk < 64; msk <<= 1) mx = fmaxf(mx, shfl_xor(mx, msk));
-        float sum = 0.f;
-        for (int i = lane; i < nr; i += 64) {
-            const float pv = exp2f(sc[hh][i] - mx);
-            sc[hh][i] = pv;
-            sum += pv;
+        for (int msk = 1; msk < 64; msk <<= 1) M = fmaxf(M, shfl_xor(M, msk));
+        float ws = 0.f, an = 0.f;
+        for (int sp = lane; sp < nsplit; sp += 64) {
+            const float wv = exp2f(sw[hh][sp] - M);
+            sw[hh][sp] = wv;
+            ws += wv;
+            an = fmaf(wv, W.ml[row0 + sp].y, an);
         }
 #pragma unroll
-        for (int msk = 1; msk < 64; msk <<= 1) sum += shfl_xor(sum, msk);
-        if (lane == 0) { mr[hh] = mx; lr[hh] = sum; }
+        for (int msk = 1; msk < 64; msk <<= 1) {
+            ws += shfl_xor(ws, msk);
+            an += shfl_xor(an, msk);
+        }
+        if (lane == 0) {
+            const float wr = nr > 0 ? exp2f(lse_r - M) : 0.f;
+            wr_s[hh] = wr;
+            wsum_s[hh] = ws + wr;
+            anum_s[hh] = an + wr;                    // fp16 tokens: u = 0
+        }
+    }
+    // window result of this thread's (query, channel) pairs into the shared output
+    __shared__ float ow[S2_MAXQ][D];
+#pragma unroll
+    for (int k = 0; k < S2_MAXQ * D / 256; k++) {
+        const int i = tid + 256 * k;
+        if (i < QPK * D) ow[i / D][i % D] = nr > 0 ? acc[k] / run_l[i / D] : 0.f;
     }
     __syncthreads();
-    // window output and merge, thread = (query head, channel)
-    for (int i = tid; i < QPK * D; i += 256) {
-        const int hh = i / D, c = i % D;
+    // thread = (query, channel quad, split phase): float4 partial rows, all
+    // loads independent
+    const int nq4 = QPK * (D / 4);                   // (query, quad) pairs
+    const int nph = 256 / nq4;                       // split phases per pair (>= 1)
+    float4 part = make_float4(0.f, 0.f, 0.f, 0.f);
+    const int pair = tid % nq4, ph = tid / nq4;
+    const int hh = pair / (D / 4), c4 = pair % (D / 4);
+    if (ph < nph) {
+        const size_t row0 = ((size_t)b * P.Hq + h * QPK + hh) * W.max_splits;
+#pragma unroll 8
+        for (int sp = ph; sp < nsplit; sp += nph) {
+            const float4 o4 = *(const float4 *)&W.o[(row0 + sp) * D + 4 * c4];
+            const float wv = sw[hh][sp];
+            part.x = fmaf(wv, o4.x, part.x);
+            part.y = fmaf(wv, o4.y, part.y);
+            part.z = fmaf(wv, o4.z, part.z);
+            part.w = fmaf(wv, o4.w, part.w);
+        }
+    }
+    red[tid] = part;
+    __syncthreads();
+    if (tid < nq4) {
+        float4 tot = red[tid];
+        for (int k = 1; k < nph; k++) {
+            const float4 v = red[tid + k * nq4];
+            tot.x += v.x; tot.y += v.y; tot.z += v.z; tot.w += v.w;
+        }
         const int hq = h * QPK + hh;
-        float acc = 0.f;
-        for (int j = 0; j < nr; j++) {
-            const int t = W0 + j;
-            const size_t slot = wit ? (size_t)(t - nkq) : (size_t)(t % P.R);
-            acc = fmaf(sc[hh][j], h2f(P.res_v[(bh * win + slot) * D + c]), acc);
-        }
-        const size_t row0 = ((size_t)b * P.Hq + hq) * W.max_splits;
-        float M = nr > 0 ? mr[hh] + log2f(lr[hh]) : -INFINITY;
-        for (int sp = 0; sp < nsplit; sp++) M = fmaxf(M, W.ml[row0 + sp].x);
-        float wsum = 0.f, num = 0.f, anum = 0.f;
-        if (nr > 0) {
-            const float wr = exp2f(mr[hh] + log2f(lr[hh]) - M);
-            wsum += wr;
-            num += wr * (acc / lr[hh]);
-            anum += wr;                                  // fp16 tokens: u = 0
-        }
-        for (int sp = 0; sp < nsplit; sp++) {
-            const float2 ml = W.ml[row0 + sp];
-            const float ws = exp2f(ml.x - M);
-            wsum += ws;
-            num = fmaf(ws, W.o[(row0 + sp) * D + c], num);
-            anum = fmaf(ws, ml.y, anum);
-        }
+        const float wsum = wsum_s[hh], wr = wr_s[hh];
         const bool any = wsum > 0.f;
-        out[((size_t)b * P.Hq + hq) * D + c] = any ? num / wsum : 0.f;
-        if (cert && c == 0) cert[(size_t)b * P.Hq + hq] = any ? anum / wsum : 0.f;
+        const float inv = any ? 1.0f / wsum : 0.f;
+        float4 o;
+        o.x = (tot.x + wr * ow[hh][4 * c4 + 0]) * inv;
+        o.y = (tot.y + wr * ow[hh][4 * c4 + 1]) * inv;
+        o.z = (tot.z + wr * ow[hh][4 * c4 + 2]) * inv;
+        o.w = (tot.w + wr * ow[hh][4 * c4 + 3]) * inv;
+        *(float4 *)&out[((size_t)b * P.Hq + hq) * D + 4 * c4] = o;
+        if (cert && c4 == 0) cert[(size_t)b * P.Hq + hq] = any ? anum_s[hh] / wsum : 0.f;
     }
 }
 
