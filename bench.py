@@ -300,7 +300,18 @@ def main():
     ap.add_argument("--split-pages", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain device copy of 1 GiB (scales FETCH_SIZE/WRITE_SIZE)")
     args = ap.parse_args()
+    if args.copy_calibration:
+        import torch
+        x = torch.ones(1 << 28, dtype=torch.float32, device="cuda")      # 1 GiB
+        y = torch.empty_like(x)
+        for _ in range(3):
+            y.copy_(x)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes": x.numel() * 4, "copies": 3}))
+        return
     if args.gpus != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
               "(--gpus must be 1)", file=sys.stderr)

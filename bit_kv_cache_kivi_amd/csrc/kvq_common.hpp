@@ -22,7 +22,7 @@ constexpr int NB = 16;          // Kitty boosted channels per KV head
 //   KC  2048 B  low 2-bit key codes, token-major, arranged as the B operand of
 //               a 16x16x32 f16 matrix-core product (see key_code_pos)
 //   KH   256 B  KITTY only: high 2-bit plane of the 16 boosted channels
-//   KS  1024 B  key {scale, zero} fp16 pairs, [2 groups][128 channel slots]
+//   KS  1024 B  key {scale, zero} fp16 pairs, [2 groups][128 channels]
 //   VC  2048 B  value codes, channel-major (see value_code_pos)
 //   VS  1024 B  value {scale, zero} fp16 pairs, [64 tokens][4 groups]
 // WITCERT, 256 tokens (one block):
@@ -82,10 +82,9 @@ __host__ __device__ inline void high_code_pos(int t, int o, int &dword, int &shi
     shift = 4 * (4 * (n & 1) + i) + 2 * (n >> 1);
 }
 
-// Key statistic slot of channel c inside a group: lanes with the same
-// (c>>3)&3 read 32 contiguous slots.
+// Key statistic slot of channel c inside a group (channel order).
 __host__ __device__ inline int key_stat_slot(int c) {
-    return 32 * ((c >> 3) & 3) + 8 * (c >> 5) + (c & 7);
+    return c;
 }
 
 // ---------------------------------------------------------------------------

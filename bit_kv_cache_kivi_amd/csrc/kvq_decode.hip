@@ -127,7 +127,7 @@ __global__ __launch_bounds__(64) void stage1_valu_kernel(KParams P, const uint16
             float bias = 0.f;
 #pragma unroll
             for (int i = 0; i < 32; i++) {
-                const uint32_t sz = kss[128 * gi + 32 * g + i];
+                const uint32_t sz = kss[128 * gi + 32 * (i >> 3) + 8 * g + (i & 7)];
                 const float sc = h2f((uint16_t)(sz & 0xffff));
                 const float ze = h2f((uint16_t)(sz >> 16));
                 a[i] = qv[i] * sc;
@@ -299,10 +299,13 @@ __device__ inline h2v cvth(uint32_t x, int sel) {
     }
 }
 
+typedef uint32_t u4v __attribute__((ext_vector_type(4)));
+
 // eight codes held in the nibbles of a masked dword -> f16 fragment (k = nibble)
 __device__ inline h8v frag8(uint32_t m) {
-    const h2v a = cvth(m, 0), b = cvth(m, 1), c = cvth(m, 2), d = cvth(m, 3);
-    return h8v{a.x, a.y, b.x, b.y, c.x, c.y, d.x, d.y};
+    const u4v v = {__builtin_bit_cast(uint32_t, cvth(m, 0)), __builtin_bit_cast(uint32_t, cvth(m, 1)),
+                   __builtin_bit_cast(uint32_t, cvth(m, 2)), __builtin_bit_cast(uint32_t, cvth(m, 3))};
+    return __builtin_bit_cast(h8v, v);
 }
 
 __device__ inline float lo16f(uint32_t v) { return h2f((uint16_t)(v & 0xffffu)); }
@@ -310,20 +313,30 @@ __device__ inline float hi16f(uint32_t v) { return h2f((uint16_t)(v >> 16)); }
 
 constexpr float LAZY_TAU = 8.0f;
 
+// Keeps a binary32 value opaque to the optimizer, so every later use sees the
+// same rounded number (no re-derivation of it from its operands).
+__device__ inline float pin(float x) {
+    asm volatile("" : "+v"(x));
+    return x;
+}
+
 // a = fl32(x * y) for two pairs, each split into f16 hi + lo with hi + lo = a
-// to within half an ulp of lo.  hi is cut by round-toward-zero in one opaque
-// packed conversion, and lo is the exact binary32 remainder a - hi rounded to
-// f16, so both parts come from the same rounded a whatever the compiler does
-// with the product (a remainder formed by an FMA against a separately rounded
-// hi can miss by one f16 ulp of hi).
-__device__ inline void mul_split2(float x0, float y0, float x1, float y1, h2v &hi, h2v &lo) {
-#pragma clang fp contract(off)
-    const float a0 = x0 * y0;
-    const float a1 = x1 * y1;
+// to within half an ulp of lo: hi is cut by round-toward-zero in one packed
+// conversion and lo is the remainder a - hi (exact in binary32) rounded to
+// f16.  a is pinned, so hi and lo come from the same rounded product (a
+// remainder formed against a differently rounded product can miss by one f16
+// ulp of hi).
+__device__ inline void mul_split2(float x0, _Float16 y0, float x1, _Float16 y1, h2v &hi, h2v &lo) {
+    const float a0 = pin(__builtin_fmaf(x0, (float)y0, 0.0f));     // the rounded product
+    const float a1 = pin(__builtin_fmaf(x1, (float)y1, 0.0f));
     const h2v h = __builtin_bit_cast(h2v, __builtin_amdgcn_cvt_pkrtz(a0, a1));
     hi = h;
-    lo = h2v{(_Float16)(a0 - (float)h.x), (_Float16)(a1 - (float)h.y)};
+    // a - hi is exact in binary32, so the fused form rounds it once to f16
+    lo = h2v{(_Float16)__builtin_fmaf(-1.0f, (float)h.x, a0), (_Float16)__builtin_fmaf(-1.0f, (float)h.y, a1)};
 }
+
+__device__ inline _Float16 lo16h(uint32_t v) { return __builtin_bit_cast(_Float16, (uint16_t)(v & 0xffffu)); }
+__device__ inline _Float16 hi16h(uint32_t v) { return __builtin_bit_cast(_Float16, (uint16_t)(v >> 16)); }
 
 struct PageRegs {
     uint4 ka, kb, va, vb, ks, vs;
@@ -356,16 +369,21 @@ struct Gqa4State {
     f4v acc[8];
 };
 
+// Rows of p [query][token] and value {s, z} [group][token] start at these
+// offsets so that the 16 (row, token octet) pairs read together by a P.V
+// operand load fall on 64 distinct LDS banks.
+__device__ constexpr int ROWB[4] = {0, 68, 160, 228};
+constexpr int AS_STRIDE = 20;       // octets per score-operand row (16 + bank padding)
+
 struct Gqa4Smem {
-    f4v zsh[PT];            // scores [token][query]
-    float psh[4][PT];       // p [query][token]
-    uint32_t vsT[4][PT];    // value {s, z} [group][token]
-    uint32_t kss[256];      // key {s, z} [group][slot]
-    h8v As[2][9][16];       // score A: [key group][row 0..7, 8 = zero][channel octet]
+    f4v zsh[PT];                    // scores [token][query]
+    float psh[292];                 // p, row i at ROWB[i]
+    uint32_t vsT[292];              // value {s, z}, row j at ROWB[j]
+    uint32_t kss[256];              // key {s, z} [group][channel]
+    h8v As[2][9][AS_STRIDE];        // score A: [key group][row 0..7, 8 = zero][channel octet]
 };
 
 // One 64-token page.  nvalid < 64 only on the last page of the prefix.
-template <bool MASK>
 __device__ inline void gqa4_page(const PageRegs &R, Gqa4State &S, Gqa4Smem &sm, const float *qc,
                                  int slot0, int lane, int nvalid, float qscale) {
     const int g = lane >> 4, r = lane & 15;
@@ -375,32 +393,42 @@ __device__ inline void gqa4_page(const PageRegs &R, Gqa4State &S, Gqa4Smem &sm, 
 
     __syncthreads();                            // previous page done with the LDS
     ((uint4 *)sm.kss)[lane] = R.ks;
-    sm.vsT[0][lane] = R.vs.x;
-    sm.vsT[1][lane] = R.vs.y;
-    sm.vsT[2][lane] = R.vs.z;
-    sm.vsT[3][lane] = R.vs.w;
+    sm.vsT[ROWB[0] + lane] = R.vs.x;
+    sm.vsT[ROWB[1] + lane] = R.vs.y;
+    sm.vsT[ROWB[2] + lane] = R.vs.z;
+    sm.vsT[ROWB[3] + lane] = R.vs.w;
     __syncthreads();
 
-    // ---- score operand: hi/lo of q_h * s_c, zero-point bias ----
+    // ---- score operand: hi/lo of q_h * s_c, zero-point bias; this lane holds
+    // channels 4*c8 .. 4*c8+3 and 64+4*c8 .. 64+4*c8+3 of query hq ----
     float bq[2][4];
 #pragma unroll
     for (int gi = 0; gi < 2; gi++) {
-        const uint4 s0 = *(const uint4 *)&sm.kss[128 * gi + slot0];
-        const uint4 s1 = *(const uint4 *)&sm.kss[128 * gi + slot0 + 4];
+        const uint4 s0 = *(const uint4 *)&sm.kss[128 * gi + 4 * c8];
+        const uint4 s1 = *(const uint4 *)&sm.kss[128 * gi + 64 + 4 * c8];
         const uint32_t sz[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
         h8v hi, lo;
         float bias = 0.f;
 #pragma unroll
         for (int e = 0; e < 8; e += 2) {
             h2v hh, ll;
-            mul_split2(qc[e], lo16f(sz[e]), qc[e + 1], lo16f(sz[e + 1]), hh, ll);
+            mul_split2(qc[e], lo16h(sz[e]), qc[e + 1], lo16h(sz[e + 1]), hh, ll);
             hi[e] = hh.x; hi[e + 1] = hh.y;
             lo[e] = ll.x; lo[e + 1] = ll.y;
-            bias = fmaf(qc[e], hi16f(sz[e]), bias);
-            bias = fmaf(qc[e + 1], hi16f(sz[e + 1]), bias);
+            bias = fmaf(qc[e], (float)hi16h(sz[e]), bias);
+            bias = fmaf(qc[e + 1], (float)hi16h(sz[e + 1]), bias);
         }
-        sm.As[gi][hq][c8] = hi;
-        sm.As[gi][4 + hq][c8] = lo;
+        // octet c8>>1 (half c8&1) and octet 8 + (c8>>1) of rows hq and 4+hq
+        {
+            const u4v hv = __builtin_bit_cast(u4v, hi), lv = __builtin_bit_cast(u4v, lo);
+            uint2 *rh = (uint2 *)&sm.As[gi][hq][0];
+            uint2 *rl = (uint2 *)&sm.As[gi][4 + hq][0];
+            const int o0 = 2 * (c8 >> 1) + (c8 & 1), o1 = 2 * (8 + (c8 >> 1)) + (c8 & 1);
+            rh[o0] = make_uint2(hv[0], hv[1]);
+            rh[o1] = make_uint2(hv[2], hv[3]);
+            rl[o0] = make_uint2(lv[0], lv[1]);
+            rl[o1] = make_uint2(lv[2], lv[3]);
+        }
         bias = row_sum16(bias);
 #pragma unroll
         for (int i = 0; i < 4; i++)
@@ -408,32 +436,36 @@ __device__ inline void gqa4_page(const PageRegs &R, Gqa4State &S, Gqa4Smem &sm, 
     }
     __syncthreads();
 
-    // ---- scores on the matrix cores ----
+    // ---- scores on the matrix cores: rows 0..3 = queries; the hi and lo
+    // operands are two products into the same accumulator; the four token
+    // tiles are independent accumulators, issued round-robin ----
     const uint32_t kd[8] = {R.ka.x, R.ka.y, R.ka.z, R.ka.w, R.kb.x, R.kb.y, R.kb.z, R.kb.w};
     f4v sc[4];
 #pragma unroll
-    for (int gi = 0; gi < 2; gi++) {
-        const f4v init = lane < 16 ? f4v{bq[gi][0], bq[gi][1], bq[gi][2], bq[gi][3]}
-                                   : f4v{0.f, 0.f, 0.f, 0.f};
-        sc[2 * gi] = init;
-        sc[2 * gi + 1] = init;
-#pragma unroll
-        for (int kc = 0; kc < 4; kc++) {
-            const h8v af = sm.As[gi][r < 8 ? r : 8][r < 8 ? 4 * kc + g : 0];
-#pragma unroll
-            for (int nn = 0; nn < 2; nn++) {
-                const int n = 2 * gi + nn;
-                const uint32_t x = kd[2 * n + (kc >> 1)];
-                const uint32_t mx = (kc & 1) ? ((x >> 2) & MSK) : (x & MSK);
-                sc[n] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af, frag8(mx), sc[n], 0, 0, 0);
-            }
-        }
+    for (int n = 0; n < 4; n++) {
+        const int gi = n >> 1;
+        sc[n] = lane < 16 ? f4v{bq[gi][0], bq[gi][1], bq[gi][2], bq[gi][3]} : f4v{0.f, 0.f, 0.f, 0.f};
     }
-    // rows h (lanes 0..15) + rows h+4 (lanes 16..31)
 #pragma unroll
-    for (int n = 0; n < 4; n++)
+    for (int kc = 0; kc < 4; kc++) {
+        h8v ahi[2], alo[2], bf[4];
 #pragma unroll
-        for (int i = 0; i < 4; i++) sc[n][i] += shfl_xor(sc[n][i], 16);
+        for (int gi = 0; gi < 2; gi++) {
+            ahi[gi] = sm.As[gi][r < 4 ? r : 8][r < 4 ? 4 * kc + g : 0];
+            alo[gi] = sm.As[gi][r < 4 ? 4 + r : 8][r < 4 ? 4 * kc + g : 0];
+        }
+#pragma unroll
+        for (int n = 0; n < 4; n++) {
+            const uint32_t x = kd[2 * n + (kc >> 1)];
+            bf[n] = frag8((kc & 1) ? ((x >> 2) & MSK) : (x & MSK));
+        }
+#pragma unroll
+        for (int n = 0; n < 4; n++)
+            sc[n] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ahi[n >> 1], bf[n], sc[n], 0, 0, 0);
+#pragma unroll
+        for (int n = 0; n < 4; n++)
+            sc[n] = __builtin_amdgcn_mfma_f32_16x16x32_f16(alo[n >> 1], bf[n], sc[n], 0, 0, 0);
+    }
     if (lane < 16) {
 #pragma unroll
         for (int n = 0; n < 4; n++) sm.zsh[16 * n + r] = sc[n];
@@ -446,7 +478,7 @@ __device__ inline void gqa4_page(const PageRegs &R, Gqa4State &S, Gqa4Smem &sm, 
     bool exceed = false;
 #pragma unroll
     for (int i = 0; i < 4; i++) {
-        if (MASK && lane >= nvalid) zz[i] = -INFINITY;
+        if (lane >= nvalid) zz[i] = -INFINITY;
         exceed |= zz[i] > S.m[i] + LAZY_TAU;
     }
     if (__any(exceed)) {
@@ -470,7 +502,7 @@ __device__ inline void gqa4_page(const PageRegs &R, Gqa4State &S, Gqa4Smem &sm, 
     for (int i = 0; i < 4; i++) {
         const float pv = __builtin_amdgcn_exp2f(zz[i] - S.m[i]);
         S.lsum[i] += pv;
-        sm.psh[i][lane] = pv;
+        sm.psh[ROWB[i] + lane] = pv;
     }
     __syncthreads();
 
@@ -479,26 +511,32 @@ __device__ inline void gqa4_page(const PageRegs &R, Gqa4State &S, Gqa4Smem &sm, 
 #pragma unroll
     for (int ks = 0; ks < 2; ks++) {
         const int t0 = 32 * ks + 8 * g;
-        const float4 pa = *(const float4 *)&sm.psh[hp][t0];
-        const float4 pb = *(const float4 *)&sm.psh[hp][t0 + 4];
-        const uint4 za = *(const uint4 *)&sm.vsT[jp][t0];
-        const uint4 zb = *(const uint4 *)&sm.vsT[jp][t0 + 4];
-        const float pe[8] = {pa.x, pa.y, pa.z, pa.w, pb.x, pb.y, pb.z, pb.w};
-        const uint32_t se[8] = {za.x, za.y, za.z, za.w, zb.x, zb.y, zb.z, zb.w};
+        const float4 pa = *(const float4 *)&sm.psh[ROWB[hp] + t0];
+        const float4 pb = *(const float4 *)&sm.psh[ROWB[hp] + t0 + 4];
+        const uint4 za = *(const uint4 *)&sm.vsT[ROWB[jp] + t0];
+        const uint4 zb = *(const uint4 *)&sm.vsT[ROWB[jp] + t0 + 4];
+        uint32_t pw[8] = {__builtin_bit_cast(uint32_t, pa.x), __builtin_bit_cast(uint32_t, pa.y),
+                          __builtin_bit_cast(uint32_t, pa.z), __builtin_bit_cast(uint32_t, pa.w),
+                          __builtin_bit_cast(uint32_t, pb.x), __builtin_bit_cast(uint32_t, pb.y),
+                          __builtin_bit_cast(uint32_t, pb.z), __builtin_bit_cast(uint32_t, pb.w)};
+        uint32_t se[8] = {za.x, za.y, za.z, za.w, zb.x, zb.y, zb.z, zb.w};
+        if (nvalid < PT) {                           // uniform: only the prefix's last page
+#pragma unroll
+            for (int e = 0; e < 8; e++) {
+                // statistics past nvalid are not written yet: zero p, s and z
+                const uint32_t keep = (t0 + e < nvalid) ? 0xffffffffu : 0u;
+                pw[e] &= keep;
+                se[e] &= keep;
+            }
+        }
+        float pv[8];
+        _Float16 sv[8];
         h8v bhi, blo;
-        float pv[8], sv[8];
 #pragma unroll
         for (int e = 0; e < 8; e++) {
-            pv[e] = pe[e];
-            sv[e] = lo16f(se[e]);
-            float zv = hi16f(se[e]);
-            if (MASK) {
-                const bool tv = t0 + e < nvalid;     // statistics past nvalid are not written yet
-                pv[e] = tv ? pv[e] : 0.f;
-                sv[e] = tv ? sv[e] : 0.f;
-                zv = tv ? zv : 0.f;
-            }
-            S.zacc = fmaf(pv[e], zv, S.zacc);
+            pv[e] = __builtin_bit_cast(float, pw[e]);
+            sv[e] = lo16h(se[e]);
+            S.zacc = fmaf(pv[e], (float)hi16h(se[e]), S.zacc);
         }
 #pragma unroll
         for (int e = 0; e < 8; e += 2) {
@@ -508,11 +546,19 @@ __device__ inline void gqa4_page(const PageRegs &R, Gqa4State &S, Gqa4Smem &sm, 
             blo[e] = ll.x; blo[e + 1] = ll.y;
         }
 #pragma unroll
-        for (int nt = 0; nt < 8; nt++) {
-            const uint32_t x = vd[nt];
-            const h8v af = frag8(ks ? ((x >> 2) & MSK) : (x & MSK));
-            S.acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af, bhi, S.acc[nt], 0, 0, 0);
-            S.acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af, blo, S.acc[nt], 0, 0, 0);
+        for (int nh = 0; nh < 2; nh++) {            // four channel tiles at a time
+            h8v af[4];
+#pragma unroll
+            for (int u = 0; u < 4; u++) {
+                const uint32_t x = vd[4 * nh + u];
+                af[u] = frag8(ks ? ((x >> 2) & MSK) : (x & MSK));
+            }
+#pragma unroll
+            for (int u = 0; u < 4; u++)
+                S.acc[4 * nh + u] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[u], bhi, S.acc[4 * nh + u], 0, 0, 0);
+#pragma unroll
+            for (int u = 0; u < 4; u++)
+                S.acc[4 * nh + u] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[u], blo, S.acc[4 * nh + u], 0, 0, 0);
         }
     }
 }
@@ -544,17 +590,15 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 8))) void
     // query for this lane's score-operand role (unscaled: keeps q s in the
     // range where the f16 remainder is a normal number)
     const int hq = g, c8 = r;
-    float qc[8];
+    float qc[8];                                  // channels 4*c8+e, 64+4*c8+e
     {
-        const uint4 raw = *(const uint4 *)(q + ((size_t)b * P.Hq + (size_t)h * 4 + hq) * D + 8 * c8);
-        const uint32_t w4[4] = {raw.x, raw.y, raw.z, raw.w};
-#pragma unroll
-        for (int i = 0; i < 4; i++) {
-            qc[2 * i] = lo16f(w4[i]);
-            qc[2 * i + 1] = hi16f(w4[i]);
-        }
+        const uint16_t *qh = q + ((size_t)b * P.Hq + (size_t)h * 4 + hq) * D;
+        const uint2 r0 = *(const uint2 *)(qh + 4 * c8);
+        const uint2 r1 = *(const uint2 *)(qh + 64 + 4 * c8);
+        qc[0] = lo16f(r0.x); qc[1] = hi16f(r0.x); qc[2] = lo16f(r0.y); qc[3] = hi16f(r0.y);
+        qc[4] = lo16f(r1.x); qc[5] = hi16f(r1.x); qc[6] = lo16f(r1.y); qc[7] = hi16f(r1.y);
     }
-    const int slot0 = 32 * (c8 & 3) + 8 * (c8 >> 2);      // key_stat_slot(8 * c8)
+    const int slot0 = 0;
     if (lane < 16) {
         sm.As[0][8][lane] = h8v{0, 0, 0, 0, 0, 0, 0, 0};
         sm.As[1][8][lane] = h8v{0, 0, 0, 0, 0, 0, 0, 0};
@@ -572,17 +616,23 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 8))) void
 
     const uint8_t *base = P.pool + (size_t)h * P.page_bytes;
     const size_t pstride = (size_t)P.Hkv * P.page_bytes;
-    PageRegs cur = load_page(base + (size_t)__builtin_amdgcn_readlane(pid_l, 0) * pstride, G, lane);
-    for (int i = 0; i < np; i++) {
-        PageRegs nxt;
-        if (i + 1 < np)                          // prefetch the next page
-            nxt = load_page(base + (size_t)__builtin_amdgcn_readlane(pid_l, i + 1) * pstride, G, lane);
-        const int nvalid = nvq - (p0 + i) * PT;
-        if (nvalid >= PT)
-            gqa4_page<false>(cur, S, sm, qc, slot0, lane, PT, qscale);
-        else
-            gqa4_page<true>(cur, S, sm, qc, slot0, lane, nvalid, qscale);
-        if (i + 1 < np) cur = nxt;
+    // two register sets used in turn: the next page loads while this one is
+    // processed
+    auto run_page = [&](const PageRegs &R, int i) {
+        gqa4_page(R, S, sm, qc, slot0, lane, min(PT, nvq - (p0 + i) * PT), qscale);
+    };
+    auto page_at = [&](int i) {
+        return base + (size_t)__builtin_amdgcn_readlane(pid_l, i) * pstride;
+    };
+    PageRegs ra = load_page(page_at(0), G, lane);
+    PageRegs rb;
+    for (int i = 0; i < np; i += 2) {
+        if (i + 1 < np) rb = load_page(page_at(i + 1), G, lane);
+        run_page(ra, i);
+        if (i + 1 < np) {
+            if (i + 2 < np) ra = load_page(page_at(i + 2), G, lane);
+            run_page(rb, i + 1);
+        }
     }
 
     // ---- reduce and write the split's partial ----

@@ -51,8 +51,7 @@ def _high_index():
 KEY_DW, KEY_SH = _key_index()
 VAL_DW, VAL_SH = _value_index()
 HI_DW, HI_SH = _high_index()
-_c = np.arange(D)
-KEY_SLOT = 32 * ((_c >> 3) & 3) + 8 * (_c >> 5) + (_c & 7)
+KEY_SLOT = np.arange(D)            # key statistics in channel order
 
 
 def _u32(block: np.ndarray, off: int, n: int) -> np.ndarray:
