@@ -320,19 +320,25 @@ __device__ inline float pin(float x) {
     return x;
 }
 
-// a = fl32(x * y) for two pairs, each split into f16 hi + lo with hi + lo = a
-// to within half an ulp of lo: hi is cut by round-toward-zero in one packed
-// conversion and lo is the remainder a - hi (exact in binary32) rounded to
-// f16.  a is pinned, so hi and lo come from the same rounded product (a
-// remainder formed against a differently rounded product can miss by one f16
-// ulp of hi).
-__device__ inline void mul_split2(float x0, _Float16 y0, float x1, _Float16 y1, h2v &hi, h2v &lo) {
+// f16 remainder pair of two binary32 values against their packed f16 heads h
+// (one per half): each half is fl16(a - head), formed by the mixed-precision
+// fused multiply-add in one rounding (a - head is exact in binary32).
+__device__ inline uint32_t rem_pair(float a0, float a1, uint32_t h) {
+    uint32_t lo;
+    asm("v_fma_mixlo_f16 %0, %1, -1.0, %2 op_sel_hi:[1,0,0]" : "=&v"(lo) : "v"(h), "v"(a0));
+    asm("v_fma_mixhi_f16 %0, %1, -1.0, %2 op_sel:[1,0,0] op_sel_hi:[1,0,0]" : "+v"(lo) : "v"(h), "v"(a1));
+    return lo;
+}
+
+// a = fl32(x * y) for two pairs, split into f16 hi + lo with hi + lo = a to
+// within half an ulp of lo: hi is cut by round-toward-zero in one packed
+// conversion and lo is the remainder.  a is pinned, so hi and lo come from the
+// same rounded product.
+__device__ inline void mul_split2(float x0, _Float16 y0, float x1, _Float16 y1, uint32_t &hi, uint32_t &lo) {
     const float a0 = pin(__builtin_fmaf(x0, (float)y0, 0.0f));     // the rounded product
     const float a1 = pin(__builtin_fmaf(x1, (float)y1, 0.0f));
-    const h2v h = __builtin_bit_cast(h2v, __builtin_amdgcn_cvt_pkrtz(a0, a1));
-    hi = h;
-    // a - hi is exact in binary32, so the fused form rounds it once to f16
-    lo = h2v{(_Float16)__builtin_fmaf(-1.0f, (float)h.x, a0), (_Float16)__builtin_fmaf(-1.0f, (float)h.y, a1)};
+    hi = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(a0, a1));
+    lo = rem_pair(a0, a1, hi);
 }
 
 __device__ inline _Float16 lo16h(uint32_t v) { return __builtin_bit_cast(_Float16, (uint16_t)(v & 0xffffu)); }
@@ -353,6 +359,27 @@ __device__ inline PageRegs load_page(const uint8_t *page, const Geom &G, int lan
     return R;
 }
 
+// The same page through a buffer descriptor of the page's own extent.  With
+// valid false the extent is zero: the loads return zeros and touch no memory,
+// so a loop can issue them unconditionally (the wait counts stay exact and
+// the prefetched pages stay in flight).
+__device__ inline uint4 bload(__amdgpu_buffer_rsrc_t rs, int off) {
+    return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0));
+}
+__device__ inline PageRegs load_page_masked(const uint8_t *page, bool valid, const Geom &G, int lane) {
+    const __amdgpu_buffer_rsrc_t rs =
+        __builtin_amdgcn_make_buffer_rsrc((void *)page, (short)0, valid ? G.bytes : 0, 0x00020000);
+    const int o = 16 * lane;
+    PageRegs R;                                 // issued in the order of use
+    R.ks = bload(rs, G.ks + o);
+    R.vs = bload(rs, G.vs + o);
+    R.ka = bload(rs, G.kc + o);
+    R.kb = bload(rs, G.kc + 1024 + o);
+    R.va = bload(rs, G.vc + o);
+    R.vb = bload(rs, G.vc + 1024 + o);
+    return R;
+}
+
 // sum over the 16 lanes of a row; the total lands in the row's lane 15
 __device__ inline float row_sum16(float v) {
     v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0u, __builtin_bit_cast(uint32_t, v), 0x111, 0xf, 0xf, true));
@@ -362,6 +389,14 @@ __device__ inline float row_sum16(float v) {
     return v;
 }
 
+// Workgroup barrier that orders LDS only: global loads issued before it (the
+// prefetched pages) stay in flight, where a full barrier would wait for them.
+__device__ inline void lds_sync() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 struct Gqa4State {
     float m[4];
     float lsum[4];
@@ -369,91 +404,78 @@ struct Gqa4State {
     f4v acc[8];
 };
 
-// Rows of p [query][token] and value {s, z} [group][token] start at these
-// offsets so that the 16 (row, token octet) pairs read together by a P.V
+// Rows of p [query][token] and value {s, z} [group][token] start at offsets
+// rowb(row) so that the 16 (row, token octet) pairs read together by a P.V
 // operand load fall on 64 distinct LDS banks.
-__device__ constexpr int ROWB[4] = {0, 68, 160, 228};
+__host__ __device__ constexpr int rowb(int i) { return i == 0 ? 0 : i == 1 ? 68 : i == 2 ? 160 : 228; }
 constexpr int AS_STRIDE = 20;       // octets per score-operand row (16 + bank padding)
 
 struct Gqa4Smem {
-    f4v zsh[PT];                    // scores [token][query]
-    float psh[292];                 // p, row i at ROWB[i]
-    uint32_t vsT[292];              // value {s, z}, row j at ROWB[j]
+    f4v zsh[2][PT];                 // scores from the hi and the lo operand rows [token][query]
+    f4v bsh[2];                     // zero-point term times qscale [key group][query]
+    float psh[292];                 // p, row i at rowb(i)
+    uint32_t vsT[292];              // value {s, z}, row j at rowb(j)
     uint32_t kss[256];              // key {s, z} [group][channel]
-    h8v As[2][9][AS_STRIDE];        // score A: [key group][row 0..7, 8 = zero][channel octet]
+    h8v As[2][9][AS_STRIDE];        // score A: [key group][row 0..3 hi, 4..7 lo, 8 = zero][channel octet]
 };
 
 // One 64-token page.  nvalid < 64 only on the last page of the prefix.
 __device__ inline void gqa4_page(const PageRegs &R, Gqa4State &S, Gqa4Smem &sm, const float *qc,
-                                 int slot0, int lane, int nvalid, float qscale) {
+                                 int lane, int nvalid, float qscale, int rb_hp, int rb_jp) {
     const int g = lane >> 4, r = lane & 15;
     const int hq = g, c8 = r;
-    const int hp = r >> 2, jp = r & 3;
+    const int hp = r >> 2;
     const uint32_t MSK = 0x33333333u;
 
-    __syncthreads();                            // previous page done with the LDS
+    lds_sync();                            // previous page done with the LDS
     ((uint4 *)sm.kss)[lane] = R.ks;
-    sm.vsT[ROWB[0] + lane] = R.vs.x;
-    sm.vsT[ROWB[1] + lane] = R.vs.y;
-    sm.vsT[ROWB[2] + lane] = R.vs.z;
-    sm.vsT[ROWB[3] + lane] = R.vs.w;
-    __syncthreads();
+    sm.vsT[rowb(0) + lane] = R.vs.x;
+    sm.vsT[rowb(1) + lane] = R.vs.y;
+    sm.vsT[rowb(2) + lane] = R.vs.z;
+    sm.vsT[rowb(3) + lane] = R.vs.w;
+    lds_sync();
 
-    // ---- score operand: hi/lo of q_h * s_c, zero-point bias; this lane holds
-    // channels 4*c8 .. 4*c8+3 and 64+4*c8 .. 64+4*c8+3 of query hq ----
-    float bq[2][4];
+    // ---- score operand: hi/lo of q_h * s_c and the zero-point term; this lane
+    // holds channels 4*c8 .. 4*c8+3 and 64+4*c8 .. 64+4*c8+3 of query hq ----
 #pragma unroll
     for (int gi = 0; gi < 2; gi++) {
         const uint4 s0 = *(const uint4 *)&sm.kss[128 * gi + 4 * c8];
         const uint4 s1 = *(const uint4 *)&sm.kss[128 * gi + 64 + 4 * c8];
         const uint32_t sz[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
-        h8v hi, lo;
+        uint32_t hv[4], lv[4];
         float bias = 0.f;
 #pragma unroll
         for (int e = 0; e < 8; e += 2) {
-            h2v hh, ll;
-            mul_split2(qc[e], lo16h(sz[e]), qc[e + 1], lo16h(sz[e + 1]), hh, ll);
-            hi[e] = hh.x; hi[e + 1] = hh.y;
-            lo[e] = ll.x; lo[e + 1] = ll.y;
+            mul_split2(qc[e], lo16h(sz[e]), qc[e + 1], lo16h(sz[e + 1]), hv[e >> 1], lv[e >> 1]);
             bias = fmaf(qc[e], (float)hi16h(sz[e]), bias);
             bias = fmaf(qc[e + 1], (float)hi16h(sz[e + 1]), bias);
         }
         // octet c8>>1 (half c8&1) and octet 8 + (c8>>1) of rows hq and 4+hq
-        {
-            const u4v hv = __builtin_bit_cast(u4v, hi), lv = __builtin_bit_cast(u4v, lo);
-            uint2 *rh = (uint2 *)&sm.As[gi][hq][0];
-            uint2 *rl = (uint2 *)&sm.As[gi][4 + hq][0];
-            const int o0 = 2 * (c8 >> 1) + (c8 & 1), o1 = 2 * (8 + (c8 >> 1)) + (c8 & 1);
-            rh[o0] = make_uint2(hv[0], hv[1]);
-            rh[o1] = make_uint2(hv[2], hv[3]);
-            rl[o0] = make_uint2(lv[0], lv[1]);
-            rl[o1] = make_uint2(lv[2], lv[3]);
-        }
+        uint2 *rh = (uint2 *)&sm.As[gi][hq][0];
+        uint2 *rl = (uint2 *)&sm.As[gi][4 + hq][0];
+        const int o0 = 2 * (c8 >> 1) + (c8 & 1), o1 = 2 * (8 + (c8 >> 1)) + (c8 & 1);
+        rh[o0] = make_uint2(hv[0], hv[1]);
+        rh[o1] = make_uint2(hv[2], hv[3]);
+        rl[o0] = make_uint2(lv[0], lv[1]);
+        rl[o1] = make_uint2(lv[2], lv[3]);
         bias = row_sum16(bias);
-#pragma unroll
-        for (int i = 0; i < 4; i++)
-            bq[gi][i] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, bias), 16 * i + 15));
+        if (r == 15) ((float *)&sm.bsh[gi])[hq] = bias * qscale;
     }
-    __syncthreads();
+    lds_sync();
 
-    // ---- scores on the matrix cores: rows 0..3 = queries; the hi and lo
-    // operands are two products into the same accumulator; the four token
-    // tiles are independent accumulators, issued round-robin ----
+    // ---- scores on the matrix cores: operand rows 0..3 carry the hi parts and
+    // rows 4..7 the lo parts of the four queries, so one product per token
+    // tile gives both; the four tiles are independent accumulators ----
     const uint32_t kd[8] = {R.ka.x, R.ka.y, R.ka.z, R.ka.w, R.kb.x, R.kb.y, R.kb.z, R.kb.w};
     f4v sc[4];
 #pragma unroll
-    for (int n = 0; n < 4; n++) {
-        const int gi = n >> 1;
-        sc[n] = lane < 16 ? f4v{bq[gi][0], bq[gi][1], bq[gi][2], bq[gi][3]} : f4v{0.f, 0.f, 0.f, 0.f};
-    }
+    for (int n = 0; n < 4; n++) sc[n] = f4v{0.f, 0.f, 0.f, 0.f};
+    const int arow = r < 8 ? r : 8;
 #pragma unroll
     for (int kc = 0; kc < 4; kc++) {
-        h8v ahi[2], alo[2], bf[4];
+        h8v af[2], bf[4];
 #pragma unroll
-        for (int gi = 0; gi < 2; gi++) {
-            ahi[gi] = sm.As[gi][r < 4 ? r : 8][r < 4 ? 4 * kc + g : 0];
-            alo[gi] = sm.As[gi][r < 4 ? 4 + r : 8][r < 4 ? 4 * kc + g : 0];
-        }
+        for (int gi = 0; gi < 2; gi++) af[gi] = sm.As[gi][arow][r < 8 ? 4 * kc + g : 0];
 #pragma unroll
         for (int n = 0; n < 4; n++) {
             const uint32_t x = kd[2 * n + (kc >> 1)];
@@ -461,26 +483,25 @@ __device__ inline void gqa4_page(const PageRegs &R, Gqa4State &S, Gqa4Smem &sm, 
         }
 #pragma unroll
         for (int n = 0; n < 4; n++)
-            sc[n] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ahi[n >> 1], bf[n], sc[n], 0, 0, 0);
-#pragma unroll
-        for (int n = 0; n < 4; n++)
-            sc[n] = __builtin_amdgcn_mfma_f32_16x16x32_f16(alo[n >> 1], bf[n], sc[n], 0, 0, 0);
+            sc[n] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[n >> 1], bf[n], sc[n], 0, 0, 0);
     }
-    if (lane < 16) {
+    if (lane < 32) {                            // rows 0..3 (lanes 0..15) and 4..7 (16..31)
 #pragma unroll
-        for (int n = 0; n < 4; n++) sm.zsh[16 * n + r] = sc[n];
+        for (int n = 0; n < 4; n++) sm.zsh[g][16 * n + r] = sc[n];
     }
-    __syncthreads();
+    lds_sync();
 
     // ---- online softmax, lane = token ----
-    const f4v z = sm.zsh[lane] * qscale;       // log2 units
+    const f4v z = (sm.zsh[0][lane] + sm.zsh[1][lane]) * qscale + sm.bsh[lane >> 5];     // log2 units
     float zz[4] = {z[0], z[1], z[2], z[3]};
+    if (nvalid < PT) {                          // uniform: only the prefix's last page
+#pragma unroll
+        for (int i = 0; i < 4; i++)
+            if (lane >= nvalid) zz[i] = -INFINITY;
+    }
     bool exceed = false;
 #pragma unroll
-    for (int i = 0; i < 4; i++) {
-        if (lane >= nvalid) zz[i] = -INFINITY;
-        exceed |= zz[i] > S.m[i] + LAZY_TAU;
-    }
+    for (int i = 0; i < 4; i++) exceed |= zz[i] > S.m[i] + LAZY_TAU;
     if (__any(exceed)) {
         float alpha[4];
 #pragma unroll
@@ -502,19 +523,19 @@ __device__ inline void gqa4_page(const PageRegs &R, Gqa4State &S, Gqa4Smem &sm, 
     for (int i = 0; i < 4; i++) {
         const float pv = __builtin_amdgcn_exp2f(zz[i] - S.m[i]);
         S.lsum[i] += pv;
-        sm.psh[ROWB[i] + lane] = pv;
+        sm.psh[rowb(i) + lane] = pv;
     }
-    __syncthreads();
+    lds_sync();
 
     // ---- P.V on the matrix cores ----
     const uint32_t vd[8] = {R.va.x, R.va.y, R.va.z, R.va.w, R.vb.x, R.vb.y, R.vb.z, R.vb.w};
 #pragma unroll
     for (int ks = 0; ks < 2; ks++) {
         const int t0 = 32 * ks + 8 * g;
-        const float4 pa = *(const float4 *)&sm.psh[ROWB[hp] + t0];
-        const float4 pb = *(const float4 *)&sm.psh[ROWB[hp] + t0 + 4];
-        const uint4 za = *(const uint4 *)&sm.vsT[ROWB[jp] + t0];
-        const uint4 zb = *(const uint4 *)&sm.vsT[ROWB[jp] + t0 + 4];
+        const float4 pa = *(const float4 *)&sm.psh[rb_hp + t0];
+        const float4 pb = *(const float4 *)&sm.psh[rb_hp + t0 + 4];
+        const uint4 za = *(const uint4 *)&sm.vsT[rb_jp + t0];
+        const uint4 zb = *(const uint4 *)&sm.vsT[rb_jp + t0 + 4];
         uint32_t pw[8] = {__builtin_bit_cast(uint32_t, pa.x), __builtin_bit_cast(uint32_t, pa.y),
                           __builtin_bit_cast(uint32_t, pa.z), __builtin_bit_cast(uint32_t, pa.w),
                           __builtin_bit_cast(uint32_t, pb.x), __builtin_bit_cast(uint32_t, pb.y),
@@ -531,20 +552,17 @@ __device__ inline void gqa4_page(const PageRegs &R, Gqa4State &S, Gqa4Smem &sm, 
         }
         float pv[8];
         _Float16 sv[8];
-        h8v bhi, blo;
 #pragma unroll
         for (int e = 0; e < 8; e++) {
             pv[e] = __builtin_bit_cast(float, pw[e]);
             sv[e] = lo16h(se[e]);
             S.zacc = fmaf(pv[e], (float)hi16h(se[e]), S.zacc);
         }
+        uint32_t bh[4], bl[4];
 #pragma unroll
-        for (int e = 0; e < 8; e += 2) {
-            h2v hh, ll;
-            mul_split2(pv[e], sv[e], pv[e + 1], sv[e + 1], hh, ll);
-            bhi[e] = hh.x; bhi[e + 1] = hh.y;
-            blo[e] = ll.x; blo[e + 1] = ll.y;
-        }
+        for (int e = 0; e < 8; e += 2) mul_split2(pv[e], sv[e], pv[e + 1], sv[e + 1], bh[e >> 1], bl[e >> 1]);
+        const h8v bhi = __builtin_bit_cast(h8v, u4v{bh[0], bh[1], bh[2], bh[3]});
+        const h8v blo = __builtin_bit_cast(h8v, u4v{bl[0], bl[1], bl[2], bl[3]});
 #pragma unroll
         for (int nh = 0; nh < 2; nh++) {            // four channel tiles at a time
             h8v af[4];
@@ -569,36 +587,36 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 8))) void
     const int lane = threadIdx.x, g = lane >> 4, r = lane & 15;
     const Geom G = geom(P.scheme);
     const size_t bh = (size_t)b * P.Hkv + h;
+    const int p0 = s * P.split_pages;
+
+    // the length, the split's page ids (one per lane) and the query are
+    // independent loads, issued together
     const int l = P.state[bh * 4];
+    int pid_l = (lane < P.split_pages && p0 + lane < P.max_pages) ? P.table[(size_t)b * P.max_pages + p0 + lane] : 0;
+    // query for this lane's score-operand role (unscaled: keeps q s in the
+    // range where the f16 remainder is a normal number)
+    const int hq = g, c8 = r;
+    const uint16_t *qh = q + ((size_t)b * P.Hq + (size_t)h * 4 + hq) * D;
+    const uint2 q0 = *(const uint2 *)(qh + 4 * c8);
+    const uint2 q1 = *(const uint2 *)(qh + 64 + 4 * c8);
+
     const int nvq = l > P.R ? l - P.R : 0;
     const int npages = (nvq + PT - 1) / PT;
-    const int p0 = s * P.split_pages;
     const int p1 = min(p0 + P.split_pages, npages);
     if (p0 >= p1) return;
     const int np = p1 - p0;                      // <= split_pages <= 64
 
     __shared__ Gqa4Smem sm;
 
-    // page ids of this split, one per lane
-    int pid_l = lane < np ? P.table[(size_t)b * P.max_pages + p0 + lane] : 0;
     const bool bad = lane < np && (pid_l < 0 || pid_l >= P.n_pages);
     if (__any(bad)) {
         if (lane == 0) atomicOr(P.status, (uint32_t)KVQ_STATUS_UNMAPPED_PAGE);
         pid_l = bad ? 0 : pid_l;                 // read page 0 instead; the result is flagged
     }
 
-    // query for this lane's score-operand role (unscaled: keeps q s in the
-    // range where the f16 remainder is a normal number)
-    const int hq = g, c8 = r;
     float qc[8];                                  // channels 4*c8+e, 64+4*c8+e
-    {
-        const uint16_t *qh = q + ((size_t)b * P.Hq + (size_t)h * 4 + hq) * D;
-        const uint2 r0 = *(const uint2 *)(qh + 4 * c8);
-        const uint2 r1 = *(const uint2 *)(qh + 64 + 4 * c8);
-        qc[0] = lo16f(r0.x); qc[1] = hi16f(r0.x); qc[2] = lo16f(r0.y); qc[3] = hi16f(r0.y);
-        qc[4] = lo16f(r1.x); qc[5] = hi16f(r1.x); qc[6] = lo16f(r1.y); qc[7] = hi16f(r1.y);
-    }
-    const int slot0 = 0;
+    qc[0] = lo16f(q0.x); qc[1] = hi16f(q0.x); qc[2] = lo16f(q0.y); qc[3] = hi16f(q0.y);
+    qc[4] = lo16f(q1.x); qc[5] = hi16f(q1.x); qc[6] = lo16f(q1.y); qc[7] = hi16f(q1.y);
     if (lane < 16) {
         sm.As[0][8][lane] = h8v{0, 0, 0, 0, 0, 0, 0, 0};
         sm.As[1][8][lane] = h8v{0, 0, 0, 0, 0, 0, 0, 0};
@@ -614,25 +632,35 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 8))) void
 #pragma unroll
     for (int nt = 0; nt < 8; nt++) S.acc[nt] = f4v{0.f, 0.f, 0.f, 0.f};
 
+    const int rb_hp = rowb(r >> 2), rb_jp = rowb(r & 3);    // this lane's P.V operand rows
     const uint8_t *base = P.pool + (size_t)h * P.page_bytes;
     const size_t pstride = (size_t)P.Hkv * P.page_bytes;
-    // two register sets used in turn: the next page loads while this one is
-    // processed
+    // three register sets used in turn: the two pages after the one being
+    // processed are in flight.  Loads past the split's end are issued too,
+    // with an empty extent.
     auto run_page = [&](const PageRegs &R, int i) {
-        gqa4_page(R, S, sm, qc, slot0, lane, min(PT, nvq - (p0 + i) * PT), qscale);
+        gqa4_page(R, S, sm, qc, lane, min(PT, nvq - (p0 + i) * PT), qscale, rb_hp, rb_jp);
     };
-    auto page_at = [&](int i) {
-        return base + (size_t)__builtin_amdgcn_readlane(pid_l, i) * pstride;
+    auto page_ld = [&](int i) {
+        const uint8_t *pg = base + (size_t)__builtin_amdgcn_readlane(pid_l, min(i, np - 1)) * pstride;
+        return load_page_masked(pg, i < np, G, lane);
     };
-    PageRegs ra = load_page(page_at(0), G, lane);
-    PageRegs rb;
-    for (int i = 0; i < np; i += 2) {
-        if (i + 1 < np) rb = load_page(page_at(i + 1), G, lane);
+    // (scheduling barriers keep each page's loads together and in order, so
+    // the wait before a page counts only the loads of the pages after it)
+    PageRegs ra = page_ld(0);
+    __builtin_amdgcn_sched_barrier(0);
+    PageRegs rb = page_ld(1);
+    __builtin_amdgcn_sched_barrier(0);
+    for (int i = 0; i < np; i += 3) {
+        PageRegs rc = page_ld(i + 2);
+        __builtin_amdgcn_sched_barrier(0);
         run_page(ra, i);
-        if (i + 1 < np) {
-            if (i + 2 < np) ra = load_page(page_at(i + 2), G, lane);
-            run_page(rb, i + 1);
-        }
+        ra = page_ld(i + 3);
+        __builtin_amdgcn_sched_barrier(0);
+        if (i + 1 < np) run_page(rb, i + 1);
+        rb = page_ld(i + 4);
+        __builtin_amdgcn_sched_barrier(0);
+        if (i + 2 < np) run_page(rc, i + 2);
     }
 
     // ---- reduce and write the split's partial ----
