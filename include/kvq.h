@@ -141,11 +141,21 @@ typedef struct kvq_cache {
 } kvq_cache_t;
 
 /* Validate `layout` and `bufs` and fill `cache`.  Host only, synchronous, no
- * device work.  Returns KVQ_OK, KVQ_EINVAL (head_dim != 128; Hq % Hkv != 0;
- * group or value_group != 32; residual % 64 != 0 or outside [64, 1024];
- * block != 256; n_boost not in {0..32} for KITTY; Hkv or layer >= 65536;
- * batch or max_pages or n_pages < 1), KVQ_ENULL or KVQ_EALIGN.
- * The residual must be divisible by the key group ("KIVI" explainer 3.3). */
+ * device work.  Returns KVQ_OK, KVQ_ENULL (cache, layout, bufs or a required
+ * buffer is NULL; boost_idx is required for KITTY only), KVQ_EALIGN (pool not
+ * 256-byte aligned; page_table, state, res_k or res_v not 16-byte aligned;
+ * status not 4-byte aligned) or KVQ_EINVAL when a field is out of range:
+ *   head_dim != 128; n_kv_heads outside [1, 65535]; n_q_heads not a multiple
+ *   of n_kv_heads, or more than 8 query heads per KV head; batch outside
+ *   [1, 65535]; max_pages or n_pages < 1; split_pages outside [0, 64] (0 picks
+ *   a default), or no split of at most 64 pages keeps max_pages within 256
+ *   splits; flags other than KVQ_FLAG_*; unknown scheme;
+ *   KIVI2 / KITTY: group or value_group != 32; residual not a multiple of 64
+ *   or outside [64, 256] (the residual is quantized in whole key groups, so it
+ *   must be divisible by the group, "KIVI" explainer 3.3, and the flush fills
+ *   whole 64-token pages); n_boost != 16 for KITTY or != 0 for KIVI2;
+ *   WITCERT: block != 256; layer >= 65536; query heads per KV head not in
+ *   {1, 2, 4, 8}. */
 int kvq_set_layout(kvq_cache_t *cache, const kvq_layout_t *layout,
                    const kvq_buffers_t *bufs);
 
