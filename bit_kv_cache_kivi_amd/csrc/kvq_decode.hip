@@ -389,12 +389,13 @@ __device__ inline float row_sum16(float v) {
     return v;
 }
 
-// Workgroup barrier that orders LDS only: global loads issued before it (the
-// prefetched pages) stay in flight, where a full barrier would wait for them.
+// LDS ordering for a workgroup of one wave.  The lanes run in lockstep and
+// the LDS serves one wave's accesses in issue order, so keeping the compiler
+// from moving LDS accesses across this point is enough.  Unlike a workgroup
+// barrier with a fence it waits for nothing: the page loads in flight are
+// not waited for.
 __device__ inline void lds_sync() {
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
-    __builtin_amdgcn_s_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+    asm volatile("" ::: "memory");
 }
 
 struct Gqa4State {
@@ -436,11 +437,11 @@ __device__ inline void gqa4_page(const PageRegs &R, Gqa4State &S, Gqa4Smem &sm, 
     lds_sync();
 
     // ---- score operand: hi/lo of q_h * s_c and the zero-point term; this lane
-    // holds channels 4*c8 .. 4*c8+3 and 64+4*c8 .. 64+4*c8+3 of query hq ----
+    // holds channels 8*c8 .. 8*c8+7 (one operand octet) of query hq ----
 #pragma unroll
     for (int gi = 0; gi < 2; gi++) {
-        const uint4 s0 = *(const uint4 *)&sm.kss[128 * gi + 4 * c8];
-        const uint4 s1 = *(const uint4 *)&sm.kss[128 * gi + 64 + 4 * c8];
+        const uint4 s0 = *(const uint4 *)&sm.kss[128 * gi + 8 * c8];
+        const uint4 s1 = *(const uint4 *)&sm.kss[128 * gi + 8 * c8 + 4];
         const uint32_t sz[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
         uint32_t hv[4], lv[4];
         float bias = 0.f;
@@ -450,14 +451,8 @@ __device__ inline void gqa4_page(const PageRegs &R, Gqa4State &S, Gqa4Smem &sm, 
             bias = fmaf(qc[e], (float)hi16h(sz[e]), bias);
             bias = fmaf(qc[e + 1], (float)hi16h(sz[e + 1]), bias);
         }
-        // octet c8>>1 (half c8&1) and octet 8 + (c8>>1) of rows hq and 4+hq
-        uint2 *rh = (uint2 *)&sm.As[gi][hq][0];
-        uint2 *rl = (uint2 *)&sm.As[gi][4 + hq][0];
-        const int o0 = 2 * (c8 >> 1) + (c8 & 1), o1 = 2 * (8 + (c8 >> 1)) + (c8 & 1);
-        rh[o0] = make_uint2(hv[0], hv[1]);
-        rh[o1] = make_uint2(hv[2], hv[3]);
-        rl[o0] = make_uint2(lv[0], lv[1]);
-        rl[o1] = make_uint2(lv[2], lv[3]);
+        sm.As[gi][hq][c8] = __builtin_bit_cast(h8v, u4v{hv[0], hv[1], hv[2], hv[3]});
+        sm.As[gi][4 + hq][c8] = __builtin_bit_cast(h8v, u4v{lv[0], lv[1], lv[2], lv[3]});
         bias = row_sum16(bias);
         if (r == 15) ((float *)&sm.bsh[gi])[hq] = bias * qscale;
     }
@@ -597,8 +592,8 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 8))) void
     // range where the f16 remainder is a normal number)
     const int hq = g, c8 = r;
     const uint16_t *qh = q + ((size_t)b * P.Hq + (size_t)h * 4 + hq) * D;
-    const uint2 q0 = *(const uint2 *)(qh + 4 * c8);
-    const uint2 q1 = *(const uint2 *)(qh + 64 + 4 * c8);
+    const uint2 q0 = *(const uint2 *)(qh + 8 * c8);
+    const uint2 q1 = *(const uint2 *)(qh + 8 * c8 + 4);
 
     const int nvq = l > P.R ? l - P.R : 0;
     const int npages = (nvq + PT - 1) / PT;
@@ -614,7 +609,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 8))) void
         pid_l = bad ? 0 : pid_l;                 // read page 0 instead; the result is flagged
     }
 
-    float qc[8];                                  // channels 4*c8+e, 64+4*c8+e
+    float qc[8];                                  // channels 8*c8+e
     qc[0] = lo16f(q0.x); qc[1] = hi16f(q0.x); qc[2] = lo16f(q0.y); qc[3] = hi16f(q0.y);
     qc[4] = lo16f(q1.x); qc[5] = hi16f(q1.x); qc[6] = lo16f(q1.y); qc[7] = hi16f(q1.y);
     if (lane < 16) {
