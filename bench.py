@@ -49,19 +49,20 @@ def log(msg: str):
 def kivi_bytes(l: int, n_kq: int, R: int, qpk: int, kitty: bool) -> dict:
     n_vq = max(0, l - R)
     kq = 52 if kitty else 48          # codes (+ Kitty high plane) + stats per token
-    stage1 = n_vq * (kq + 48)
+    paged = n_vq * (kq + 48)
     window = (n_kq - n_vq) * kq + (l - n_kq) * 256 + (l - n_vq) * 256
     qo = qpk * (256 + 512)
     table = ((l + 63) // 64) * 4
-    return dict(stage1=stage1, decode=stage1 + window + qo + table)
+    # stage 1 streams the paged prefix and, as one more split, the fp16 window
+    return dict(stage1=paged + window, decode=paged + window + qo + table)
 
 
 def witcert_bytes(l: int, n_q: int, qpk: int) -> dict:
-    stage1 = n_q * 258
+    paged = n_q * 258
     window = (l - n_q) * 512
     qo = qpk * (256 + 512 + 4)
     table = ((l + 255) // 256) * 4
-    return dict(stage1=stage1, decode=stage1 + window + qo + table)
+    return dict(stage1=paged + window, decode=paged + window + qo + table)
 
 
 def write_bytes(w: inputs.Workload, l_before: int, n_kq_before: int) -> int:

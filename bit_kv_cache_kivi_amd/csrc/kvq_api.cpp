@@ -81,6 +81,11 @@ int max_splits(const kvq_cache_t *C) {
     return (C->layout.max_pages + C->split_pages - 1) / C->split_pages;
 }
 
+// 64-token chunks of the fp16 window, each a stage-1 partial of its own
+int n_win(const kvq_cache_t *C) {
+    return C->layout.scheme == KVQ_SCHEME_WITCERT ? kvq::WPT / kvq::PT : C->layout.residual / kvq::PT;
+}
+
 }  // namespace
 
 extern "C" {
@@ -131,7 +136,10 @@ int kvq_set_layout(kvq_cache_t *cache, const kvq_layout_t *layout, const kvq_buf
 
 size_t kvq_workspace_bytes(const kvq_cache_t *cache) {
     if (check_cache(cache) != KVQ_OK) return 0;
-    const size_t rows = (size_t)cache->layout.batch * cache->layout.n_q_heads * max_splits(cache);
+    // one partial row per query head and split, and per 64-token chunk of the
+    // fp16 window
+    const size_t rows =
+        (size_t)cache->layout.batch * cache->layout.n_q_heads * (max_splits(cache) + n_win(cache));
     return rows * kvq::D * sizeof(float) + rows * sizeof(float2) + 256;
 }
 
@@ -163,7 +171,8 @@ int kvq_decode_attention(const kvq_cache_t *cache, const uint16_t *q, float *out
     if (ws_bytes < kvq_workspace_bytes(cache)) return KVQ_EWORKSPACE;
     kvq::Workspace W;
     W.max_splits = max_splits(cache);
-    const size_t rows = (size_t)cache->layout.batch * cache->layout.n_q_heads * W.max_splits;
+    W.n_win = n_win(cache);
+    const size_t rows = (size_t)cache->layout.batch * cache->layout.n_q_heads * (W.max_splits + W.n_win);
     W.o = (float *)workspace;
     W.ml = (float2 *)((char *)workspace + rows * kvq::D * sizeof(float));
     W.ev_begin = cache->ev_stage1_begin;

@@ -43,13 +43,304 @@ __device__ inline float2v cvt2(uint32_t x, int sel) {
 // over g.  Value side: channels 16d + r (d = 0..7) over tokens 32ks + 8g + j;
 // partial outputs are summed over g at the end.
 // ---------------------------------------------------------------------------
+typedef _Float16 h8v __attribute__((ext_vector_type(8)));
+typedef _Float16 h2v __attribute__((ext_vector_type(2)));
+typedef float f4v __attribute__((ext_vector_type(4)));
+typedef uint32_t u4v __attribute__((ext_vector_type(4)));
+
+// Keeps a binary32 value opaque to the optimizer, so every later use sees the
+// same rounded number (no re-derivation of it from its operands).
+__device__ inline float pin(float x) {
+    asm volatile("" : "+v"(x));
+    return x;
+}
+
+// f16 remainder pair of two binary32 values against their packed f16 heads h
+// (one per half): each half is fl16(a - head), formed by the mixed-precision
+// fused multiply-add in one rounding (a - head is exact in binary32).
+__device__ inline uint32_t rem_pair(float a0, float a1, uint32_t h) {
+    uint32_t lo;
+    asm("v_fma_mixlo_f16 %0, %1, -1.0, %2 op_sel_hi:[1,0,0]" : "=&v"(lo) : "v"(h), "v"(a0));
+    asm("v_fma_mixhi_f16 %0, %1, -1.0, %2 op_sel:[1,0,0] op_sel_hi:[1,0,0]" : "+v"(lo) : "v"(h), "v"(a1));
+    return lo;
+}
+
+// LDS ordering for a workgroup of one wave.  The lanes run in lockstep and
+// the LDS serves one wave's accesses in issue order, so keeping the compiler
+// from moving LDS accesses across this point is enough.  Unlike a workgroup
+// barrier with a fence it waits for nothing: the page loads in flight are
+// not waited for.
+__device__ inline void lds_sync() {
+    asm volatile("" ::: "memory");
+}
+
+__device__ inline float half_lo(uint32_t v) { return h2f((uint16_t)(v & 0xffffu)); }
+__device__ inline float half_hi(uint32_t v) { return h2f((uint16_t)(v >> 16)); }
+
+// ---------------------------------------------------------------------------
+// The fp16-value window of one (request, KV head), as one more stage-1
+// partial (row max_splits of each query head).  The window holds the newest
+// values that are not quantized yet: the last R tokens for KIVI2 / KITTY
+// (values are quantized per token as they leave it, keys per group of G
+// tokens when the residual fills; "KIVI" explainer 3.3), the active block for
+// WITCERT.  Keys of window tokens below n_kq are already quantized and are
+// dequantized here; the others come from the fp16 key residual.
+// One wave serves NQ queries of the KV head: lane = token of a 64-token chunk
+// for the scores and the online softmax, lane = channel pair for P.V.
+// ---------------------------------------------------------------------------
+struct WinSmem {
+    uint32_t ks[2][256];        // key {s, z} of the (at most two) pages of the chunk's quantized keys
+    f4v zsh[2][PT];             // scores of the chunk: token -> queries 0..3, 4..7
+    float4 pT[PT][2];           // p of the chunk: token -> queries 0..3, 4..7
+};
+
+// Two binary32 values split into f16 hi + lo (hi cut toward zero, lo the
+// rounded remainder): hi + lo carries each value to within ~2^-22 of it.
+__device__ inline void split_hl(float x0, float x1, uint32_t &hi, uint32_t &lo) {
+    const float a0 = pin(x0), a1 = pin(x1);
+    hi = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(a0, a1));
+    lo = rem_pair(a0, a1, hi);
+}
+
+template <int NQ, int VPF, int SCHEME>
+__device__ void window_partial(const KParams &P, const uint16_t *__restrict__ q, const Workspace &W,
+                               float qscale, int b, int h, int hq0, int wc, int lane, WinSmem &ws) {
+    const Geom G = geom(SCHEME);
+    constexpr bool wit = SCHEME == KVQ_SCHEME_WITCERT;
+    constexpr bool kitty = SCHEME == KVQ_SCHEME_KITTY;
+    const int g = lane >> 4, r = lane & 15;
+    const size_t bh = (size_t)b * P.Hkv + h;
+    const int l = P.state[bh * 4], nkq = P.state[bh * 4 + 1];
+    const int W0 = wit ? nkq : (l > P.R ? l - P.R : 0);        // first fp16-value token
+    const int win = wit ? WPT : P.R;
+    const int t0 = W0 + PT * wc;                                  // this chunk: [t0, t0 + n)
+    const int n = max(0, min(PT, l - t0));
+    const int pA = t0 / PT;
+    const bool anyq = !wit && n > 0 && t0 < nkq;   // uniform: some key of the chunk is still quantized
+
+    // every load the chunk needs is issued first: page ids, values (lane =
+    // channels 2*lane, 2*lane+1; VPF tokens per round) and the query operand
+    int pid_l = -1;
+    if (anyq && lane < 2 && (pA + lane) * PT < min(t0 + n, nkq)) {
+        pid_l = P.table[(size_t)b * P.max_pages + pA + lane];
+        if (pid_l < 0 || pid_l >= P.n_pages) {
+            atomicOr(P.status, (uint32_t)KVQ_STATUS_UNMAPPED_PAGE);
+            pid_l = 0;                            // read page 0 instead; the result is flagged
+        }
+    }
+    uint32_t vv[VPF];
+    auto load_v = [&](int tt0) {
+        int slot = wit ? t0 + tt0 - nkq : (t0 + tt0) % P.R;
+#pragma unroll
+        for (int u = 0; u < VPF; u++) {
+            vv[u] = tt0 + u < n ? *(const uint32_t *)(P.res_v + (bh * win + (size_t)slot) * D + 2 * lane) : 0u;
+            if (++slot == win) slot = 0;          // the value ring wraps (KIVI2 / KITTY)
+        }
+    };
+    load_v(0);
+    // A operand of the score product: row = query (exact in f16), k = channel
+    // 32 kc + 8 g + i; rows NQ..15 are zero
+    h8v aq[4];
+#pragma unroll
+    for (int kc = 0; kc < 4; kc++) {
+        uint4 raw = make_uint4(0u, 0u, 0u, 0u);
+        if (r < NQ) raw = *(const uint4 *)(q + ((size_t)b * P.Hq + hq0 + r) * D + 32 * kc + 8 * g);
+        aq[kc] = __builtin_bit_cast(h8v, raw);
+    }
+    int pids[2] = {-1, -1};
+    if (anyq) {
+        pids[0] = __builtin_amdgcn_readlane(pid_l, 0);
+        pids[1] = __builtin_amdgcn_readlane(pid_l, 1);
+#pragma unroll
+        for (int pi = 0; pi < 2; pi++)
+            if (pids[pi] >= 0) ((uint4 *)ws.ks[pi])[lane] = ((const uint4 *)(cpage(P, pids[pi], h) + G.ks))[lane];
+    }
+    lds_sync();
+
+    // ---- scores on the matrix cores: tile nt = tokens t0 + 16 nt .. + 15;
+    // B lane: token t0 + 16 nt + r, channels 32 kc + 8 g + i ----
+#pragma unroll 1
+    for (int nt = 0; nt < 4; nt++) {
+        f4v sc = f4v{0.f, 0.f, 0.f, 0.f};
+        const int tt = 16 * nt + r, t = t0 + tt;
+        uint4 bh4[4], bl4[4];
+#pragma unroll
+        for (int kc = 0; kc < 4; kc++) {
+            bh4[kc] = make_uint4(0u, 0u, 0u, 0u);
+            bl4[kc] = make_uint4(0u, 0u, 0u, 0u);
+        }
+        if (tt < n) {
+            if (wit || t >= nkq) {                // fp16 key: exact in the operand
+                const uint4 *kr = (const uint4 *)(P.res_k + (bh * win + (size_t)(t - nkq)) * D);
+#pragma unroll
+                for (int kc = 0; kc < 4; kc++) bh4[kc] = kr[4 * kc + g];
+            } else {                              // quantized key: fl32(code s + z), split hi + lo
+                const int pi = t / PT - pA, tp = t % PT, gi = tp >> 5, n16 = tp >> 4;
+                const uint8_t *pg = cpage(P, pi ? pids[1] : pids[0], h);
+                const uint32_t *kcw = (const uint32_t *)(pg + G.kc);
+                uint32_t xa[2];
+#pragma unroll
+                for (int a = 0; a < 2; a++) {
+                    const int d = 2 * n16 + a;
+                    xa[a] = kcw[(d >> 2) * 256 + (16 * g + (tp & 15)) * 4 + (d & 3)];
+                }
+                uint32_t kh[4] = {0u, 0u, 0u, 0u};
+                if (kitty) {
+#pragma unroll
+                    for (int u = 0; u < 4; u++) kh[u] = ((const uint32_t *)(pg + G.kh))[16 * u + (tp & 15)];
+                }
+                const int hsh = 2 * (n16 >> 1) + 16 * (n16 & 1);
+#pragma unroll
+                for (int kc = 0; kc < 4; kc++) {
+                    const uint4 s0 = *(const uint4 *)&ws.ks[pi][128 * gi + 32 * kc + 8 * g];
+                    const uint4 s1 = *(const uint4 *)&ws.ks[pi][128 * gi + 32 * kc + 8 * g + 4];
+                    const uint32_t sz[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
+                    float kf[8];
+#pragma unroll
+                    for (int i = 0; i < 8; i++) {
+                        uint32_t code = (xa[kc >> 1] >> (4 * i + 2 * (kc & 1))) & 3u;
+                        if (kitty) {
+                            const int o = P.boost_idx[(size_t)h * D + 32 * kc + 8 * g + i];
+                            if (o < NB) code |= ((kh[o >> 2] >> (hsh + 4 * (o & 3))) & 3u) << 2;
+                        }
+                        kf[i] = fmaf((float)code, half_lo(sz[i]), half_hi(sz[i]));   // code * s exact
+                    }
+                    uint32_t hv[4], lv[4];
+#pragma unroll
+                    for (int e = 0; e < 4; e++) split_hl(kf[2 * e], kf[2 * e + 1], hv[e], lv[e]);
+                    bh4[kc] = make_uint4(hv[0], hv[1], hv[2], hv[3]);
+                    bl4[kc] = make_uint4(lv[0], lv[1], lv[2], lv[3]);
+                }
+            }
+        }
+#pragma unroll
+        for (int kc = 0; kc < 4; kc++) {
+            sc = __builtin_amdgcn_mfma_f32_16x16x32_f16(aq[kc], __builtin_bit_cast(h8v, bh4[kc]), sc, 0, 0, 0);
+            if (anyq)
+                sc = __builtin_amdgcn_mfma_f32_16x16x32_f16(aq[kc], __builtin_bit_cast(h8v, bl4[kc]), sc, 0, 0, 0);
+        }
+        // C rows 0..3 (queries 0..3) sit in lanes 0..15, rows 4..7 in lanes 16..31
+        if (lane < 16 * ((NQ + 3) / 4)) ws.zsh[g][16 * nt + r] = sc;
+    }
+    lds_sync();
+
+    // ---- softmax over the chunk, lane = token (log2 units) ----
+    float zq[8];
+    {
+        const f4v z0 = ws.zsh[0][lane];
+        zq[0] = z0[0]; zq[1] = z0[1]; zq[2] = z0[2]; zq[3] = z0[3];
+        if (NQ > 4) {
+            const f4v z1 = ws.zsh[1][lane];
+            zq[4] = z1[0]; zq[5] = z1[1]; zq[6] = z1[2]; zq[7] = z1[3];
+        }
+    }
+    float m[NQ], lsum[NQ], pv[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int j = 0; j < NQ; j++) {
+        const float zz = lane < n ? zq[j] * qscale : -INFINITY;
+        float mx = zz;
+#pragma unroll
+        for (int msk = 1; msk < 64; msk <<= 1) mx = fmaxf(mx, shfl_xor(mx, msk));
+        const float p = n > 0 ? __builtin_amdgcn_exp2f(zz - mx) : 0.f;
+        float sum = p;
+#pragma unroll
+        for (int msk = 1; msk < 64; msk <<= 1) sum += shfl_xor(sum, msk);
+        m[j] = mx;
+        lsum[j] = sum;
+        pv[j] = p;
+    }
+    ws.pT[lane][0] = make_float4(pv[0], pv[1], pv[2], pv[3]);
+    if (NQ > 4) ws.pT[lane][1] = make_float4(pv[4], pv[5], pv[6], pv[7]);
+    lds_sync();
+
+    // ---- P.V, lane = channels 2*lane, 2*lane+1 ----
+    float acc[NQ][2];
+#pragma unroll
+    for (int j = 0; j < NQ; j++) acc[j][0] = acc[j][1] = 0.f;
+#pragma unroll 1
+    for (int tt0 = 0; tt0 < n; tt0 += VPF) {
+        if (tt0 > 0) load_v(tt0);
+#pragma unroll
+        for (int u = 0; u < VPF; u++) {
+            const int tt = tt0 + u;
+            if (tt < n) {
+                const float v0 = half_lo(vv[u]), v1 = half_hi(vv[u]);
+                const float4 pa = ws.pT[tt][0];
+                float pq[8] = {pa.x, pa.y, pa.z, pa.w, 0.f, 0.f, 0.f, 0.f};
+                if (NQ > 4) {
+                    const float4 pb = ws.pT[tt][1];
+                    pq[4] = pb.x; pq[5] = pb.y; pq[6] = pb.z; pq[7] = pb.w;
+                }
+#pragma unroll
+                for (int j = 0; j < NQ; j++) {
+                    acc[j][0] = fmaf(pq[j], v0, acc[j][0]);
+                    acc[j][1] = fmaf(pq[j], v1, acc[j][1]);
+                }
+            }
+        }
+    }
+
+    // ---- the chunk's partial (an empty chunk gets lse = -inf) ----
+#pragma unroll
+    for (int j = 0; j < NQ; j++) {
+        const size_t row = part_row(W, P.Hq, b, hq0 + j, W.max_splits + wc);
+        const float il = lsum[j] > 0.f ? 1.0f / lsum[j] : 0.f;
+        *(float2 *)(W.o + row * D + 2 * lane) = make_float2(acc[j][0] * il, acc[j][1] * il);
+        if (lane == 0) W.ml[row] = make_float2(n > 0 ? m[j] + log2f(lsum[j]) : -INFINITY, 1.0f);
+    }
+}
+
+// Work item of a stage-1 workgroup.  The grid has max_splits + n_win items
+// per (head, request); the first heads x requests x n_win items of the
+// dispatch order are the window chunks, so that these start first and
+// overlap the paged splits instead of trailing them.
+struct S1Item {
+    bool window;
+    int s, hd, b;        // s: paged split, or window chunk for a window item
+};
+
+__device__ inline S1Item s1_item(int max_splits, int n_win) {
+    const int nh = gridDim.y, nb = gridDim.z;
+    const int L = blockIdx.x + gridDim.x * (blockIdx.y + nh * blockIdx.z);
+    const int nw = nh * nb * n_win;
+    S1Item it;
+    if (L < nw) {
+        it.window = true;
+        it.s = L % n_win;
+        const int rest = L / n_win;
+        it.hd = rest % nh;
+        it.b = rest / nh;
+    } else {
+        const int L2 = L - nw;
+        it.window = false;
+        it.s = L2 % max_splits;
+        const int rest = L2 / max_splits;
+        it.hd = rest % nh;
+        it.b = rest / nh;
+    }
+    return it;
+}
+
 template <bool KITTY>
 __global__ __launch_bounds__(64) void stage1_valu_kernel(KParams P, const uint16_t *__restrict__ q,
                                                          Workspace W, float qscale) {
-    const int s = blockIdx.x, hq = blockIdx.y, b = blockIdx.z;
+    const S1Item it = s1_item(W.max_splits, W.n_win);
+    const int s = it.s, hq = it.hd, b = it.b;
     const int lane = threadIdx.x, g = lane >> 4, r = lane & 15;
     const int h = hq / P.qpk;
     const Geom G = geom(P.scheme);
+    __shared__ union {
+        struct {
+            uint32_t kss[256];
+            float4 wsh[PT];
+            int inv[NB];
+        } pg;
+        WinSmem win;
+    } U;
+    if (it.window) {                             // this query head's fp16 window
+        window_partial<1, 16, KITTY ? KVQ_SCHEME_KITTY : KVQ_SCHEME_KIVI2>(P, q, W, qscale, b, h, hq, s, lane, U.win);
+        return;
+    }
     const size_t bh = (size_t)b * P.Hkv + h;
     const int l = P.state[bh * 4];
     const int nvq = l > P.R ? l - P.R : 0;
@@ -58,9 +349,9 @@ __global__ __launch_bounds__(64) void stage1_valu_kernel(KParams P, const uint16
     const int p1 = min(p0 + P.split_pages, npages);
     if (p0 >= p1) return;
 
-    __shared__ uint32_t kss[256];
-    __shared__ float4 wsh[PT];
-    __shared__ int inv[NB];
+    uint32_t *kss = U.pg.kss;
+    float4 *wsh = U.pg.wsh;
+    int *inv = U.pg.inv;
 
     const uint16_t *qh = q + ((size_t)b * P.Hq + hq) * D;
     float qv[32];
@@ -258,7 +549,7 @@ __global__ __launch_bounds__(64) void stage1_valu_kernel(KParams P, const uint16
         for (int jv = 0; jv < 4; jv++) zacc[jv] += shfl_xor(zacc[jv], msk);
     }
     const float inv_l = 1.0f / lpart;
-    const size_t row = ((size_t)b * P.Hq + hq) * W.max_splits + s;
+    const size_t row = part_row(W, P.Hq, b, hq, s);
     if (g == 0) {
 #pragma unroll
         for (int d = 0; d < 8; d++) W.o[row * D + 16 * d + r] = (o[d] + zacc[d >> 1]) * inv_l;
@@ -286,9 +577,6 @@ __global__ __launch_bounds__(64) void stage1_valu_kernel(KParams P, const uint16
 // score exceeds m + 8 (log2 units), so p <= 256 and the rescale is rare; the
 // split's lse = m + log2(l) stays exact.
 // ---------------------------------------------------------------------------
-typedef _Float16 h8v __attribute__((ext_vector_type(8)));
-typedef _Float16 h2v __attribute__((ext_vector_type(2)));
-typedef float f4v __attribute__((ext_vector_type(4)));
 
 __device__ inline h2v cvth(uint32_t x, int sel) {
     switch (sel) {
@@ -299,7 +587,6 @@ __device__ inline h2v cvth(uint32_t x, int sel) {
     }
 }
 
-typedef uint32_t u4v __attribute__((ext_vector_type(4)));
 
 // eight codes held in the nibbles of a masked dword -> f16 fragment (k = nibble)
 __device__ inline h8v frag8(uint32_t m) {
@@ -312,23 +599,6 @@ __device__ inline float lo16f(uint32_t v) { return h2f((uint16_t)(v & 0xffffu));
 __device__ inline float hi16f(uint32_t v) { return h2f((uint16_t)(v >> 16)); }
 
 constexpr float LAZY_TAU = 8.0f;
-
-// Keeps a binary32 value opaque to the optimizer, so every later use sees the
-// same rounded number (no re-derivation of it from its operands).
-__device__ inline float pin(float x) {
-    asm volatile("" : "+v"(x));
-    return x;
-}
-
-// f16 remainder pair of two binary32 values against their packed f16 heads h
-// (one per half): each half is fl16(a - head), formed by the mixed-precision
-// fused multiply-add in one rounding (a - head is exact in binary32).
-__device__ inline uint32_t rem_pair(float a0, float a1, uint32_t h) {
-    uint32_t lo;
-    asm("v_fma_mixlo_f16 %0, %1, -1.0, %2 op_sel_hi:[1,0,0]" : "=&v"(lo) : "v"(h), "v"(a0));
-    asm("v_fma_mixhi_f16 %0, %1, -1.0, %2 op_sel:[1,0,0] op_sel_hi:[1,0,0]" : "+v"(lo) : "v"(h), "v"(a1));
-    return lo;
-}
 
 // a = fl32(x * y) for two pairs, split into f16 hi + lo with hi + lo = a to
 // within half an ulp of lo: hi is cut by round-toward-zero in one packed
@@ -387,15 +657,6 @@ __device__ inline float row_sum16(float v) {
     v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0u, __builtin_bit_cast(uint32_t, v), 0x114, 0xf, 0xf, true));
     v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0u, __builtin_bit_cast(uint32_t, v), 0x118, 0xf, 0xf, true));
     return v;
-}
-
-// LDS ordering for a workgroup of one wave.  The lanes run in lockstep and
-// the LDS serves one wave's accesses in issue order, so keeping the compiler
-// from moving LDS accesses across this point is enough.  Unlike a workgroup
-// barrier with a fence it waits for nothing: the page loads in flight are
-// not waited for.
-__device__ inline void lds_sync() {
-    asm volatile("" ::: "memory");
 }
 
 struct Gqa4State {
@@ -578,9 +839,19 @@ __device__ inline void gqa4_page(const PageRegs &R, Gqa4State &S, Gqa4Smem &sm, 
 
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 8))) void stage1_gqa4_mfma_kernel(KParams P, const uint16_t *__restrict__ q,
                                                               Workspace W, float qscale) {
-    const int s = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+    const S1Item it = s1_item(W.max_splits, W.n_win);
+    const int s = it.s, h = it.hd, b = it.b;
     const int lane = threadIdx.x, g = lane >> 4, r = lane & 15;
     const Geom G = geom(P.scheme);
+    __shared__ union {
+        Gqa4Smem pg;
+        WinSmem win;
+    } U;
+    if (it.window) {                             // the KV head's fp16 window
+        window_partial<4, PT, KVQ_SCHEME_KIVI2>(P, q, W, qscale, b, h, 4 * h, s, lane, U.win);
+        return;
+    }
+    Gqa4Smem &sm = U.pg;
     const size_t bh = (size_t)b * P.Hkv + h;
     const int p0 = s * P.split_pages;
 
@@ -600,8 +871,6 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 8))) void
     const int p1 = min(p0 + P.split_pages, npages);
     if (p0 >= p1) return;
     const int np = p1 - p0;                      // <= split_pages <= 64
-
-    __shared__ Gqa4Smem sm;
 
     const bool bad = lane < np && (pid_l < 0 || pid_l >= P.n_pages);
     if (__any(bad)) {
@@ -668,7 +937,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 8))) void
     S.zacc += shfl_xor(S.zacc, 32);
     const float lh = hp == 0 ? S.lsum[0] : hp == 1 ? S.lsum[1] : hp == 2 ? S.lsum[2] : S.lsum[3];
     const float il = 1.0f / lh;
-    const size_t row = ((size_t)b * P.Hq + (size_t)h * 4 + hp) * W.max_splits + s;
+    const size_t row = part_row(W, P.Hq, b, 4 * h + hp, s);
 #pragma unroll
     for (int nt = 0; nt < 8; nt++) {
         if (jp == (nt >> 1)) {
@@ -679,7 +948,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 8))) void
     if (lane < 4) {
         const float li = lane == 0 ? S.lsum[0] : lane == 1 ? S.lsum[1] : lane == 2 ? S.lsum[2] : S.lsum[3];
         const float mi = lane == 0 ? S.m[0] : lane == 1 ? S.m[1] : lane == 2 ? S.m[2] : S.m[3];
-        const size_t row_i = ((size_t)b * P.Hq + (size_t)h * 4 + lane) * W.max_splits + s;
+        const size_t row_i = part_row(W, P.Hq, b, 4 * h + lane, s);
         W.ml[row_i] = make_float2(mi + log2f(li), 1.0f);
     }
 }
@@ -696,9 +965,15 @@ template <int QPK>
 __global__ __launch_bounds__(64) void stage1_witcert_kernel(KParams P, const uint16_t *__restrict__ q,
                                                             Workspace W, float qscale, float sm_scale,
                                                             float kappa) {
-    const int s = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+    const S1Item it = s1_item(W.max_splits, W.n_win);
+    const int s = it.s, h = it.hd, b = it.b;
     const int lane = threadIdx.x, cq = lane & 31, tp = lane >> 5;
     const Geom G = geom(P.scheme);
+    if (it.window) {                             // the KV head's active block (fp16 tail)
+        __shared__ WinSmem win;
+        window_partial<QPK, 16, KVQ_SCHEME_WITCERT>(P, q, W, qscale, b, h, QPK * h, s, lane, win);
+        return;
+    }
     const size_t bh = (size_t)b * P.Hkv + h;
     const int nq = P.state[bh * 4 + 1];
     const int npages = nq / WPT;
@@ -810,7 +1085,7 @@ __global__ __launch_bounds__(64) void stage1_witcert_kernel(KParams P, const uin
             const float mine = o[hh][e] * sa;
             oo[e] = mine + shfl_xor(mine, 32);
         }
-        const size_t row = ((size_t)b * P.Hq + h * QPK + hh) * W.max_splits + s;
+        const size_t row = part_row(W, P.Hq, b, h * QPK + hh, s);
         if (tp == 0) {
             const float il = 1.0f / lt;
             *(float4 *)(W.o + row * D + 4 * cq) = make_float4(oo[0] * il, oo[1] * il, oo[2] * il, oo[3] * il);
@@ -819,240 +1094,58 @@ __global__ __launch_bounds__(64) void stage1_witcert_kernel(KParams P, const uin
     }
 }
 
+constexpr int S2_MAXSPLIT = 256;     // paged splits per query head (kvq_set_layout keeps <= 256)
+
 // ---------------------------------------------------------------------------
-// Stage 2: fp16 window (and 2-bit keys of [n_vq, n_kq)) + LSE merge.
-// One 256-thread block per (KV head, request), all query heads of the group.
+// Stage 2: log-sum-exp merge of one query head's partials (the paged splits
+// and the fp16 window): weights w_s = 2^(lse_s - max), o = sum w_s o_s /
+// sum w_s, and for WITCERT the certificate A = sum w_s A_s / sum w_s (the
+// per-split form of A is exact under this merge; "WitCert" Key structure).
+// One wave per (query head, request); lane = channel pair.
 // ---------------------------------------------------------------------------
-constexpr int S2_MAXQ = 8;
-constexpr int S2_MAXW = 256;
-constexpr int S2_MAXSPLIT = 256;
-
-__device__ inline float key_tilde_page(const KParams &P, const Geom &G, const uint8_t *page,
-                                       int tp, int c, int h) {
-    int dw, sh;
-    key_code_pos(tp, c, dw, sh);
-    uint32_t code = (((const uint32_t *)(page + G.kc))[dw] >> sh) & 3u;
-    const uint32_t sz = ((const uint32_t *)(page + G.ks))[128 * (tp >> 5) + key_stat_slot(c)];
-    if (P.scheme == KVQ_SCHEME_KITTY) {
-        const int o = P.boost_idx[(size_t)h * D + c];
-        if (o < NB) {
-            int dh, shh;
-            high_code_pos(tp, o, dh, shh);
-            code |= ((((const uint32_t *)(page + G.kh))[dh] >> shh) & 3u) << 2;
-        }
-    }
-    const float cs = (float)code * h2f((uint16_t)(sz & 0xffff));
-    return cs + h2f((uint16_t)(sz >> 16));
-}
-
-constexpr int S2_CH = 64;      // window tokens staged per chunk
-
-__global__ __launch_bounds__(256) void stage2_kernel(KParams P, const uint16_t *__restrict__ q,
-                                                    float *__restrict__ out, float *__restrict__ cert,
-                                                    Workspace W, float qscale) {
-    const int h = blockIdx.x, b = blockIdx.y;
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-    const int QPK = P.qpk;
-    const Geom G = geom(P.scheme);
+__global__ __launch_bounds__(64) void merge_kernel(KParams P, float *__restrict__ out,
+                                                   float *__restrict__ cert, Workspace W) {
+    const int hq = blockIdx.x, b = blockIdx.y, lane = threadIdx.x;
     const bool wit = P.scheme == KVQ_SCHEME_WITCERT;
+    const int h = hq / P.qpk;
     const size_t bh = (size_t)b * P.Hkv + h;
     const int l = P.state[bh * 4], nkq = P.state[bh * 4 + 1];
-    const int W0 = wit ? nkq : (l > P.R ? l - P.R : 0);        // first fp16-value token
-    const int nr = l - W0;
-    const int win = wit ? WPT : P.R;
-    const int npages = wit ? nkq / WPT : (W0 + PT - 1) / PT;
+    const int npages = wit ? nkq / WPT : ((l > P.R ? l - P.R : 0) + PT - 1) / PT;
     const int nsplit = (npages + P.split_pages - 1) / P.split_pages;
+    const int ne = nsplit + W.n_win;              // entries nsplit.. are the window chunks
+    const size_t row0 = part_row(W, P.Hq, b, hq, 0);
+    auto row_of = [&](int e) { return row0 + (size_t)(e < nsplit ? e : W.max_splits + e - nsplit); };
 
-    __shared__ float qs[S2_MAXQ][D];
-    __shared__ float kt[S2_CH][D + 1];      // padded: row reads by different lanes hit different banks
-    __shared__ uint16_t vt[S2_CH][D];
-    __shared__ float ps[S2_MAXQ][S2_CH];
-    __shared__ float run_m[S2_MAXQ], run_l[S2_MAXQ], run_a[S2_MAXQ];
-    __shared__ int wpid[8];                 // pages of the 2-bit-key part of the window
-    const int wp0 = W0 / PT;
-    if (tid < 8) {
-        int pid = -1;
-        if (!wit && (wp0 + tid) * PT < nkq) {
-            pid = P.table[(size_t)b * P.max_pages + wp0 + tid];
-            if (pid < 0 || pid >= P.n_pages) {
-                atomicOr(P.status, (uint32_t)KVQ_STATUS_UNMAPPED_PAGE);
-                pid = 0;                         // read page 0 instead; the result is flagged
-            }
-        }
-        wpid[tid] = pid;
+    __shared__ float wsh[S2_MAXSPLIT + WPT / PT];
+    float M = -INFINITY;
+    for (int e = lane; e < ne; e += 64) M = fmaxf(M, W.ml[row_of(e)].x);
+#pragma unroll
+    for (int msk = 1; msk < 64; msk <<= 1) M = fmaxf(M, shfl_xor(M, msk));
+    float ws = 0.f, an = 0.f;
+    for (int e = lane; e < ne; e += 64) {
+        const float2 ml = W.ml[row_of(e)];
+        const float w = M == -INFINITY ? 0.f : exp2f(ml.x - M);
+        wsh[e] = w;
+        ws += w;
+        an = fmaf(w, ml.y, an);
     }
-    for (int i = tid; i < QPK * D; i += 256)
-        qs[i / D][i % D] = h2f(q[((size_t)b * P.Hq + (size_t)h * QPK + i / D) * D + i % D]);
-    if (tid < S2_MAXQ) {
-        run_m[tid] = -INFINITY;
-        run_l[tid] = 0.f;
-        run_a[tid] = 0.f;
+#pragma unroll
+    for (int msk = 1; msk < 64; msk <<= 1) {
+        ws += shfl_xor(ws, msk);
+        an += shfl_xor(an, msk);
     }
-    float acc[S2_MAXQ * D / 256];           // this thread's (query, channel) window outputs
-#pragma unroll
-    for (int k = 0; k < S2_MAXQ * D / 256; k++) acc[k] = 0.f;
-    __syncthreads();
-
-    for (int c0 = 0; c0 < nr; c0 += S2_CH) {
-        const int n = min(S2_CH, nr - c0);
-        // stage values (fp16 rows, 16 B per load) and keys (binary32; dequantized
-        // where still 2-bit) of the chunk
-#pragma unroll
-        for (int k = 0; k < S2_CH * D / 8 / 256; k++) {
-            const int i = tid + 256 * k;
-            const int tt = i / (D / 8), c8 = i % (D / 8);
-            if (tt < n) {
-                const int t = W0 + c0 + tt;
-                const size_t vslot = wit ? (size_t)(t - nkq) : (size_t)(t % P.R);
-                *(uint4 *)&vt[tt][8 * c8] = *(const uint4 *)&P.res_v[(bh * win + vslot) * D + 8 * c8];
-                if (wit || t >= nkq) {
-                    const uint4 kr = *(const uint4 *)&P.res_k[(bh * win + (size_t)(t - nkq)) * D + 8 * c8];
-                    const uint32_t kw[4] = {kr.x, kr.y, kr.z, kr.w};
-#pragma unroll
-                    for (int e = 0; e < 4; e++) {
-                        kt[tt][8 * c8 + 2 * e] = lo16f(kw[e]);
-                        kt[tt][8 * c8 + 2 * e + 1] = hi16f(kw[e]);
-                    }
-                } else {
-                    const uint8_t *page = cpage(P, wpid[t / PT - wp0], h);
-#pragma unroll
-                    for (int e = 0; e < 8; e++)
-                        kt[tt][8 * c8 + e] = key_tilde_page(P, G, page, t % PT, 8 * c8 + e, h);
-                }
-            }
-        }
-        __syncthreads();
-        // scores, thread = (query, token); a wave shares one query
-        for (int i = tid; i < QPK * S2_CH; i += 256) {
-            const int hh = i / S2_CH, tt = i % S2_CH;
-            if (tt < n) {
-                float dot = 0.f;
-#pragma unroll 16
-                for (int c = 0; c < D; c++) dot = fmaf(qs[hh][c], kt[tt][c], dot);
-                ps[hh][tt] = dot * qscale;
-            }
-        }
-        __syncthreads();
-        // online softmax over the window, one wave per query
-        for (int hh = wave; hh < QPK; hh += 4) {
-            const float zv = lane < n ? ps[hh][lane] : -INFINITY;
-            float mx = zv;
-#pragma unroll
-            for (int msk = 1; msk < 64; msk <<= 1) mx = fmaxf(mx, shfl_xor(mx, msk));
-            const float mo = run_m[hh];
-            const float mn = fmaxf(mo, mx);
-            const float pv = lane < n ? exp2f(zv - mn) : 0.f;
-            if (lane < n) ps[hh][lane] = pv;
-            float sum = pv;
-#pragma unroll
-            for (int msk = 1; msk < 64; msk <<= 1) sum += shfl_xor(sum, msk);
-            if (lane == 0) {
-                const float al = exp2f(mo - mn);
-                run_a[hh] = al;
-                run_l[hh] = run_l[hh] * al + sum;
-                run_m[hh] = mn;
-            }
-        }
-        __syncthreads();
-        // window P.V, thread = (query, channel)
-#pragma unroll
-        for (int k = 0; k < S2_MAXQ * D / 256; k++) {
-            const int i = tid + 256 * k;
-            if (i < QPK * D) {
-                const int hh = i / D, c = i % D;
-                float a = acc[k] * run_a[hh];
-#pragma unroll 16
-                for (int tt = 0; tt < n; tt++) a = fmaf(ps[hh][tt], h2f(vt[tt][c]), a);
-                acc[k] = a;
-            }
-        }
-        __syncthreads();
-    }
-
-    // merge the window with the stage-1 splits: log-sum-exp weights once per
-    // (query, split) in shared memory
-    __shared__ float sw[S2_MAXQ][S2_MAXSPLIT];
-    __shared__ float wr_s[S2_MAXQ], wsum_s[S2_MAXQ], anum_s[S2_MAXQ];
-    __shared__ float4 red[256];
-    for (int i = tid; i < QPK * nsplit; i += 256) {
-        const int hh = i / nsplit, sp = i % nsplit;
-        sw[hh][sp] = W.ml[((size_t)b * P.Hq + h * QPK + hh) * W.max_splits + sp].x;
-    }
-    __syncthreads();
-    for (int hh = wave; hh < QPK; hh += 4) {
-        const size_t row0 = ((size_t)b * P.Hq + h * QPK + hh) * W.max_splits;
-        const float lr = run_l[hh], mr = run_m[hh];
-        const float lse_r = nr > 0 ? mr + log2f(lr) : -INFINITY;
-        float M = lse_r;
-        for (int sp = lane; sp < nsplit; sp += 64) M = fmaxf(M, sw[hh][sp]);
-#pragma unroll
-        for (int msk = 1; msk < 64; msk <<= 1) M = fmaxf(M, shfl_xor(M, msk));
-        float ws = 0.f, an = 0.f;
-        for (int sp = lane; sp < nsplit; sp += 64) {
-            const float wv = exp2f(sw[hh][sp] - M);
-            sw[hh][sp] = wv;
-            ws += wv;
-            an = fmaf(wv, W.ml[row0 + sp].y, an);
-        }
-#pragma unroll
-        for (int msk = 1; msk < 64; msk <<= 1) {
-            ws += shfl_xor(ws, msk);
-            an += shfl_xor(an, msk);
-        }
-        if (lane == 0) {
-            const float wr = nr > 0 ? exp2f(lse_r - M) : 0.f;
-            wr_s[hh] = wr;
-            wsum_s[hh] = ws + wr;
-            anum_s[hh] = an + wr;                    // fp16 tokens: u = 0
-        }
-    }
-    // window result of this thread's (query, channel) pairs into the shared output
-    __shared__ float ow[S2_MAXQ][D];
-#pragma unroll
-    for (int k = 0; k < S2_MAXQ * D / 256; k++) {
-        const int i = tid + 256 * k;
-        if (i < QPK * D) ow[i / D][i % D] = nr > 0 ? acc[k] / run_l[i / D] : 0.f;
-    }
-    __syncthreads();
-    // thread = (query, channel quad, split phase): float4 partial rows, all
-    // loads independent
-    const int nq4 = QPK * (D / 4);                   // (query, quad) pairs
-    const int nph = 256 / nq4;                       // split phases per pair (>= 1)
-    float4 part = make_float4(0.f, 0.f, 0.f, 0.f);
-    const int pair = tid % nq4, ph = tid / nq4;
-    const int hh = pair / (D / 4), c4 = pair % (D / 4);
-    if (ph < nph) {
-        const size_t row0 = ((size_t)b * P.Hq + h * QPK + hh) * W.max_splits;
+    lds_sync();
+    float2 acc = make_float2(0.f, 0.f);
 #pragma unroll 8
-        for (int sp = ph; sp < nsplit; sp += nph) {
-            const float4 o4 = *(const float4 *)&W.o[(row0 + sp) * D + 4 * c4];
-            const float wv = sw[hh][sp];
-            part.x = fmaf(wv, o4.x, part.x);
-            part.y = fmaf(wv, o4.y, part.y);
-            part.z = fmaf(wv, o4.z, part.z);
-            part.w = fmaf(wv, o4.w, part.w);
-        }
+    for (int e = 0; e < ne; e++) {
+        const float2 o = *(const float2 *)(W.o + row_of(e) * D + 2 * lane);
+        const float w = wsh[e];
+        acc.x = fmaf(w, o.x, acc.x);
+        acc.y = fmaf(w, o.y, acc.y);
     }
-    red[tid] = part;
-    __syncthreads();
-    if (tid < nq4) {
-        float4 tot = red[tid];
-        for (int k = 1; k < nph; k++) {
-            const float4 v = red[tid + k * nq4];
-            tot.x += v.x; tot.y += v.y; tot.z += v.z; tot.w += v.w;
-        }
-        const int hq = h * QPK + hh;
-        const float wsum = wsum_s[hh], wr = wr_s[hh];
-        const bool any = wsum > 0.f;
-        const float inv = any ? 1.0f / wsum : 0.f;
-        float4 o;
-        o.x = (tot.x + wr * ow[hh][4 * c4 + 0]) * inv;
-        o.y = (tot.y + wr * ow[hh][4 * c4 + 1]) * inv;
-        o.z = (tot.z + wr * ow[hh][4 * c4 + 2]) * inv;
-        o.w = (tot.w + wr * ow[hh][4 * c4 + 3]) * inv;
-        *(float4 *)&out[((size_t)b * P.Hq + hq) * D + 4 * c4] = o;
-        if (cert && c4 == 0) cert[(size_t)b * P.Hq + hq] = any ? anum_s[hh] / wsum : 0.f;
-    }
+    const float inv = ws > 0.f ? 1.0f / ws : 0.f;
+    *(float2 *)(out + ((size_t)b * P.Hq + hq) * D + 2 * lane) = make_float2(acc.x * inv, acc.y * inv);
+    if (cert && lane == 0) cert[(size_t)b * P.Hq + hq] = ws > 0.f ? an / ws : 0.f;
 }
 
 // ---------------------------------------------------------------------------
@@ -1064,7 +1157,7 @@ hipError_t launch_decode(const KParams &P, const uint16_t *q, float *out, float 
         if (e != hipSuccess) return e;
     }
     if (P.scheme == KVQ_SCHEME_WITCERT) {
-        dim3 g1(W.max_splits, P.Hkv, P.B);
+        dim3 g1(W.max_splits + W.n_win, P.Hkv, P.B);  // + the window chunks of each KV head
         switch (P.qpk) {
             case 1: stage1_witcert_kernel<1><<<g1, 64, 0, s>>>(P, q, W, qscale, sm_scale, kappa); break;
             case 2: stage1_witcert_kernel<2><<<g1, 64, 0, s>>>(P, q, W, qscale, sm_scale, kappa); break;
@@ -1073,10 +1166,10 @@ hipError_t launch_decode(const KParams &P, const uint16_t *q, float *out, float 
             default: return hipErrorInvalidValue;
         }
     } else if (P.scheme == KVQ_SCHEME_KIVI2 && P.qpk == 4 && !P.force_generic) {
-        dim3 g1(W.max_splits, P.Hkv, P.B);
+        dim3 g1(W.max_splits + W.n_win, P.Hkv, P.B);
         stage1_gqa4_mfma_kernel<<<g1, 64, 0, s>>>(P, q, W, qscale);
     } else {
-        dim3 g1(W.max_splits, P.Hq, P.B);
+        dim3 g1(W.max_splits + W.n_win, P.Hq, P.B);   // + the window chunks of each query head
         if (P.scheme == KVQ_SCHEME_KITTY)
             stage1_valu_kernel<true><<<g1, 64, 0, s>>>(P, q, W, qscale);
         else
@@ -1088,7 +1181,7 @@ hipError_t launch_decode(const KParams &P, const uint16_t *q, float *out, float 
         e = hipEventRecord(W.ev_end, s);
         if (e != hipSuccess) return e;
     }
-    stage2_kernel<<<dim3(P.Hkv, P.B), 256, 0, s>>>(P, q, out, cert, W, qscale);
+    merge_kernel<<<dim3(P.Hq, P.B), 64, 0, s>>>(P, out, cert, W);
     return hipGetLastError();
 }
 

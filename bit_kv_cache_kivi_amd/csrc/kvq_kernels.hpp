@@ -23,12 +23,22 @@ struct KParams {
 
 // Stage-1 partial results: per (request, query head, split):
 //   o[128] fp32 (acc / l_s), then {lse_s, A_s} fp32 pairs.
+// Stage-1 partials: per query head, rows 0 .. max_splits-1 for the paged
+// splits and rows max_splits .. max_splits+n_win-1 for the 64-token chunks
+// of the fp16 window.
 struct Workspace {
-    float *o;        // [B][Hq][max_splits][128]
-    float2 *ml;      // [B][Hq][max_splits]  (lse in log2 units, A)
+    float *o;        // [B][Hq][max_splits + n_win][128]
+    float2 *ml;      // [B][Hq][max_splits + n_win]  (lse in log2 units, A)
     int max_splits;
+    int n_win;       // window chunks: residual / 64 (KIVI2 / KITTY), 4 (WITCERT)
     hipEvent_t ev_begin, ev_end;   // optional stage-1 timing events
 };
+
+// Row of the partial of query head hq of request b, split s (s >= max_splits:
+// window chunk s - max_splits).
+__host__ __device__ inline size_t part_row(const Workspace &W, int Hq, int b, int hq, int s) {
+    return ((size_t)b * Hq + hq) * (size_t)(W.max_splits + W.n_win) + s;
+}
 
 // write path (kvq_write.hip)
 hipError_t launch_append(const KParams &P, const uint16_t *k, const uint16_t *v, hipStream_t s);

@@ -151,7 +151,8 @@ def test_split_resolution_and_workspace(K):
         rc, cache = set_layout(K, L)
         assert rc == K.KVQ_OK and cache.split_pages == want, (scheme, max_pages)
         splits = -(-max_pages // want)
-        rows = 2 * 8 * splits
+        n_win = 4 if scheme == "witcert" else 128 // 64     # 64-token chunks of the fp16 window
+        rows = 2 * 8 * (splits + n_win)
         assert K.kvq_workspace_bytes(cache) == rows * 128 * 4 + rows * 8 + 256
     L = K.make_layout("kivi2", B=1, Hq=1, Hkv=1, max_pages=16385, n_pages=8)
     assert set_layout(K, L)[0] == K.KVQ_EINVAL          # would need splits of 128 pages
