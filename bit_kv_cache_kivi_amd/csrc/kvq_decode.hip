@@ -1101,7 +1101,7 @@ constexpr int S2_MAXSPLIT = 256;     // paged splits per query head (kvq_set_lay
 // and the fp16 window): weights w_s = 2^(lse_s - max), o = sum w_s o_s /
 // sum w_s, and for WITCERT the certificate A = sum w_s A_s / sum w_s (the
 // per-split form of A is exact under this merge; "WitCert" Key structure).
-// One wave per (query head, request); lane = channel pair.
+// One wave per (query head, request).
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(64) void merge_kernel(KParams P, float *__restrict__ out,
                                                    float *__restrict__ cert, Workspace W) {
@@ -1115,6 +1115,17 @@ __global__ __launch_bounds__(64) void merge_kernel(KParams P, float *__restrict_
     const int ne = nsplit + W.n_win;              // entries nsplit.. are the window chunks
     const size_t row0 = part_row(W, P.Hq, b, hq, 0);
     auto row_of = [&](int e) { return row0 + (size_t)(e < nsplit ? e : W.max_splits + e - nsplit); };
+
+    // output rows: lane = (entry parity ph, channel quad c4); the first 32
+    // entries' loads go out with the log-sum-exp reads
+    constexpr int BATCH = 16;
+    const int ph = lane >> 5, c4 = lane & 31;
+    float4 ov[BATCH];
+#pragma unroll
+    for (int k = 0; k < BATCH; k++) {
+        const int e = ph + 2 * k;
+        ov[k] = e < ne ? *(const float4 *)(W.o + row_of(e) * D + 4 * c4) : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
 
     __shared__ float wsh[S2_MAXSPLIT + WPT / PT];
     float M = -INFINITY;
@@ -1135,16 +1146,33 @@ __global__ __launch_bounds__(64) void merge_kernel(KParams P, float *__restrict_
         an += shfl_xor(an, msk);
     }
     lds_sync();
-    float2 acc = make_float2(0.f, 0.f);
-#pragma unroll 8
-    for (int e = 0; e < ne; e++) {
-        const float2 o = *(const float2 *)(W.o + row_of(e) * D + 2 * lane);
-        const float w = wsh[e];
-        acc.x = fmaf(w, o.x, acc.x);
-        acc.y = fmaf(w, o.y, acc.y);
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int e0 = 0; e0 < ne; e0 += 2 * BATCH) {
+        if (e0 > 0) {
+#pragma unroll
+            for (int k = 0; k < BATCH; k++) {
+                const int e = e0 + ph + 2 * k;
+                ov[k] = e < ne ? *(const float4 *)(W.o + row_of(e) * D + 4 * c4) : make_float4(0.f, 0.f, 0.f, 0.f);
+            }
+        }
+#pragma unroll
+        for (int k = 0; k < BATCH; k++) {
+            const int e = e0 + ph + 2 * k;
+            const float w = e < ne ? wsh[e] : 0.f;
+            acc.x = fmaf(w, ov[k].x, acc.x);
+            acc.y = fmaf(w, ov[k].y, acc.y);
+            acc.z = fmaf(w, ov[k].z, acc.z);
+            acc.w = fmaf(w, ov[k].w, acc.w);
+        }
     }
+    acc.x += shfl_xor(acc.x, 32);
+    acc.y += shfl_xor(acc.y, 32);
+    acc.z += shfl_xor(acc.z, 32);
+    acc.w += shfl_xor(acc.w, 32);
     const float inv = ws > 0.f ? 1.0f / ws : 0.f;
-    *(float2 *)(out + ((size_t)b * P.Hq + hq) * D + 2 * lane) = make_float2(acc.x * inv, acc.y * inv);
+    if (ph == 0)
+        *(float4 *)(out + ((size_t)b * P.Hq + hq) * D + 4 * c4) =
+            make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
     if (cert && lane == 0) cert[(size_t)b * P.Hq + hq] = ws > 0.f ? an / ws : 0.f;
 }
 
