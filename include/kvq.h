@@ -98,7 +98,7 @@ typedef struct kvq_layout {
     int32_t group;           /* G, key group tokens; must be 32 (KIVI2/KITTY) */
     int32_t value_group;     /* value group channels; must be 32 (KIVI2/KITTY) */
     int32_t residual;        /* R, key/value fp16 window; multiple of 64 (so of
-                                G), 64 .. 1024 (KIVI2/KITTY) */
+                                G), 64 .. 256 (KIVI2/KITTY) */
     int32_t block;           /* WitCert block tokens; must be 256 (WITCERT) */
     int32_t n_boost;         /* KITTY boosted key channels: 16 (0 for others) */
     int32_t max_pages;       /* page-table row length per request */
