@@ -837,7 +837,7 @@ __device__ inline void gqa4_page(const PageRegs &R, Gqa4State &S, Gqa4Smem &sm, 
     }
 }
 
-__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 8))) void stage1_gqa4_mfma_kernel(KParams P, const uint16_t *__restrict__ q,
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(3, 8))) void stage1_gqa4_mfma_kernel(KParams P, const uint16_t *__restrict__ q,
                                                               Workspace W, float qscale) {
     const S1Item it = s1_item(W.max_splits, W.n_win);
     const int s = it.s, h = it.hd, b = it.b;
@@ -899,9 +899,10 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 8))) void
     const int rb_hp = rowb(r >> 2), rb_jp = rowb(r & 3);    // this lane's P.V operand rows
     const uint8_t *base = P.pool + (size_t)h * P.page_bytes;
     const size_t pstride = (size_t)P.Hkv * P.page_bytes;
-    // three register sets used in turn: the two pages after the one being
-    // processed are in flight.  Loads past the split's end are issued too,
-    // with an empty extent.
+    // two register sets used in turn: the page after the one being processed
+    // is in flight.  (A deeper ring costs the registers of a third wave per
+    // SIMD, which hides more latency than a second page in flight.)  Loads
+    // past the split's end are issued too, with an empty extent.
     auto run_page = [&](const PageRegs &R, int i) {
         gqa4_page(R, S, sm, qc, lane, min(PT, nvq - (p0 + i) * PT), qscale, rb_hp, rb_jp);
     };
@@ -913,18 +914,13 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 8))) void
     // the wait before a page counts only the loads of the pages after it)
     PageRegs ra = page_ld(0);
     __builtin_amdgcn_sched_barrier(0);
-    PageRegs rb = page_ld(1);
-    __builtin_amdgcn_sched_barrier(0);
-    for (int i = 0; i < np; i += 3) {
-        PageRegs rc = page_ld(i + 2);
+    for (int i = 0; i < np; i += 2) {
+        PageRegs rb = page_ld(i + 1);
         __builtin_amdgcn_sched_barrier(0);
         run_page(ra, i);
-        ra = page_ld(i + 3);
+        ra = page_ld(i + 2);
         __builtin_amdgcn_sched_barrier(0);
         if (i + 1 < np) run_page(rb, i + 1);
-        rb = page_ld(i + 4);
-        __builtin_amdgcn_sched_barrier(0);
-        if (i + 2 < np) run_page(rc, i + 2);
     }
 
     // ---- reduce and write the split's partial ----
