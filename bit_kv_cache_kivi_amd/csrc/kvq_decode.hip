@@ -74,6 +74,20 @@ __device__ inline void lds_sync() {
     asm volatile("" ::: "memory");
 }
 
+// Loads through a buffer descriptor of a page's own extent.  With valid false
+// the extent is zero: the loads return zeros and touch no memory, so a loop
+// can issue them unconditionally (the wait counts stay exact and the
+// prefetched pages stay in flight).
+__device__ inline __amdgpu_buffer_rsrc_t page_rsrc(const uint8_t *page, bool valid, const Geom &G) {
+    return __builtin_amdgcn_make_buffer_rsrc((void *)page, (short)0, valid ? G.bytes : 0, 0x00020000);
+}
+__device__ inline uint4 bload(__amdgpu_buffer_rsrc_t rs, int off) {
+    return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0));
+}
+__device__ inline uint32_t bload1(__amdgpu_buffer_rsrc_t rs, int off) {
+    return __builtin_amdgcn_raw_buffer_load_b32(rs, off, 0, 0);
+}
+
 __device__ inline float half_lo(uint32_t v) { return h2f((uint16_t)(v & 0xffffu)); }
 __device__ inline float half_hi(uint32_t v) { return h2f((uint16_t)(v >> 16)); }
 
@@ -369,12 +383,12 @@ __global__ __launch_bounds__(64) void stage1_valu_kernel(KParams P, const uint16
     int slotb[4] = {0, 0, 0, 0};
     if (KITTY) {
         if (lane < NB) inv[lane] = 0;
-        __syncthreads();
+        lds_sync();
         for (int c = lane; c < D; c += 64) {
             const int o = P.boost_idx[(size_t)h * D + c];
             if (o < NB) inv[o] = c;
         }
-        __syncthreads();
+        lds_sync();
 #pragma unroll
         for (int i = 0; i < 4; i++) {
             const int c = inv[4 * g + i];
@@ -390,24 +404,44 @@ __global__ __launch_bounds__(64) void stage1_valu_kernel(KParams P, const uint16
 #pragma unroll
     for (int d = 0; d < 8; d++) o[d] = 0.f;
 
-    for (int p = p0; p < p1; p++) {
-        const int pid = P.table[(size_t)b * P.max_pages + p];
-        if (pid < 0 || pid >= P.n_pages) {
-            if (lane == 0) atomicOr(P.status, (uint32_t)KVQ_STATUS_UNMAPPED_PAGE);
-            continue;
-        }
-        const uint8_t *page = cpage(P, pid, h);
-        const uint4 *kc4 = (const uint4 *)(page + G.kc);
-        const uint4 *vc4 = (const uint4 *)(page + G.vc);
-        const uint4 ka = kc4[lane], kb = kc4[64 + lane];
-        const uint4 va = vc4[lane], vb = vc4[64 + lane];
-        const uint4 vsz = ((const uint4 *)(page + G.vs))[lane];
-        const uint4 ksz = ((const uint4 *)(page + G.ks))[lane];
-        uint32_t khw = 0;
-        if (KITTY) khw = ((const uint32_t *)(page + G.kh))[lane];
-        __syncthreads();                                 // previous page's LDS reads done
+    // the split's page ids, one per lane (an id outside the pool is flagged
+    // and page 0 read instead)
+    const int np = p1 - p0;                      // <= split_pages <= 64
+    int pid_l = lane < np ? P.table[(size_t)b * P.max_pages + p0 + lane] : 0;
+    const bool bad = lane < np && (pid_l < 0 || pid_l >= P.n_pages);
+    if (__any(bad)) {
+        if (lane == 0) atomicOr(P.status, (uint32_t)KVQ_STATUS_UNMAPPED_PAGE);
+        pid_l = bad ? 0 : pid_l;
+    }
+    const uint8_t *base = P.pool + (size_t)h * P.page_bytes;
+    const size_t pstride = (size_t)P.Hkv * P.page_bytes;
+    struct VPage {
+        uint4 ksz, vsz, ka, kb, va, vb;
+        uint32_t khw;
+    };
+    // two register sets used in turn: the next page loads while this one is
+    // processed (unconditional loads, empty extent past the split's end)
+    auto ldp = [&](int i) {
+        const uint8_t *pg = base + (size_t)__builtin_amdgcn_readlane(pid_l, min(i, np - 1)) * pstride;
+        const __amdgpu_buffer_rsrc_t rs = page_rsrc(pg, i < np, G);
+        const int o = 16 * lane;
+        VPage R;
+        R.ksz = bload(rs, G.ks + o);
+        R.vsz = bload(rs, G.vs + o);
+        R.ka = bload(rs, G.kc + o);
+        R.kb = bload(rs, G.kc + 1024 + o);
+        R.va = bload(rs, G.vc + o);
+        R.vb = bload(rs, G.vc + 1024 + o);
+        R.khw = KITTY ? bload1(rs, G.kh + 4 * lane) : 0u;
+        __builtin_amdgcn_sched_barrier(0);
+        return R;
+    };
+    auto run_page = [&](const VPage &R, int p) {
+        const uint4 ka = R.ka, kb = R.kb, va = R.va, vb = R.vb, vsz = R.vsz, ksz = R.ksz;
+        const uint32_t khw = R.khw;
+        lds_sync();                                 // previous page's LDS reads done
         ((uint4 *)kss)[lane] = ksz;
-        __syncthreads();
+        lds_sync();
 
         // ---- scores --------------------------------------------------------
         const uint32_t kd[8] = {ka.x, ka.y, ka.z, ka.w, kb.x, kb.y, kb.z, kb.w};
@@ -503,7 +537,7 @@ __global__ __launch_bounds__(64) void stage1_valu_kernel(KParams P, const uint16
         wsh[lane] = wv;
 #pragma unroll
         for (int d = 0; d < 8; d++) o[d] *= alpha;
-        __syncthreads();
+        lds_sync();
 
         // ---- P.V -------------------------------------------------------------
         float4 wt[16];
@@ -534,6 +568,13 @@ __global__ __launch_bounds__(64) void stage1_valu_kernel(KParams P, const uint16
             }
             o[d] = acc;
         }
+    };
+    VPage ra = ldp(0);
+    for (int i = 0; i < np; i += 2) {
+        VPage rb = ldp(i + 1);
+        run_page(ra, p0 + i);
+        ra = ldp(i + 2);
+        if (i + 1 < np) run_page(rb, p0 + i + 1);
     }
 
     // ---- reduce and write the split's partial ----------------------------------
@@ -618,27 +659,8 @@ struct PageRegs {
     uint4 ka, kb, va, vb, ks, vs;
 };
 
-__device__ inline PageRegs load_page(const uint8_t *page, const Geom &G, int lane) {
-    PageRegs R;
-    R.ka = ((const uint4 *)(page + G.kc))[lane];
-    R.kb = ((const uint4 *)(page + G.kc))[64 + lane];
-    R.va = ((const uint4 *)(page + G.vc))[lane];
-    R.vb = ((const uint4 *)(page + G.vc))[64 + lane];
-    R.ks = ((const uint4 *)(page + G.ks))[lane];
-    R.vs = ((const uint4 *)(page + G.vs))[lane];
-    return R;
-}
-
-// The same page through a buffer descriptor of the page's own extent.  With
-// valid false the extent is zero: the loads return zeros and touch no memory,
-// so a loop can issue them unconditionally (the wait counts stay exact and
-// the prefetched pages stay in flight).
-__device__ inline uint4 bload(__amdgpu_buffer_rsrc_t rs, int off) {
-    return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0));
-}
 __device__ inline PageRegs load_page_masked(const uint8_t *page, bool valid, const Geom &G, int lane) {
-    const __amdgpu_buffer_rsrc_t rs =
-        __builtin_amdgcn_make_buffer_rsrc((void *)page, (short)0, valid ? G.bytes : 0, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rs = page_rsrc(page, valid, G);
     const int o = 16 * lane;
     PageRegs R;                                 // issued in the order of use
     R.ks = bload(rs, G.ks + o);
@@ -950,6 +972,282 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(3, 8))) void
 }
 
 // ---------------------------------------------------------------------------
+// Stage 1, KIVI2 / KITTY, one query head per wave on the matrix cores (any
+// group size, MHA included).  The same 16x16x32 f16 products as the group
+// kernel, with the one query spread over operand rows and columns instead of
+// four queries:
+//   scores: A row 0 = hi(q s_c), row 1 = lo(q s_c), rows 2..15 zero; lane
+//     (group gi = L >> 5, channels 4 (L & 31) .. +3) forms the four products
+//     of its own key statistics, so the operand costs four products a lane.
+//   Kitty high plane: the 16 boosted channels' hi/lo operands (gathered from
+//     the row-0/1 operand) against the plane's codes, converted with scale 8
+//     so that each f16 is 4 * high; one product per 16-token tile, the A
+//     fragment keeping the nibble half of that tile and zeroing the other.
+//   P.V, transposed: A = value codes (channel rows, token k), B column
+//     (part, j) = hi (part 0) or lo (part 1) of p_t s_{t,j}, columns 8..15
+//     zero; lane = token forms its four products and stores them as f16 rows
+//     [part][group][token] in LDS.  Channel tile nt keeps column nt/2 (hi)
+//     and 4 + nt/2 (lo).
+// ---------------------------------------------------------------------------
+constexpr int BS_STRIDE = 72;       // f16 per P.V operand row (64 tokens + bank skew)
+
+struct HeadSmem {
+    h8v As[2][3][AS_STRIDE];        // score A: [key group][row 0 hi, 1 lo, 2 zero][channel octet]
+    _Float16 Bs[2][4][BS_STRIDE];   // P.V B: [hi, lo][value group][token]
+    h8v Bz;                         // zero fragment for B columns 8..15
+    float zsh[PT];                  // scores, hi + lo rows [token]
+    int inv[NB];                    // Kitty: boosted offset -> channel
+};
+
+__device__ inline h8v frag8_x4(uint32_t m) {     // codes times 4
+    const u4v v = {__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(m, 8.0f, 0)),
+                   __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(m, 8.0f, 1)),
+                   __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(m, 8.0f, 2)),
+                   __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(m, 8.0f, 3))};
+    return __builtin_bit_cast(h8v, v);
+}
+
+struct HeadPage {
+    PageRegs R;
+    uint32_t khw;                   // Kitty high plane, dword = lane
+};
+
+template <bool KITTY>
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(3, 8)))
+void stage1_head_mfma_kernel(KParams P, const uint16_t *__restrict__ q, Workspace W, float qscale) {
+    const S1Item it = s1_item(W.max_splits, W.n_win);
+    const int s = it.s, hq = it.hd, b = it.b;
+    const int lane = threadIdx.x, g = lane >> 4, r = lane & 15;
+    const int h = hq / P.qpk;
+    const Geom G = geom(P.scheme);
+    __shared__ union {
+        HeadSmem pg;
+        WinSmem win;
+    } U;
+    if (it.window) {                             // this query head's fp16 window
+        window_partial<1, 16, KITTY ? KVQ_SCHEME_KITTY : KVQ_SCHEME_KIVI2>(P, q, W, qscale, b, h, hq, s, lane, U.win);
+        return;
+    }
+    HeadSmem &sm = U.pg;
+    const size_t bh = (size_t)b * P.Hkv + h;
+    const int p0 = s * P.split_pages;
+    const int l = P.state[bh * 4];
+    int pid_l = (lane < P.split_pages && p0 + lane < P.max_pages) ? P.table[(size_t)b * P.max_pages + p0 + lane] : 0;
+    // this lane's four channels of the score operand: 4 (lane & 31) .. +3
+    const uint16_t *qh = q + ((size_t)b * P.Hq + hq) * D;
+    const uint2 qraw = *(const uint2 *)(qh + 4 * (lane & 31));
+
+    const int nvq = l > P.R ? l - P.R : 0;
+    const int npages = (nvq + PT - 1) / PT;
+    const int p1 = min(p0 + P.split_pages, npages);
+    if (p0 >= p1) return;
+    const int np = p1 - p0;                      // <= split_pages <= 64
+
+    const bool bad = lane < np && (pid_l < 0 || pid_l >= P.n_pages);
+    if (__any(bad)) {
+        if (lane == 0) atomicOr(P.status, (uint32_t)KVQ_STATUS_UNMAPPED_PAGE);
+        pid_l = bad ? 0 : pid_l;                 // read page 0 instead; the result is flagged
+    }
+    const float qp[4] = {lo16f(qraw.x), hi16f(qraw.x), lo16f(qraw.y), hi16f(qraw.y)};
+
+    if (lane < 16) {
+        sm.As[0][2][lane] = h8v{0, 0, 0, 0, 0, 0, 0, 0};
+        sm.As[1][2][lane] = h8v{0, 0, 0, 0, 0, 0, 0, 0};
+    }
+    if (lane == 0) sm.Bz = h8v{0, 0, 0, 0, 0, 0, 0, 0};
+    int kc_off[4] = {0, 0, 0, 0};                // Kitty: channels of offsets 4g .. 4g+3
+    if (KITTY) {
+        if (lane < NB) sm.inv[lane] = 0;
+        lds_sync();
+        for (int c = lane; c < D; c += 64) {
+            const int o = P.boost_idx[(size_t)h * D + c];
+            if (o < NB) sm.inv[o] = c;
+        }
+        lds_sync();
+#pragma unroll
+        for (int i = 0; i < 4; i++) kc_off[i] = sm.inv[4 * g + i];
+    }
+
+    // operand roles
+    const int gi_p = lane >> 5;                  // key group of this lane's products
+    const int arow = r < 2 ? r : 2;              // score A row read by this lane
+    const _Float16 *bsrc[2];                     // P.V B fragment of this lane, per 32-token step
+#pragma unroll
+    for (int ks = 0; ks < 2; ks++)
+        bsrc[ks] = r < 8 ? &sm.Bs[r >> 2][r & 3][32 * ks + 8 * g] : (const _Float16 *)&sm.Bz;
+
+    float m = -INFINITY, lsum = 0.f;             // lsum: this lane's tokens
+    float zacc[4] = {0.f, 0.f, 0.f, 0.f};        // sum_t p_t z_{t,j}, this lane's tokens
+    f4v acc[8];
+#pragma unroll
+    for (int nt = 0; nt < 8; nt++) acc[nt] = f4v{0.f, 0.f, 0.f, 0.f};
+    const uint32_t MSK = 0x33333333u;
+
+    auto run_page = [&](const HeadPage &HP, int nvalid) {
+        const PageRegs &R = HP.R;
+        lds_sync();                              // previous page done with the LDS
+        // ---- score operand: four products of this lane, hi and lo ----
+        float bias;
+        {
+            const uint32_t sz[4] = {R.ks.x, R.ks.y, R.ks.z, R.ks.w};
+            uint32_t hv[2], lv[2];
+            mul_split2(qp[0], lo16h(sz[0]), qp[1], lo16h(sz[1]), hv[0], lv[0]);
+            mul_split2(qp[2], lo16h(sz[2]), qp[3], lo16h(sz[3]), hv[1], lv[1]);
+            bias = qp[0] * (float)hi16h(sz[0]);
+            bias = fmaf(qp[1], (float)hi16h(sz[1]), bias);
+            bias = fmaf(qp[2], (float)hi16h(sz[2]), bias);
+            bias = fmaf(qp[3], (float)hi16h(sz[3]), bias);
+            ((uint2 *)&sm.As[gi_p][0][0])[lane & 31] = make_uint2(hv[0], hv[1]);
+            ((uint2 *)&sm.As[gi_p][1][0])[lane & 31] = make_uint2(lv[0], lv[1]);
+        }
+        bias = row_sum16(bias);                  // lanes 15, 31, 47, 63
+        const float bias0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, bias), 15)) +
+                            __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, bias), 31));
+        const float bias1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, bias), 47)) +
+                            __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, bias), 63));
+        lds_sync();
+
+        // ---- scores on the matrix cores ----
+        const uint32_t kd[8] = {R.ka.x, R.ka.y, R.ka.z, R.ka.w, R.kb.x, R.kb.y, R.kb.z, R.kb.w};
+        f4v sc[4];
+#pragma unroll
+        for (int n = 0; n < 4; n++) sc[n] = f4v{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kc = 0; kc < 4; kc++) {
+            h8v af[2], bf[4];
+#pragma unroll
+            for (int gi = 0; gi < 2; gi++) af[gi] = sm.As[gi][arow][4 * kc + g];
+#pragma unroll
+            for (int n = 0; n < 4; n++) {
+                const uint32_t x = kd[2 * n + (kc >> 1)];
+                bf[n] = frag8((kc & 1) ? ((x >> 2) & MSK) : (x & MSK));
+            }
+#pragma unroll
+            for (int n = 0; n < 4; n++)
+                sc[n] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[n >> 1], bf[n], sc[n], 0, 0, 0);
+        }
+        if (KITTY) {
+            // tile n: key group n >> 1, plane half n >> 1 (bit 2), nibble half n & 1
+            const h8v bk0 = frag8_x4(HP.khw & MSK), bk1 = frag8_x4((HP.khw >> 2) & MSK);
+#pragma unroll
+            for (int gi = 0; gi < 2; gi++) {
+                const _Float16 *row = (const _Float16 *)&sm.As[gi][arow][0];
+                const _Float16 a0 = row[kc_off[0]], a1 = row[kc_off[1]], a2 = row[kc_off[2]], a3 = row[kc_off[3]];
+                const _Float16 z = 0;
+                const h8v alo = h8v{a0, a1, a2, a3, z, z, z, z};
+                const h8v ahi = h8v{z, z, z, z, a0, a1, a2, a3};
+                const h8v bk = gi ? bk1 : bk0;
+                sc[2 * gi] = __builtin_amdgcn_mfma_f32_16x16x32_f16(alo, bk, sc[2 * gi], 0, 0, 0);
+                sc[2 * gi + 1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ahi, bk, sc[2 * gi + 1], 0, 0, 0);
+            }
+        }
+        if (lane < 16) {                         // rows 0 (hi) and 1 (lo) of each token tile
+#pragma unroll
+            for (int n = 0; n < 4; n++) sm.zsh[16 * n + r] = sc[n][0] + sc[n][1];
+        }
+        lds_sync();
+
+        // ---- online softmax, lane = token ----
+        float zt = sm.zsh[lane] * qscale + (lane < 32 ? bias0 : bias1) * qscale;     // log2 units
+        if (lane >= nvalid) zt = -INFINITY;
+        if (__any(zt > m + LAZY_TAU)) {
+            float mt = zt;
+#pragma unroll
+            for (int msk = 1; msk < 64; msk <<= 1) mt = fmaxf(mt, shfl_xor(mt, msk));
+            const float mn = fmaxf(m, mt);
+            const float alpha = __builtin_amdgcn_exp2f(m - mn);
+            m = mn;
+            lsum *= alpha;
+#pragma unroll
+            for (int j = 0; j < 4; j++) zacc[j] *= alpha;
+#pragma unroll
+            for (int nt = 0; nt < 8; nt++) acc[nt] *= alpha;
+        }
+        const float pt = __builtin_amdgcn_exp2f(zt - m);                 // 0 past nvalid
+        lsum += pt;
+
+        // ---- P.V operand: p_t s_{t,j}, hi and lo, lane = token ----
+        {
+            // statistics past nvalid are not written yet: use zero
+            const uint32_t keep = lane < nvalid ? 0xffffffffu : 0u;
+            const uint32_t vw[4] = {R.vs.x & keep, R.vs.y & keep, R.vs.z & keep, R.vs.w & keep};
+#pragma unroll
+            for (int j = 0; j < 4; j++) zacc[j] = fmaf(pt, (float)hi16h(vw[j]), zacc[j]);
+            uint32_t hv[2], lv[2];
+            mul_split2(pt, lo16h(vw[0]), pt, lo16h(vw[1]), hv[0], lv[0]);
+            mul_split2(pt, lo16h(vw[2]), pt, lo16h(vw[3]), hv[1], lv[1]);
+            sm.Bs[0][0][lane] = lo16h(hv[0]);
+            sm.Bs[0][1][lane] = hi16h(hv[0]);
+            sm.Bs[0][2][lane] = lo16h(hv[1]);
+            sm.Bs[0][3][lane] = hi16h(hv[1]);
+            sm.Bs[1][0][lane] = lo16h(lv[0]);
+            sm.Bs[1][1][lane] = hi16h(lv[0]);
+            sm.Bs[1][2][lane] = lo16h(lv[1]);
+            sm.Bs[1][3][lane] = hi16h(lv[1]);
+        }
+        lds_sync();
+
+        // ---- P.V on the matrix cores ----
+        const uint32_t vd[8] = {R.va.x, R.va.y, R.va.z, R.va.w, R.vb.x, R.vb.y, R.vb.z, R.vb.w};
+#pragma unroll
+        for (int ks = 0; ks < 2; ks++) {
+            const h8v bfr = *(const h8v *)bsrc[ks];
+#pragma unroll
+            for (int nt = 0; nt < 8; nt++) {
+                const uint32_t x = vd[nt];
+                const h8v afr = frag8(ks ? ((x >> 2) & MSK) : (x & MSK));
+                acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(afr, bfr, acc[nt], 0, 0, 0);
+            }
+        }
+    };
+
+    const uint8_t *base = P.pool + (size_t)h * P.page_bytes;
+    const size_t pstride = (size_t)P.Hkv * P.page_bytes;
+    auto page_ld = [&](int i) {
+        const uint8_t *pg = base + (size_t)__builtin_amdgcn_readlane(pid_l, min(i, np - 1)) * pstride;
+        HeadPage HP;
+        HP.R = load_page_masked(pg, i < np, G, lane);
+        HP.khw = KITTY ? bload1(page_rsrc(pg, i < np, G), G.kh + 4 * lane) : 0u;
+        return HP;
+    };
+    // two register sets used in turn (the page after the one being processed
+    // is in flight); loads past the split's end are issued with an empty extent
+    HeadPage ra = page_ld(0);
+    __builtin_amdgcn_sched_barrier(0);
+    for (int i = 0; i < np; i += 2) {
+        HeadPage rb = page_ld(i + 1);
+        __builtin_amdgcn_sched_barrier(0);
+        run_page(ra, min(PT, nvq - (p0 + i) * PT));
+        ra = page_ld(i + 2);
+        __builtin_amdgcn_sched_barrier(0);
+        if (i + 1 < np) run_page(rb, min(PT, nvq - (p0 + i + 1) * PT));
+    }
+
+    // ---- reduce and write the split's partial ----
+#pragma unroll
+    for (int msk = 1; msk < 64; msk <<= 1) lsum += shfl_xor(lsum, msk);
+#pragma unroll
+    for (int j = 0; j < 4; j++)
+#pragma unroll
+        for (int msk = 1; msk < 64; msk <<= 1) zacc[j] += shfl_xor(zacc[j], msk);
+    const float il = 1.0f / lsum;
+    const size_t row = part_row(W, P.Hq, b, hq, s);
+#pragma unroll
+    for (int nt = 0; nt < 8; nt++) {
+        f4v lo;                                   // column 4 + j, four lanes up
+#pragma unroll
+        for (int i = 0; i < 4; i++) lo[i] = __shfl_down(acc[nt][i], 4, 16);
+        const int jv = nt >> 1;
+        if (r == jv) {
+            const float zj = jv == 0 ? zacc[0] : jv == 1 ? zacc[1] : jv == 2 ? zacc[2] : zacc[3];
+            const f4v o = (acc[nt] + lo + zj) * il;
+            *(float4 *)(W.o + row * D + 16 * nt + 4 * g) = make_float4(o[0], o[1], o[2], o[3]);
+        }
+    }
+    if (lane == 0) W.ml[row] = make_float2(m + log2f(lsum), 1.0f);
+}
+
+// ---------------------------------------------------------------------------
 // Stage 1, WITCERT: INT8 codes with the Philox dither regenerated in the
 // kernel, and the certificate accumulated next to the output.  One wave per
 // (split, KV head, request) serves all QPK query heads of the KV head, so each
@@ -1194,10 +1492,18 @@ hipError_t launch_decode(const KParams &P, const uint16_t *q, float *out, float 
         stage1_gqa4_mfma_kernel<<<g1, 64, 0, s>>>(P, q, W, qscale);
     } else {
         dim3 g1(W.max_splits + W.n_win, P.Hq, P.B);   // + the window chunks of each query head
-        if (P.scheme == KVQ_SCHEME_KITTY)
-            stage1_valu_kernel<true><<<g1, 64, 0, s>>>(P, q, W, qscale);
-        else
-            stage1_valu_kernel<false><<<g1, 64, 0, s>>>(P, q, W, qscale);
+        const bool kitty = P.scheme == KVQ_SCHEME_KITTY;
+        if (P.force_generic) {
+            if (kitty)
+                stage1_valu_kernel<true><<<g1, 64, 0, s>>>(P, q, W, qscale);
+            else
+                stage1_valu_kernel<false><<<g1, 64, 0, s>>>(P, q, W, qscale);
+        } else {
+            if (kitty)
+                stage1_head_mfma_kernel<true><<<g1, 64, 0, s>>>(P, q, W, qscale);
+            else
+                stage1_head_mfma_kernel<false><<<g1, 64, 0, s>>>(P, q, W, qscale);
+        }
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;

@@ -64,8 +64,9 @@ enum {
 
 /* layout flags */
 enum {
-    KVQ_FLAG_GENERIC_STAGE1 = 1  /* run the per-query-head VALU stage 1 even where
-                                    a matrix-core stage 1 exists (comparison) */
+    KVQ_FLAG_GENERIC_STAGE1 = 1  /* KIVI2 / KITTY: run the per-query-head VALU
+                                    stage 1 instead of the matrix-core one
+                                    (a second implementation, for comparison) */
 };
 
 /* host-side return codes */

@@ -50,9 +50,10 @@ def _check_decode(case, out, cert, q, kappa=0.0, cert_check=False):
     return worst
 
 
-@pytest.mark.parametrize("Hq,Hkv,flags", [(2, 2, 0), (8, 2, 0), (8, 2, 1), (16, 4, 0)])
+@pytest.mark.parametrize("Hq,Hkv,flags", [(2, 2, 0), (2, 2, 1), (8, 2, 0), (8, 2, 1), (16, 4, 0), (6, 3, 0)])
 def test_kivi_prefill_decode_small(Hq, Hkv, flags):
-    # (8, 2, 0): matrix-core GQA stage 1; (8, 2, 1): the generic VALU stage 1
+    # flags 0: matrix-core stage 1 (group of 4: one wave per KV head; other
+    # group sizes: one wave per query head); flags 1: the VALU stage 1
     w = inputs.workload(3, B=3, Hq=Hq, Hkv=Hkv, ctx=(700, 1301, 2113), steps=3)
     case = _case(w, extra_tokens=300, split_pages=4, flags=flags)
     case.check_status()
@@ -99,9 +100,10 @@ def test_kivi_short_contexts(ctx):
     case.check_store()
 
 
-def test_kitty_calibrate_store_decode():
+@pytest.mark.parametrize("flags", [0, 1])
+def test_kitty_calibrate_store_decode(flags):
     w = inputs.workload(4, B=2, Hq=2, Hkv=2, ctx=(1100, 1500))
-    case = _case(w, extra_tokens=200, split_pages=3)
+    case = _case(w, extra_tokens=200, split_pages=3, flags=flags)
     idx_gpu = case.cache.boost_idx.cpu().numpy()
     assert np.array_equal(idx_gpu, case.idx)
     case.check_state()
