@@ -609,11 +609,14 @@ __global__ __launch_bounds__(64) void stage1_valu_kernel(KParams P, const uint16
 //   B is the page's key codes, exact in f16 (2-bit code c in a nibble is the
 //   fp4 value c/2, scaled by 2 on conversion).  The accumulator starts at
 //   sum_c q_h z_c; rows h and h+4 are added afterwards.
-// P.V, transposed: O^T[c][(h,j)] = sum_t code_{t,c} (p_{h,t} s_{t,j}), A =
-//   value codes (channel rows, token columns), B columns = (query h, value
-//   group j): all 16 columns carry data; hi and lo parts of p s are two
-//   products into one accumulator; column (h, j) is kept for channels of
-//   group j.  sum_t p_{h,t} z_{t,j} is accumulated on the side.
+// P.V, transposed: O^T[c][col] = sum_t code_{t,c} B[t][col], A = value codes
+//   (channel rows, token columns).  Channel tile nt (16 channels) lies in
+//   value group j = nt / 2; B column (query h, part, js) holds the hi (part
+//   0) or lo (part 1) half of p_{h,t} s_{t,j} with j = js for tiles 0..3 and
+//   j = 2 + js for tiles 4..7, so one product per tile and 32-token step
+//   carries both halves of all four queries; columns (h, 0, js) and
+//   (h, 1, js) are added at the end.  sum_t p_{h,t} z_{t,j} is accumulated
+//   on the side.
 // Online softmax with lazy rescaling: the running maximum m moves only when a
 // score exceeds m + 8 (log2 units), so p <= 256 and the rescale is rare; the
 // split's lse = m + log2(l) stays exact.
@@ -684,7 +687,7 @@ __device__ inline float row_sum16(float v) {
 struct Gqa4State {
     float m[4];
     float lsum[4];
-    float zacc;
+    float zacc[2];                  // sum_t p_{h,t} z_{t,j}, j = js and 2 + js of this lane's column
     f4v acc[8];
 };
 
@@ -704,8 +707,8 @@ struct Gqa4Smem {
 };
 
 // One 64-token page.  nvalid < 64 only on the last page of the prefix.
-__device__ inline void gqa4_page(const PageRegs &R, Gqa4State &S, Gqa4Smem &sm, const float *qc,
-                                 int lane, int nvalid, float qscale, int rb_hp, int rb_jp) {
+__device__ inline void gqa4_page(const PageRegs &R, Gqa4State &S, Gqa4Smem &sm, const _Float16 *qc,
+                                 int lane, int nvalid, float qscale, int rb_h, int rb_j0, int rb_j1) {
     const int g = lane >> 4, r = lane & 15;
     const int hq = g, c8 = r;
     const int hp = r >> 2;
@@ -730,9 +733,9 @@ __device__ inline void gqa4_page(const PageRegs &R, Gqa4State &S, Gqa4Smem &sm, 
         float bias = 0.f;
 #pragma unroll
         for (int e = 0; e < 8; e += 2) {
-            mul_split2(qc[e], lo16h(sz[e]), qc[e + 1], lo16h(sz[e + 1]), hv[e >> 1], lv[e >> 1]);
-            bias = fmaf(qc[e], (float)hi16h(sz[e]), bias);
-            bias = fmaf(qc[e + 1], (float)hi16h(sz[e + 1]), bias);
+            mul_split2((float)qc[e], lo16h(sz[e]), (float)qc[e + 1], lo16h(sz[e + 1]), hv[e >> 1], lv[e >> 1]);
+            bias = fmaf((float)qc[e], (float)hi16h(sz[e]), bias);
+            bias = fmaf((float)qc[e + 1], (float)hi16h(sz[e + 1]), bias);
         }
         sm.As[gi][hq][c8] = __builtin_bit_cast(h8v, u4v{hv[0], hv[1], hv[2], hv[3]});
         sm.As[gi][4 + hq][c8] = __builtin_bit_cast(h8v, u4v{lv[0], lv[1], lv[2], lv[3]});
@@ -751,17 +754,15 @@ __device__ inline void gqa4_page(const PageRegs &R, Gqa4State &S, Gqa4Smem &sm, 
     const int arow = r < 8 ? r : 8;
 #pragma unroll
     for (int kc = 0; kc < 4; kc++) {
-        h8v af[2], bf[4];
+        h8v af[2];
 #pragma unroll
         for (int gi = 0; gi < 2; gi++) af[gi] = sm.As[gi][arow][r < 8 ? 4 * kc + g : 0];
 #pragma unroll
         for (int n = 0; n < 4; n++) {
             const uint32_t x = kd[2 * n + (kc >> 1)];
-            bf[n] = frag8((kc & 1) ? ((x >> 2) & MSK) : (x & MSK));
+            const h8v bf = frag8((kc & 1) ? ((x >> 2) & MSK) : (x & MSK));
+            sc[n] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[n >> 1], bf, sc[n], 0, 0, 0);
         }
-#pragma unroll
-        for (int n = 0; n < 4; n++)
-            sc[n] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[n >> 1], bf[n], sc[n], 0, 0, 0);
     }
     if (lane < 32) {                            // rows 0..3 (lanes 0..15) and 4..7 (16..31)
 #pragma unroll
@@ -787,13 +788,16 @@ __device__ inline void gqa4_page(const PageRegs &R, Gqa4State &S, Gqa4Smem &sm, 
             float mt = zz[i];
 #pragma unroll
             for (int msk = 1; msk < 64; msk <<= 1) mt = fmaxf(mt, shfl_xor(mt, msk));
+            // the same in every lane: kept in a scalar register
+            mt = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, mt)));
             const float mn = fmaxf(S.m[i], mt);
             alpha[i] = __builtin_amdgcn_exp2f(S.m[i] - mn);
             S.m[i] = mn;
             S.lsum[i] *= alpha[i];
         }
         const float ap = hp == 0 ? alpha[0] : hp == 1 ? alpha[1] : hp == 2 ? alpha[2] : alpha[3];
-        S.zacc *= ap;
+        S.zacc[0] *= ap;
+        S.zacc[1] *= ap;
 #pragma unroll
         for (int nt = 0; nt < 8; nt++) S.acc[nt] *= ap;
     }
@@ -805,56 +809,57 @@ __device__ inline void gqa4_page(const PageRegs &R, Gqa4State &S, Gqa4Smem &sm, 
     }
     lds_sync();
 
-    // ---- P.V on the matrix cores ----
+    // ---- P.V on the matrix cores: B column r = (query h, part, js) carries
+    // the hi (part 0) or lo (part 1) half of p_{h,t} s_{t,j} for value group
+    // j = js (channel tiles 0..3) or j = 2 + js (tiles 4..7); one product per
+    // tile gives both halves ----
     const uint32_t vd[8] = {R.va.x, R.va.y, R.va.z, R.va.w, R.vb.x, R.vb.y, R.vb.z, R.vb.w};
+    const bool lo_part = (lane >> 1) & 1;
 #pragma unroll
     for (int ks = 0; ks < 2; ks++) {
         const int t0 = 32 * ks + 8 * g;
-        const float4 pa = *(const float4 *)&sm.psh[rb_hp + t0];
-        const float4 pb = *(const float4 *)&sm.psh[rb_hp + t0 + 4];
-        const uint4 za = *(const uint4 *)&sm.vsT[rb_jp + t0];
-        const uint4 zb = *(const uint4 *)&sm.vsT[rb_jp + t0 + 4];
+        const float4 pa = *(const float4 *)&sm.psh[rb_h + t0];
+        const float4 pb = *(const float4 *)&sm.psh[rb_h + t0 + 4];
         uint32_t pw[8] = {__builtin_bit_cast(uint32_t, pa.x), __builtin_bit_cast(uint32_t, pa.y),
                           __builtin_bit_cast(uint32_t, pa.z), __builtin_bit_cast(uint32_t, pa.w),
                           __builtin_bit_cast(uint32_t, pb.x), __builtin_bit_cast(uint32_t, pb.y),
                           __builtin_bit_cast(uint32_t, pb.z), __builtin_bit_cast(uint32_t, pb.w)};
-        uint32_t se[8] = {za.x, za.y, za.z, za.w, zb.x, zb.y, zb.z, zb.w};
+        const int nv = nvalid - t0;                  // valid tokens of this lane's eight
         if (nvalid < PT) {                           // uniform: only the prefix's last page
 #pragma unroll
-            for (int e = 0; e < 8; e++) {
-                // statistics past nvalid are not written yet: zero p, s and z
-                const uint32_t keep = (t0 + e < nvalid) ? 0xffffffffu : 0u;
-                pw[e] &= keep;
-                se[e] &= keep;
-            }
+            for (int e = 0; e < 8; e++) pw[e] &= (e < nv) ? 0xffffffffu : 0u;
         }
         float pv[8];
-        _Float16 sv[8];
 #pragma unroll
-        for (int e = 0; e < 8; e++) {
-            pv[e] = __builtin_bit_cast(float, pw[e]);
-            sv[e] = lo16h(se[e]);
-            S.zacc = fmaf(pv[e], (float)hi16h(se[e]), S.zacc);
-        }
-        uint32_t bh[4], bl[4];
+        for (int e = 0; e < 8; e++) pv[e] = __builtin_bit_cast(float, pw[e]);
 #pragma unroll
-        for (int e = 0; e < 8; e += 2) mul_split2(pv[e], sv[e], pv[e + 1], sv[e + 1], bh[e >> 1], bl[e >> 1]);
-        const h8v bhi = __builtin_bit_cast(h8v, u4v{bh[0], bh[1], bh[2], bh[3]});
-        const h8v blo = __builtin_bit_cast(h8v, u4v{bl[0], bl[1], bl[2], bl[3]});
+        for (int js2 = 0; js2 < 2; js2++) {
+            const int rb = js2 ? rb_j1 : rb_j0;
+            const uint4 za = *(const uint4 *)&sm.vsT[rb + t0];
+            const uint4 zb = *(const uint4 *)&sm.vsT[rb + t0 + 4];
+            uint32_t se[8] = {za.x, za.y, za.z, za.w, zb.x, zb.y, zb.z, zb.w};
+            if (nvalid < PT) {
+                // statistics past nvalid are not written yet: zero s and z
 #pragma unroll
-        for (int nh = 0; nh < 2; nh++) {            // four channel tiles at a time
-            h8v af[4];
+                for (int e = 0; e < 8; e++) se[e] &= (e < nv) ? 0xffffffffu : 0u;
+            }
+            _Float16 sv[8];
+#pragma unroll
+            for (int e = 0; e < 8; e++) {
+                sv[e] = lo16h(se[e]);
+                S.zacc[js2] = fmaf(pv[e], (float)hi16h(se[e]), S.zacc[js2]);
+            }
+            uint32_t bh[4], bl[4];
+#pragma unroll
+            for (int e = 0; e < 8; e += 2) mul_split2(pv[e], sv[e], pv[e + 1], sv[e + 1], bh[e >> 1], bl[e >> 1]);
+            const h8v bv = __builtin_bit_cast(h8v, lo_part ? u4v{bl[0], bl[1], bl[2], bl[3]} : u4v{bh[0], bh[1], bh[2], bh[3]});
 #pragma unroll
             for (int u = 0; u < 4; u++) {
-                const uint32_t x = vd[4 * nh + u];
-                af[u] = frag8(ks ? ((x >> 2) & MSK) : (x & MSK));
+                const int nt = 4 * js2 + u;
+                const uint32_t x = vd[nt];
+                const h8v af = frag8(ks ? ((x >> 2) & MSK) : (x & MSK));
+                S.acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af, bv, S.acc[nt], 0, 0, 0);
             }
-#pragma unroll
-            for (int u = 0; u < 4; u++)
-                S.acc[4 * nh + u] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[u], bhi, S.acc[4 * nh + u], 0, 0, 0);
-#pragma unroll
-            for (int u = 0; u < 4; u++)
-                S.acc[4 * nh + u] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[u], blo, S.acc[4 * nh + u], 0, 0, 0);
         }
     }
 }
@@ -900,9 +905,9 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(3, 8))) void
         pid_l = bad ? 0 : pid_l;                 // read page 0 instead; the result is flagged
     }
 
-    float qc[8];                                  // channels 8*c8+e
-    qc[0] = lo16f(q0.x); qc[1] = hi16f(q0.x); qc[2] = lo16f(q0.y); qc[3] = hi16f(q0.y);
-    qc[4] = lo16f(q1.x); qc[5] = hi16f(q1.x); qc[6] = lo16f(q1.y); qc[7] = hi16f(q1.y);
+    _Float16 qc[8];                               // channels 8*c8+e (kept as f16: half the registers)
+    qc[0] = lo16h(q0.x); qc[1] = hi16h(q0.x); qc[2] = lo16h(q0.y); qc[3] = hi16h(q0.y);
+    qc[4] = lo16h(q1.x); qc[5] = hi16h(q1.x); qc[6] = lo16h(q1.y); qc[7] = hi16h(q1.y);
     if (lane < 16) {
         sm.As[0][8][lane] = h8v{0, 0, 0, 0, 0, 0, 0, 0};
         sm.As[1][8][lane] = h8v{0, 0, 0, 0, 0, 0, 0, 0};
@@ -914,11 +919,14 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(3, 8))) void
         S.m[i] = -INFINITY;
         S.lsum[i] = 0.f;
     }
-    S.zacc = 0.f;
+    S.zacc[0] = 0.f;
+    S.zacc[1] = 0.f;
 #pragma unroll
     for (int nt = 0; nt < 8; nt++) S.acc[nt] = f4v{0.f, 0.f, 0.f, 0.f};
 
-    const int rb_hp = rowb(r >> 2), rb_jp = rowb(r & 3);    // this lane's P.V operand rows
+    // this lane's P.V operand rows: p of query r >> 2, {s, z} of groups r & 1 and 2 + (r & 1)
+    static_assert(rowb(2) - rowb(0) == rowb(3) - rowb(1), "value rows 2, 3 at one offset from rows 0, 1");
+    const int rb_h = rowb(r >> 2), rb_j0 = rowb(r & 1), rb_j1 = rb_j0 + (rowb(2) - rowb(0));
     const uint8_t *base = P.pool + (size_t)h * P.page_bytes;
     const size_t pstride = (size_t)P.Hkv * P.page_bytes;
     // two register sets used in turn: the page after the one being processed
@@ -926,7 +934,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(3, 8))) void
     // SIMD, which hides more latency than a second page in flight.)  Loads
     // past the split's end are issued too, with an empty extent.
     auto run_page = [&](const PageRegs &R, int i) {
-        gqa4_page(R, S, sm, qc, lane, min(PT, nvq - (p0 + i) * PT), qscale, rb_hp, rb_jp);
+        gqa4_page(R, S, sm, qc, lane, min(PT, nvq - (p0 + i) * PT), qscale, rb_h, rb_j0, rb_j1);
     };
     auto page_ld = [&](int i) {
         const uint8_t *pg = base + (size_t)__builtin_amdgcn_readlane(pid_l, min(i, np - 1)) * pstride;
@@ -946,20 +954,26 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(3, 8))) void
     }
 
     // ---- reduce and write the split's partial ----
-    const int hp = r >> 2, jp = r & 3;
+    const int hp = r >> 2, part = (r >> 1) & 1, js = r & 1;
 #pragma unroll
     for (int i = 0; i < 4; i++)
 #pragma unroll
         for (int msk = 1; msk < 64; msk <<= 1) S.lsum[i] += shfl_xor(S.lsum[i], msk);
-    S.zacc += shfl_xor(S.zacc, 16);
-    S.zacc += shfl_xor(S.zacc, 32);
+#pragma unroll
+    for (int k = 0; k < 2; k++) {
+        S.zacc[k] += shfl_xor(S.zacc[k], 16);
+        S.zacc[k] += shfl_xor(S.zacc[k], 32);
+    }
     const float lh = hp == 0 ? S.lsum[0] : hp == 1 ? S.lsum[1] : hp == 2 ? S.lsum[2] : S.lsum[3];
     const float il = 1.0f / lh;
     const size_t row = part_row(W, P.Hq, b, 4 * h + hp, s);
 #pragma unroll
     for (int nt = 0; nt < 8; nt++) {
-        if (jp == (nt >> 1)) {
-            const f4v o = (S.acc[nt] + S.zacc) * il;
+        f4v lo;                                   // the lo column, two lanes up
+#pragma unroll
+        for (int i = 0; i < 4; i++) lo[i] = __shfl_down(S.acc[nt][i], 2, 16);
+        if (part == 0 && js == ((nt >> 1) & 1)) {
+            const f4v o = (S.acc[nt] + lo + S.zacc[nt >> 2]) * il;
             *(float4 *)(W.o + row * D + 16 * nt + 4 * g) = make_float4(o[0], o[1], o[2], o[3]);
         }
     }
