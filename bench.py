@@ -342,7 +342,7 @@ def main():
     s1_avg_ms = float(np.mean(s1_ms))
     s1_gbs = float(np.mean(s1_bytes)) / (s1_avg_ms * 1e-3) / 1e9
     kernel = ("stage1_witcert" if w.scheme == "witcert" else
-              "stage1_gqa4_mfma" if (w.scheme == "kivi2" and w.group == 4) else "stage1_valu")
+              "stage1_gqa4_mfma" if (w.scheme == "kivi2" and w.group == 4) else "stage1_head_mfma")
     if w.scheme == "witcert":
         # integer-ALU bound: Philox4x32-10 calls (one per token, channel quad
         # and side of every quantized block) x 100 integer ops per call (10
