@@ -687,28 +687,32 @@ __device__ inline float row_sum16(float v) {
 struct Gqa4State {
     float m[4];
     float lsum[4];
-    float zacc[2];                  // sum_t p_{h,t} z_{t,j}, j = js and 2 + js of this lane's column
+    float zacc[4][4];               // sum_t p_{h,t} z_{t,j} over this lane's tokens [query][group]
     f4v acc[8];
 };
 
-// Rows of p [query][token] and value {s, z} [group][token] start at offsets
-// rowb(row) so that the 16 (row, token octet) pairs read together by a P.V
-// operand load fall on 64 distinct LDS banks.
-__host__ __device__ constexpr int rowb(int i) { return i == 0 ? 0 : i == 1 ? 68 : i == 2 ? 160 : 228; }
 constexpr int AS_STRIDE = 20;       // octets per score-operand row (16 + bank padding)
 
+// f16 per P.V operand column row: 64 tokens + 8, so that the 16 columns read
+// by one 16-lane group of an operand load start on 16 distinct 4-bank groups
+constexpr int BT_STRIDE = 72;
+
+// The key statistics, the scores and the P.V operand are live in turn within
+// a page step (one wave: LDS accesses complete in program order), so they
+// share storage; 10.4 KB per wave keeps twelve waves per compute unit.
 struct Gqa4Smem {
-    f4v zsh[2][PT];                 // scores from the hi and the lo operand rows [token][query]
     f4v bsh[2];                     // zero-point term times qscale [key group][query]
-    float psh[292];                 // p, row i at rowb(i)
-    uint32_t vsT[292];              // value {s, z}, row j at rowb(j)
-    uint32_t kss[256];              // key {s, z} [group][channel]
     h8v As[2][9][AS_STRIDE];        // score A: [key group][row 0..3 hi, 4..7 lo, 8 = zero][channel octet]
+    union {
+        uint32_t kss[256];              // key {s, z} [group][channel]
+        f4v zsh[2][PT];                 // scores from the hi and the lo operand rows [token][query]
+        _Float16 Bs[2][16][BT_STRIDE];  // P.V B: [operand][column (h, part, js)][token]
+    };
 };
 
 // One 64-token page.  nvalid < 64 only on the last page of the prefix.
 __device__ inline void gqa4_page(const PageRegs &R, Gqa4State &S, Gqa4Smem &sm, const _Float16 *qc,
-                                 int lane, int nvalid, float qscale, int rb_h, int rb_j0, int rb_j1) {
+                                 int lane, int nvalid, float qscale) {
     const int g = lane >> 4, r = lane & 15;
     const int hq = g, c8 = r;
     const int hp = r >> 2;
@@ -716,10 +720,6 @@ __device__ inline void gqa4_page(const PageRegs &R, Gqa4State &S, Gqa4Smem &sm, 
 
     lds_sync();                            // previous page done with the LDS
     ((uint4 *)sm.kss)[lane] = R.ks;
-    sm.vsT[rowb(0) + lane] = R.vs.x;
-    sm.vsT[rowb(1) + lane] = R.vs.y;
-    sm.vsT[rowb(2) + lane] = R.vs.z;
-    sm.vsT[rowb(3) + lane] = R.vs.w;
     lds_sync();
 
     // ---- score operand: hi/lo of q_h * s_c and the zero-point term; this lane
@@ -796,66 +796,60 @@ __device__ inline void gqa4_page(const PageRegs &R, Gqa4State &S, Gqa4Smem &sm, 
             S.lsum[i] *= alpha[i];
         }
         const float ap = hp == 0 ? alpha[0] : hp == 1 ? alpha[1] : hp == 2 ? alpha[2] : alpha[3];
-        S.zacc[0] *= ap;
-        S.zacc[1] *= ap;
+#pragma unroll
+        for (int i = 0; i < 4; i++)
+#pragma unroll
+            for (int j = 0; j < 4; j++) S.zacc[i][j] *= alpha[i];
 #pragma unroll
         for (int nt = 0; nt < 8; nt++) S.acc[nt] *= ap;
     }
+    float pq[4];                                // p of this lane's token, per query
 #pragma unroll
     for (int i = 0; i < 4; i++) {
-        const float pv = __builtin_amdgcn_exp2f(zz[i] - S.m[i]);
-        S.lsum[i] += pv;
-        sm.psh[rowb(i) + lane] = pv;
+        pq[i] = __builtin_amdgcn_exp2f(zz[i] - S.m[i]);
+        S.lsum[i] += pq[i];
+    }
+
+    // ---- P.V operand, lane = token: p_{h,t} s_{t,j} split into f16 hi and
+    // lo, stored as the B columns (h, part, js) of operand j >> 1 (j = 2 (j >> 1)
+    // + js); sum_t p_{h,t} z_{t,j} on the side ----
+    {
+        uint32_t vw[4] = {R.vs.x, R.vs.y, R.vs.z, R.vs.w};
+        if (nvalid < PT) {                      // uniform: statistics past nvalid are not written yet
+#pragma unroll
+            for (int j = 0; j < 4; j++) vw[j] &= lane < nvalid ? 0xffffffffu : 0u;
+        }
+#pragma unroll
+        for (int h = 0; h < 4; h++) {
+#pragma unroll
+            for (int j = 0; j < 4; j++) S.zacc[h][j] = fmaf(pq[h], (float)hi16h(vw[j]), S.zacc[h][j]);
+            uint32_t h01, l01, h23, l23;
+            mul_split2(pq[h], lo16h(vw[0]), pq[h], lo16h(vw[1]), h01, l01);
+            mul_split2(pq[h], lo16h(vw[2]), pq[h], lo16h(vw[3]), h23, l23);
+            sm.Bs[0][4 * h + 0][lane] = lo16h(h01);
+            sm.Bs[0][4 * h + 1][lane] = hi16h(h01);
+            sm.Bs[0][4 * h + 2][lane] = lo16h(l01);
+            sm.Bs[0][4 * h + 3][lane] = hi16h(l01);
+            sm.Bs[1][4 * h + 0][lane] = lo16h(h23);
+            sm.Bs[1][4 * h + 1][lane] = hi16h(h23);
+            sm.Bs[1][4 * h + 2][lane] = lo16h(l23);
+            sm.Bs[1][4 * h + 3][lane] = hi16h(l23);
+        }
     }
     lds_sync();
 
-    // ---- P.V on the matrix cores: B column r = (query h, part, js) carries
-    // the hi (part 0) or lo (part 1) half of p_{h,t} s_{t,j} for value group
-    // j = js (channel tiles 0..3) or j = 2 + js (tiles 4..7); one product per
-    // tile gives both halves ----
+    // ---- P.V on the matrix cores: channel tiles 0..3 (value groups 0, 1)
+    // take operand 0, tiles 4..7 (groups 2, 3) operand 1; one product per tile
+    // and 32-token step carries both halves of all four queries ----
     const uint32_t vd[8] = {R.va.x, R.va.y, R.va.z, R.va.w, R.vb.x, R.vb.y, R.vb.z, R.vb.w};
-    const bool lo_part = (lane >> 1) & 1;
 #pragma unroll
     for (int ks = 0; ks < 2; ks++) {
-        const int t0 = 32 * ks + 8 * g;
-        const float4 pa = *(const float4 *)&sm.psh[rb_h + t0];
-        const float4 pb = *(const float4 *)&sm.psh[rb_h + t0 + 4];
-        uint32_t pw[8] = {__builtin_bit_cast(uint32_t, pa.x), __builtin_bit_cast(uint32_t, pa.y),
-                          __builtin_bit_cast(uint32_t, pa.z), __builtin_bit_cast(uint32_t, pa.w),
-                          __builtin_bit_cast(uint32_t, pb.x), __builtin_bit_cast(uint32_t, pb.y),
-                          __builtin_bit_cast(uint32_t, pb.z), __builtin_bit_cast(uint32_t, pb.w)};
-        const int nv = nvalid - t0;                  // valid tokens of this lane's eight
-        if (nvalid < PT) {                           // uniform: only the prefix's last page
 #pragma unroll
-            for (int e = 0; e < 8; e++) pw[e] &= (e < nv) ? 0xffffffffu : 0u;
-        }
-        float pv[8];
-#pragma unroll
-        for (int e = 0; e < 8; e++) pv[e] = __builtin_bit_cast(float, pw[e]);
-#pragma unroll
-        for (int js2 = 0; js2 < 2; js2++) {
-            const int rb = js2 ? rb_j1 : rb_j0;
-            const uint4 za = *(const uint4 *)&sm.vsT[rb + t0];
-            const uint4 zb = *(const uint4 *)&sm.vsT[rb + t0 + 4];
-            uint32_t se[8] = {za.x, za.y, za.z, za.w, zb.x, zb.y, zb.z, zb.w};
-            if (nvalid < PT) {
-                // statistics past nvalid are not written yet: zero s and z
-#pragma unroll
-                for (int e = 0; e < 8; e++) se[e] &= (e < nv) ? 0xffffffffu : 0u;
-            }
-            _Float16 sv[8];
-#pragma unroll
-            for (int e = 0; e < 8; e++) {
-                sv[e] = lo16h(se[e]);
-                S.zacc[js2] = fmaf(pv[e], (float)hi16h(se[e]), S.zacc[js2]);
-            }
-            uint32_t bh[4], bl[4];
-#pragma unroll
-            for (int e = 0; e < 8; e += 2) mul_split2(pv[e], sv[e], pv[e + 1], sv[e + 1], bh[e >> 1], bl[e >> 1]);
-            const h8v bv = __builtin_bit_cast(h8v, lo_part ? u4v{bl[0], bl[1], bl[2], bl[3]} : u4v{bh[0], bh[1], bh[2], bh[3]});
+        for (int o = 0; o < 2; o++) {
+            const h8v bv = *(const h8v *)&sm.Bs[o][r][32 * ks + 8 * g];
 #pragma unroll
             for (int u = 0; u < 4; u++) {
-                const int nt = 4 * js2 + u;
+                const int nt = 4 * o + u;
                 const uint32_t x = vd[nt];
                 const h8v af = frag8(ks ? ((x >> 2) & MSK) : (x & MSK));
                 S.acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af, bv, S.acc[nt], 0, 0, 0);
@@ -919,14 +913,13 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(3, 8))) void
         S.m[i] = -INFINITY;
         S.lsum[i] = 0.f;
     }
-    S.zacc[0] = 0.f;
-    S.zacc[1] = 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; i++)
+#pragma unroll
+        for (int j = 0; j < 4; j++) S.zacc[i][j] = 0.f;
 #pragma unroll
     for (int nt = 0; nt < 8; nt++) S.acc[nt] = f4v{0.f, 0.f, 0.f, 0.f};
 
-    // this lane's P.V operand rows: p of query r >> 2, {s, z} of groups r & 1 and 2 + (r & 1)
-    static_assert(rowb(2) - rowb(0) == rowb(3) - rowb(1), "value rows 2, 3 at one offset from rows 0, 1");
-    const int rb_h = rowb(r >> 2), rb_j0 = rowb(r & 1), rb_j1 = rb_j0 + (rowb(2) - rowb(0));
     const uint8_t *base = P.pool + (size_t)h * P.page_bytes;
     const size_t pstride = (size_t)P.Hkv * P.page_bytes;
     // two register sets used in turn: the page after the one being processed
@@ -934,7 +927,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(3, 8))) void
     // SIMD, which hides more latency than a second page in flight.)  Loads
     // past the split's end are issued too, with an empty extent.
     auto run_page = [&](const PageRegs &R, int i) {
-        gqa4_page(R, S, sm, qc, lane, min(PT, nvq - (p0 + i) * PT), qscale, rb_h, rb_j0, rb_j1);
+        gqa4_page(R, S, sm, qc, lane, min(PT, nvq - (p0 + i) * PT), qscale);
     };
     auto page_ld = [&](int i) {
         const uint8_t *pg = base + (size_t)__builtin_amdgcn_readlane(pid_l, min(i, np - 1)) * pstride;
@@ -960,10 +953,11 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(3, 8))) void
 #pragma unroll
         for (int msk = 1; msk < 64; msk <<= 1) S.lsum[i] += shfl_xor(S.lsum[i], msk);
 #pragma unroll
-    for (int k = 0; k < 2; k++) {
-        S.zacc[k] += shfl_xor(S.zacc[k], 16);
-        S.zacc[k] += shfl_xor(S.zacc[k], 32);
-    }
+    for (int i = 0; i < 4; i++)
+#pragma unroll
+        for (int j = 0; j < 4; j++)
+#pragma unroll
+            for (int msk = 1; msk < 64; msk <<= 1) S.zacc[i][j] += shfl_xor(S.zacc[i][j], msk);
     const float lh = hp == 0 ? S.lsum[0] : hp == 1 ? S.lsum[1] : hp == 2 ? S.lsum[2] : S.lsum[3];
     const float il = 1.0f / lh;
     const size_t row = part_row(W, P.Hq, b, 4 * h + hp, s);
@@ -973,7 +967,9 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(3, 8))) void
 #pragma unroll
         for (int i = 0; i < 4; i++) lo[i] = __shfl_down(S.acc[nt][i], 2, 16);
         if (part == 0 && js == ((nt >> 1) & 1)) {
-            const f4v o = (S.acc[nt] + lo + S.zacc[nt >> 2]) * il;
+            const int j = nt >> 1;
+            const float zj = hp == 0 ? S.zacc[0][j] : hp == 1 ? S.zacc[1][j] : hp == 2 ? S.zacc[2][j] : S.zacc[3][j];
+            const f4v o = (S.acc[nt] + lo + zj) * il;
             *(float4 *)(W.o + row * D + 16 * nt + 4 * g) = make_float4(o[0], o[1], o[2], o[3]);
         }
     }
