@@ -697,50 +697,48 @@ constexpr int AS_STRIDE = 20;       // octets per score-operand row (16 + bank p
 // by one 16-lane group of an operand load start on 16 distinct 4-bank groups
 constexpr int BT_STRIDE = 72;
 
-// The key statistics, the scores and the P.V operand are live in turn within
-// a page step (one wave: LDS accesses complete in program order), so they
-// share storage; 10.4 KB per wave keeps twelve waves per compute unit.
+// The scores and the P.V operand are live in turn within a page step (one
+// wave: LDS accesses complete in program order), so they share storage.
 struct Gqa4Smem {
-    f4v bsh[2];                     // zero-point term times qscale [key group][query]
     h8v As[2][9][AS_STRIDE];        // score A: [key group][row 0..3 hi, 4..7 lo, 8 = zero][channel octet]
     union {
-        uint32_t kss[256];              // key {s, z} [group][channel]
         f4v zsh[2][PT];                 // scores from the hi and the lo operand rows [token][query]
         _Float16 Bs[2][16][BT_STRIDE];  // P.V B: [operand][column (h, part, js)][token]
     };
 };
 
 // One 64-token page.  nvalid < 64 only on the last page of the prefix.
-__device__ inline void gqa4_page(const PageRegs &R, Gqa4State &S, Gqa4Smem &sm, const _Float16 *qc,
+__device__ inline void gqa4_page(const PageRegs &R, Gqa4State &S, Gqa4Smem &sm, const uint2 *qw,
                                  int lane, int nvalid, float qscale) {
     const int g = lane >> 4, r = lane & 15;
-    const int hq = g, c8 = r;
     const int hp = r >> 2;
     const uint32_t MSK = 0x33333333u;
 
     lds_sync();                            // previous page done with the LDS
-    ((uint4 *)sm.kss)[lane] = R.ks;
-    lds_sync();
 
-    // ---- score operand: hi/lo of q_h * s_c and the zero-point term; this lane
-    // holds channels 8*c8 .. 8*c8+7 (one operand octet) of query hq ----
+    // ---- score operand from the lane's own key statistics (key group
+    // lane >> 5, channels 4 (lane & 31) .. +3): hi/lo of q_h s_c for the four
+    // queries, and the zero-point sums, added over the group's 32 lanes ----
+    const int gi_p = lane >> 5;
+    const uint32_t sz[4] = {R.ks.x, R.ks.y, R.ks.z, R.ks.w};
+    float bias0[4], bias1[4];              // [query] for key groups 0 and 1, times qscale
 #pragma unroll
-    for (int gi = 0; gi < 2; gi++) {
-        const uint4 s0 = *(const uint4 *)&sm.kss[128 * gi + 8 * c8];
-        const uint4 s1 = *(const uint4 *)&sm.kss[128 * gi + 8 * c8 + 4];
-        const uint32_t sz[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
-        uint32_t hv[4], lv[4];
-        float bias = 0.f;
+    for (int h = 0; h < 4; h++) {
+        const _Float16 qe[4] = {lo16h(qw[h].x), hi16h(qw[h].x), lo16h(qw[h].y), hi16h(qw[h].y)};
+        uint32_t hv0, lv0, hv1, lv1;
+        mul_split2((float)qe[0], lo16h(sz[0]), (float)qe[1], lo16h(sz[1]), hv0, lv0);
+        mul_split2((float)qe[2], lo16h(sz[2]), (float)qe[3], lo16h(sz[3]), hv1, lv1);
+        ((uint2 *)&sm.As[gi_p][h][0])[lane & 31] = make_uint2(hv0, hv1);
+        ((uint2 *)&sm.As[gi_p][4 + h][0])[lane & 31] = make_uint2(lv0, lv1);
+        float bz = (float)qe[0] * (float)hi16h(sz[0]);
 #pragma unroll
-        for (int e = 0; e < 8; e += 2) {
-            mul_split2((float)qc[e], lo16h(sz[e]), (float)qc[e + 1], lo16h(sz[e + 1]), hv[e >> 1], lv[e >> 1]);
-            bias = fmaf((float)qc[e], (float)hi16h(sz[e]), bias);
-            bias = fmaf((float)qc[e + 1], (float)hi16h(sz[e + 1]), bias);
-        }
-        sm.As[gi][hq][c8] = __builtin_bit_cast(h8v, u4v{hv[0], hv[1], hv[2], hv[3]});
-        sm.As[gi][4 + hq][c8] = __builtin_bit_cast(h8v, u4v{lv[0], lv[1], lv[2], lv[3]});
-        bias = row_sum16(bias);
-        if (r == 15) ((float *)&sm.bsh[gi])[hq] = bias * qscale;
+        for (int e = 1; e < 4; e++) bz = fmaf((float)qe[e], (float)hi16h(sz[e]), bz);
+        bz = row_sum16(bz);                // row totals in lanes 15, 31, 47, 63
+        const int bzi = __builtin_bit_cast(int, bz);
+        bias0[h] = (__builtin_bit_cast(float, __builtin_amdgcn_readlane(bzi, 15)) +
+                    __builtin_bit_cast(float, __builtin_amdgcn_readlane(bzi, 31))) * qscale;
+        bias1[h] = (__builtin_bit_cast(float, __builtin_amdgcn_readlane(bzi, 47)) +
+                    __builtin_bit_cast(float, __builtin_amdgcn_readlane(bzi, 63))) * qscale;
     }
     lds_sync();
 
@@ -771,7 +769,9 @@ __device__ inline void gqa4_page(const PageRegs &R, Gqa4State &S, Gqa4Smem &sm, 
     lds_sync();
 
     // ---- online softmax, lane = token ----
-    const f4v z = (sm.zsh[0][lane] + sm.zsh[1][lane]) * qscale + sm.bsh[lane >> 5];     // log2 units
+    const bool g1 = lane >= 32;                 // token in key group 1
+    const f4v bz4 = g1 ? f4v{bias1[0], bias1[1], bias1[2], bias1[3]} : f4v{bias0[0], bias0[1], bias0[2], bias0[3]};
+    const f4v z = (sm.zsh[0][lane] + sm.zsh[1][lane]) * qscale + bz4;     // log2 units
     float zz[4] = {z[0], z[1], z[2], z[3]};
     if (nvalid < PT) {                          // uniform: only the prefix's last page
 #pragma unroll
@@ -880,12 +880,12 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(3, 8))) void
     // independent loads, issued together
     const int l = P.state[bh * 4];
     int pid_l = (lane < P.split_pages && p0 + lane < P.max_pages) ? P.table[(size_t)b * P.max_pages + p0 + lane] : 0;
-    // query for this lane's score-operand role (unscaled: keeps q s in the
-    // range where the f16 remainder is a normal number)
-    const int hq = g, c8 = r;
-    const uint16_t *qh = q + ((size_t)b * P.Hq + (size_t)h * 4 + hq) * D;
-    const uint2 q0 = *(const uint2 *)(qh + 8 * c8);
-    const uint2 q1 = *(const uint2 *)(qh + 8 * c8 + 4);
+    // the four queries at this lane's score-operand channels 4 (lane & 31) .. +3
+    // (unscaled: keeps q s in the range where the f16 remainder is a normal number)
+    uint2 qw[4];
+#pragma unroll
+    for (int hq = 0; hq < 4; hq++)
+        qw[hq] = *(const uint2 *)(q + ((size_t)b * P.Hq + (size_t)h * 4 + hq) * D + 4 * (lane & 31));
 
     const int nvq = l > P.R ? l - P.R : 0;
     const int npages = (nvq + PT - 1) / PT;
@@ -899,9 +899,6 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(3, 8))) void
         pid_l = bad ? 0 : pid_l;                 // read page 0 instead; the result is flagged
     }
 
-    _Float16 qc[8];                               // channels 8*c8+e (kept as f16: half the registers)
-    qc[0] = lo16h(q0.x); qc[1] = hi16h(q0.x); qc[2] = lo16h(q0.y); qc[3] = hi16h(q0.y);
-    qc[4] = lo16h(q1.x); qc[5] = hi16h(q1.x); qc[6] = lo16h(q1.y); qc[7] = hi16h(q1.y);
     if (lane < 16) {
         sm.As[0][8][lane] = h8v{0, 0, 0, 0, 0, 0, 0, 0};
         sm.As[1][8][lane] = h8v{0, 0, 0, 0, 0, 0, 0, 0};
@@ -927,7 +924,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(3, 8))) void
     // SIMD, which hides more latency than a second page in flight.)  Loads
     // past the split's end are issued too, with an empty extent.
     auto run_page = [&](const PageRegs &R, int i) {
-        gqa4_page(R, S, sm, qc, lane, min(PT, nvq - (p0 + i) * PT), qscale);
+        gqa4_page(R, S, sm, qw, lane, min(PT, nvq - (p0 + i) * PT), qscale);
     };
     auto page_ld = [&](int i) {
         const uint8_t *pg = base + (size_t)__builtin_amdgcn_readlane(pid_l, min(i, np - 1)) * pstride;
