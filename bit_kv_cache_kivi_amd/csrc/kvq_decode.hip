@@ -1262,6 +1262,22 @@ void stage1_head_mfma_kernel(KParams P, const uint16_t *__restrict__ q, Workspac
 // Philox4x32-10 block gives the four dither words of channels 4cq..4cq+3)
 // and token phase tp = L >> 5.
 // ---------------------------------------------------------------------------
+// Sum over the 32 lanes of each half-wave, in every lane: a DPP butterfly
+// within each 16-lane row (pair swaps, quad swaps, half-row and row mirrors)
+// and one swizzle that swaps the two rows of a half.
+template <int CTRL>
+__device__ inline float dpp_f(float x) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0u, __builtin_bit_cast(uint32_t, x), CTRL, 0xf, 0xf, false));
+}
+__device__ inline float half_sum32(float v) {
+    v += dpp_f<0xB1>(v);                // quad_perm [1, 0, 3, 2]
+    v += dpp_f<0x4E>(v);                // quad_perm [2, 3, 0, 1]
+    v += dpp_f<0x141>(v);               // row_half_mirror
+    v += dpp_f<0x140>(v);               // row_mirror
+    v += __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, v), 0x401F));  // lane ^ 16
+    return v;
+}
+
 template <int QPK>
 __global__ __launch_bounds__(64) void stage1_witcert_kernel(KParams P, const uint16_t *__restrict__ q,
                                                             Workspace W, float qscale, float sm_scale,
@@ -1353,18 +1369,24 @@ __global__ __launch_bounds__(64) void stage1_witcert_kernel(KParams P, const uin
                 float part = 0.f;
 #pragma unroll
                 for (int e = 0; e < 4; e++) part = fmaf(qv[hh][e], kx[e], part);
+                const float z2 = half_sum32(part) * qscale;
+                // per token phase: each half-wave sees its own token stream.
+                // Lazy rescaling: the running maximum moves only when a score
+                // exceeds it by 8 (log2 units), so p <= 256 and the rescale is rare
+                if (__any(z2 > m[hh] + LAZY_TAU)) {
+                    const float mnew = fmaxf(m[hh], z2);
+                    const float alpha = __builtin_amdgcn_exp2f(m[hh] - mnew);
+                    m[hh] = mnew;
+                    lp[hh] *= alpha;
+                    ap[hh] *= alpha;
 #pragma unroll
-                for (int msk = 1; msk < 32; msk <<= 1) part += shfl_xor(part, msk);
-                const float z2 = part * qscale;
-                // per token phase: each half-wave sees its own token stream
-                const float mnew = fmaxf(m[hh], z2);
-                const float alpha = exp2f(m[hh] - mnew);
-                const float pr = exp2f(z2 - mnew);
-                m[hh] = mnew;
-                lp[hh] = lp[hh] * alpha + pr;
-                ap[hh] = ap[hh] * alpha + pr * eu[hh];
+                    for (int e = 0; e < 4; e++) o[hh][e] *= alpha;
+                }
+                const float pr = __builtin_amdgcn_exp2f(z2 - m[hh]);
+                lp[hh] += pr;
+                ap[hh] = fmaf(pr, eu[hh], ap[hh]);
 #pragma unroll
-                for (int e = 0; e < 4; e++) o[hh][e] = fmaf(pr, vx[e], o[hh][e] * alpha);
+                for (int e = 0; e < 4; e++) o[hh][e] = fmaf(pr, vx[e], o[hh][e]);
             }
         }
     }
