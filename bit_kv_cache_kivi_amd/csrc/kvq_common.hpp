@@ -154,6 +154,14 @@ __device__ inline uint64_t mul_wide(uint32_t m, uint32_t x) {
     return r;
 }
 
+// a ^ b ^ k in one three-input bitwise instruction (truth table 0x96, the
+// same for any order of the inputs); k is uniform across the wave
+__device__ inline uint32_t xor3(uint32_t a, uint32_t b, uint32_t k) {
+    uint32_t d;
+    asm("v_bitop3_b32 %0, %1, %2, %3 bitop3:0x96" : "=v"(d) : "v"(a), "v"(b), "s"(k));
+    return d;
+}
+
 __device__ inline U4 philox4x32_10(U4 c, uint32_t k0, uint32_t k1) {
 #pragma unroll
     for (int r = 0; r < 10; r++) {
@@ -166,9 +174,9 @@ __device__ inline U4 philox4x32_10(U4 c, uint32_t k0, uint32_t k1) {
         const uint32_t lo0 = (uint32_t)p0, hi0 = (uint32_t)(p0 >> 32);
         const uint32_t lo1 = (uint32_t)p1, hi1 = (uint32_t)(p1 >> 32);
         U4 n;
-        n.x = hi1 ^ c.y ^ k0;
+        n.x = xor3(hi1, c.y, k0);
         n.y = lo1;
-        n.z = hi0 ^ c.w ^ k1;
+        n.z = xor3(hi0, c.w, k1);
         n.w = lo0;
         c = n;
     }
