@@ -1355,14 +1355,15 @@ __global__ __launch_bounds__(64) void stage1_witcert_kernel(KParams P, const uin
             const uint32_t vw = *(const uint32_t *)(vcod + (size_t)t * D + 4 * cq);
             const uint32_t ukw[4] = {uk.x, uk.y, uk.z, uk.w};
             const uint32_t uvw[4] = {uv.x, uv.y, uv.z, uv.w};
+            // x = s (code - xi), with code - xi = (code + 1/2) - (u >> 8) 2^-24
+            // rounded once, as a subtraction of xi would round it
             float kx[4], vx[4];
 #pragma unroll
             for (int e = 0; e < 4; e++) {
-#pragma clang fp contract(off)
                 const float kcode = (float)(int8_t)((kw >> (8 * e)) & 0xff);
                 const float vcode = (float)(int8_t)((vw >> (8 * e)) & 0xff);
-                kx[e] = ks[e] * (kcode - dither_from_word(ukw[e]));
-                vx[e] = vs[e] * (vcode - dither_from_word(uvw[e]));
+                kx[e] = ks[e] * __builtin_fmaf((float)(ukw[e] >> 8), -0x1p-24f, kcode + 0.5f);
+                vx[e] = vs[e] * __builtin_fmaf((float)(uvw[e] >> 8), -0x1p-24f, vcode + 0.5f);
             }
 #pragma unroll
             for (int hh = 0; hh < QPK; hh++) {
