@@ -33,8 +33,19 @@ from bit_kv_cache_kivi_amd import inputs  # noqa: E402
 
 METRIC = "quantized-KV decode attn: effective KV GB/s (% of HBM peak) + tokens/s, 1 GPU"
 HBM_PEAK_GBS = 8000.0
-INT_ALU_PEAK_TOPS = 256 * 64 * 2.4e9 / 1e12      # 32-bit integer VALU ops, all CUs
-PHILOX_OPS = 100                                  # per Philox4x32-10 call
+VALU_PEAK_TOPS = 256 * 64 * 2.4e9 / 1e12         # full-rate 32-bit VALU lane ops, all CUs
+PHILOX_VALU_OPS = 40                              # per Philox4x32-10 call on gfx950 (see below)
+
+
+def witcert_ops_per_call(qpk: int) -> int:
+    """Algorithmic VALU lane operations per Philox call (= per 4 quantized
+    elements of one side), counted in operations gfx950 runs at full rate:
+    the generator, 10 rounds x (2 32x32->64 multiply-adds + 2 three-input
+    XORs), the key schedule being per block and scalar; then per element the
+    dither from its word (shift, convert), the dequantization (code convert,
+    code + 1/2, fused subtraction of the dither, times the scale) and one FMA
+    per query head (the score on the key side, P.V on the value side)."""
+    return PHILOX_VALU_OPS + 4 * (2 + 4 + qpk)
 PROFILES = os.path.join(ROOT, "profiles")
 KERNEL_SOURCES = ["bit_kv_cache_kivi_amd/csrc/kvq_decode.hip",
                   "bit_kv_cache_kivi_amd/csrc/kvq_common.hpp"]
@@ -344,15 +355,16 @@ def main():
     kernel = ("stage1_witcert" if w.scheme == "witcert" else
               "stage1_gqa4_mfma" if (w.scheme == "kivi2" and w.group == 4) else "stage1_head_mfma")
     if w.scheme == "witcert":
-        # integer-ALU bound: Philox4x32-10 calls (one per token, channel quad
-        # and side of every quantized block) x 100 integer ops per call (10
-        # rounds of 2 mulhilo = 4 multiplies, 4 xor, 2 key additions),
-        # against 256 CUs x 64 lanes x 2.4 GHz of 32-bit integer VALU ops
+        # VALU bound: Philox4x32-10 calls (one per token, channel quad and
+        # side of every quantized block) x the algorithmic VALU operations per
+        # call, against 256 CUs x 64 lanes x 2.4 GHz of full-rate VALU ops
         calls = float(np.mean(s1_calls))
-        tops = calls * PHILOX_OPS / (s1_avg_ms * 1e-3) / 1e12
+        ops_call = witcert_ops_per_call(w.group)
+        tops = calls * ops_call / (s1_avg_ms * 1e-3) / 1e12
         roof = {"kernel": kernel, "bound": "alu", "achieved": round(tops, 2),
-                "peak": INT_ALU_PEAK_TOPS, "unit": "TOP/s",
-                "frac": round(tops / INT_ALU_PEAK_TOPS, 4),
+                "peak": VALU_PEAK_TOPS, "unit": "TOP/s",
+                "frac": round(tops / VALU_PEAK_TOPS, 4),
+                "valu_ops_per_philox_call": ops_call,
                 "traffic": traffic_entry(kernel, w.name),
                 "avg_launch_us": round(s1_avg_ms * 1e3, 2),
                 "philox_calls_per_launch": int(calls),
