@@ -1,6 +1,7 @@
 // kvq_api.cpp -- host side of libkvq.so: validation, launch geometry and
 // workspace sizing behind the C ABI of include/kvq.h.  Never allocates, frees
 // or synchronizes device memory.
+#include <algorithm>
 #include <string.h>
 
 #include "kvq.h"
@@ -125,10 +126,15 @@ int kvq_set_layout(kvq_cache_t *cache, const kvq_layout_t *layout, const kvq_buf
     cache->page_tokens = G.tokens;
     cache->page_bytes = G.bytes;
     int sp = layout->split_pages;
-    if (sp == 0) sp = layout->scheme == KVQ_SCHEME_WITCERT ? 1 : 8;
-    // stage 2 merges at most 256 splits per query head
-    while ((layout->max_pages + sp - 1) / sp > 256) sp *= 2;
-    if (sp > 64) return KVQ_EINVAL;
+    if (sp == 0) {
+        // default: one 256-token block per split for WITCERT; 8 pages for
+        // short caches, 12 for longer ones (fewer partials to merge, enough
+        // splits to fill the chip), at least what keeps <= 256 splits
+        sp = layout->scheme == KVQ_SCHEME_WITCERT ? 1 : (layout->max_pages <= 128 ? 8 : 12);
+        sp = std::max(sp, (layout->max_pages + 255) / 256);
+    }
+    // the merge takes at most 256 splits per query head
+    if ((layout->max_pages + sp - 1) / sp > 256 || sp > 64) return KVQ_EINVAL;
     cache->split_pages = sp;
     cache->magic = MAGIC;
     return KVQ_OK;

@@ -104,7 +104,9 @@ typedef struct kvq_layout {
     int32_t n_boost;         /* KITTY boosted key channels: 16 (0 for others) */
     int32_t max_pages;       /* page-table row length per request */
     int32_t n_pages;         /* pages in the pool */
-    int32_t split_pages;     /* stage-1 split size in pages (0: default) */
+    int32_t split_pages;     /* stage-1 split size in pages; 0: 8 when max_pages
+                                <= 128, else 12 (1 for WITCERT), raised to
+                                ceil(max_pages / 256) where that is larger */
     int32_t flags;           /* KVQ_FLAG_* */
     uint32_t layer;          /* WITCERT dither counter field; < 65536 */
     uint64_t seed;           /* WITCERT dither key */
@@ -149,8 +151,8 @@ typedef struct kvq_cache {
  *   head_dim != 128; n_kv_heads outside [1, 65535]; n_q_heads not a multiple
  *   of n_kv_heads, or more than 8 query heads per KV head; batch outside
  *   [1, 65535]; max_pages or n_pages < 1; split_pages outside [0, 64] (0 picks
- *   a default), or no split of at most 64 pages keeps max_pages within 256
- *   splits; flags other than KVQ_FLAG_*; unknown scheme;
+ *   a default), or max_pages needs more than 256 splits of the resolved size
+ *   (at most 64 pages); flags other than KVQ_FLAG_*; unknown scheme;
  *   KIVI2 / KITTY: group or value_group != 32; residual not a multiple of 64
  *   or outside [64, 256] (the residual is quantized in whole key groups, so it
  *   must be divisible by the group, "KIVI" explainer 3.3, and the flush fills

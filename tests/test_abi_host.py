@@ -142,10 +142,11 @@ def test_null_and_alignment(K):
 
 
 def test_split_resolution_and_workspace(K):
-    # default split 8 pages (1 for WITCERT's 256-token pages), doubled until
-    # at most 256 splits cover max_pages
-    for scheme, max_pages, want in (("kivi2", 512, 8), ("kivi2", 2048, 8), ("kivi2", 4096, 16),
-                                    ("kivi2", 16384, 64), ("witcert", 64, 1),
+    # default split: 8 pages up to 128 pages of cache, 12 above (1 for
+    # WITCERT's 256-token pages), raised to what keeps at most 256 splits
+    for scheme, max_pages, want in (("kivi2", 100, 8), ("kivi2", 128, 8), ("kitty", 129, 12),
+                                    ("kivi2", 512, 12), ("kivi2", 3072, 12), ("kivi2", 3073, 13),
+                                    ("kivi2", 4096, 16), ("kivi2", 16384, 64), ("witcert", 64, 1),
                                     ("witcert", 1024, 4)):
         L = K.make_layout(scheme, B=2, Hq=8, Hkv=2, max_pages=max_pages, n_pages=max_pages)
         rc, cache = set_layout(K, L)
