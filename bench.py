@@ -170,10 +170,13 @@ def setup_gpu(w: inputs.Workload, extra: int, split_pages: int):
     return cache
 
 
-def run_gpu(w: inputs.Workload, steps: int, warmup: int, split_pages: int):
+def run_gpu(w: inputs.Workload, steps: int, warmup: int, split_pages: int, copies: int = 1):
+    """copies > 1: that many independent caches of the workload, used in turn
+    (step i on copy i mod copies), so that no cache stays resident in the
+    memory-side cache between its steps (a cold-cache figure)."""
     import torch
     from bit_kv_cache_kivi_amd import kvq
-    cache = setup_gpu(w, extra=steps + warmup + 8, split_pages=split_pages)
+    caches = [setup_gpu(w, extra=steps + warmup + 8, split_pages=split_pages) for _ in range(copies)]
     n = steps + warmup
     # every step's inputs resident in HBM before timing
     ks, vs, qs = [], [], []
@@ -195,13 +198,15 @@ def run_gpu(w: inputs.Workload, steps: int, warmup: int, split_pages: int):
     assert all(a.cuda_event and b.cuda_event for a, b in ev1)
 
     def one(i, evs=None):
+        cache = caches[i % copies]
+        j = i // copies                     # this copy's own step number
         if evs is not None:
             kvq.kvq_set_stage1_events(cache.cache, evs[0].cuda_event, evs[1].cuda_event)
         else:
             kvq.kvq_set_stage1_events(cache.cache, None, None)
         cache.flush()
-        cache.append(ks[i], vs[i])
-        cache.decode(qs[i], out, cert, sm_scale=w.sm_scale, kappa=kappa)
+        cache.append(ks[j], vs[j])
+        cache.decode(qs[j], out, cert, sm_scale=w.sm_scale, kappa=kappa)
 
     for i in range(warmup):
         one(i)
@@ -211,10 +216,11 @@ def run_gpu(w: inputs.Workload, steps: int, warmup: int, split_pages: int):
         one(warmup + j, ev1[j])
     torch.cuda.synchronize()
     dt = time.perf_counter() - t0
-    kvq.kvq_set_stage1_events(cache.cache, None, None)
-    st = cache.status_word()
-    if st != 0:
-        raise RuntimeError(f"device status {st:#x}")
+    for cache in caches:
+        kvq.kvq_set_stage1_events(cache.cache, None, None)
+        st = cache.status_word()
+        if st != 0:
+            raise RuntimeError(f"device status {st:#x}")
     if not torch.isfinite(out).all():
         raise RuntimeError("non-finite output")
     s1_ms = [a.elapsed_time(b) for a, b in ev1]
@@ -226,14 +232,16 @@ def run_gpu(w: inputs.Workload, steps: int, warmup: int, split_pages: int):
 # CPU oracle baseline (bounded sample of the same workload)
 # ---------------------------------------------------------------------------
 
-def cpu_baseline(w: inputs.Workload, warmup: int, target_s: float = 15.0):
+def cpu_baseline(w: inputs.Workload, warmup: int, target_s: float = 15.0, threads: int = 0,
+                 n_pairs: int = 0):
     from oracle import oracle as O
     sid = {"kivi2": O.KIVI, "kitty": O.KITTY, "witcert": O.WITCERT}[w.scheme]
-    threads = max(1, min(16, len(os.sched_getaffinity(0))))
+    if threads <= 0:
+        threads = max(1, min(16, len(os.sched_getaffinity(0))))
     idx = None
     if w.scheme == "kitty":
         idx = [O.kitty_select(inputs.kitty_calibration(w, h), w.nb) for h in range(w.Hkv)]
-    pairs = [(b, b % w.Hkv) for b in range(w.B)]
+    pairs = [(b, b % w.Hkv) for b in range(n_pairs if n_pairs > 0 else w.B)]
     seed = 0x5EED_0000_0000_0000 | w.seed
 
     def make(pair):
@@ -312,6 +320,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", type=int, default=3)
     ap.add_argument("--split-pages", type=int, default=0)
+    ap.add_argument("--cold", action="store_true",
+                    help="two cache copies used in turn, so the memory-side cache holds neither")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--copy-calibration", action="store_true",
@@ -333,19 +343,21 @@ def main():
     w = inputs.workload(args.workload)
     log(f"workload {w.name}: B={w.B} Hq={w.Hq} Hkv={w.Hkv} ctx mean "
         f"{np.mean(w.ctx):.0f}, steps={args.steps} warmup={args.warmup}")
-    dt, s1_ms = run_gpu(w, args.steps, args.warmup, args.split_pages)
+    copies = 2 if args.cold else 1
+    dt, s1_ms = run_gpu(w, args.steps, args.warmup, args.split_pages, copies)
 
-    # algorithmic bytes of the timed steps
-    states = [state_after_prefill(w, l) for l in w.ctx]
-    for _ in range(args.warmup):
-        _, _, states = step_bytes(w, states)
+    # algorithmic bytes of the timed steps (step i advances copy i mod copies)
+    cstates = [[state_after_prefill(w, l) for l in w.ctx] for _ in range(copies)]
+    for i in range(args.warmup):
+        _, _, cstates[i % copies] = step_bytes(w, cstates[i % copies])
     tot = 0
     s1_bytes = []
     s1_calls = []
-    for _ in range(args.steps):
+    for i in range(args.warmup, args.warmup + args.steps):
+        states = cstates[i % copies]
         s1_calls.append(sum(w.Hkv * 2 * (n_kq // w.BLK) * w.BLK * (w.D // 4) for (_, n_kq) in
                             [step_state(w, l, k) for (l, k) in states]) if w.scheme == "witcert" else 0)
-        b, s1, states = step_bytes(w, states)
+        b, s1, cstates[i % copies] = step_bytes(w, states)
         tot += b
         s1_bytes.append(s1)
     gbs = tot / dt / 1e9
@@ -367,6 +379,7 @@ def main():
                 "valu_ops_per_philox_call": ops_call,
                 "traffic": traffic_entry(kernel, w.name),
                 "avg_launch_us": round(s1_avg_ms * 1e3, 2),
+                "median_launch_us": round(float(np.median(s1_ms)) * 1e3, 2),
                 "philox_calls_per_launch": int(calls),
                 "algorithmic_bytes_per_launch": int(np.mean(s1_bytes)),
                 "hbm_gbs": round(s1_gbs, 1)}
@@ -376,6 +389,7 @@ def main():
                 "frac": round(s1_gbs / HBM_PEAK_GBS, 4),
                 "traffic": traffic_entry(kernel, w.name),
                 "avg_launch_us": round(s1_avg_ms * 1e3, 2),
+                "median_launch_us": round(float(np.median(s1_ms)) * 1e3, 2),
                 "algorithmic_bytes_per_launch": int(np.mean(s1_bytes))}
     rec = {"metric": METRIC, "value": round(gbs, 1), "unit": "GB/s", "n_gpus": 1,
            "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
@@ -385,13 +399,18 @@ def main():
                       "head_dim": w.D, "ctx_mean": float(np.mean(w.ctx)),
                       "ctx_min": int(min(w.ctx)), "ctx_max": int(max(w.ctx)),
                       "page_tokens": 256 if w.scheme == "witcert" else 64,
-                      "G": w.G, "R": w.R, "layers": 1},
+                      "G": w.G, "R": w.R, "layers": 1, "cache_copies": copies},
            "tokens_per_s": round(w.B / (ms_step * 1e-3), 1),
+           # the same step time for 32 such attention layers and nothing else
+           "tokens_per_s_attention_only_32_layers": round(w.B / (ms_step * 1e-3) / 32, 1),
            "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
            "roofline": roof}
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a bounded sample ...")
         rec["cpu_baseline"] = cpu_baseline(w, args.warmup, args.cpu_seconds)
+        one_t = cpu_baseline(w, args.warmup, max(2.0, args.cpu_seconds / 4), threads=1, n_pairs=4)
+        rec["cpu_baseline"]["single_thread"] = {"value": one_t["value"], "unit": one_t["unit"],
+                                                "sample": one_t["sample"]}
     print(json.dumps(rec), flush=True)
 
 
