@@ -267,6 +267,38 @@ void ko_kitty_select(const uint16_t *k, long T, int D, int nb, uint8_t *idx)
 }
 
 /* ------------------------------------------------------------------------ */
+/* Kitty dynamic boost selection for one selection unit of T tokens.        */
+/* [KITTY] "Channel-Wise Precision Boost Mechanism": the importance of a    */
+/* channel within a group is its mean absolute value, and the top K of the  */
+/* group are boosted.  Readings: the unit is one 64-token page of the cache */
+/* (the pages' groups are their own pages); the mean is compared through    */
+/* the exact sum sum_t |x_{t,c}| (T is fixed, and binary16 values add       */
+/* exactly in binary64 at these sizes); ties go to the lower channel;       */
+/* offsets follow ascending channel order, others get the sentinel nb + 1. */
+/* ------------------------------------------------------------------------ */
+
+void ko_kitty_select_dyn(const uint16_t *k, long T, long ld, int D, int nb, uint8_t *idx)
+{
+    double *imp = (double *)calloc((size_t)D, sizeof(double));
+    char *chosen = (char *)calloc((size_t)D, 1);
+    for (long t = 0; t < T; t++)
+        for (int c = 0; c < D; c++)
+            imp[c] += fabs((double)ko_f16_to_f32(k[t * ld + c]));
+    for (int j = 0; j < nb; j++) {
+        int best = -1;
+        for (int c = 0; c < D; c++)
+            if (!chosen[c] && (best < 0 || imp[c] > imp[best]))
+                best = c;
+        chosen[best] = 1;
+    }
+    int off = 0;
+    for (int c = 0; c < D; c++)
+        idx[c] = chosen[c] ? (uint8_t)(off++) : (uint8_t)(nb + 1);
+    free(imp);
+    free(chosen);
+}
+
+/* ------------------------------------------------------------------------ */
 /* One (request, KV head) stream: the raw fp16 history plus the quantized   */
 /* record, advanced by the same three calls as the library:                 */
 /*   flush  -> append -> decode   (the Kitty pipeline order: attention runs  */
@@ -276,7 +308,7 @@ void ko_kitty_select(const uint16_t *k, long T, int D, int nb, uint8_t *idx)
 /* a token's fp16 value is read only while it is inside a residual window. */
 /* ------------------------------------------------------------------------ */
 
-enum { KO_KIVI = 0, KO_KITTY = 1, KO_WITCERT = 2 };
+enum { KO_KIVI = 0, KO_KITTY = 1, KO_WITCERT = 2, KO_KITTY_DYN = 3 };
 
 typedef struct ko_stream {
     int scheme, D, G, R, VG, BLK, nb, bits_v;
@@ -289,25 +321,35 @@ typedef struct ko_stream {
     uint8_t *Vc;             /* [cap][D] */
     uint16_t *Ks, *Kz;       /* KIVI/Kitty: [cap/G][D];  WitCert Ks: [cap/BLK][D] */
     uint16_t *Vs, *Vz;       /* KIVI/Kitty: [cap][D/VG]; WitCert Vs: [cap/BLK][D] */
-    uint8_t idx[256];        /* Kitty boost index per channel */
+    uint8_t idx[256];        /* Kitty boost index per channel (static) */
+    long sel;                /* Kitty dynamic: tokens per selection unit */
+    uint8_t *uidx;           /* Kitty dynamic: [cap/sel + 1][D] boost index per unit */
     uint64_t seed;
     uint32_t req, layer, kvh;
 } ko_stream;
 
+/* sel: tokens per selection unit for KO_KITTY_DYN (a multiple of G that
+ * divides R, so a flush always quantizes whole units); ignored otherwise. */
 ko_stream *ko_stream_new(int scheme, int D, int G, int R, int VG, int BLK,
                          int nb, const uint8_t *idx, long cap,
-                         uint64_t seed, uint32_t req, uint32_t layer, uint32_t kvh)
+                         uint64_t seed, uint32_t req, uint32_t layer, uint32_t kvh, long sel)
 {
     if (D <= 0 || D > 256 || cap <= 0) return NULL;
+    if (scheme < KO_KIVI || scheme > KO_KITTY_DYN) return NULL;
     if (scheme != KO_WITCERT) {
         if (G <= 0 || R <= 0 || R % G != 0 || VG <= 0 || D % VG != 0) return NULL;
         if (nb < 0 || nb > D) return NULL;
     } else if (BLK <= 0) {
         return NULL;
     }
+    if (scheme == KO_KITTY_DYN && (sel <= 0 || sel % G != 0 || R % sel != 0)) return NULL;
     ko_stream *s = (ko_stream *)calloc(1, sizeof(ko_stream));
     s->scheme = scheme; s->D = D; s->G = G; s->R = R; s->VG = VG; s->BLK = BLK;
-    s->nb = (scheme == KO_KITTY) ? nb : 0;
+    s->nb = (scheme == KO_KITTY || scheme == KO_KITTY_DYN) ? nb : 0;
+    if (scheme == KO_KITTY_DYN) {
+        s->sel = sel;
+        s->uidx = (uint8_t *)calloc((size_t)((cap / sel + 1) * D), 1);
+    }
     s->cap = cap;
     s->seed = seed; s->req = req; s->layer = layer; s->kvh = kvh;
     s->Kraw = (uint16_t *)calloc((size_t)(cap * D), 2);
@@ -330,20 +372,37 @@ void ko_stream_free(ko_stream *s)
     if (!s) return;
     free(s->Kraw); free(s->Vraw); free(s->Kc); free(s->Vc);
     free(s->Ks); free(s->Kz); free(s->Vs); free(s->Vz);
+    free(s->uidx);
     free(s);
 }
 
-static int key_bits(const ko_stream *s, int c)
+/* Boost index of key group g, channel c: the head's static index, or the
+ * index of the selection unit holding the group. */
+static int boost_off(const ko_stream *s, long g, int c)
 {
-    return (s->scheme == KO_KITTY && s->idx[c] < s->nb) ? 4 : 2;
+    if (s->scheme == KO_KITTY) return s->idx[c];
+    if (s->scheme == KO_KITTY_DYN) return s->uidx[(g * s->G / s->sel) * s->D + c];
+    return s->nb + 1;
+}
+
+static int key_bits(const ko_stream *s, long g, int c)
+{
+    return boost_off(s, g, c) < s->nb ? 4 : 2;
 }
 
 /* [KIVI] 3.3: keys gather in the residual; once R have gathered they are
- * quantized per channel in R/G groups of G tokens and the residual clears. */
+ * quantized per channel in R/G groups of G tokens and the residual clears.
+ * Kitty dynamic: the first group of a selection unit selects the unit's
+ * boosted channels from the unit's raw keys (all present: units divide R). */
 static void quant_key_group(ko_stream *s, long g)
 {
+    if (s->scheme == KO_KITTY_DYN && (g * s->G) % s->sel == 0) {
+        long u = g * s->G / s->sel;
+        ko_kitty_select_dyn(&s->Kraw[u * s->sel * s->D], s->sel, s->D, s->D, s->nb,
+                            &s->uidx[u * s->D]);
+    }
     for (int c = 0; c < s->D; c++)
-        ko_quant_asym(&s->Kraw[g * s->G * s->D + c], s->G, s->D, key_bits(s, c),
+        ko_quant_asym(&s->Kraw[g * s->G * s->D + c], s->G, s->D, key_bits(s, g, c),
                       &s->Ks[g * s->D + c], &s->Kz[g * s->D + c],
                       &s->Kc[g * s->G * s->D + c], s->D);
 }
@@ -458,6 +517,7 @@ const uint16_t *ko_stream_kscale(const ko_stream *s) { return s->Ks; }
 const uint16_t *ko_stream_kzero(const ko_stream *s) { return s->Kz; }
 const uint16_t *ko_stream_vscale(const ko_stream *s) { return s->Vs; }
 const uint16_t *ko_stream_vzero(const ko_stream *s) { return s->Vz; }
+const uint8_t *ko_stream_uidx(const ko_stream *s) { return s->uidx; }
 
 /* Dequantized (or raw fp16) key / value of token t, channel c, as binary32.
  * [KIVI] eq. 3: the key is the quantized group for t < n_kq and the fp16

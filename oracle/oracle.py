@@ -19,7 +19,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 SRC = os.path.join(HERE, "kvq_oracle.c")
 LIB = os.path.join(HERE, "_build", "libkvq_oracle.so")
 
-KIVI, KITTY, WITCERT = 0, 1, 2
+KIVI, KITTY, WITCERT, KITTY_DYN = 0, 1, 2, 3
 
 GCC_FLAGS = ["-std=c11", "-O2", "-fPIC", "-shared", "-ffp-contract=off",
              "-fno-fast-math", "-fno-finite-math-only"]
@@ -60,16 +60,17 @@ def lib():
         L.ko_witcert_dequant.argtypes = [C.c_int, C.c_uint16, C.c_float]
         L.ko_witcert_dequant.restype = C.c_float
         L.ko_kitty_select.argtypes = [P, C.c_long, C.c_int, C.c_int, P]
+        L.ko_kitty_select_dyn.argtypes = [P, C.c_long, C.c_long, C.c_int, C.c_int, P]
         L.ko_stream_new.argtypes = [C.c_int, C.c_int, C.c_int, C.c_int, C.c_int,
                                     C.c_int, C.c_int, P, C.c_long, C.c_uint64,
-                                    C.c_uint32, C.c_uint32, C.c_uint32]
+                                    C.c_uint32, C.c_uint32, C.c_uint32, C.c_long]
         L.ko_stream_new.restype = P
         L.ko_stream_free.argtypes = [P]
         L.ko_stream_flush.argtypes = [P]
         L.ko_stream_append.argtypes = [P, P, P]
         L.ko_stream_prefill.argtypes = [P, P, P, C.c_long]
         L.ko_stream_state.argtypes = [P, P]
-        for name in ("ko_stream_kcodes", "ko_stream_vcodes"):
+        for name in ("ko_stream_kcodes", "ko_stream_vcodes", "ko_stream_uidx"):
             getattr(L, name).argtypes = [P]
             getattr(L, name).restype = C.POINTER(C.c_uint8)
         for name in ("ko_stream_kscale", "ko_stream_kzero", "ko_stream_vscale",
@@ -151,6 +152,16 @@ def kitty_select(k: np.ndarray, nb: int) -> np.ndarray:
     return idx
 
 
+def kitty_select_dyn(k: np.ndarray, nb: int) -> np.ndarray:
+    """Dynamic boost index of one selection unit k [T][D] (fp16 bits):
+    top nb channels by mean |x| over the unit, ties to the lower channel."""
+    k = np.ascontiguousarray(k, dtype=np.uint16)
+    T, D = k.shape
+    idx = np.zeros(D, np.uint8)
+    lib().ko_kitty_select_dyn(_p(k), T, D, D, nb, _p(idx))
+    return idx
+
+
 # --------------------------------------------------------------------------
 # one (request, KV head) stream
 # --------------------------------------------------------------------------
@@ -160,13 +171,13 @@ class Stream:
 
     def __init__(self, scheme: int, cap: int, D: int = 128, G: int = 32, R: int = 128,
                  VG: int = 32, BLK: int = 256, nb: int = 0, idx=None,
-                 seed: int = 0, req: int = 0, layer: int = 0, kvh: int = 0):
+                 seed: int = 0, req: int = 0, layer: int = 0, kvh: int = 0, sel: int = 64):
         self.scheme, self.cap, self.D, self.G, self.R = scheme, cap, D, G, R
-        self.VG, self.BLK, self.nb = VG, BLK, nb
+        self.VG, self.BLK, self.nb, self.sel = VG, BLK, nb, sel
         self._idx = None if idx is None else np.ascontiguousarray(idx, np.uint8)
         h = lib().ko_stream_new(scheme, D, G, R, VG, BLK, nb,
                                 None if self._idx is None else _p(self._idx),
-                                cap, seed, req, layer, kvh)
+                                cap, seed, req, layer, kvh, sel)
         if not h:
             raise ValueError("invalid stream parameters")
         self.h = h
@@ -208,6 +219,11 @@ class Stream:
 
     def value_codes(self):
         return self._arr("ko_stream_vcodes", self.cap * self.D, np.uint8).reshape(self.cap, self.D)
+
+    def unit_index(self):
+        """Kitty dynamic: boost index per selection unit [cap/sel + 1][D]."""
+        n = self.cap // self.sel + 1
+        return self._arr("ko_stream_uidx", n * self.D, np.uint8).reshape(n, self.D)
 
     def key_stats(self):
         """(scale, zero) fp16 bits: [groups][D] (WitCert: [blocks][D], zero unused)."""
