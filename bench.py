@@ -59,11 +59,18 @@ def log(msg: str):
 # algorithmic byte accounts (per (request, KV head) at decode time)
 # ---------------------------------------------------------------------------
 
-def kivi_bytes(l: int, n_kq: int, R: int, qpk: int, kitty: bool) -> dict:
+def key_q_bytes(scheme: str, n: int) -> int:
+    """Quantized key bytes of n tokens: codes (+ Kitty high plane) + stats,
+    and for Kitty dynamic the 16 channel ids of each 64-token page touched."""
+    if scheme == "kitty_dyn":
+        return n * 52 + ((n + 63) // 64) * 16
+    return n * (52 if scheme == "kitty" else 48)
+
+
+def kivi_bytes(l: int, n_kq: int, R: int, qpk: int, scheme: str) -> dict:
     n_vq = max(0, l - R)
-    kq = 52 if kitty else 48          # codes (+ Kitty high plane) + stats per token
-    paged = n_vq * (kq + 48)
-    window = (n_kq - n_vq) * kq + (l - n_kq) * 256 + (l - n_vq) * 256
+    paged = key_q_bytes(scheme, n_vq) + n_vq * 48
+    window = key_q_bytes(scheme, n_kq - n_vq) + (l - n_kq) * 256 + (l - n_vq) * 256
     qo = qpk * (256 + 512)
     table = ((l + 63) // 64) * 4
     # stage 1 streams the paged prefix and, as one more split, the fp16 window
@@ -88,7 +95,7 @@ def write_bytes(w: inputs.Workload, l_before: int, n_kq_before: int) -> int:
     if l_before >= w.R:
         b += 256 + 48                  # value leaving the window, its codes + stats
     if l_before - n_kq_before == w.R:
-        b += w.R * 256 + w.R * (52 if w.scheme == "kitty" else 48)
+        b += w.R * 256 + key_q_bytes(w.scheme, w.R)
     return b
 
 
@@ -117,7 +124,7 @@ def step_bytes(w: inputs.Workload, states):
         if w.scheme == "witcert":
             d = witcert_bytes(l2, k2, w.group)
         else:
-            d = kivi_bytes(l2, k2, w.R, w.group, w.scheme == "kitty")
+            d = kivi_bytes(l2, k2, w.R, w.group, w.scheme)
         tot += w.Hkv * (wb + d["decode"])
         s1 += w.Hkv * d["stage1"]
         new.append((l2, k2))
@@ -235,7 +242,7 @@ def run_gpu(w: inputs.Workload, steps: int, warmup: int, split_pages: int, copie
 def cpu_baseline(w: inputs.Workload, warmup: int, target_s: float = 15.0, threads: int = 0,
                  n_pairs: int = 0):
     from oracle import oracle as O
-    sid = {"kivi2": O.KIVI, "kitty": O.KITTY, "witcert": O.WITCERT}[w.scheme]
+    sid = {"kivi2": O.KIVI, "kitty": O.KITTY, "witcert": O.WITCERT, "kitty_dyn": O.KITTY_DYN}[w.scheme]
     if threads <= 0:
         threads = max(1, min(16, len(os.sched_getaffinity(0))))
     idx = None
@@ -278,7 +285,7 @@ def cpu_baseline(w: inputs.Workload, warmup: int, target_s: float = 15.0, thread
                 wb = write_bytes(w, l, n_kq)
                 l2, k2 = step_state(w, l, n_kq)
                 d = (witcert_bytes(l2, k2, w.group) if w.scheme == "witcert"
-                     else kivi_bytes(l2, k2, w.R, w.group, w.scheme == "kitty"))
+                     else kivi_bytes(l2, k2, w.R, w.group, w.scheme))
                 done_bytes += wb + d["decode"]
                 states[i] = (l2, k2)
             rounds += 1

@@ -27,12 +27,16 @@ int validate_layout(const kvq_layout_t *L) {
     switch (L->scheme) {
         case KVQ_SCHEME_KIVI2:
         case KVQ_SCHEME_KITTY:
+        case KVQ_SCHEME_KITTY_DYN:
             if (L->group != 32 || L->value_group != 32) return KVQ_EINVAL;
             // the key residual is quantized in whole groups: R % G == 0, and
             // the flush writes whole 64-token pages
             if (L->residual % L->group != 0 || L->residual % kvq::PT != 0) return KVQ_EINVAL;
             if (L->residual < kvq::PT || L->residual > 256) return KVQ_EINVAL;
-            if (L->scheme == KVQ_SCHEME_KITTY ? L->n_boost != kvq::NB : L->n_boost != 0)
+            if (kvq::is_kitty(L->scheme) ? L->n_boost != kvq::NB : L->n_boost != 0)
+                return KVQ_EINVAL;
+            // the VALU stage 1 reads the head's static boost table only
+            if (L->scheme == KVQ_SCHEME_KITTY_DYN && (L->flags & KVQ_FLAG_GENERIC_STAGE1))
                 return KVQ_EINVAL;
             break;
         case KVQ_SCHEME_WITCERT:
@@ -93,13 +97,13 @@ extern "C" {
 
 int64_t kvq_page_bytes(const kvq_layout_t *L) {
     if (!L) return 0;
-    if (L->scheme < KVQ_SCHEME_KIVI2 || L->scheme > KVQ_SCHEME_WITCERT) return 0;
+    if (L->scheme < KVQ_SCHEME_KIVI2 || L->scheme > KVQ_SCHEME_KITTY_DYN) return 0;
     return kvq::geom(L->scheme).bytes;
 }
 
 int32_t kvq_page_tokens(const kvq_layout_t *L) {
     if (!L) return 0;
-    if (L->scheme < KVQ_SCHEME_KIVI2 || L->scheme > KVQ_SCHEME_WITCERT) return 0;
+    if (L->scheme < KVQ_SCHEME_KIVI2 || L->scheme > KVQ_SCHEME_KITTY_DYN) return 0;
     return kvq::geom(L->scheme).tokens;
 }
 

@@ -18,20 +18,26 @@ constexpr int NB = 16;          // Kitty boosted channels per KV head
 // Page geometry.  One (page, KV head) block; the pool is
 // [n_pages][n_kv_heads][page_bytes].
 //
-// KIVI2 / KITTY, 64 tokens:
+// KIVI2 / KITTY / KITTY_DYN, 64 tokens:
 //   KC  2048 B  low 2-bit key codes, token-major, arranged as the B operand of
 //               a 16x16x32 f16 matrix-core product (see key_code_pos)
-//   KH   256 B  KITTY only: high 2-bit plane of the 16 boosted channels
+//   KH   256 B  KITTY*: high 2-bit plane of the 16 boosted channels
 //   KS  1024 B  key {scale, zero} fp16 pairs, [2 groups][128 channels]
 //   VC  2048 B  value codes, channel-major (see value_code_pos)
 //   VS  1024 B  value {scale, zero} fp16 pairs, [64 tokens][4 groups]
+//   KI    16 B  KITTY_DYN: the page's boosted channel ids, ascending (the
+//               high-plane offset of KI[o] is o)
 // WITCERT, 256 tokens (one block):
 //   KC 32768 B int8 [256][128];  KS 256 B fp16 [128];
 //   VC 32768 B int8 [256][128];  VS 256 B fp16 [128]
 // ---------------------------------------------------------------------------
 struct Geom {
-    int kc, kh, ks, vc, vs, bytes, tokens;
+    int kc, kh, ks, vc, vs, ki, bytes, tokens;
 };
+
+__host__ __device__ constexpr bool is_kitty(int scheme) {
+    return scheme == KVQ_SCHEME_KITTY || scheme == KVQ_SCHEME_KITTY_DYN;
+}
 
 __host__ __device__ inline Geom geom(int scheme) {
     Geom g{};
@@ -40,6 +46,9 @@ __host__ __device__ inline Geom geom(int scheme) {
         g.tokens = WPT;
     } else if (scheme == KVQ_SCHEME_KITTY) {
         g.kc = 0; g.kh = 2048; g.ks = 2304; g.vc = 3328; g.vs = 5376; g.bytes = 6400;
+        g.tokens = PT;
+    } else if (scheme == KVQ_SCHEME_KITTY_DYN) {
+        g.kc = 0; g.kh = 2048; g.ks = 2304; g.vc = 3328; g.vs = 5376; g.ki = 6400; g.bytes = 6416;
         g.tokens = PT;
     } else {
         g.kc = 0; g.kh = 0; g.ks = 2048; g.vc = 3072; g.vs = 5120; g.bytes = 6144;

@@ -104,6 +104,7 @@ __device__ inline float half_hi(uint32_t v) { return h2f((uint16_t)(v >> 16)); }
 // ---------------------------------------------------------------------------
 struct WinSmem {
     uint32_t ks[2][256];        // key {s, z} of the (at most two) pages of the chunk's quantized keys
+    uint8_t bidx[2][D];         // KITTY_DYN: those pages' boost offsets per channel
     f4v zsh[2][PT];             // scores of the chunk: token -> queries 0..3, 4..7
     float4 pT[PT][2];           // p of the chunk: token -> queries 0..3, 4..7
 };
@@ -121,7 +122,8 @@ __device__ void window_partial(const KParams &P, const uint16_t *__restrict__ q,
                                float qscale, int b, int h, int hq0, int wc, int lane, WinSmem &ws) {
     const Geom G = geom(SCHEME);
     constexpr bool wit = SCHEME == KVQ_SCHEME_WITCERT;
-    constexpr bool kitty = SCHEME == KVQ_SCHEME_KITTY;
+    constexpr bool kitty = is_kitty(SCHEME);
+    constexpr bool dyn = SCHEME == KVQ_SCHEME_KITTY_DYN;
     const int g = lane >> 4, r = lane & 15;
     const size_t bh = (size_t)b * P.Hkv + h;
     const int l = P.state[bh * 4], nkq = P.state[bh * 4 + 1];
@@ -168,6 +170,18 @@ __device__ void window_partial(const KParams &P, const uint16_t *__restrict__ q,
 #pragma unroll
         for (int pi = 0; pi < 2; pi++)
             if (pids[pi] >= 0) ((uint4 *)ws.ks[pi])[lane] = ((const uint4 *)(cpage(P, pids[pi], h) + G.ks))[lane];
+        if (dyn) {                                // channel -> offset from the pages' channel ids
+#pragma unroll
+            for (int pi = 0; pi < 2; pi++) {
+                ws.bidx[pi][2 * lane] = (uint8_t)(NB + 1);
+                ws.bidx[pi][2 * lane + 1] = (uint8_t)(NB + 1);
+            }
+            lds_sync();
+            if (lane < 2 * NB) {
+                const int pi = lane / NB, o = lane % NB;
+                if (pids[pi] >= 0) ws.bidx[pi][cpage(P, pids[pi], h)[G.ki + o] & (D - 1)] = (uint8_t)o;
+            }
+        }
     }
     lds_sync();
 
@@ -214,7 +228,8 @@ __device__ void window_partial(const KParams &P, const uint16_t *__restrict__ q,
                     for (int i = 0; i < 8; i++) {
                         uint32_t code = (xa[kc >> 1] >> (4 * i + 2 * (kc & 1))) & 3u;
                         if (kitty) {
-                            const int o = P.boost_idx[(size_t)h * D + 32 * kc + 8 * g + i];
+                            const int o = dyn ? ws.bidx[pi][32 * kc + 8 * g + i]
+                                              : P.boost_idx[(size_t)h * D + 32 * kc + 8 * g + i];
                             if (o < NB) code |= ((kh[o >> 2] >> (hsh + 4 * (o & 3))) & 3u) << 2;
                         }
                         kf[i] = fmaf((float)code, half_lo(sz[i]), half_hi(sz[i]));   // code * s exact
@@ -1017,11 +1032,13 @@ __device__ inline h8v frag8_x4(uint32_t m) {     // codes times 4
 struct HeadPage {
     PageRegs R;
     uint32_t khw;                   // Kitty high plane, dword = lane
+    uint32_t kiw;                   // KITTY_DYN: channel ids of offsets 4g .. 4g+3
 };
 
-template <bool KITTY>
+template <bool KITTY, bool DYN>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(3, 8)))
 void stage1_head_mfma_kernel(KParams P, const uint16_t *__restrict__ q, Workspace W, float qscale) {
+    constexpr int SCHEME = DYN ? KVQ_SCHEME_KITTY_DYN : KITTY ? KVQ_SCHEME_KITTY : KVQ_SCHEME_KIVI2;
     const S1Item it = s1_item(W.max_splits, W.n_win);
     const int s = it.s, hq = it.hd, b = it.b;
     const int lane = threadIdx.x, g = lane >> 4, r = lane & 15;
@@ -1032,7 +1049,7 @@ void stage1_head_mfma_kernel(KParams P, const uint16_t *__restrict__ q, Workspac
         WinSmem win;
     } U;
     if (it.window) {                             // this query head's fp16 window
-        window_partial<1, 16, KITTY ? KVQ_SCHEME_KITTY : KVQ_SCHEME_KIVI2>(P, q, W, qscale, b, h, hq, s, lane, U.win);
+        window_partial<1, 16, SCHEME>(P, q, W, qscale, b, h, hq, s, lane, U.win);
         return;
     }
     HeadSmem &sm = U.pg;
@@ -1063,7 +1080,7 @@ void stage1_head_mfma_kernel(KParams P, const uint16_t *__restrict__ q, Workspac
     }
     if (lane == 0) sm.Bz = h8v{0, 0, 0, 0, 0, 0, 0, 0};
     int kc_off[4] = {0, 0, 0, 0};                // Kitty: channels of offsets 4g .. 4g+3
-    if (KITTY) {
+    if (KITTY && !DYN) {
         if (lane < NB) sm.inv[lane] = 0;
         lds_sync();
         for (int c = lane; c < D; c += 64) {
@@ -1134,6 +1151,10 @@ void stage1_head_mfma_kernel(KParams P, const uint16_t *__restrict__ q, Workspac
                 sc[n] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[n >> 1], bf[n], sc[n], 0, 0, 0);
         }
         if (KITTY) {
+            if (DYN) {                           // this page's boosted channels
+#pragma unroll
+                for (int i = 0; i < 4; i++) kc_off[i] = (HP.kiw >> (8 * i)) & (D - 1);
+            }
             // tile n: key group n >> 1, plane half n >> 1 (bit 2), nibble half n & 1
             const h8v bk0 = frag8_x4(HP.khw & MSK), bk1 = frag8_x4((HP.khw >> 2) & MSK);
 #pragma unroll
@@ -1215,6 +1236,7 @@ void stage1_head_mfma_kernel(KParams P, const uint16_t *__restrict__ q, Workspac
         HeadPage HP;
         HP.R = load_page_masked(pg, i < np, G, lane);
         HP.khw = KITTY ? bload1(page_rsrc(pg, i < np, G), G.kh + 4 * lane) : 0u;
+        HP.kiw = DYN ? bload1(page_rsrc(pg, i < np, G), G.ki + 4 * g) : 0u;
         return HP;
     };
     // two register sets used in turn (the page after the one being processed
@@ -1529,10 +1551,12 @@ hipError_t launch_decode(const KParams &P, const uint16_t *q, float *out, float 
             else
                 stage1_valu_kernel<false><<<g1, 64, 0, s>>>(P, q, W, qscale);
         } else {
-            if (kitty)
-                stage1_head_mfma_kernel<true><<<g1, 64, 0, s>>>(P, q, W, qscale);
+            if (P.scheme == KVQ_SCHEME_KITTY_DYN)
+                stage1_head_mfma_kernel<true, true><<<g1, 64, 0, s>>>(P, q, W, qscale);
+            else if (kitty)
+                stage1_head_mfma_kernel<true, false><<<g1, 64, 0, s>>>(P, q, W, qscale);
             else
-                stage1_head_mfma_kernel<false><<<g1, 64, 0, s>>>(P, q, W, qscale);
+                stage1_head_mfma_kernel<false, false><<<g1, 64, 0, s>>>(P, q, W, qscale);
         }
     }
     hipError_t e = hipGetLastError();

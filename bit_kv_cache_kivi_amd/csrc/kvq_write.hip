@@ -28,10 +28,50 @@ __device__ inline bool page_ok(const KParams &P, int pid) {
 // half = tid >> 7) takes the two 32-token groups half, half + 2 ... of its
 // channel.  codes: LDS scratch [64][128].
 // ---------------------------------------------------------------------------
+// |x| * 2^24 of a binary16 value as an exact integer (finite values: at most
+// 2^40, so 64 of them add exactly in 64 bits)
+__device__ inline uint64_t mag24(uint16_t h) {
+    const uint32_t e = (h >> 10) & 31u, m = h & 0x3ffu;
+    return e == 0 ? (uint64_t)m : (uint64_t)(0x400u | m) << (e - 1);
+}
+
+// KITTY_DYN: the page's boosted channels, the NB largest sum_t |x_{t,c}| over
+// its 64 tokens (the mean up to the fixed count; ties to the lower channel),
+// into bits4 / inv and the page's KI bytes (channel ids, ascending)
+__device__ void select_page_boost(const Geom &G, const uint16_t *src, uint8_t *page, int *inv,
+                                  uint8_t *bits4) {
+    __shared__ uint64_t imp[D];
+    const int tid = threadIdx.x;
+    if (tid < D) {
+        uint64_t sum = 0;
+        for (int t = 0; t < PT; t++) sum += mag24(src[(size_t)t * D + tid]);
+        imp[tid] = sum;
+    }
+    __syncthreads();
+    if (tid < D) {
+        const uint64_t mine = imp[tid];
+        int rank = 0;
+        for (int c2 = 0; c2 < D; c2++) {
+            const uint64_t o = imp[c2];
+            rank += (o > mine || (o == mine && c2 < tid)) ? 1 : 0;
+        }
+        bits4[tid] = rank < NB ? 1 : 0;
+    }
+    __syncthreads();
+    if (tid < D && bits4[tid]) {
+        int off = 0;
+        for (int c2 = 0; c2 < tid; c2++) off += bits4[c2];
+        inv[off] = tid;
+        page[G.ki + off] = (uint8_t)tid;
+    }
+    __syncthreads();
+}
+
 __device__ void quant_key_page(const KParams &P, const Geom &G, const uint16_t *src,
-                               uint8_t *page, const int *inv, const uint8_t *bits4,
+                               uint8_t *page, int *inv, uint8_t *bits4,
                                uint8_t (*codes)[D]) {
     const int tid = threadIdx.x;
+    if (P.scheme == KVQ_SCHEME_KITTY_DYN) select_page_boost(G, src, page, inv, bits4);
     const int c = tid & 127;
     const int gi = tid >> 7;                         // group 0 or 1 of the page
     const float lmax = bits4[c] ? 15.0f : 3.0f;
@@ -66,7 +106,7 @@ __device__ void quant_key_page(const KParams &P, const Geom &G, const uint16_t *
             }
         kc[w] = val;
     }
-    if (P.scheme == KVQ_SCHEME_KITTY && tid < 64) {
+    if (is_kitty(P.scheme) && tid < 64) {
         uint32_t *kh = (uint32_t *)(page + G.kh);
         int g = tid >> 4, r = tid & 15;
         uint32_t val = 0;

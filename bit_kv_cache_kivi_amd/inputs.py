@@ -40,7 +40,7 @@ _CTX_K, _CTX_V, _STEP_Q, _STEP_K, _STEP_V, _OUTLIERS, _LENGTHS, _PAGES, _QDEC = 
 class Workload:
     wid: int
     name: str
-    scheme: str            # "kivi2" | "kitty" | "witcert"
+    scheme: str            # "kivi2" | "kitty" | "witcert" | "kitty_dyn"
     B: int
     Hq: int
     Hkv: int
@@ -73,7 +73,7 @@ def _lengths3(B: int, lo: int, hi: int, seed: int) -> tuple:
 
 
 def workload(wid: int, **over) -> Workload:
-    """The five workloads at full size; keyword overrides give scaled-down cases."""
+    """The workloads at full size; keyword overrides give scaled-down cases."""
     if wid == 1:
         w = dict(wid=1, name="kivi2-b1-h1-ctx1024", scheme="kivi2", B=1, Hq=1, Hkv=1,
                  ctx=(1024,), outlier_ch=(3, 77), outlier_factor=20.0, steps=1, seed=1)
@@ -90,6 +90,11 @@ def workload(wid: int, **over) -> Workload:
     elif wid == 5:
         w = dict(wid=5, name="witcert-int8-b32-32q8kv-ctx16384", scheme="witcert", B=32, Hq=32,
                  Hkv=8, ctx=(16384,) * 32, steps=1, seed=5)
+    elif wid == 6:
+        # workload 4's shapes with the boosted set chosen per page
+        w = dict(wid=6, name="kitty-dyn-mha-b16-h32-ctx32768", scheme="kitty_dyn", B=16, Hq=32,
+                 Hkv=32, ctx=(32768,) * 16, n_outliers=4, outlier_factor=15.0, nb=16, steps=1,
+                 seed=6)
     else:
         raise ValueError(wid)
     w.update(over)

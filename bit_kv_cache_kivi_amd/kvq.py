@@ -18,8 +18,9 @@ import numpy as np
 PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG, "libkvq.so")
 
-KVQ_SCHEME_KIVI2, KVQ_SCHEME_KITTY, KVQ_SCHEME_WITCERT = 0, 1, 2
-SCHEMES = {"kivi2": KVQ_SCHEME_KIVI2, "kitty": KVQ_SCHEME_KITTY, "witcert": KVQ_SCHEME_WITCERT}
+KVQ_SCHEME_KIVI2, KVQ_SCHEME_KITTY, KVQ_SCHEME_WITCERT, KVQ_SCHEME_KITTY_DYN = 0, 1, 2, 3
+SCHEMES = {"kivi2": KVQ_SCHEME_KIVI2, "kitty": KVQ_SCHEME_KITTY, "witcert": KVQ_SCHEME_WITCERT,
+           "kitty_dyn": KVQ_SCHEME_KITTY_DYN}
 
 KVQ_OK, KVQ_EINVAL, KVQ_ENULL, KVQ_EALIGN, KVQ_ENOLAYOUT, KVQ_EWORKSPACE, KVQ_ELAUNCH = \
     0, -1, -2, -3, -4, -5, -6
@@ -148,7 +149,8 @@ def make_layout(scheme: str, B: int, Hq: int, Hkv: int, max_pages: int, n_pages:
     s = SCHEMES[scheme]
     return kvq_layout_t(scheme=s, head_dim=128, n_q_heads=Hq, n_kv_heads=Hkv, batch=B, group=32,
                         value_group=32, residual=R, block=256,
-                        n_boost=(16 if s == KVQ_SCHEME_KITTY else 0) if nb is None else nb,
+                        n_boost=(16 if s in (KVQ_SCHEME_KITTY, KVQ_SCHEME_KITTY_DYN) else 0)
+                        if nb is None else nb,
                         max_pages=max_pages, n_pages=n_pages, split_pages=split_pages,
                         flags=flags, layer=layer, seed=seed)
 

@@ -17,6 +17,16 @@
  *                      summary: Channel-Wise Precision Boost Mechanism;
  *                      Page-Centric Memory Layout and Dense-Sparse
  *                      Decomposition; Algorithm 1.)
+ *   KVQ_SCHEME_KITTY_DYN
+ *                      KITTY with the boosted set chosen per 64-token page:
+ *                      the n_boost channels of largest mean |key| over the
+ *                      page's tokens (ties to the lower channel), picked when
+ *                      the page's keys are quantized; the page stores the
+ *                      chosen channel ids in ascending order (16 bytes).
+ *                      ("Kitty" summary: Channel-Wise Precision Boost
+ *                      Mechanism, importance as the mean absolute value of a
+ *                      group; a group here is one page.)  No calibration and
+ *                      no boost_idx buffer.
  *   KVQ_SCHEME_WITCERT INT8 keys and values with subtractive dither:
  *                      x_hat = s (round(x/s + xi) - xi), s = amax/126.5 per
  *                      (256-token block, channel) stored fp16 and used for
@@ -59,14 +69,16 @@ extern "C" {
 enum {
     KVQ_SCHEME_KIVI2 = 0,
     KVQ_SCHEME_KITTY = 1,
-    KVQ_SCHEME_WITCERT = 2
+    KVQ_SCHEME_WITCERT = 2,
+    KVQ_SCHEME_KITTY_DYN = 3
 };
 
 /* layout flags */
 enum {
     KVQ_FLAG_GENERIC_STAGE1 = 1  /* KIVI2 / KITTY: run the per-query-head VALU
                                     stage 1 instead of the matrix-core one
-                                    (a second implementation, for comparison) */
+                                    (a second implementation, for comparison);
+                                    not available for KITTY_DYN */
 };
 
 /* host-side return codes */
@@ -99,9 +111,10 @@ typedef struct kvq_layout {
     int32_t group;           /* G, key group tokens; must be 32 (KIVI2/KITTY) */
     int32_t value_group;     /* value group channels; must be 32 (KIVI2/KITTY) */
     int32_t residual;        /* R, key/value fp16 window; multiple of 64 (so of
-                                G), 64 .. 256 (KIVI2/KITTY) */
+                                G), 64 .. 256 (KIVI2/KITTY/KITTY_DYN) */
     int32_t block;           /* WitCert block tokens; must be 256 (WITCERT) */
-    int32_t n_boost;         /* KITTY boosted key channels: 16 (0 for others) */
+    int32_t n_boost;         /* KITTY / KITTY_DYN boosted key channels: 16
+                                (0 for others) */
     int32_t max_pages;       /* page-table row length per request */
     int32_t n_pages;         /* pages in the pool */
     int32_t split_pages;     /* stage-1 split size in pages; 0: 8 when max_pages
@@ -153,10 +166,11 @@ typedef struct kvq_cache {
  *   [1, 65535]; max_pages or n_pages < 1; split_pages outside [0, 64] (0 picks
  *   a default), or max_pages needs more than 256 splits of the resolved size
  *   (at most 64 pages); flags other than KVQ_FLAG_*; unknown scheme;
- *   KIVI2 / KITTY: group or value_group != 32; residual not a multiple of 64
- *   or outside [64, 256] (the residual is quantized in whole key groups, so it
- *   must be divisible by the group, "KIVI" explainer 3.3, and the flush fills
- *   whole 64-token pages); n_boost != 16 for KITTY or != 0 for KIVI2;
+ *   KIVI2 / KITTY / KITTY_DYN: group or value_group != 32; residual not a
+ *   multiple of 64 or outside [64, 256] (the residual is quantized in whole
+ *   key groups, so it must be divisible by the group, "KIVI" explainer 3.3,
+ *   and the flush fills whole 64-token pages); n_boost != 16 for KITTY and
+ *   KITTY_DYN or != 0 for KIVI2; KVQ_FLAG_GENERIC_STAGE1 with KITTY_DYN;
  *   WITCERT: block != 256; layer >= 65536; query heads per KV head not in
  *   {1, 2, 4, 8}. */
 int kvq_set_layout(kvq_cache_t *cache, const kvq_layout_t *layout,

@@ -7,7 +7,7 @@ import numpy as np
 from bit_kv_cache_kivi_amd import inputs
 from layout_unpack import PT, WPT, gather_kivi, page_block, witcert_block
 
-SCHEME_ID = {"kivi2": 0, "kitty": 1, "witcert": 2}
+SCHEME_ID = {"kivi2": 0, "kitty": 1, "witcert": 2, "kitty_dyn": 3}
 
 
 class Case:
@@ -58,7 +58,7 @@ class Case:
         for b, h in self.sample:
             s = O.Stream(self.sid, self.cap, D=128, G=w.G, R=w.R, VG=w.VG, BLK=w.BLK,
                          nb=w.nb, idx=None if self.idx is None else self.idx[h],
-                         seed=self.seed, req=b, layer=0, kvh=h)
+                         seed=self.seed, req=b, layer=0, kvh=h, sel=PT)
             K, V = inputs.context_kv(w, b, h)
             s.prefill(K, V)
             self.streams[(b, h)] = s
@@ -144,8 +144,14 @@ class Case:
                 assert np.array_equal(rk[b, h, :n], Kraw[n_kq:l])
                 assert np.array_equal(rv[b, h, :n], Vraw[n_kq:l])
                 continue
+            pidx = []
             kc, ks, kz, vc, vs, vz = gather_kivi(pool, self.table[b], h, w.Hkv, self.sid, n_kq,
-                                                 n_vq, None if self.idx is None else self.idx[h])
+                                                 n_vq, None if self.idx is None else self.idx[h],
+                                                 page_idx=pidx)
+            if w.scheme == "kitty_dyn":               # each key page's boosted channel set
+                ou = s.unit_index()
+                for p in range(n_kq // PT):
+                    assert np.array_equal(pidx[p], ou[p]), ("page boost index", b, h, p)
             okc, ovc = s.key_codes(), s.value_codes()
             oks, okz = s.key_stats()
             ovs, ovz = s.value_stats()

@@ -10,11 +10,13 @@ D = 128
 PT = 64
 WPT = 256
 
-GEOM = {  # kc, kh, ks, vc, vs, bytes
+GEOM = {  # kc, kh, ks, vc, vs, (ki,) bytes
     0: dict(kc=0, kh=0, ks=2048, vc=3072, vs=5120, bytes=6144, tokens=PT),
     1: dict(kc=0, kh=2048, ks=2304, vc=3328, vs=5376, bytes=6400, tokens=PT),
     2: dict(kc=0, kh=0, ks=32768, vc=33024, vs=65792, bytes=66048, tokens=WPT),
+    3: dict(kc=0, kh=2048, ks=2304, vc=3328, vs=5376, ki=6400, bytes=6416, tokens=PT),
 }
+KITTY_SCHEMES = (1, 3)
 
 
 def _key_index():
@@ -66,7 +68,7 @@ def key_codes(block: np.ndarray, scheme: int) -> np.ndarray:
 
 
 def key_high(block: np.ndarray) -> np.ndarray:
-    """Kitty high plane [64][16] by boosted offset."""
+    """Kitty high plane [64][16] by boosted offset (same place in both Kitty schemes)."""
     g = GEOM[1]
     kh = _u32(block, g["kh"], 64)
     return ((kh[HI_DW] >> HI_SH) & 3).astype(np.uint8)
@@ -77,6 +79,15 @@ def key_stats(block: np.ndarray, scheme: int):
     g = GEOM[scheme]
     ks = _u32(block, g["ks"], 256).reshape(2, 128)[:, KEY_SLOT]
     return (ks & 0xFFFF).astype(np.uint16), (ks >> 16).astype(np.uint16)
+
+
+def page_boost_index(block: np.ndarray, nb: int = 16) -> np.ndarray:
+    """Kitty dynamic: the page's boost index per channel (offset, or nb + 1)
+    from its stored channel ids."""
+    ids = block[GEOM[3]["ki"]:GEOM[3]["ki"] + nb]
+    idx = np.full(D, nb + 1, np.uint8)
+    idx[ids.astype(np.int64)] = np.arange(nb, dtype=np.uint8)
+    return idx
 
 
 def value_codes(block: np.ndarray, scheme: int) -> np.ndarray:
@@ -108,10 +119,12 @@ def page_block(pool: np.ndarray, pid: int, h: int, Hkv: int, scheme: int) -> np.
     return pool[off:off + nb]
 
 
-def gather_kivi(pool, table_row, h, Hkv, scheme, n_kq, n_vq, idx=None):
+def gather_kivi(pool, table_row, h, Hkv, scheme, n_kq, n_vq, idx=None, page_idx=None):
     """Logical record of one (request, KV head) for tokens below n_kq / n_vq:
     key codes (4-bit for Kitty boosted channels) [n_kq][128], key stats
-    [n_kq/32][128] x2, value codes [n_vq][128], value stats [n_vq][4] x2."""
+    [n_kq/32][128] x2, value codes [n_vq][128], value stats [n_vq][4] x2.
+    Kitty dynamic: each page's own index; pass a list as page_idx to receive
+    the indices of the key pages."""
     kcodes = np.zeros((n_kq, D), np.uint8)
     ks = np.zeros((n_kq // 32, D), np.uint16)
     kz = np.zeros((n_kq // 32, D), np.uint16)
@@ -123,11 +136,14 @@ def gather_kivi(pool, table_row, h, Hkv, scheme, n_kq, n_vq, idx=None):
         t0 = p * PT
         if t0 < n_kq:
             codes = key_codes(blk, scheme).astype(np.uint8)
-            if scheme == 1:
+            if scheme in KITTY_SCHEMES:
+                pidx = idx if scheme == 1 else page_boost_index(blk)
+                if page_idx is not None:
+                    page_idx.append(pidx)
                 hi = key_high(blk)
                 for c in range(D):
-                    if idx[c] < 16:
-                        codes[:, c] |= hi[:, idx[c]] << 2
+                    if pidx[c] < 16:
+                        codes[:, c] |= hi[:, pidx[c]] << 2
             kcodes[t0:t0 + PT] = codes
             s, z = key_stats(blk, scheme)
             ks[t0 // 32:t0 // 32 + 2] = s

@@ -58,20 +58,23 @@ def set_layout(K, L, B=None):
     return rc, cache
 
 
-@pytest.mark.parametrize("scheme", ["kivi2", "kitty", "witcert"])
+@pytest.mark.parametrize("scheme", ["kivi2", "kitty", "witcert", "kitty_dyn"])
 def test_valid_layouts(K, scheme):
     L = K.make_layout(scheme, B=64, Hq=32, Hkv=8, max_pages=512, n_pages=32768)
     rc, cache = set_layout(K, L)
     assert rc == K.KVQ_OK
     assert cache.page_tokens == (256 if scheme == "witcert" else 64)
-    assert cache.page_bytes == {"kivi2": 6144, "kitty": 6400, "witcert": 66048}[scheme]
+    assert cache.page_bytes == {"kivi2": 6144, "kitty": 6400, "witcert": 66048,
+                                "kitty_dyn": 6416}[scheme]
 
 
 def test_page_geometry_and_bytes_per_token(K):
     # 96 B/token/KV head for KIVI-2 (codes + fp16 statistics of keys and
     # values), 100 with Kitty's 16-channel high plane, 258 for the INT8 block
-    # scheme (128 codes + an fp16 scale per 256-token block and channel, twice)
-    for scheme, bpt in (("kivi2", 96.0), ("kitty", 100.0), ("witcert", 258.0)):
+    # scheme (128 codes + an fp16 scale per 256-token block and channel, twice);
+    # Kitty dynamic adds the page's 16 boosted channel ids (0.25 B/token)
+    for scheme, bpt in (("kivi2", 96.0), ("kitty", 100.0), ("witcert", 258.0),
+                        ("kitty_dyn", 100.25)):
         L = K.make_layout(scheme, B=1, Hq=1, Hkv=1, max_pages=1, n_pages=1)
         assert K.bytes_per_token(L) == bpt
         assert K.page_bytes(L) == bpt * K.page_tokens(L)
@@ -83,7 +86,7 @@ def test_page_geometry_and_bytes_per_token(K):
 INVALID = [
     ("head_dim", 64), ("n_kv_heads", 0), ("n_kv_heads", 65536), ("n_q_heads", 12),
     ("n_q_heads", 72), ("batch", 0), ("batch", 65536), ("max_pages", 0), ("n_pages", 0),
-    ("split_pages", -1), ("split_pages", 65), ("flags", 2), ("scheme", 3),
+    ("split_pages", -1), ("split_pages", 65), ("flags", 2), ("scheme", 4), ("scheme", -1),
     ("group", 64), ("value_group", 16), ("residual", 96), ("residual", 100),
     ("residual", 0), ("residual", 320), ("n_boost", 4),
 ]
@@ -111,6 +114,15 @@ def test_residual_must_hold_whole_key_groups(K):
 def test_kitty_and_witcert_fields(K):
     L = K.make_layout("kitty", B=1, Hq=4, Hkv=4, max_pages=8, n_pages=8, nb=0)
     assert set_layout(K, L)[0] == K.KVQ_EINVAL
+    L = K.make_layout("kitty_dyn", B=1, Hq=4, Hkv=4, max_pages=8, n_pages=8, nb=8)
+    assert set_layout(K, L)[0] == K.KVQ_EINVAL
+    # the VALU stage 1 knows only the static boost table
+    L = K.make_layout("kitty_dyn", B=1, Hq=4, Hkv=4, max_pages=8, n_pages=8,
+                      flags=K.FLAG_GENERIC_STAGE1)
+    assert set_layout(K, L)[0] == K.KVQ_EINVAL
+    L = K.make_layout("kitty", B=1, Hq=4, Hkv=4, max_pages=8, n_pages=8,
+                      flags=K.FLAG_GENERIC_STAGE1)
+    assert set_layout(K, L)[0] == K.KVQ_OK
     L = K.make_layout("witcert", B=1, Hq=32, Hkv=8, max_pages=8, n_pages=8)
     L.block = 128
     assert set_layout(K, L)[0] == K.KVQ_EINVAL
@@ -134,6 +146,8 @@ def test_null_and_alignment(K):
     assert set_layout(K, L, bufs(K, boost_idx=0))[0] == K.KVQ_OK      # only Kitty needs it
     Lk = K.make_layout("kitty", B=1, Hq=1, Hkv=1, max_pages=8, n_pages=8)
     assert set_layout(K, Lk, bufs(K, boost_idx=0))[0] == K.KVQ_ENULL
+    Ld = K.make_layout("kitty_dyn", B=1, Hq=1, Hkv=1, max_pages=8, n_pages=8)
+    assert set_layout(K, Ld, bufs(K, boost_idx=0))[0] == K.KVQ_OK    # chosen per page
     for f, off in (("pool", 16), ("page_table", 4), ("state", 8), ("res_k", 2), ("res_v", 8),
                    ("status", 2)):
         b = bufs(K)

@@ -81,5 +81,9 @@ def test_kitty_b16_h32_ctx32768():
     _run(inputs.workload(4))
 
 
+def test_kitty_dynamic_b16_h32_ctx32768():
+    _run(inputs.workload(6))
+
+
 def test_witcert_b32_32q8kv_ctx16384_certificate():
     _run(inputs.workload(5), kappa=2.0, cert_check=True)

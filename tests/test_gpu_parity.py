@@ -117,6 +117,25 @@ def test_kitty_calibrate_store_decode(flags):
     case.check_store()
 
 
+@pytest.mark.parametrize("Hq,Hkv,split", [(2, 2, 3), (8, 2, 2)])
+def test_kitty_dynamic_store_decode(Hq, Hkv, split):
+    # boosted set chosen per page: bit-exact codes, high plane and per-page
+    # channel ids through prefill and two flushes, decode to the tolerance
+    w = inputs.workload(6, B=2, Hq=Hq, Hkv=Hkv, ctx=(1100, 1500))
+    case = _case(w, extra_tokens=300, split_pages=split)
+    case.check_state()
+    case.check_store()
+    out, cert, q = case.decode_now(1)
+    _check_decode(case, out, cert, q)
+    for i in range(260):
+        out, cert, q = case.step(decode=(i % 64 == 63 or i in (0, 1, 127, 128)))
+        if out is not None:
+            _check_decode(case, out, cert, q)
+    case.check_status()
+    case.check_state()
+    case.check_store()
+
+
 @pytest.mark.parametrize("Hq,Hkv", [(8, 2), (2, 2)])
 def test_witcert_store_decode_certificate(Hq, Hkv):
     w = inputs.workload(5, B=2, Hq=Hq, Hkv=Hkv, ctx=(700, 1024))
