@@ -323,17 +323,23 @@ typedef struct ko_stream {
     uint16_t *Vs, *Vz;       /* KIVI/Kitty: [cap][D/VG]; WitCert Vs: [cap/BLK][D] */
     uint8_t idx[256];        /* Kitty boost index per channel (static) */
     long sel;                /* Kitty dynamic: tokens per selection unit */
+    long sink;               /* leading tokens kept fp16 for keys and values */
     uint8_t *uidx;           /* Kitty dynamic: [cap/sel + 1][D] boost index per unit */
     uint64_t seed;
     uint32_t req, layer, kvh;
 } ko_stream;
 
 /* sel: tokens per selection unit for KO_KITTY_DYN (a multiple of G that
- * divides R, so a flush always quantizes whole units); ignored otherwise. */
+ * divides R, so a flush always quantizes whole units); ignored otherwise.
+ * sink: the first `sink` tokens of the stream stay fp16, keys and values
+ * ([KITTY] sink tokens; KIVI2 / Kitty only); groups, selection units and the
+ * value FIFO then start at token `sink`. */
 ko_stream *ko_stream_new(int scheme, int D, int G, int R, int VG, int BLK,
                          int nb, const uint8_t *idx, long cap,
-                         uint64_t seed, uint32_t req, uint32_t layer, uint32_t kvh, long sel)
+                         uint64_t seed, uint32_t req, uint32_t layer, uint32_t kvh, long sel,
+                         long sink)
 {
+    if (sink < 0 || (sink > 0 && scheme == KO_WITCERT)) return NULL;
     if (D <= 0 || D > 256 || cap <= 0) return NULL;
     if (scheme < KO_KIVI || scheme > KO_KITTY_DYN) return NULL;
     if (scheme != KO_WITCERT) {
@@ -351,6 +357,7 @@ ko_stream *ko_stream_new(int scheme, int D, int G, int R, int VG, int BLK,
         s->uidx = (uint8_t *)calloc((size_t)((cap / sel + 1) * D), 1);
     }
     s->cap = cap;
+    s->sink = sink;
     s->seed = seed; s->req = req; s->layer = layer; s->kvh = kvh;
     s->Kraw = (uint16_t *)calloc((size_t)(cap * D), 2);
     s->Vraw = (uint16_t *)calloc((size_t)(cap * D), 2);
@@ -376,6 +383,9 @@ void ko_stream_free(ko_stream *s)
     free(s);
 }
 
+/* Key groups and selection units count from token `sink`: group g holds
+ * tokens [sink + gG, sink + (g+1)G). */
+
 /* Boost index of key group g, channel c: the head's static index, or the
  * index of the selection unit holding the group. */
 static int boost_off(const ko_stream *s, long g, int c)
@@ -396,15 +406,16 @@ static int key_bits(const ko_stream *s, long g, int c)
  * boosted channels from the unit's raw keys (all present: units divide R). */
 static void quant_key_group(ko_stream *s, long g)
 {
+    long t0 = s->sink + g * s->G;
     if (s->scheme == KO_KITTY_DYN && (g * s->G) % s->sel == 0) {
         long u = g * s->G / s->sel;
-        ko_kitty_select_dyn(&s->Kraw[u * s->sel * s->D], s->sel, s->D, s->D, s->nb,
+        ko_kitty_select_dyn(&s->Kraw[(s->sink + u * s->sel) * s->D], s->sel, s->D, s->D, s->nb,
                             &s->uidx[u * s->D]);
     }
     for (int c = 0; c < s->D; c++)
-        ko_quant_asym(&s->Kraw[g * s->G * s->D + c], s->G, s->D, key_bits(s, g, c),
+        ko_quant_asym(&s->Kraw[t0 * s->D + c], s->G, s->D, key_bits(s, g, c),
                       &s->Ks[g * s->D + c], &s->Kz[g * s->D + c],
-                      &s->Kc[g * s->G * s->D + c], s->D);
+                      &s->Kc[t0 * s->D + c], s->D);
 }
 
 /* [KIVI] 3.3: values leave the R-token FIFO one at a time, each quantized per
@@ -452,7 +463,7 @@ int ko_stream_flush(ko_stream *s)
         return 1;
     }
     if (s->l - s->n_kq != s->R) return 0;
-    for (long g = s->n_kq / s->G; g < (s->n_kq + s->R) / s->G; g++)
+    for (long g = (s->n_kq - s->sink) / s->G; g < (s->n_kq - s->sink + s->R) / s->G; g++)
         quant_key_group(s, g);
     s->n_kq += s->R;
     return 1;
@@ -467,7 +478,13 @@ int ko_stream_append(ko_stream *s, const uint16_t *k, const uint16_t *v)
     if (s->l - s->n_kq >= lim || s->l >= s->cap) return -1;
     memcpy(&s->Kraw[s->l * s->D], k, 2 * (size_t)s->D);
     memcpy(&s->Vraw[s->l * s->D], v, 2 * (size_t)s->D);
-    if (s->scheme != KO_WITCERT && s->l >= s->R) {
+    if (s->l < s->sink) {
+        /* a sink token: kept fp16, never in the residual or the FIFO */
+        s->l += 1;
+        s->n_kq = s->n_vq = s->l;
+        return 0;
+    }
+    if (s->scheme != KO_WITCERT && s->l - s->sink >= s->R) {
         /* the FIFO overflows: the oldest value, token l - R, is quantized */
         quant_value_token(s, s->l - s->R);
         s->n_vq = s->l - s->R + 1;
@@ -495,12 +512,17 @@ int ko_stream_prefill(ko_stream *s, const uint16_t *K, const uint16_t *V, long l
         s->n_vq = s->n_kq;
         return 0;
     }
-    long rk = ((l0 - 1) % s->R) + 1;
+    if (l0 <= s->sink) {                 /* all sink tokens */
+        s->n_kq = s->n_vq = l0;
+        return 0;
+    }
+    long lq = l0 - s->sink;              /* tokens after the sink */
+    long rk = ((lq - 1) % s->R) + 1;
     s->n_kq = l0 - rk;
-    for (long g = 0; g < s->n_kq / s->G; g++)
+    for (long g = 0; g < (s->n_kq - s->sink) / s->G; g++)
         quant_key_group(s, g);
-    s->n_vq = l0 > s->R ? l0 - s->R : 0;
-    for (long t = 0; t < s->n_vq; t++)
+    s->n_vq = s->sink + (lq > s->R ? lq - s->R : 0);
+    for (long t = s->sink; t < s->n_vq; t++)
         quant_value_token(s, t);
     return 0;
 }
@@ -524,20 +546,20 @@ const uint8_t *ko_stream_uidx(const ko_stream *s) { return s->uidx; }
  * residual after; the value is quantized for t < n_vq and fp16 after. */
 static float key_tilde(const ko_stream *s, long t, int c)
 {
-    if (t >= s->n_kq)
+    if (t < s->sink || t >= s->n_kq)
         return ko_f16_to_f32(s->Kraw[t * s->D + c]);
     if (s->scheme == KO_WITCERT) {
         long b = t / s->BLK;
         float xi = ko_dither(s->seed, 0, s->req, s->layer, s->kvh, (uint32_t)t, (uint32_t)c);
         return ko_witcert_dequant((int8_t)s->Kc[t * s->D + c], s->Ks[b * s->D + c], xi);
     }
-    long g = t / s->G;
+    long g = (t - s->sink) / s->G;
     return ko_dequant_asym(s->Kc[t * s->D + c], s->Ks[g * s->D + c], s->Kz[g * s->D + c]);
 }
 
 static float value_tilde(const ko_stream *s, long t, int c)
 {
-    if (t >= s->n_vq)
+    if (t < s->sink || t >= s->n_vq)
         return ko_f16_to_f32(s->Vraw[t * s->D + c]);
     if (s->scheme == KO_WITCERT) {
         long b = t / s->BLK;

@@ -63,7 +63,7 @@ def lib():
         L.ko_kitty_select_dyn.argtypes = [P, C.c_long, C.c_long, C.c_int, C.c_int, P]
         L.ko_stream_new.argtypes = [C.c_int, C.c_int, C.c_int, C.c_int, C.c_int,
                                     C.c_int, C.c_int, P, C.c_long, C.c_uint64,
-                                    C.c_uint32, C.c_uint32, C.c_uint32, C.c_long]
+                                    C.c_uint32, C.c_uint32, C.c_uint32, C.c_long, C.c_long]
         L.ko_stream_new.restype = P
         L.ko_stream_free.argtypes = [P]
         L.ko_stream_flush.argtypes = [P]
@@ -171,13 +171,14 @@ class Stream:
 
     def __init__(self, scheme: int, cap: int, D: int = 128, G: int = 32, R: int = 128,
                  VG: int = 32, BLK: int = 256, nb: int = 0, idx=None,
-                 seed: int = 0, req: int = 0, layer: int = 0, kvh: int = 0, sel: int = 64):
+                 seed: int = 0, req: int = 0, layer: int = 0, kvh: int = 0, sel: int = 64,
+                 sink: int = 0):
         self.scheme, self.cap, self.D, self.G, self.R = scheme, cap, D, G, R
-        self.VG, self.BLK, self.nb, self.sel = VG, BLK, nb, sel
+        self.VG, self.BLK, self.nb, self.sel, self.sink = VG, BLK, nb, sel, sink
         self._idx = None if idx is None else np.ascontiguousarray(idx, np.uint8)
         h = lib().ko_stream_new(scheme, D, G, R, VG, BLK, nb,
                                 None if self._idx is None else _p(self._idx),
-                                cap, seed, req, layer, kvh, sel)
+                                cap, seed, req, layer, kvh, sel, sink)
         if not h:
             raise ValueError("invalid stream parameters")
         self.h = h
@@ -226,7 +227,8 @@ class Stream:
         return self._arr("ko_stream_uidx", n * self.D, np.uint8).reshape(n, self.D)
 
     def key_stats(self):
-        """(scale, zero) fp16 bits: [groups][D] (WitCert: [blocks][D], zero unused)."""
+        """(scale, zero) fp16 bits: [groups][D] (WitCert: [blocks][D], zero unused);
+        groups count from the first token after the sink."""
         n = (self.cap // (self.BLK if self.scheme == WITCERT else self.G)) + 1
         s = self._arr("ko_stream_kscale", n * self.D, np.uint16).reshape(n, self.D)
         z = self._arr("ko_stream_kzero", n * self.D, np.uint16).reshape(n, self.D)
