@@ -24,6 +24,10 @@ int validate_layout(const kvq_layout_t *L) {
     if (L->max_pages < 1 || L->n_pages < 1) return KVQ_EINVAL;
     if (L->split_pages < 0 || L->split_pages > 64) return KVQ_EINVAL;
     if (L->flags & ~KVQ_FLAG_GENERIC_STAGE1) return KVQ_EINVAL;
+    if (L->reserved != 0) return KVQ_EINVAL;
+    // sink tokens: one stage-1 chunk of at most 64 fp16 tokens (KIVI2 / Kitty)
+    if (L->sink < 0 || L->sink > kvq::PT) return KVQ_EINVAL;
+    if (L->sink > 0 && L->scheme == KVQ_SCHEME_WITCERT) return KVQ_EINVAL;
     switch (L->scheme) {
         case KVQ_SCHEME_KIVI2:
         case KVQ_SCHEME_KITTY:
@@ -60,6 +64,9 @@ kvq::KParams params(const kvq_cache_t *C) {
     P.res_v = C->bufs.res_v;
     P.boost_idx = C->bufs.boost_idx;
     P.status = C->bufs.status;
+    P.sink_k = C->bufs.sink_k;
+    P.sink_v = C->bufs.sink_v;
+    P.sink = L.sink;
     P.B = L.batch;
     P.Hq = L.n_q_heads;
     P.Hkv = L.n_kv_heads;
@@ -88,7 +95,8 @@ int max_splits(const kvq_cache_t *C) {
 
 // 64-token chunks of the fp16 window, each a stage-1 partial of its own
 int n_win(const kvq_cache_t *C) {
-    return C->layout.scheme == KVQ_SCHEME_WITCERT ? kvq::WPT / kvq::PT : C->layout.residual / kvq::PT;
+    return C->layout.scheme == KVQ_SCHEME_WITCERT ? kvq::WPT / kvq::PT
+                                                  : C->layout.residual / kvq::PT + (C->layout.sink > 0 ? 1 : 0);
 }
 
 }  // namespace
@@ -120,6 +128,9 @@ int kvq_set_layout(kvq_cache_t *cache, const kvq_layout_t *layout, const kvq_buf
         !bufs->status)
         return KVQ_ENULL;
     if (layout->scheme == KVQ_SCHEME_KITTY && !bufs->boost_idx) return KVQ_ENULL;
+    if (layout->sink > 0 && (!bufs->sink_k || !bufs->sink_v)) return KVQ_ENULL;
+    if ((bufs->sink_k && !aligned(bufs->sink_k, 16)) || (bufs->sink_v && !aligned(bufs->sink_v, 16)))
+        return KVQ_EALIGN;
     if (!aligned(bufs->pool, 256) || !aligned(bufs->page_table, 16) || !aligned(bufs->state, 16) ||
         !aligned(bufs->res_k, 16) || !aligned(bufs->res_v, 16) || !aligned(bufs->status, 4))
         return KVQ_EALIGN;

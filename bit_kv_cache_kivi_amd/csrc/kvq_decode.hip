@@ -127,17 +127,20 @@ __device__ void window_partial(const KParams &P, const uint16_t *__restrict__ q,
     const int g = lane >> 4, r = lane & 15;
     const size_t bh = (size_t)b * P.Hkv + h;
     const int l = P.state[bh * 4], nkq = P.state[bh * 4 + 1];
-    const int W0 = wit ? nkq : (l > P.R ? l - P.R : 0);        // first fp16-value token
+    const int S = wit ? 0 : P.sink;
+    // the last chunk item is the sink segment [0, min(l, S)) when there is one
+    const bool sinkc = S > 0 && wc == W.n_win - 1;
+    const int W0 = wit ? nkq : max(S, l - P.R);                // first fp16-value token after the sink
     const int win = wit ? WPT : P.R;
-    const int t0 = W0 + PT * wc;                                  // this chunk: [t0, t0 + n)
-    const int n = max(0, min(PT, l - t0));
-    const int pA = t0 / PT;
-    const bool anyq = !wit && n > 0 && t0 < nkq;   // uniform: some key of the chunk is still quantized
+    const int t0 = sinkc ? 0 : W0 + PT * wc;                      // this chunk: [t0, t0 + n)
+    const int n = sinkc ? min(l, S) : max(0, min(PT, l - t0));
+    const int pA = (t0 - S) / PT;                                 // quantized positions count from S
+    const bool anyq = !wit && !sinkc && n > 0 && t0 < nkq;        // uniform: a key of the chunk is quantized
 
     // every load the chunk needs is issued first: page ids, values (lane =
     // channels 2*lane, 2*lane+1; VPF tokens per round) and the query operand
     int pid_l = -1;
-    if (anyq && lane < 2 && (pA + lane) * PT < min(t0 + n, nkq)) {
+    if (anyq && lane < 2 && S + (pA + lane) * PT < min(t0 + n, nkq)) {
         pid_l = P.table[(size_t)b * P.max_pages + pA + lane];
         if (pid_l < 0 || pid_l >= P.n_pages) {
             atomicOr(P.status, (uint32_t)KVQ_STATUS_UNMAPPED_PAGE);
@@ -146,6 +149,12 @@ __device__ void window_partial(const KParams &P, const uint16_t *__restrict__ q,
     }
     uint32_t vv[VPF];
     auto load_v = [&](int tt0) {
+        if (sinkc) {
+#pragma unroll
+            for (int u = 0; u < VPF; u++)
+                vv[u] = tt0 + u < n ? *(const uint32_t *)(P.sink_v + (bh * S + (size_t)(tt0 + u)) * D + 2 * lane) : 0u;
+            return;
+        }
         int slot = wit ? t0 + tt0 - nkq : (t0 + tt0) % P.R;
 #pragma unroll
         for (int u = 0; u < VPF; u++) {
@@ -198,12 +207,13 @@ __device__ void window_partial(const KParams &P, const uint16_t *__restrict__ q,
             bl4[kc] = make_uint4(0u, 0u, 0u, 0u);
         }
         if (tt < n) {
-            if (wit || t >= nkq) {                // fp16 key: exact in the operand
-                const uint4 *kr = (const uint4 *)(P.res_k + (bh * win + (size_t)(t - nkq)) * D);
+            if (wit || sinkc || t >= nkq) {       // fp16 key: exact in the operand
+                const uint4 *kr = sinkc ? (const uint4 *)(P.sink_k + (bh * S + (size_t)t) * D)
+                                        : (const uint4 *)(P.res_k + (bh * win + (size_t)(t - nkq)) * D);
 #pragma unroll
                 for (int kc = 0; kc < 4; kc++) bh4[kc] = kr[4 * kc + g];
             } else {                              // quantized key: fl32(code s + z), split hi + lo
-                const int pi = t / PT - pA, tp = t % PT, gi = tp >> 5, n16 = tp >> 4;
+                const int pi = (t - S) / PT - pA, tp = (t - S) % PT, gi = tp >> 5, n16 = tp >> 4;
                 const uint8_t *pg = cpage(P, pi ? pids[1] : pids[0], h);
                 const uint32_t *kcw = (const uint32_t *)(pg + G.kc);
                 uint32_t xa[2];
@@ -372,7 +382,7 @@ __global__ __launch_bounds__(64) void stage1_valu_kernel(KParams P, const uint16
     }
     const size_t bh = (size_t)b * P.Hkv + h;
     const int l = P.state[bh * 4];
-    const int nvq = l > P.R ? l - P.R : 0;
+    const int nvq = max(0, l - P.sink - P.R);          // quantized values, counted from the sink
     const int npages = (nvq + PT - 1) / PT;
     const int p0 = s * P.split_pages;
     const int p1 = min(p0 + P.split_pages, npages);
@@ -902,7 +912,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(3, 8))) void
     for (int hq = 0; hq < 4; hq++)
         qw[hq] = *(const uint2 *)(q + ((size_t)b * P.Hq + (size_t)h * 4 + hq) * D + 4 * (lane & 31));
 
-    const int nvq = l > P.R ? l - P.R : 0;
+    const int nvq = max(0, l - P.sink - P.R);          // quantized values, counted from the sink
     const int npages = (nvq + PT - 1) / PT;
     const int p1 = min(p0 + P.split_pages, npages);
     if (p0 >= p1) return;
@@ -1061,7 +1071,7 @@ void stage1_head_mfma_kernel(KParams P, const uint16_t *__restrict__ q, Workspac
     const uint16_t *qh = q + ((size_t)b * P.Hq + hq) * D;
     const uint2 qraw = *(const uint2 *)(qh + 4 * (lane & 31));
 
-    const int nvq = l > P.R ? l - P.R : 0;
+    const int nvq = max(0, l - P.sink - P.R);          // quantized values, counted from the sink
     const int npages = (nvq + PT - 1) / PT;
     const int p1 = min(p0 + P.split_pages, npages);
     if (p0 >= p1) return;
@@ -1456,7 +1466,7 @@ __global__ __launch_bounds__(64) void merge_kernel(KParams P, float *__restrict_
     const int h = hq / P.qpk;
     const size_t bh = (size_t)b * P.Hkv + h;
     const int l = P.state[bh * 4], nkq = P.state[bh * 4 + 1];
-    const int npages = wit ? nkq / WPT : ((l > P.R ? l - P.R : 0) + PT - 1) / PT;
+    const int npages = wit ? nkq / WPT : (max(0, l - P.sink - P.R) + PT - 1) / PT;
     const int nsplit = (npages + P.split_pages - 1) / P.split_pages;
     const int ne = nsplit + W.n_win;              // entries nsplit.. are the window chunks
     const size_t row0 = part_row(W, P.Hq, b, hq, 0);

@@ -15,7 +15,10 @@ struct KParams {
     uint16_t *res_v;
     const uint8_t *boost_idx;
     uint32_t *status;
+    uint16_t *sink_k;             // [B][Hkv][sink][D] fp16 (sink > 0)
+    uint16_t *sink_v;
     int B, Hq, Hkv, R, max_pages, n_pages, page_bytes, scheme, qpk, split_pages;
+    int sink;                     // leading fp16 tokens; quantized positions are t - sink
     int force_generic;            // 1: use the per-query-head VALU stage 1
     uint32_t layer;
     uint64_t seed;
@@ -25,12 +28,12 @@ struct KParams {
 //   o[128] fp32 (acc / l_s), then {lse_s, A_s} fp32 pairs.
 // Stage-1 partials: per query head, rows 0 .. max_splits-1 for the paged
 // splits and rows max_splits .. max_splits+n_win-1 for the 64-token chunks
-// of the fp16 window.
+// of the fp16 window, the last of them the sink tokens when there are any.
 struct Workspace {
     float *o;        // [B][Hq][max_splits + n_win][128]
     float2 *ml;      // [B][Hq][max_splits + n_win]  (lse in log2 units, A)
     int max_splits;
-    int n_win;       // window chunks: residual / 64 (KIVI2 / KITTY), 4 (WITCERT)
+    int n_win;       // window chunks: residual / 64 (KIVI2 / KITTY) + 1 with sink tokens, 4 (WITCERT)
     hipEvent_t ev_begin, ev_end;   // optional stage-1 timing events
 };
 

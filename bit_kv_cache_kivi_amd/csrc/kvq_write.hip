@@ -151,22 +151,32 @@ __global__ __launch_bounds__(64) void append_kivi_kernel(KParams P, const uint16
     const size_t bh = (size_t)b * P.Hkv + h;
     int32_t *st = P.state + bh * 4;
     const int l = st[0], nkq = st[1];
-    const int R = P.R;
+    const int R = P.R, S = P.sink;
+    const uint32_t *kin = (const uint32_t *)(kn + bh * D);
+    const uint32_t *vin = (const uint32_t *)(vn + bh * D);
+    if (l < S) {                                     // a sink token: kept fp16, outside the windows
+        ((uint32_t *)P.sink_k)[(bh * S + (size_t)l) * (D / 2) + lane] = kin[lane];
+        ((uint32_t *)P.sink_v)[(bh * S + (size_t)l) * (D / 2) + lane] = vin[lane];
+        if (lane == 0) {
+            st[0] = l + 1;
+            st[1] = l + 1;
+        }
+        return;
+    }
     if (l - nkq >= R) {
         if (lane == 0) atomicOr(P.status, (uint32_t)KVQ_STATUS_RESIDUAL_FULL);
         return;
     }
-    if (l >= P.max_pages * PT) {
+    if (l >= S + P.max_pages * PT) {
         if (lane == 0) atomicOr(P.status, (uint32_t)KVQ_STATUS_CAPACITY);
         return;
     }
-    const uint32_t *kin = (const uint32_t *)(kn + bh * D);
-    const uint32_t *vin = (const uint32_t *)(vn + bh * D);
     uint32_t *rk = (uint32_t *)(P.res_k + (bh * R + (size_t)(l - nkq)) * D);
     uint32_t *rv = (uint32_t *)(P.res_v + (bh * R + (size_t)(l % R)) * D);
-    if (l >= R) {
-        // the token leaving the fp16 value window is quantized per token
-        const int t = l - R;
+    if (l - S >= R) {
+        // the token leaving the fp16 value window is quantized per token, at
+        // quantized position t - S
+        const int t = l - R - S;
         const int pid = P.table[(size_t)b * P.max_pages + t / PT];
         if (!page_ok(P, pid)) {
             if (lane == 0) atomicOr(P.status, (uint32_t)KVQ_STATUS_UNMAPPED_PAGE);
@@ -218,10 +228,11 @@ __global__ __launch_bounds__(256) void flush_kivi_kernel(KParams P) {
     __shared__ uint8_t bits4[D];
     __shared__ int bad;
     const int np = P.R / PT;
+    const int p0 = (nkq - P.sink) / PT;              // quantized positions count from the sink
     if (tid == 0) {
         bad = 0;
         for (int p = 0; p < np; p++)
-            if (!page_ok(P, P.table[(size_t)b * P.max_pages + nkq / PT + p])) bad = 1;
+            if (!page_ok(P, P.table[(size_t)b * P.max_pages + p0 + p])) bad = 1;
     }
     load_boost(P, h, inv, bits4);                    // contains __syncthreads
     if (bad) {
@@ -229,7 +240,7 @@ __global__ __launch_bounds__(256) void flush_kivi_kernel(KParams P) {
         return;
     }
     for (int p = 0; p < np; p++) {
-        const int pid = P.table[(size_t)b * P.max_pages + nkq / PT + p];
+        const int pid = P.table[(size_t)b * P.max_pages + p0 + p];
         quant_key_page(P, G, P.res_k + (bh * P.R + (size_t)p * PT) * D, page_ptr(P, pid, h),
                        inv, bits4, codes);
     }
@@ -247,15 +258,18 @@ __global__ __launch_bounds__(256) void prefill_kivi_kernel(KParams P, int req0,
     const int p = blockIdx.x, h = blockIdx.y, rr = blockIdx.z, b = req0 + rr;
     const int tid = threadIdx.x;
     const Geom G = geom(P.scheme);
-    const int R = P.R;
+    const int R = P.R, S = P.sink;
     const int len = lengths[rr];
-    if (len < 0 || len > P.max_pages * PT || (long long)len > ld) {
+    if (len < 0 || len > S + P.max_pages * PT || (long long)len > ld) {
         if (p == 0 && tid == 0) atomicOr(P.status, (uint32_t)KVQ_STATUS_BAD_LENGTH);
         return;
     }
-    const int rk = len ? ((len - 1) % R) + 1 : 0;
+    // tokens past the sink: the key residual keeps ((lq - 1) mod R) + 1 of
+    // them, the value window the newest min(lq, R)
+    const int lq = max(0, len - S);
+    const int rk = lq ? ((lq - 1) % R) + 1 : 0;
     const int nkq = len - rk;
-    const int nvq = len > R ? len - R : 0;
+    const int nvq = S + (lq > R ? lq - R : 0);
     const size_t bh = (size_t)b * P.Hkv + h;
     if (p == 0 && tid == 0) {
         P.state[bh * 4 + 0] = len;
@@ -263,10 +277,18 @@ __global__ __launch_bounds__(256) void prefill_kivi_kernel(KParams P, int req0,
         P.state[bh * 4 + 2] = 0;
         P.state[bh * 4 + 3] = 0;
     }
-    const int t0 = p * PT;
-    if (t0 >= len) return;
     const uint16_t *Ks = K + ((size_t)rr * P.Hkv + h) * (size_t)ld * D;
     const uint16_t *Vs = V + ((size_t)rr * P.Hkv + h) * (size_t)ld * D;
+    if (p == 0) {                                    // the sink tokens, fp16
+        const int ns = min(len, S);
+        for (int i = tid; i < ns * (D / 2); i += 256) {
+            const int t = i / (D / 2), w = i % (D / 2);
+            ((uint32_t *)P.sink_k)[(bh * S + (size_t)t) * (D / 2) + w] = ((const uint32_t *)Ks)[(size_t)t * (D / 2) + w];
+            ((uint32_t *)P.sink_v)[(bh * S + (size_t)t) * (D / 2) + w] = ((const uint32_t *)Vs)[(size_t)t * (D / 2) + w];
+        }
+    }
+    const int t0 = S + p * PT;                       // page p holds quantized positions p*64 ..
+    if (t0 >= len) return;
     // fp16 windows: keys [nkq, len) and values [nvq, len) of this page
     for (int i = tid; i < PT * (D / 2); i += 256) {
         const int t = t0 + i / (D / 2), w = i % (D / 2);
@@ -289,7 +311,7 @@ __global__ __launch_bounds__(256) void prefill_kivi_kernel(KParams P, int req0,
     __shared__ int inv[NB];
     __shared__ uint8_t bits4[D];
     load_boost(P, h, inv, bits4);
-    if (t0 < nkq)                                    // nkq is a multiple of 128: whole page
+    if (t0 < nkq)                                    // nkq - S is a multiple of 128: whole page
         quant_key_page(P, G, Ks + (size_t)t0 * D, page, inv, bits4, codes);
     if (t0 < nvq) {
         // values, per token, groups of 32 channels: thread (token tl, group jv)

@@ -39,13 +39,13 @@ class kvq_layout_t(C.Structure):
                 ("value_group", C.c_int32), ("residual", C.c_int32), ("block", C.c_int32),
                 ("n_boost", C.c_int32), ("max_pages", C.c_int32), ("n_pages", C.c_int32),
                 ("split_pages", C.c_int32), ("flags", C.c_int32), ("layer", C.c_uint32),
-                ("seed", C.c_uint64)]
+                ("seed", C.c_uint64), ("sink", C.c_int32), ("reserved", C.c_int32)]
 
 
 class kvq_buffers_t(C.Structure):
     _fields_ = [("pool", C.c_void_p), ("page_table", C.c_void_p), ("state", C.c_void_p),
                 ("res_k", C.c_void_p), ("res_v", C.c_void_p), ("boost_idx", C.c_void_p),
-                ("status", C.c_void_p)]
+                ("status", C.c_void_p), ("sink_k", C.c_void_p), ("sink_v", C.c_void_p)]
 
 
 class kvq_cache_t(C.Structure):
@@ -145,14 +145,14 @@ def kvq_workspace_bytes(cache: kvq_cache_t) -> int:
 
 def make_layout(scheme: str, B: int, Hq: int, Hkv: int, max_pages: int, n_pages: int,
                 R: int = 128, seed: int = 0, layer: int = 0, split_pages: int = 0,
-                nb: int | None = None, flags: int = 0) -> kvq_layout_t:
+                nb: int | None = None, flags: int = 0, sink: int = 0) -> kvq_layout_t:
     s = SCHEMES[scheme]
     return kvq_layout_t(scheme=s, head_dim=128, n_q_heads=Hq, n_kv_heads=Hkv, batch=B, group=32,
                         value_group=32, residual=R, block=256,
                         n_boost=(16 if s in (KVQ_SCHEME_KITTY, KVQ_SCHEME_KITTY_DYN) else 0)
                         if nb is None else nb,
                         max_pages=max_pages, n_pages=n_pages, split_pages=split_pages,
-                        flags=flags, layer=layer, seed=seed)
+                        flags=flags, layer=layer, seed=seed, sink=sink, reserved=0)
 
 
 def page_bytes(layout: kvq_layout_t) -> int:
@@ -196,6 +196,9 @@ class KVCache:
         self.res_k = torch.zeros((B, Hkv, W, 128), dtype=torch.int16, device=device)
         self.res_v = torch.zeros((B, Hkv, W, 128), dtype=torch.int16, device=device)
         self.status = torch.zeros((4,), dtype=torch.int32, device=device)
+        S = layout.sink
+        self.sink_k = torch.zeros((B, Hkv, S, 128), dtype=torch.int16, device=device) if S else None
+        self.sink_v = torch.zeros((B, Hkv, S, 128), dtype=torch.int16, device=device) if S else None
         if layout.scheme == KVQ_SCHEME_KITTY:
             idx = np.full((Hkv, 128), 17, np.uint8) if boost_idx is None else boost_idx
             self.boost_idx = torch.from_numpy(np.ascontiguousarray(idx, np.uint8)).to(device)
@@ -205,7 +208,8 @@ class KVCache:
             pool=self.pool.data_ptr(), page_table=self.page_table.data_ptr(),
             state=self.state.data_ptr(), res_k=self.res_k.data_ptr(), res_v=self.res_v.data_ptr(),
             boost_idx=self.boost_idx.data_ptr() if self.boost_idx is not None else None,
-            status=self.status.data_ptr())
+            status=self.status.data_ptr(),
+            sink_k=self.sink_k.data_ptr() if S else None, sink_v=self.sink_v.data_ptr() if S else None)
         self.cache = kvq_set_layout(layout, self.bufs)
         self.ws_bytes = kvq_workspace_bytes(self.cache)
         self.workspace = torch.empty((self.ws_bytes,), dtype=torch.uint8, device=device)

@@ -96,9 +96,10 @@ enum {
 enum {
     KVQ_STATUS_RESIDUAL_FULL = 1u,  /* append found the key residual / active
                                        block full: flush was skipped */
-    KVQ_STATUS_CAPACITY = 2u,       /* append beyond max_pages * page_tokens */
+    KVQ_STATUS_CAPACITY = 2u,       /* append beyond sink + max_pages * page_tokens */
     KVQ_STATUS_UNMAPPED_PAGE = 4u,  /* page-table entry outside [0, n_pages) */
-    KVQ_STATUS_BAD_LENGTH = 8u      /* prefill length outside [0, capacity] */
+    KVQ_STATUS_BAD_LENGTH = 8u      /* prefill length outside [0, capacity]
+                                       (capacity: sink + max_pages * page_tokens) */
 };
 
 /* Layout.  Fields the caller fills before kvq_set_layout. */
@@ -123,6 +124,12 @@ typedef struct kvq_layout {
     int32_t flags;           /* KVQ_FLAG_* */
     uint32_t layer;          /* WITCERT dither counter field; < 65536 */
     uint64_t seed;           /* WITCERT dither key */
+    int32_t sink;            /* KIVI2 / KITTY / KITTY_DYN: the first `sink`
+                                tokens of every request stay fp16, keys and
+                                values ("Kitty" summary, sink tokens); key
+                                groups, pages and the value window count from
+                                token `sink`; 0 .. 64, 0 for WITCERT */
+    int32_t reserved;        /* must be 0 */
 } kvq_layout_t;
 
 /* Caller-owned device buffers. */
@@ -141,6 +148,9 @@ typedef struct kvq_buffers {
     const uint8_t *boost_idx; /* KITTY: [n_kv_heads][D] offset of each channel
                                  in the high plane, or n_boost + 1 */
     uint32_t *status;         /* one uint32 of sticky KVQ_STATUS_* bits */
+    uint16_t *sink_k;         /* sink > 0: [batch][n_kv_heads][sink][D] fp16
+                                 keys of the sink tokens; else may be NULL */
+    uint16_t *sink_v;         /* sink > 0: the same for values */
 } kvq_buffers_t;
 
 /* Filled by kvq_set_layout; plain data, copyable. */
@@ -158,9 +168,10 @@ typedef struct kvq_cache {
 
 /* Validate `layout` and `bufs` and fill `cache`.  Host only, synchronous, no
  * device work.  Returns KVQ_OK, KVQ_ENULL (cache, layout, bufs or a required
- * buffer is NULL; boost_idx is required for KITTY only), KVQ_EALIGN (pool not
- * 256-byte aligned; page_table, state, res_k or res_v not 16-byte aligned;
- * status not 4-byte aligned) or KVQ_EINVAL when a field is out of range:
+ * buffer is NULL; boost_idx is required for KITTY only, sink_k and sink_v
+ * when sink > 0), KVQ_EALIGN (pool not 256-byte aligned; page_table, state,
+ * res_k, res_v, sink_k or sink_v not 16-byte aligned; status not 4-byte
+ * aligned) or KVQ_EINVAL when a field is out of range:
  *   head_dim != 128; n_kv_heads outside [1, 65535]; n_q_heads not a multiple
  *   of n_kv_heads, or more than 8 query heads per KV head; batch outside
  *   [1, 65535]; max_pages or n_pages < 1; split_pages outside [0, 64] (0 picks
@@ -171,6 +182,7 @@ typedef struct kvq_cache {
  *   key groups, so it must be divisible by the group, "KIVI" explainer 3.3,
  *   and the flush fills whole 64-token pages); n_boost != 16 for KITTY and
  *   KITTY_DYN or != 0 for KIVI2; KVQ_FLAG_GENERIC_STAGE1 with KITTY_DYN;
+ *   sink outside [0, 64] or non-zero for WITCERT; reserved != 0;
  *   WITCERT: block != 256; layer >= 65536; query heads per KV head not in
  *   {1, 2, 4, 8}. */
 int kvq_set_layout(kvq_cache_t *cache, const kvq_layout_t *layout,

@@ -14,12 +14,13 @@ class Case:
     """One workload on the GPU plus its oracle streams."""
 
     def __init__(self, w: inputs.Workload, extra_tokens: int = 0, split_pages: int = 0,
-                 poison: bool = True, sample=None, flags: int = 0):
+                 poison: bool = True, sample=None, flags: int = 0, sink: int = 0):
         import torch
         from bit_kv_cache_kivi_amd import kvq
         from oracle import oracle as O
         self.torch, self.kvq, self.O = torch, kvq, O
         self.w = w
+        self.S = sink
         self.sid = SCHEME_ID[w.scheme]
         self.pt = WPT if w.scheme == "witcert" else PT
         self.cap = max(w.ctx) + extra_tokens
@@ -35,7 +36,8 @@ class Case:
             self.idx = np.stack([O.kitty_select(inputs.kitty_calibration(w, h), w.nb)
                                  for h in range(w.Hkv)])
         layout = kvq.make_layout(w.scheme, w.B, w.Hq, w.Hkv, self.max_pages, self.n_pages,
-                                 R=w.R, seed=self.seed, split_pages=split_pages, flags=flags)
+                                 R=w.R, seed=self.seed, split_pages=split_pages, flags=flags,
+                                 sink=sink)
         self.cache = kvq.KVCache(layout, self.table, poison=poison)
         if w.scheme == "kitty":
             calib = np.stack([inputs.kitty_calibration(w, h) for h in range(w.Hkv)])
@@ -58,7 +60,7 @@ class Case:
         for b, h in self.sample:
             s = O.Stream(self.sid, self.cap, D=128, G=w.G, R=w.R, VG=w.VG, BLK=w.BLK,
                          nb=w.nb, idx=None if self.idx is None else self.idx[h],
-                         seed=self.seed, req=b, layer=0, kvh=h, sel=PT)
+                         seed=self.seed, req=b, layer=0, kvh=h, sel=PT, sink=sink)
             K, V = inputs.context_kv(w, b, h)
             s.prefill(K, V)
             self.streams[(b, h)] = s
@@ -144,21 +146,30 @@ class Case:
                 assert np.array_equal(rk[b, h, :n], Kraw[n_kq:l])
                 assert np.array_equal(rv[b, h, :n], Vraw[n_kq:l])
                 continue
+            # pages hold quantized positions t - S; the sink tokens sit apart
+            S = self.S
+            qk, qv = max(0, n_kq - S), max(0, n_vq - S)
             pidx = []
-            kc, ks, kz, vc, vs, vz = gather_kivi(pool, self.table[b], h, w.Hkv, self.sid, n_kq,
-                                                 n_vq, None if self.idx is None else self.idx[h],
+            kc, ks, kz, vc, vs, vz = gather_kivi(pool, self.table[b], h, w.Hkv, self.sid, qk,
+                                                 qv, None if self.idx is None else self.idx[h],
                                                  page_idx=pidx)
             if w.scheme == "kitty_dyn":               # each key page's boosted channel set
                 ou = s.unit_index()
-                for p in range(n_kq // PT):
+                for p in range(qk // PT):
                     assert np.array_equal(pidx[p], ou[p]), ("page boost index", b, h, p)
             okc, ovc = s.key_codes(), s.value_codes()
             oks, okz = s.key_stats()
             ovs, ovz = s.value_stats()
-            assert np.array_equal(kc, okc[:n_kq]), ("key codes", b, h)
-            assert np.array_equal(ks, oks[:n_kq // 32]) and np.array_equal(kz, okz[:n_kq // 32])
-            assert np.array_equal(vc, ovc[:n_vq]), ("value codes", b, h)
-            assert np.array_equal(vs, ovs[:n_vq]) and np.array_equal(vz, ovz[:n_vq])
+            assert np.array_equal(kc, okc[S:S + qk]), ("key codes", b, h)
+            assert np.array_equal(ks, oks[:qk // 32]) and np.array_equal(kz, okz[:qk // 32])
+            assert np.array_equal(vc, ovc[S:S + qv]), ("value codes", b, h)
+            assert np.array_equal(vs, ovs[S:S + qv]) and np.array_equal(vz, ovz[S:S + qv])
+            if S:
+                ns = min(l, S)
+                sk = self.cache.sink_k.cpu().numpy().view(np.uint16)
+                sv = self.cache.sink_v.cpu().numpy().view(np.uint16)
+                assert np.array_equal(sk[b, h, :ns], Kraw[:ns]), ("sink keys", b, h)
+                assert np.array_equal(sv[b, h, :ns], Vraw[:ns]), ("sink values", b, h)
             assert np.array_equal(rk[b, h, :l - n_kq], Kraw[n_kq:l]), ("key residual", b, h)
             for t in range(n_vq, l):
                 assert np.array_equal(rv[b, h, t % w.R], Vraw[t]), ("value window", b, h, t)

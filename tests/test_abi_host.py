@@ -47,7 +47,8 @@ A256 = 0x7f0000000000
 
 def bufs(K, **over):
     b = dict(pool=A256, page_table=A256 + 0x1000, state=A256 + 0x2000, res_k=A256 + 0x3000,
-             res_v=A256 + 0x4000, boost_idx=A256 + 0x5000, status=A256 + 0x6000)
+             res_v=A256 + 0x4000, boost_idx=A256 + 0x5000, status=A256 + 0x6000,
+             sink_k=A256 + 0x7000, sink_v=A256 + 0x8000)
     b.update(over)
     return K.kvq_buffers_t(**b)
 
@@ -209,3 +210,28 @@ def test_error_strings(K):
         s = lib.kvq_strerror(code)
         assert isinstance(s, bytes) and len(s) > 0
     assert lib.kvq_strerror(K.KVQ_EWORKSPACE) != lib.kvq_strerror(K.KVQ_EINVAL)
+
+
+def test_sink_fields_and_workspace(K):
+    # sink tokens: 0 .. 64 for KIVI2 / Kitty, none for WITCERT; the sink
+    # buffers are required and aligned when sink > 0; one more window chunk
+    for sink, rc_want in ((0, K.KVQ_OK), (32, K.KVQ_OK), (64, K.KVQ_OK), (65, K.KVQ_EINVAL),
+                          (-1, K.KVQ_EINVAL)):
+        L = K.make_layout("kivi2", B=2, Hq=8, Hkv=2, max_pages=64, n_pages=64, sink=sink)
+        assert set_layout(K, L)[0] == rc_want, sink
+    L = K.make_layout("witcert", B=2, Hq=8, Hkv=2, max_pages=8, n_pages=8, sink=32)
+    assert set_layout(K, L)[0] == K.KVQ_EINVAL
+    L = K.make_layout("kivi2", B=2, Hq=8, Hkv=2, max_pages=64, n_pages=64)
+    L.reserved = 1
+    assert set_layout(K, L)[0] == K.KVQ_EINVAL
+    L = K.make_layout("kitty_dyn", B=2, Hq=8, Hkv=2, max_pages=64, n_pages=64, sink=32)
+    assert set_layout(K, L, bufs(K, sink_k=0))[0] == K.KVQ_ENULL
+    assert set_layout(K, L, bufs(K, sink_v=0))[0] == K.KVQ_ENULL
+    b = bufs(K)
+    b.sink_k += 8
+    assert set_layout(K, L, b)[0] == K.KVQ_EALIGN
+    rc, cache = set_layout(K, L)
+    assert rc == K.KVQ_OK
+    splits = -(-64 // cache.split_pages)
+    rows = 2 * 8 * (splits + 128 // 64 + 1)          # window chunks + the sink chunk
+    assert K.kvq_workspace_bytes(cache) == rows * 128 * 4 + rows * 8 + 256

@@ -117,6 +117,44 @@ def test_kitty_calibrate_store_decode(flags):
     case.check_store()
 
 
+@pytest.mark.parametrize("wid,Hq,Hkv", [(2, 2, 2), (3, 8, 2), (4, 2, 2), (6, 4, 1)])
+def test_sink_tokens_store_decode(wid, Hq, Hkv):
+    # the first 32 tokens stay fp16: bit-exact store (sink buffers included)
+    # and decode through prefill and two flushes, for KIVI-2 (one query head
+    # per wave and the group-of-4 kernel) and both Kitty schemes
+    w = inputs.workload(wid, B=2, Hq=Hq, Hkv=Hkv, ctx=(700, 1129))
+    case = _case(w, extra_tokens=300, split_pages=3, sink=32)
+    case.check_state()
+    case.check_store()
+    out, cert, q = case.decode_now(2)
+    _check_decode(case, out, cert, q)
+    for i in range(260):
+        out, cert, q = case.step(decode=(i % 64 == 63 or i in (0, 1, 127, 128)))
+        if out is not None:
+            _check_decode(case, out, cert, q)
+    case.check_status()
+    case.check_state()
+    case.check_store()
+
+
+@pytest.mark.parametrize("ctx", [(1,), (2,), (31,), (32,), (33,), (159,), (160,), (161,), (290,)])
+def test_sink_short_contexts(ctx):
+    # contexts inside, at and just past the sink, and around the first flush
+    w = inputs.workload(2, B=1, Hq=4, Hkv=1, ctx=ctx)
+    case = _case(w, extra_tokens=200, split_pages=1, sink=32)
+    case.check_state()
+    case.check_store()
+    if ctx[0] > 0:
+        out, cert, q = case.decode_now(5)
+        _check_decode(case, out, cert, q)
+    for i in range(40):
+        out, cert, q = case.step(decode=(i % 7 == 6 or i in (0, 1)))
+        if out is not None:
+            _check_decode(case, out, cert, q)
+    case.check_status()
+    case.check_store()
+
+
 @pytest.mark.parametrize("Hq,Hkv,split", [(2, 2, 3), (8, 2, 2)])
 def test_kitty_dynamic_store_decode(Hq, Hkv, split):
     # boosted set chosen per page: bit-exact codes, high plane and per-page
