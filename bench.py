@@ -67,10 +67,14 @@ def key_q_bytes(scheme: str, n: int) -> int:
     return n * (52 if scheme == "kitty" else 48)
 
 
-def kivi_bytes(l: int, n_kq: int, R: int, qpk: int, scheme: str) -> dict:
-    n_vq = max(0, l - R)
+def kivi_bytes(l: int, n_kq: int, R: int, qpk: int, scheme: str, sink: int = 0) -> dict:
+    """n_kq: absolute (keys below it are quantized or sink tokens)."""
+    ns = min(l, sink)                              # fp16 sink tokens, keys and values
+    n_vq = max(0, l - sink - R)                    # quantized values after the sink
+    kq = max(0, n_kq - sink)                       # quantized keys after the sink
     paged = key_q_bytes(scheme, n_vq) + n_vq * 48
-    window = key_q_bytes(scheme, n_kq - n_vq) + (l - n_kq) * 256 + (l - n_vq) * 256
+    window = key_q_bytes(scheme, kq - n_vq) + (l - max(n_kq, ns)) * 256 + (l - ns - n_vq) * 256
+    window += ns * 512
     qo = qpk * (256 + 512)
     table = ((l + 63) // 64) * 4
     # stage 1 streams the paged prefix and, as one more split, the fp16 window
@@ -92,7 +96,9 @@ def write_bytes(w: inputs.Workload, l_before: int, n_kq_before: int) -> int:
         if l_before - n_kq_before == w.BLK:
             b += 2 * w.BLK * 256 + 2 * (w.BLK * 128 + 256)
         return b
-    if l_before >= w.R:
+    if l_before < w.sink:
+        return b                       # a sink token: fp16 only
+    if l_before - w.sink >= w.R:
         b += 256 + 48                  # value leaving the window, its codes + stats
     if l_before - n_kq_before == w.R:
         b += w.R * 256 + key_q_bytes(w.scheme, w.R)
@@ -101,12 +107,17 @@ def write_bytes(w: inputs.Workload, l_before: int, n_kq_before: int) -> int:
 
 def state_after_prefill(w: inputs.Workload, l0: int):
     W = w.BLK if w.scheme == "witcert" else w.R
-    r = ((l0 - 1) % W) + 1 if l0 else 0
+    if l0 <= w.sink:
+        return l0, l0
+    lq = l0 - w.sink
+    r = ((lq - 1) % W) + 1
     return l0, l0 - r
 
 
 def step_state(w: inputs.Workload, l: int, n_kq: int):
     W = w.BLK if w.scheme == "witcert" else w.R
+    if l < w.sink:
+        return l + 1, l + 1
     if l - n_kq == W:
         n_kq += W
     return l + 1, n_kq
@@ -124,7 +135,7 @@ def step_bytes(w: inputs.Workload, states):
         if w.scheme == "witcert":
             d = witcert_bytes(l2, k2, w.group)
         else:
-            d = kivi_bytes(l2, k2, w.R, w.group, w.scheme)
+            d = kivi_bytes(l2, k2, w.R, w.group, w.scheme, w.sink)
         tot += w.Hkv * (wb + d["decode"])
         s1 += w.Hkv * d["stage1"]
         new.append((l2, k2))
@@ -151,7 +162,8 @@ def setup_gpu(w: inputs.Workload, extra: int, split_pages: int):
     n_pages = w.B * max_pages
     table = inputs.page_permutation(w, n_pages).reshape(w.B, max_pages)
     layout = kvq.make_layout(w.scheme, w.B, w.Hq, w.Hkv, max_pages, n_pages, R=w.R,
-                             seed=0x5EED_0000_0000_0000 | w.seed, split_pages=split_pages)
+                             seed=0x5EED_0000_0000_0000 | w.seed, split_pages=split_pages,
+                             sink=w.sink)
     cache = kvq.KVCache(layout, table)
     if w.scheme == "kitty":
         calib = np.stack([inputs.kitty_calibration(w, h) for h in range(w.Hkv)])
@@ -254,7 +266,8 @@ def cpu_baseline(w: inputs.Workload, warmup: int, target_s: float = 15.0, thread
     def make(pair):
         b, h = pair
         s = O.Stream(sid, w.ctx[b] + warmup + 210, G=w.G, R=w.R, VG=w.VG, BLK=w.BLK, nb=w.nb,
-                     idx=None if idx is None else idx[h], seed=seed, req=b, kvh=h)
+                     idx=None if idx is None else idx[h], seed=seed, req=b, kvh=h,
+                     sink=w.sink)
         K, V = inputs.context_kv(w, b, h)
         s.prefill(K, V)
         return s, b, h
@@ -285,7 +298,7 @@ def cpu_baseline(w: inputs.Workload, warmup: int, target_s: float = 15.0, thread
                 wb = write_bytes(w, l, n_kq)
                 l2, k2 = step_state(w, l, n_kq)
                 d = (witcert_bytes(l2, k2, w.group) if w.scheme == "witcert"
-                     else kivi_bytes(l2, k2, w.R, w.group, w.scheme))
+                     else kivi_bytes(l2, k2, w.R, w.group, w.scheme, w.sink))
                 done_bytes += wb + d["decode"]
                 states[i] = (l2, k2)
             rounds += 1

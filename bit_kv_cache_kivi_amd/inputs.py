@@ -51,6 +51,7 @@ class Workload:
     BLK: int = 256
     page_tokens: int = 64
     nb: int = 0            # Kitty boosted channels per head
+    sink: int = 0          # leading tokens kept fp16 (keys and values)
     ctx: tuple = ()        # per-request context length before the first step
     outlier_ch: tuple = ()  # fixed channels (workload 1) or () for seeded
     n_outliers: int = 0
@@ -95,6 +96,11 @@ def workload(wid: int, **over) -> Workload:
         w = dict(wid=6, name="kitty-dyn-mha-b16-h32-ctx32768", scheme="kitty_dyn", B=16, Hq=32,
                  Hkv=32, ctx=(32768,) * 16, n_outliers=4, outlier_factor=15.0, nb=16, steps=1,
                  seed=6)
+    elif wid == 7:
+        # workload 3's shapes and lengths with 32 fp16 sink tokens per request
+        w = dict(wid=7, name="kivi2-sink32-gqa-b64-32q8kv-ctx8k-32k-paged", scheme="kivi2", B=64,
+                 Hq=32, Hkv=8, ctx=_lengths3(64, 8192, 32768, 3), n_outliers=4,
+                 outlier_factor=15.0, sink=32, steps=1, seed=7)
     else:
         raise ValueError(wid)
     w.update(over)

@@ -14,12 +14,13 @@ class Case:
     """One workload on the GPU plus its oracle streams."""
 
     def __init__(self, w: inputs.Workload, extra_tokens: int = 0, split_pages: int = 0,
-                 poison: bool = True, sample=None, flags: int = 0, sink: int = 0):
+                 poison: bool = True, sample=None, flags: int = 0, sink: int | None = None):
         import torch
         from bit_kv_cache_kivi_amd import kvq
         from oracle import oracle as O
         self.torch, self.kvq, self.O = torch, kvq, O
         self.w = w
+        sink = w.sink if sink is None else sink
         self.S = sink
         self.sid = SCHEME_ID[w.scheme]
         self.pt = WPT if w.scheme == "witcert" else PT

@@ -85,5 +85,9 @@ def test_kitty_dynamic_b16_h32_ctx32768():
     _run(inputs.workload(6))
 
 
+def test_gqa_sink32_b64_ctx8k_32k():
+    _run(inputs.workload(7))
+
+
 def test_witcert_b32_32q8kv_ctx16384_certificate():
     _run(inputs.workload(5), kappa=2.0, cert_check=True)
