@@ -59,21 +59,23 @@ def log(msg: str):
 # algorithmic byte accounts (per (request, KV head) at decode time)
 # ---------------------------------------------------------------------------
 
-def key_q_bytes(scheme: str, n: int) -> int:
-    """Quantized key bytes of n tokens: codes (+ Kitty high plane) + stats,
-    and for Kitty dynamic the 16 channel ids of each 64-token page touched."""
+def key_q_bytes(scheme: str, n: int, nb: int = 16) -> int:
+    """Quantized key bytes of n tokens: codes + stats (48 B) + the Kitty high
+    plane (nb/4 B), and for Kitty dynamic the channel ids of each 64-token
+    page touched (max(16, nb) B)."""
     if scheme == "kitty_dyn":
-        return n * 52 + ((n + 63) // 64) * 16
-    return n * (52 if scheme == "kitty" else 48)
+        return n * (48 + nb // 4) + ((n + 63) // 64) * max(16, nb)
+    return n * (48 + nb // 4) if scheme == "kitty" else n * 48
 
 
-def kivi_bytes(l: int, n_kq: int, R: int, qpk: int, scheme: str, sink: int = 0) -> dict:
+def kivi_bytes(l: int, n_kq: int, R: int, qpk: int, scheme: str, sink: int = 0,
+               nb: int = 16) -> dict:
     """n_kq: absolute (keys below it are quantized or sink tokens)."""
     ns = min(l, sink)                              # fp16 sink tokens, keys and values
     n_vq = max(0, l - sink - R)                    # quantized values after the sink
     kq = max(0, n_kq - sink)                       # quantized keys after the sink
-    paged = key_q_bytes(scheme, n_vq) + n_vq * 48
-    window = key_q_bytes(scheme, kq - n_vq) + (l - max(n_kq, ns)) * 256 + (l - ns - n_vq) * 256
+    paged = key_q_bytes(scheme, n_vq, nb) + n_vq * 48
+    window = key_q_bytes(scheme, kq - n_vq, nb) + (l - max(n_kq, ns)) * 256 + (l - ns - n_vq) * 256
     window += ns * 512
     qo = qpk * (256 + 512)
     table = ((l + 63) // 64) * 4
@@ -101,7 +103,7 @@ def write_bytes(w: inputs.Workload, l_before: int, n_kq_before: int) -> int:
     if l_before - w.sink >= w.R:
         b += 256 + 48                  # value leaving the window, its codes + stats
     if l_before - n_kq_before == w.R:
-        b += w.R * 256 + key_q_bytes(w.scheme, w.R)
+        b += w.R * 256 + key_q_bytes(w.scheme, w.R, w.nb or 16)
     return b
 
 
@@ -135,7 +137,7 @@ def step_bytes(w: inputs.Workload, states):
         if w.scheme == "witcert":
             d = witcert_bytes(l2, k2, w.group)
         else:
-            d = kivi_bytes(l2, k2, w.R, w.group, w.scheme, w.sink)
+            d = kivi_bytes(l2, k2, w.R, w.group, w.scheme, w.sink, w.nb or 16)
         tot += w.Hkv * (wb + d["decode"])
         s1 += w.Hkv * d["stage1"]
         new.append((l2, k2))
@@ -163,7 +165,7 @@ def setup_gpu(w: inputs.Workload, extra: int, split_pages: int):
     table = inputs.page_permutation(w, n_pages).reshape(w.B, max_pages)
     layout = kvq.make_layout(w.scheme, w.B, w.Hq, w.Hkv, max_pages, n_pages, R=w.R,
                              seed=0x5EED_0000_0000_0000 | w.seed, split_pages=split_pages,
-                             sink=w.sink)
+                             sink=w.sink, nb=w.nb if w.nb else None)
     cache = kvq.KVCache(layout, table)
     if w.scheme == "kitty":
         calib = np.stack([inputs.kitty_calibration(w, h) for h in range(w.Hkv)])
@@ -298,7 +300,7 @@ def cpu_baseline(w: inputs.Workload, warmup: int, target_s: float = 15.0, thread
                 wb = write_bytes(w, l, n_kq)
                 l2, k2 = step_state(w, l, n_kq)
                 d = (witcert_bytes(l2, k2, w.group) if w.scheme == "witcert"
-                     else kivi_bytes(l2, k2, w.R, w.group, w.scheme, w.sink))
+                     else kivi_bytes(l2, k2, w.R, w.group, w.scheme, w.sink, w.nb or 16))
                 done_bytes += wb + d["decode"]
                 states[i] = (l2, k2)
             rounds += 1

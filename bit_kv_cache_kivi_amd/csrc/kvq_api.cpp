@@ -37,8 +37,11 @@ int validate_layout(const kvq_layout_t *L) {
             // the flush writes whole 64-token pages
             if (L->residual % L->group != 0 || L->residual % kvq::PT != 0) return KVQ_EINVAL;
             if (L->residual < kvq::PT || L->residual > 256) return KVQ_EINVAL;
-            if (kvq::is_kitty(L->scheme) ? L->n_boost != kvq::NB : L->n_boost != 0)
+            if (kvq::is_kitty(L->scheme) ? (L->n_boost != kvq::NB && L->n_boost != kvq::NB_MAX)
+                                         : L->n_boost != 0)
                 return KVQ_EINVAL;
+            // the VALU stage 1 handles 16 boosted channels only
+            if (L->n_boost > kvq::NB && (L->flags & KVQ_FLAG_GENERIC_STAGE1)) return KVQ_EINVAL;
             // the VALU stage 1 reads the head's static boost table only
             if (L->scheme == KVQ_SCHEME_KITTY_DYN && (L->flags & KVQ_FLAG_GENERIC_STAGE1))
                 return KVQ_EINVAL;
@@ -67,6 +70,7 @@ kvq::KParams params(const kvq_cache_t *C) {
     P.sink_k = C->bufs.sink_k;
     P.sink_v = C->bufs.sink_v;
     P.sink = L.sink;
+    P.nb = kvq::is_kitty(L.scheme) ? L.n_boost : 0;
     P.B = L.batch;
     P.Hq = L.n_q_heads;
     P.Hkv = L.n_kv_heads;
@@ -106,13 +110,13 @@ extern "C" {
 int64_t kvq_page_bytes(const kvq_layout_t *L) {
     if (!L) return 0;
     if (L->scheme < KVQ_SCHEME_KIVI2 || L->scheme > KVQ_SCHEME_KITTY_DYN) return 0;
-    return kvq::geom(L->scheme).bytes;
+    return kvq::geom(L->scheme, L->n_boost).bytes;
 }
 
 int32_t kvq_page_tokens(const kvq_layout_t *L) {
     if (!L) return 0;
     if (L->scheme < KVQ_SCHEME_KIVI2 || L->scheme > KVQ_SCHEME_KITTY_DYN) return 0;
-    return kvq::geom(L->scheme).tokens;
+    return kvq::geom(L->scheme, L->n_boost).tokens;
 }
 
 double kvq_bytes_per_token(const kvq_layout_t *L) {
@@ -137,7 +141,7 @@ int kvq_set_layout(kvq_cache_t *cache, const kvq_layout_t *layout, const kvq_buf
     memset(cache, 0, sizeof(*cache));
     cache->layout = *layout;
     cache->bufs = *bufs;
-    const kvq::Geom G = kvq::geom(layout->scheme);
+    const kvq::Geom G = kvq::geom(layout->scheme, layout->n_boost);
     cache->page_tokens = G.tokens;
     cache->page_bytes = G.bytes;
     int sp = layout->split_pages;

@@ -12,21 +12,23 @@ namespace kvq {
 constexpr int D = 128;          // head dim
 constexpr int PT = 64;          // tokens per KIVI2/KITTY page
 constexpr int WPT = 256;        // tokens per WITCERT page (= one block)
-constexpr int NB = 16;          // Kitty boosted channels per KV head
+constexpr int NB = 16;          // Kitty boosted channels per KV head (alpha = 1/8)
+constexpr int NB_MAX = 32;      // Kitty-Pro: alpha = 1/4
 
 // ---------------------------------------------------------------------------
 // Page geometry.  One (page, KV head) block; the pool is
 // [n_pages][n_kv_heads][page_bytes].
 //
-// KIVI2 / KITTY / KITTY_DYN, 64 tokens:
+// KIVI2 / KITTY / KITTY_DYN, 64 tokens (nb boosted channels, 16 or 32):
 //   KC  2048 B  low 2-bit key codes, token-major, arranged as the B operand of
 //               a 16x16x32 f16 matrix-core product (see key_code_pos)
-//   KH   256 B  KITTY*: high 2-bit plane of the 16 boosted channels
+//   KH  16 nb B KITTY*: high 2-bit plane of the boosted channels, one 256-B
+//               plane per 16 offsets (see high_code_pos)
 //   KS  1024 B  key {scale, zero} fp16 pairs, [2 groups][128 channels]
 //   VC  2048 B  value codes, channel-major (see value_code_pos)
 //   VS  1024 B  value {scale, zero} fp16 pairs, [64 tokens][4 groups]
-//   KI    16 B  KITTY_DYN: the page's boosted channel ids, ascending (the
-//               high-plane offset of KI[o] is o)
+//   KI  max(16, nb) B  KITTY_DYN: the page's boosted channel ids, ascending
+//               (the high-plane offset of KI[o] is o)
 // WITCERT, 256 tokens (one block):
 //   KC 32768 B int8 [256][128];  KS 256 B fp16 [128];
 //   VC 32768 B int8 [256][128];  VS 256 B fp16 [128]
@@ -39,16 +41,18 @@ __host__ __device__ constexpr bool is_kitty(int scheme) {
     return scheme == KVQ_SCHEME_KITTY || scheme == KVQ_SCHEME_KITTY_DYN;
 }
 
-__host__ __device__ inline Geom geom(int scheme) {
+__host__ __device__ inline Geom geom(int scheme, int nb = NB) {
     Geom g{};
     if (scheme == KVQ_SCHEME_WITCERT) {
         g.kc = 0; g.kh = 0; g.ks = 32768; g.vc = 33024; g.vs = 65792; g.bytes = 66048;
         g.tokens = WPT;
-    } else if (scheme == KVQ_SCHEME_KITTY) {
-        g.kc = 0; g.kh = 2048; g.ks = 2304; g.vc = 3328; g.vs = 5376; g.bytes = 6400;
-        g.tokens = PT;
-    } else if (scheme == KVQ_SCHEME_KITTY_DYN) {
-        g.kc = 0; g.kh = 2048; g.ks = 2304; g.vc = 3328; g.vs = 5376; g.ki = 6400; g.bytes = 6416;
+    } else if (is_kitty(scheme)) {
+        g.kc = 0; g.kh = 2048; g.ks = 2048 + 16 * nb; g.vc = g.ks + 1024; g.vs = g.vc + 2048;
+        g.bytes = g.vs + 1024;
+        if (scheme == KVQ_SCHEME_KITTY_DYN) {
+            g.ki = g.bytes;
+            g.bytes += nb > 16 ? nb : 16;
+        }
         g.tokens = PT;
     } else {
         g.kc = 0; g.kh = 0; g.ks = 2048; g.vc = 3072; g.vs = 5120; g.bytes = 6144;
@@ -82,12 +86,13 @@ __host__ __device__ inline void value_code_pos(int t, int c, int &dword, int &sh
     shift = 4 * j + 2 * ks;
 }
 
-// Kitty high plane: (token t in page, boosted offset o in [0,16)).
-// Dword 16*(o>>2) + (t&15) (the lane whose KC data holds token t), bit
+// Kitty high plane: (token t in page, boosted offset o in [0, nb)).  Plane
+// q = o >> 4 holds offsets 16q .. 16q+15 in 64 dwords: dword
+// 64q + 16*((o&15)>>2) + (t&15) (the lane whose KC data holds token t), bit
 // 4*(4*(n&1) + (o&3)) + 2*(n>>1) with n = t >> 4.
 __host__ __device__ inline void high_code_pos(int t, int o, int &dword, int &shift) {
-    int n = t >> 4, r = t & 15, g = o >> 2, i = o & 3;
-    dword = 16 * g + r;
+    int n = t >> 4, r = t & 15, q = o >> 4, g = (o & 15) >> 2, i = o & 3;
+    dword = 64 * q + 16 * g + r;
     shift = 4 * (4 * (n & 1) + i) + 2 * (n >> 1);
 }
 

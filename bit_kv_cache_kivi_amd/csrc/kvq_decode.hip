@@ -120,7 +120,7 @@ __device__ inline void split_hl(float x0, float x1, uint32_t &hi, uint32_t &lo) 
 template <int NQ, int VPF, int SCHEME>
 __device__ void window_partial(const KParams &P, const uint16_t *__restrict__ q, const Workspace &W,
                                float qscale, int b, int h, int hq0, int wc, int lane, WinSmem &ws) {
-    const Geom G = geom(SCHEME);
+    const Geom G = geom(SCHEME, P.nb);
     constexpr bool wit = SCHEME == KVQ_SCHEME_WITCERT;
     constexpr bool kitty = is_kitty(SCHEME);
     constexpr bool dyn = SCHEME == KVQ_SCHEME_KITTY_DYN;
@@ -182,12 +182,12 @@ __device__ void window_partial(const KParams &P, const uint16_t *__restrict__ q,
         if (dyn) {                                // channel -> offset from the pages' channel ids
 #pragma unroll
             for (int pi = 0; pi < 2; pi++) {
-                ws.bidx[pi][2 * lane] = (uint8_t)(NB + 1);
-                ws.bidx[pi][2 * lane + 1] = (uint8_t)(NB + 1);
+                ws.bidx[pi][2 * lane] = (uint8_t)(NB_MAX + 1);
+                ws.bidx[pi][2 * lane + 1] = (uint8_t)(NB_MAX + 1);
             }
             lds_sync();
-            if (lane < 2 * NB) {
-                const int pi = lane / NB, o = lane % NB;
+            if (lane < 2 * P.nb) {
+                const int pi = lane / P.nb, o = lane % P.nb;
                 if (pids[pi] >= 0) ws.bidx[pi][cpage(P, pids[pi], h)[G.ki + o] & (D - 1)] = (uint8_t)o;
             }
         }
@@ -222,10 +222,12 @@ __device__ void window_partial(const KParams &P, const uint16_t *__restrict__ q,
                     const int d = 2 * n16 + a;
                     xa[a] = kcw[(d >> 2) * 256 + (16 * g + (tp & 15)) * 4 + (d & 3)];
                 }
-                uint32_t kh[4] = {0u, 0u, 0u, 0u};
+                uint32_t kh[8] = {0u, 0u, 0u, 0u, 0u, 0u, 0u, 0u};   // offsets 4u .. 4u+3
                 if (kitty) {
 #pragma unroll
-                    for (int u = 0; u < 4; u++) kh[u] = ((const uint32_t *)(pg + G.kh))[16 * u + (tp & 15)];
+                    for (int u = 0; u < 8; u++)
+                        if (4 * u < P.nb)
+                            kh[u] = ((const uint32_t *)(pg + G.kh))[64 * (u >> 2) + 16 * (u & 3) + (tp & 15)];
                 }
                 const int hsh = 2 * (n16 >> 1) + 16 * (n16 & 1);
 #pragma unroll
@@ -240,7 +242,7 @@ __device__ void window_partial(const KParams &P, const uint16_t *__restrict__ q,
                         if (kitty) {
                             const int o = dyn ? ws.bidx[pi][32 * kc + 8 * g + i]
                                               : P.boost_idx[(size_t)h * D + 32 * kc + 8 * g + i];
-                            if (o < NB) code |= ((kh[o >> 2] >> (hsh + 4 * (o & 3))) & 3u) << 2;
+                            if (o < P.nb) code |= ((kh[o >> 2] >> (hsh + 4 * (o & 3))) & 3u) << 2;
                         }
                         kf[i] = fmaf((float)code, half_lo(sz[i]), half_hi(sz[i]));   // code * s exact
                     }
@@ -367,7 +369,7 @@ __global__ __launch_bounds__(64) void stage1_valu_kernel(KParams P, const uint16
     const int s = it.s, hq = it.hd, b = it.b;
     const int lane = threadIdx.x, g = lane >> 4, r = lane & 15;
     const int h = hq / P.qpk;
-    const Geom G = geom(P.scheme);
+    const Geom G = geom(P.scheme, P.nb);
     __shared__ union {
         struct {
             uint32_t kss[256];
@@ -888,7 +890,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(3, 8))) void
     const S1Item it = s1_item(W.max_splits, W.n_win);
     const int s = it.s, h = it.hd, b = it.b;
     const int lane = threadIdx.x, g = lane >> 4, r = lane & 15;
-    const Geom G = geom(P.scheme);
+    const Geom G = geom(P.scheme, P.nb);
     __shared__ union {
         Gqa4Smem pg;
         WinSmem win;
@@ -1028,7 +1030,7 @@ struct HeadSmem {
     _Float16 Bs[2][4][BS_STRIDE];   // P.V B: [hi, lo][value group][token]
     h8v Bz;                         // zero fragment for B columns 8..15
     float zsh[PT];                  // scores, hi + lo rows [token]
-    int inv[NB];                    // Kitty: boosted offset -> channel
+    int inv[NB_MAX];                // Kitty: boosted offset -> channel
 };
 
 __device__ inline h8v frag8_x4(uint32_t m) {     // codes times 4
@@ -1041,8 +1043,8 @@ __device__ inline h8v frag8_x4(uint32_t m) {     // codes times 4
 
 struct HeadPage {
     PageRegs R;
-    uint32_t khw;                   // Kitty high plane, dword = lane
-    uint32_t kiw;                   // KITTY_DYN: channel ids of offsets 4g .. 4g+3
+    uint32_t khw[2];                // Kitty high planes (offsets 0..15, 16..31), dword = lane
+    uint32_t kiw[2];                // KITTY_DYN: channel ids of offsets 16q + 4g .. +3
 };
 
 template <bool KITTY, bool DYN>
@@ -1053,7 +1055,7 @@ void stage1_head_mfma_kernel(KParams P, const uint16_t *__restrict__ q, Workspac
     const int s = it.s, hq = it.hd, b = it.b;
     const int lane = threadIdx.x, g = lane >> 4, r = lane & 15;
     const int h = hq / P.qpk;
-    const Geom G = geom(P.scheme);
+    const Geom G = geom(P.scheme, P.nb);
     __shared__ union {
         HeadSmem pg;
         WinSmem win;
@@ -1089,17 +1091,18 @@ void stage1_head_mfma_kernel(KParams P, const uint16_t *__restrict__ q, Workspac
         sm.As[1][2][lane] = h8v{0, 0, 0, 0, 0, 0, 0, 0};
     }
     if (lane == 0) sm.Bz = h8v{0, 0, 0, 0, 0, 0, 0, 0};
-    int kc_off[4] = {0, 0, 0, 0};                // Kitty: channels of offsets 4g .. 4g+3
+    int kc_off[8] = {0, 0, 0, 0, 0, 0, 0, 0};    // Kitty: channels of offsets 16q + 4g + i
+    const int planes = P.nb >> 4;                // Kitty high planes: 1 (16 boosted) or 2 (32)
     if (KITTY && !DYN) {
-        if (lane < NB) sm.inv[lane] = 0;
+        if (lane < NB_MAX) sm.inv[lane] = 0;
         lds_sync();
         for (int c = lane; c < D; c += 64) {
             const int o = P.boost_idx[(size_t)h * D + c];
-            if (o < NB) sm.inv[o] = c;
+            if (o < P.nb) sm.inv[o] = c;
         }
         lds_sync();
 #pragma unroll
-        for (int i = 0; i < 4; i++) kc_off[i] = sm.inv[4 * g + i];
+        for (int i = 0; i < 8; i++) kc_off[i] = sm.inv[16 * (i >> 2) + 4 * g + (i & 3)];
     }
 
     // operand roles
@@ -1161,22 +1164,27 @@ void stage1_head_mfma_kernel(KParams P, const uint16_t *__restrict__ q, Workspac
                 sc[n] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[n >> 1], bf[n], sc[n], 0, 0, 0);
         }
         if (KITTY) {
-            if (DYN) {                           // this page's boosted channels
 #pragma unroll
-                for (int i = 0; i < 4; i++) kc_off[i] = (HP.kiw >> (8 * i)) & (D - 1);
-            }
-            // tile n: key group n >> 1, plane half n >> 1 (bit 2), nibble half n & 1
-            const h8v bk0 = frag8_x4(HP.khw & MSK), bk1 = frag8_x4((HP.khw >> 2) & MSK);
+            for (int qp = 0; qp < 2; qp++) {
+                if (qp < planes) {               // uniform
+                    int co[4];                   // channels of offsets 16 qp + 4g + i
 #pragma unroll
-            for (int gi = 0; gi < 2; gi++) {
-                const _Float16 *row = (const _Float16 *)&sm.As[gi][arow][0];
-                const _Float16 a0 = row[kc_off[0]], a1 = row[kc_off[1]], a2 = row[kc_off[2]], a3 = row[kc_off[3]];
-                const _Float16 z = 0;
-                const h8v alo = h8v{a0, a1, a2, a3, z, z, z, z};
-                const h8v ahi = h8v{z, z, z, z, a0, a1, a2, a3};
-                const h8v bk = gi ? bk1 : bk0;
-                sc[2 * gi] = __builtin_amdgcn_mfma_f32_16x16x32_f16(alo, bk, sc[2 * gi], 0, 0, 0);
-                sc[2 * gi + 1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ahi, bk, sc[2 * gi + 1], 0, 0, 0);
+                    for (int i = 0; i < 4; i++)
+                        co[i] = DYN ? (HP.kiw[qp] >> (8 * i)) & (D - 1) : kc_off[4 * qp + i];
+                    // tile n: key group n >> 1, plane half n >> 1 (bit 2), nibble half n & 1
+                    const h8v bk0 = frag8_x4(HP.khw[qp] & MSK), bk1 = frag8_x4((HP.khw[qp] >> 2) & MSK);
+#pragma unroll
+                    for (int gi = 0; gi < 2; gi++) {
+                        const _Float16 *row = (const _Float16 *)&sm.As[gi][arow][0];
+                        const _Float16 a0 = row[co[0]], a1 = row[co[1]], a2 = row[co[2]], a3 = row[co[3]];
+                        const _Float16 z = 0;
+                        const h8v alo = h8v{a0, a1, a2, a3, z, z, z, z};
+                        const h8v ahi = h8v{z, z, z, z, a0, a1, a2, a3};
+                        const h8v bk = gi ? bk1 : bk0;
+                        sc[2 * gi] = __builtin_amdgcn_mfma_f32_16x16x32_f16(alo, bk, sc[2 * gi], 0, 0, 0);
+                        sc[2 * gi + 1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ahi, bk, sc[2 * gi + 1], 0, 0, 0);
+                    }
+                }
             }
         }
         if (lane < 16) {                         // rows 0 (hi) and 1 (lo) of each token tile
@@ -1245,8 +1253,12 @@ void stage1_head_mfma_kernel(KParams P, const uint16_t *__restrict__ q, Workspac
         const uint8_t *pg = base + (size_t)__builtin_amdgcn_readlane(pid_l, min(i, np - 1)) * pstride;
         HeadPage HP;
         HP.R = load_page_masked(pg, i < np, G, lane);
-        HP.khw = KITTY ? bload1(page_rsrc(pg, i < np, G), G.kh + 4 * lane) : 0u;
-        HP.kiw = DYN ? bload1(page_rsrc(pg, i < np, G), G.ki + 4 * g) : 0u;
+#pragma unroll
+        for (int qp = 0; qp < 2; qp++) {
+            const bool on = qp < planes;
+            HP.khw[qp] = KITTY && on ? bload1(page_rsrc(pg, i < np, G), G.kh + 256 * qp + 4 * lane) : 0u;
+            HP.kiw[qp] = DYN && on ? bload1(page_rsrc(pg, i < np, G), G.ki + 16 * qp + 4 * g) : 0u;
+        }
         return HP;
     };
     // two register sets used in turn (the page after the one being processed
@@ -1317,7 +1329,7 @@ __global__ __launch_bounds__(64) void stage1_witcert_kernel(KParams P, const uin
     const S1Item it = s1_item(W.max_splits, W.n_win);
     const int s = it.s, h = it.hd, b = it.b;
     const int lane = threadIdx.x, cq = lane & 31, tp = lane >> 5;
-    const Geom G = geom(P.scheme);
+    const Geom G = geom(P.scheme, P.nb);
     if (it.window) {                             // the KV head's active block (fp16 tail)
         __shared__ WinSmem win;
         window_partial<QPK, 16, KVQ_SCHEME_WITCERT>(P, q, W, qscale, b, h, QPK * h, s, lane, win);

@@ -19,6 +19,7 @@ struct KParams {
     uint16_t *sink_v;
     int B, Hq, Hkv, R, max_pages, n_pages, page_bytes, scheme, qpk, split_pages;
     int sink;                     // leading fp16 tokens; quantized positions are t - sink
+    int nb;                       // Kitty boosted channels (16 or 32; 0 for others)
     int force_generic;            // 1: use the per-query-head VALU stage 1
     uint32_t layer;
     uint64_t seed;

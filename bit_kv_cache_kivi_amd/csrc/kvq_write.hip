@@ -39,7 +39,7 @@ __device__ inline uint64_t mag24(uint16_t h) {
 // its 64 tokens (the mean up to the fixed count; ties to the lower channel),
 // into bits4 / inv and the page's KI bytes (channel ids, ascending)
 __device__ void select_page_boost(const Geom &G, const uint16_t *src, uint8_t *page, int *inv,
-                                  uint8_t *bits4) {
+                                  uint8_t *bits4, int nb) {
     __shared__ uint64_t imp[D];
     const int tid = threadIdx.x;
     if (tid < D) {
@@ -55,7 +55,7 @@ __device__ void select_page_boost(const Geom &G, const uint16_t *src, uint8_t *p
             const uint64_t o = imp[c2];
             rank += (o > mine || (o == mine && c2 < tid)) ? 1 : 0;
         }
-        bits4[tid] = rank < NB ? 1 : 0;
+        bits4[tid] = rank < nb ? 1 : 0;
     }
     __syncthreads();
     if (tid < D && bits4[tid]) {
@@ -71,7 +71,7 @@ __device__ void quant_key_page(const KParams &P, const Geom &G, const uint16_t *
                                uint8_t *page, int *inv, uint8_t *bits4,
                                uint8_t (*codes)[D]) {
     const int tid = threadIdx.x;
-    if (P.scheme == KVQ_SCHEME_KITTY_DYN) select_page_boost(G, src, page, inv, bits4);
+    if (P.scheme == KVQ_SCHEME_KITTY_DYN) select_page_boost(G, src, page, inv, bits4, P.nb);
     const int c = tid & 127;
     const int gi = tid >> 7;                         // group 0 or 1 of the page
     const float lmax = bits4[c] ? 15.0f : 3.0f;
@@ -106,13 +106,14 @@ __device__ void quant_key_page(const KParams &P, const Geom &G, const uint16_t *
             }
         kc[w] = val;
     }
-    if (is_kitty(P.scheme) && tid < 64) {
+    if (is_kitty(P.scheme) && tid < 4 * P.nb) {
+        // high plane q = tid >> 6 (offsets 16q ..): dword tid (see high_code_pos)
         uint32_t *kh = (uint32_t *)(page + G.kh);
-        int g = tid >> 4, r = tid & 15;
+        int q = tid >> 6, g = (tid >> 4) & 3, r = tid & 15;
         uint32_t val = 0;
         for (int n = 0; n < 4; n++)
             for (int i = 0; i < 4; i++) {
-                int o = 4 * g + i;
+                int o = 16 * q + 4 * g + i;
                 int cc = inv[o];
                 uint32_t hi = (uint32_t)(codes[16 * n + r][cc] >> 2);
                 val |= hi << (4 * (4 * (n & 1) + i) + 2 * (n >> 1));
@@ -126,13 +127,13 @@ __device__ void quant_key_page(const KParams &P, const Geom &G, const uint16_t *
 // and inv[o] (channel of high-plane offset o).
 __device__ void load_boost(const KParams &P, int h, int *inv, uint8_t *bits4) {
     const int tid = threadIdx.x;
-    if (tid < NB) inv[tid] = 0;
+    if (tid < NB_MAX) inv[tid] = 0;
     __syncthreads();
     if (tid < D) {
         bits4[tid] = 0;
         if (P.scheme == KVQ_SCHEME_KITTY) {
             int o = P.boost_idx[(size_t)h * D + tid];
-            if (o < NB) {
+            if (o < P.nb) {
                 bits4[tid] = 1;
                 inv[o] = tid;
             }
@@ -147,7 +148,7 @@ __device__ void load_boost(const KParams &P, int h, int *inv, uint8_t *bits4) {
 __global__ __launch_bounds__(64) void append_kivi_kernel(KParams P, const uint16_t *__restrict__ kn,
                                                          const uint16_t *__restrict__ vn) {
     const int h = blockIdx.x, b = blockIdx.y, lane = threadIdx.x;
-    const Geom G = geom(P.scheme);
+    const Geom G = geom(P.scheme, P.nb);
     const size_t bh = (size_t)b * P.Hkv + h;
     int32_t *st = P.state + bh * 4;
     const int l = st[0], nkq = st[1];
@@ -218,13 +219,13 @@ __global__ __launch_bounds__(64) void append_kivi_kernel(KParams P, const uint16
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void flush_kivi_kernel(KParams P) {
     const int h = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
-    const Geom G = geom(P.scheme);
+    const Geom G = geom(P.scheme, P.nb);
     const size_t bh = (size_t)b * P.Hkv + h;
     int32_t *st = P.state + bh * 4;
     const int l = st[0], nkq = st[1];
     if (l - nkq != P.R) return;
     __shared__ uint8_t codes[PT][D];
-    __shared__ int inv[NB];
+    __shared__ int inv[NB_MAX];
     __shared__ uint8_t bits4[D];
     __shared__ int bad;
     const int np = P.R / PT;
@@ -257,7 +258,7 @@ __global__ __launch_bounds__(256) void prefill_kivi_kernel(KParams P, int req0,
                                                           const int32_t *__restrict__ lengths) {
     const int p = blockIdx.x, h = blockIdx.y, rr = blockIdx.z, b = req0 + rr;
     const int tid = threadIdx.x;
-    const Geom G = geom(P.scheme);
+    const Geom G = geom(P.scheme, P.nb);
     const int R = P.R, S = P.sink;
     const int len = lengths[rr];
     if (len < 0 || len > S + P.max_pages * PT || (long long)len > ld) {
@@ -308,7 +309,7 @@ __global__ __launch_bounds__(256) void prefill_kivi_kernel(KParams P, int req0,
     }
     uint8_t *page = page_ptr(P, pid, h);
     __shared__ uint8_t codes[PT][D];
-    __shared__ int inv[NB];
+    __shared__ int inv[NB_MAX];
     __shared__ uint8_t bits4[D];
     load_boost(P, h, inv, bits4);
     if (t0 < nkq)                                    // nkq - S is a multiple of 128: whole page
@@ -356,7 +357,7 @@ __global__ __launch_bounds__(256) void prefill_kivi_kernel(KParams P, int req0,
 // Kitty calibration: static boost set per KV head from a calibration slice
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(128) void kitty_calibrate_kernel(const uint16_t *__restrict__ calib,
-                                                             int T, uint8_t *__restrict__ idx_out) {
+                                                             int T, int nb, uint8_t *__restrict__ idx_out) {
     const int h = blockIdx.x, c = threadIdx.x;
     __shared__ float am[D];
     __shared__ uint8_t chosen[D];
@@ -366,7 +367,7 @@ __global__ __launch_bounds__(128) void kitty_calibrate_kernel(const uint16_t *__
     chosen[c] = 0;
     __syncthreads();
     if (c == 0) {
-        for (int j = 0; j < NB; j++) {
+        for (int j = 0; j < nb; j++) {
             int best = -1;
             for (int cc = 0; cc < D; cc++)
                 if (!chosen[cc] && (best < 0 || am[cc] > am[best])) best = cc;
@@ -374,7 +375,7 @@ __global__ __launch_bounds__(128) void kitty_calibrate_kernel(const uint16_t *__
         }
         int off = 0;
         for (int cc = 0; cc < D; cc++)
-            idx_out[(size_t)h * D + cc] = chosen[cc] ? (uint8_t)(off++) : (uint8_t)(NB + 1);
+            idx_out[(size_t)h * D + cc] = chosen[cc] ? (uint8_t)(off++) : (uint8_t)(nb + 1);
     }
 }
 
@@ -469,7 +470,7 @@ __device__ void quant_witcert_block(const KParams &P, int b, int h, int blk, int
 
 __global__ __launch_bounds__(256) void flush_witcert_kernel(KParams P) {
     const int h = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
-    const Geom G = geom(P.scheme);
+    const Geom G = geom(P.scheme, P.nb);
     const size_t bh = (size_t)b * P.Hkv + h;
     int32_t *st = P.state + bh * 4;
     const int l = st[0], nq = st[1];
@@ -500,7 +501,7 @@ __global__ __launch_bounds__(256) void prefill_witcert_kernel(KParams P, int req
                                                              const int32_t *__restrict__ lengths) {
     const int p = blockIdx.x, h = blockIdx.y, rr = blockIdx.z, b = req0 + rr;
     const int tid = threadIdx.x;
-    const Geom G = geom(P.scheme);
+    const Geom G = geom(P.scheme, P.nb);
     const int len = lengths[rr];
     if (len < 0 || len > P.max_pages * WPT || (long long)len > ld) {
         if (p == 0 && tid == 0) atomicOr(P.status, (uint32_t)KVQ_STATUS_BAD_LENGTH);
@@ -580,7 +581,7 @@ hipError_t launch_prefill(const KParams &P, int req0, int n_req, const uint16_t 
 
 hipError_t launch_kitty_calibrate(const KParams &P, const uint16_t *calib, int n_tokens,
                                   uint8_t *idx_out, hipStream_t s) {
-    kitty_calibrate_kernel<<<P.Hkv, 128, 0, s>>>(calib, n_tokens, idx_out);
+    kitty_calibrate_kernel<<<P.Hkv, 128, 0, s>>>(calib, n_tokens, P.nb, idx_out);
     return hipGetLastError();
 }
 

@@ -96,6 +96,11 @@ def workload(wid: int, **over) -> Workload:
         w = dict(wid=6, name="kitty-dyn-mha-b16-h32-ctx32768", scheme="kitty_dyn", B=16, Hq=32,
                  Hkv=32, ctx=(32768,) * 16, n_outliers=4, outlier_factor=15.0, nb=16, steps=1,
                  seed=6)
+    elif wid == 8:
+        # Kitty-Pro: workload 4 with a quarter of the key channels boosted
+        w = dict(wid=8, name="kitty-pro-mha-b16-h32-ctx32768", scheme="kitty", B=16, Hq=32,
+                 Hkv=32, ctx=(32768,) * 16, n_outliers=4, outlier_factor=15.0, nb=32, steps=1,
+                 seed=8)
     elif wid == 7:
         # workload 3's shapes and lengths with 32 fp16 sink tokens per request
         w = dict(wid=7, name="kivi2-sink32-gqa-b64-32q8kv-ctx8k-32k-paged", scheme="kivi2", B=64,

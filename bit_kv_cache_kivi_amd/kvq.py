@@ -200,7 +200,7 @@ class KVCache:
         self.sink_k = torch.zeros((B, Hkv, S, 128), dtype=torch.int16, device=device) if S else None
         self.sink_v = torch.zeros((B, Hkv, S, 128), dtype=torch.int16, device=device) if S else None
         if layout.scheme == KVQ_SCHEME_KITTY:
-            idx = np.full((Hkv, 128), 17, np.uint8) if boost_idx is None else boost_idx
+            idx = np.full((Hkv, 128), layout.n_boost + 1, np.uint8) if boost_idx is None else boost_idx
             self.boost_idx = torch.from_numpy(np.ascontiguousarray(idx, np.uint8)).to(device)
         else:
             self.boost_idx = None

@@ -38,7 +38,7 @@ class Case:
                                  for h in range(w.Hkv)])
         layout = kvq.make_layout(w.scheme, w.B, w.Hq, w.Hkv, self.max_pages, self.n_pages,
                                  R=w.R, seed=self.seed, split_pages=split_pages, flags=flags,
-                                 sink=sink)
+                                 sink=sink, nb=w.nb if w.nb else None)
         self.cache = kvq.KVCache(layout, self.table, poison=poison)
         if w.scheme == "kitty":
             calib = np.stack([inputs.kitty_calibration(w, h) for h in range(w.Hkv)])
@@ -153,7 +153,7 @@ class Case:
             pidx = []
             kc, ks, kz, vc, vs, vz = gather_kivi(pool, self.table[b], h, w.Hkv, self.sid, qk,
                                                  qv, None if self.idx is None else self.idx[h],
-                                                 page_idx=pidx)
+                                                 page_idx=pidx, nb=w.nb if w.nb else 16)
             if w.scheme == "kitty_dyn":               # each key page's boosted channel set
                 ou = s.unit_index()
                 for p in range(qk // PT):

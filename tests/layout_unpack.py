@@ -10,12 +10,23 @@ D = 128
 PT = 64
 WPT = 256
 
-GEOM = {  # kc, kh, ks, vc, vs, (ki,) bytes
-    0: dict(kc=0, kh=0, ks=2048, vc=3072, vs=5120, bytes=6144, tokens=PT),
-    1: dict(kc=0, kh=2048, ks=2304, vc=3328, vs=5376, bytes=6400, tokens=PT),
-    2: dict(kc=0, kh=0, ks=32768, vc=33024, vs=65792, bytes=66048, tokens=WPT),
-    3: dict(kc=0, kh=2048, ks=2304, vc=3328, vs=5376, ki=6400, bytes=6416, tokens=PT),
-}
+def geom(scheme: int, nb: int = 16) -> dict:
+    """Block layout: KIVI-2 (0), Kitty (1, nb boosted channels: one 256-B high
+    plane per 16), WitCert (2), Kitty dynamic (3: Kitty + the page's nb
+    channel ids, at least 16 bytes)."""
+    if scheme == 0:
+        return dict(kc=0, kh=0, ks=2048, vc=3072, vs=5120, bytes=6144, tokens=PT)
+    if scheme == 2:
+        return dict(kc=0, kh=0, ks=32768, vc=33024, vs=65792, bytes=66048, tokens=WPT)
+    ks = 2048 + 16 * nb
+    g = dict(kc=0, kh=2048, ks=ks, vc=ks + 1024, vs=ks + 3072, bytes=ks + 4096, tokens=PT)
+    if scheme == 3:
+        g["ki"] = g["bytes"]
+        g["bytes"] += max(16, nb)
+    return g
+
+
+GEOM = {s: geom(s) for s in range(4)}
 KITTY_SCHEMES = (1, 3)
 
 
@@ -41,11 +52,11 @@ def _value_index():
     return dword, shift
 
 
-def _high_index():
+def _high_index(nb=16):
     t = np.arange(PT)[:, None]
-    o = np.arange(16)[None, :]
-    n, r, g, i = t >> 4, t & 15, o >> 2, o & 3
-    dword = 16 * g + r
+    o = np.arange(nb)[None, :]
+    n, r, q, g, i = t >> 4, t & 15, o >> 4, (o & 15) >> 2, o & 3
+    dword = 64 * q + 16 * g + r
     shift = 4 * (4 * (n & 1) + i) + 2 * (n >> 1)
     return dword, shift
 
@@ -62,21 +73,22 @@ def _u32(block: np.ndarray, off: int, n: int) -> np.ndarray:
 
 def key_codes(block: np.ndarray, scheme: int) -> np.ndarray:
     """Low 2-bit key codes [64][128]."""
-    g = GEOM[scheme]
+    g = geom(scheme)
     kc = _u32(block, g["kc"], 512)
     return ((kc[KEY_DW] >> KEY_SH) & 3).astype(np.uint8)
 
 
-def key_high(block: np.ndarray) -> np.ndarray:
-    """Kitty high plane [64][16] by boosted offset (same place in both Kitty schemes)."""
-    g = GEOM[1]
-    kh = _u32(block, g["kh"], 64)
-    return ((kh[HI_DW] >> HI_SH) & 3).astype(np.uint8)
+def key_high(block: np.ndarray, nb: int = 16) -> np.ndarray:
+    """Kitty high planes [64][nb] by boosted offset (same place in both Kitty schemes)."""
+    g = geom(1, nb)
+    kh = _u32(block, g["kh"], 4 * nb)
+    dw, sh = _high_index(nb)
+    return ((kh[dw] >> sh) & 3).astype(np.uint8)
 
 
-def key_stats(block: np.ndarray, scheme: int):
+def key_stats(block: np.ndarray, scheme: int, nb: int = 16):
     """(scale, zero) fp16 bits [2 groups][128 channels]."""
-    g = GEOM[scheme]
+    g = geom(scheme, nb)
     ks = _u32(block, g["ks"], 256).reshape(2, 128)[:, KEY_SLOT]
     return (ks & 0xFFFF).astype(np.uint16), (ks >> 16).astype(np.uint16)
 
@@ -84,21 +96,22 @@ def key_stats(block: np.ndarray, scheme: int):
 def page_boost_index(block: np.ndarray, nb: int = 16) -> np.ndarray:
     """Kitty dynamic: the page's boost index per channel (offset, or nb + 1)
     from its stored channel ids."""
-    ids = block[GEOM[3]["ki"]:GEOM[3]["ki"] + nb]
+    ki = geom(3, nb)["ki"]
+    ids = block[ki:ki + nb]
     idx = np.full(D, nb + 1, np.uint8)
     idx[ids.astype(np.int64)] = np.arange(nb, dtype=np.uint8)
     return idx
 
 
-def value_codes(block: np.ndarray, scheme: int) -> np.ndarray:
-    g = GEOM[scheme]
+def value_codes(block: np.ndarray, scheme: int, nb: int = 16) -> np.ndarray:
+    g = geom(scheme, nb)
     vc = _u32(block, g["vc"], 512)
     return ((vc[VAL_DW] >> VAL_SH) & 3).astype(np.uint8)
 
 
-def value_stats(block: np.ndarray, scheme: int):
+def value_stats(block: np.ndarray, scheme: int, nb: int = 16):
     """(scale, zero) fp16 bits [64 tokens][4 groups]."""
-    g = GEOM[scheme]
+    g = geom(scheme, nb)
     vs = _u32(block, g["vs"], 256).reshape(64, 4)
     return (vs & 0xFFFF).astype(np.uint16), (vs >> 16).astype(np.uint16)
 
@@ -113,13 +126,13 @@ def witcert_block(block: np.ndarray):
     return kc, ks, vc, vs
 
 
-def page_block(pool: np.ndarray, pid: int, h: int, Hkv: int, scheme: int) -> np.ndarray:
-    nb = GEOM[scheme]["bytes"]
-    off = (pid * Hkv + h) * nb
-    return pool[off:off + nb]
+def page_block(pool: np.ndarray, pid: int, h: int, Hkv: int, scheme: int, nb: int = 16) -> np.ndarray:
+    nbytes = geom(scheme, nb)["bytes"]
+    off = (pid * Hkv + h) * nbytes
+    return pool[off:off + nbytes]
 
 
-def gather_kivi(pool, table_row, h, Hkv, scheme, n_kq, n_vq, idx=None, page_idx=None):
+def gather_kivi(pool, table_row, h, Hkv, scheme, n_kq, n_vq, idx=None, page_idx=None, nb=16):
     """Logical record of one (request, KV head) for tokens below n_kq / n_vq:
     key codes (4-bit for Kitty boosted channels) [n_kq][128], key stats
     [n_kq/32][128] x2, value codes [n_vq][128], value stats [n_vq][4] x2.
@@ -132,26 +145,26 @@ def gather_kivi(pool, table_row, h, Hkv, scheme, n_kq, n_vq, idx=None, page_idx=
     vs = np.zeros((n_vq, 4), np.uint16)
     vz = np.zeros((n_vq, 4), np.uint16)
     for p in range((max(n_kq, n_vq) + PT - 1) // PT):
-        blk = page_block(pool, int(table_row[p]), h, Hkv, scheme)
+        blk = page_block(pool, int(table_row[p]), h, Hkv, scheme, nb)
         t0 = p * PT
         if t0 < n_kq:
             codes = key_codes(blk, scheme).astype(np.uint8)
             if scheme in KITTY_SCHEMES:
-                pidx = idx if scheme == 1 else page_boost_index(blk)
+                pidx = idx if scheme == 1 else page_boost_index(blk, nb)
                 if page_idx is not None:
                     page_idx.append(pidx)
-                hi = key_high(blk)
+                hi = key_high(blk, nb)
                 for c in range(D):
-                    if pidx[c] < 16:
+                    if pidx[c] < nb:
                         codes[:, c] |= hi[:, pidx[c]] << 2
             kcodes[t0:t0 + PT] = codes
-            s, z = key_stats(blk, scheme)
+            s, z = key_stats(blk, scheme, nb)
             ks[t0 // 32:t0 // 32 + 2] = s
             kz[t0 // 32:t0 // 32 + 2] = z
         if t0 < n_vq:
             n = min(PT, n_vq - t0)
-            vcodes[t0:t0 + n] = value_codes(blk, scheme)[:n]
-            s, z = value_stats(blk, scheme)
+            vcodes[t0:t0 + n] = value_codes(blk, scheme, nb)[:n]
+            s, z = value_stats(blk, scheme, nb)
             vs[t0:t0 + n] = s[:n]
             vz[t0:t0 + n] = z[:n]
     return kcodes, ks, kz, vcodes, vs, vz

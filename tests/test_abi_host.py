@@ -74,9 +74,11 @@ def test_page_geometry_and_bytes_per_token(K):
     # values), 100 with Kitty's 16-channel high plane, 258 for the INT8 block
     # scheme (128 codes + an fp16 scale per 256-token block and channel, twice);
     # Kitty dynamic adds the page's 16 boosted channel ids (0.25 B/token)
-    for scheme, bpt in (("kivi2", 96.0), ("kitty", 100.0), ("witcert", 258.0),
-                        ("kitty_dyn", 100.25)):
-        L = K.make_layout(scheme, B=1, Hq=1, Hkv=1, max_pages=1, n_pages=1)
+    # Kitty-Pro (32 boosted channels): one more 256-B high plane, 104 B/token
+    for scheme, nb, bpt in (("kivi2", None, 96.0), ("kitty", None, 100.0), ("witcert", None, 258.0),
+                            ("kitty_dyn", None, 100.25), ("kitty", 32, 104.0),
+                            ("kitty_dyn", 32, 104.5)):
+        L = K.make_layout(scheme, B=1, Hq=1, Hkv=1, max_pages=1, n_pages=1, nb=nb)
         assert K.bytes_per_token(L) == bpt
         assert K.page_bytes(L) == bpt * K.page_tokens(L)
     bad = K.make_layout("kivi2", B=1, Hq=1, Hkv=1, max_pages=1, n_pages=1)
@@ -115,7 +117,13 @@ def test_residual_must_hold_whole_key_groups(K):
 def test_kitty_and_witcert_fields(K):
     L = K.make_layout("kitty", B=1, Hq=4, Hkv=4, max_pages=8, n_pages=8, nb=0)
     assert set_layout(K, L)[0] == K.KVQ_EINVAL
-    L = K.make_layout("kitty_dyn", B=1, Hq=4, Hkv=4, max_pages=8, n_pages=8, nb=8)
+    for scheme in ("kitty", "kitty_dyn"):
+        for nb, want in ((8, K.KVQ_EINVAL), (16, K.KVQ_OK), (24, K.KVQ_EINVAL), (32, K.KVQ_OK),
+                         (64, K.KVQ_EINVAL)):
+            L = K.make_layout(scheme, B=1, Hq=4, Hkv=4, max_pages=8, n_pages=8, nb=nb)
+            assert set_layout(K, L)[0] == want, (scheme, nb)
+    L = K.make_layout("kitty", B=1, Hq=4, Hkv=4, max_pages=8, n_pages=8, nb=32,
+                      flags=K.FLAG_GENERIC_STAGE1)          # the VALU stage 1: 16 only
     assert set_layout(K, L)[0] == K.KVQ_EINVAL
     # the VALU stage 1 knows only the static boost table
     L = K.make_layout("kitty_dyn", B=1, Hq=4, Hkv=4, max_pages=8, n_pages=8,

@@ -155,6 +155,41 @@ def test_sink_short_contexts(ctx):
     case.check_store()
 
 
+@pytest.mark.parametrize("wid,Hq,Hkv", [(8, 2, 2), (8, 8, 2)])
+def test_kitty_pro_32_boosted_store_decode(wid, Hq, Hkv):
+    # 32 boosted channels (two high planes), static set from the calibration
+    w = inputs.workload(wid, B=2, Hq=Hq, Hkv=Hkv, ctx=(1100, 1500))
+    case = _case(w, extra_tokens=200, split_pages=3)
+    idx_gpu = case.cache.boost_idx.cpu().numpy()
+    assert np.array_equal(idx_gpu, case.idx)
+    assert (idx_gpu < 32).sum(axis=1).tolist() == [32] * Hkv
+    case.check_state()
+    case.check_store()
+    out, cert, q = case.decode_now(1)
+    _check_decode(case, out, cert, q)
+    for i in range(130):
+        out, cert, q = case.step(decode=(i % 64 == 63))
+        if out is not None:
+            _check_decode(case, out, cert, q)
+    case.check_store()
+
+
+def test_kitty_pro_dynamic_with_sink():
+    # 32 boosted channels chosen per page, behind 32 sink tokens
+    w = inputs.workload(6, B=2, Hq=4, Hkv=2, ctx=(900, 1300), nb=32)
+    case = _case(w, extra_tokens=200, split_pages=2, sink=32)
+    case.check_state()
+    case.check_store()
+    out, cert, q = case.decode_now(1)
+    _check_decode(case, out, cert, q)
+    for i in range(140):
+        out, cert, q = case.step(decode=(i % 64 == 63 or i == 0))
+        if out is not None:
+            _check_decode(case, out, cert, q)
+    case.check_status()
+    case.check_store()
+
+
 @pytest.mark.parametrize("Hq,Hkv,split", [(2, 2, 3), (8, 2, 2)])
 def test_kitty_dynamic_store_decode(Hq, Hkv, split):
     # boosted set chosen per page: bit-exact codes, high plane and per-page

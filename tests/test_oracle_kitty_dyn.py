@@ -146,3 +146,40 @@ def test_boosted_channels_take_sixteen_levels_within_bound():
 def test_selection_unit_must_divide_the_residual(sel):
     with pytest.raises(ValueError):
         O.Stream(O.KITTY_DYN, 1024, nb=NB, sel=sel)       # R = 128, G = 32
+
+
+def brute_select_amax(k, nb):
+    amax = np.abs(f32(k)).max(axis=0)
+    order = np.lexsort((np.arange(D), -amax))
+    chosen = np.sort(order[:nb])
+    idx = np.full(D, nb + 1, np.uint8)
+    idx[chosen] = np.arange(nb)
+    return idx
+
+
+@pytest.mark.parametrize("scheme", [O.KITTY, O.KITTY_DYN])
+def test_kitty_pro_boosts_a_quarter_of_the_channels(scheme):
+    # Kitty-Pro reading: alpha = 1/4, 32 of 128 key channels at 4 bits
+    rng = np.random.default_rng(16)
+    K = f16(rng.standard_normal((700, D)) * rng.uniform(0.1, 6, D))
+    V = f16(rng.standard_normal((700, D)))
+    idx = O.kitty_select(K[:512], 32) if scheme == O.KITTY else None
+    if idx is not None:
+        assert np.array_equal(idx, brute_select_amax(K[:512], 32))
+    s = O.Stream(scheme, 1024, nb=32, idx=idx, sel=64)
+    s.prefill(K, V)
+    l, n_kq, _ = s.state
+    codes = s.key_codes()[:n_kq]
+    for p in range(n_kq // 64):
+        pidx = idx if scheme == O.KITTY else s.unit_index()[p]
+        if scheme == O.KITTY_DYN:
+            assert np.array_equal(pidx, brute_select(K[64 * p:64 * p + 64], 32))
+        boosted = pidx < 32
+        assert boosted.sum() == 32
+        page = codes[64 * p:64 * p + 64]
+        assert page[:, ~boosted].max() <= 3 and page[:, boosted].max() > 3
+    Kt, _ = s.dequant(0, n_kq)
+    ks, _ = s.key_stats()
+    step = f32(ks[: n_kq // 32]).repeat(32, axis=0).astype(np.float64)
+    err = np.abs(f32(K[:n_kq]).astype(np.float64) - Kt)
+    assert np.all(err <= step / 2 * (1 + 2.0 ** -20) + 1e-30)
