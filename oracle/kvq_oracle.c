@@ -308,7 +308,9 @@ void ko_kitty_select_dyn(const uint16_t *k, long T, long ld, int D, int nb, uint
 /* a token's fp16 value is read only while it is inside a residual window. */
 /* ------------------------------------------------------------------------ */
 
-enum { KO_KIVI = 0, KO_KITTY = 1, KO_WITCERT = 2, KO_KITTY_DYN = 3 };
+/* KO_KIVI4: the KIVI scheme at 4 bits for keys and values ([KIVI] reports
+ * its quantizer at 2 and 4 bits; the same groups, statistics and windows). */
+enum { KO_KIVI = 0, KO_KITTY = 1, KO_WITCERT = 2, KO_KITTY_DYN = 3, KO_KIVI4 = 4 };
 
 typedef struct ko_stream {
     int scheme, D, G, R, VG, BLK, nb, bits_v;
@@ -341,7 +343,7 @@ ko_stream *ko_stream_new(int scheme, int D, int G, int R, int VG, int BLK,
 {
     if (sink < 0 || (sink > 0 && scheme == KO_WITCERT)) return NULL;
     if (D <= 0 || D > 256 || cap <= 0) return NULL;
-    if (scheme < KO_KIVI || scheme > KO_KITTY_DYN) return NULL;
+    if (scheme < KO_KIVI || scheme > KO_KIVI4) return NULL;
     if (scheme != KO_WITCERT) {
         if (G <= 0 || R <= 0 || R % G != 0 || VG <= 0 || D % VG != 0) return NULL;
         if (nb < 0 || nb > D) return NULL;
@@ -352,6 +354,7 @@ ko_stream *ko_stream_new(int scheme, int D, int G, int R, int VG, int BLK,
     ko_stream *s = (ko_stream *)calloc(1, sizeof(ko_stream));
     s->scheme = scheme; s->D = D; s->G = G; s->R = R; s->VG = VG; s->BLK = BLK;
     s->nb = (scheme == KO_KITTY || scheme == KO_KITTY_DYN) ? nb : 0;
+    s->bits_v = (scheme == KO_KIVI4) ? 4 : 2;
     if (scheme == KO_KITTY_DYN) {
         s->sel = sel;
         s->uidx = (uint8_t *)calloc((size_t)((cap / sel + 1) * D), 1);
@@ -397,6 +400,7 @@ static int boost_off(const ko_stream *s, long g, int c)
 
 static int key_bits(const ko_stream *s, long g, int c)
 {
+    if (s->scheme == KO_KIVI4) return 4;
     return boost_off(s, g, c) < s->nb ? 4 : 2;
 }
 
@@ -424,7 +428,7 @@ static void quant_value_token(ko_stream *s, long t)
 {
     int ng = s->D / s->VG;
     for (int j = 0; j < ng; j++)
-        ko_quant_asym(&s->Vraw[t * s->D + j * s->VG], s->VG, 1, 2,
+        ko_quant_asym(&s->Vraw[t * s->D + j * s->VG], s->VG, 1, s->bits_v,
                       &s->Vs[t * ng + j], &s->Vz[t * ng + j],
                       &s->Vc[t * s->D + j * s->VG], 1);
 }

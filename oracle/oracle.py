@@ -19,7 +19,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 SRC = os.path.join(HERE, "kvq_oracle.c")
 LIB = os.path.join(HERE, "_build", "libkvq_oracle.so")
 
-KIVI, KITTY, WITCERT, KITTY_DYN = 0, 1, 2, 3
+KIVI, KITTY, WITCERT, KITTY_DYN, KIVI4 = 0, 1, 2, 3, 4
 
 GCC_FLAGS = ["-std=c11", "-O2", "-fPIC", "-shared", "-ffp-contract=off",
              "-fno-fast-math", "-fno-finite-math-only"]
