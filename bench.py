@@ -62,10 +62,18 @@ def log(msg: str):
 def key_q_bytes(scheme: str, n: int, nb: int = 16) -> int:
     """Quantized key bytes of n tokens: codes + stats (48 B) + the Kitty high
     plane (nb/4 B), and for Kitty dynamic the channel ids of each 64-token
-    page touched (max(16, nb) B)."""
+    page touched (max(16, nb) B); KIVI-4: 64 B of codes + 16 B of stats."""
+    if scheme == "kivi4":
+        return n * 80
     if scheme == "kitty_dyn":
         return n * (48 + nb // 4) + ((n + 63) // 64) * max(16, nb)
     return n * (48 + nb // 4) if scheme == "kitty" else n * 48
+
+
+def value_q_bytes(scheme: str) -> int:
+    """Quantized value bytes per token: codes (2 or 4 bits x 128) + 4 groups'
+    fp16 (scale, zero)."""
+    return 80 if scheme == "kivi4" else 48
 
 
 def kivi_bytes(l: int, n_kq: int, R: int, qpk: int, scheme: str, sink: int = 0,
@@ -74,7 +82,7 @@ def kivi_bytes(l: int, n_kq: int, R: int, qpk: int, scheme: str, sink: int = 0,
     ns = min(l, sink)                              # fp16 sink tokens, keys and values
     n_vq = max(0, l - sink - R)                    # quantized values after the sink
     kq = max(0, n_kq - sink)                       # quantized keys after the sink
-    paged = key_q_bytes(scheme, n_vq, nb) + n_vq * 48
+    paged = key_q_bytes(scheme, n_vq, nb) + n_vq * value_q_bytes(scheme)
     window = key_q_bytes(scheme, kq - n_vq, nb) + (l - max(n_kq, ns)) * 256 + (l - ns - n_vq) * 256
     window += ns * 512
     qo = qpk * (256 + 512)
@@ -101,7 +109,7 @@ def write_bytes(w: inputs.Workload, l_before: int, n_kq_before: int) -> int:
     if l_before < w.sink:
         return b                       # a sink token: fp16 only
     if l_before - w.sink >= w.R:
-        b += 256 + 48                  # value leaving the window, its codes + stats
+        b += 256 + value_q_bytes(w.scheme)     # value leaving the window, its codes + stats
     if l_before - n_kq_before == w.R:
         b += w.R * 256 + key_q_bytes(w.scheme, w.R, w.nb or 16)
     return b
@@ -256,7 +264,8 @@ def run_gpu(w: inputs.Workload, steps: int, warmup: int, split_pages: int, copie
 def cpu_baseline(w: inputs.Workload, warmup: int, target_s: float = 15.0, threads: int = 0,
                  n_pairs: int = 0):
     from oracle import oracle as O
-    sid = {"kivi2": O.KIVI, "kitty": O.KITTY, "witcert": O.WITCERT, "kitty_dyn": O.KITTY_DYN}[w.scheme]
+    sid = {"kivi2": O.KIVI, "kitty": O.KITTY, "witcert": O.WITCERT, "kitty_dyn": O.KITTY_DYN,
+           "kivi4": O.KIVI4}[w.scheme]
     if threads <= 0:
         threads = max(1, min(16, len(os.sched_getaffinity(0))))
     idx = None
@@ -416,7 +425,7 @@ def main():
     rec = {"metric": METRIC, "value": round(gbs, 1), "unit": "GB/s", "n_gpus": 1,
            "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
            "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-           "dtype": "u2+f32" if w.scheme != "witcert" else "i8+f32", "data": "synthetic",
+           "dtype": {"witcert": "i8+f32", "kivi4": "u4+f32"}.get(w.scheme, "u2+f32"), "data": "synthetic",
            "config": {"workload": w.name, "batch": w.B, "q_heads": w.Hq, "kv_heads": w.Hkv,
                       "head_dim": w.D, "ctx_mean": float(np.mean(w.ctx)),
                       "ctx_min": int(min(w.ctx)), "ctx_max": int(max(w.ctx)),

@@ -32,6 +32,7 @@ int validate_layout(const kvq_layout_t *L) {
         case KVQ_SCHEME_KIVI2:
         case KVQ_SCHEME_KITTY:
         case KVQ_SCHEME_KITTY_DYN:
+        case KVQ_SCHEME_KIVI4:
             if (L->group != 32 || L->value_group != 32) return KVQ_EINVAL;
             // the key residual is quantized in whole groups: R % G == 0, and
             // the flush writes whole 64-token pages
@@ -42,6 +43,8 @@ int validate_layout(const kvq_layout_t *L) {
                 return KVQ_EINVAL;
             // the VALU stage 1 handles 16 boosted channels only
             if (L->n_boost > kvq::NB && (L->flags & KVQ_FLAG_GENERIC_STAGE1)) return KVQ_EINVAL;
+            // nor 4-bit codes
+            if (L->scheme == KVQ_SCHEME_KIVI4 && (L->flags & KVQ_FLAG_GENERIC_STAGE1)) return KVQ_EINVAL;
             // the VALU stage 1 reads the head's static boost table only
             if (L->scheme == KVQ_SCHEME_KITTY_DYN && (L->flags & KVQ_FLAG_GENERIC_STAGE1))
                 return KVQ_EINVAL;
@@ -109,13 +112,13 @@ extern "C" {
 
 int64_t kvq_page_bytes(const kvq_layout_t *L) {
     if (!L) return 0;
-    if (L->scheme < KVQ_SCHEME_KIVI2 || L->scheme > KVQ_SCHEME_KITTY_DYN) return 0;
+    if (L->scheme < KVQ_SCHEME_KIVI2 || L->scheme > KVQ_SCHEME_KIVI4) return 0;
     return kvq::geom(L->scheme, L->n_boost).bytes;
 }
 
 int32_t kvq_page_tokens(const kvq_layout_t *L) {
     if (!L) return 0;
-    if (L->scheme < KVQ_SCHEME_KIVI2 || L->scheme > KVQ_SCHEME_KITTY_DYN) return 0;
+    if (L->scheme < KVQ_SCHEME_KIVI2 || L->scheme > KVQ_SCHEME_KIVI4) return 0;
     return kvq::geom(L->scheme, L->n_boost).tokens;
 }
 

@@ -29,6 +29,9 @@ constexpr int NB_MAX = 32;      // Kitty-Pro: alpha = 1/4
 //   VS  1024 B  value {scale, zero} fp16 pairs, [64 tokens][4 groups]
 //   KI  max(16, nb) B  KITTY_DYN: the page's boosted channel ids, ascending
 //               (the high-plane offset of KI[o] is o)
+// KIVI4, 64 tokens:
+//   KC 4096 B 4-bit key codes (see key_code_pos4), KS 1024 B as KIVI2,
+//   VC 4096 B 4-bit value codes (see value_code_pos4), VS 1024 B as KIVI2
 // WITCERT, 256 tokens (one block):
 //   KC 32768 B int8 [256][128];  KS 256 B fp16 [128];
 //   VC 32768 B int8 [256][128];  VS 256 B fp16 [128]
@@ -53,6 +56,9 @@ __host__ __device__ inline Geom geom(int scheme, int nb = NB) {
             g.ki = g.bytes;
             g.bytes += nb > 16 ? nb : 16;
         }
+        g.tokens = PT;
+    } else if (scheme == KVQ_SCHEME_KIVI4) {
+        g.kc = 0; g.kh = 0; g.ks = 4096; g.vc = 5120; g.vs = 9216; g.bytes = 10240;
         g.tokens = PT;
     } else {
         g.kc = 0; g.kh = 0; g.ks = 2048; g.vc = 3072; g.vs = 5120; g.bytes = 6144;
@@ -84,6 +90,29 @@ __host__ __device__ inline void value_code_pos(int t, int c, int &dword, int &sh
     int lane = 16 * g + r;
     dword = (nt >> 2) * 256 + lane * 4 + (nt & 3);
     shift = 4 * j + 2 * ks;
+}
+
+// KIVI4 codes, eight to a dword: the dword's code k (k = 0..7) sits in byte
+// k & 3 at nibble k >> 2, so the dword masked with 0x0F0F0F0F holds codes
+// 0..3 one per byte and (x >> 4) & 0x0F0F0F0F codes 4..7.  A byte holding
+// b < 16 reads as the e4m3 number b / 512 (subnormal for b < 8, exponent 1
+// above), so the packed fp8 -> f16 converter with scale 512 yields the codes
+// exactly, in k order.
+// Keys: lane L = 16*((c>>3)&3) + (t&15) loads dwords {256*p + 4*L + i},
+// p = t >> 4 (token tile), i = c >> 5; code k = c & 7.
+__host__ __device__ inline void key_code_pos4(int t, int c, int &dword, int &shift) {
+    int n = t >> 4, r = t & 15, kc = c >> 5, g = (c >> 3) & 3, k = c & 7;
+    dword = 256 * n + 4 * (16 * g + r) + kc;
+    shift = 8 * (k & 3) + 4 * (k >> 2);
+}
+
+// Values: lane L = 16*((t>>3)&3) + (c&15) holds dword d = 8*(t>>5) + (c>>4)
+// at 256*(d>>2) + 4*L + (d&3); code k = t & 7.
+__host__ __device__ inline void value_code_pos4(int t, int c, int &dword, int &shift) {
+    int nt = c >> 4, r = c & 15, ks = t >> 5, g = (t >> 3) & 3, k = t & 7;
+    int d = 8 * ks + nt;
+    dword = 256 * (d >> 2) + 4 * (16 * g + r) + (d & 3);
+    shift = 8 * (k & 3) + 4 * (k >> 2);
 }
 
 // Kitty high plane: (token t in page, boosted offset o in [0, nb)).  Plane

@@ -124,6 +124,7 @@ __device__ void window_partial(const KParams &P, const uint16_t *__restrict__ q,
     constexpr bool wit = SCHEME == KVQ_SCHEME_WITCERT;
     constexpr bool kitty = is_kitty(SCHEME);
     constexpr bool dyn = SCHEME == KVQ_SCHEME_KITTY_DYN;
+    constexpr bool four = SCHEME == KVQ_SCHEME_KIVI4;
     const int g = lane >> 4, r = lane & 15;
     const size_t bh = (size_t)b * P.Hkv + h;
     const int l = P.state[bh * 4], nkq = P.state[bh * 4 + 1];
@@ -216,11 +217,15 @@ __device__ void window_partial(const KParams &P, const uint16_t *__restrict__ q,
                 const int pi = (t - S) / PT - pA, tp = (t - S) % PT, gi = tp >> 5, n16 = tp >> 4;
                 const uint8_t *pg = cpage(P, pi ? pids[1] : pids[0], h);
                 const uint32_t *kcw = (const uint32_t *)(pg + G.kc);
-                uint32_t xa[2];
+                uint32_t xa[4];                   // KIVI2: xa[0..1]; KIVI4: one dword per kc
 #pragma unroll
-                for (int a = 0; a < 2; a++) {
-                    const int d = 2 * n16 + a;
-                    xa[a] = kcw[(d >> 2) * 256 + (16 * g + (tp & 15)) * 4 + (d & 3)];
+                for (int a = 0; a < 4; a++) {
+                    if (four) {
+                        xa[a] = kcw[256 * n16 + 4 * (16 * g + (tp & 15)) + a];
+                    } else if (a < 2) {
+                        const int d = 2 * n16 + a;
+                        xa[a] = kcw[(d >> 2) * 256 + (16 * g + (tp & 15)) * 4 + (d & 3)];
+                    }
                 }
                 uint32_t kh[8] = {0u, 0u, 0u, 0u, 0u, 0u, 0u, 0u};   // offsets 4u .. 4u+3
                 if (kitty) {
@@ -238,7 +243,9 @@ __device__ void window_partial(const KParams &P, const uint16_t *__restrict__ q,
                     float kf[8];
 #pragma unroll
                     for (int i = 0; i < 8; i++) {
-                        uint32_t code = (xa[kc >> 1] >> (4 * i + 2 * (kc & 1))) & 3u;
+                        const uint32_t code0 = four ? (xa[kc] >> (8 * (i & 3) + 4 * (i >> 2))) & 15u
+                                                    : (xa[kc >> 1] >> (4 * i + 2 * (kc & 1))) & 3u;
+                        uint32_t code = code0;
                         if (kitty) {
                             const int o = dyn ? ws.bidx[pi][32 * kc + 8 * g + i]
                                               : P.boost_idx[(size_t)h * D + 32 * kc + 8 * g + i];
@@ -1006,7 +1013,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(3, 8))) void
 }
 
 // ---------------------------------------------------------------------------
-// Stage 1, KIVI2 / KITTY, one query head per wave on the matrix cores (any
+// Stage 1, KIVI2 / KITTY / KIVI4, one query head per wave on the matrix cores (any
 // group size, MHA included).  The same 16x16x32 f16 products as the group
 // kernel, with the one query spread over operand rows and columns instead of
 // four queries:
@@ -1041,16 +1048,29 @@ __device__ inline h8v frag8_x4(uint32_t m) {     // codes times 4
     return __builtin_bit_cast(h8v, v);
 }
 
+// eight 4-bit codes of a dword (code k in byte k & 3, nibble k >> 2) -> f16
+// fragment in k order: a byte b < 16 is the e4m3 number b / 512
+__device__ inline h8v frag8_b4(uint32_t x) {
+    const uint32_t lo = x & 0x0F0F0F0Fu, hi = (x >> 4) & 0x0F0F0F0Fu;
+    const u4v v = {__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(lo, 512.0f, false)),
+                   __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(lo, 512.0f, true)),
+                   __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(hi, 512.0f, false)),
+                   __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(hi, 512.0f, true))};
+    return __builtin_bit_cast(h8v, v);
+}
+
 struct HeadPage {
     PageRegs R;
+    uint4 k2, k3, v2, v3;           // KIVI4: the second halves of the key and value codes
     uint32_t khw[2];                // Kitty high planes (offsets 0..15, 16..31), dword = lane
     uint32_t kiw[2];                // KITTY_DYN: channel ids of offsets 16q + 4g .. +3
 };
 
-template <bool KITTY, bool DYN>
-__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(3, 8)))
+template <bool KITTY, bool DYN, bool FOUR>
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(FOUR ? 2 : 3, 8)))
 void stage1_head_mfma_kernel(KParams P, const uint16_t *__restrict__ q, Workspace W, float qscale) {
-    constexpr int SCHEME = DYN ? KVQ_SCHEME_KITTY_DYN : KITTY ? KVQ_SCHEME_KITTY : KVQ_SCHEME_KIVI2;
+    constexpr int SCHEME = FOUR ? KVQ_SCHEME_KIVI4
+                                : DYN ? KVQ_SCHEME_KITTY_DYN : KITTY ? KVQ_SCHEME_KITTY : KVQ_SCHEME_KIVI2;
     const S1Item it = s1_item(W.max_splits, W.n_win);
     const int s = it.s, hq = it.hd, b = it.b;
     const int lane = threadIdx.x, g = lane >> 4, r = lane & 15;
@@ -1145,7 +1165,10 @@ void stage1_head_mfma_kernel(KParams P, const uint16_t *__restrict__ q, Workspac
         lds_sync();
 
         // ---- scores on the matrix cores ----
-        const uint32_t kd[8] = {R.ka.x, R.ka.y, R.ka.z, R.ka.w, R.kb.x, R.kb.y, R.kb.z, R.kb.w};
+        // KIVI2: dword 2n + (kc >> 1) of token tile n holds kc's codes at
+        // bit pair kc & 1 of each nibble; KIVI4: dword 4n + kc
+        const uint32_t kd[16] = {R.ka.x, R.ka.y, R.ka.z, R.ka.w, R.kb.x, R.kb.y, R.kb.z, R.kb.w,
+                                 HP.k2.x, HP.k2.y, HP.k2.z, HP.k2.w, HP.k3.x, HP.k3.y, HP.k3.z, HP.k3.w};
         f4v sc[4];
 #pragma unroll
         for (int n = 0; n < 4; n++) sc[n] = f4v{0.f, 0.f, 0.f, 0.f};
@@ -1156,8 +1179,12 @@ void stage1_head_mfma_kernel(KParams P, const uint16_t *__restrict__ q, Workspac
             for (int gi = 0; gi < 2; gi++) af[gi] = sm.As[gi][arow][4 * kc + g];
 #pragma unroll
             for (int n = 0; n < 4; n++) {
-                const uint32_t x = kd[2 * n + (kc >> 1)];
-                bf[n] = frag8((kc & 1) ? ((x >> 2) & MSK) : (x & MSK));
+                if (FOUR) {
+                    bf[n] = frag8_b4(kd[4 * n + kc]);
+                } else {
+                    const uint32_t x = kd[2 * n + (kc >> 1)];
+                    bf[n] = frag8((kc & 1) ? ((x >> 2) & MSK) : (x & MSK));
+                }
             }
 #pragma unroll
             for (int n = 0; n < 4; n++)
@@ -1234,14 +1261,17 @@ void stage1_head_mfma_kernel(KParams P, const uint16_t *__restrict__ q, Workspac
         lds_sync();
 
         // ---- P.V on the matrix cores ----
-        const uint32_t vd[8] = {R.va.x, R.va.y, R.va.z, R.va.w, R.vb.x, R.vb.y, R.vb.z, R.vb.w};
+        // KIVI2: dword nt holds both 32-token steps (bit pair ks of each
+        // nibble); KIVI4: dword 8 ks + nt
+        const uint32_t vd[16] = {R.va.x, R.va.y, R.va.z, R.va.w, R.vb.x, R.vb.y, R.vb.z, R.vb.w,
+                                 HP.v2.x, HP.v2.y, HP.v2.z, HP.v2.w, HP.v3.x, HP.v3.y, HP.v3.z, HP.v3.w};
 #pragma unroll
         for (int ks = 0; ks < 2; ks++) {
             const h8v bfr = *(const h8v *)bsrc[ks];
 #pragma unroll
             for (int nt = 0; nt < 8; nt++) {
                 const uint32_t x = vd[nt];
-                const h8v afr = frag8(ks ? ((x >> 2) & MSK) : (x & MSK));
+                const h8v afr = FOUR ? frag8_b4(vd[8 * ks + nt]) : frag8(ks ? ((x >> 2) & MSK) : (x & MSK));
                 acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(afr, bfr, acc[nt], 0, 0, 0);
             }
         }
@@ -1253,6 +1283,15 @@ void stage1_head_mfma_kernel(KParams P, const uint16_t *__restrict__ q, Workspac
         const uint8_t *pg = base + (size_t)__builtin_amdgcn_readlane(pid_l, min(i, np - 1)) * pstride;
         HeadPage HP;
         HP.R = load_page_masked(pg, i < np, G, lane);
+        if (FOUR) {
+            const __amdgpu_buffer_rsrc_t rs = page_rsrc(pg, i < np, G);
+            HP.k2 = bload(rs, G.kc + 2048 + 16 * lane);
+            HP.k3 = bload(rs, G.kc + 3072 + 16 * lane);
+            HP.v2 = bload(rs, G.vc + 2048 + 16 * lane);
+            HP.v3 = bload(rs, G.vc + 3072 + 16 * lane);
+        } else {
+            HP.k2 = HP.k3 = HP.v2 = HP.v3 = make_uint4(0u, 0u, 0u, 0u);
+        }
 #pragma unroll
         for (int qp = 0; qp < 2; qp++) {
             const bool on = qp < planes;
@@ -1574,11 +1613,13 @@ hipError_t launch_decode(const KParams &P, const uint16_t *q, float *out, float 
                 stage1_valu_kernel<false><<<g1, 64, 0, s>>>(P, q, W, qscale);
         } else {
             if (P.scheme == KVQ_SCHEME_KITTY_DYN)
-                stage1_head_mfma_kernel<true, true><<<g1, 64, 0, s>>>(P, q, W, qscale);
+                stage1_head_mfma_kernel<true, true, false><<<g1, 64, 0, s>>>(P, q, W, qscale);
             else if (kitty)
-                stage1_head_mfma_kernel<true, false><<<g1, 64, 0, s>>>(P, q, W, qscale);
+                stage1_head_mfma_kernel<true, false, false><<<g1, 64, 0, s>>>(P, q, W, qscale);
+            else if (P.scheme == KVQ_SCHEME_KIVI4)
+                stage1_head_mfma_kernel<false, false, true><<<g1, 64, 0, s>>>(P, q, W, qscale);
             else
-                stage1_head_mfma_kernel<false, false><<<g1, 64, 0, s>>>(P, q, W, qscale);
+                stage1_head_mfma_kernel<false, false, false><<<g1, 64, 0, s>>>(P, q, W, qscale);
         }
     }
     hipError_t e = hipGetLastError();

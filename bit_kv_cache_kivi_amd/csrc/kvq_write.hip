@@ -74,7 +74,8 @@ __device__ void quant_key_page(const KParams &P, const Geom &G, const uint16_t *
     if (P.scheme == KVQ_SCHEME_KITTY_DYN) select_page_boost(G, src, page, inv, bits4, P.nb);
     const int c = tid & 127;
     const int gi = tid >> 7;                         // group 0 or 1 of the page
-    const float lmax = bits4[c] ? 15.0f : 3.0f;
+    const bool four = P.scheme == KVQ_SCHEME_KIVI4;
+    const float lmax = (four || bits4[c]) ? 15.0f : 3.0f;
     float xs[32];
     float mn = 0.f, mx = 0.f;
 #pragma unroll
@@ -90,21 +91,32 @@ __device__ void quant_key_page(const KParams &P, const Geom &G, const uint16_t *
     ks[128 * gi + key_stat_slot(c)] = (uint32_t)ap.s16 | ((uint32_t)ap.z16 << 16);
     __syncthreads();
     uint32_t *kc = (uint32_t *)(page + G.kc);
-    for (int w = tid; w < 512; w += 256) {
-        int d = 4 * (w >> 8) + (w & 3);
-        int L = (w >> 2) & 63;
-        int g = L >> 4, r = L & 15;
-        int t = 16 * (d >> 1) + r;
-        int kcb = 2 * (d & 1);
-        uint32_t val = 0;
+    if (four) {                                      // 1024 dwords (see key_code_pos4)
+        for (int w = tid; w < 1024; w += 256) {
+            const int n = w >> 8, L = (w >> 2) & 63, kq = w & 3;
+            const int t = 16 * n + (L & 15), c0 = 32 * kq + 8 * (L >> 4);
+            uint32_t val = 0;
 #pragma unroll
-        for (int hh = 0; hh < 2; hh++)
+            for (int k = 0; k < 8; k++) val |= (uint32_t)codes[t][c0 + k] << (8 * (k & 3) + 4 * (k >> 2));
+            kc[w] = val;
+        }
+    } else {
+        for (int w = tid; w < 512; w += 256) {
+            int d = 4 * (w >> 8) + (w & 3);
+            int L = (w >> 2) & 63;
+            int g = L >> 4, r = L & 15;
+            int t = 16 * (d >> 1) + r;
+            int kcb = 2 * (d & 1);
+            uint32_t val = 0;
 #pragma unroll
-            for (int j = 0; j < 8; j++) {
-                int cc = 32 * (kcb + hh) + 8 * g + j;
-                val |= (uint32_t)(codes[t][cc] & 3) << (4 * j + 2 * hh);
-            }
-        kc[w] = val;
+            for (int hh = 0; hh < 2; hh++)
+#pragma unroll
+                for (int j = 0; j < 8; j++) {
+                    int cc = 32 * (kcb + hh) + 8 * g + j;
+                    val |= (uint32_t)(codes[t][cc] & 3) << (4 * j + 2 * hh);
+                }
+            kc[w] = val;
+        }
     }
     if (is_kitty(P.scheme) && tid < 4 * P.nb) {
         // high plane q = tid >> 6 (offsets 16q ..): dword tid (see high_code_pos)
@@ -143,7 +155,7 @@ __device__ void load_boost(const KParams &P, int h, int *inv, uint8_t *bits4) {
 }
 
 // ---------------------------------------------------------------------------
-// append (KIVI2 / KITTY): one wave per (KV head, request)
+// append (KIVI2 / KITTY / KIVI4): one wave per (KV head, request)
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(64) void append_kivi_kernel(KParams P, const uint16_t *__restrict__ kn,
                                                          const uint16_t *__restrict__ vn) {
@@ -192,16 +204,20 @@ __global__ __launch_bounds__(64) void append_kivi_kernel(KParams P, const uint16
             mn = fminf(mn, shfl_xor(mn, m));
             mx = fmaxf(mx, shfl_xor(mx, m));
         }
-        const AsymParams ap = asym_params(mn, mx, 3.0f);
-        const uint32_t code[2] = {asym_code(x0, ap, 3.0f), asym_code(x1, ap, 3.0f)};
+        const bool four = P.scheme == KVQ_SCHEME_KIVI4;
+        const float lmax = four ? 15.0f : 3.0f;
+        const AsymParams ap = asym_params(mn, mx, lmax);
+        const uint32_t code[2] = {asym_code(x0, ap, lmax), asym_code(x1, ap, lmax)};
         const int tp = t % PT;
         uint32_t *vc = (uint32_t *)(page + G.vc);
+        const uint32_t cm = four ? 15u : 3u;
 #pragma unroll
         for (int e = 0; e < 2; e++) {
             int dw, sh;
-            value_code_pos(tp, 2 * lane + e, dw, sh);
+            if (four) value_code_pos4(tp, 2 * lane + e, dw, sh);
+            else value_code_pos(tp, 2 * lane + e, dw, sh);
             uint32_t w = vc[dw];
-            w = (w & ~(3u << sh)) | (code[e] << sh);
+            w = (w & ~(cm << sh)) | (code[e] << sh);
             vc[dw] = w;
         }
         if ((lane & 15) == 0) {
@@ -215,7 +231,7 @@ __global__ __launch_bounds__(64) void append_kivi_kernel(KParams P, const uint16
 }
 
 // ---------------------------------------------------------------------------
-// flush (KIVI2 / KITTY): 256 threads per (KV head, request)
+// flush (KIVI2 / KITTY / KIVI4): 256 threads per (KV head, request)
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void flush_kivi_kernel(KParams P) {
     const int h = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
@@ -249,7 +265,7 @@ __global__ __launch_bounds__(256) void flush_kivi_kernel(KParams P) {
 }
 
 // ---------------------------------------------------------------------------
-// prefill (KIVI2 / KITTY): one 256-thread block per (page, KV head, request)
+// prefill (KIVI2 / KITTY / KIVI4): one 256-thread block per (page, KV head, request)
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void prefill_kivi_kernel(KParams P, int req0,
                                                           const uint16_t *__restrict__ K,
@@ -318,6 +334,8 @@ __global__ __launch_bounds__(256) void prefill_kivi_kernel(KParams P, int req0,
         // values, per token, groups of 32 channels: thread (token tl, group jv)
         const int tl = tid >> 2, jv = tid & 3;
         const int t = t0 + tl;
+        const bool four = P.scheme == KVQ_SCHEME_KIVI4;
+        const float lmax = four ? 15.0f : 3.0f;
         if (t < nvq) {
             float xs[32];
             float mn = 0.f, mx = 0.f;
@@ -327,9 +345,9 @@ __global__ __launch_bounds__(256) void prefill_kivi_kernel(KParams P, int req0,
                 if (i == 0) { mn = xs[0]; mx = xs[0]; }
                 else { mn = fminf(mn, xs[i]); mx = fmaxf(mx, xs[i]); }
             }
-            AsymParams ap = asym_params(mn, mx, 3.0f);
+            AsymParams ap = asym_params(mn, mx, lmax);
 #pragma unroll
-            for (int i = 0; i < 32; i++) codes[tl][32 * jv + i] = (uint8_t)asym_code(xs[i], ap, 3.0f);
+            for (int i = 0; i < 32; i++) codes[tl][32 * jv + i] = (uint8_t)asym_code(xs[i], ap, lmax);
             ((uint32_t *)(page + G.vs))[tl * 4 + jv] = (uint32_t)ap.s16 | ((uint32_t)ap.z16 << 16);
         } else {
 #pragma unroll
@@ -337,18 +355,29 @@ __global__ __launch_bounds__(256) void prefill_kivi_kernel(KParams P, int req0,
         }
         __syncthreads();
         uint32_t *vc = (uint32_t *)(page + G.vc);
-        for (int w = tid; w < 512; w += 256) {
-            const int nt = 4 * (w >> 8) + (w & 3);
-            const int L = (w >> 2) & 63;
-            const int g = L >> 4, r = L & 15;
-            const int c = 16 * nt + r;
-            uint32_t val = 0;
+        if (four) {                                  // 1024 dwords (see value_code_pos4)
+            for (int w = tid; w < 1024; w += 256) {
+                const int d = 4 * (w >> 8) + (w & 3), L = (w >> 2) & 63;
+                const int c = 16 * (d & 7) + (L & 15), tb = 32 * (d >> 3) + 8 * (L >> 4);
+                uint32_t val = 0;
 #pragma unroll
-            for (int ks = 0; ks < 2; ks++)
+                for (int k = 0; k < 8; k++) val |= (uint32_t)codes[tb + k][c] << (8 * (k & 3) + 4 * (k >> 2));
+                vc[w] = val;
+            }
+        } else {
+            for (int w = tid; w < 512; w += 256) {
+                const int nt = 4 * (w >> 8) + (w & 3);
+                const int L = (w >> 2) & 63;
+                const int g = L >> 4, r = L & 15;
+                const int c = 16 * nt + r;
+                uint32_t val = 0;
 #pragma unroll
-                for (int j = 0; j < 8; j++)
-                    val |= (uint32_t)codes[32 * ks + 8 * g + j][c] << (4 * j + 2 * ks);
-            vc[w] = val;
+                for (int ks = 0; ks < 2; ks++)
+#pragma unroll
+                    for (int j = 0; j < 8; j++)
+                        val |= (uint32_t)codes[32 * ks + 8 * g + j][c] << (4 * j + 2 * ks);
+                vc[w] = val;
+            }
         }
     }
 }

@@ -40,7 +40,7 @@ _CTX_K, _CTX_V, _STEP_Q, _STEP_K, _STEP_V, _OUTLIERS, _LENGTHS, _PAGES, _QDEC = 
 class Workload:
     wid: int
     name: str
-    scheme: str            # "kivi2" | "kitty" | "witcert" | "kitty_dyn"
+    scheme: str            # "kivi2" | "kitty" | "witcert" | "kitty_dyn" | "kivi4"
     B: int
     Hq: int
     Hkv: int
@@ -106,6 +106,10 @@ def workload(wid: int, **over) -> Workload:
         w = dict(wid=7, name="kivi2-sink32-gqa-b64-32q8kv-ctx8k-32k-paged", scheme="kivi2", B=64,
                  Hq=32, Hkv=8, ctx=_lengths3(64, 8192, 32768, 3), n_outliers=4,
                  outlier_factor=15.0, sink=32, steps=1, seed=7)
+    elif wid == 9:
+        # KIVI-4: workload 4's shapes with 4-bit keys and values, no boosting
+        w = dict(wid=9, name="kivi4-mha-b16-h32-ctx32768", scheme="kivi4", B=16, Hq=32,
+                 Hkv=32, ctx=(32768,) * 16, n_outliers=4, outlier_factor=15.0, steps=1, seed=9)
     else:
         raise ValueError(wid)
     w.update(over)

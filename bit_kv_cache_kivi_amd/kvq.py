@@ -18,9 +18,10 @@ import numpy as np
 PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG, "libkvq.so")
 
-KVQ_SCHEME_KIVI2, KVQ_SCHEME_KITTY, KVQ_SCHEME_WITCERT, KVQ_SCHEME_KITTY_DYN = 0, 1, 2, 3
+KVQ_SCHEME_KIVI2, KVQ_SCHEME_KITTY, KVQ_SCHEME_WITCERT, KVQ_SCHEME_KITTY_DYN, KVQ_SCHEME_KIVI4 = \
+    0, 1, 2, 3, 4
 SCHEMES = {"kivi2": KVQ_SCHEME_KIVI2, "kitty": KVQ_SCHEME_KITTY, "witcert": KVQ_SCHEME_WITCERT,
-           "kitty_dyn": KVQ_SCHEME_KITTY_DYN}
+           "kitty_dyn": KVQ_SCHEME_KITTY_DYN, "kivi4": KVQ_SCHEME_KIVI4}
 
 KVQ_OK, KVQ_EINVAL, KVQ_ENULL, KVQ_EALIGN, KVQ_ENOLAYOUT, KVQ_EWORKSPACE, KVQ_ELAUNCH = \
     0, -1, -2, -3, -4, -5, -6

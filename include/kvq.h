@@ -27,6 +27,10 @@
  *                      Mechanism, importance as the mean absolute value of a
  *                      group; a group here is one page.)  No calibration and
  *                      no boost_idx buffer.
+ *   KVQ_SCHEME_KIVI4   KIVI2's groups, statistics and windows at 4 bits for
+ *                      keys and values (16 levels per group; "KIVI"
+ *                      explainer, its 2- and 4-bit variants): 160 B per
+ *                      token and KV head.
  *   KVQ_SCHEME_WITCERT INT8 keys and values with subtractive dither:
  *                      x_hat = s (round(x/s + xi) - xi), s = amax/126.5 per
  *                      (256-token block, channel) stored fp16 and used for
@@ -70,7 +74,8 @@ enum {
     KVQ_SCHEME_KIVI2 = 0,
     KVQ_SCHEME_KITTY = 1,
     KVQ_SCHEME_WITCERT = 2,
-    KVQ_SCHEME_KITTY_DYN = 3
+    KVQ_SCHEME_KITTY_DYN = 3,
+    KVQ_SCHEME_KIVI4 = 4
 };
 
 /* layout flags */
@@ -177,11 +182,12 @@ typedef struct kvq_cache {
  *   [1, 65535]; max_pages or n_pages < 1; split_pages outside [0, 64] (0 picks
  *   a default), or max_pages needs more than 256 splits of the resolved size
  *   (at most 64 pages); flags other than KVQ_FLAG_*; unknown scheme;
- *   KIVI2 / KITTY / KITTY_DYN: group or value_group != 32; residual not a
+ *   KIVI2 / KITTY / KITTY_DYN / KIVI4: group or value_group != 32; residual not a
  *   multiple of 64 or outside [64, 256] (the residual is quantized in whole
  *   key groups, so it must be divisible by the group, "KIVI" explainer 3.3,
  *   and the flush fills whole 64-token pages); n_boost != 16 for KITTY and
- *   KITTY_DYN or != 0 for KIVI2; KVQ_FLAG_GENERIC_STAGE1 with KITTY_DYN;
+ *   KITTY_DYN or != 0 for KIVI2 and KIVI4; KVQ_FLAG_GENERIC_STAGE1 with
+ *   KITTY_DYN or KIVI4;
  *   sink outside [0, 64] or non-zero for WITCERT; reserved != 0;
  *   WITCERT: block != 256; layer >= 65536; query heads per KV head not in
  *   {1, 2, 4, 8}. */

@@ -7,7 +7,7 @@ import numpy as np
 from bit_kv_cache_kivi_amd import inputs
 from layout_unpack import PT, WPT, gather_kivi, page_block, witcert_block
 
-SCHEME_ID = {"kivi2": 0, "kitty": 1, "witcert": 2, "kitty_dyn": 3}
+SCHEME_ID = {"kivi2": 0, "kitty": 1, "witcert": 2, "kitty_dyn": 3, "kivi4": 4}
 
 
 class Case:

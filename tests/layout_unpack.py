@@ -13,7 +13,9 @@ WPT = 256
 def geom(scheme: int, nb: int = 16) -> dict:
     """Block layout: KIVI-2 (0), Kitty (1, nb boosted channels: one 256-B high
     plane per 16), WitCert (2), Kitty dynamic (3: Kitty + the page's nb
-    channel ids, at least 16 bytes)."""
+    channel ids, at least 16 bytes), KIVI-4 (4: 4-bit key and value codes)."""
+    if scheme == 4:
+        return dict(kc=0, kh=0, ks=4096, vc=5120, vs=9216, bytes=10240, tokens=PT)
     if scheme == 0:
         return dict(kc=0, kh=0, ks=2048, vc=3072, vs=5120, bytes=6144, tokens=PT)
     if scheme == 2:
@@ -26,7 +28,7 @@ def geom(scheme: int, nb: int = 16) -> dict:
     return g
 
 
-GEOM = {s: geom(s) for s in range(4)}
+GEOM = {s: geom(s) for s in range(5)}
 KITTY_SCHEMES = (1, 3)
 
 
@@ -52,6 +54,30 @@ def _value_index():
     return dword, shift
 
 
+def _nibble_shift(k):
+    """4-bit code k (0..7) of a KIVI-4 dword: byte k % 4, nibble k // 4."""
+    return 8 * (k & 3) + 4 * (k >> 2)
+
+
+def _key_index4():
+    """KIVI-4 keys: token t, channel c -> dword 256 (t // 16) + 4 lane +
+    c // 32 with lane = 16 ((c // 8) % 4) + t % 16; code c % 8 of the dword."""
+    t = np.arange(PT)[:, None]
+    c = np.arange(D)[None, :]
+    lane = 16 * ((c >> 3) & 3) + (t & 15)
+    return 256 * (t >> 4) + 4 * lane + (c >> 5), _nibble_shift(c & 7)
+
+
+def _value_index4():
+    """KIVI-4 values: dword d = 8 (t // 32) + c // 16 of lane 16 ((t // 8) % 4)
+    + c % 16 at 256 (d // 4) + 4 lane + d % 4; code t % 8 of the dword."""
+    t = np.arange(PT)[:, None]
+    c = np.arange(D)[None, :]
+    lane = 16 * ((t >> 3) & 3) + (c & 15)
+    d = 8 * (t >> 5) + (c >> 4)
+    return 256 * (d >> 2) + 4 * lane + (d & 3), _nibble_shift(t & 7)
+
+
 def _high_index(nb=16):
     t = np.arange(PT)[:, None]
     o = np.arange(nb)[None, :]
@@ -64,6 +90,8 @@ def _high_index(nb=16):
 KEY_DW, KEY_SH = _key_index()
 VAL_DW, VAL_SH = _value_index()
 HI_DW, HI_SH = _high_index()
+KEY4_DW, KEY4_SH = _key_index4()
+VAL4_DW, VAL4_SH = _value_index4()
 KEY_SLOT = np.arange(D)            # key statistics in channel order
 
 
@@ -72,8 +100,10 @@ def _u32(block: np.ndarray, off: int, n: int) -> np.ndarray:
 
 
 def key_codes(block: np.ndarray, scheme: int) -> np.ndarray:
-    """Low 2-bit key codes [64][128]."""
+    """Low 2-bit key codes [64][128] (KIVI-4: the 4-bit codes)."""
     g = geom(scheme)
+    if scheme == 4:
+        return ((_u32(block, g["kc"], 1024)[KEY4_DW] >> KEY4_SH) & 15).astype(np.uint8)
     kc = _u32(block, g["kc"], 512)
     return ((kc[KEY_DW] >> KEY_SH) & 3).astype(np.uint8)
 
@@ -105,6 +135,8 @@ def page_boost_index(block: np.ndarray, nb: int = 16) -> np.ndarray:
 
 def value_codes(block: np.ndarray, scheme: int, nb: int = 16) -> np.ndarray:
     g = geom(scheme, nb)
+    if scheme == 4:
+        return ((_u32(block, g["vc"], 1024)[VAL4_DW] >> VAL4_SH) & 15).astype(np.uint8)
     vc = _u32(block, g["vc"], 512)
     return ((vc[VAL_DW] >> VAL_SH) & 3).astype(np.uint8)
 

@@ -59,14 +59,14 @@ def set_layout(K, L, B=None):
     return rc, cache
 
 
-@pytest.mark.parametrize("scheme", ["kivi2", "kitty", "witcert", "kitty_dyn"])
+@pytest.mark.parametrize("scheme", ["kivi2", "kitty", "witcert", "kitty_dyn", "kivi4"])
 def test_valid_layouts(K, scheme):
     L = K.make_layout(scheme, B=64, Hq=32, Hkv=8, max_pages=512, n_pages=32768)
     rc, cache = set_layout(K, L)
     assert rc == K.KVQ_OK
     assert cache.page_tokens == (256 if scheme == "witcert" else 64)
     assert cache.page_bytes == {"kivi2": 6144, "kitty": 6400, "witcert": 66048,
-                                "kitty_dyn": 6416}[scheme]
+                                "kitty_dyn": 6416, "kivi4": 10240}[scheme]
 
 
 def test_page_geometry_and_bytes_per_token(K):
@@ -74,10 +74,11 @@ def test_page_geometry_and_bytes_per_token(K):
     # values), 100 with Kitty's 16-channel high plane, 258 for the INT8 block
     # scheme (128 codes + an fp16 scale per 256-token block and channel, twice);
     # Kitty dynamic adds the page's 16 boosted channel ids (0.25 B/token)
-    # Kitty-Pro (32 boosted channels): one more 256-B high plane, 104 B/token
+    # Kitty-Pro (32 boosted channels): one more 256-B high plane, 104 B/token;
+    # KIVI-4: 64 + 64 B of codes and the same 32 B of statistics, 160 B/token
     for scheme, nb, bpt in (("kivi2", None, 96.0), ("kitty", None, 100.0), ("witcert", None, 258.0),
                             ("kitty_dyn", None, 100.25), ("kitty", 32, 104.0),
-                            ("kitty_dyn", 32, 104.5)):
+                            ("kitty_dyn", 32, 104.5), ("kivi4", None, 160.0)):
         L = K.make_layout(scheme, B=1, Hq=1, Hkv=1, max_pages=1, n_pages=1, nb=nb)
         assert K.bytes_per_token(L) == bpt
         assert K.page_bytes(L) == bpt * K.page_tokens(L)
@@ -89,7 +90,7 @@ def test_page_geometry_and_bytes_per_token(K):
 INVALID = [
     ("head_dim", 64), ("n_kv_heads", 0), ("n_kv_heads", 65536), ("n_q_heads", 12),
     ("n_q_heads", 72), ("batch", 0), ("batch", 65536), ("max_pages", 0), ("n_pages", 0),
-    ("split_pages", -1), ("split_pages", 65), ("flags", 2), ("scheme", 4), ("scheme", -1),
+    ("split_pages", -1), ("split_pages", 65), ("flags", 2), ("scheme", 5), ("scheme", -1),
     ("group", 64), ("value_group", 16), ("residual", 96), ("residual", 100),
     ("residual", 0), ("residual", 320), ("n_boost", 4),
 ]
@@ -141,6 +142,22 @@ def test_kitty_and_witcert_fields(K):
     assert set_layout(K, L)[0] == K.KVQ_EINVAL
     L = K.make_layout("kivi2", B=1, Hq=24, Hkv=8, max_pages=8, n_pages=8)      # fine for KIVI-2
     assert set_layout(K, L)[0] == K.KVQ_OK
+
+
+def test_kivi4_fields(K):
+    # KIVI-4 shares KIVI-2's groups and windows, has no boosted channels, and
+    # its 4-bit codes have no VALU stage 1
+    L = K.make_layout("kivi4", B=1, Hq=24, Hkv=8, max_pages=8, n_pages=8, sink=16)
+    assert set_layout(K, L)[0] == K.KVQ_OK
+    for nb in (16, 32):
+        L = K.make_layout("kivi4", B=1, Hq=4, Hkv=4, max_pages=8, n_pages=8, nb=nb)
+        assert set_layout(K, L)[0] == K.KVQ_EINVAL
+    L = K.make_layout("kivi4", B=1, Hq=4, Hkv=4, max_pages=8, n_pages=8, flags=K.FLAG_GENERIC_STAGE1)
+    assert set_layout(K, L)[0] == K.KVQ_EINVAL
+    for field, value in (("group", 64), ("value_group", 16), ("residual", 96)):
+        L = K.make_layout("kivi4", B=1, Hq=4, Hkv=4, max_pages=8, n_pages=8)
+        setattr(L, field, value)
+        assert set_layout(K, L)[0] == K.KVQ_EINVAL
 
 
 def test_null_and_alignment(K):

@@ -89,6 +89,10 @@ def test_kitty_pro_b16_h32_ctx32768():
     _run(inputs.workload(8))
 
 
+def test_kivi4_b16_h32_ctx32768():
+    _run(inputs.workload(9))
+
+
 def test_gqa_sink32_b64_ctx8k_32k():
     _run(inputs.workload(7))
 

@@ -117,11 +117,11 @@ def test_kitty_calibrate_store_decode(flags):
     case.check_store()
 
 
-@pytest.mark.parametrize("wid,Hq,Hkv", [(2, 2, 2), (3, 8, 2), (4, 2, 2), (6, 4, 1)])
+@pytest.mark.parametrize("wid,Hq,Hkv", [(2, 2, 2), (3, 8, 2), (4, 2, 2), (6, 4, 1), (9, 8, 2)])
 def test_sink_tokens_store_decode(wid, Hq, Hkv):
     # the first 32 tokens stay fp16: bit-exact store (sink buffers included)
     # and decode through prefill and two flushes, for KIVI-2 (one query head
-    # per wave and the group-of-4 kernel) and both Kitty schemes
+    # per wave and the group-of-4 kernel), both Kitty schemes and KIVI-4
     w = inputs.workload(wid, B=2, Hq=Hq, Hkv=Hkv, ctx=(700, 1129))
     case = _case(w, extra_tokens=300, split_pages=3, sink=32)
     case.check_state()
@@ -184,6 +184,43 @@ def test_kitty_pro_dynamic_with_sink():
     _check_decode(case, out, cert, q)
     for i in range(140):
         out, cert, q = case.step(decode=(i % 64 == 63 or i == 0))
+        if out is not None:
+            _check_decode(case, out, cert, q)
+    case.check_status()
+    case.check_store()
+
+
+@pytest.mark.parametrize("Hq,Hkv,split", [(2, 2, 3), (8, 2, 2), (6, 3, 1), (4, 4, 64)])
+def test_kivi4_store_decode(Hq, Hkv, split):
+    # 4-bit keys and values: bit-exact codes and statistics through prefill,
+    # two flushes and per-token value quantization; decode to the tolerance
+    # (one query head per wave for every group size)
+    w = inputs.workload(9, B=3, Hq=Hq, Hkv=Hkv, ctx=(700, 1301, 2113))
+    case = _case(w, extra_tokens=300, split_pages=split)
+    case.check_state()
+    case.check_store()
+    out, cert, q = case.decode_now(1)
+    _check_decode(case, out, cert, q)
+    for i in range(260):
+        out, cert, q = case.step(decode=(i % 64 == 63 or i in (0, 1, 127, 128)))
+        if out is not None:
+            _check_decode(case, out, cert, q)
+    case.check_status()
+    case.check_state()
+    case.check_store()
+
+
+@pytest.mark.parametrize("ctx", [(1,), (63,), (128,), (129,), (192,), (193,), (300,)])
+def test_kivi4_short_contexts(ctx):
+    # contexts inside the fp16 windows, at their edges and past the first flush
+    w = inputs.workload(9, B=1, Hq=2, Hkv=1, ctx=ctx)
+    case = _case(w, extra_tokens=200, split_pages=1)
+    case.check_state()
+    case.check_store()
+    out, cert, q = case.decode_now(3)
+    _check_decode(case, out, cert, q)
+    for i in range(70):
+        out, cert, q = case.step(decode=(i % 9 == 8 or i in (0, 1)))
         if out is not None:
             _check_decode(case, out, cert, q)
     case.check_status()
