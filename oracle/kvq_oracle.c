@@ -29,13 +29,16 @@
  *           dither, s = amax/126.5 stored fp16 and reused, Philox4x32-10
  *           five-tuple), "Key structure" paragraph (certificate A and the
  *           split LSE merge), the quantised-path certificate paragraph
- *           (varsigma^2 formula).
+ *           (varsigma^2 formula), and the certified-deployment paragraphs
+ *           (per-token scales over groups of G_c channels, the slot-keyed
+ *           Philox tuple, the fixed outlier RoPE-pair bypass left out of
+ *           the group amax).
  *   Philox4x32-10: Salmon, Moraes, Dror, Shaw, "Parallel random numbers:
  *           as easy as 1, 2, 3" (SC'11), the reference WitCert cites for
  *           its dither generator.
  *
- * Where the pages are silent the readings taken here are listed in the
- * design notes of the repository and repeated at each function below.
+ * Where the pages are silent, the reading taken is stated at the function
+ * that takes it.
  */
 #include <math.h>
 #include <stdint.h>
@@ -189,6 +192,24 @@ float ko_dither(uint64_t seed, int side, uint32_t req, uint32_t layer,
     return (float)(u >> 8) * 0x1p-24f - 0.5f;
 }
 
+/* Paging-safe WitCert dither ([WITCERT] certified deployment: the counter
+ * is keyed by the cache slot, which paging, prefix sharing and retraction
+ * never change, instead of the sequence position).  Reading: the tuple
+ * (layer, KV head, slot, channel) fills the same counter words, the slot's
+ * low and high halves taking the places of token and request:
+ *   counter = (slot_lo, channel >> 2, (layer << 16) | kv_head, slot_hi),
+ * key, output word and xi as in ko_dither. */
+float ko_dither_slot(uint64_t seed, int side, uint32_t layer, uint32_t kvh,
+                     uint64_t slot, uint32_t ch)
+{
+    uint32_t ctr[4] = { (uint32_t)slot, ch >> 2, (layer << 16) | kvh, (uint32_t)(slot >> 32) };
+    uint32_t key[2] = { (uint32_t)seed, (uint32_t)(seed >> 32) ^ (uint32_t)side };
+    uint32_t out[4];
+    ko_philox4x32_10(ctr, key, out);
+    uint32_t u = out[ch & 3];
+    return (float)(u >> 8) * 0x1p-24f - 0.5f;
+}
+
 /* ------------------------------------------------------------------------ */
 /* WitCert INT8 subtractive-dither block quantizer for one channel of one   */
 /* block of n tokens.  [WITCERT] write kernel: x_hat = s (round(x/s + xi)  */
@@ -232,6 +253,42 @@ float ko_witcert_dequant(int code, uint16_t s16, float xi)
 {
     float t = (float)code - xi;
     return ko_f16_to_f32(s16) * t;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Outlier RoPE-pair selection for the paging-safe WitCert storage.         */
+/* [WITCERT] certified deployment: a fixed set of m RoPE pairs per (layer,  */
+/* KV head), chosen from the leading part of a sequence, is stored fp16.    */
+/* Readings: pair i is channels (i, i + D/2) (the rotate-half RoPE layout); */
+/* its importance is max over the calibration tokens of x_i^2 + x_{i+D/2}^2 */
+/* (the pair's squared norm, which the rotation keeps), each square exact   */
+/* in binary32 and the sum rounded once; the m largest are taken, ties to   */
+/* the lower pair.  mask[c] = 1 for both channels of a chosen pair.         */
+/* ------------------------------------------------------------------------ */
+
+void ko_witcert_select_pairs(const uint16_t *k, long T, int D, int m, uint8_t *mask)
+{
+    int H = D / 2;
+    float imp[128];
+    for (int i = 0; i < H; i++) {
+        imp[i] = 0.0f;
+        for (long t = 0; t < T; t++) {
+            float a = ko_f16_to_f32(k[t * D + i]);
+            float b = ko_f16_to_f32(k[t * D + i + H]);
+            float e = a * a + b * b;
+            if (e > imp[i]) imp[i] = e;
+        }
+    }
+    for (int c = 0; c < D; c++) mask[c] = 0;
+    for (int r = 0; r < m && r < H; r++) {
+        int best = -1;
+        for (int i = 0; i < H; i++) {
+            if (mask[i]) continue;
+            if (best < 0 || imp[i] > imp[best]) best = i;
+        }
+        mask[best] = 1;
+        mask[best + H] = 1;
+    }
 }
 
 /* ------------------------------------------------------------------------ */
@@ -310,7 +367,13 @@ void ko_kitty_select_dyn(const uint16_t *k, long T, long ld, int D, int nb, uint
 
 /* KO_KIVI4: the KIVI scheme at 4 bits for keys and values ([KIVI] reports
  * its quantizer at 2 and 4 bits; the same groups, statistics and windows). */
-enum { KO_KIVI = 0, KO_KITTY = 1, KO_WITCERT = 2, KO_KITTY_DYN = 3, KO_KIVI4 = 4 };
+/* KO_WITCERT_TOK: the paging-safe WitCert storage ([WITCERT] certified
+ * deployment): every token is quantized when it is written, keys and values
+ * alike, with one scale per (token, group of VG channels), the dither keyed
+ * by the token's cache slot, and a fixed set of key channels (outlier RoPE
+ * pairs) kept fp16 and left out of their group's amax. */
+enum { KO_KIVI = 0, KO_KITTY = 1, KO_WITCERT = 2, KO_KITTY_DYN = 3, KO_KIVI4 = 4,
+       KO_WITCERT_TOK = 5 };
 
 typedef struct ko_stream {
     int scheme, D, G, R, VG, BLK, nb, bits_v;
@@ -327,12 +390,16 @@ typedef struct ko_stream {
     long sel;                /* Kitty dynamic: tokens per selection unit */
     long sink;               /* leading tokens kept fp16 for keys and values */
     uint8_t *uidx;           /* Kitty dynamic: [cap/sel + 1][D] boost index per unit */
+    uint64_t *slot;          /* KO_WITCERT_TOK: cache slot of each token [cap] */
+    uint8_t byp[256];        /* KO_WITCERT_TOK: 1 = key channel stored fp16 */
     uint64_t seed;
     uint32_t req, layer, kvh;
 } ko_stream;
 
 /* sel: tokens per selection unit for KO_KITTY_DYN (a multiple of G that
  * divides R, so a flush always quantizes whole units); ignored otherwise.
+ * KO_WITCERT_TOK: idx[c] != 0 marks a bypassed key channel (NULL: none);
+ * VG is the scale group; token t sits in slot t until ko_stream_set_slots.
  * sink: the first `sink` tokens of the stream stay fp16, keys and values
  * ([KITTY] sink tokens; KIVI2 / Kitty only); groups, selection units and the
  * value FIFO then start at token `sink`. */
@@ -341,10 +408,12 @@ ko_stream *ko_stream_new(int scheme, int D, int G, int R, int VG, int BLK,
                          uint64_t seed, uint32_t req, uint32_t layer, uint32_t kvh, long sel,
                          long sink)
 {
-    if (sink < 0 || (sink > 0 && scheme == KO_WITCERT)) return NULL;
+    if (sink < 0 || (sink > 0 && (scheme == KO_WITCERT || scheme == KO_WITCERT_TOK))) return NULL;
     if (D <= 0 || D > 256 || cap <= 0) return NULL;
-    if (scheme < KO_KIVI || scheme > KO_KIVI4) return NULL;
-    if (scheme != KO_WITCERT) {
+    if (scheme < KO_KIVI || scheme > KO_WITCERT_TOK) return NULL;
+    if (scheme == KO_WITCERT_TOK) {
+        if (VG <= 0 || D % VG != 0) return NULL;
+    } else if (scheme != KO_WITCERT) {
         if (G <= 0 || R <= 0 || R % G != 0 || VG <= 0 || D % VG != 0) return NULL;
         if (nb < 0 || nb > D) return NULL;
     } else if (BLK <= 0) {
@@ -367,9 +436,15 @@ ko_stream *ko_stream_new(int scheme, int D, int G, int R, int VG, int BLK,
     s->Kc = (uint8_t *)calloc((size_t)(cap * D), 1);
     s->Vc = (uint8_t *)calloc((size_t)(cap * D), 1);
     long ngk = (scheme == KO_WITCERT) ? cap / BLK + 1 : cap / G + 1;
+    if (scheme == KO_WITCERT_TOK) ngk = cap * (D / VG) / D + 1;
     s->Ks = (uint16_t *)calloc((size_t)(ngk * D), 2);
     s->Kz = (uint16_t *)calloc((size_t)(ngk * D), 2);
     long nvs = (scheme == KO_WITCERT) ? (cap / BLK + 1) * D : cap * (D / VG);
+    if (scheme == KO_WITCERT_TOK) {
+        s->slot = (uint64_t *)calloc((size_t)cap, sizeof(uint64_t));
+        for (long t = 0; t < cap; t++) s->slot[t] = (uint64_t)t;
+        for (int c = 0; c < D; c++) s->byp[c] = (idx && idx[c]) ? 1 : 0;
+    }
     s->Vs = (uint16_t *)calloc((size_t)nvs, 2);
     s->Vz = (uint16_t *)calloc((size_t)nvs, 2);
     for (int c = 0; c < D; c++)
@@ -377,12 +452,21 @@ ko_stream *ko_stream_new(int scheme, int D, int G, int R, int VG, int BLK,
     return s;
 }
 
+/* KO_WITCERT_TOK: cache slot of every token (cap values), before any token
+ * is written.  Returns 0, or -1 for another scheme or a stream in use. */
+int ko_stream_set_slots(ko_stream *s, const uint64_t *slots)
+{
+    if (s->scheme != KO_WITCERT_TOK || s->l != 0) return -1;
+    memcpy(s->slot, slots, sizeof(uint64_t) * (size_t)s->cap);
+    return 0;
+}
+
 void ko_stream_free(ko_stream *s)
 {
     if (!s) return;
     free(s->Kraw); free(s->Vraw); free(s->Kc); free(s->Vc);
     free(s->Ks); free(s->Kz); free(s->Vs); free(s->Vz);
-    free(s->uidx);
+    free(s->uidx); free(s->slot);
     free(s);
 }
 
@@ -454,11 +538,47 @@ static void quant_witcert_block(ko_stream *s, long b)
     free(xi);
 }
 
+/* KO_WITCERT_TOK: token t is quantized as it is written, per group of VG
+ * channels on each side ([WITCERT] certified deployment: the scale depends
+ * on the current token only).  Each group is the block quantizer above over
+ * its non-bypassed channels (bypassed key channels are left out of the amax
+ * and get code 0; they are read back fp16), with the dither of the token's
+ * slot. */
+static void quant_witcert_token(ko_stream *s, long t)
+{
+    int ng = s->D / s->VG;
+    uint16_t x[256];
+    float xi[256];
+    int8_t cd[256];
+    int ch[256];
+    for (int side = 0; side < 2; side++) {
+        const uint16_t *raw = (side ? s->Vraw : s->Kraw) + t * s->D;
+        uint8_t *codes = (side ? s->Vc : s->Kc) + t * s->D;
+        uint16_t *sc = (side ? s->Vs : s->Ks) + t * ng;
+        for (int g = 0; g < ng; g++) {
+            int n = 0;
+            for (int c = g * s->VG; c < (g + 1) * s->VG; c++) {
+                codes[c] = 0;
+                if (side == 0 && s->byp[c]) continue;
+                ch[n] = c;
+                x[n] = raw[c];
+                xi[n] = ko_dither_slot(s->seed, side, s->layer, s->kvh, s->slot[t], (uint32_t)c);
+                n++;
+            }
+            uint16_t s16 = 0;
+            if (n > 0) ko_witcert_quant(x, n, 1, xi, &s16, cd, 1);
+            for (int i = 0; i < n; i++) codes[ch[i]] = (uint8_t)cd[i];
+            sc[g] = s16;
+        }
+    }
+}
+
 /* Flush: KIVI/Kitty quantize the key residual when it holds R tokens;
  * WitCert quantizes the active block when it holds BLK tokens.
  * Returns 1 when something was quantized, 0 otherwise. */
 int ko_stream_flush(ko_stream *s)
 {
+    if (s->scheme == KO_WITCERT_TOK) return 0;      /* nothing waits: tokens are quantized on write */
     if (s->scheme == KO_WITCERT) {
         if (s->l - s->n_kq != s->BLK) return 0;
         quant_witcert_block(s, s->n_kq / s->BLK);
@@ -479,9 +599,16 @@ int ko_stream_flush(ko_stream *s)
 int ko_stream_append(ko_stream *s, const uint16_t *k, const uint16_t *v)
 {
     long lim = (s->scheme == KO_WITCERT) ? s->BLK : s->R;
-    if (s->l - s->n_kq >= lim || s->l >= s->cap) return -1;
+    if (s->scheme != KO_WITCERT_TOK && s->l - s->n_kq >= lim) return -1;
+    if (s->l >= s->cap) return -1;
     memcpy(&s->Kraw[s->l * s->D], k, 2 * (size_t)s->D);
     memcpy(&s->Vraw[s->l * s->D], v, 2 * (size_t)s->D);
+    if (s->scheme == KO_WITCERT_TOK) {
+        quant_witcert_token(s, s->l);
+        s->l += 1;
+        s->n_kq = s->n_vq = s->l;
+        return 0;
+    }
     if (s->l < s->sink) {
         /* a sink token: kept fp16, never in the residual or the FIFO */
         s->l += 1;
@@ -508,6 +635,11 @@ int ko_stream_prefill(ko_stream *s, const uint16_t *K, const uint16_t *V, long l
     memcpy(s->Vraw, V, 2 * (size_t)(l0 * s->D));
     s->l = l0;
     if (l0 == 0) return 0;
+    if (s->scheme == KO_WITCERT_TOK) {
+        for (long t = 0; t < l0; t++) quant_witcert_token(s, t);
+        s->n_kq = s->n_vq = l0;
+        return 0;
+    }
     if (s->scheme == KO_WITCERT) {
         long r = ((l0 - 1) % s->BLK) + 1;
         s->n_kq = l0 - r;
@@ -552,6 +684,11 @@ static float key_tilde(const ko_stream *s, long t, int c)
 {
     if (t < s->sink || t >= s->n_kq)
         return ko_f16_to_f32(s->Kraw[t * s->D + c]);
+    if (s->scheme == KO_WITCERT_TOK) {
+        if (s->byp[c]) return ko_f16_to_f32(s->Kraw[t * s->D + c]);
+        float xi = ko_dither_slot(s->seed, 0, s->layer, s->kvh, s->slot[t], (uint32_t)c);
+        return ko_witcert_dequant((int8_t)s->Kc[t * s->D + c], s->Ks[t * (s->D / s->VG) + c / s->VG], xi);
+    }
     if (s->scheme == KO_WITCERT) {
         long b = t / s->BLK;
         float xi = ko_dither(s->seed, 0, s->req, s->layer, s->kvh, (uint32_t)t, (uint32_t)c);
@@ -565,6 +702,10 @@ static float value_tilde(const ko_stream *s, long t, int c)
 {
     if (t < s->sink || t >= s->n_vq)
         return ko_f16_to_f32(s->Vraw[t * s->D + c]);
+    if (s->scheme == KO_WITCERT_TOK) {
+        float xi = ko_dither_slot(s->seed, 1, s->layer, s->kvh, s->slot[t], (uint32_t)c);
+        return ko_witcert_dequant((int8_t)s->Vc[t * s->D + c], s->Vs[t * (s->D / s->VG) + c / s->VG], xi);
+    }
     if (s->scheme == KO_WITCERT) {
         long b = t / s->BLK;
         float xi = ko_dither(s->seed, 1, s->req, s->layer, s->kvh, (uint32_t)t, (uint32_t)c);
@@ -592,6 +733,8 @@ void ko_stream_dequant(const ko_stream *s, long t0, long t1, float *Kt, float *V
 /*   varsigma^2_{h,b} = (sm_scale^2 / 12) sum_c q_{h,c}^2 s_{c,b}^2 (key     */
 /*   scales of block b), u_t = kappa * sqrt(varsigma^2) for quantized keys,  */
 /*   u_t = 0 for fp16 keys, A_h = sum_t p_t exp(u_t).                        */
+/* KO_WITCERT_TOK: s_{c,t} is the scale of channel c's group at token t, and */
+/* 0 for a bypassed (fp16) key channel, which carries no quantization error. */
 /* Reading: kappa is a caller-supplied multiplier of the standard deviation. */
 /* ------------------------------------------------------------------------ */
 
@@ -620,12 +763,16 @@ void ko_stream_attend_range(const ko_stream *s, const uint16_t *q, int nq,
             if (z[i] > m) m = z[i];
             u[i] = 0.0;
             long t = t0 + i;
-            if (s->scheme == KO_WITCERT && t < s->n_kq) {
+            if ((s->scheme == KO_WITCERT || s->scheme == KO_WITCERT_TOK) && t < s->n_kq) {
                 long b = t / s->BLK;
                 double v2 = 0.0;
                 for (int c = 0; c < D; c++) {
                     double qc = ko_f16_to_f32(qh[c]);
-                    double sc = ko_f16_to_f32(s->Ks[b * D + c]);
+                    double sc;
+                    if (s->scheme == KO_WITCERT)
+                        sc = ko_f16_to_f32(s->Ks[b * D + c]);
+                    else
+                        sc = s->byp[c] ? 0.0 : ko_f16_to_f32(s->Ks[t * (D / s->VG) + c / s->VG]);
                     v2 += qc * qc * sc * sc;
                 }
                 v2 *= (double)sm_scale * (double)sm_scale / 12.0;

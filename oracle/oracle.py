@@ -19,7 +19,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 SRC = os.path.join(HERE, "kvq_oracle.c")
 LIB = os.path.join(HERE, "_build", "libkvq_oracle.so")
 
-KIVI, KITTY, WITCERT, KITTY_DYN, KIVI4 = 0, 1, 2, 3, 4
+KIVI, KITTY, WITCERT, KITTY_DYN, KIVI4, WITCERT_TOK = 0, 1, 2, 3, 4, 5
 
 GCC_FLAGS = ["-std=c11", "-O2", "-fPIC", "-shared", "-ffp-contract=off",
              "-fno-fast-math", "-fno-finite-math-only"]
@@ -56,6 +56,11 @@ def lib():
         L.ko_dither.argtypes = [C.c_uint64, C.c_int, C.c_uint32, C.c_uint32,
                                 C.c_uint32, C.c_uint32, C.c_uint32]
         L.ko_dither.restype = C.c_float
+        L.ko_dither_slot.argtypes = [C.c_uint64, C.c_int, C.c_uint32, C.c_uint32,
+                                     C.c_uint64, C.c_uint32]
+        L.ko_dither_slot.restype = C.c_float
+        L.ko_witcert_select_pairs.argtypes = [P, C.c_long, C.c_int, C.c_int, P]
+        L.ko_stream_set_slots.argtypes = [P, P]
         L.ko_witcert_quant.argtypes = [P, C.c_long, C.c_long, P, P, P, C.c_long]
         L.ko_witcert_dequant.argtypes = [C.c_int, C.c_uint16, C.c_float]
         L.ko_witcert_dequant.restype = C.c_float
@@ -129,6 +134,20 @@ def dither(seed: int, side: int, req: int, layer: int, kvh: int, token: int, ch:
     return lib().ko_dither(seed, side, req, layer, kvh, token, ch)
 
 
+def dither_slot(seed: int, side: int, layer: int, kvh: int, slot: int, ch: int) -> float:
+    return lib().ko_dither_slot(seed, side, layer, kvh, slot, ch)
+
+
+def witcert_select_pairs(k: np.ndarray, m: int) -> np.ndarray:
+    """Bypass mask [D] (1 for both channels of the m chosen RoPE pairs) from a
+    calibration slice k [T][D] (fp16 bits)."""
+    k = np.ascontiguousarray(k, dtype=np.uint16)
+    T, D = k.shape
+    mask = np.zeros(D, np.uint8)
+    lib().ko_witcert_select_pairs(_p(k), T, D, m, _p(mask))
+    return mask
+
+
 def witcert_quant(x: np.ndarray, xi: np.ndarray):
     """Quantize one channel-block (fp16 bits) with dither xi.  Returns (s16, int8 codes)."""
     x = np.ascontiguousarray(x, dtype=np.uint16)
@@ -172,7 +191,9 @@ class Stream:
     def __init__(self, scheme: int, cap: int, D: int = 128, G: int = 32, R: int = 128,
                  VG: int = 32, BLK: int = 256, nb: int = 0, idx=None,
                  seed: int = 0, req: int = 0, layer: int = 0, kvh: int = 0, sel: int = 64,
-                 sink: int = 0):
+                 sink: int = 0, slots=None):
+        """WITCERT_TOK: idx = bypass mask [D] (or None), VG = scale group,
+        slots = cache slot of every token [cap] (default: slot t for token t)."""
         self.scheme, self.cap, self.D, self.G, self.R = scheme, cap, D, G, R
         self.VG, self.BLK, self.nb, self.sel, self.sink = VG, BLK, nb, sel, sink
         self._idx = None if idx is None else np.ascontiguousarray(idx, np.uint8)
@@ -182,6 +203,11 @@ class Stream:
         if not h:
             raise ValueError("invalid stream parameters")
         self.h = h
+        if slots is not None:
+            self._slots = np.ascontiguousarray(slots, np.uint64)
+            assert self._slots.shape == (cap,)
+            if lib().ko_stream_set_slots(h, _p(self._slots)) != 0:
+                raise ValueError("slots rejected")
 
     def __del__(self):
         h = getattr(self, "h", None)
@@ -227,8 +253,13 @@ class Stream:
         return self._arr("ko_stream_uidx", n * self.D, np.uint8).reshape(n, self.D)
 
     def key_stats(self):
-        """(scale, zero) fp16 bits: [groups][D] (WitCert: [blocks][D], zero unused);
-        groups count from the first token after the sink."""
+        """(scale, zero) fp16 bits: [groups][D] (WitCert: [blocks][D], zero unused;
+        WITCERT_TOK: scales [cap][D/VG]); groups count from the first token after
+        the sink."""
+        if self.scheme == WITCERT_TOK:
+            ng = self.D // self.VG
+            s = self._arr("ko_stream_kscale", self.cap * ng, np.uint16).reshape(self.cap, ng)
+            return s, np.zeros_like(s)
         n = (self.cap // (self.BLK if self.scheme == WITCERT else self.G)) + 1
         s = self._arr("ko_stream_kscale", n * self.D, np.uint16).reshape(n, self.D)
         z = self._arr("ko_stream_kzero", n * self.D, np.uint16).reshape(n, self.D)
@@ -243,6 +274,8 @@ class Stream:
             return s, z
         ng = self.D // self.VG
         s = self._arr("ko_stream_vscale", self.cap * ng, np.uint16).reshape(self.cap, ng)
+        if self.scheme == WITCERT_TOK:
+            return s, np.zeros_like(s)
         z = self._arr("ko_stream_vzero", self.cap * ng, np.uint16).reshape(self.cap, ng)
         return s, z
 
