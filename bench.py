@@ -91,6 +91,15 @@ def kivi_bytes(l: int, n_kq: int, R: int, qpk: int, scheme: str, sink: int = 0,
     return dict(stage1=paged + window, decode=paged + window + qo + table)
 
 
+def witcert_paged_bytes(l: int, qpk: int, nb: int) -> dict:
+    """Every token quantized: 136 B per side (int8 codes + four fp16 group
+    scales) + 16 B of bypassed key values when there are bypassed pairs."""
+    paged = l * (272 + (16 if nb > 0 else 0))
+    qo = qpk * (256 + 512 + 4)
+    table = ((l + 63) // 64) * 4
+    return dict(stage1=paged, decode=paged + qo + table)
+
+
 def witcert_bytes(l: int, n_q: int, qpk: int) -> dict:
     paged = n_q * 258
     window = (l - n_q) * 512
@@ -101,6 +110,8 @@ def witcert_bytes(l: int, n_q: int, qpk: int) -> dict:
 
 def write_bytes(w: inputs.Workload, l_before: int, n_kq_before: int) -> int:
     """Append (+ value pack) and flush-if-due bytes of one (request, KV head)."""
+    if w.scheme == "witcert_paged":    # new k, v in; the token's record out
+        return 512 + 272 + (16 if w.nb > 0 else 0)
     b = 512 + 512                      # new k, v in; fp16 windows out
     if w.scheme == "witcert":
         if l_before - n_kq_before == w.BLK:
@@ -116,6 +127,8 @@ def write_bytes(w: inputs.Workload, l_before: int, n_kq_before: int) -> int:
 
 
 def state_after_prefill(w: inputs.Workload, l0: int):
+    if w.scheme == "witcert_paged":
+        return l0, l0
     W = w.BLK if w.scheme == "witcert" else w.R
     if l0 <= w.sink:
         return l0, l0
@@ -125,6 +138,8 @@ def state_after_prefill(w: inputs.Workload, l0: int):
 
 
 def step_state(w: inputs.Workload, l: int, n_kq: int):
+    if w.scheme == "witcert_paged":
+        return l + 1, l + 1
     W = w.BLK if w.scheme == "witcert" else w.R
     if l < w.sink:
         return l + 1, l + 1
@@ -144,6 +159,8 @@ def step_bytes(w: inputs.Workload, states):
         l2, k2 = step_state(w, l, n_kq)
         if w.scheme == "witcert":
             d = witcert_bytes(l2, k2, w.group)
+        elif w.scheme == "witcert_paged":
+            d = witcert_paged_bytes(l2, w.group, w.nb)
         else:
             d = kivi_bytes(l2, k2, w.R, w.group, w.scheme, w.sink, w.nb or 16)
         tot += w.Hkv * (wb + d["decode"])
@@ -173,11 +190,15 @@ def setup_gpu(w: inputs.Workload, extra: int, split_pages: int):
     table = inputs.page_permutation(w, n_pages).reshape(w.B, max_pages)
     layout = kvq.make_layout(w.scheme, w.B, w.Hq, w.Hkv, max_pages, n_pages, R=w.R,
                              seed=0x5EED_0000_0000_0000 | w.seed, split_pages=split_pages,
-                             sink=w.sink, nb=w.nb if w.nb else None)
+                             sink=w.sink, nb=w.nb if (w.nb or w.scheme == "witcert_paged") else None)
     cache = kvq.KVCache(layout, table)
-    if w.scheme == "kitty":
+    if w.scheme == "kitty" or (w.scheme == "witcert_paged" and w.nb > 0):
         calib = np.stack([inputs.kitty_calibration(w, h) for h in range(w.Hkv)])
-        cache.kitty_calibrate(torch.from_numpy(calib.view(np.float16)).cuda())
+        ct = torch.from_numpy(calib.view(np.float16)).cuda()
+        if w.scheme == "kitty":
+            cache.kitty_calibrate(ct)
+        else:
+            cache.witcert_calibrate(ct)
     threads = min(16, os.cpu_count() or 1)
     t0 = time.time()
     with cf.ThreadPoolExecutor(threads) as ex:
@@ -219,7 +240,7 @@ def run_gpu(w: inputs.Workload, steps: int, warmup: int, split_pages: int, copie
     stream = torch.cuda.current_stream()
     ev1 = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
            for _ in range(steps)]
-    kappa = 1.0 if w.scheme == "witcert" else 0.0
+    kappa = 1.0 if w.scheme in ("witcert", "witcert_paged") else 0.0
     for a, b in ev1:            # torch creates the HIP event at its first record
         a.record()
         b.record()
@@ -265,12 +286,14 @@ def cpu_baseline(w: inputs.Workload, warmup: int, target_s: float = 15.0, thread
                  n_pairs: int = 0):
     from oracle import oracle as O
     sid = {"kivi2": O.KIVI, "kitty": O.KITTY, "witcert": O.WITCERT, "kitty_dyn": O.KITTY_DYN,
-           "kivi4": O.KIVI4}[w.scheme]
+           "kivi4": O.KIVI4, "witcert_paged": O.WITCERT_TOK}[w.scheme]
     if threads <= 0:
         threads = max(1, min(16, len(os.sched_getaffinity(0))))
     idx = None
     if w.scheme == "kitty":
         idx = [O.kitty_select(inputs.kitty_calibration(w, h), w.nb) for h in range(w.Hkv)]
+    if w.scheme == "witcert_paged" and w.nb > 0:     # bypass masks (slots: token index)
+        idx = [O.witcert_select_pairs(inputs.kitty_calibration(w, h), w.nb) for h in range(w.Hkv)]
     pairs = [(b, b % w.Hkv) for b in range(n_pairs if n_pairs > 0 else w.B)]
     seed = 0x5EED_0000_0000_0000 | w.seed
 
@@ -288,7 +311,7 @@ def cpu_baseline(w: inputs.Workload, warmup: int, target_s: float = 15.0, thread
         s.flush()
         s.append(k[b, h], v[b, h])
         s.decode(q[b, h * w.group:(h + 1) * w.group], w.sm_scale,
-                 1.0 if w.scheme == "witcert" else 0.0)
+                 1.0 if w.scheme in ("witcert", "witcert_paged") else 0.0)
 
     # rounds of one flush/append/decode step on every sampled pair, until the
     # timed work reaches about target_s (bounded by max_rounds)
@@ -309,6 +332,7 @@ def cpu_baseline(w: inputs.Workload, warmup: int, target_s: float = 15.0, thread
                 wb = write_bytes(w, l, n_kq)
                 l2, k2 = step_state(w, l, n_kq)
                 d = (witcert_bytes(l2, k2, w.group) if w.scheme == "witcert"
+                     else witcert_paged_bytes(l2, w.group, w.nb) if w.scheme == "witcert_paged"
                      else kivi_bytes(l2, k2, w.R, w.group, w.scheme, w.sink, w.nb or 16))
                 done_bytes += wb + d["decode"]
                 states[i] = (l2, k2)
@@ -386,8 +410,13 @@ def main():
     s1_calls = []
     for i in range(args.warmup, args.warmup + args.steps):
         states = cstates[i % copies]
-        s1_calls.append(sum(w.Hkv * 2 * (n_kq // w.BLK) * w.BLK * (w.D // 4) for (_, n_kq) in
-                            [step_state(w, l, k) for (l, k) in states]) if w.scheme == "witcert" else 0)
+        nxt = [step_state(w, l, k) for (l, k) in states]
+        if w.scheme == "witcert":        # tokens of the quantized blocks x quads x sides
+            s1_calls.append(sum(w.Hkv * 2 * (n_kq // w.BLK) * w.BLK * (w.D // 4) for (_, n_kq) in nxt))
+        elif w.scheme == "witcert_paged":   # every token
+            s1_calls.append(sum(w.Hkv * 2 * l * (w.D // 4) for (l, _) in nxt))
+        else:
+            s1_calls.append(0)
         b, s1, cstates[i % copies] = step_bytes(w, states)
         tot += b
         s1_bytes.append(s1)
@@ -396,8 +425,9 @@ def main():
     s1_avg_ms = float(np.mean(s1_ms))
     s1_gbs = float(np.mean(s1_bytes)) / (s1_avg_ms * 1e-3) / 1e9
     kernel = ("stage1_witcert" if w.scheme == "witcert" else
+              "stage1_witcert_paged" if w.scheme == "witcert_paged" else
               "stage1_gqa4_mfma" if (w.scheme == "kivi2" and w.group == 4) else "stage1_head_mfma")
-    if w.scheme == "witcert":
+    if w.scheme in ("witcert", "witcert_paged"):
         # VALU bound: Philox4x32-10 calls (one per token, channel quad and
         # side of every quantized block) x the algorithmic VALU operations per
         # call, against 256 CUs x 64 lanes x 2.4 GHz of full-rate VALU ops
@@ -425,7 +455,8 @@ def main():
     rec = {"metric": METRIC, "value": round(gbs, 1), "unit": "GB/s", "n_gpus": 1,
            "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
            "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-           "dtype": {"witcert": "i8+f32", "kivi4": "u4+f32"}.get(w.scheme, "u2+f32"), "data": "synthetic",
+           "dtype": {"witcert": "i8+f32", "witcert_paged": "i8+f32", "kivi4": "u4+f32"}.get(w.scheme, "u2+f32"),
+           "data": "synthetic",
            "config": {"workload": w.name, "batch": w.B, "q_heads": w.Hq, "kv_heads": w.Hkv,
                       "head_dim": w.D, "ctx_mean": float(np.mean(w.ctx)),
                       "ctx_min": int(min(w.ctx)), "ctx_max": int(max(w.ctx)),

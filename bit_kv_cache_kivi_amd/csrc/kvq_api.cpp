@@ -27,7 +27,8 @@ int validate_layout(const kvq_layout_t *L) {
     if (L->reserved != 0) return KVQ_EINVAL;
     // sink tokens: one stage-1 chunk of at most 64 fp16 tokens (KIVI2 / Kitty)
     if (L->sink < 0 || L->sink > kvq::PT) return KVQ_EINVAL;
-    if (L->sink > 0 && L->scheme == KVQ_SCHEME_WITCERT) return KVQ_EINVAL;
+    if (L->sink > 0 && (L->scheme == KVQ_SCHEME_WITCERT || L->scheme == KVQ_SCHEME_WITCERT_PAGED))
+        return KVQ_EINVAL;
     switch (L->scheme) {
         case KVQ_SCHEME_KIVI2:
         case KVQ_SCHEME_KITTY:
@@ -48,6 +49,15 @@ int validate_layout(const kvq_layout_t *L) {
             // the VALU stage 1 reads the head's static boost table only
             if (L->scheme == KVQ_SCHEME_KITTY_DYN && (L->flags & KVQ_FLAG_GENERIC_STAGE1))
                 return KVQ_EINVAL;
+            break;
+        case KVQ_SCHEME_WITCERT_PAGED:
+            // scales per (token, 32-channel group); at most 4 bypassed pairs
+            // (an 8-entry fp16 row per token)
+            if (L->group != 32 || L->value_group != 32) return KVQ_EINVAL;
+            if (L->n_boost < 0 || L->n_boost > 4) return KVQ_EINVAL;
+            if (L->flags != 0) return KVQ_EINVAL;
+            if (L->layer >= 65536u) return KVQ_EINVAL;
+            if (qpk != 1 && qpk != 2 && qpk != 4 && qpk != 8) return KVQ_EINVAL;
             break;
         case KVQ_SCHEME_WITCERT:
             if (L->block != kvq::WPT) return KVQ_EINVAL;
@@ -73,7 +83,7 @@ kvq::KParams params(const kvq_cache_t *C) {
     P.sink_k = C->bufs.sink_k;
     P.sink_v = C->bufs.sink_v;
     P.sink = L.sink;
-    P.nb = kvq::is_kitty(L.scheme) ? L.n_boost : 0;
+    P.nb = (kvq::is_kitty(L.scheme) || L.scheme == KVQ_SCHEME_WITCERT_PAGED) ? L.n_boost : 0;
     P.B = L.batch;
     P.Hq = L.n_q_heads;
     P.Hkv = L.n_kv_heads;
@@ -102,6 +112,7 @@ int max_splits(const kvq_cache_t *C) {
 
 // 64-token chunks of the fp16 window, each a stage-1 partial of its own
 int n_win(const kvq_cache_t *C) {
+    if (C->layout.scheme == KVQ_SCHEME_WITCERT_PAGED) return 0;   // no fp16 tail
     return C->layout.scheme == KVQ_SCHEME_WITCERT ? kvq::WPT / kvq::PT
                                                   : C->layout.residual / kvq::PT + (C->layout.sink > 0 ? 1 : 0);
 }
@@ -112,13 +123,13 @@ extern "C" {
 
 int64_t kvq_page_bytes(const kvq_layout_t *L) {
     if (!L) return 0;
-    if (L->scheme < KVQ_SCHEME_KIVI2 || L->scheme > KVQ_SCHEME_KIVI4) return 0;
+    if (L->scheme < KVQ_SCHEME_KIVI2 || L->scheme > KVQ_SCHEME_WITCERT_PAGED) return 0;
     return kvq::geom(L->scheme, L->n_boost).bytes;
 }
 
 int32_t kvq_page_tokens(const kvq_layout_t *L) {
     if (!L) return 0;
-    if (L->scheme < KVQ_SCHEME_KIVI2 || L->scheme > KVQ_SCHEME_KIVI4) return 0;
+    if (L->scheme < KVQ_SCHEME_KIVI2 || L->scheme > KVQ_SCHEME_WITCERT_PAGED) return 0;
     return kvq::geom(L->scheme, L->n_boost).tokens;
 }
 
@@ -131,15 +142,17 @@ int kvq_set_layout(kvq_cache_t *cache, const kvq_layout_t *layout, const kvq_buf
     if (!cache || !layout || !bufs) return KVQ_ENULL;
     int rc = validate_layout(layout);
     if (rc != KVQ_OK) return rc;
-    if (!bufs->pool || !bufs->page_table || !bufs->state || !bufs->res_k || !bufs->res_v ||
-        !bufs->status)
-        return KVQ_ENULL;
+    const bool wtok = layout->scheme == KVQ_SCHEME_WITCERT_PAGED;   // no residual buffers
+    if (!bufs->pool || !bufs->page_table || !bufs->state || !bufs->status) return KVQ_ENULL;
+    if (!wtok && (!bufs->res_k || !bufs->res_v)) return KVQ_ENULL;
     if (layout->scheme == KVQ_SCHEME_KITTY && !bufs->boost_idx) return KVQ_ENULL;
+    if (wtok && layout->n_boost > 0 && !bufs->boost_idx) return KVQ_ENULL;
     if (layout->sink > 0 && (!bufs->sink_k || !bufs->sink_v)) return KVQ_ENULL;
     if ((bufs->sink_k && !aligned(bufs->sink_k, 16)) || (bufs->sink_v && !aligned(bufs->sink_v, 16)))
         return KVQ_EALIGN;
     if (!aligned(bufs->pool, 256) || !aligned(bufs->page_table, 16) || !aligned(bufs->state, 16) ||
-        !aligned(bufs->res_k, 16) || !aligned(bufs->res_v, 16) || !aligned(bufs->status, 4))
+        (bufs->res_k && !aligned(bufs->res_k, 16)) || (bufs->res_v && !aligned(bufs->res_v, 16)) ||
+        !aligned(bufs->status, 4))
         return KVQ_EALIGN;
     memset(cache, 0, sizeof(*cache));
     cache->layout = *layout;
@@ -152,7 +165,9 @@ int kvq_set_layout(kvq_cache_t *cache, const kvq_layout_t *layout, const kvq_buf
         // default: one 256-token block per split for WITCERT; 8 pages for
         // short caches, 12 for longer ones (fewer partials to merge, enough
         // splits to fill the chip), at least what keeps <= 256 splits
-        sp = layout->scheme == KVQ_SCHEME_WITCERT ? 1 : (layout->max_pages <= 128 ? 8 : 12);
+        sp = layout->scheme == KVQ_SCHEME_WITCERT ? 1
+             : wtok                                 ? 4      // 256 tokens, as one WITCERT block
+             : (layout->max_pages <= 128 ? 8 : 12);
         sp = std::max(sp, (layout->max_pages + 255) / 256);
     }
     // the merge takes at most 256 splits per query head
@@ -232,6 +247,20 @@ int kvq_kitty_calibrate(const kvq_cache_t *cache, const uint16_t *calib, int32_t
     if (!calib || !idx_out) return KVQ_ENULL;
     if (n_tokens < 1) return KVQ_EINVAL;
     return kvq::launch_kitty_calibrate(params(cache), calib, n_tokens, idx_out, stream) == hipSuccess
+               ? KVQ_OK
+               : KVQ_ELAUNCH;
+}
+
+int kvq_witcert_calibrate(const kvq_cache_t *cache, const uint16_t *calib, int32_t n_tokens,
+                          uint8_t *idx_out, hipStream_t stream) {
+    int rc = check_cache(cache);
+    if (rc != KVQ_OK) return rc;
+    if (cache->layout.scheme != KVQ_SCHEME_WITCERT_PAGED || cache->layout.n_boost < 1)
+        return KVQ_EINVAL;
+    if (!calib || !idx_out) return KVQ_ENULL;
+    if (n_tokens < 1) return KVQ_EINVAL;
+    return kvq::launch_witcert_calibrate(params(cache), calib, n_tokens, idx_out, stream) ==
+                   hipSuccess
                ? KVQ_OK
                : KVQ_ELAUNCH;
 }

@@ -32,6 +32,12 @@ constexpr int NB_MAX = 32;      // Kitty-Pro: alpha = 1/4
 // KIVI4, 64 tokens:
 //   KC 4096 B 4-bit key codes (see key_code_pos4), KS 1024 B as KIVI2,
 //   VC 4096 B 4-bit value codes (see value_code_pos4), VS 1024 B as KIVI2
+// WITCERT_PAGED, 64 tokens, every token quantized on write:
+//   KC 8192 B int8 [64][128];  VC 8192 B int8 [64][128];
+//   KS 512 B fp16 [64][4] key scales per (token, 32-channel group);
+//   VS 512 B fp16 [64][4] value scales;
+//   KH 1024 B fp16 [64][8] (nb > 0): the token's bypassed key channels, by
+//   offset (ascending channel order), the rest of the row unused
 // WITCERT, 256 tokens (one block):
 //   KC 32768 B int8 [256][128];  KS 256 B fp16 [128];
 //   VC 32768 B int8 [256][128];  VS 256 B fp16 [128]
@@ -56,6 +62,11 @@ __host__ __device__ inline Geom geom(int scheme, int nb = NB) {
             g.ki = g.bytes;
             g.bytes += nb > 16 ? nb : 16;
         }
+        g.tokens = PT;
+    } else if (scheme == KVQ_SCHEME_WITCERT_PAGED) {
+        // nb = bypassed RoPE pairs; KH holds the fp16 bypass row of each token
+        g.kc = 0; g.vc = 8192; g.ks = 16384; g.vs = 16896; g.kh = 17408;
+        g.bytes = 17408 + (nb > 0 ? 1024 : 0);
         g.tokens = PT;
     } else if (scheme == KVQ_SCHEME_KIVI4) {
         g.kc = 0; g.kh = 0; g.ks = 4096; g.vc = 5120; g.vs = 9216; g.bytes = 10240;

@@ -1501,6 +1501,197 @@ __global__ __launch_bounds__(64) void stage1_witcert_kernel(KParams P, const uin
     }
 }
 
+// ---------------------------------------------------------------------------
+// Stage 1, WITCERT_PAGED: every token of the split is quantized (no fp16
+// tail); one wave per (split, KV head, request) serves the QPK query heads,
+// lane = (channel quad cq, token phase tp) as in the block kernel, with the
+// dither counter keyed by the token's slot (page_id * 64 + position) and one
+// scale per (token, 32-channel group).  Per page, lane t first stages token
+// t's key and value scales in LDS and computes e^{u_t} for the QPK queries:
+// u_t = kappa sqrt((sm^2/12) sum_g s_{t,g}^2 Q_g) with Q_g the query's sum of
+// q_c^2 over the group's quantized channels (a bypassed channel carries no
+// error).  Bypassed key channels: their q is zeroed in the lane's operand and
+// lane cq < 2 nb adds q_c x_c for the bypass row's entry cq instead.
+// ---------------------------------------------------------------------------
+struct WtokSmem {
+    uint2 ks[PT], vs[PT];           // the page's key / value scales per token (4 fp16)
+    float eu[PT][8];                // e^{u_t} per token and query head
+    int inv[8];                     // bypass row entry -> channel
+};
+
+template <int QPK>
+__global__ __launch_bounds__(64) void stage1_witcert_paged_kernel(KParams P, const uint16_t *__restrict__ q,
+                                                                  Workspace W, float qscale, float sm_scale,
+                                                                  float kappa) {
+    const int s = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+    const int lane = threadIdx.x, cq = lane & 31, tp = lane >> 5;
+    const Geom G = geom(P.scheme, P.nb);
+    const size_t bh = (size_t)b * P.Hkv + h;
+    const int l = P.state[bh * 4];
+    const int npages = (l + PT - 1) / PT;
+    const int p0 = s * P.split_pages;
+    const int p1 = min(p0 + P.split_pages, npages);
+    if (p0 >= p1) return;
+    __shared__ WtokSmem sm;
+    const int nbyp = 2 * P.nb;                   // bypassed key channels
+
+    // bypass flags of this lane's channels and the channel of row entry cq
+    bool byp[4] = {false, false, false, false};
+    if (nbyp > 0) {
+        const uint32_t ow = *(const uint32_t *)(P.boost_idx + (size_t)h * D + 4 * cq);
+#pragma unroll
+        for (int e = 0; e < 4; e++) {
+            const int o = (int)((ow >> (8 * e)) & 0xffu);
+            byp[e] = o < nbyp;
+            if (byp[e] && tp == 0) sm.inv[o] = 4 * cq + e;
+        }
+    }
+    lds_sync();
+    const bool bslot = cq < nbyp;                // this lane adds bypass entry cq
+    const int bch = bslot ? sm.inv[cq] : 0;
+
+    float qv[QPK][4], qb[QPK], Qg[QPK][4];
+#pragma unroll
+    for (int hh = 0; hh < QPK; hh++) {
+        const uint16_t *qh = q + ((size_t)b * P.Hq + h * QPK + hh) * D;
+        const uint2 raw = *(const uint2 *)(qh + 4 * cq);
+        const float qq[4] = {h2f((uint16_t)(raw.x & 0xffff)), h2f((uint16_t)(raw.x >> 16)),
+                             h2f((uint16_t)(raw.y & 0xffff)), h2f((uint16_t)(raw.y >> 16))};
+        float q2 = 0.f;
+#pragma unroll
+        for (int e = 0; e < 4; e++) {
+            qv[hh][e] = byp[e] ? 0.f : qq[e];
+            q2 = fmaf(qv[hh][e], qv[hh][e], q2);
+        }
+        qb[hh] = bslot ? h2f(qh[bch]) : 0.f;
+        // Q_g: the 8 lanes of group g = cq >> 3 hold its channels
+#pragma unroll
+        for (int msk = 1; msk < 8; msk <<= 1) q2 += shfl_xor(q2, msk);
+#pragma unroll
+        for (int g = 0; g < 4; g++)
+            Qg[hh][g] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, q2), 8 * g));
+    }
+    float m[QPK], lp[QPK], ap[QPK], o[QPK][4];
+#pragma unroll
+    for (int hh = 0; hh < QPK; hh++) {
+        m[hh] = -INFINITY; lp[hh] = 0.f; ap[hh] = 0.f;
+        o[hh][0] = o[hh][1] = o[hh][2] = o[hh][3] = 0.f;
+    }
+    const uint32_t k0 = (uint32_t)P.seed;
+    const uint32_t k1 = (uint32_t)(P.seed >> 32);
+    const uint32_t c2 = (P.layer << 16) | (uint32_t)h;
+    const float LOG2E = 1.4426950408889634f;
+    const float cc = sm_scale * sm_scale * (1.0f / 12.0f);
+    const int gq = cq >> 3;                      // this lane's scale group
+
+    for (int p = p0; p < p1; p++) {
+        int pid = P.table[(size_t)b * P.max_pages + p];
+        if (pid < 0 || pid >= P.n_pages) {
+            if (lane == 0) atomicOr(P.status, (uint32_t)KVQ_STATUS_UNMAPPED_PAGE);
+            pid = 0;                              // read page 0 instead; the result is flagged
+        }
+        const uint8_t *page = cpage(P, pid, h);
+        const int nvalid = min(PT, l - p * PT);
+        lds_sync();                               // the previous page's LDS reads are done
+        {
+            // lane = token: scales and e^{u_t}
+            const bool ok = lane < nvalid;
+            const uint2 ksr = ok ? *(const uint2 *)(page + G.ks + 8 * lane) : make_uint2(0u, 0u);
+            const uint2 vsr = ok ? *(const uint2 *)(page + G.vs + 8 * lane) : make_uint2(0u, 0u);
+            sm.ks[lane] = ksr;
+            sm.vs[lane] = vsr;
+            const float sg[4] = {h2f((uint16_t)(ksr.x & 0xffff)), h2f((uint16_t)(ksr.x >> 16)),
+                                 h2f((uint16_t)(ksr.y & 0xffff)), h2f((uint16_t)(ksr.y >> 16))};
+#pragma unroll
+            for (int hh = 0; hh < QPK; hh++) {
+                float v2 = 0.f;
+#pragma unroll
+                for (int g = 0; g < 4; g++) v2 = fmaf(sg[g] * sg[g], Qg[hh][g], v2);
+                sm.eu[lane][hh] = exp2f(kappa * sqrtf(v2 * cc) * LOG2E);
+            }
+        }
+        lds_sync();
+        const int8_t *kcod = (const int8_t *)(page + G.kc);
+        const int8_t *vcod = (const int8_t *)(page + G.vc);
+        const uint16_t *kbr = (const uint16_t *)(page + G.kh);
+        const uint64_t slot0 = (uint64_t)pid * PT;
+        for (int i = 0; 2 * i < nvalid; i++) {
+            const int t = 2 * i + tp;
+            const bool valid = t < nvalid;        // the page's last token may be odd
+            const uint64_t slot = slot0 + (uint64_t)t;
+            const U4 uk = philox4x32_10(U4{(uint32_t)slot, (uint32_t)cq, c2, (uint32_t)(slot >> 32)}, k0, k1);
+            const U4 uv = philox4x32_10(U4{(uint32_t)slot, (uint32_t)cq, c2, (uint32_t)(slot >> 32)}, k0, k1 ^ 1u);
+            const uint32_t kw = valid ? *(const uint32_t *)(kcod + (size_t)t * D + 4 * cq) : 0u;
+            const uint32_t vw = valid ? *(const uint32_t *)(vcod + (size_t)t * D + 4 * cq) : 0u;
+            const float kbv = (nbyp > 0 && valid) ? h2f(kbr[8 * t + (bslot ? cq : 0)]) : 0.f;
+            const uint2 ksr = sm.ks[t], vsr = sm.vs[t];
+            const uint32_t kss = gq < 2 ? ksr.x : ksr.y, vss = gq < 2 ? vsr.x : vsr.y;
+            const float ks = h2f((uint16_t)((gq & 1) ? (kss >> 16) : (kss & 0xffff)));
+            const float vs = h2f((uint16_t)((gq & 1) ? (vss >> 16) : (vss & 0xffff)));
+            const uint32_t ukw[4] = {uk.x, uk.y, uk.z, uk.w};
+            const uint32_t uvw[4] = {uv.x, uv.y, uv.z, uv.w};
+            float kx[4], vx[4];
+#pragma unroll
+            for (int e = 0; e < 4; e++) {
+                const float kcode = (float)(int8_t)((kw >> (8 * e)) & 0xff);
+                const float vcode = (float)(int8_t)((vw >> (8 * e)) & 0xff);
+                kx[e] = ks * __builtin_fmaf((float)(ukw[e] >> 8), -0x1p-24f, kcode + 0.5f);
+                vx[e] = vs * __builtin_fmaf((float)(uvw[e] >> 8), -0x1p-24f, vcode + 0.5f);
+            }
+            float eut[QPK];
+#pragma unroll
+            for (int hh = 0; hh < QPK; hh++) eut[hh] = sm.eu[t][hh];
+#pragma unroll
+            for (int hh = 0; hh < QPK; hh++) {
+                float part = qb[hh] * kbv;
+#pragma unroll
+                for (int e = 0; e < 4; e++) part = fmaf(qv[hh][e], kx[e], part);
+                float z2 = half_sum32(part) * qscale;
+                if (!valid) z2 = -INFINITY;
+                if (__any(z2 > m[hh] + LAZY_TAU)) {
+                    const float mnew = fmaxf(m[hh], z2);
+                    // a half-wave with no valid token yet keeps m = -inf
+                    const float alpha = mnew == -INFINITY ? 1.0f : __builtin_amdgcn_exp2f(m[hh] - mnew);
+                    m[hh] = mnew;
+                    lp[hh] *= alpha;
+                    ap[hh] *= alpha;
+#pragma unroll
+                    for (int e = 0; e < 4; e++) o[hh][e] *= alpha;
+                }
+                const float pr = valid ? __builtin_amdgcn_exp2f(z2 - m[hh]) : 0.f;
+                lp[hh] += pr;
+                ap[hh] = fmaf(pr, eut[hh], ap[hh]);
+#pragma unroll
+                for (int e = 0; e < 4; e++) o[hh][e] = fmaf(pr, vx[e], o[hh][e]);
+            }
+        }
+    }
+    // combine the two token phases (lanes L and L ^ 32); the phase-0 half
+    // always holds the split's first token
+#pragma unroll
+    for (int hh = 0; hh < QPK; hh++) {
+        const float mo = shfl_xor(m[hh], 32);
+        const float mt = fmaxf(m[hh], mo);
+        const float sa = m[hh] == -INFINITY ? 0.f : exp2f(m[hh] - mt);
+        const float lo = shfl_xor(lp[hh] * sa, 32);
+        const float ao = shfl_xor(ap[hh] * sa, 32);
+        const float lt = lp[hh] * sa + lo;
+        const float at = ap[hh] * sa + ao;
+        float oo[4];
+#pragma unroll
+        for (int e = 0; e < 4; e++) {
+            const float mine = o[hh][e] * sa;
+            oo[e] = mine + shfl_xor(mine, 32);
+        }
+        const size_t row = part_row(W, P.Hq, b, h * QPK + hh, s);
+        if (tp == 0) {
+            const float il = 1.0f / lt;
+            *(float4 *)(W.o + row * D + 4 * cq) = make_float4(oo[0] * il, oo[1] * il, oo[2] * il, oo[3] * il);
+        }
+        if (lane == 0) W.ml[row] = make_float2(mt + log2f(lt), at / lt);
+    }
+}
+
 constexpr int S2_MAXSPLIT = 256;     // paged splits per query head (kvq_set_layout keeps <= 256)
 
 // ---------------------------------------------------------------------------
@@ -1517,7 +1708,9 @@ __global__ __launch_bounds__(64) void merge_kernel(KParams P, float *__restrict_
     const int h = hq / P.qpk;
     const size_t bh = (size_t)b * P.Hkv + h;
     const int l = P.state[bh * 4], nkq = P.state[bh * 4 + 1];
-    const int npages = wit ? nkq / WPT : (max(0, l - P.sink - P.R) + PT - 1) / PT;
+    const int npages = wit ? nkq / WPT
+                       : P.scheme == KVQ_SCHEME_WITCERT_PAGED ? (l + PT - 1) / PT
+                                                             : (max(0, l - P.sink - P.R) + PT - 1) / PT;
     const int nsplit = (npages + P.split_pages - 1) / P.split_pages;
     const int ne = nsplit + W.n_win;              // entries nsplit.. are the window chunks
     const size_t row0 = part_row(W, P.Hq, b, hq, 0);
@@ -1591,7 +1784,16 @@ hipError_t launch_decode(const KParams &P, const uint16_t *q, float *out, float 
         hipError_t e = hipEventRecord(W.ev_begin, s);
         if (e != hipSuccess) return e;
     }
-    if (P.scheme == KVQ_SCHEME_WITCERT) {
+    if (P.scheme == KVQ_SCHEME_WITCERT_PAGED) {
+        dim3 g1(W.max_splits, P.Hkv, P.B);            // no fp16 tail, no window chunks
+        switch (P.qpk) {
+            case 1: stage1_witcert_paged_kernel<1><<<g1, 64, 0, s>>>(P, q, W, qscale, sm_scale, kappa); break;
+            case 2: stage1_witcert_paged_kernel<2><<<g1, 64, 0, s>>>(P, q, W, qscale, sm_scale, kappa); break;
+            case 4: stage1_witcert_paged_kernel<4><<<g1, 64, 0, s>>>(P, q, W, qscale, sm_scale, kappa); break;
+            case 8: stage1_witcert_paged_kernel<8><<<g1, 64, 0, s>>>(P, q, W, qscale, sm_scale, kappa); break;
+            default: return hipErrorInvalidValue;
+        }
+    } else if (P.scheme == KVQ_SCHEME_WITCERT) {
         dim3 g1(W.max_splits + W.n_win, P.Hkv, P.B);  // + the window chunks of each KV head
         switch (P.qpk) {
             case 1: stage1_witcert_kernel<1><<<g1, 64, 0, s>>>(P, q, W, qscale, sm_scale, kappa); break;

@@ -19,7 +19,8 @@ struct KParams {
     uint16_t *sink_v;
     int B, Hq, Hkv, R, max_pages, n_pages, page_bytes, scheme, qpk, split_pages;
     int sink;                     // leading fp16 tokens; quantized positions are t - sink
-    int nb;                       // Kitty boosted channels (16 or 32; 0 for others)
+    int nb;                       // Kitty boosted channels (16 or 32); WITCERT_PAGED
+                                  // bypassed RoPE pairs (0 .. 4); 0 for others
     int force_generic;            // 1: use the per-query-head VALU stage 1
     uint32_t layer;
     uint64_t seed;
@@ -34,7 +35,8 @@ struct Workspace {
     float *o;        // [B][Hq][max_splits + n_win][128]
     float2 *ml;      // [B][Hq][max_splits + n_win]  (lse in log2 units, A)
     int max_splits;
-    int n_win;       // window chunks: residual / 64 (KIVI2 / KITTY) + 1 with sink tokens, 4 (WITCERT)
+    int n_win;       // window chunks: residual / 64 (KIVI2 / KITTY) + 1 with sink tokens,
+                     // 4 (WITCERT), 0 (WITCERT_PAGED)
     hipEvent_t ev_begin, ev_end;   // optional stage-1 timing events
 };
 
@@ -52,6 +54,8 @@ hipError_t launch_prefill(const KParams &P, int req0, int n_req, const uint16_t 
                           hipStream_t s);
 hipError_t launch_kitty_calibrate(const KParams &P, const uint16_t *calib, int n_tokens,
                                   uint8_t *idx_out, hipStream_t s);
+hipError_t launch_witcert_calibrate(const KParams &P, const uint16_t *calib, int n_tokens,
+                                    uint8_t *idx_out, hipStream_t s);
 
 // read path (kvq_decode.hip)
 hipError_t launch_decode(const KParams &P, const uint16_t *q, float *out, float *cert,

@@ -579,10 +579,233 @@ __global__ __launch_bounds__(256) void prefill_witcert_kernel(KParams P, int req
 // ---------------------------------------------------------------------------
 // launchers
 // ---------------------------------------------------------------------------
+// ---------------------------------------------------------------------------
+// WITCERT_PAGED: each token quantized as it is written ("WitCert" page,
+// certified deployment): one fp16 scale s = amax/126.5 per (token, group of
+// 32 channels) on each side, quantized with the stored scale; the dither of
+// channel c from the Philox4x32-10 block with counter (slot_lo, c >> 2,
+// (layer << 16) | KV head, slot_hi), word c & 3, slot = page_id * 64 +
+// position in the page; bypassed key channels (the fixed outlier RoPE pairs)
+// are left out of their group's amax, get code 0 and are kept fp16 in the
+// token's bypass row.
+// ---------------------------------------------------------------------------
+__device__ inline uint16_t witcert_scale16(float a) {
+#pragma clang fp contract(off)
+    uint16_t s16 = 0;
+    if (a > 0.0f) {
+        s16 = f2h(a / 126.5f);
+        if (127.0f * h2f(s16) <= a) s16 = (uint16_t)(s16 + 1);
+    }
+    return s16;
+}
+
+__device__ inline uint32_t witcert_code8(uint16_t xb, float s, bool nz, uint32_t word) {
+#pragma clang fp contract(off)
+    float c = 0.0f;
+    if (nz) {
+        const float xi = dither_from_word(word);
+        const float q = h2f(xb) / s;
+        c = rintf(q + xi);
+        c = fminf(fmaxf(c, -127.0f), 127.0f);
+    }
+    return (uint32_t)(uint8_t)(int8_t)(int)c;
+}
+
+__device__ inline U4 slot_philox(const KParams &P, int h, uint64_t slot, uint32_t quad, int side) {
+    return philox4x32_10(U4{(uint32_t)slot, quad, (P.layer << 16) | (uint32_t)h, (uint32_t)(slot >> 32)},
+                         (uint32_t)P.seed, (uint32_t)(P.seed >> 32) ^ (uint32_t)side);
+}
+
+// Bypass offset of channel c of KV head h (2 nb + 1 when not bypassed).
+__device__ inline int bypass_off(const KParams &P, int h, int c) {
+    return P.nb > 0 ? (int)P.boost_idx[(size_t)h * D + c] : 1;
+}
+
+// One side of one token by one wave: lane = channels 2 lane, 2 lane + 1
+// (quad lane >> 1, Philox words 2 (lane & 1) and 2 (lane & 1) + 1); the 16
+// lanes of a group reduce its amax with shuffles.
+__device__ inline void witcert_token_wave(const KParams &P, int h, uint64_t slot, int side,
+                                          uint32_t xin, bool byp0, bool byp1,
+                                          uint8_t *codes_row, uint16_t *scale_row) {
+    const int lane = threadIdx.x;
+    const uint16_t x0 = (uint16_t)(xin & 0xffffu), x1 = (uint16_t)(xin >> 16);
+    float a = fmaxf(byp0 ? 0.0f : fabsf(h2f(x0)), byp1 ? 0.0f : fabsf(h2f(x1)));
+#pragma unroll
+    for (int m = 8; m >= 1; m >>= 1) a = fmaxf(a, shfl_xor(a, m));
+    const uint16_t s16 = witcert_scale16(a);
+    const float s = h2f(s16);
+    const U4 u = slot_philox(P, h, slot, (uint32_t)(lane >> 1), side);
+    const uint32_t w0 = (lane & 1) ? u.z : u.x, w1 = (lane & 1) ? u.w : u.y;
+    const uint32_t c0 = byp0 ? 0u : witcert_code8(x0, s, s16 != 0, w0);
+    const uint32_t c1 = byp1 ? 0u : witcert_code8(x1, s, s16 != 0, w1);
+    ((uint16_t *)codes_row)[lane] = (uint16_t)(c0 | (c1 << 8));
+    if ((lane & 15) == 0) scale_row[lane >> 4] = s16;
+}
+
+__global__ __launch_bounds__(64) void append_witcert_paged_kernel(KParams P, const uint16_t *__restrict__ kn,
+                                                                  const uint16_t *__restrict__ vn) {
+    const int h = blockIdx.x, b = blockIdx.y, lane = threadIdx.x;
+    const Geom G = geom(P.scheme, P.nb);
+    const size_t bh = (size_t)b * P.Hkv + h;
+    int32_t *st = P.state + bh * 4;
+    const int l = st[0];
+    if (l >= P.max_pages * PT) {
+        if (lane == 0) atomicOr(P.status, (uint32_t)KVQ_STATUS_CAPACITY);
+        return;
+    }
+    const int pid = P.table[(size_t)b * P.max_pages + l / PT];
+    if (!page_ok(P, pid)) {
+        if (lane == 0) atomicOr(P.status, (uint32_t)KVQ_STATUS_UNMAPPED_PAGE);
+        return;
+    }
+    uint8_t *page = page_ptr(P, pid, h);
+    const int tp = l % PT;
+    const uint64_t slot = (uint64_t)pid * PT + (uint64_t)tp;
+    const uint32_t kin = ((const uint32_t *)kn)[bh * (D / 2) + lane];
+    const uint32_t vin = ((const uint32_t *)vn)[bh * (D / 2) + lane];
+    const int o0 = bypass_off(P, h, 2 * lane), o1 = bypass_off(P, h, 2 * lane + 1);
+    const bool b0 = o0 < 2 * P.nb, b1 = o1 < 2 * P.nb;
+    witcert_token_wave(P, h, slot, 0, kin, b0, b1, page + G.kc + (size_t)tp * D,
+                       (uint16_t *)(page + G.ks) + 4 * tp);
+    witcert_token_wave(P, h, slot, 1, vin, false, false, page + G.vc + (size_t)tp * D,
+                       (uint16_t *)(page + G.vs) + 4 * tp);
+    uint16_t *kb = (uint16_t *)(page + G.kh) + 8 * tp;
+    if (b0) kb[o0] = (uint16_t)(kin & 0xffffu);
+    if (b1) kb[o1] = (uint16_t)(kin >> 16);
+    if (lane == 0) {
+        st[0] = l + 1;
+        st[1] = l + 1;
+    }
+}
+
+// prefill: one 256-thread block per (page, KV head, request); thread (token
+// tl = tid >> 2, group g = tid & 3) quantizes the group's 32 channels of one
+// token on each side (eight Philox blocks per side).
+__global__ __launch_bounds__(256) void prefill_witcert_paged_kernel(KParams P, int req0,
+                                                                   const uint16_t *__restrict__ K,
+                                                                   const uint16_t *__restrict__ V,
+                                                                   long long ld,
+                                                                   const int32_t *__restrict__ lengths) {
+    const int p = blockIdx.x, h = blockIdx.y, rr = blockIdx.z, b = req0 + rr;
+    const int tid = threadIdx.x;
+    const Geom G = geom(P.scheme, P.nb);
+    const int len = lengths[rr];
+    if (len < 0 || len > P.max_pages * PT || (long long)len > ld) {
+        if (p == 0 && tid == 0) atomicOr(P.status, (uint32_t)KVQ_STATUS_BAD_LENGTH);
+        return;
+    }
+    const size_t bh = (size_t)b * P.Hkv + h;
+    if (p == 0 && tid == 0) {
+        P.state[bh * 4 + 0] = len;
+        P.state[bh * 4 + 1] = len;
+        P.state[bh * 4 + 2] = 0;
+        P.state[bh * 4 + 3] = 0;
+    }
+    const int t0 = p * PT;
+    if (t0 >= len) return;
+    const int pid = P.table[(size_t)b * P.max_pages + p];
+    if (!page_ok(P, pid)) {
+        if (tid == 0) atomicOr(P.status, (uint32_t)KVQ_STATUS_UNMAPPED_PAGE);
+        return;
+    }
+    uint8_t *page = page_ptr(P, pid, h);
+    const int tl = tid >> 2, g = tid & 3;
+    const int t = t0 + tl;
+    if (t >= len) return;
+    const uint64_t slot = (uint64_t)pid * PT + (uint64_t)tl;
+    for (int side = 0; side < 2; side++) {
+        const uint16_t *src = (side ? V : K) + (((size_t)rr * P.Hkv + h) * (size_t)ld + t) * D + 32 * g;
+        uint16_t x[32];
+#pragma unroll
+        for (int j = 0; j < 4; j++) {
+            const uint4 v4 = ((const uint4 *)src)[j];
+            const uint32_t w[4] = {v4.x, v4.y, v4.z, v4.w};
+#pragma unroll
+            for (int e = 0; e < 4; e++) {
+                x[8 * j + 2 * e] = (uint16_t)(w[e] & 0xffffu);
+                x[8 * j + 2 * e + 1] = (uint16_t)(w[e] >> 16);
+            }
+        }
+        bool byp[32];
+        float a = 0.0f;
+#pragma unroll
+        for (int j = 0; j < 32; j++) {
+            byp[j] = side == 0 && bypass_off(P, h, 32 * g + j) < 2 * P.nb;
+            if (!byp[j]) a = fmaxf(a, fabsf(h2f(x[j])));
+        }
+        const uint16_t s16 = witcert_scale16(a);
+        const float s = h2f(s16);
+        uint32_t *crow = (uint32_t *)(page + (side ? G.vc : G.kc) + (size_t)tl * D + 32 * g);
+#pragma unroll
+        for (int qd = 0; qd < 8; qd++) {
+            const U4 u = slot_philox(P, h, slot, (uint32_t)(8 * g + qd), side);
+            const uint32_t wv[4] = {u.x, u.y, u.z, u.w};
+            uint32_t packed = 0;
+#pragma unroll
+            for (int e = 0; e < 4; e++) {
+                const int j = 4 * qd + e;
+                const uint32_t c = byp[j] ? 0u : witcert_code8(x[j], s, s16 != 0, wv[e]);
+                packed |= c << (8 * e);
+            }
+            crow[qd] = packed;
+        }
+        ((uint16_t *)(page + (side ? G.vs : G.ks)))[4 * tl + g] = s16;
+        if (side == 0) {
+            uint16_t *kb = (uint16_t *)(page + G.kh) + 8 * tl;
+#pragma unroll
+            for (int j = 0; j < 32; j++)
+                if (byp[j]) kb[bypass_off(P, h, 32 * g + j)] = x[j];
+        }
+    }
+}
+
+// Fixed bypass set per KV head: pair i = channels (i, i + 64); importance
+// max_t (x_i^2 + x_{i+64}^2) (squares exact in binary32, one rounding for
+// the sum); the nb largest, ties to the lower pair; offsets in ascending
+// channel order, others 2 nb + 1.  One wave per KV head, lane = pair.
+__global__ __launch_bounds__(64) void witcert_calibrate_kernel(const uint16_t *__restrict__ calib, int T,
+                                                               int nb, uint8_t *__restrict__ idx_out) {
+    const int h = blockIdx.x, i = threadIdx.x;
+    __shared__ float imp[D / 2];
+    __shared__ uint8_t chosen[D];
+    float e = 0.0f;
+    for (int t = 0; t < T; t++) {
+#pragma clang fp contract(off)
+        const float a = h2f(calib[((size_t)h * T + t) * D + i]);
+        const float c = h2f(calib[((size_t)h * T + t) * D + i + D / 2]);
+        const float v = a * a + c * c;
+        e = fmaxf(e, v);
+    }
+    imp[i] = e;
+    chosen[i] = 0;
+    chosen[i + D / 2] = 0;
+    __syncthreads();
+    if (i == 0) {
+        for (int r = 0; r < nb; r++) {
+            int best = -1;
+            for (int j = 0; j < D / 2; j++)
+                if (!chosen[j] && (best < 0 || imp[j] > imp[best])) best = j;
+            chosen[best] = 1;
+            chosen[best + D / 2] = 1;
+        }
+        int off = 0;
+        for (int c = 0; c < D; c++)
+            idx_out[(size_t)h * D + c] = chosen[c] ? (uint8_t)(off++) : (uint8_t)(2 * nb + 1);
+    }
+}
+
+hipError_t launch_witcert_calibrate(const KParams &P, const uint16_t *calib, int n_tokens,
+                                    uint8_t *idx_out, hipStream_t s) {
+    witcert_calibrate_kernel<<<P.Hkv, 64, 0, s>>>(calib, n_tokens, P.nb, idx_out);
+    return hipGetLastError();
+}
+
 hipError_t launch_append(const KParams &P, const uint16_t *k, const uint16_t *v, hipStream_t s) {
     dim3 grid(P.Hkv, P.B);
     if (P.scheme == KVQ_SCHEME_WITCERT)
         append_witcert_kernel<<<grid, 64, 0, s>>>(P, k, v);
+    else if (P.scheme == KVQ_SCHEME_WITCERT_PAGED)
+        append_witcert_paged_kernel<<<grid, 64, 0, s>>>(P, k, v);
     else
         append_kivi_kernel<<<grid, 64, 0, s>>>(P, k, v);
     return hipGetLastError();
@@ -590,6 +813,7 @@ hipError_t launch_append(const KParams &P, const uint16_t *k, const uint16_t *v,
 
 hipError_t launch_flush(const KParams &P, hipStream_t s) {
     dim3 grid(P.Hkv, P.B);
+    if (P.scheme == KVQ_SCHEME_WITCERT_PAGED) return hipSuccess;   // tokens are quantized on write
     if (P.scheme == KVQ_SCHEME_WITCERT)
         flush_witcert_kernel<<<grid, 256, 0, s>>>(P);
     else
@@ -603,6 +827,8 @@ hipError_t launch_prefill(const KParams &P, int req0, int n_req, const uint16_t 
     dim3 grid(P.max_pages, P.Hkv, n_req);
     if (P.scheme == KVQ_SCHEME_WITCERT)
         prefill_witcert_kernel<<<grid, 256, 0, s>>>(P, req0, K, V, ld, lengths);
+    else if (P.scheme == KVQ_SCHEME_WITCERT_PAGED)
+        prefill_witcert_paged_kernel<<<grid, 256, 0, s>>>(P, req0, K, V, ld, lengths);
     else
         prefill_kivi_kernel<<<grid, 256, 0, s>>>(P, req0, K, V, ld, lengths);
     return hipGetLastError();

@@ -25,6 +25,13 @@ own datasets and models are not used):
      of request 0).
   5  WitCert INT8 dither: B=32, 32 query / 8 KV heads, context 16384 plus
      one appended token, plain N(0,1).
+  6  workload 4 with the Kitty boosted set chosen per 64-token page.
+  7  workload 3 with 32 fp16 sink tokens per request.
+  8  workload 4 with 32 boosted channels (Kitty-Pro).
+  9  workload 4's shapes with 4-bit keys and values (KIVI-4).
+ 10  WitCert paging-safe storage: workload 5's shapes, keys with four seeded
+     outlier RoPE pairs (channels i and i + 64, x15) that the four-pair
+     bypass set should find.
 """
 from __future__ import annotations
 
@@ -40,7 +47,7 @@ _CTX_K, _CTX_V, _STEP_Q, _STEP_K, _STEP_V, _OUTLIERS, _LENGTHS, _PAGES, _QDEC = 
 class Workload:
     wid: int
     name: str
-    scheme: str            # "kivi2" | "kitty" | "witcert" | "kitty_dyn" | "kivi4"
+    scheme: str            # "kivi2" | "kitty" | "witcert" | "kitty_dyn" | "kivi4" | "witcert_paged"
     B: int
     Hq: int
     Hkv: int
@@ -55,6 +62,7 @@ class Workload:
     ctx: tuple = ()        # per-request context length before the first step
     outlier_ch: tuple = ()  # fixed channels (workload 1) or () for seeded
     n_outliers: int = 0
+    outlier_pairs: bool = False  # seeded outliers are RoPE pairs (i, i + D/2)
     outlier_factor: float = 1.0
     steps: int = 1
     seed: int = 0
@@ -106,6 +114,11 @@ def workload(wid: int, **over) -> Workload:
         w = dict(wid=7, name="kivi2-sink32-gqa-b64-32q8kv-ctx8k-32k-paged", scheme="kivi2", B=64,
                  Hq=32, Hkv=8, ctx=_lengths3(64, 8192, 32768, 3), n_outliers=4,
                  outlier_factor=15.0, sink=32, steps=1, seed=7)
+    elif wid == 10:
+        # WitCert paging-safe storage at workload 5's shapes, 4 bypassed pairs
+        w = dict(wid=10, name="witcert-paged-b32-32q8kv-ctx16384", scheme="witcert_paged", B=32,
+                 Hq=32, Hkv=8, ctx=(16384,) * 32, n_outliers=4, outlier_pairs=True,
+                 outlier_factor=15.0, nb=4, steps=1, seed=10)
     elif wid == 9:
         # KIVI-4: workload 4's shapes with 4-bit keys and values, no boosting
         w = dict(wid=9, name="kivi4-mha-b16-h32-ctx32768", scheme="kivi4", B=16, Hq=32,
@@ -132,6 +145,9 @@ def outlier_channels(w: Workload, kvh: int) -> tuple:
         return tuple(w.outlier_ch)
     if w.n_outliers == 0:
         return ()
+    if w.outlier_pairs:
+        pr = _rng(w, _OUTLIERS, kvh).choice(w.D // 2, w.n_outliers, replace=False)
+        return tuple(sorted(int(c) for i in pr for c in (i, i + w.D // 2)))
     ch = _rng(w, _OUTLIERS, kvh).choice(w.D, w.n_outliers, replace=False)
     return tuple(int(c) for c in sorted(ch))
 
@@ -172,7 +188,7 @@ def page_permutation(w: Workload, n_pages: int) -> np.ndarray:
 
 
 def kitty_calibration(w: Workload, kvh: int, n: int = 1024) -> np.ndarray:
-    """Calibration slice for the static Kitty boost set: the first n context
-    keys of request 0 for this KV head."""
+    """Calibration slice for a static channel set (Kitty's boost set, WitCert's
+    bypassed pairs): the first n context keys of request 0 for this KV head."""
     K, _ = context_kv(w, 0, kvh, n=min(n, w.ctx[0]))
     return K

@@ -18,10 +18,11 @@ import numpy as np
 PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG, "libkvq.so")
 
-KVQ_SCHEME_KIVI2, KVQ_SCHEME_KITTY, KVQ_SCHEME_WITCERT, KVQ_SCHEME_KITTY_DYN, KVQ_SCHEME_KIVI4 = \
-    0, 1, 2, 3, 4
+(KVQ_SCHEME_KIVI2, KVQ_SCHEME_KITTY, KVQ_SCHEME_WITCERT, KVQ_SCHEME_KITTY_DYN, KVQ_SCHEME_KIVI4,
+ KVQ_SCHEME_WITCERT_PAGED) = 0, 1, 2, 3, 4, 5
 SCHEMES = {"kivi2": KVQ_SCHEME_KIVI2, "kitty": KVQ_SCHEME_KITTY, "witcert": KVQ_SCHEME_WITCERT,
-           "kitty_dyn": KVQ_SCHEME_KITTY_DYN, "kivi4": KVQ_SCHEME_KIVI4}
+           "kitty_dyn": KVQ_SCHEME_KITTY_DYN, "kivi4": KVQ_SCHEME_KIVI4,
+           "witcert_paged": KVQ_SCHEME_WITCERT_PAGED}
 
 KVQ_OK, KVQ_EINVAL, KVQ_ENULL, KVQ_EALIGN, KVQ_ENOLAYOUT, KVQ_EWORKSPACE, KVQ_ELAUNCH = \
     0, -1, -2, -3, -4, -5, -6
@@ -31,7 +32,8 @@ FLAG_GENERIC_STAGE1 = 1
 EXPORTS = ("kvq_set_layout", "kvq_append_token", "kvq_flush_key_group",
            "kvq_decode_attention", "kvq_page_bytes", "kvq_page_tokens",
            "kvq_bytes_per_token", "kvq_workspace_bytes", "kvq_prefill",
-           "kvq_kitty_calibrate", "kvq_set_stage1_events", "kvq_strerror")
+           "kvq_kitty_calibrate", "kvq_witcert_calibrate", "kvq_set_stage1_events",
+           "kvq_strerror")
 
 
 class kvq_layout_t(C.Structure):
@@ -84,6 +86,7 @@ def lib():
         L.kvq_prefill.argtypes = [C.POINTER(kvq_cache_t), C.c_int32, C.c_int32, P, P,
                                   C.c_int64, P, S]
         L.kvq_kitty_calibrate.argtypes = [C.POINTER(kvq_cache_t), P, C.c_int32, P, S]
+        L.kvq_witcert_calibrate.argtypes = [C.POINTER(kvq_cache_t), P, C.c_int32, P, S]
         L.kvq_set_stage1_events.argtypes = [C.POINTER(kvq_cache_t), P, P]
         L.kvq_strerror.argtypes = [C.c_int]
         L.kvq_strerror.restype = C.c_char_p
@@ -136,6 +139,12 @@ def kvq_kitty_calibrate(cache: kvq_cache_t, calib_ptr: int, n_tokens: int, idx_p
            "kvq_kitty_calibrate")
 
 
+def kvq_witcert_calibrate(cache: kvq_cache_t, calib_ptr: int, n_tokens: int, idx_ptr: int,
+                          stream: int):
+    _check(lib().kvq_witcert_calibrate(C.byref(cache), calib_ptr, n_tokens, idx_ptr, stream),
+           "kvq_witcert_calibrate")
+
+
 def kvq_set_stage1_events(cache: kvq_cache_t, begin: int | None, end: int | None):
     _check(lib().kvq_set_stage1_events(C.byref(cache), begin, end), "kvq_set_stage1_events")
 
@@ -150,7 +159,8 @@ def make_layout(scheme: str, B: int, Hq: int, Hkv: int, max_pages: int, n_pages:
     s = SCHEMES[scheme]
     return kvq_layout_t(scheme=s, head_dim=128, n_q_heads=Hq, n_kv_heads=Hkv, batch=B, group=32,
                         value_group=32, residual=R, block=256,
-                        n_boost=(16 if s in (KVQ_SCHEME_KITTY, KVQ_SCHEME_KITTY_DYN) else 0)
+                        n_boost=(16 if s in (KVQ_SCHEME_KITTY, KVQ_SCHEME_KITTY_DYN)
+                                 else 4 if s == KVQ_SCHEME_WITCERT_PAGED else 0)
                         if nb is None else nb,
                         max_pages=max_pages, n_pages=n_pages, split_pages=split_pages,
                         flags=flags, layer=layer, seed=seed, sink=sink, reserved=0)
@@ -188,26 +198,30 @@ class KVCache:
         self.page_bytes = page_bytes(layout)
         self.page_tokens = page_tokens(layout)
         W = 256 if layout.scheme == KVQ_SCHEME_WITCERT else layout.residual
+        wtok = layout.scheme == KVQ_SCHEME_WITCERT_PAGED    # no fp16 residual buffers
         fill = 0xFF if poison else 0
         self.pool = torch.full((layout.n_pages * Hkv * self.page_bytes,), fill, dtype=torch.uint8,
                                device=device)
         pt = np.ascontiguousarray(page_table, dtype=np.int32).reshape(B, layout.max_pages)
         self.page_table = torch.from_numpy(pt).to(device)
         self.state = torch.zeros((B, Hkv, 4), dtype=torch.int32, device=device)
-        self.res_k = torch.zeros((B, Hkv, W, 128), dtype=torch.int16, device=device)
-        self.res_v = torch.zeros((B, Hkv, W, 128), dtype=torch.int16, device=device)
+        self.res_k = None if wtok else torch.zeros((B, Hkv, W, 128), dtype=torch.int16, device=device)
+        self.res_v = None if wtok else torch.zeros((B, Hkv, W, 128), dtype=torch.int16, device=device)
         self.status = torch.zeros((4,), dtype=torch.int32, device=device)
         S = layout.sink
         self.sink_k = torch.zeros((B, Hkv, S, 128), dtype=torch.int16, device=device) if S else None
         self.sink_v = torch.zeros((B, Hkv, S, 128), dtype=torch.int16, device=device) if S else None
-        if layout.scheme == KVQ_SCHEME_KITTY:
-            idx = np.full((Hkv, 128), layout.n_boost + 1, np.uint8) if boost_idx is None else boost_idx
+        if layout.scheme == KVQ_SCHEME_KITTY or (wtok and layout.n_boost > 0):
+            sentinel = layout.n_boost + 1 if not wtok else 2 * layout.n_boost + 1
+            idx = np.full((Hkv, 128), sentinel, np.uint8) if boost_idx is None else boost_idx
             self.boost_idx = torch.from_numpy(np.ascontiguousarray(idx, np.uint8)).to(device)
         else:
             self.boost_idx = None
         self.bufs = kvq_buffers_t(
             pool=self.pool.data_ptr(), page_table=self.page_table.data_ptr(),
-            state=self.state.data_ptr(), res_k=self.res_k.data_ptr(), res_v=self.res_v.data_ptr(),
+            state=self.state.data_ptr(),
+            res_k=None if wtok else self.res_k.data_ptr(),
+            res_v=None if wtok else self.res_v.data_ptr(),
             boost_idx=self.boost_idx.data_ptr() if self.boost_idx is not None else None,
             status=self.status.data_ptr(),
             sink_k=self.sink_k.data_ptr() if S else None, sink_v=self.sink_v.data_ptr() if S else None)
@@ -244,6 +258,13 @@ class KVCache:
         assert self.boost_idx is not None
         kvq_kitty_calibrate(self.cache, calib.data_ptr(), calib.shape[1],
                             self.boost_idx.data_ptr(), self.stream())
+
+    def witcert_calibrate(self, calib):
+        """calib: fp16 [Hkv][T][128] on the device; fills the bypass index
+        (WitCert paging-safe storage)."""
+        assert self.boost_idx is not None
+        kvq_witcert_calibrate(self.cache, calib.data_ptr(), calib.shape[1],
+                              self.boost_idx.data_ptr(), self.stream())
 
     def status_word(self) -> int:
         return int(self.status[0].item())

@@ -40,6 +40,20 @@
  *                      accumulated in the attention pass.  ("WitCert" page:
  *                      write-kernel paragraph, "Key structure", quantised-path
  *                      certificate paragraph.)
+ *   KVQ_SCHEME_WITCERT_PAGED
+ *                      WitCert's storage for token-granular paging: every
+ *                      token quantized when written (no fp16 tail), INT8 with
+ *                      subtractive dither and one fp16 scale s = amax/126.5
+ *                      per (token, 32-channel group) on each side; the dither
+ *                      keyed by (layer, KV head, slot, channel), slot =
+ *                      page_id * 64 + position in the page, so it survives
+ *                      paging and prefix sharing; n_boost = m fixed outlier
+ *                      RoPE key pairs (channels i and i + 64) per KV head
+ *                      stored fp16 and left out of their group's amax; the
+ *                      certificate uses each token's group scales (a
+ *                      bypassed channel adds no error).  136 B per token and
+ *                      side + 16 B when m > 0.  ("WitCert" page, certified-deployment
+ *                      paragraphs.)
  *
  * Step order per decode step (all calls asynchronous on the caller's stream,
  * none synchronizes, allocates or frees, so a step can be captured in a HIP
@@ -75,7 +89,8 @@ enum {
     KVQ_SCHEME_KITTY = 1,
     KVQ_SCHEME_WITCERT = 2,
     KVQ_SCHEME_KITTY_DYN = 3,
-    KVQ_SCHEME_KIVI4 = 4
+    KVQ_SCHEME_KIVI4 = 4,
+    KVQ_SCHEME_WITCERT_PAGED = 5
 };
 
 /* layout flags */
@@ -120,20 +135,23 @@ typedef struct kvq_layout {
                                 G), 64 .. 256 (KIVI2/KITTY/KITTY_DYN) */
     int32_t block;           /* WitCert block tokens; must be 256 (WITCERT) */
     int32_t n_boost;         /* KITTY / KITTY_DYN boosted key channels: 16
-                                (0 for others) */
+                                or 32; WITCERT_PAGED: bypassed RoPE pairs
+                                m, 0 .. 4; 0 for others */
     int32_t max_pages;       /* page-table row length per request */
     int32_t n_pages;         /* pages in the pool */
     int32_t split_pages;     /* stage-1 split size in pages; 0: 8 when max_pages
-                                <= 128, else 12 (1 for WITCERT), raised to
-                                ceil(max_pages / 256) where that is larger */
+                                <= 128, else 12 (1 for WITCERT, 4 for
+                                WITCERT_PAGED), raised to ceil(max_pages /
+                                256) where that is larger */
     int32_t flags;           /* KVQ_FLAG_* */
-    uint32_t layer;          /* WITCERT dither counter field; < 65536 */
-    uint64_t seed;           /* WITCERT dither key */
+    uint32_t layer;          /* WITCERT(_PAGED) dither counter field; < 65536 */
+    uint64_t seed;           /* WITCERT(_PAGED) dither key */
     int32_t sink;            /* KIVI2 / KITTY / KITTY_DYN: the first `sink`
                                 tokens of every request stay fp16, keys and
                                 values ("Kitty" summary, sink tokens); key
                                 groups, pages and the value window count from
-                                token `sink`; 0 .. 64, 0 for WITCERT */
+                                token `sink`; 0 .. 64, 0 for WITCERT and
+                                WITCERT_PAGED */
     int32_t reserved;        /* must be 0 */
 } kvq_layout_t;
 
@@ -149,9 +167,14 @@ typedef struct kvq_buffers {
                                  W = residual (KIVI2/KITTY) or block (WITCERT) */
     uint16_t *res_v;          /* [batch][n_kv_heads][W][D] fp16 value window:
                                  ring by token index (KIVI2/KITTY) or active
-                                 block (WITCERT) */
+                                 block (WITCERT); WITCERT_PAGED: unused, may
+                                 be NULL (also res_k) */
     const uint8_t *boost_idx; /* KITTY: [n_kv_heads][D] offset of each channel
-                                 in the high plane, or n_boost + 1 */
+                                 in the high plane, or n_boost + 1;
+                                 WITCERT_PAGED with n_boost > 0: offset of a
+                                 bypassed key channel in its token's fp16
+                                 bypass row (0 .. 2 n_boost - 1, both channels
+                                 of each pair), or 2 n_boost + 1 */
     uint32_t *status;         /* one uint32 of sticky KVQ_STATUS_* bits */
     uint16_t *sink_k;         /* sink > 0: [batch][n_kv_heads][sink][D] fp16
                                  keys of the sink tokens; else may be NULL */
@@ -162,7 +185,7 @@ typedef struct kvq_buffers {
 typedef struct kvq_cache {
     kvq_layout_t layout;
     kvq_buffers_t bufs;
-    int32_t page_tokens;      /* 64 (KIVI2/KITTY) or 256 (WITCERT) */
+    int32_t page_tokens;      /* 256 (WITCERT), else 64 */
     int32_t split_pages;      /* resolved stage-1 split, pages */
     int64_t page_bytes;       /* bytes of one (page, KV head) block */
     int32_t magic;            /* set by kvq_set_layout */
@@ -188,9 +211,14 @@ typedef struct kvq_cache {
  *   and the flush fills whole 64-token pages); n_boost != 16 for KITTY and
  *   KITTY_DYN or != 0 for KIVI2 and KIVI4; KVQ_FLAG_GENERIC_STAGE1 with
  *   KITTY_DYN or KIVI4;
- *   sink outside [0, 64] or non-zero for WITCERT; reserved != 0;
+ *   sink outside [0, 64] or non-zero for WITCERT / WITCERT_PAGED; reserved
+ *   != 0;
  *   WITCERT: block != 256; layer >= 65536; query heads per KV head not in
- *   {1, 2, 4, 8}. */
+ *   {1, 2, 4, 8};
+ *   WITCERT_PAGED: group or value_group != 32; n_boost outside [0, 4];
+ *   layer >= 65536; query heads per KV head not in {1, 2, 4, 8}; any flag.
+ * KVQ_ENULL also for a NULL boost_idx with KITTY, or with WITCERT_PAGED and
+ * n_boost > 0. */
 int kvq_set_layout(kvq_cache_t *cache, const kvq_layout_t *layout,
                    const kvq_buffers_t *bufs);
 
@@ -199,6 +227,8 @@ int kvq_set_layout(kvq_cache_t *cache, const kvq_layout_t *layout,
  * l - n_kq; the value goes to ring slot l mod R after the token leaving the
  * window (l - R, when l >= R) is quantized per token into the pages ("KIVI"
  * explainer 3.3 value FIFO).  WITCERT: key and value go to the active block.
+ * WITCERT_PAGED: key and value are quantized into slot l mod 64 of page
+ * page_table[b][l / 64] at once (n_kq = l + 1).
  * Then l += 1.  Device errors: RESIDUAL_FULL, CAPACITY, UNMAPPED_PAGE. */
 int kvq_append_token(const kvq_cache_t *cache, const uint16_t *k_new,
                      const uint16_t *v_new, hipStream_t stream);
@@ -207,7 +237,7 @@ int kvq_append_token(const kvq_cache_t *cache, const uint16_t *k_new,
  * (KIVI2/KITTY: per channel, R/G groups of G tokens, written to the pages;
  * "KIVI" explainer 3.3) or whose active block holds 256 tokens (WITCERT:
  * keys and values, per channel).  A no-op elsewhere, so it may be called every
- * step. */
+ * step (WITCERT_PAGED: always a no-op, nothing is launched). */
 int kvq_flush_key_group(const kvq_cache_t *cache, hipStream_t stream);
 
 /* Decode attention for one query token per request over the current state.
@@ -233,7 +263,8 @@ int64_t kvq_page_bytes(const kvq_layout_t *layout);
 int32_t kvq_page_tokens(const kvq_layout_t *layout);
 
 /* Quantized bytes per token per KV head, keys and values together, statistics
- * included (96 for KIVI2, 100 for KITTY with 16 boosted, 258 for WITCERT). */
+ * included (96 for KIVI2, 100 for KITTY with 16 boosted, 160 for KIVI4, 258
+ * for WITCERT, 272 + (16 when n_boost > 0) for WITCERT_PAGED). */
 double kvq_bytes_per_token(const kvq_layout_t *layout);
 
 /* Workspace bytes kvq_decode_attention needs for this cache. */
@@ -243,7 +274,8 @@ size_t kvq_workspace_bytes(const kvq_cache_t *cache);
  * [req0, req0 + n_req), K, V: device fp16 [n_req][n_kv_heads][ld_tokens][D],
  * lengths: device int32 [n_req].  Leaves each (request, KV head) exactly as
  * streaming its tokens through flush/append would: r_k = ((l-1) mod R) + 1 keys
- * (WITCERT: ((l-1) mod 256) + 1 tokens) stay fp16, values keep the newest R. */
+ * (WITCERT: ((l-1) mod 256) + 1 tokens) stay fp16, values keep the newest R;
+ * WITCERT_PAGED: every token quantized. */
 int kvq_prefill(const kvq_cache_t *cache, int32_t req0, int32_t n_req,
                 const uint16_t *K, const uint16_t *V, int64_t ld_tokens,
                 const int32_t *lengths, hipStream_t stream);
@@ -255,6 +287,17 @@ int kvq_prefill(const kvq_cache_t *cache, int32_t req0, int32_t n_req,
  * ("Kitty" summary: Selecting the Top-K Channels; The Boost Index Tensor). */
 int kvq_kitty_calibrate(const kvq_cache_t *cache, const uint16_t *calib,
                         int32_t n_tokens, uint8_t *idx_out, hipStream_t stream);
+
+/* WITCERT_PAGED fixed bypass set from a calibration slice: calib: device
+ * fp16 [n_kv_heads][n_tokens][D]; idx_out: device uint8 [n_kv_heads][D] in
+ * boost_idx's format.  The n_boost RoPE pairs (i, i + 64) with the largest
+ * max_t (x_i^2 + x_{i+64}^2) over the slice are bypassed (each square exact
+ * in binary32 and the sum rounded once; ties to the lower pair), offsets in
+ * ascending channel order ("WitCert" page, certified deployment: a fixed
+ * per-(layer, KV head) pair set chosen from the start of a sequence).
+ * KVQ_EINVAL for another scheme, n_boost = 0 or n_tokens < 1. */
+int kvq_witcert_calibrate(const kvq_cache_t *cache, const uint16_t *calib,
+                          int32_t n_tokens, uint8_t *idx_out, hipStream_t stream);
 
 /* Optional timing hook: when both events are non-NULL, kvq_decode_attention
  * records `begin` on its stream right before the stage-1 kernel and `end`

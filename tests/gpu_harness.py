@@ -5,9 +5,9 @@ from __future__ import annotations
 import numpy as np
 
 from bit_kv_cache_kivi_amd import inputs
-from layout_unpack import PT, WPT, gather_kivi, page_block, witcert_block
+from layout_unpack import PT, WPT, gather_kivi, page_block, witcert_block, witcert_paged_block
 
-SCHEME_ID = {"kivi2": 0, "kitty": 1, "witcert": 2, "kitty_dyn": 3, "kivi4": 4}
+SCHEME_ID = {"kivi2": 0, "kitty": 1, "witcert": 2, "kitty_dyn": 3, "kivi4": 4, "witcert_paged": 5}
 
 
 class Case:
@@ -36,13 +36,22 @@ class Case:
         if w.scheme == "kitty":
             self.idx = np.stack([O.kitty_select(inputs.kitty_calibration(w, h), w.nb)
                                  for h in range(w.Hkv)])
+        self.bypass = None                           # WitCert paging-safe: bypass mask per head
+        if w.scheme == "witcert_paged" and w.nb > 0:
+            self.bypass = np.stack([O.witcert_select_pairs(inputs.kitty_calibration(w, h), w.nb)
+                                    for h in range(w.Hkv)])
         layout = kvq.make_layout(w.scheme, w.B, w.Hq, w.Hkv, self.max_pages, self.n_pages,
                                  R=w.R, seed=self.seed, split_pages=split_pages, flags=flags,
-                                 sink=sink, nb=w.nb if w.nb else None)
+                                 sink=sink,
+                                 nb=w.nb if (w.nb or w.scheme == "witcert_paged") else None)
         self.cache = kvq.KVCache(layout, self.table, poison=poison)
-        if w.scheme == "kitty":
+        if w.scheme in ("kitty", "witcert_paged") and (w.scheme == "kitty" or w.nb > 0):
             calib = np.stack([inputs.kitty_calibration(w, h) for h in range(w.Hkv)])
-            self.cache.kitty_calibrate(torch.from_numpy(calib.view(np.float16)).cuda())
+            ct = torch.from_numpy(calib.view(np.float16)).cuda()
+            if w.scheme == "kitty":
+                self.cache.kitty_calibrate(ct)
+            else:
+                self.cache.witcert_calibrate(ct)
         # prefill, one request at a time (host inputs drawn by a thread pool)
         def gen(b):
             K = np.stack([inputs.context_kv(w, b, h)[0] for h in range(w.Hkv)])
@@ -59,9 +68,14 @@ class Case:
         # oracle streams for the sampled (request, KV head) pairs
         self.streams = {}
         for b, h in self.sample:
+            idx, slots = (None if self.idx is None else self.idx[h]), None
+            if w.scheme == "witcert_paged":
+                idx = None if self.bypass is None else self.bypass[h]
+                t = np.arange(self.cap)
+                slots = (self.table[b][t // PT].astype(np.uint64) * PT + (t % PT)).astype(np.uint64)
             s = O.Stream(self.sid, self.cap, D=128, G=w.G, R=w.R, VG=w.VG, BLK=w.BLK,
-                         nb=w.nb, idx=None if self.idx is None else self.idx[h],
-                         seed=self.seed, req=b, layer=0, kvh=h, sel=PT, sink=sink)
+                         nb=w.nb, idx=idx, seed=self.seed, req=b, layer=0, kvh=h, sel=PT,
+                         sink=sink, slots=slots)
             K, V = inputs.context_kv(w, b, h)
             s.prefill(K, V)
             self.streams[(b, h)] = s
@@ -126,9 +140,11 @@ class Case:
     def check_store(self):
         """Bit-exact codes, statistics and fp16 windows against the oracle."""
         pool = self.cache.pool.cpu().numpy()
+        w = self.w
+        if w.scheme == "witcert_paged":
+            return self._check_store_paged(pool)
         rk = self.cache.res_k.cpu().numpy().view(np.uint16)
         rv = self.cache.res_v.cpu().numpy().view(np.uint16)
-        w = self.w
         for (b, h), s in self.streams.items():
             l, n_kq, n_vq = s.state
             Kraw, Vraw = self._raw(s, l)
@@ -174,6 +190,30 @@ class Case:
             assert np.array_equal(rk[b, h, :l - n_kq], Kraw[n_kq:l]), ("key residual", b, h)
             for t in range(n_vq, l):
                 assert np.array_equal(rv[b, h, t % w.R], Vraw[t]), ("value window", b, h, t)
+
+    def _check_store_paged(self, pool):
+        """WitCert paging-safe: every token's int8 codes, group scales and
+        bypass row against the oracle, bit for bit."""
+        w = self.w
+        for (b, h), s in self.streams.items():
+            l, n_kq, _ = s.state
+            assert n_kq == l
+            Kraw, _ = self._raw(s, l)
+            okc, ovc = s.key_codes().view(np.int8), s.value_codes().view(np.int8)
+            oks, _ = s.key_stats()
+            ovs, _ = s.value_stats()
+            for p in range((l + PT - 1) // PT):
+                n = min(PT, l - p * PT)
+                kc, ks, vc, vs, kb = witcert_paged_block(
+                    page_block(pool, int(self.table[b, p]), h, w.Hkv, 5, w.nb), w.nb)
+                sl = slice(p * PT, p * PT + n)
+                assert np.array_equal(kc[:n], okc[sl]), ("key codes", b, h, p)
+                assert np.array_equal(vc[:n], ovc[sl]), ("value codes", b, h, p)
+                assert np.array_equal(ks[:n], oks[sl]) and np.array_equal(vs[:n], ovs[sl]), \
+                    ("scales", b, h, p)
+                if self.bypass is not None:
+                    ch = np.nonzero(self.bypass[h])[0]          # offsets in ascending channel order
+                    assert np.array_equal(kb[:n, :len(ch)], Kraw[sl][:, ch]), ("bypass row", b, h, p)
 
     def _raw(self, s, l):
         # raw fp16 history, rebuilt from the seeded inputs

@@ -13,7 +13,12 @@ WPT = 256
 def geom(scheme: int, nb: int = 16) -> dict:
     """Block layout: KIVI-2 (0), Kitty (1, nb boosted channels: one 256-B high
     plane per 16), WitCert (2), Kitty dynamic (3: Kitty + the page's nb
-    channel ids, at least 16 bytes), KIVI-4 (4: 4-bit key and value codes)."""
+    channel ids, at least 16 bytes), KIVI-4 (4: 4-bit key and value codes),
+    WitCert paging-safe (5: per-token int8 rows, scales per 32-channel group,
+    an 8-entry fp16 bypass row per token when nb pairs > 0)."""
+    if scheme == 5:
+        return dict(kc=0, vc=8192, ks=16384, vs=16896, kb=17408,
+                    bytes=17408 + (1024 if nb > 0 else 0), tokens=PT)
     if scheme == 4:
         return dict(kc=0, kh=0, ks=4096, vc=5120, vs=9216, bytes=10240, tokens=PT)
     if scheme == 0:
@@ -146,6 +151,18 @@ def value_stats(block: np.ndarray, scheme: int, nb: int = 16):
     g = geom(scheme, nb)
     vs = _u32(block, g["vs"], 256).reshape(64, 4)
     return (vs & 0xFFFF).astype(np.uint16), (vs >> 16).astype(np.uint16)
+
+
+def witcert_paged_block(block: np.ndarray, nb: int):
+    """(key codes int8 [64][128], key scales [64][4], value codes, value
+    scales, bypass rows fp16 [64][8] or None)."""
+    g = geom(5, nb)
+    kc = block[g["kc"]:g["kc"] + PT * D].view(np.int8).reshape(PT, D)
+    vc = block[g["vc"]:g["vc"] + PT * D].view(np.int8).reshape(PT, D)
+    ks = block[g["ks"]:g["ks"] + PT * 8].view(np.uint16).reshape(PT, 4)
+    vs = block[g["vs"]:g["vs"] + PT * 8].view(np.uint16).reshape(PT, 4)
+    kb = block[g["kb"]:g["kb"] + PT * 16].view(np.uint16).reshape(PT, 8) if nb > 0 else None
+    return kc, ks, vc, vs, kb
 
 
 def witcert_block(block: np.ndarray):

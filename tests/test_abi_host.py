@@ -59,14 +59,14 @@ def set_layout(K, L, B=None):
     return rc, cache
 
 
-@pytest.mark.parametrize("scheme", ["kivi2", "kitty", "witcert", "kitty_dyn", "kivi4"])
+@pytest.mark.parametrize("scheme", ["kivi2", "kitty", "witcert", "kitty_dyn", "kivi4", "witcert_paged"])
 def test_valid_layouts(K, scheme):
     L = K.make_layout(scheme, B=64, Hq=32, Hkv=8, max_pages=512, n_pages=32768)
     rc, cache = set_layout(K, L)
     assert rc == K.KVQ_OK
     assert cache.page_tokens == (256 if scheme == "witcert" else 64)
     assert cache.page_bytes == {"kivi2": 6144, "kitty": 6400, "witcert": 66048,
-                                "kitty_dyn": 6416, "kivi4": 10240}[scheme]
+                                "kitty_dyn": 6416, "kivi4": 10240, "witcert_paged": 18432}[scheme]
 
 
 def test_page_geometry_and_bytes_per_token(K):
@@ -90,7 +90,7 @@ def test_page_geometry_and_bytes_per_token(K):
 INVALID = [
     ("head_dim", 64), ("n_kv_heads", 0), ("n_kv_heads", 65536), ("n_q_heads", 12),
     ("n_q_heads", 72), ("batch", 0), ("batch", 65536), ("max_pages", 0), ("n_pages", 0),
-    ("split_pages", -1), ("split_pages", 65), ("flags", 2), ("scheme", 5), ("scheme", -1),
+    ("split_pages", -1), ("split_pages", 65), ("flags", 2), ("scheme", 6), ("scheme", -1),
     ("group", 64), ("value_group", 16), ("residual", 96), ("residual", 100),
     ("residual", 0), ("residual", 320), ("n_boost", 4),
 ]
@@ -142,6 +142,53 @@ def test_kitty_and_witcert_fields(K):
     assert set_layout(K, L)[0] == K.KVQ_EINVAL
     L = K.make_layout("kivi2", B=1, Hq=24, Hkv=8, max_pages=8, n_pages=8)      # fine for KIVI-2
     assert set_layout(K, L)[0] == K.KVQ_OK
+
+
+def test_witcert_paged_bytes_match_the_page(K):
+    # WitCert certified deployment: 136 B per token, head and side at G_c = 32
+    # (K+V 272 B), and 16 B of fp16 bypass values for m = 4 pairs
+    import json
+    with open(os.path.join(ROOT, "tests", "golden", "witcert_paged.json")) as f:
+        g = json.load(f)
+    L = K.make_layout("witcert_paged", B=1, Hq=1, Hkv=1, max_pages=1, n_pages=1, nb=0)
+    assert K.bytes_per_token(L) == g["bytes_per_token_kv"]
+    L = K.make_layout("witcert_paged", B=1, Hq=1, Hkv=1, max_pages=1, n_pages=1, nb=g["m"])
+    assert K.bytes_per_token(L) == g["bytes_per_token_kv"] + g["bypass_bytes"]
+    assert K.page_tokens(L) == 64
+
+
+def test_witcert_paged_fields(K):
+    def lay(**kw):
+        args = dict(B=1, Hq=8, Hkv=2, max_pages=8, n_pages=8)
+        args.update(kw)
+        return K.make_layout("witcert_paged", **args)
+    for nb, want in ((0, K.KVQ_OK), (1, K.KVQ_OK), (4, K.KVQ_OK), (5, K.KVQ_EINVAL), (-1, K.KVQ_EINVAL)):
+        assert set_layout(K, lay(nb=nb))[0] == want, nb
+    assert set_layout(K, lay(Hq=6))[0] == K.KVQ_EINVAL              # 3 query heads per KV head
+    assert set_layout(K, lay(sink=16))[0] == K.KVQ_EINVAL
+    assert set_layout(K, lay(flags=K.FLAG_GENERIC_STAGE1))[0] == K.KVQ_EINVAL
+    assert set_layout(K, lay(layer=65536))[0] == K.KVQ_EINVAL
+    for field, value in (("group", 64), ("value_group", 16)):
+        L = lay()
+        setattr(L, field, value)
+        assert set_layout(K, L)[0] == K.KVQ_EINVAL
+    # no fp16 residual buffers; the bypass index only with bypassed pairs
+    assert set_layout(K, lay(), bufs(K, res_k=0, res_v=0))[0] == K.KVQ_OK
+    assert set_layout(K, lay(), bufs(K, boost_idx=0))[0] == K.KVQ_ENULL
+    assert set_layout(K, lay(nb=0), bufs(K, boost_idx=0))[0] == K.KVQ_OK
+    # default split 4 pages (256 tokens); no window chunks in the workspace
+    rc, cache = set_layout(K, lay(max_pages=100, n_pages=100))
+    assert rc == K.KVQ_OK and cache.split_pages == 4
+    assert K.kvq_workspace_bytes(cache) == 1 * 8 * 25 * (128 * 4 + 8) + 256
+    # calibration: the scheme and m > 0 are checked before any launch
+    lib = K.lib()
+    a = C.c_void_p(A256 + 0x20000)
+    assert lib.kvq_witcert_calibrate(C.byref(cache), a, 0, a, None) == K.KVQ_EINVAL
+    assert lib.kvq_witcert_calibrate(C.byref(cache), None, 8, a, None) == K.KVQ_ENULL
+    rc0, c0 = set_layout(K, lay(nb=0))
+    assert lib.kvq_witcert_calibrate(C.byref(c0), a, 8, a, None) == K.KVQ_EINVAL
+    rc2, c2 = set_layout(K, K.make_layout("kivi2", B=1, Hq=8, Hkv=2, max_pages=8, n_pages=8))
+    assert lib.kvq_witcert_calibrate(C.byref(c2), a, 8, a, None) == K.KVQ_EINVAL
 
 
 def test_kivi4_fields(K):
@@ -213,6 +260,7 @@ def test_calls_on_an_unset_cache_launch_nothing(K):
     assert lib.kvq_prefill(C.byref(cache), 0, 1, None, None, C.c_int64(1), None,
                            None) == K.KVQ_ENOLAYOUT
     assert lib.kvq_kitty_calibrate(C.byref(cache), None, 1, None, None) == K.KVQ_ENOLAYOUT
+    assert lib.kvq_witcert_calibrate(C.byref(cache), None, 1, None, None) == K.KVQ_ENOLAYOUT
     assert lib.kvq_append_token(None, None, None, None) == K.KVQ_ENULL
 
 

@@ -97,5 +97,9 @@ def test_gqa_sink32_b64_ctx8k_32k():
     _run(inputs.workload(7))
 
 
+def test_witcert_paged_b32_32q8kv_ctx16384_certificate():
+    _run(inputs.workload(10), kappa=2.0, cert_check=True)
+
+
 def test_witcert_b32_32q8kv_ctx16384_certificate():
     _run(inputs.workload(5), kappa=2.0, cert_check=True)

@@ -246,6 +246,49 @@ def test_kitty_dynamic_store_decode(Hq, Hkv, split):
     case.check_store()
 
 
+@pytest.mark.parametrize("Hq,Hkv,nb,split", [(8, 2, 4, 0), (2, 2, 4, 3), (4, 4, 0, 1), (16, 2, 2, 2),
+                                             (1, 1, 4, 64)])
+def test_witcert_paged_store_decode_certificate(Hq, Hkv, nb, split):
+    # every token quantized on write with slot-keyed dither: bit-exact codes,
+    # per-token group scales and bypass rows through prefill and appends that
+    # cross pages; decode and certificate to the tolerance
+    w = inputs.workload(10, B=3, Hq=Hq, Hkv=Hkv, ctx=(700, 1301, 2113), nb=nb)
+    case = _case(w, extra_tokens=200, split_pages=split)
+    if nb:
+        idx = case.cache.boost_idx.cpu().numpy()
+        assert np.array_equal((idx < 2 * nb).astype(np.uint8), case.bypass)
+        for h in range(Hkv):                          # offsets in ascending channel order
+            ch = np.nonzero(case.bypass[h])[0]
+            assert idx[h, ch].tolist() == list(range(2 * nb))
+    case.check_state()
+    case.check_store()
+    out, cert, q = case.decode_now(1, kappa=2.0)
+    _check_decode(case, out, cert, q, kappa=2.0, cert_check=True)
+    for i in range(130):
+        out, cert, q = case.step(decode=(i % 16 == 15 or i in (0, 1)), kappa=1.0)
+        if out is not None:
+            _check_decode(case, out, cert, q, kappa=1.0, cert_check=True)
+    case.check_status()
+    case.check_state()
+    case.check_store()
+
+
+@pytest.mark.parametrize("ctx", [(1,), (2,), (63,), (64,), (65,), (130,)])
+def test_witcert_paged_short_contexts(ctx):
+    w = inputs.workload(10, B=1, Hq=4, Hkv=1, ctx=ctx)
+    case = _case(w, extra_tokens=140, split_pages=1)
+    case.check_state()
+    case.check_store()
+    out, cert, q = case.decode_now(2, kappa=1.5)
+    _check_decode(case, out, cert, q, kappa=1.5, cert_check=True)
+    for i in range(70):
+        out, cert, q = case.step(decode=(i % 5 == 4 or i in (0, 1)), kappa=1.5)
+        if out is not None:
+            _check_decode(case, out, cert, q, kappa=1.5, cert_check=True)
+    case.check_status()
+    case.check_store()
+
+
 @pytest.mark.parametrize("Hq,Hkv", [(8, 2), (2, 2)])
 def test_witcert_store_decode_certificate(Hq, Hkv):
     w = inputs.workload(5, B=2, Hq=Hq, Hkv=Hkv, ctx=(700, 1024))
