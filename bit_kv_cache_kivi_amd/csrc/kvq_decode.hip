@@ -13,6 +13,8 @@
 // Folding: for a key group, q.k~ = sum_c (q_c s_c) code_c + sum_c q_c z_c;
 // for a value group, sum_t p_t v~_t = sum_t (p_t s_t) code_t + sum_t p_t z_t.
 // Only small integer codes are touched per element.
+#include <type_traits>
+
 #include "kvq_common.hpp"
 #include "kvq_kernels.hpp"
 
@@ -1514,8 +1516,9 @@ __global__ __launch_bounds__(64) void stage1_witcert_kernel(KParams P, const uin
 // lane cq < 2 nb adds q_c x_c for the bypass row's entry cq instead.
 // ---------------------------------------------------------------------------
 struct WtokSmem {
-    uint2 ks[PT], vs[PT];           // the page's key / value scales per token (4 fp16)
+    float ks[4][PT], vs[4][PT];
     float eu[PT][8];                // e^{u_t} per token and query head
+    float kb[8][PT];                // bypass row entries [entry][token]
     int inv[8];                     // bypass row entry -> channel
 };
 
@@ -1584,24 +1587,50 @@ __global__ __launch_bounds__(64) void stage1_witcert_paged_kernel(KParams P, con
     const float cc = sm_scale * sm_scale * (1.0f / 12.0f);
     const int gq = cq >> 3;                      // this lane's scale group
 
-    for (int p = p0; p < p1; p++) {
-        int pid = P.table[(size_t)b * P.max_pages + p];
-        if (pid < 0 || pid >= P.n_pages) {
+    // the split's page ids, one per lane (at most 64 pages)
+    const int np = p1 - p0;
+    int pid_l = lane < np ? P.table[(size_t)b * P.max_pages + p0 + lane] : 0;
+    {
+        const bool bad = lane < np && (pid_l < 0 || pid_l >= P.n_pages);
+        if (__any(bad)) {
             if (lane == 0) atomicOr(P.status, (uint32_t)KVQ_STATUS_UNMAPPED_PAGE);
-            pid = 0;                              // read page 0 instead; the result is flagged
+            pid_l = bad ? 0 : pid_l;              // read page 0 instead; the result is flagged
         }
+    }
+    // per-page rows of lane = token: key scales, value scales, bypass row;
+    // the next page's rows are loaded while the current page is processed
+    struct Rows { uint2 ks, vs; uint4 br; };
+    auto rows = [&](int i) {
+        Rows r;
+        const uint8_t *pg = cpage(P, __builtin_amdgcn_readlane(pid_l, i), h);
+        const bool ok = lane < min(PT, l - (p0 + i) * PT);
+        r.ks = ok ? *(const uint2 *)(pg + G.ks + 8 * lane) : make_uint2(0u, 0u);
+        r.vs = ok ? *(const uint2 *)(pg + G.vs + 8 * lane) : make_uint2(0u, 0u);
+        r.br = (ok && nbyp > 0) ? *(const uint4 *)(pg + G.kh + 16 * lane) : make_uint4(0u, 0u, 0u, 0u);
+        return r;
+    };
+    Rows cur = rows(0);
+    for (int pi = 0; pi < np; pi++) {
+        const int p = p0 + pi;
+        const int pid = __builtin_amdgcn_readlane(pid_l, pi);
         const uint8_t *page = cpage(P, pid, h);
         const int nvalid = min(PT, l - p * PT);
         lds_sync();                               // the previous page's LDS reads are done
         {
             // lane = token: scales and e^{u_t}
-            const bool ok = lane < nvalid;
-            const uint2 ksr = ok ? *(const uint2 *)(page + G.ks + 8 * lane) : make_uint2(0u, 0u);
-            const uint2 vsr = ok ? *(const uint2 *)(page + G.vs + 8 * lane) : make_uint2(0u, 0u);
-            sm.ks[lane] = ksr;
-            sm.vs[lane] = vsr;
+            const uint2 ksr = cur.ks, vsr = cur.vs;
             const float sg[4] = {h2f((uint16_t)(ksr.x & 0xffff)), h2f((uint16_t)(ksr.x >> 16)),
                                  h2f((uint16_t)(ksr.y & 0xffff)), h2f((uint16_t)(ksr.y >> 16))};
+            const float sv[4] = {h2f((uint16_t)(vsr.x & 0xffff)), h2f((uint16_t)(vsr.x >> 16)),
+                                 h2f((uint16_t)(vsr.y & 0xffff)), h2f((uint16_t)(vsr.y >> 16))};
+#pragma unroll
+            for (int g = 0; g < 4; g++) { sm.ks[g][lane] = sg[g]; sm.vs[g][lane] = sv[g]; }
+            if (nbyp > 0) {
+                const uint32_t bw[4] = {cur.br.x, cur.br.y, cur.br.z, cur.br.w};
+#pragma unroll
+                for (int e = 0; e < 8; e++)
+                    sm.kb[e][lane] = e < nbyp ? h2f((uint16_t)((bw[e >> 1] >> (16 * (e & 1))) & 0xffffu)) : 0.f;
+            }
 #pragma unroll
             for (int hh = 0; hh < QPK; hh++) {
                 float v2 = 0.f;
@@ -1610,24 +1639,20 @@ __global__ __launch_bounds__(64) void stage1_witcert_paged_kernel(KParams P, con
                 sm.eu[lane][hh] = exp2f(kappa * sqrtf(v2 * cc) * LOG2E);
             }
         }
+        if (pi + 1 < np) cur = rows(pi + 1);
         lds_sync();
         const int8_t *kcod = (const int8_t *)(page + G.kc);
         const int8_t *vcod = (const int8_t *)(page + G.vc);
-        const uint16_t *kbr = (const uint16_t *)(page + G.kh);
-        const uint64_t slot0 = (uint64_t)pid * PT;
-        for (int i = 0; 2 * i < nvalid; i++) {
-            const int t = 2 * i + tp;
-            const bool valid = t < nvalid;        // the page's last token may be odd
-            const uint64_t slot = slot0 + (uint64_t)t;
-            const U4 uk = philox4x32_10(U4{(uint32_t)slot, (uint32_t)cq, c2, (uint32_t)(slot >> 32)}, k0, k1);
-            const U4 uv = philox4x32_10(U4{(uint32_t)slot, (uint32_t)cq, c2, (uint32_t)(slot >> 32)}, k0, k1 ^ 1u);
-            const uint32_t kw = valid ? *(const uint32_t *)(kcod + (size_t)t * D + 4 * cq) : 0u;
-            const uint32_t vw = valid ? *(const uint32_t *)(vcod + (size_t)t * D + 4 * cq) : 0u;
-            const float kbv = (nbyp > 0 && valid) ? h2f(kbr[8 * t + (bslot ? cq : 0)]) : 0.f;
-            const uint2 ksr = sm.ks[t], vsr = sm.vs[t];
-            const uint32_t kss = gq < 2 ? ksr.x : ksr.y, vss = gq < 2 ? vsr.x : vsr.y;
-            const float ks = h2f((uint16_t)((gq & 1) ? (kss >> 16) : (kss & 0xffff)));
-            const float vs = h2f((uint16_t)((gq & 1) ? (vss >> 16) : (vss & 0xffff)));
+        const uint32_t slot_lo0 = (uint32_t)pid * (uint32_t)PT;
+        const uint32_t slot_hi = (uint32_t)((uint64_t)pid * PT >> 32);
+        auto token = [&](auto chk, int t, uint32_t kw, uint32_t vw) {
+            constexpr bool CHK = decltype(chk)::value;
+            const bool valid = !CHK || t < nvalid;
+            const uint32_t slot = slot_lo0 + (uint32_t)t;
+            const U4 uk = philox4x32_10(U4{slot, (uint32_t)cq, c2, slot_hi}, k0, k1);
+            const U4 uv = philox4x32_10(U4{slot, (uint32_t)cq, c2, slot_hi}, k0, k1 ^ 1u);
+            const float kbv = nbyp > 0 ? sm.kb[cq & 7][t] : 0.f;     // 0 past the page's tokens
+            const float ks = sm.ks[gq][t], vs = sm.vs[gq][t];
             const uint32_t ukw[4] = {uk.x, uk.y, uk.z, uk.w};
             const uint32_t uvw[4] = {uv.x, uv.y, uv.z, uv.w};
             float kx[4], vx[4];
@@ -1647,7 +1672,7 @@ __global__ __launch_bounds__(64) void stage1_witcert_paged_kernel(KParams P, con
 #pragma unroll
                 for (int e = 0; e < 4; e++) part = fmaf(qv[hh][e], kx[e], part);
                 float z2 = half_sum32(part) * qscale;
-                if (!valid) z2 = -INFINITY;
+                if (CHK && !valid) z2 = -INFINITY;
                 if (__any(z2 > m[hh] + LAZY_TAU)) {
                     const float mnew = fmaxf(m[hh], z2);
                     // a half-wave with no valid token yet keeps m = -inf
@@ -1664,7 +1689,21 @@ __global__ __launch_bounds__(64) void stage1_witcert_paged_kernel(KParams P, con
 #pragma unroll
                 for (int e = 0; e < 4; e++) o[hh][e] = fmaf(pr, vx[e], o[hh][e]);
             }
+        };
+        // every pair of tokens is whole except, for an odd count, the last
+        // codes of the next token in flight while one is processed; a token
+        // past the page's count has zero scales, so its codes read as 0
+        const uint32_t *kq = (const uint32_t *)(kcod + 4 * cq), *vq = (const uint32_t *)(vcod + 4 * cq);
+        uint32_t kwn = kq[tp * (D / 4)], vwn = vq[tp * (D / 4)];
+#pragma unroll 1
+        for (int i = 0; i < (nvalid >> 1); i++) {
+            const uint32_t kw = kwn, vw = vwn;
+            const int tn = min(2 * i + 2 + tp, PT - 1);
+            kwn = kq[tn * (D / 4)];
+            vwn = vq[tn * (D / 4)];
+            token(std::false_type{}, 2 * i + tp, kw, vw);
         }
+        if (nvalid & 1) token(std::true_type{}, (nvalid & ~1) + tp, kwn, vwn);
     }
     // combine the two token phases (lanes L and L ^ 32); the phase-0 half
     // always holds the split's first token
