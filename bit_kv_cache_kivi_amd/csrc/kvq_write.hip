@@ -39,9 +39,7 @@ __device__ inline uint64_t mag24(uint16_t h) {
 // its 64 tokens (the mean up to the fixed count; ties to the lower channel),
 // into bits4 / inv and the page's KI bytes (channel ids, ascending)
 __device__ void select_page_boost(const Geom &G, const uint16_t *src, uint8_t *page, int *inv,
-                                  uint8_t *bits4, int nb) {
-    __shared__ uint64_t imp[D];
-    const int tid = threadIdx.x;
+                                  uint8_t *bits4, int nb, uint64_t *imp, int tid) {
     if (tid < D) {
         uint64_t sum = 0;
         for (int t = 0; t < PT; t++) sum += mag24(src[(size_t)t * D + tid]);
@@ -67,11 +65,13 @@ __device__ void select_page_boost(const Geom &G, const uint16_t *src, uint8_t *p
     __syncthreads();
 }
 
+// tid: the thread's index among the page's 256 (a block may quantize several
+// pages side by side, each with its own LDS arrays; every thread of the block
+// calls this once, so the barriers match).
 __device__ void quant_key_page(const KParams &P, const Geom &G, const uint16_t *src,
                                uint8_t *page, int *inv, uint8_t *bits4,
-                               uint8_t (*codes)[D]) {
-    const int tid = threadIdx.x;
-    if (P.scheme == KVQ_SCHEME_KITTY_DYN) select_page_boost(G, src, page, inv, bits4, P.nb);
+                               uint8_t (*codes)[D], uint64_t *imp, int tid) {
+    if (P.scheme == KVQ_SCHEME_KITTY_DYN) select_page_boost(G, src, page, inv, bits4, P.nb, imp, tid);
     const int c = tid & 127;
     const int gi = tid >> 7;                         // group 0 or 1 of the page
     const bool four = P.scheme == KVQ_SCHEME_KIVI4;
@@ -136,9 +136,8 @@ __device__ void quant_key_page(const KParams &P, const Geom &G, const uint16_t *
 }
 
 // Kitty boost tables of KV head h in LDS: bits4[c] (channel takes 16 levels)
-// and inv[o] (channel of high-plane offset o).
-__device__ void load_boost(const KParams &P, int h, int *inv, uint8_t *bits4) {
-    const int tid = threadIdx.x;
+// and inv[o] (channel of high-plane offset o); tid as in quant_key_page.
+__device__ void load_boost(const KParams &P, int h, int *inv, uint8_t *bits4, int tid) {
     if (tid < NB_MAX) inv[tid] = 0;
     __syncthreads();
     if (tid < D) {
@@ -231,37 +230,39 @@ __global__ __launch_bounds__(64) void append_kivi_kernel(KParams P, const uint16
 }
 
 // ---------------------------------------------------------------------------
-// flush (KIVI2 / KITTY / KIVI4): 256 threads per (KV head, request)
+// flush (KIVI2 / KITTY / KIVI4): 256 threads per page of the residual (R / 64
+// pages, quantized side by side) per (KV head, request)
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void flush_kivi_kernel(KParams P) {
-    const int h = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
+constexpr int FLUSH_MAX_PAGES = 4;                   // R <= 256
+__global__ __launch_bounds__(256 * FLUSH_MAX_PAGES) void flush_kivi_kernel(KParams P) {
+    const int h = blockIdx.x, b = blockIdx.y;
+    const int pi = threadIdx.x >> 8, tid = threadIdx.x & 255;   // page of the residual, thread in it
     const Geom G = geom(P.scheme, P.nb);
     const size_t bh = (size_t)b * P.Hkv + h;
     int32_t *st = P.state + bh * 4;
     const int l = st[0], nkq = st[1];
     if (l - nkq != P.R) return;
-    __shared__ uint8_t codes[PT][D];
-    __shared__ int inv[NB_MAX];
-    __shared__ uint8_t bits4[D];
+    __shared__ uint8_t codes[FLUSH_MAX_PAGES][PT][D];
+    __shared__ int inv[FLUSH_MAX_PAGES][NB_MAX];
+    __shared__ uint8_t bits4[FLUSH_MAX_PAGES][D];
+    __shared__ uint64_t imp[FLUSH_MAX_PAGES][D];
     __shared__ int bad;
-    const int np = P.R / PT;
+    const int np = P.R / PT;                         // = blockDim.x / 256
     const int p0 = (nkq - P.sink) / PT;              // quantized positions count from the sink
-    if (tid == 0) {
+    if (threadIdx.x == 0) {
         bad = 0;
         for (int p = 0; p < np; p++)
             if (!page_ok(P, P.table[(size_t)b * P.max_pages + p0 + p])) bad = 1;
     }
-    load_boost(P, h, inv, bits4);                    // contains __syncthreads
+    load_boost(P, h, inv[pi], bits4[pi], tid);       // contains __syncthreads
     if (bad) {
-        if (tid == 0) atomicOr(P.status, (uint32_t)KVQ_STATUS_UNMAPPED_PAGE);
+        if (threadIdx.x == 0) atomicOr(P.status, (uint32_t)KVQ_STATUS_UNMAPPED_PAGE);
         return;
     }
-    for (int p = 0; p < np; p++) {
-        const int pid = P.table[(size_t)b * P.max_pages + p0 + p];
-        quant_key_page(P, G, P.res_k + (bh * P.R + (size_t)p * PT) * D, page_ptr(P, pid, h),
-                       inv, bits4, codes);
-    }
-    if (tid == 0) st[1] = nkq + P.R;
+    const int pid = P.table[(size_t)b * P.max_pages + p0 + pi];
+    quant_key_page(P, G, P.res_k + (bh * P.R + (size_t)pi * PT) * D, page_ptr(P, pid, h),
+                   inv[pi], bits4[pi], codes[pi], imp[pi], tid);
+    if (threadIdx.x == 0) st[1] = nkq + P.R;         // after the block's last barrier: all read nkq
 }
 
 // ---------------------------------------------------------------------------
@@ -327,9 +328,10 @@ __global__ __launch_bounds__(256) void prefill_kivi_kernel(KParams P, int req0,
     __shared__ uint8_t codes[PT][D];
     __shared__ int inv[NB_MAX];
     __shared__ uint8_t bits4[D];
-    load_boost(P, h, inv, bits4);
+    __shared__ uint64_t imp[D];
+    load_boost(P, h, inv, bits4, tid);
     if (t0 < nkq)                                    // nkq - S is a multiple of 128: whole page
-        quant_key_page(P, G, Ks + (size_t)t0 * D, page, inv, bits4, codes);
+        quant_key_page(P, G, Ks + (size_t)t0 * D, page, inv, bits4, codes, imp, tid);
     if (t0 < nvq) {
         // values, per token, groups of 32 channels: thread (token tl, group jv)
         const int tl = tid >> 2, jv = tid & 3;
@@ -817,7 +819,7 @@ hipError_t launch_flush(const KParams &P, hipStream_t s) {
     if (P.scheme == KVQ_SCHEME_WITCERT)
         flush_witcert_kernel<<<grid, 256, 0, s>>>(P);
     else
-        flush_kivi_kernel<<<grid, 256, 0, s>>>(P);
+        flush_kivi_kernel<<<grid, 256 * (P.R / PT), 0, s>>>(P);
     return hipGetLastError();
 }
 

@@ -289,6 +289,65 @@ def test_witcert_paged_short_contexts(ctx):
     case.check_store()
 
 
+def test_witcert_paged_prefix_sharing():
+    # two requests share the pages of a 512-token prefix (the same slots): the
+    # second request's prefill rewrites them with the same bytes, because a
+    # token's record depends only on its values and its slot; both requests
+    # decode to the oracle, each stream keyed by its own page table
+    import torch
+    from bit_kv_cache_kivi_amd import kvq
+    from oracle import oracle as O
+    w = inputs.workload(10, B=2, Hq=4, Hkv=2, ctx=(900, 1100))
+    shared, max_pages = 8, 20
+    table = np.zeros((2, max_pages), np.int32)
+    table[0] = np.arange(max_pages)
+    table[1, :shared] = np.arange(shared)
+    table[1, shared:] = max_pages + np.arange(max_pages - shared)
+    n_pages = 2 * max_pages
+    layout = kvq.make_layout("witcert_paged", 2, w.Hq, w.Hkv, max_pages, n_pages,
+                             seed=0x5EED_0000_0000_0000 | w.seed, split_pages=3, nb=w.nb)
+    cache = kvq.KVCache(layout, table, poison=True)
+    calib = np.stack([inputs.kitty_calibration(w, h) for h in range(w.Hkv)])
+    cache.witcert_calibrate(torch.from_numpy(calib.view(np.float16)).cuda())
+    masks = [O.witcert_select_pairs(calib[h], w.nb) for h in range(w.Hkv)]
+    K0 = np.stack([inputs.context_kv(w, 0, h)[0] for h in range(w.Hkv)])
+    V0 = np.stack([inputs.context_kv(w, 0, h)[1] for h in range(w.Hkv)])
+    K1 = np.stack([inputs.context_kv(w, 1, h)[0] for h in range(w.Hkv)])
+    V1 = np.stack([inputs.context_kv(w, 1, h)[1] for h in range(w.Hkv)])
+    P = shared * 64
+    K1[:, :P], V1[:, :P] = K0[:, :P], V0[:, :P]             # the shared prefix
+    ctx = (900, 1100)
+    for b, (K, V) in enumerate(((K0, V0), (K1, V1))):
+        cache.prefill(b, torch.from_numpy(K.view(np.float16)).cuda()[None].contiguous(),
+                      torch.from_numpy(V.view(np.float16)).cuda()[None].contiguous(),
+                      torch.tensor([ctx[b]], dtype=torch.int32, device="cuda"))
+        torch.cuda.synchronize()
+        if b == 0:
+            pool0 = cache.pool.cpu().numpy().copy()
+    pool1 = cache.pool.cpu().numpy()
+    pb = cache.page_bytes * w.Hkv
+    assert np.array_equal(pool1[:shared * pb], pool0[:shared * pb])    # rewritten identically
+    assert cache.status_word() == 0
+    q = inputs.step_q(w, 0)
+    out = torch.full((2, w.Hq, 128), float("nan"), dtype=torch.float32, device="cuda")
+    cert = torch.full((2, w.Hq), float("nan"), dtype=torch.float32, device="cuda")
+    cache.decode(torch.from_numpy(q.view(np.float16)).cuda(), out, cert, sm_scale=w.sm_scale,
+                 kappa=1.0)
+    torch.cuda.synchronize()
+    o, c = out.cpu().numpy(), cert.cpu().numpy()
+    g = w.group
+    for b, (K, V) in enumerate(((K0, V0), (K1, V1))):
+        t = np.arange(ctx[b] + 8)
+        slots = (table[b][t // 64].astype(np.uint64) * 64 + (t % 64)).astype(np.uint64)
+        for h in range(w.Hkv):
+            s = O.Stream(O.WITCERT_TOK, ctx[b] + 8, VG=32, idx=masks[h],
+                         seed=0x5EED_0000_0000_0000 | w.seed, req=b, layer=0, kvh=h, slots=slots)
+            s.prefill(K[h, :ctx[b]], V[h, :ctx[b]])
+            ref, rc = s.decode(q[b, h * g:(h + 1) * g], w.sm_scale, 1.0)
+            assert np.abs(o[b, h * g:(h + 1) * g] - ref).max() <= TOL_O, (b, h)
+            assert np.all(np.abs(c[b, h * g:(h + 1) * g] - rc) <= TOL_CERT * np.abs(rc))
+
+
 @pytest.mark.parametrize("Hq,Hkv", [(8, 2), (2, 2)])
 def test_witcert_store_decode_certificate(Hq, Hkv):
     w = inputs.workload(5, B=2, Hq=Hq, Hkv=Hkv, ctx=(700, 1024))
