@@ -377,3 +377,29 @@ def test_append_refuses_full_residual_and_flags():
     torch.cuda.synchronize()
     assert int(case.cache.status[0].item()) & 1
     assert torch.equal(case.cache.state, st0)
+
+
+def test_witcert_paged_capacity_and_unmapped_page_flags():
+    # WitCert paging-safe: an append past max_pages * 64 tokens sets CAPACITY,
+    # one into a page whose table entry is out of range sets UNMAPPED_PAGE;
+    # both leave the state as it was
+    import torch
+    from bit_kv_cache_kivi_amd import kvq
+    w = inputs.workload(10, B=1, Hq=4, Hkv=1, ctx=(128,))
+    k, v = inputs.step_kv(w, 0)
+    kt = torch.from_numpy(k.view(np.float16)).cuda()
+    vt = torch.from_numpy(v.view(np.float16)).cuda()
+    case = _case(w, extra_tokens=0, poison=False)           # capacity 2 pages = 128 tokens
+    st0 = case.cache.state.clone()
+    case.cache.append(kt, vt)
+    torch.cuda.synchronize()
+    assert int(case.cache.status[0].item()) == kvq.STATUS_CAPACITY
+    assert torch.equal(case.cache.state, st0)
+    # a table whose third entry is out of range: the 129th token has no page
+    case2 = _case(w, extra_tokens=64, poison=False)
+    case2.cache.page_table[0, 2] = 10 ** 6
+    st0 = case2.cache.state.clone()
+    case2.cache.append(kt, vt)
+    torch.cuda.synchronize()
+    assert int(case2.cache.status[0].item()) == kvq.STATUS_UNMAPPED_PAGE
+    assert torch.equal(case2.cache.state, st0)
