@@ -144,6 +144,23 @@ def test_kitty_and_witcert_fields(K):
     assert set_layout(K, L)[0] == K.KVQ_OK
 
 
+def test_byte_accounts_match_the_pages(K):
+    # Kitty: the high plane adds 2 bits per boosted channel, 2 + 2 alpha bits
+    # per key element; WitCert blocks: 128 int8 codes + an fp16 scale per
+    # 256-token block and channel = 129 B per token and side
+    import json
+    with open(os.path.join(ROOT, "tests", "golden", "byte_accounts.json")) as f:
+        g = json.load(f)
+    base = K.page_bytes(K.make_layout("kivi2", B=1, Hq=1, Hkv=1, max_pages=1, n_pages=1))
+    for alpha, bits in g["kitty_bits_per_key_element"].items():
+        nb = int(float(alpha) * 128)
+        L = K.make_layout("kitty", B=1, Hq=1, Hkv=1, max_pages=1, n_pages=1, nb=nb)
+        high_bits = (K.page_bytes(L) - base) * 8 / (64 * 128)   # per key element
+        assert 2 + high_bits == bits, (alpha, 2 + high_bits)
+    L = K.make_layout("witcert", B=1, Hq=1, Hkv=1, max_pages=1, n_pages=1)
+    assert K.bytes_per_token(L) == 2 * g["witcert_int8_bytes_per_token_per_side"]
+
+
 def test_witcert_paged_bytes_match_the_page(K):
     # WitCert certified deployment: 136 B per token, head and side at G_c = 32
     # (K+V 272 B), and 16 B of fp16 bypass values for m = 4 pairs
