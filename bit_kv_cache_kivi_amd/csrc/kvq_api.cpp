@@ -162,12 +162,12 @@ int kvq_set_layout(kvq_cache_t *cache, const kvq_layout_t *layout, const kvq_buf
     cache->page_bytes = G.bytes;
     int sp = layout->split_pages;
     if (sp == 0) {
-        // default: one 256-token block per split for WITCERT; 8 pages for
-        // short caches, 12 for longer ones (fewer partials to merge, enough
-        // splits to fill the chip), at least what keeps <= 256 splits
+        // default: one 256-token block per split for WITCERT; 4 pages for
+        // short caches (more splits to fill the chip), 12 for longer ones
+        // (fewer partials to merge), at least what keeps <= 256 splits
         sp = layout->scheme == KVQ_SCHEME_WITCERT ? 1
              : wtok                                 ? 4      // 256 tokens, as one WITCERT block
-             : (layout->max_pages <= 128 ? 8 : 12);
+             : (layout->max_pages <= 128 ? 4 : 12);
         sp = std::max(sp, (layout->max_pages + 255) / 256);
     }
     // the merge takes at most 256 splits per query head

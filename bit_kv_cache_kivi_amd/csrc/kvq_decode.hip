@@ -1757,7 +1757,7 @@ __global__ __launch_bounds__(64) void merge_kernel(KParams P, float *__restrict_
 
     // output rows: lane = (entry parity ph, channel quad c4); the first 32
     // entries' loads go out with the log-sum-exp reads
-    constexpr int BATCH = 16;
+    constexpr int BATCH = 24;                // 48 entries per batch: one for caches up to ~540 pages
     const int ph = lane >> 5, c4 = lane & 31;
     float4 ov[BATCH];
 #pragma unroll

@@ -139,7 +139,7 @@ typedef struct kvq_layout {
                                 m, 0 .. 4; 0 for others */
     int32_t max_pages;       /* page-table row length per request */
     int32_t n_pages;         /* pages in the pool */
-    int32_t split_pages;     /* stage-1 split size in pages; 0: 8 when max_pages
+    int32_t split_pages;     /* stage-1 split size in pages; 0: 4 when max_pages
                                 <= 128, else 12 (1 for WITCERT, 4 for
                                 WITCERT_PAGED), raised to ceil(max_pages /
                                 256) where that is larger */

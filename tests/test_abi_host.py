@@ -246,9 +246,9 @@ def test_null_and_alignment(K):
 
 
 def test_split_resolution_and_workspace(K):
-    # default split: 8 pages up to 128 pages of cache, 12 above (1 for
+    # default split: 4 pages up to 128 pages of cache, 12 above (1 for
     # WITCERT's 256-token pages), raised to what keeps at most 256 splits
-    for scheme, max_pages, want in (("kivi2", 100, 8), ("kivi2", 128, 8), ("kitty", 129, 12),
+    for scheme, max_pages, want in (("kivi2", 100, 4), ("kivi2", 128, 4), ("kitty", 129, 12),
                                     ("kivi2", 512, 12), ("kivi2", 3072, 12), ("kivi2", 3073, 13),
                                     ("kivi2", 4096, 16), ("kivi2", 16384, 64), ("witcert", 64, 1),
                                     ("witcert", 1024, 4)):
