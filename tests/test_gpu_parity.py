@@ -50,7 +50,8 @@ def _check_decode(case, out, cert, q, kappa=0.0, cert_check=False):
     return worst
 
 
-@pytest.mark.parametrize("Hq,Hkv,flags", [(2, 2, 0), (2, 2, 1), (8, 2, 0), (8, 2, 1), (16, 4, 0), (6, 3, 0)])
+@pytest.mark.parametrize("Hq,Hkv,flags", [(2, 2, 0), (2, 2, 1), (8, 2, 0), (8, 2, 1), (16, 4, 0), (6, 3, 0),
+                                           (16, 2, 0), (16, 2, 1)])
 def test_kivi_prefill_decode_small(Hq, Hkv, flags):
     # flags 0: matrix-core stage 1 (group of 4: one wave per KV head; other
     # group sizes: one wave per query head); flags 1: the VALU stage 1
@@ -203,6 +204,28 @@ def test_kivi4_store_decode(Hq, Hkv, split):
     _check_decode(case, out, cert, q)
     for i in range(260):
         out, cert, q = case.step(decode=(i % 64 == 63 or i in (0, 1, 127, 128)))
+        if out is not None:
+            _check_decode(case, out, cert, q)
+    case.check_status()
+    case.check_state()
+    case.check_store()
+
+
+@pytest.mark.parametrize("R", [64, 192, 256])
+@pytest.mark.parametrize("wid,Hq,Hkv", [(3, 8, 2), (2, 2, 2), (4, 4, 1), (9, 2, 1)])
+def test_residual_sizes(R, wid, Hq, Hkv):
+    # fp16 windows of 64, 192 and 256 tokens (one to four pages flushed at
+    # once, as many window chunks): bit-exact store through prefill and
+    # flushes, decode to the tolerance, for the group-of-4 kernel, the
+    # one-query-head kernel, Kitty and KIVI-4
+    w = inputs.workload(wid, B=2, Hq=Hq, Hkv=Hkv, ctx=(700, R + 37), R=R)
+    case = _case(w, extra_tokens=2 * R + 40, split_pages=3)
+    case.check_state()
+    case.check_store()
+    out, cert, q = case.decode_now(1)
+    _check_decode(case, out, cert, q)
+    for i in range(2 * R + 20):
+        out, cert, q = case.step(decode=(i % 37 == 36 or i in (0, R - 1, R)))
         if out is not None:
             _check_decode(case, out, cert, q)
     case.check_status()
