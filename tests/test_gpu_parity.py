@@ -212,7 +212,7 @@ def test_kivi4_store_decode(Hq, Hkv, split):
 
 
 @pytest.mark.parametrize("R", [64, 192, 256])
-@pytest.mark.parametrize("wid,Hq,Hkv", [(3, 8, 2), (2, 2, 2), (4, 4, 1), (9, 2, 1)])
+@pytest.mark.parametrize("wid,Hq,Hkv", [(3, 8, 2), (2, 2, 2), (4, 4, 1), (9, 2, 1), (6, 4, 1), (8, 2, 2)])
 def test_residual_sizes(R, wid, Hq, Hkv):
     # fp16 windows of 64, 192 and 256 tokens (one to four pages flushed at
     # once, as many window chunks): bit-exact store through prefill and
@@ -426,3 +426,44 @@ def test_witcert_paged_capacity_and_unmapped_page_flags():
     torch.cuda.synchronize()
     assert int(case2.cache.status[0].item()) == kvq.STATUS_UNMAPPED_PAGE
     assert torch.equal(case2.cache.state, st0)
+
+
+@pytest.mark.parametrize("wid,Hq,Hkv,flags", [(3, 8, 2, 0), (2, 2, 2, 0), (2, 2, 2, 1), (5, 8, 2, 0),
+                                              (10, 8, 2, 0)])
+def test_decode_flags_unmapped_page(wid, Hq, Hkv, flags):
+    # a page-table entry of the quantized prefix out of range: decode reads
+    # another page instead (never the entry), sets UNMAPPED_PAGE and still
+    # writes finite outputs for every query head
+    import torch
+    from bit_kv_cache_kivi_amd import kvq
+    ctx = (1500, 1500) if wid != 5 else (1300, 1300)
+    w = inputs.workload(wid, B=2, Hq=Hq, Hkv=Hkv, ctx=ctx)
+    case = _case(w, extra_tokens=64, split_pages=2, poison=False, flags=flags)
+    case.check_status()
+    case.cache.page_table[1, 1] = case.n_pages + 5           # inside the quantized prefix
+    torch.cuda.synchronize()
+    out, cert, q = case.decode_now(0, kappa=1.0)
+    assert int(case.cache.status[0].item()) == kvq.STATUS_UNMAPPED_PAGE
+    assert torch.isfinite(out).all()
+    # request 0 does not touch the entry: its outputs still match the oracle
+    g = w.group
+    for (b, h) in case.streams:
+        if b != 0:
+            continue
+        ref, _ = case.oracle_decode(q, b, h, 1.0)
+        assert np.abs(out.cpu().numpy()[b, h * g:(h + 1) * g] - ref).max() <= TOL_O
+
+
+def test_prefill_flags_bad_length():
+    # a prefill length beyond the capacity sets BAD_LENGTH and writes nothing
+    import torch
+    from bit_kv_cache_kivi_amd import kvq
+    w = inputs.workload(3, B=1, Hq=4, Hkv=1, ctx=(300,))
+    case = _case(w, extra_tokens=0, poison=False)            # capacity 320 tokens
+    pool0 = case.cache.pool.clone()
+    state0 = case.cache.state.clone()
+    K = torch.zeros((1, 1, 400, 128), dtype=torch.float16, device="cuda")
+    case.cache.prefill(0, K, K, torch.tensor([400], dtype=torch.int32, device="cuda"))
+    torch.cuda.synchronize()
+    assert int(case.cache.status[0].item()) == kvq.STATUS_BAD_LENGTH
+    assert torch.equal(case.cache.pool, pool0) and torch.equal(case.cache.state, state0)
