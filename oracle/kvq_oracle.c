@@ -518,7 +518,7 @@ static void quant_value_token(ko_stream *s, long t)
 }
 
 /* [WITCERT]: a completed block of BLK tokens is quantized channel by channel
- * (per-256-token-block, per-channel scale), keys and values alike. */
+ * (one scale per 256-token block and channel), keys and values alike. */
 static void quant_witcert_block(ko_stream *s, long b)
 {
     float *xi = (float *)malloc(sizeof(float) * (size_t)s->BLK);
