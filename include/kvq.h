@@ -52,8 +52,8 @@
  *                      stored fp16 and left out of their group's amax; the
  *                      certificate uses each token's group scales (a
  *                      bypassed channel adds no error).  136 B per token and
- *                      side + 16 B when m > 0.  ("WitCert" page, certified-deployment
- *                      paragraphs.)
+ *                      side + 16 B when m > 0.  ("WitCert" page, the
+ *                      certified-deployment paragraphs.)
  *
  * Step order per decode step (all calls asynchronous on the caller's stream,
  * none synchronizes, allocates or frees, so a step can be captured in a HIP
