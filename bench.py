@@ -392,7 +392,7 @@ def main():
         print(json.dumps({"copy_bytes": x.numel() * 4, "copies": 3}))
         return
     if args.gpus != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
+        print("bench.py measures one GPU only: the library has no multi-GPU path "
               "(--gpus must be 1)", file=sys.stderr)
         sys.exit(2)
     w = inputs.workload(args.workload)
