@@ -467,3 +467,24 @@ def test_prefill_flags_bad_length():
     torch.cuda.synchronize()
     assert int(case.cache.status[0].item()) == kvq.STATUS_BAD_LENGTH
     assert torch.equal(case.cache.pool, pool0) and torch.equal(case.cache.state, state0)
+
+
+@pytest.mark.parametrize("wid,Hq,Hkv", [(2, 2, 2), (3, 8, 2), (4, 2, 2), (5, 8, 2), (6, 4, 1), (7, 8, 2),
+                                        (9, 4, 2), (10, 8, 2)])
+def test_empty_request_decodes_to_zero_then_grows(wid, Hq, Hkv):
+    # request 1 holds no token: attention over an empty set is taken as a zero
+    # output, a zero certificate and no effect on the other request; then it
+    # receives its first tokens through the ordinary step (request 0 keeps its
+    # context: the calibration slice of the boosted or bypassed channels is
+    # drawn from it)
+    w = inputs.workload(wid, B=2, Hq=Hq, Hkv=Hkv, ctx=(300, 0))
+    case = _case(w, extra_tokens=64, split_pages=2)
+    case.check_status()
+    out, cert, q = case.decode_now(3, kappa=1.0)
+    assert np.all(out.cpu().numpy()[1] == 0.0) and np.all(cert.cpu().numpy()[1] == 0.0)
+    wit = w.scheme in ("witcert", "witcert_paged")
+    _check_decode(case, out, cert, q, kappa=1.0, cert_check=wit)
+    for i in range(3):
+        out, cert, q = case.step(kappa=1.0)
+        _check_decode(case, out, cert, q, kappa=1.0, cert_check=wit)
+    case.check_status()
