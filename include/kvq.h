@@ -248,8 +248,18 @@ int kvq_flush_key_group(const kvq_cache_t *cache, hipStream_t stream);
  * h / (n_q_heads / n_kv_heads).  workspace: device, >= kvq_workspace_bytes().
  * Stage 1 splits the tokens whose key and value are both quantized; stage 2
  * attends to the fp16 window and merges all partials with log-sum-exp
- * weights ("WitCert" Key structure).  Returns KVQ_EWORKSPACE if ws_bytes is too
- * small. */
+ * weights ("WitCert" Key structure).  A request with no token gets a zero
+ * output row and a zero certificate.  Returns KVQ_EWORKSPACE if ws_bytes is
+ * too small.
+ * Range of the matrix-core stage 1 (KIVI2, KITTY, KITTY_DYN and KIVI4
+ * without KVQ_FLAG_GENERIC_STAGE1): it feeds q_c s_c (key scales) and p_t s_t
+ * (value scales, with softmax weights p_t <= 256 by the lazily moved
+ * maximum) to f16 products as a head plus remainder pair, so the stated
+ * accuracy needs |q_c s_c| < 65504 and every value scale s_t <= 255 (a
+ * value group spanning at most 765 for 2-bit codes, 3825 for 4-bit);
+ * beyond that the output is unspecified and may be non-finite.  The fp16
+ * window, the VALU stage 1 and the WITCERT schemes compute in binary32 and
+ * have no such limit. */
 int kvq_decode_attention(const kvq_cache_t *cache, const uint16_t *q, float *out,
                          float *cert, float sm_scale, float kappa,
                          void *workspace, size_t ws_bytes, hipStream_t stream);
