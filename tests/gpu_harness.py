@@ -14,12 +14,14 @@ class Case:
     """One workload on the GPU plus its oracle streams."""
 
     def __init__(self, w: inputs.Workload, extra_tokens: int = 0, split_pages: int = 0,
-                 poison: bool = True, sample=None, flags: int = 0, sink: int | None = None):
+                 poison: bool = True, sample=None, flags: int = 0, sink: int | None = None,
+                 kv_scale=(1.0, 1.0)):
         import torch
         from bit_kv_cache_kivi_amd import kvq
         from oracle import oracle as O
         self.torch, self.kvq, self.O = torch, kvq, O
         self.w = w
+        self.kv_scale = kv_scale
         sink = w.sink if sink is None else sink
         self.S = sink
         self.sid = SCHEME_ID[w.scheme]
@@ -54,8 +56,8 @@ class Case:
                 self.cache.witcert_calibrate(ct)
         # prefill, one request at a time (host inputs drawn by a thread pool)
         def gen(b):
-            K = np.stack([inputs.context_kv(w, b, h)[0] for h in range(w.Hkv)])
-            V = np.stack([inputs.context_kv(w, b, h)[1] for h in range(w.Hkv)])
+            K = np.stack([self._kv(*inputs.context_kv(w, b, h))[0] for h in range(w.Hkv)])
+            V = np.stack([self._kv(*inputs.context_kv(w, b, h))[1] for h in range(w.Hkv)])
             return K, V
         import concurrent.futures as cf
         with cf.ThreadPoolExecutor(min(16, w.B)) as ex:
@@ -78,10 +80,20 @@ class Case:
             s = O.Stream(self.sid, self.cap, D=128, G=w.G, R=w.R, VG=w.VG, BLK=w.BLK,
                          nb=w.nb, idx=idx, seed=self.seed, req=b, layer=0, kvh=h, sel=PT,
                          sink=sink, slots=slots)
-            K, V = inputs.context_kv(w, b, h)
+            K, V = self._kv(*inputs.context_kv(w, b, h))
             s.prefill(K, V)
             self.streams[(b, h)] = s
         self.steps_done = 0
+
+    def _kv(self, K, V):
+        """The generated fp16 keys and values times the case's kv_scale (the
+        same fp16 arrays go to the GPU and to the oracle)."""
+        ks, vs = self.kv_scale
+        def sc(x, f):
+            if f == 1.0:
+                return x
+            return (x.view(np.float16).astype(np.float32) * np.float32(f)).astype(np.float16).view(np.uint16)
+        return sc(K, ks), sc(V, vs)
 
     @property
     def seed(self) -> int:
@@ -94,7 +106,7 @@ class Case:
         torch = self.torch
         w = self.w
         step_id = self.steps_done
-        k, v = inputs.step_kv(w, step_id)
+        k, v = self._kv(*inputs.step_kv(w, step_id))
         q = inputs.step_q(w, step_id)
         self.cache.flush()
         kt = torch.from_numpy(k.view(np.float16)).cuda()
@@ -220,10 +232,10 @@ class Case:
     def _raw(self, s, l):
         # raw fp16 history, rebuilt from the seeded inputs
         b, h = [k for k, v in self.streams.items() if v is s][0]
-        K0, V0 = inputs.context_kv(self.w, b, h)
+        K0, V0 = self._kv(*inputs.context_kv(self.w, b, h))
         ks, vs = [K0], [V0]
         for i in range(self.steps_done):
-            k, v = inputs.step_kv(self.w, i)
+            k, v = self._kv(*inputs.step_kv(self.w, i))
             ks.append(k[b, h][None])
             vs.append(v[b, h][None])
         return np.concatenate(ks)[:l], np.concatenate(vs)[:l]

@@ -488,3 +488,30 @@ def test_empty_request_decodes_to_zero_then_grows(wid, Hq, Hkv):
         out, cert, q = case.step(kappa=1.0)
         _check_decode(case, out, cert, q, kappa=1.0, cert_check=wit)
     case.check_status()
+
+
+@pytest.mark.parametrize("KS,VS", [(1.0, 60.0), (20.0, 1.0)])
+@pytest.mark.parametrize("wid,Hq,Hkv", [(3, 8, 2), (2, 2, 2), (4, 2, 2), (9, 2, 2), (6, 4, 1)])
+def test_large_magnitudes_inside_the_operand_range(wid, Hq, Hkv, KS, VS):
+    # values x60: value scales up to ~150, inside the P.V operands' range
+    # (at most 255); keys x20: |q s| up to ~3300 and scores twenty times wider
+    # (|q s| below 65504).  Errors grow with the values (the output's scale)
+    # and with the keys (the scores' scale), so the bound is 1e-5 x KS x VS.
+    w = inputs.workload(wid, B=2, Hq=Hq, Hkv=Hkv, ctx=(700, 1129))
+    case = _case(w, extra_tokens=160, split_pages=3, kv_scale=(KS, VS))
+    case.check_state()
+    case.check_store()
+    g = w.group
+    tol = TOL_O * KS * VS
+    for i in range(130):                        # crosses a key flush
+        out, cert, q = case.step(decode=(i % 43 == 42 or i in (0, 129)))
+        if out is None:
+            continue
+        o = out.cpu().numpy()
+        for (b, h) in case.streams:
+            ref, _ = case.oracle_decode(q, b, h)
+            got = o[b, h * g:(h + 1) * g].astype(np.float64)
+            assert np.all(np.isfinite(got)), (b, h)
+            assert np.abs(got - ref).max() <= tol, (b, h, np.abs(got - ref).max())
+    case.check_store()
+    case.check_status()
