@@ -79,15 +79,17 @@ __device__ inline void lds_sync() {
 // Loads through a buffer descriptor of a page's own extent.  With valid false
 // the extent is zero: the loads return zeros and touch no memory, so a loop
 // can issue them unconditionally (the wait counts stay exact and the
-// prefetched pages stay in flight).
+// prefetched pages stay in flight).  Page loads carry the non-temporal hint:
+// every page is read once per step, so the caches should not keep it.
+constexpr int LOAD_NT = 2;          // cache-policy bit of a buffer load: nt
 __device__ inline __amdgpu_buffer_rsrc_t page_rsrc(const uint8_t *page, bool valid, const Geom &G) {
     return __builtin_amdgcn_make_buffer_rsrc((void *)page, (short)0, valid ? G.bytes : 0, 0x00020000);
 }
 __device__ inline uint4 bload(__amdgpu_buffer_rsrc_t rs, int off) {
-    return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0));
+    return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, LOAD_NT));
 }
 __device__ inline uint32_t bload1(__amdgpu_buffer_rsrc_t rs, int off) {
-    return __builtin_amdgcn_raw_buffer_load_b32(rs, off, 0, 0);
+    return __builtin_amdgcn_raw_buffer_load_b32(rs, off, 0, LOAD_NT);
 }
 
 __device__ inline float half_lo(uint32_t v) { return h2f((uint16_t)(v & 0xffffu)); }
@@ -691,12 +693,68 @@ __device__ inline void mul_split2(float x0, _Float16 y0, float x1, _Float16 y1, 
     lo = rem_pair(a0, a1, hi);
 }
 
+// hi + lo of the two products q0 s0 and q1 s1 (q0, q1 the f16 halves of q;
+// s0, s1 the f16 in the low halves of their registers): hi = fl16(q s) and
+// lo = fl16(q s - hi), each formed from the exact product by one
+// mixed-precision fused multiply-add.
+__device__ inline void split_qs(uint32_t q, uint32_t s0, uint32_t s1, uint32_t &hi, uint32_t &lo) {
+    uint32_t h, l;
+    asm("v_fma_mixlo_f16 %0, %1, %2, 0 op_sel_hi:[1,1,0]" : "=&v"(h) : "v"(q), "v"(s0));
+    asm("v_fma_mixhi_f16 %0, %1, %2, 0 op_sel:[1,0,0] op_sel_hi:[1,1,0]" : "+v"(h) : "v"(q), "v"(s1));
+    asm("v_fma_mixlo_f16 %0, %1, %2, -%3 op_sel_hi:[1,1,1]" : "=&v"(l) : "v"(q), "v"(s0), "v"(h));
+    asm("v_fma_mixhi_f16 %0, %1, %2, -%3 op_sel:[1,0,1] op_sel_hi:[1,1,1]" : "+v"(l) : "v"(q), "v"(s1), "v"(h));
+    hi = h;
+    lo = l;
+}
+
+// The same for p s0 and p s1 with p binary32: hi = fl16(p s), lo = fl16(p s -
+// hi) from the fused products, so hi + lo is p s to within ~2^-22 of it.
+__device__ inline void split_ps(float p, uint32_t s0, uint32_t s1, uint32_t &hi, uint32_t &lo) {
+    uint32_t h, l;
+    asm("v_fma_mixlo_f16 %0, %1, %2, 0 op_sel_hi:[0,1,0]" : "=&v"(h) : "v"(p), "v"(s0));
+    asm("v_fma_mixhi_f16 %0, %1, %2, 0 op_sel_hi:[0,1,0]" : "+v"(h) : "v"(p), "v"(s1));
+    asm("v_fma_mixlo_f16 %0, %1, %2, -%3 op_sel_hi:[0,1,1]" : "=&v"(l) : "v"(p), "v"(s0), "v"(h));
+    asm("v_fma_mixhi_f16 %0, %1, %2, -%3 op_sel:[0,0,1] op_sel_hi:[0,1,1]" : "+v"(l) : "v"(p), "v"(s1), "v"(h));
+    hi = h;
+    lo = l;
+}
+
+// acc + q z in binary32 (exact product): q the f16 in half QH of its
+// register, z the f16 in the high half of its own (a key group's {s, z})
+template <int QH>
+__device__ inline float fma_qz(uint32_t q, uint32_t z, float acc) {
+    float d;
+    if constexpr (QH == 0)
+        asm("v_fma_mix_f32 %0, %1, %2, %3 op_sel:[0,1,0] op_sel_hi:[1,1,0]" : "=v"(d) : "v"(q), "v"(z), "v"(acc));
+    else
+        asm("v_fma_mix_f32 %0, %1, %2, %3 op_sel:[1,1,0] op_sel_hi:[1,1,0]" : "=v"(d) : "v"(q), "v"(z), "v"(acc));
+    return d;
+}
+
+template <int CTRL>
+__device__ inline float dppf(float x) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0u, __builtin_bit_cast(uint32_t, x), CTRL, 0xf, 0xf, true));
+}
+
 __device__ inline _Float16 lo16h(uint32_t v) { return __builtin_bit_cast(_Float16, (uint16_t)(v & 0xffffu)); }
 __device__ inline _Float16 hi16h(uint32_t v) { return __builtin_bit_cast(_Float16, (uint16_t)(v >> 16)); }
 
 struct PageRegs {
     uint4 ka, kb, va, vb, ks, vs;
 };
+
+__device__ inline PageRegs load_page_ext(const uint8_t *page, int extent, const Geom &G, int lane) {
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc((void *)page, (short)0, extent, 0x00020000);
+    const int o = 16 * lane;
+    PageRegs R;
+    R.ks = bload(rs, G.ks + o);
+    R.vs = bload(rs, G.vs + o);
+    R.ka = bload(rs, G.kc + o);
+    R.kb = bload(rs, G.kc + 1024 + o);
+    R.va = bload(rs, G.vc + o);
+    R.vb = bload(rs, G.vc + 1024 + o);
+    return R;
+}
 
 __device__ inline PageRegs load_page_masked(const uint8_t *page, bool valid, const Geom &G, int lane) {
     const __amdgpu_buffer_rsrc_t rs = page_rsrc(page, valid, G);
@@ -749,6 +807,7 @@ __device__ inline void gqa4_page(const PageRegs &R, Gqa4State &S, Gqa4Smem &sm, 
     const int g = lane >> 4, r = lane & 15;
     const int hp = r >> 2;
     const uint32_t MSK = 0x33333333u;
+    float bias[4];                         // sum_c q_h z_c of this lane's key group, times qscale
 
     lds_sync();                            // previous page done with the LDS
 
@@ -757,25 +816,38 @@ __device__ inline void gqa4_page(const PageRegs &R, Gqa4State &S, Gqa4Smem &sm, 
     // queries, and the zero-point sums, added over the group's 32 lanes ----
     const int gi_p = lane >> 5;
     const uint32_t sz[4] = {R.ks.x, R.ks.y, R.ks.z, R.ks.w};
-    float bias0[4], bias1[4];              // [query] for key groups 0 and 1, times qscale
+    float bzp[4];                          // this lane's share of sum_c q_h z_c [query]
 #pragma unroll
     for (int h = 0; h < 4; h++) {
-        const _Float16 qe[4] = {lo16h(qw[h].x), hi16h(qw[h].x), lo16h(qw[h].y), hi16h(qw[h].y)};
         uint32_t hv0, lv0, hv1, lv1;
-        mul_split2((float)qe[0], lo16h(sz[0]), (float)qe[1], lo16h(sz[1]), hv0, lv0);
-        mul_split2((float)qe[2], lo16h(sz[2]), (float)qe[3], lo16h(sz[3]), hv1, lv1);
+        split_qs(qw[h].x, sz[0], sz[1], hv0, lv0);
+        split_qs(qw[h].y, sz[2], sz[3], hv1, lv1);
         ((uint2 *)&sm.As[gi_p][h][0])[lane & 31] = make_uint2(hv0, hv1);
         ((uint2 *)&sm.As[gi_p][4 + h][0])[lane & 31] = make_uint2(lv0, lv1);
-        float bz = (float)qe[0] * (float)hi16h(sz[0]);
-#pragma unroll
-        for (int e = 1; e < 4; e++) bz = fmaf((float)qe[e], (float)hi16h(sz[e]), bz);
-        bz = row_sum16(bz);                // row totals in lanes 15, 31, 47, 63
-        const int bzi = __builtin_bit_cast(int, bz);
-        bias0[h] = (__builtin_bit_cast(float, __builtin_amdgcn_readlane(bzi, 15)) +
-                    __builtin_bit_cast(float, __builtin_amdgcn_readlane(bzi, 31))) * qscale;
-        bias1[h] = (__builtin_bit_cast(float, __builtin_amdgcn_readlane(bzi, 47)) +
-                    __builtin_bit_cast(float, __builtin_amdgcn_readlane(bzi, 63))) * qscale;
+        float bz = fma_qz<0>(qw[h].x, sz[0], 0.0f);
+        bz = fma_qz<1>(qw[h].x, sz[1], bz);
+        bz = fma_qz<0>(qw[h].y, sz[2], bz);
+        bzp[h] = fma_qz<1>(qw[h].y, sz[3], bz);
     }
+    // Sum the shares over the 32 lanes of the key group, reduce-scatter
+    // style: after the two quad exchanges lane L holds query 2 (L & 1) +
+    // ((L >> 1) & 1) summed over its quad; rotations within the 16-lane row
+    // and one exchange between the group's two rows finish the sum.
+    const bool b0 = lane & 1, b1 = (lane & 2) != 0;
+    float k0 = b0 ? bzp[2] : bzp[0], k1 = b0 ? bzp[3] : bzp[1];
+    k0 += dppf<0xB1>(b0 ? bzp[0] : bzp[2]);            // quad_perm [1,0,3,2]
+    k1 += dppf<0xB1>(b0 ? bzp[1] : bzp[3]);
+    float kq = b1 ? k1 : k0;
+    kq += dppf<0x4E>(b1 ? k0 : k1);                    // quad_perm [2,3,0,1]
+    kq += dppf<0x124>(kq);                             // row_ror:4
+    kq += dppf<0x128>(kq);                             // row_ror:8
+    kq += __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, kq), 0x401F));  // lane ^ 16
+    kq *= qscale;
+    // query h sits in quad position (h >> 1) + 2 (h & 1): 0, 2, 1, 3
+    bias[0] = dppf<0x00>(kq);
+    bias[1] = dppf<0xAA>(kq);
+    bias[2] = dppf<0x55>(kq);
+    bias[3] = dppf<0xFF>(kq);
     lds_sync();
 
     // ---- scores on the matrix cores: operand rows 0..3 carry the hi parts and
@@ -805,8 +877,7 @@ __device__ inline void gqa4_page(const PageRegs &R, Gqa4State &S, Gqa4Smem &sm, 
     lds_sync();
 
     // ---- online softmax, lane = token ----
-    const bool g1 = lane >= 32;                 // token in key group 1
-    const f4v bz4 = g1 ? f4v{bias1[0], bias1[1], bias1[2], bias1[3]} : f4v{bias0[0], bias0[1], bias0[2], bias0[3]};
+    const f4v bz4 = f4v{bias[0], bias[1], bias[2], bias[3]};   // lane = token: its key group's
     const f4v z = (sm.zsh[0][lane] + sm.zsh[1][lane]) * qscale + bz4;     // log2 units
     float zz[4] = {z[0], z[1], z[2], z[3]};
     if (nvalid < PT) {                          // uniform: only the prefix's last page
@@ -850,18 +921,15 @@ __device__ inline void gqa4_page(const PageRegs &R, Gqa4State &S, Gqa4Smem &sm, 
     // lo, stored as the B columns (h, part, js) of operand j >> 1 (j = 2 (j >> 1)
     // + js); sum_t p_{h,t} z_{t,j} on the side ----
     {
-        uint32_t vw[4] = {R.vs.x, R.vs.y, R.vs.z, R.vs.w};
-        if (nvalid < PT) {                      // uniform: statistics past nvalid are not written yet
-#pragma unroll
-            for (int j = 0; j < 4; j++) vw[j] &= lane < nvalid ? 0xffffffffu : 0u;
-        }
+        // (statistics of tokens past nvalid read as zeros: the page's extent)
+        const uint32_t vw[4] = {R.vs.x, R.vs.y, R.vs.z, R.vs.w};
 #pragma unroll
         for (int h = 0; h < 4; h++) {
 #pragma unroll
             for (int j = 0; j < 4; j++) S.zacc[h][j] = fmaf(pq[h], (float)hi16h(vw[j]), S.zacc[h][j]);
             uint32_t h01, l01, h23, l23;
-            mul_split2(pq[h], lo16h(vw[0]), pq[h], lo16h(vw[1]), h01, l01);
-            mul_split2(pq[h], lo16h(vw[2]), pq[h], lo16h(vw[3]), h23, l23);
+            split_ps(pq[h], vw[0], vw[1], h01, l01);
+            split_ps(pq[h], vw[2], vw[3], h23, l23);
             sm.Bs[0][4 * h + 0][lane] = lo16h(h01);
             sm.Bs[0][4 * h + 1][lane] = hi16h(h01);
             sm.Bs[0][4 * h + 2][lane] = lo16h(l01);
@@ -964,7 +1032,10 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(3, 8))) void
     };
     auto page_ld = [&](int i) {
         const uint8_t *pg = base + (size_t)__builtin_amdgcn_readlane(pid_l, min(i, np - 1)) * pstride;
-        return load_page_masked(pg, i < np, G, lane);
+        // extent: the whole page, up to the value statistics of its last
+        // valid token on the prefix's last page, nothing past the split
+        const int ext = i < np ? G.vs + 16 * min(PT, nvq - (p0 + i) * PT) : 0;
+        return load_page_ext(pg, ext, G, lane);
     };
     // (scheduling barriers keep each page's loads together and in order, so
     // the wait before a page counts only the loads of the pages after it)
