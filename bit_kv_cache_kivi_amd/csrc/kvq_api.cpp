@@ -202,16 +202,10 @@ int kvq_flush_key_group(const kvq_cache_t *cache, hipStream_t stream) {
     return kvq::launch_flush(params(cache), stream) == hipSuccess ? KVQ_OK : KVQ_ELAUNCH;
 }
 
-int kvq_decode_attention(const kvq_cache_t *cache, const uint16_t *q, float *out, float *cert,
-                         float sm_scale, float kappa, void *workspace, size_t ws_bytes,
-                         hipStream_t stream) {
-    int rc = check_cache(cache);
-    if (rc != KVQ_OK) return rc;
-    if (!q || !out || !workspace) return KVQ_ENULL;
-    if (!aligned(q, 16) || !aligned(out, 16) || !aligned(workspace, 256) ||
-        (cert && !aligned(cert, 4)))
-        return KVQ_EALIGN;
-    if (ws_bytes < kvq_workspace_bytes(cache)) return KVQ_EWORKSPACE;
+namespace {
+// kvq_decode_attention's launch once the workspace is known good
+int decode_with(const kvq_cache_t *cache, const uint16_t *q, float *out, float *cert,
+                float sm_scale, float kappa, void *workspace, hipStream_t stream) {
     kvq::Workspace W;
     W.max_splits = max_splits(cache);
     W.n_win = n_win(cache);
@@ -223,6 +217,39 @@ int kvq_decode_attention(const kvq_cache_t *cache, const uint16_t *q, float *out
     return kvq::launch_decode(params(cache), q, out, cert, sm_scale, kappa, W, stream) == hipSuccess
                ? KVQ_OK
                : KVQ_ELAUNCH;
+}
+
+int check_decode_args(const uint16_t *q, const float *out, const float *cert) {
+    if (!q || !out) return KVQ_ENULL;
+    if (!aligned(q, 16) || !aligned(out, 16) || (cert && !aligned(cert, 4))) return KVQ_EALIGN;
+    return KVQ_OK;
+}
+}  // namespace
+
+int kvq_decode_attention(const kvq_cache_t *cache, const uint16_t *q, float *out, float *cert,
+                         float sm_scale, float kappa, void *workspace, size_t ws_bytes,
+                         hipStream_t stream) {
+    int rc = check_cache(cache);
+    if (rc != KVQ_OK) return rc;
+    if ((rc = check_decode_args(q, out, cert)) != KVQ_OK) return rc;
+    if (!workspace) return KVQ_ENULL;
+    if (!aligned(workspace, 256)) return KVQ_EALIGN;
+    if (ws_bytes < kvq_workspace_bytes(cache)) return KVQ_EWORKSPACE;
+    return decode_with(cache, q, out, cert, sm_scale, kappa, workspace, stream);
+}
+
+int kvq_decode_attention_noalloc(const kvq_cache_t *cache, const uint16_t *q, float *out,
+                                 float *cert, float sm_scale, float kappa, hipStream_t stream) {
+    int rc = check_cache(cache);
+    if (rc != KVQ_OK) return rc;
+    if ((rc = check_decode_args(q, out, cert)) != KVQ_OK) return rc;
+    // the size check comes before any device call
+    if (kvq_workspace_bytes(cache) > KVQ_NOALLOC_SCRATCH_BYTES) return KVQ_ENOSCRATCH;
+    void *ws = nullptr;
+    size_t ws_bytes = 0;
+    if (kvq::noalloc_scratch(&ws, &ws_bytes) != hipSuccess) return KVQ_ELAUNCH;
+    if (ws_bytes < kvq_workspace_bytes(cache)) return KVQ_ENOSCRATCH;
+    return decode_with(cache, q, out, cert, sm_scale, kappa, ws, stream);
 }
 
 int kvq_prefill(const kvq_cache_t *cache, int32_t req0, int32_t n_req, const uint16_t *K,
@@ -282,7 +309,8 @@ const char *kvq_strerror(int code) {
         case KVQ_EALIGN: return "device pointer misaligned";
         case KVQ_ENOLAYOUT: return "cache not initialised by kvq_set_layout";
         case KVQ_EWORKSPACE: return "workspace too small";
-        case KVQ_ELAUNCH: return "kernel launch failed";
+        case KVQ_ELAUNCH: return "kernel launch or HIP call failed";
+        case KVQ_ENOSCRATCH: return "cache needs more workspace than the no-alloc scratch array holds";
         default: return "unknown";
     }
 }

@@ -13,10 +13,18 @@
 // Folding: for a key group, q.k~ = sum_c (q_c s_c) code_c + sum_c q_c z_c;
 // for a value group, sum_t p_t v~_t = sum_t (p_t s_t) code_t + sum_t p_t z_t.
 // Only small integer codes are touched per element.
+#include <atomic>
+#include <mutex>
 #include <type_traits>
 
+#include "kvq.h"
 #include "kvq_common.hpp"
 #include "kvq_kernels.hpp"
+
+// Stage-1 partials of kvq_decode_attention_noalloc: one array per device,
+// kept for the life of the process.  Host code must use the address from
+// hipGetSymbolAddress (per device), never this name.
+static __device__ __align__(256) uint8_t scratch[KVQ_NOALLOC_SCRATCH_BYTES];
 
 namespace kvq {
 
@@ -1887,6 +1895,33 @@ __global__ __launch_bounds__(64) void merge_kernel(KParams P, float *__restrict_
 }
 
 // ---------------------------------------------------------------------------
+namespace {
+constexpr int MAX_DEVICES = 64;
+std::atomic<void *> scratch_ptr[MAX_DEVICES];
+std::mutex scratch_mu;
+}  // namespace
+
+hipError_t noalloc_scratch(void **ptr, size_t *bytes) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= MAX_DEVICES) return hipErrorInvalidDevice;
+    void *p = scratch_ptr[dev].load(std::memory_order_acquire);
+    if (!p) {
+        std::lock_guard<std::mutex> lock(scratch_mu);
+        p = scratch_ptr[dev].load(std::memory_order_relaxed);
+        if (!p) {
+            e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));     // device `dev` is current
+            if (e != hipSuccess) return e;
+            if (!p) return hipErrorInvalidSymbol;
+            scratch_ptr[dev].store(p, std::memory_order_release);
+        }
+    }
+    *ptr = p;
+    *bytes = sizeof(scratch);
+    return hipSuccess;
+}
+
 hipError_t launch_decode(const KParams &P, const uint16_t *q, float *out, float *cert,
                          float sm_scale, float kappa, const Workspace &W, hipStream_t s) {
     const float qscale = sm_scale * 1.4426950408889634f;

@@ -61,4 +61,8 @@ hipError_t launch_witcert_calibrate(const KParams &P, const uint16_t *calib, int
 hipError_t launch_decode(const KParams &P, const uint16_t *q, float *out, float *cert,
                          float sm_scale, float kappa, const Workspace &W, hipStream_t s);
 
+// Device address of the fixed scratch array of the current device (resolved
+// once per device with hipGetSymbolAddress); *bytes gets its size.
+hipError_t noalloc_scratch(void **ptr, size_t *bytes);
+
 }  // namespace kvq

@@ -24,14 +24,15 @@ SCHEMES = {"kivi2": KVQ_SCHEME_KIVI2, "kitty": KVQ_SCHEME_KITTY, "witcert": KVQ_
            "kitty_dyn": KVQ_SCHEME_KITTY_DYN, "kivi4": KVQ_SCHEME_KIVI4,
            "witcert_paged": KVQ_SCHEME_WITCERT_PAGED}
 
-KVQ_OK, KVQ_EINVAL, KVQ_ENULL, KVQ_EALIGN, KVQ_ENOLAYOUT, KVQ_EWORKSPACE, KVQ_ELAUNCH = \
-    0, -1, -2, -3, -4, -5, -6
+KVQ_OK, KVQ_EINVAL, KVQ_ENULL, KVQ_EALIGN, KVQ_ENOLAYOUT, KVQ_EWORKSPACE, KVQ_ELAUNCH, \
+    KVQ_ENOSCRATCH = 0, -1, -2, -3, -4, -5, -6, -7
+NOALLOC_SCRATCH_BYTES = 64 << 20          # KVQ_NOALLOC_SCRATCH_BYTES
 STATUS_RESIDUAL_FULL, STATUS_CAPACITY, STATUS_UNMAPPED_PAGE, STATUS_BAD_LENGTH = 1, 2, 4, 8
 FLAG_GENERIC_STAGE1 = 1
 
 EXPORTS = ("kvq_set_layout", "kvq_append_token", "kvq_flush_key_group",
-           "kvq_decode_attention", "kvq_page_bytes", "kvq_page_tokens",
-           "kvq_bytes_per_token", "kvq_workspace_bytes", "kvq_prefill",
+           "kvq_decode_attention", "kvq_decode_attention_noalloc", "kvq_page_bytes",
+           "kvq_page_tokens", "kvq_bytes_per_token", "kvq_workspace_bytes", "kvq_prefill",
            "kvq_kitty_calibrate", "kvq_witcert_calibrate", "kvq_set_stage1_events",
            "kvq_strerror")
 
@@ -75,6 +76,8 @@ def lib():
         L.kvq_flush_key_group.argtypes = [C.POINTER(kvq_cache_t), S]
         L.kvq_decode_attention.argtypes = [C.POINTER(kvq_cache_t), P, P, P, C.c_float,
                                            C.c_float, P, C.c_size_t, S]
+        L.kvq_decode_attention_noalloc.argtypes = [C.POINTER(kvq_cache_t), P, P, P, C.c_float,
+                                                   C.c_float, S]
         L.kvq_page_bytes.argtypes = [C.POINTER(kvq_layout_t)]
         L.kvq_page_bytes.restype = C.c_int64
         L.kvq_page_tokens.argtypes = [C.POINTER(kvq_layout_t)]
@@ -125,6 +128,13 @@ def kvq_decode_attention(cache: kvq_cache_t, q_ptr: int, out_ptr: int, cert_ptr:
                          sm_scale: float, kappa: float, ws_ptr: int, ws_bytes: int, stream: int):
     _check(lib().kvq_decode_attention(C.byref(cache), q_ptr, out_ptr, cert_ptr, sm_scale, kappa,
                                       ws_ptr, ws_bytes, stream), "kvq_decode_attention")
+
+
+def kvq_decode_attention_noalloc(cache: kvq_cache_t, q_ptr: int, out_ptr: int,
+                                 cert_ptr: int | None, sm_scale: float, kappa: float,
+                                 stream: int):
+    _check(lib().kvq_decode_attention_noalloc(C.byref(cache), q_ptr, out_ptr, cert_ptr, sm_scale,
+                                              kappa, stream), "kvq_decode_attention_noalloc")
 
 
 def kvq_prefill(cache: kvq_cache_t, req0: int, n_req: int, k_ptr: int, v_ptr: int,
@@ -246,6 +256,16 @@ class KVCache:
         kvq_decode_attention(self.cache, q.data_ptr(), out.data_ptr(),
                              None if cert is None else cert.data_ptr(), sm_scale, kappa,
                              self.workspace.data_ptr(), self.ws_bytes, self.stream())
+
+    def decode_noalloc(self, q, out, cert=None, sm_scale: float = 1.0 / 128 ** 0.5,
+                       kappa: float = 0.0):
+        """decode() through kvq_decode_attention_noalloc: the library's
+        per-device scratch array instead of this cache's workspace."""
+        assert q.dtype == self.torch.float16 and q.is_contiguous()
+        assert out.dtype == self.torch.float32 and out.is_contiguous()
+        kvq_decode_attention_noalloc(self.cache, q.data_ptr(), out.data_ptr(),
+                                     None if cert is None else cert.data_ptr(), sm_scale, kappa,
+                                     self.stream())
 
     def prefill(self, req0: int, K, V, lengths):
         """K, V: fp16 [n_req][Hkv][ld][128] on the device; lengths int32 [n_req]."""

@@ -109,8 +109,14 @@ enum {
     KVQ_EALIGN = -3,      /* a device pointer is misaligned */
     KVQ_ENOLAYOUT = -4,   /* cache was not filled by kvq_set_layout */
     KVQ_EWORKSPACE = -5,  /* workspace smaller than kvq_workspace_bytes() */
-    KVQ_ELAUNCH = -6      /* a kernel launch failed (hipGetLastError) */
+    KVQ_ELAUNCH = -6,     /* a kernel launch or HIP call failed (hipGetLastError) */
+    KVQ_ENOSCRATCH = -7   /* kvq_decode_attention_noalloc: the cache needs more
+                             than KVQ_NOALLOC_SCRATCH_BYTES of workspace */
 };
+
+/* Size of the device scratch array behind kvq_decode_attention_noalloc: one
+ * array per GPU the library runs on, held until the process ends. */
+#define KVQ_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
 
 /* device status bits (sticky, OR-ed into *status) */
 enum {
@@ -263,6 +269,25 @@ int kvq_flush_key_group(const kvq_cache_t *cache, hipStream_t stream);
 int kvq_decode_attention(const kvq_cache_t *cache, const uint16_t *q, float *out,
                          float *cert, float sm_scale, float kappa,
                          void *workspace, size_t ws_bytes, hipStream_t stream);
+
+/* kvq_decode_attention without a caller-supplied workspace, for callers that
+ * cannot allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid allocation).  The stage-1 partials go to a
+ * file-scope device array of KVQ_NOALLOC_SCRATCH_BYTES on the current device
+ * (hipGetDevice); its address is resolved once per device, on the first call
+ * made with that device current.  Same kernels and results as
+ * kvq_decode_attention with a workspace.  Allocates and frees nothing.
+ * Returns KVQ_ENOSCRATCH, before any device work, when kvq_workspace_bytes()
+ * of the cache exceeds KVQ_NOALLOC_SCRATCH_BYTES (for the GQA workload of 64
+ * requests x 32 query heads with 32K-token page tables, 48 MB are needed);
+ * KVQ_ELAUNCH if the device or the array's address cannot be obtained.
+ * Every call on one GPU shares that GPU's array: calls whose execution
+ * overlaps on one GPU (other streams, other threads) race on it and must be
+ * ordered by the caller.  Nothing in the array needs clearing between calls:
+ * each call writes every partial it reads. */
+int kvq_decode_attention_noalloc(const kvq_cache_t *cache, const uint16_t *q, float *out,
+                                 float *cert, float sm_scale, float kappa,
+                                 hipStream_t stream);
 
 /* ---- helpers ---------------------------------------------------------- */
 

@@ -325,3 +325,25 @@ def test_sink_fields_and_workspace(K):
     splits = -(-64 // cache.split_pages)
     rows = 2 * 8 * (splits + 128 // 64 + 1)          # window chunks + the sink chunk
     assert K.kvq_workspace_bytes(cache) == rows * 128 * 4 + rows * 8 + 256
+
+
+def test_noalloc_rejects_oversized_cache_before_device_work(K):
+    # kvq_decode_attention_noalloc refuses a cache whose workspace exceeds the
+    # scratch array, before any HIP call (no GPU needed to see it)
+    L = K.make_layout("kivi2", B=128, Hq=32, Hkv=8, max_pages=512, n_pages=128 * 512)
+    rc, cache = set_layout(K, L)
+    assert rc == K.KVQ_OK
+    assert K.kvq_workspace_bytes(cache) > K.NOALLOC_SCRATCH_BYTES
+    a = A256 + 0x10000
+    lib = K.lib()
+    rc = lib.kvq_decode_attention_noalloc(C.byref(cache), C.c_void_p(a), C.c_void_p(a + 0x1000),
+                                          None, C.c_float(1.0), C.c_float(0.0), None)
+    assert rc == K.KVQ_ENOSCRATCH
+    assert lib.kvq_decode_attention_noalloc(C.byref(cache), None, C.c_void_p(a), None,
+                                            C.c_float(1.0), C.c_float(0.0), None) == K.KVQ_ENULL
+    s = lib.kvq_strerror(K.KVQ_ENOSCRATCH)
+    assert s and s != lib.kvq_strerror(K.KVQ_EWORKSPACE)
+    # the header's size and the binding's agree
+    text = open(HEADER).read()
+    assert "KVQ_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)" in text
+    assert K.NOALLOC_SCRATCH_BYTES == 64 << 20

@@ -1,0 +1,74 @@
+"""kvq_decode_attention_noalloc, the decode entry point for callers that cannot
+allocate (the library's per-device scratch array instead of a workspace),
+through the C ABI against kvq_decode_attention with a caller workspace: the
+same output on two calls in a row, the second with a smaller cache, and a
+WitCert call with its certificate.  The bar is the parity tests' (max |delta
+o| <= 1e-5; certificate relative 1e-5); the two entry points run the same
+kernels, so the outputs are also compared bit for bit."""
+import numpy as np
+import pytest
+
+from bit_kv_cache_kivi_amd import inputs
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    torch = pytest.importorskip("torch")
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from bit_kv_cache_kivi_amd import kvq
+    kvq.lib()          # the HIP library must load: no fallback
+
+
+def _both(case, step_id, kappa=0.0):
+    """decode() then decode_noalloc() on the same query; host copies."""
+    torch = case.torch
+    w = case.w
+    q = inputs.step_q(w, step_id)
+    qt = torch.from_numpy(q.view(np.float16)).cuda()
+    res = []
+    for fn in (case.cache.decode, case.cache.decode_noalloc):
+        out = torch.full((w.B, w.Hq, 128), float("nan"), dtype=torch.float32, device="cuda")
+        cert = torch.full((w.B, w.Hq), float("nan"), dtype=torch.float32, device="cuda")
+        fn(qt, out, cert, sm_scale=w.sm_scale, kappa=kappa)
+        torch.cuda.synchronize()
+        res.append((out.cpu().numpy(), cert.cpu().numpy()))
+    case.check_status()
+    return res, q
+
+
+def _same(a, b, tol=1e-5):
+    assert np.all(np.isfinite(b))
+    assert np.abs(a.astype(np.float64) - b).max() <= tol
+    assert np.array_equal(a, b)
+
+
+def test_noalloc_matches_workspace_entry_twice_second_smaller():
+    from gpu_harness import Case
+    from bit_kv_cache_kivi_amd import kvq
+    big_w = inputs.workload(3, B=4, Hq=32, Hkv=8, ctx=(3000, 5100, 6400, 1900))
+    big = Case(big_w, extra_tokens=64, split_pages=4, sample=[(0, 0), (2, 7), (3, 3)])
+    small_w = inputs.workload(3, B=2, Hq=8, Hkv=2, ctx=(700, 1301))
+    small = Case(small_w, extra_tokens=64, split_pages=4)
+    assert kvq.kvq_workspace_bytes(big.cache.cache) > kvq.kvq_workspace_bytes(small.cache.cache)
+    for case, sid in ((big, 5), (small, 6)):
+        ((o_ws, _), (o_na, _)), q = _both(case, sid)
+        _same(o_ws, o_na)
+        g = case.w.group
+        for (b, h) in case.streams:                  # and the oracle, for the sampled pairs
+            ref, _ = case.oracle_decode(q, b, h)
+            assert np.abs(o_na[b, h * g:(h + 1) * g].astype(np.float64) - ref).max() <= 1e-5
+
+
+def test_noalloc_witcert_certificate():
+    from gpu_harness import Case
+    w = inputs.workload(5, B=2, Hq=8, Hkv=2, ctx=(600, 1000))
+    case = Case(w, extra_tokens=64)
+    ((o_ws, c_ws), (o_na, c_na)), _ = _both(case, 3, kappa=1.0)
+    _same(o_ws, o_na)
+    assert np.array_equal(np.isinf(c_ws), np.isinf(c_na))
+    fin = np.isfinite(c_ws)
+    assert np.all(np.abs(c_ws[fin].astype(np.float64) - c_na[fin]) <= 1e-5 * np.abs(c_ws[fin]))
+    assert np.array_equal(c_ws, c_na)
