@@ -38,7 +38,7 @@ int validate_layout(const kvq_layout_t *L) {
             // the key residual is quantized in whole groups: R % G == 0, and
             // the flush writes whole 64-token pages
             if (L->residual % L->group != 0 || L->residual % kvq::PT != 0) return KVQ_EINVAL;
-            if (L->residual < kvq::PT || L->residual > 256) return KVQ_EINVAL;
+            if (L->residual < kvq::PT || L->residual > kvq::MAX_RESIDUAL) return KVQ_EINVAL;
             if (kvq::is_kitty(L->scheme) ? (L->n_boost != kvq::NB && L->n_boost != kvq::NB_MAX)
                                          : L->n_boost != 0)
                 return KVQ_EINVAL;
@@ -168,10 +168,10 @@ int kvq_set_layout(kvq_cache_t *cache, const kvq_layout_t *layout, const kvq_buf
         sp = layout->scheme == KVQ_SCHEME_WITCERT ? 1
              : wtok                                 ? 4      // 256 tokens, as one WITCERT block
              : (layout->max_pages <= 128 ? 4 : 12);
-        sp = std::max(sp, (layout->max_pages + 255) / 256);
+        sp = std::max(sp, (layout->max_pages + kvq::MAX_SPLITS - 1) / kvq::MAX_SPLITS);
     }
-    // the merge takes at most 256 splits per query head
-    if ((layout->max_pages + sp - 1) / sp > 256 || sp > 64) return KVQ_EINVAL;
+    // the merge takes at most MAX_SPLITS splits per query head
+    if ((layout->max_pages + sp - 1) / sp > kvq::MAX_SPLITS || sp > 64) return KVQ_EINVAL;
     cache->split_pages = sp;
     cache->magic = MAGIC;
     return KVQ_OK;
@@ -302,6 +302,20 @@ int kvq_set_stage1_events(kvq_cache_t *cache, hipEvent_t begin, hipEvent_t end) 
 }
 
 const char *kvq_strerror(int code) {
+    if (code > 0) {                        // a device status word
+        const unsigned known = KVQ_STATUS_RESIDUAL_FULL | KVQ_STATUS_CAPACITY |
+                               KVQ_STATUS_UNMAPPED_PAGE | KVQ_STATUS_BAD_LENGTH | KVQ_STATUS_RANGE;
+        const unsigned u = (unsigned)code;
+        if (u & ~known) return "unknown";
+        switch (u) {
+            case KVQ_STATUS_RESIDUAL_FULL: return "append found the key residual or active block full (flush skipped)";
+            case KVQ_STATUS_CAPACITY: return "append beyond the page table's capacity";
+            case KVQ_STATUS_UNMAPPED_PAGE: return "page-table entry outside the pool";
+            case KVQ_STATUS_BAD_LENGTH: return "prefill length outside [0, capacity]";
+            case KVQ_STATUS_RANGE: return "outside the matrix-core stage 1's operand range (value scale above 255 or a non-finite split)";
+            default: return "several device status bits";
+        }
+    }
     switch (code) {
         case KVQ_OK: return "ok";
         case KVQ_EINVAL: return "invalid layout or argument";

@@ -14,6 +14,15 @@ constexpr int PT = 64;          // tokens per KIVI2/KITTY page
 constexpr int WPT = 256;        // tokens per WITCERT page (= one block)
 constexpr int NB = 16;          // Kitty boosted channels per KV head (alpha = 1/8)
 constexpr int NB_MAX = 32;      // Kitty-Pro: alpha = 1/4
+// Largest value scale the matrix-core stage 1 carries: it forms p_t s_t with
+// softmax weights p_t <= 256 as an f16 head, which must stay below 65504.
+constexpr float VALUE_SCALE_MAX = 255.0f;
+constexpr int MAX_RESIDUAL = 256;                  // largest fp16 window R (tokens)
+constexpr int MAX_SPLITS = 256;                    // largest paged split count per query head
+// window chunks per query head: R / 64 chunks plus one for the sink tokens
+// (WITCERT: one 256-token block of four chunks)
+constexpr int MAX_WIN = MAX_RESIDUAL / PT + 1;
+static_assert(MAX_WIN >= WPT / PT, "window chunk bound");
 
 // ---------------------------------------------------------------------------
 // Page geometry.  One (page, KV head) block; the pool is

@@ -1,14 +1,15 @@
 // kvq_decode.hip -- read path: split-KV stage 1 over the quantized prefix and
-// stage 2 (fp16 window + log-sum-exp merge).
+// the fp16 window, stage 2 (log-sum-exp merge).
 //
 // Attention for query head h of KV head g: z_t = sm_scale q.k~_t over every
 // token, p = softmax(z), o = sum_t p_t v~_t, with k~, v~ the dequantized or
 // fp16 tokens ("KIVI" explainer eq. 3).  Stage 1 takes the prefix [0, n_vq)
-// whose keys and values are both quantized, split into runs of pages, and
-// emits per split (acc / l_s, lse_s, A_s); stage 2 attends to the fp16 window
-// (keys of [n_vq, n_kq) still 2-bit) and merges every partial with
-// log-sum-exp weights; the certificate A_s merges with the same weights
-// ("WitCert" Key structure).  Scores are kept in log2 units: z2 = z log2(e).
+// whose keys and values are both quantized, split into runs of pages, and the
+// fp16 window (keys of [n_vq, n_kq) still 2-bit) and sink tokens in 64-token
+// chunks, and emits per split or chunk (acc / l_s, lse_s, A_s); stage 2
+// merges every partial with log-sum-exp weights; the certificate A_s merges
+// with the same weights ("WitCert" Key structure).  Scores are kept in log2
+// units: z2 = z log2(e).
 //
 // Folding: for a key group, q.k~ = sum_c (q_c s_c) code_c + sum_c q_c z_c;
 // for a value group, sum_t p_t v~_t = sum_t (p_t s_t) code_t + sum_t p_t z_t.
@@ -82,6 +83,13 @@ __device__ inline uint32_t rem_pair(float a0, float a1, uint32_t h) {
 // not waited for.
 __device__ inline void lds_sync() {
     asm volatile("" ::: "memory");
+}
+
+// A matrix-core stage-1 split whose result is not finite: an f16 operand head
+// (q_c s_c or p_t s_t) overflowed, or the inputs were not finite.  Reported
+// in the status word; the partial is written as it came out.
+__device__ inline void flag_range(const KParams &P, bool bad, int lane) {
+    if (__any(bad) && lane == 0) atomicOr(P.status, (uint32_t)KVQ_STATUS_RANGE);
 }
 
 // Loads through a buffer descriptor of a page's own extent.  With valid false
@@ -1073,6 +1081,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(3, 8))) void
     const float lh = hp == 0 ? S.lsum[0] : hp == 1 ? S.lsum[1] : hp == 2 ? S.lsum[2] : S.lsum[3];
     const float il = 1.0f / lh;
     const size_t row = part_row(W, P.Hq, b, 4 * h + hp, s);
+    bool nonfinite = !__builtin_isfinite(lh);
 #pragma unroll
     for (int nt = 0; nt < 8; nt++) {
         f4v lo;                                   // the lo column, two lanes up
@@ -1082,9 +1091,12 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(3, 8))) void
             const int j = nt >> 1;
             const float zj = hp == 0 ? S.zacc[0][j] : hp == 1 ? S.zacc[1][j] : hp == 2 ? S.zacc[2][j] : S.zacc[3][j];
             const f4v o = (S.acc[nt] + lo + zj) * il;
+#pragma unroll
+            for (int i = 0; i < 4; i++) nonfinite |= !__builtin_isfinite(o[i]);
             *(float4 *)(W.o + row * D + 16 * nt + 4 * g) = make_float4(o[0], o[1], o[2], o[3]);
         }
     }
+    flag_range(P, nonfinite, lane);
     if (lane < 4) {
         const float li = lane == 0 ? S.lsum[0] : lane == 1 ? S.lsum[1] : lane == 2 ? S.lsum[2] : S.lsum[3];
         const float mi = lane == 0 ? S.m[0] : lane == 1 ? S.m[1] : lane == 2 ? S.m[2] : S.m[3];
@@ -1403,6 +1415,7 @@ void stage1_head_mfma_kernel(KParams P, const uint16_t *__restrict__ q, Workspac
         for (int msk = 1; msk < 64; msk <<= 1) zacc[j] += shfl_xor(zacc[j], msk);
     const float il = 1.0f / lsum;
     const size_t row = part_row(W, P.Hq, b, hq, s);
+    bool nonfinite = !__builtin_isfinite(lsum);
 #pragma unroll
     for (int nt = 0; nt < 8; nt++) {
         f4v lo;                                   // column 4 + j, four lanes up
@@ -1412,9 +1425,12 @@ void stage1_head_mfma_kernel(KParams P, const uint16_t *__restrict__ q, Workspac
         if (r == jv) {
             const float zj = jv == 0 ? zacc[0] : jv == 1 ? zacc[1] : jv == 2 ? zacc[2] : zacc[3];
             const f4v o = (acc[nt] + lo + zj) * il;
+#pragma unroll
+            for (int i = 0; i < 4; i++) nonfinite |= !__builtin_isfinite(o[i]);
             *(float4 *)(W.o + row * D + 16 * nt + 4 * g) = make_float4(o[0], o[1], o[2], o[3]);
         }
     }
+    flag_range(P, nonfinite, lane);
     if (lane == 0) W.ml[row] = make_float2(m + log2f(lsum), 1.0f);
 }
 
@@ -1810,7 +1826,7 @@ __global__ __launch_bounds__(64) void stage1_witcert_paged_kernel(KParams P, con
     }
 }
 
-constexpr int S2_MAXSPLIT = 256;     // paged splits per query head (kvq_set_layout keeps <= 256)
+
 
 // ---------------------------------------------------------------------------
 // Stage 2: log-sum-exp merge of one query head's partials (the paged splits
@@ -1845,7 +1861,9 @@ __global__ __launch_bounds__(64) void merge_kernel(KParams P, float *__restrict_
         ov[k] = e < ne ? *(const float4 *)(W.o + row_of(e) * D + 4 * c4) : make_float4(0.f, 0.f, 0.f, 0.f);
     }
 
-    __shared__ float wsh[S2_MAXSPLIT + WPT / PT];
+    // a weight per entry: at most MAX_SPLITS paged splits plus MAX_WIN window
+    // chunks (kvq_set_layout keeps both bounds)
+    __shared__ float wsh[MAX_SPLITS + MAX_WIN];
     float M = -INFINITY;
     for (int e = lane; e < ne; e += 64) M = fmaxf(M, W.ml[row_of(e)].x);
 #pragma unroll

@@ -18,6 +18,12 @@ __device__ inline uint8_t *page_ptr(const KParams &P, int pid, int h) {
     return P.pool + ((size_t)pid * P.Hkv + h) * (size_t)P.page_bytes;
 }
 
+// A stored value scale the matrix-core stage 1 cannot carry (above
+// VALUE_SCALE_MAX): reported when the layout decodes on the matrix cores.
+__device__ inline void flag_value_scale(const KParams &P, float s) {
+    if (!P.force_generic && s > VALUE_SCALE_MAX) atomicOr(P.status, (uint32_t)KVQ_STATUS_RANGE);
+}
+
 __device__ inline bool page_ok(const KParams &P, int pid) {
     return pid >= 0 && pid < P.n_pages;
 }
@@ -222,6 +228,7 @@ __global__ __launch_bounds__(64) void append_kivi_kernel(KParams P, const uint16
         if ((lane & 15) == 0) {
             uint32_t *vs = (uint32_t *)(page + G.vs);
             vs[tp * 4 + (lane >> 4)] = (uint32_t)ap.s16 | ((uint32_t)ap.z16 << 16);
+            flag_value_scale(P, ap.s);
         }
     }
     rk[lane] = kin[lane];
@@ -351,6 +358,7 @@ __global__ __launch_bounds__(256) void prefill_kivi_kernel(KParams P, int req0,
 #pragma unroll
             for (int i = 0; i < 32; i++) codes[tl][32 * jv + i] = (uint8_t)asym_code(xs[i], ap, lmax);
             ((uint32_t *)(page + G.vs))[tl * 4 + jv] = (uint32_t)ap.s16 | ((uint32_t)ap.z16 << 16);
+            flag_value_scale(P, ap.s);
         } else {
 #pragma unroll
             for (int i = 0; i < 32; i++) codes[tl][32 * jv + i] = 0;

@@ -27,7 +27,8 @@ SCHEMES = {"kivi2": KVQ_SCHEME_KIVI2, "kitty": KVQ_SCHEME_KITTY, "witcert": KVQ_
 KVQ_OK, KVQ_EINVAL, KVQ_ENULL, KVQ_EALIGN, KVQ_ENOLAYOUT, KVQ_EWORKSPACE, KVQ_ELAUNCH, \
     KVQ_ENOSCRATCH = 0, -1, -2, -3, -4, -5, -6, -7
 NOALLOC_SCRATCH_BYTES = 64 << 20          # KVQ_NOALLOC_SCRATCH_BYTES
-STATUS_RESIDUAL_FULL, STATUS_CAPACITY, STATUS_UNMAPPED_PAGE, STATUS_BAD_LENGTH = 1, 2, 4, 8
+STATUS_RESIDUAL_FULL, STATUS_CAPACITY, STATUS_UNMAPPED_PAGE, STATUS_BAD_LENGTH, STATUS_RANGE = \
+    1, 2, 4, 8, 16
 FLAG_GENERIC_STAGE1 = 1
 
 EXPORTS = ("kvq_set_layout", "kvq_append_token", "kvq_flush_key_group",

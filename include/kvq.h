@@ -124,8 +124,16 @@ enum {
                                        block full: flush was skipped */
     KVQ_STATUS_CAPACITY = 2u,       /* append beyond sink + max_pages * page_tokens */
     KVQ_STATUS_UNMAPPED_PAGE = 4u,  /* page-table entry outside [0, n_pages) */
-    KVQ_STATUS_BAD_LENGTH = 8u      /* prefill length outside [0, capacity]
+    KVQ_STATUS_BAD_LENGTH = 8u,     /* prefill length outside [0, capacity]
                                        (capacity: sink + max_pages * page_tokens) */
+    KVQ_STATUS_RANGE = 16u          /* outside the matrix-core stage 1's operand
+                                       range (see kvq_decode_attention): append
+                                       or prefill stored a value scale above
+                                       255, or a stage-1 split's result was not
+                                       finite (an f16 operand head |q_c s_c| or
+                                       p_t s_t overflowed, or non-finite
+                                       inputs); not set under
+                                       KVQ_FLAG_GENERIC_STAGE1 or for WITCERT */
 };
 
 /* Layout.  Fields the caller fills before kvq_set_layout. */
@@ -214,9 +222,9 @@ typedef struct kvq_cache {
  *   KIVI2 / KITTY / KITTY_DYN / KIVI4: group or value_group != 32; residual not a
  *   multiple of 64 or outside [64, 256] (the residual is quantized in whole
  *   key groups, so it must be divisible by the group, "KIVI" explainer 3.3,
- *   and the flush fills whole 64-token pages); n_boost != 16 for KITTY and
- *   KITTY_DYN or != 0 for KIVI2 and KIVI4; KVQ_FLAG_GENERIC_STAGE1 with
- *   KITTY_DYN or KIVI4;
+ *   and the flush fills whole 64-token pages); n_boost other than 16 or 32
+ *   for KITTY and KITTY_DYN, or != 0 for KIVI2 and KIVI4;
+ *   KVQ_FLAG_GENERIC_STAGE1 with KITTY_DYN, KIVI4 or n_boost 32;
  *   sink outside [0, 64] or non-zero for WITCERT / WITCERT_PAGED; reserved
  *   != 0;
  *   WITCERT: block != 256; layer >= 65536; query heads per KV head not in
@@ -252,9 +260,10 @@ int kvq_flush_key_group(const kvq_cache_t *cache, hipStream_t stream);
  * +inf is a valid value); sm_scale multiplies q.k; kappa multiplies the
  * certificate's per-block standard deviation.  Query head h reads KV head
  * h / (n_q_heads / n_kv_heads).  workspace: device, >= kvq_workspace_bytes().
- * Stage 1 splits the tokens whose key and value are both quantized; stage 2
- * attends to the fp16 window and merges all partials with log-sum-exp
- * weights ("WitCert" Key structure).  A request with no token gets a zero
+ * Stage 1 covers the tokens whose key and value are both quantized in splits
+ * of split_pages pages, and the fp16 window (and the sink tokens) in 64-token
+ * chunks, each a partial of its own; stage 2 merges all partials with
+ * log-sum-exp weights ("WitCert" Key structure).  A request with no token gets a zero
  * output row and a zero certificate.  Returns KVQ_EWORKSPACE if ws_bytes is
  * too small.
  * Range of the matrix-core stage 1 (KIVI2, KITTY, KITTY_DYN and KIVI4
@@ -265,7 +274,8 @@ int kvq_flush_key_group(const kvq_cache_t *cache, hipStream_t stream);
  * value group spanning at most 765 for 2-bit codes, 3825 for 4-bit);
  * beyond that the output is unspecified and may be non-finite.  The fp16
  * window, the VALU stage 1 and the WITCERT schemes compute in binary32 and
- * have no such limit. */
+ * have no such limit.  The matrix-core path reports leaving that range
+ * with KVQ_STATUS_RANGE. */
 int kvq_decode_attention(const kvq_cache_t *cache, const uint16_t *q, float *out,
                          float *cert, float sm_scale, float kappa,
                          void *workspace, size_t ws_bytes, hipStream_t stream);
@@ -339,7 +349,10 @@ int kvq_witcert_calibrate(const kvq_cache_t *cache, const uint16_t *calib,
  * right after it (caller-owned events; NULL, NULL turns the hook off). */
 int kvq_set_stage1_events(kvq_cache_t *cache, hipEvent_t begin, hipEvent_t end);
 
-/* Static description of a return code or status bit set. */
+/* Static description of a host return code (KVQ_OK, KVQ_E*: code <= 0) or
+ * of a device status word (code > 0): one KVQ_STATUS_* bit gets its own
+ * description, several bits "several device status bits", a word with an
+ * undefined bit "unknown". */
 const char *kvq_strerror(int code);
 
 #ifdef __cplusplus

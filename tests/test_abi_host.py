@@ -295,11 +295,28 @@ def test_decode_rejects_small_workspace_before_launching(K):
 
 def test_error_strings(K):
     lib = K.lib()
-    for code in (K.KVQ_OK, K.KVQ_EINVAL, K.KVQ_ENULL, K.KVQ_EALIGN, K.KVQ_ENOLAYOUT,
-                 K.KVQ_EWORKSPACE, K.KVQ_ELAUNCH, -99, 1, 15):
-        s = lib.kvq_strerror(code)
-        assert isinstance(s, bytes) and len(s) > 0
-    assert lib.kvq_strerror(K.KVQ_EWORKSPACE) != lib.kvq_strerror(K.KVQ_EINVAL)
+    lib.kvq_strerror.restype = C.c_char_p
+    codes = (K.KVQ_OK, K.KVQ_EINVAL, K.KVQ_ENULL, K.KVQ_EALIGN, K.KVQ_ENOLAYOUT,
+             K.KVQ_EWORKSPACE, K.KVQ_ELAUNCH, K.KVQ_ENOSCRATCH)
+    texts = [lib.kvq_strerror(c) for c in codes]
+    assert all(isinstance(t, bytes) and len(t) > 0 for t in texts)
+    assert len(set(texts)) == len(codes)                    # one text per return code
+    assert lib.kvq_strerror(-99) == b"unknown"
+    # device status words: each bit its own text, several bits one text,
+    # undefined bits "unknown"
+    bits = (K.STATUS_RESIDUAL_FULL, K.STATUS_CAPACITY, K.STATUS_UNMAPPED_PAGE,
+            K.STATUS_BAD_LENGTH, K.STATUS_RANGE)
+    btexts = [lib.kvq_strerror(b) for b in bits]
+    assert len(set(btexts)) == len(bits) and not set(btexts) & set(texts)
+    assert b"unknown" not in btexts
+    many = lib.kvq_strerror(K.STATUS_CAPACITY | K.STATUS_RANGE)
+    assert many == b"several device status bits" and many not in btexts
+    assert lib.kvq_strerror(32) == b"unknown" and lib.kvq_strerror(1 | 64) == b"unknown"
+    # the header declares each bit the binding names
+    text = open(HEADER).read()
+    for name, val in (("RESIDUAL_FULL", 1), ("CAPACITY", 2), ("UNMAPPED_PAGE", 4),
+                      ("BAD_LENGTH", 8), ("RANGE", 16)):
+        assert re.search(rf"KVQ_STATUS_{name}\s*=\s*{val}u", text), name
 
 
 def test_sink_fields_and_workspace(K):

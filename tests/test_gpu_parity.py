@@ -233,6 +233,28 @@ def test_residual_sizes(R, wid, Hq, Hkv):
     case.check_store()
 
 
+@pytest.mark.parametrize("wid,Hq,Hkv", [(7, 8, 2), (7, 2, 2)])
+def test_merge_most_entries(wid, Hq, Hkv):
+    # the largest merge a layout allows: a 256-token window plus the sink
+    # chunk (five window chunks) and one-page splits over a request that
+    # fills a 256-page table (252 paged splits: the window's 256 tokens and
+    # the sink occupy the rest of its capacity), for the group-of-4 kernel
+    # and the one-query-head kernel; then steps up to the capacity
+    w = inputs.workload(wid, B=2, Hq=Hq, Hkv=Hkv, ctx=(16384 - 16, 900), R=256, sink=32)
+    case = _case(w, extra_tokens=16, split_pages=1)
+    assert case.max_pages == 256
+    case.check_state()
+    case.check_store()
+    out, cert, q = case.decode_now(2)
+    _check_decode(case, out, cert, q)
+    for i in range(16):
+        out, cert, q = case.step(decode=(i in (0, 15)))
+        if out is not None:
+            _check_decode(case, out, cert, q)
+    case.check_status()
+    case.check_state()
+
+
 @pytest.mark.parametrize("ctx", [(1,), (63,), (128,), (129,), (192,), (193,), (300,)])
 def test_kivi4_short_contexts(ctx):
     # contexts inside the fp16 windows, at their edges and past the first flush
@@ -452,6 +474,43 @@ def test_decode_flags_unmapped_page(wid, Hq, Hkv, flags):
             continue
         ref, _ = case.oracle_decode(q, b, h, 1.0)
         assert np.abs(out.cpu().numpy()[b, h * g:(h + 1) * g] - ref).max() <= TOL_O
+
+
+def test_range_flag_value_scale_and_operand_overflow():
+    # leaving the matrix-core stage 1's operand range is reported, and every
+    # kernel still exits normally: (a) values x300 give value scales of a few
+    # hundred (above 255), flagged when the prefill stores them; (b) queries
+    # x2000 against the outlier key channels make |q_c s_c| overflow the f16
+    # operand head, and the stage-1 splits come out non-finite and flag it.
+    # The VALU stage 1 (binary32) has no such range: the same inputs raise no
+    # flag there and decode to finite outputs.
+    import torch
+    from bit_kv_cache_kivi_amd import kvq
+    w = inputs.workload(3, B=2, Hq=8, Hkv=2, ctx=(700, 1301))
+    big_v = _case(w, extra_tokens=64, split_pages=4, kv_scale=(1.0, 300.0))
+    assert big_v.cache.status_word() == kvq.STATUS_RANGE
+    big_v.decode_now(0)
+    assert big_v.cache.status_word() == kvq.STATUS_RANGE
+    generic = _case(w, extra_tokens=64, split_pages=4, kv_scale=(1.0, 300.0),
+                    flags=kvq.FLAG_GENERIC_STAGE1)
+    out, _, _ = generic.decode_now(0)
+    generic.check_status()
+    assert torch.isfinite(out).all()
+
+    plain = _case(w, extra_tokens=64, split_pages=4)
+    plain.check_status()
+    q = (inputs.step_q(w, 0).view(np.float16).astype(np.float32) * 2000.0).astype(np.float16)
+    assert np.isfinite(q.astype(np.float32)).all()
+    qt = torch.from_numpy(q).cuda()
+    out = torch.empty((w.B, w.Hq, 128), dtype=torch.float32, device="cuda")
+    plain.cache.decode(qt, out, sm_scale=w.sm_scale)
+    torch.cuda.synchronize()
+    assert plain.cache.status_word() == kvq.STATUS_RANGE
+    g2 = _case(w, extra_tokens=64, split_pages=4, flags=kvq.FLAG_GENERIC_STAGE1)
+    g2.cache.decode(qt, out, sm_scale=w.sm_scale)
+    torch.cuda.synchronize()
+    g2.check_status()
+    assert torch.isfinite(out).all()
 
 
 def test_prefill_flags_bad_length():
