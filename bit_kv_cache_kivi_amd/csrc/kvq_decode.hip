@@ -461,7 +461,7 @@ __global__ __launch_bounds__(64) void stage1_valu_kernel(KParams P, const uint16
     // the split's page ids, one per lane (an id outside the pool is flagged
     // and page 0 read instead)
     const int np = p1 - p0;                      // <= split_pages <= 64
-    int pid_l = lane < np ? P.table[(size_t)b * P.max_pages + p0 + lane] : 0;
+    int pid_l = (lane < np && p0 + lane < P.max_pages) ? P.table[(size_t)b * P.max_pages + p0 + lane] : 0;
     const bool bad = lane < np && (pid_l < 0 || pid_l >= P.n_pages);
     if (__any(bad)) {
         if (lane == 0) atomicOr(P.status, (uint32_t)KVQ_STATUS_UNMAPPED_PAGE);
@@ -795,10 +795,17 @@ __device__ inline float row_sum16(float v) {
 }
 
 struct Gqa4State {
-    float m[4];
-    float lsum[4];
-    float zacc[4][4];               // sum_t p_{h,t} z_{t,j} over this lane's tokens [query][group]
+    float m[4];                     // running maximum per query (log2 units), the same in every lane
+    float ma, mb;                   // m of this lane's two queries a = 2 (lane >> 4 & 1), a + 1
+    float la, lb;                   // this lane's share of l for queries a and a + 1
+    float za[4], zb[4];             // sum_t p_t z_{t,j} over this lane's tokens [group j]
     f4v acc[8];
+};
+
+// A page's registers: key statistics and codes, the value statistics of the
+// lane's two softmax tokens, and the value codes.
+struct Gqa4Page {
+    uint4 ks, vs0, vs1, ka, kb, va, vb;
 };
 
 constexpr int AS_STRIDE = 20;       // octets per score-operand row (16 + bank padding)
@@ -807,23 +814,44 @@ constexpr int AS_STRIDE = 20;       // octets per score-operand row (16 + bank p
 // by one 16-lane group of an operand load start on 16 distinct 4-bank groups
 constexpr int BT_STRIDE = 72;
 
-// The scores and the P.V operand are live in turn within a page step (one
-// wave: LDS accesses complete in program order), so they share storage.
 struct Gqa4Smem {
-    h8v As[2][9][AS_STRIDE];        // score A: [key group][row 0..3 hi, 4..7 lo, 8 = zero][channel octet]
-    union {
-        f4v zsh[2][PT];                 // scores from the hi and the lo operand rows [token][query]
-        _Float16 Bs[2][16][BT_STRIDE];  // P.V B: [operand][column (h, part, js)][token]
-    };
+    h8v As[2][8][AS_STRIDE];        // score A: [key group][row 2h = hi(q_h s), 2h + 1 = lo][channel octet]
+    h8v Az[AS_STRIDE];              // a zero row (the other key group's operand rows)
+    _Float16 Bs[2][16][BT_STRIDE];  // P.V B: [operand][column (h, part, js)][token]
 };
 
+// Token of this lane's first softmax score (the second is 16 later): lane
+// 16 G + r holds tokens 32 (G >> 1) + r, + 16, both in key group G >> 1.
+__device__ inline int gqa4_token(int lane) { return 32 * (lane >> 5) + (lane & 15); }
+
+__device__ inline Gqa4Page load_gqa4_page(const uint8_t *page, int extent, const Geom &G, int lane) {
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc((void *)page, (short)0, extent, 0x00020000);
+    const int o = 16 * lane, t0 = gqa4_token(lane);
+    Gqa4Page R;                                 // issued in the order of use
+    R.ks = bload(rs, G.ks + o);
+    R.ka = bload(rs, G.kc + o);
+    R.kb = bload(rs, G.kc + 1024 + o);
+    R.vs0 = bload(rs, G.vs + 16 * t0);
+    R.vs1 = bload(rs, G.vs + 16 * (t0 + 16));
+    R.va = bload(rs, G.vc + o);
+    R.vb = bload(rs, G.vc + 1024 + o);
+    return R;
+}
+
 // One 64-token page.  nvalid < 64 only on the last page of the prefix.
-__device__ inline void gqa4_page(const PageRegs &R, Gqa4State &S, Gqa4Smem &sm, const uint2 *qw,
-                                 int lane, int nvalid, float qscale) {
+//
+// Scores: operand A1 carries key group 0's hi/lo rows in rows 0..7 and zeros
+// in rows 8..15, A2 the zeros in rows 0..7 and group 1's rows in rows 8..15;
+// accumulator s[n2] takes A1 x tile n2 and A2 x tile n2 + 2.  Lane 16 G + r
+// then holds, for queries a = 2 (G & 1) and a + 1, the hi and lo sums of
+// token 32 (G >> 1) + r in s[0] and of the token 16 later in s[1]: the
+// softmax runs in the products' own layout, two tokens by two queries a
+// lane, and every token of a lane is in key group G >> 1.
+__device__ inline void gqa4_page(const Gqa4Page &R, Gqa4State &S, Gqa4Smem &sm, const uint2 *qw,
+                                 const h8v *a1, const h8v *a2, int lane, int nvalid, float qscale) {
     const int g = lane >> 4, r = lane & 15;
     const int hp = r >> 2;
     const uint32_t MSK = 0x33333333u;
-    float bias[4];                         // sum_c q_h z_c of this lane's key group, times qscale
 
     lds_sync();                            // previous page done with the LDS
 
@@ -838,122 +866,143 @@ __device__ inline void gqa4_page(const PageRegs &R, Gqa4State &S, Gqa4Smem &sm, 
         uint32_t hv0, lv0, hv1, lv1;
         split_qs(qw[h].x, sz[0], sz[1], hv0, lv0);
         split_qs(qw[h].y, sz[2], sz[3], hv1, lv1);
-        ((uint2 *)&sm.As[gi_p][h][0])[lane & 31] = make_uint2(hv0, hv1);
-        ((uint2 *)&sm.As[gi_p][4 + h][0])[lane & 31] = make_uint2(lv0, lv1);
+        ((uint2 *)&sm.As[gi_p][2 * h][0])[lane & 31] = make_uint2(hv0, hv1);
+        ((uint2 *)&sm.As[gi_p][2 * h + 1][0])[lane & 31] = make_uint2(lv0, lv1);
         float bz = fma_qz<0>(qw[h].x, sz[0], 0.0f);
         bz = fma_qz<1>(qw[h].x, sz[1], bz);
         bz = fma_qz<0>(qw[h].y, sz[2], bz);
         bzp[h] = fma_qz<1>(qw[h].y, sz[3], bz);
     }
     // Sum the shares over the 32 lanes of the key group, reduce-scatter
-    // style: after the two quad exchanges lane L holds query 2 (L & 1) +
-    // ((L >> 1) & 1) summed over its quad; rotations within the 16-lane row
-    // and one exchange between the group's two rows finish the sum.
-    const bool b0 = lane & 1, b1 = (lane & 2) != 0;
-    float k0 = b0 ? bzp[2] : bzp[0], k1 = b0 ? bzp[3] : bzp[1];
-    k0 += dppf<0xB1>(b0 ? bzp[0] : bzp[2]);            // quad_perm [1,0,3,2]
-    k1 += dppf<0xB1>(b0 ? bzp[1] : bzp[3]);
+    // style.  With f = (L & 1) ^ (L >> 4 & 1), the first quad exchange keeps
+    // queries (0, 1) where f = 0 and (2, 3) where f = 1, the second keeps the
+    // first of the pair where L & 2 = 0: quad position p holds query
+    // 2 (p & 1 ^ L >> 4 & 1) + (p >> 1), so positions 0 and 2 hold the two
+    // queries a, a + 1 of the lane's score layout.  Rotations within the row
+    // add the row's quads; the two rows of the group hold a query at quad
+    // positions differing in bit 0, hence the exchange with lane ^ 17.
+    const bool f = ((lane ^ (lane >> 4)) & 1) != 0, b1 = (lane & 2) != 0;
+    float k0 = f ? bzp[2] : bzp[0], k1 = f ? bzp[3] : bzp[1];
+    k0 += dppf<0xB1>(f ? bzp[0] : bzp[2]);             // quad_perm [1,0,3,2]
+    k1 += dppf<0xB1>(f ? bzp[1] : bzp[3]);
     float kq = b1 ? k1 : k0;
     kq += dppf<0x4E>(b1 ? k0 : k1);                    // quad_perm [2,3,0,1]
     kq += dppf<0x124>(kq);                             // row_ror:4
     kq += dppf<0x128>(kq);                             // row_ror:8
-    kq += __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, kq), 0x401F));  // lane ^ 16
+    kq += __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, kq), 0x441F));  // lane ^ 17
     kq *= qscale;
-    // query h sits in quad position (h >> 1) + 2 (h & 1): 0, 2, 1, 3
-    bias[0] = dppf<0x00>(kq);
-    bias[1] = dppf<0xAA>(kq);
-    bias[2] = dppf<0x55>(kq);
-    bias[3] = dppf<0xFF>(kq);
+    const float bias_a = dppf<0x00>(kq), bias_b = dppf<0xAA>(kq);
     lds_sync();
 
-    // ---- scores on the matrix cores: operand rows 0..3 carry the hi parts and
-    // rows 4..7 the lo parts of the four queries, so one product per token
-    // tile gives both; the four tiles are independent accumulators ----
+    // ---- scores on the matrix cores ----
     const uint32_t kd[8] = {R.ka.x, R.ka.y, R.ka.z, R.ka.w, R.kb.x, R.kb.y, R.kb.z, R.kb.w};
-    f4v sc[4];
-#pragma unroll
-    for (int n = 0; n < 4; n++) sc[n] = f4v{0.f, 0.f, 0.f, 0.f};
-    const int arow = r < 8 ? r : 8;
+    f4v sc[2] = {f4v{0.f, 0.f, 0.f, 0.f}, f4v{0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
     for (int kc = 0; kc < 4; kc++) {
-        h8v af[2];
+        const h8v af1 = a1[4 * kc + g], af2 = a2[4 * kc + g];
 #pragma unroll
-        for (int gi = 0; gi < 2; gi++) af[gi] = sm.As[gi][arow][r < 8 ? 4 * kc + g : 0];
-#pragma unroll
-        for (int n = 0; n < 4; n++) {
-            const uint32_t x = kd[2 * n + (kc >> 1)];
+        for (int n2 = 0; n2 < 2; n2++) {
+            const uint32_t x = kd[2 * n2 + (kc >> 1)];
             const h8v bf = frag8((kc & 1) ? ((x >> 2) & MSK) : (x & MSK));
-            sc[n] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[n >> 1], bf, sc[n], 0, 0, 0);
+            sc[n2] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af1, bf, sc[n2], 0, 0, 0);
+        }
+#pragma unroll
+        for (int n2 = 0; n2 < 2; n2++) {
+            const uint32_t x = kd[2 * (n2 + 2) + (kc >> 1)];
+            const h8v bf = frag8((kc & 1) ? ((x >> 2) & MSK) : (x & MSK));
+            sc[n2] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af2, bf, sc[n2], 0, 0, 0);
         }
     }
-    if (lane < 32) {                            // rows 0..3 (lanes 0..15) and 4..7 (16..31)
-#pragma unroll
-        for (int n = 0; n < 4; n++) sm.zsh[g][16 * n + r] = sc[n];
-    }
-    lds_sync();
 
-    // ---- online softmax, lane = token ----
-    const f4v bz4 = f4v{bias[0], bias[1], bias[2], bias[3]};   // lane = token: its key group's
-    const f4v z = (sm.zsh[0][lane] + sm.zsh[1][lane]) * qscale + bz4;     // log2 units
-    float zz[4] = {z[0], z[1], z[2], z[3]};
+    // ---- online softmax: tokens t0 and t0 + 16, queries a and a + 1 ----
+    float z[2][2];                              // [token][query a, a + 1], log2 units
+#pragma unroll
+    for (int j = 0; j < 2; j++) {
+        z[j][0] = fmaf(sc[j][0] + sc[j][1], qscale, bias_a);
+        z[j][1] = fmaf(sc[j][2] + sc[j][3], qscale, bias_b);
+    }
+    const int t0 = gqa4_token(lane);
     if (nvalid < PT) {                          // uniform: only the prefix's last page
 #pragma unroll
-        for (int i = 0; i < 4; i++)
-            if (lane >= nvalid) zz[i] = -INFINITY;
+        for (int j = 0; j < 2; j++)
+            if (t0 + 16 * j >= nvalid) z[j][0] = z[j][1] = -INFINITY;
     }
-    bool exceed = false;
-#pragma unroll
-    for (int i = 0; i < 4; i++) exceed |= zz[i] > S.m[i] + LAZY_TAU;
+    const bool exceed = z[0][0] > S.ma + LAZY_TAU || z[1][0] > S.ma + LAZY_TAU ||
+                        z[0][1] > S.mb + LAZY_TAU || z[1][1] > S.mb + LAZY_TAU;
     if (__any(exceed)) {
+        // the new maxima: over the 32 lanes holding each query (lane bits
+        // 0..3 and 5), then moved in every lane
+        float mt[2] = {fmaxf(z[0][0], z[1][0]), fmaxf(z[0][1], z[1][1])};
+#pragma unroll
+        for (int k = 0; k < 2; k++) {
+#pragma unroll
+            for (int msk = 1; msk < 16; msk <<= 1) mt[k] = fmaxf(mt[k], shfl_xor(mt[k], msk));
+            mt[k] = fmaxf(mt[k], shfl_xor(mt[k], 32));
+        }
         float alpha[4];
 #pragma unroll
         for (int i = 0; i < 4; i++) {
-            float mt = zz[i];
-#pragma unroll
-            for (int msk = 1; msk < 64; msk <<= 1) mt = fmaxf(mt, shfl_xor(mt, msk));
-            // the same in every lane: kept in a scalar register
-            mt = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, mt)));
-            const float mn = fmaxf(S.m[i], mt);
+            // query i lives in lanes 16 (i >> 1) + ..: slot i & 1 of lane 16 (i >> 1)
+            const float mi = __builtin_bit_cast(float, __builtin_amdgcn_readlane(
+                                 __builtin_bit_cast(int, mt[i & 1]), 16 * (i >> 1)));
+            const float mn = fmaxf(S.m[i], mi);
             alpha[i] = __builtin_amdgcn_exp2f(S.m[i] - mn);
             S.m[i] = mn;
-            S.lsum[i] *= alpha[i];
+        }
+        const bool hi2 = (g & 1) != 0;
+        S.ma = hi2 ? S.m[2] : S.m[0];
+        S.mb = hi2 ? S.m[3] : S.m[1];
+        const float aa = hi2 ? alpha[2] : alpha[0], ab = hi2 ? alpha[3] : alpha[1];
+        S.la *= aa;
+        S.lb *= ab;
+#pragma unroll
+        for (int j = 0; j < 4; j++) {
+            S.za[j] *= aa;
+            S.zb[j] *= ab;
         }
         const float ap = hp == 0 ? alpha[0] : hp == 1 ? alpha[1] : hp == 2 ? alpha[2] : alpha[3];
 #pragma unroll
-        for (int i = 0; i < 4; i++)
-#pragma unroll
-            for (int j = 0; j < 4; j++) S.zacc[i][j] *= alpha[i];
-#pragma unroll
         for (int nt = 0; nt < 8; nt++) S.acc[nt] *= ap;
     }
-    float pq[4];                                // p of this lane's token, per query
+    float p[2][2];                              // [token][query a, a + 1]
 #pragma unroll
-    for (int i = 0; i < 4; i++) {
-        pq[i] = __builtin_amdgcn_exp2f(zz[i] - S.m[i]);
-        S.lsum[i] += pq[i];
+    for (int j = 0; j < 2; j++) {
+        p[j][0] = __builtin_amdgcn_exp2f(z[j][0] - S.ma);
+        p[j][1] = __builtin_amdgcn_exp2f(z[j][1] - S.mb);
     }
+    S.la += p[0][0] + p[1][0];
+    S.lb += p[0][1] + p[1][1];
 
-    // ---- P.V operand, lane = token: p_{h,t} s_{t,j} split into f16 hi and
-    // lo, stored as the B columns (h, part, js) of operand j >> 1 (j = 2 (j >> 1)
-    // + js); sum_t p_{h,t} z_{t,j} on the side ----
+    // ---- P.V operand: p_{h,t} s_{t,j} split into f16 hi and lo, stored as
+    // the B columns (h, part, js) of operand j >> 1 (js = j & 1) at token t;
+    // sum_t p_{h,t} z_{t,j} on the side.  (Statistics of tokens past nvalid
+    // read as zeros: the page's extent.) ----
     {
-        // (statistics of tokens past nvalid read as zeros: the page's extent)
-        const uint32_t vw[4] = {R.vs.x, R.vs.y, R.vs.z, R.vs.w};
+        const int ha = 2 * (g & 1);
 #pragma unroll
-        for (int h = 0; h < 4; h++) {
+        for (int j = 0; j < 2; j++) {
+            const uint4 v4 = j ? R.vs1 : R.vs0;
+            const uint32_t vw[4] = {v4.x, v4.y, v4.z, v4.w};
+            const int t = t0 + 16 * j;
 #pragma unroll
-            for (int j = 0; j < 4; j++) S.zacc[h][j] = fmaf(pq[h], (float)hi16h(vw[j]), S.zacc[h][j]);
-            uint32_t h01, l01, h23, l23;
-            split_ps(pq[h], vw[0], vw[1], h01, l01);
-            split_ps(pq[h], vw[2], vw[3], h23, l23);
-            sm.Bs[0][4 * h + 0][lane] = lo16h(h01);
-            sm.Bs[0][4 * h + 1][lane] = hi16h(h01);
-            sm.Bs[0][4 * h + 2][lane] = lo16h(l01);
-            sm.Bs[0][4 * h + 3][lane] = hi16h(l01);
-            sm.Bs[1][4 * h + 0][lane] = lo16h(h23);
-            sm.Bs[1][4 * h + 1][lane] = hi16h(h23);
-            sm.Bs[1][4 * h + 2][lane] = lo16h(l23);
-            sm.Bs[1][4 * h + 3][lane] = hi16h(l23);
+            for (int k = 0; k < 2; k++) {
+                const float pk = p[j][k];
+                float *zk = k ? S.zb : S.za;
+#pragma unroll
+                for (int jv = 0; jv < 4; jv++) zk[jv] = fmaf(pk, (float)hi16h(vw[jv]), zk[jv]);
+                uint32_t h01, l01, h23, l23;
+                split_ps(pk, vw[0], vw[1], h01, l01);
+                split_ps(pk, vw[2], vw[3], h23, l23);
+                const int c = 4 * (ha + k);
+                sm.Bs[0][c + 0][t] = lo16h(h01);
+                sm.Bs[0][c + 1][t] = hi16h(h01);
+                sm.Bs[0][c + 2][t] = lo16h(l01);
+                sm.Bs[0][c + 3][t] = hi16h(l01);
+                sm.Bs[1][c + 0][t] = lo16h(h23);
+                sm.Bs[1][c + 1][t] = hi16h(h23);
+                sm.Bs[1][c + 2][t] = lo16h(l23);
+                sm.Bs[1][c + 3][t] = hi16h(l23);
+            }
         }
     }
     lds_sync();
@@ -996,22 +1045,22 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(3, 8))) void
     const size_t bh = (size_t)b * P.Hkv + h;
     const int p0 = s * P.split_pages;
 
-    // the length, the split's page ids (one per lane) and the query are
-    // independent loads, issued together
+    // the length first: a split past the prefix exits before any other load
     const int l = P.state[bh * 4];
-    int pid_l = (lane < P.split_pages && p0 + lane < P.max_pages) ? P.table[(size_t)b * P.max_pages + p0 + lane] : 0;
-    // the four queries at this lane's score-operand channels 4 (lane & 31) .. +3
-    // (unscaled: keeps q s in the range where the f16 remainder is a normal number)
-    uint2 qw[4];
-#pragma unroll
-    for (int hq = 0; hq < 4; hq++)
-        qw[hq] = *(const uint2 *)(q + ((size_t)b * P.Hq + (size_t)h * 4 + hq) * D + 4 * (lane & 31));
-
     const int nvq = max(0, l - P.sink - P.R);          // quantized values, counted from the sink
     const int npages = (nvq + PT - 1) / PT;
     const int p1 = min(p0 + P.split_pages, npages);
     if (p0 >= p1) return;
     const int np = p1 - p0;                      // <= split_pages <= 64
+
+    // the split's page ids (one per lane) and the four queries at this lane's
+    // score-operand channels 4 (lane & 31) .. +3 (unscaled: keeps q s in the
+    // range where the f16 remainder is a normal number)
+    int pid_l = (lane < np && p0 + lane < P.max_pages) ? P.table[(size_t)b * P.max_pages + p0 + lane] : 0;
+    uint2 qw[4];
+#pragma unroll
+    for (int hq = 0; hq < 4; hq++)
+        qw[hq] = *(const uint2 *)(q + ((size_t)b * P.Hq + (size_t)h * 4 + hq) * D + 4 * (lane & 31));
 
     const bool bad = lane < np && (pid_l < 0 || pid_l >= P.n_pages);
     if (__any(bad)) {
@@ -1019,21 +1068,19 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(3, 8))) void
         pid_l = bad ? 0 : pid_l;                 // read page 0 instead; the result is flagged
     }
 
-    if (lane < 16) {
-        sm.As[0][8][lane] = h8v{0, 0, 0, 0, 0, 0, 0, 0};
-        sm.As[1][8][lane] = h8v{0, 0, 0, 0, 0, 0, 0, 0};
-    }
+    if (lane < 16) sm.Az[lane] = h8v{0, 0, 0, 0, 0, 0, 0, 0};
+    // this lane's score-operand rows: row r & 7 of key group 0 (A1) or 1 (A2)
+    // where its row r belongs to that group's half, else the zero row
+    const h8v *a1 = r < 8 ? &sm.As[0][r][0] : &sm.Az[0];
+    const h8v *a2 = r < 8 ? &sm.Az[0] : &sm.As[1][r - 8][0];
 
     Gqa4State S;
 #pragma unroll
-    for (int i = 0; i < 4; i++) {
-        S.m[i] = -INFINITY;
-        S.lsum[i] = 0.f;
-    }
+    for (int i = 0; i < 4; i++) S.m[i] = -INFINITY;
+    S.ma = S.mb = -INFINITY;
+    S.la = S.lb = 0.f;
 #pragma unroll
-    for (int i = 0; i < 4; i++)
-#pragma unroll
-        for (int j = 0; j < 4; j++) S.zacc[i][j] = 0.f;
+    for (int j = 0; j < 4; j++) S.za[j] = S.zb[j] = 0.f;
 #pragma unroll
     for (int nt = 0; nt < 8; nt++) S.acc[nt] = f4v{0.f, 0.f, 0.f, 0.f};
 
@@ -1043,22 +1090,22 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(3, 8))) void
     // is in flight.  (A deeper ring costs the registers of a third wave per
     // SIMD, which hides more latency than a second page in flight.)  Loads
     // past the split's end are issued too, with an empty extent.
-    auto run_page = [&](const PageRegs &R, int i) {
-        gqa4_page(R, S, sm, qw, lane, min(PT, nvq - (p0 + i) * PT), qscale);
+    auto run_page = [&](const Gqa4Page &R, int i) {
+        gqa4_page(R, S, sm, qw, a1, a2, lane, min(PT, nvq - (p0 + i) * PT), qscale);
     };
     auto page_ld = [&](int i) {
         const uint8_t *pg = base + (size_t)__builtin_amdgcn_readlane(pid_l, min(i, np - 1)) * pstride;
         // extent: the whole page, up to the value statistics of its last
         // valid token on the prefix's last page, nothing past the split
         const int ext = i < np ? G.vs + 16 * min(PT, nvq - (p0 + i) * PT) : 0;
-        return load_page_ext(pg, ext, G, lane);
+        return load_gqa4_page(pg, ext, G, lane);
     };
     // (scheduling barriers keep each page's loads together and in order, so
     // the wait before a page counts only the loads of the pages after it)
-    PageRegs ra = page_ld(0);
+    Gqa4Page ra = page_ld(0);
     __builtin_amdgcn_sched_barrier(0);
     for (int i = 0; i < np; i += 2) {
-        PageRegs rb = page_ld(i + 1);
+        Gqa4Page rb = page_ld(i + 1);
         __builtin_amdgcn_sched_barrier(0);
         run_page(ra, i);
         ra = page_ld(i + 2);
@@ -1067,18 +1114,28 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(3, 8))) void
     }
 
     // ---- reduce and write the split's partial ----
+    // l and the zero-point sums of query a, a + 1: over the 32 lanes holding
+    // them (lane bits 0..3 and 5); query i then sits in lane 16 (i >> 1)
+#pragma unroll
+    for (int msk = 1; msk < 64; msk <<= 1) {
+        if (msk == 16) continue;
+        S.la += shfl_xor(S.la, msk);
+        S.lb += shfl_xor(S.lb, msk);
+#pragma unroll
+        for (int j = 0; j < 4; j++) {
+            S.za[j] += shfl_xor(S.za[j], msk);
+            S.zb[j] += shfl_xor(S.zb[j], msk);
+        }
+    }
+    auto query_val = [&](float va, float vb, int i) {   // value of query i, uniform
+        const float v = (i & 1) ? vb : va;
+        return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 16 * (i >> 1)));
+    };
+    float lsum[4];
+#pragma unroll
+    for (int i = 0; i < 4; i++) lsum[i] = query_val(S.la, S.lb, i);
     const int hp = r >> 2, part = (r >> 1) & 1, js = r & 1;
-#pragma unroll
-    for (int i = 0; i < 4; i++)
-#pragma unroll
-        for (int msk = 1; msk < 64; msk <<= 1) S.lsum[i] += shfl_xor(S.lsum[i], msk);
-#pragma unroll
-    for (int i = 0; i < 4; i++)
-#pragma unroll
-        for (int j = 0; j < 4; j++)
-#pragma unroll
-            for (int msk = 1; msk < 64; msk <<= 1) S.zacc[i][j] += shfl_xor(S.zacc[i][j], msk);
-    const float lh = hp == 0 ? S.lsum[0] : hp == 1 ? S.lsum[1] : hp == 2 ? S.lsum[2] : S.lsum[3];
+    const float lh = hp == 0 ? lsum[0] : hp == 1 ? lsum[1] : hp == 2 ? lsum[2] : lsum[3];
     const float il = 1.0f / lh;
     const size_t row = part_row(W, P.Hq, b, 4 * h + hp, s);
     bool nonfinite = !__builtin_isfinite(lh);
@@ -1087,9 +1144,13 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(3, 8))) void
         f4v lo;                                   // the lo column, two lanes up
 #pragma unroll
         for (int i = 0; i < 4; i++) lo[i] = __shfl_down(S.acc[nt][i], 2, 16);
-        if (part == 0 && js == ((nt >> 1) & 1)) {
-            const int j = nt >> 1;
-            const float zj = hp == 0 ? S.zacc[0][j] : hp == 1 ? S.zacc[1][j] : hp == 2 ? S.zacc[2][j] : S.zacc[3][j];
+        const int j = nt >> 1;
+        // z sums of value group j for the four queries (uniform reads)
+        float zq[4];
+#pragma unroll
+        for (int i = 0; i < 4; i++) zq[i] = query_val(S.za[j], S.zb[j], i);
+        if (part == 0 && js == (j & 1)) {
+            const float zj = hp == 0 ? zq[0] : hp == 1 ? zq[1] : hp == 2 ? zq[2] : zq[3];
             const f4v o = (S.acc[nt] + lo + zj) * il;
 #pragma unroll
             for (int i = 0; i < 4; i++) nonfinite |= !__builtin_isfinite(o[i]);
@@ -1098,7 +1159,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(3, 8))) void
     }
     flag_range(P, nonfinite, lane);
     if (lane < 4) {
-        const float li = lane == 0 ? S.lsum[0] : lane == 1 ? S.lsum[1] : lane == 2 ? S.lsum[2] : S.lsum[3];
+        const float li = lane == 0 ? lsum[0] : lane == 1 ? lsum[1] : lane == 2 ? lsum[2] : lsum[3];
         const float mi = lane == 0 ? S.m[0] : lane == 1 ? S.m[1] : lane == 2 ? S.m[2] : S.m[3];
         const size_t row_i = part_row(W, P.Hq, b, 4 * h + lane, s);
         W.ml[row_i] = make_float2(mi + log2f(li), 1.0f);
@@ -1684,7 +1745,7 @@ __global__ __launch_bounds__(64) void stage1_witcert_paged_kernel(KParams P, con
 
     // the split's page ids, one per lane (at most 64 pages)
     const int np = p1 - p0;
-    int pid_l = lane < np ? P.table[(size_t)b * P.max_pages + p0 + lane] : 0;
+    int pid_l = (lane < np && p0 + lane < P.max_pages) ? P.table[(size_t)b * P.max_pages + p0 + lane] : 0;
     {
         const bool bad = lane < np && (pid_l < 0 || pid_l >= P.n_pages);
         if (__any(bad)) {
