@@ -164,10 +164,17 @@ int kvq_set_layout(kvq_cache_t *cache, const kvq_layout_t *layout, const kvq_buf
     if (sp == 0) {
         // default: one 256-token block per split for WITCERT; 4 pages for
         // short caches (more splits to fill the chip), 12 for longer ones
-        // (fewer partials to merge), at least what keeps <= 256 splits
+        // (fewer partials to merge), 16 for the GQA kernel, whose splits run
+        // from a work list (longest first, so no split size is favoured by
+        // the dispatch order), at least what keeps <= 256 splits
+        const bool gqa4 = layout->scheme == KVQ_SCHEME_KIVI2 &&
+                          layout->n_q_heads == 4 * layout->n_kv_heads &&
+                          !(layout->flags & KVQ_FLAG_GENERIC_STAGE1);
         sp = layout->scheme == KVQ_SCHEME_WITCERT ? 1
              : wtok                                 ? 4      // 256 tokens, as one WITCERT block
-             : (layout->max_pages <= 128 ? 4 : 12);
+             : layout->max_pages <= 128             ? 4
+             : gqa4                                 ? 16
+                                                    : 12;
         sp = std::max(sp, (layout->max_pages + kvq::MAX_SPLITS - 1) / kvq::MAX_SPLITS);
     }
     // the merge takes at most MAX_SPLITS splits per query head
@@ -183,7 +190,10 @@ size_t kvq_workspace_bytes(const kvq_cache_t *cache) {
     // fp16 window
     const size_t rows =
         (size_t)cache->layout.batch * cache->layout.n_q_heads * (max_splits(cache) + n_win(cache));
-    return rows * kvq::D * sizeof(float) + rows * sizeof(float2) + 256;
+    // and the stage-1 work list: one item per (request, KV head, split),
+    // then its length (in the last 256 bytes)
+    const size_t items = (size_t)cache->layout.batch * cache->layout.n_kv_heads * max_splits(cache);
+    return rows * kvq::D * sizeof(float) + rows * sizeof(float2) + items * sizeof(uint2) + 256;
 }
 
 int kvq_append_token(const kvq_cache_t *cache, const uint16_t *k_new, const uint16_t *v_new,
@@ -210,8 +220,11 @@ int decode_with(const kvq_cache_t *cache, const uint16_t *q, float *out, float *
     W.max_splits = max_splits(cache);
     W.n_win = n_win(cache);
     const size_t rows = (size_t)cache->layout.batch * cache->layout.n_q_heads * (W.max_splits + W.n_win);
+    const size_t items = (size_t)cache->layout.batch * cache->layout.n_kv_heads * W.max_splits;
     W.o = (float *)workspace;
     W.ml = (float2 *)((char *)workspace + rows * kvq::D * sizeof(float));
+    W.items = (uint2 *)((char *)W.ml + rows * sizeof(float2));
+    W.n_items = (uint32_t *)(W.items + items);
     W.ev_begin = cache->ev_stage1_begin;
     W.ev_end = cache->ev_stage1_end;
     return kvq::launch_decode(params(cache), q, out, cert, sm_scale, kappa, W, stream) == hipSuccess

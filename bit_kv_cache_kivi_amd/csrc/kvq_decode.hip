@@ -1027,31 +1027,106 @@ __device__ inline void gqa4_page(const Gqa4Page &R, Gqa4State &S, Gqa4Smem &sm, 
     }
 }
 
+// Stage-1 work list of the GQA kernel: the paged splits that hold pages,
+// full ones (split_pages pages) first in (request, KV head, split) order,
+// then each pair's shorter last split, longest first.  Workgroups are
+// dispatched in order and round-robin over the XCDs, so similar items sit
+// side by side and the shortest run last.  Item: x = b Hkv + h, y = split |
+// pages << 8 | valid tokens of its last page << 16.  One workgroup.
+constexpr int PLAN_T = 1024;
+
+__global__ __launch_bounds__(PLAN_T) void plan_kernel(KParams P, Workspace W) {
+    const int npair = P.B * P.Hkv, sp = P.split_pages, tid = threadIdx.x;
+    __shared__ int cnt[65];                 // short last splits per page count
+    __shared__ int cur[65];                 // their next free slot
+    __shared__ int scan[PLAN_T];
+    __shared__ int carry;
+    for (int i = tid; i < 65; i += PLAN_T) cnt[i] = 0;
+    if (tid == 0) carry = 0;
+    __syncthreads();
+    // quantized values of a pair, and its pages (capped by its page-table row)
+    auto nvq_of = [&](int pr) { return max(0, P.state[(size_t)pr * 4] - P.sink - P.R); };
+    auto pages_of = [&](int nvq) { return min((nvq + PT - 1) / PT, P.max_pages); };
+    // pass 1: the full splits (their total) and the short ones per page count
+    int nfull_tot = 0;
+    for (int pr = tid; pr < npair; pr += PLAN_T) {
+        const int npg = pages_of(nvq_of(pr));
+        nfull_tot += npg / sp;
+        if (npg % sp) atomicAdd(&cnt[npg % sp], 1);
+    }
+    scan[tid] = nfull_tot;
+    __syncthreads();
+    for (int off = PLAN_T / 2; off > 0; off >>= 1) {
+        if (tid < off) scan[tid] += scan[tid + off];
+        __syncthreads();
+    }
+    const int F = scan[0];
+    __syncthreads();
+    if (tid == 0) {                         // short splits after the full ones, longest first
+        int o = F;
+        for (int k = sp - 1; k >= 1; k--) {
+            cur[k] = o;
+            o += cnt[k];
+        }
+        *W.n_items = (uint32_t)o;
+    }
+    __syncthreads();
+    // pass 2: the items, full splits at their prefix position in pair order
+    for (int c0 = 0; c0 < npair; c0 += PLAN_T) {
+        const int pr = c0 + tid;
+        const int nvq = pr < npair ? nvq_of(pr) : 0;
+        const int npg = pages_of(nvq);
+        const int nfull = npg / sp, rem = npg % sp;
+        const int nv_last = npg ? min(PT, nvq - (npg - 1) * PT) : 0;
+        scan[tid] = nfull;                  // inclusive scan over the chunk
+        __syncthreads();
+        for (int off = 1; off < PLAN_T; off <<= 1) {
+            const int v = tid >= off ? scan[tid - off] : 0;
+            __syncthreads();
+            scan[tid] += v;
+            __syncthreads();
+        }
+        const int first = carry + scan[tid] - nfull;
+        for (int k = 0; k < nfull; k++) {
+            const bool last = rem == 0 && k == nfull - 1;
+            W.items[first + k] = make_uint2((uint32_t)pr, (uint32_t)k | (uint32_t)sp << 8 |
+                                                          (uint32_t)(last ? nv_last : PT) << 16);
+        }
+        if (rem) {
+            const int slot = atomicAdd(&cur[rem], 1);
+            W.items[slot] = make_uint2((uint32_t)pr, (uint32_t)nfull | (uint32_t)rem << 8 | (uint32_t)nv_last << 16);
+        }
+        __syncthreads();
+        if (tid == PLAN_T - 1) carry += scan[tid];
+        __syncthreads();
+    }
+}
+
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(3, 8))) void stage1_gqa4_mfma_kernel(KParams P, const uint16_t *__restrict__ q,
                                                               Workspace W, float qscale) {
-    const S1Item it = s1_item(W.max_splits, W.n_win);
-    const int s = it.s, h = it.hd, b = it.b;
     const int lane = threadIdx.x, g = lane >> 4, r = lane & 15;
     const Geom G = geom(P.scheme, P.nb);
     __shared__ union {
         Gqa4Smem pg;
         WinSmem win;
     } U;
-    if (it.window) {                             // the KV head's fp16 window
-        window_partial<4, PT, KVQ_SCHEME_KIVI2>(P, q, W, qscale, b, h, 4 * h, s, lane, U.win);
+    // the window chunks come first in the grid; then the paged splits, in the
+    // order of the work list (longest first), and workgroups past its end exit
+    const int L = blockIdx.x + gridDim.x * (blockIdx.y + gridDim.y * blockIdx.z);
+    const int nw = gridDim.y * gridDim.z * W.n_win;
+    if (L < nw) {                                // the KV head's fp16 window
+        const S1Item it = s1_item(W.max_splits, W.n_win);
+        window_partial<4, PT, KVQ_SCHEME_KIVI2>(P, q, W, qscale, it.b, it.hd, 4 * it.hd, it.s, lane, U.win);
         return;
     }
+    if (L - nw >= (int)*W.n_items) return;
+    const uint2 item = W.items[L - nw];
+    const int b = (int)(item.x / (uint32_t)P.Hkv), h = (int)(item.x % (uint32_t)P.Hkv);
+    const int s = item.y & 255, np = (item.y >> 8) & 127, nv_last = item.y >> 16;
     Gqa4Smem &sm = U.pg;
-    const size_t bh = (size_t)b * P.Hkv + h;
     const int p0 = s * P.split_pages;
-
-    // the length first: a split past the prefix exits before any other load
-    const int l = P.state[bh * 4];
-    const int nvq = max(0, l - P.sink - P.R);          // quantized values, counted from the sink
-    const int npages = (nvq + PT - 1) / PT;
-    const int p1 = min(p0 + P.split_pages, npages);
-    if (p0 >= p1) return;
-    const int np = p1 - p0;                      // <= split_pages <= 64
+    // valid tokens of the split's page i (only the prefix's last page is short)
+    auto nvalid = [&](int i) { return i == np - 1 ? nv_last : PT; };
 
     // the split's page ids (one per lane) and the four queries at this lane's
     // score-operand channels 4 (lane & 31) .. +3 (unscaled: keeps q s in the
@@ -1091,13 +1166,13 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(3, 8))) void
     // SIMD, which hides more latency than a second page in flight.)  Loads
     // past the split's end are issued too, with an empty extent.
     auto run_page = [&](const Gqa4Page &R, int i) {
-        gqa4_page(R, S, sm, qw, a1, a2, lane, min(PT, nvq - (p0 + i) * PT), qscale);
+        gqa4_page(R, S, sm, qw, a1, a2, lane, nvalid(i), qscale);
     };
     auto page_ld = [&](int i) {
         const uint8_t *pg = base + (size_t)__builtin_amdgcn_readlane(pid_l, min(i, np - 1)) * pstride;
         // extent: the whole page, up to the value statistics of its last
         // valid token on the prefix's last page, nothing past the split
-        const int ext = i < np ? G.vs + 16 * min(PT, nvq - (p0 + i) * PT) : 0;
+        const int ext = i < np ? G.vs + 16 * nvalid(i) : 0;
         return load_gqa4_page(pg, ext, G, lane);
     };
     // (scheduling barriers keep each page's loads together and in order, so
@@ -1906,7 +1981,7 @@ __global__ __launch_bounds__(64) void merge_kernel(KParams P, float *__restrict_
     const int npages = wit ? nkq / WPT
                        : P.scheme == KVQ_SCHEME_WITCERT_PAGED ? (l + PT - 1) / PT
                                                              : (max(0, l - P.sink - P.R) + PT - 1) / PT;
-    const int nsplit = (npages + P.split_pages - 1) / P.split_pages;
+    const int nsplit = min((npages + P.split_pages - 1) / P.split_pages, W.max_splits);
     const int ne = nsplit + W.n_win;              // entries nsplit.. are the window chunks
     const size_t row0 = part_row(W, P.Hq, b, hq, 0);
     auto row_of = [&](int e) { return row0 + (size_t)(e < nsplit ? e : W.max_splits + e - nsplit); };
@@ -2004,6 +2079,8 @@ hipError_t noalloc_scratch(void **ptr, size_t *bytes) {
 hipError_t launch_decode(const KParams &P, const uint16_t *q, float *out, float *cert,
                          float sm_scale, float kappa, const Workspace &W, hipStream_t s) {
     const float qscale = sm_scale * 1.4426950408889634f;
+    const bool gqa4 = P.scheme == KVQ_SCHEME_KIVI2 && P.qpk == 4 && !P.force_generic;
+    if (gqa4) plan_kernel<<<1, PLAN_T, 0, s>>>(P, W);
     if (W.ev_begin) {
         hipError_t e = hipEventRecord(W.ev_begin, s);
         if (e != hipSuccess) return e;
@@ -2026,7 +2103,7 @@ hipError_t launch_decode(const KParams &P, const uint16_t *q, float *out, float 
             case 8: stage1_witcert_kernel<8><<<g1, 64, 0, s>>>(P, q, W, qscale, sm_scale, kappa); break;
             default: return hipErrorInvalidValue;
         }
-    } else if (P.scheme == KVQ_SCHEME_KIVI2 && P.qpk == 4 && !P.force_generic) {
+    } else if (gqa4) {
         dim3 g1(W.max_splits + W.n_win, P.Hkv, P.B);
         stage1_gqa4_mfma_kernel<<<g1, 64, 0, s>>>(P, q, W, qscale);
     } else {

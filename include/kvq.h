@@ -154,9 +154,10 @@ typedef struct kvq_layout {
     int32_t max_pages;       /* page-table row length per request */
     int32_t n_pages;         /* pages in the pool */
     int32_t split_pages;     /* stage-1 split size in pages; 0: 4 when max_pages
-                                <= 128, else 12 (1 for WITCERT, 4 for
-                                WITCERT_PAGED), raised to ceil(max_pages /
-                                256) where that is larger */
+                                <= 128, else 16 for KIVI2 with 4 query heads
+                                per KV head and 12 otherwise (1 for WITCERT,
+                                4 for WITCERT_PAGED), raised to
+                                ceil(max_pages / 256) where that is larger */
     int32_t flags;           /* KVQ_FLAG_* */
     uint32_t layer;          /* WITCERT(_PAGED) dither counter field; < 65536 */
     uint64_t seed;           /* WITCERT(_PAGED) dither key */

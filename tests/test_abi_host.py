@@ -53,6 +53,14 @@ def bufs(K, **over):
     return K.kvq_buffers_t(**b)
 
 
+def ws_bytes(B, Hq, Hkv, splits, n_win):
+    """Workspace of kvq_decode_attention: a partial row (128 fp32 + {lse, A})
+    per query head and split or window chunk, a stage-1 work-list item (8 B)
+    per (request, KV head, split), and 256 bytes for the list's length."""
+    rows = B * Hq * (splits + n_win)
+    return rows * (128 * 4 + 8) + B * Hkv * splits * 8 + 256
+
+
 def set_layout(K, L, B=None):
     cache = K.kvq_cache_t()
     rc = K.lib().kvq_set_layout(C.byref(cache), C.byref(L), C.byref(B if B is not None else bufs(K)))
@@ -196,7 +204,7 @@ def test_witcert_paged_fields(K):
     # default split 4 pages (256 tokens); no window chunks in the workspace
     rc, cache = set_layout(K, lay(max_pages=100, n_pages=100))
     assert rc == K.KVQ_OK and cache.split_pages == 4
-    assert K.kvq_workspace_bytes(cache) == 1 * 8 * 25 * (128 * 4 + 8) + 256
+    assert K.kvq_workspace_bytes(cache) == ws_bytes(B=1, Hq=8, Hkv=2, splits=25, n_win=0)
     # calibration: the scheme and m > 0 are checked before any launch
     lib = K.lib()
     a = C.c_void_p(A256 + 0x20000)
@@ -246,19 +254,25 @@ def test_null_and_alignment(K):
 
 
 def test_split_resolution_and_workspace(K):
-    # default split: 4 pages up to 128 pages of cache, 12 above (1 for
+    # default split: 4 pages up to 128 pages of cache, above that 16 for the
+    # KIVI2 group-of-4 kernel (its work list) and 12 otherwise (1 for
     # WITCERT's 256-token pages), raised to what keeps at most 256 splits
-    for scheme, max_pages, want in (("kivi2", 100, 4), ("kivi2", 128, 4), ("kitty", 129, 12),
-                                    ("kivi2", 512, 12), ("kivi2", 3072, 12), ("kivi2", 3073, 13),
-                                    ("kivi2", 4096, 16), ("kivi2", 16384, 64), ("witcert", 64, 1),
-                                    ("witcert", 1024, 4)):
-        L = K.make_layout(scheme, B=2, Hq=8, Hkv=2, max_pages=max_pages, n_pages=max_pages)
+    cases = (("kivi2", 8, 100, 4), ("kivi2", 8, 128, 4), ("kitty", 8, 129, 12),
+             ("kivi2", 8, 129, 16), ("kivi2", 8, 512, 16), ("kivi2", 8, 4096, 16),
+             ("kivi2", 8, 4097, 17), ("kivi2", 8, 16384, 64),
+             ("kivi2", 2, 129, 12), ("kivi2", 2, 512, 12), ("kivi2", 2, 3072, 12),
+             ("kivi2", 2, 3073, 13), ("kivi2", 4, 512, 12), ("kivi4", 8, 512, 12),
+             ("witcert", 8, 64, 1), ("witcert", 8, 1024, 4))
+    for scheme, Hq, max_pages, want in cases:
+        L = K.make_layout(scheme, B=2, Hq=Hq, Hkv=2, max_pages=max_pages, n_pages=max_pages)
         rc, cache = set_layout(K, L)
-        assert rc == K.KVQ_OK and cache.split_pages == want, (scheme, max_pages)
+        assert rc == K.KVQ_OK and cache.split_pages == want, (scheme, Hq, max_pages)
         splits = -(-max_pages // want)
         n_win = 4 if scheme == "witcert" else 128 // 64     # 64-token chunks of the fp16 window
-        rows = 2 * 8 * (splits + n_win)
-        assert K.kvq_workspace_bytes(cache) == rows * 128 * 4 + rows * 8 + 256
+        assert K.kvq_workspace_bytes(cache) == ws_bytes(B=2, Hq=Hq, Hkv=2, splits=splits, n_win=n_win)
+    # the VALU stage 1 keeps 12
+    L = K.make_layout("kivi2", B=2, Hq=8, Hkv=2, max_pages=512, n_pages=512, flags=K.FLAG_GENERIC_STAGE1)
+    assert set_layout(K, L)[1].split_pages == 12
     L = K.make_layout("kivi2", B=1, Hq=1, Hkv=1, max_pages=16385, n_pages=8)
     assert set_layout(K, L)[0] == K.KVQ_EINVAL          # would need splits of 128 pages
     L = K.make_layout("kivi2", B=1, Hq=1, Hkv=1, max_pages=100, n_pages=8, split_pages=3)
@@ -340,8 +354,8 @@ def test_sink_fields_and_workspace(K):
     rc, cache = set_layout(K, L)
     assert rc == K.KVQ_OK
     splits = -(-64 // cache.split_pages)
-    rows = 2 * 8 * (splits + 128 // 64 + 1)          # window chunks + the sink chunk
-    assert K.kvq_workspace_bytes(cache) == rows * 128 * 4 + rows * 8 + 256
+    # window chunks + the sink chunk
+    assert K.kvq_workspace_bytes(cache) == ws_bytes(B=2, Hq=8, Hkv=2, splits=splits, n_win=128 // 64 + 1)
 
 
 def test_noalloc_rejects_oversized_cache_before_device_work(K):
