@@ -106,9 +106,17 @@ int check_cache(const kvq_cache_t *C) {
     return KVQ_OK;
 }
 
-int max_splits(const kvq_cache_t *C) {
-    return (C->layout.max_pages + C->split_pages - 1) / C->split_pages;
+bool gqa4(const kvq_layout_t &L) {
+    return kvq::gqa4_path(L.scheme, L.n_q_heads / L.n_kv_heads, (L.flags & KVQ_FLAG_GENERIC_STAGE1) != 0);
 }
+
+// partial rows per query head for the paged splits of a request of up to
+// max_pages pages
+int splits_for(const kvq_layout_t &L, int sp) {
+    return gqa4(L) ? kvq::gqa_splits_bound(L.max_pages, sp) : (L.max_pages + sp - 1) / sp;
+}
+
+int max_splits(const kvq_cache_t *C) { return splits_for(C->layout, C->split_pages); }
 
 // 64-token chunks of the fp16 window, each a stage-1 partial of its own
 int n_win(const kvq_cache_t *C) {
@@ -164,21 +172,20 @@ int kvq_set_layout(kvq_cache_t *cache, const kvq_layout_t *layout, const kvq_buf
     if (sp == 0) {
         // default: one 256-token block per split for WITCERT; 4 pages for
         // short caches (more splits to fill the chip), 12 for longer ones
-        // (fewer partials to merge), 16 for the GQA kernel, whose splits run
-        // from a work list (longest first, so no split size is favoured by
-        // the dispatch order), at least what keeps <= 256 splits
-        const bool gqa4 = layout->scheme == KVQ_SCHEME_KIVI2 &&
-                          layout->n_q_heads == 4 * layout->n_kv_heads &&
-                          !(layout->flags & KVQ_FLAG_GENERIC_STAGE1);
+        // (fewer partials to merge); for the GQA kernel, whose splits run
+        // from a work list with a tail of quarter-length splits, bodies of
+        // 8 pages for short caches and 32 for longer ones; at least what
+        // keeps <= 256 splits
+        const bool g4 = gqa4(*layout);
         sp = layout->scheme == KVQ_SCHEME_WITCERT ? 1
              : wtok                                 ? 4      // 256 tokens, as one WITCERT block
+             : g4                                   ? (layout->max_pages <= 128 ? 8 : 32)
              : layout->max_pages <= 128             ? 4
-             : gqa4                                 ? 16
                                                     : 12;
-        sp = std::max(sp, (layout->max_pages + kvq::MAX_SPLITS - 1) / kvq::MAX_SPLITS);
+        while (sp < 64 && splits_for(*layout, sp) > kvq::MAX_SPLITS) sp++;
     }
     // the merge takes at most MAX_SPLITS splits per query head
-    if ((layout->max_pages + sp - 1) / sp > kvq::MAX_SPLITS || sp > 64) return KVQ_EINVAL;
+    if (sp > 64 || splits_for(*layout, sp) > kvq::MAX_SPLITS) return KVQ_EINVAL;
     cache->split_pages = sp;
     cache->magic = MAGIC;
     return KVQ_OK;
@@ -193,7 +200,7 @@ size_t kvq_workspace_bytes(const kvq_cache_t *cache) {
     // and the stage-1 work list: one item per (request, KV head, split),
     // then its length (in the last 256 bytes)
     const size_t items = (size_t)cache->layout.batch * cache->layout.n_kv_heads * max_splits(cache);
-    return rows * kvq::D * sizeof(float) + rows * sizeof(float2) + items * sizeof(uint2) + 256;
+    return rows * kvq::D * sizeof(float) + rows * sizeof(float2) + items * sizeof(uint4) + 256;
 }
 
 int kvq_append_token(const kvq_cache_t *cache, const uint16_t *k_new, const uint16_t *v_new,
@@ -223,7 +230,7 @@ int decode_with(const kvq_cache_t *cache, const uint16_t *q, float *out, float *
     const size_t items = (size_t)cache->layout.batch * cache->layout.n_kv_heads * W.max_splits;
     W.o = (float *)workspace;
     W.ml = (float2 *)((char *)workspace + rows * kvq::D * sizeof(float));
-    W.items = (uint2 *)((char *)W.ml + rows * sizeof(float2));
+    W.items = (uint4 *)((char *)W.ml + rows * sizeof(float2));
     W.n_items = (uint32_t *)(W.items + items);
     W.ev_begin = cache->ev_stage1_begin;
     W.ev_end = cache->ev_stage1_end;

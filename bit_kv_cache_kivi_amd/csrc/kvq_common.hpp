@@ -59,6 +59,39 @@ __host__ __device__ constexpr bool is_kitty(int scheme) {
     return scheme == KVQ_SCHEME_KITTY || scheme == KVQ_SCHEME_KITTY_DYN;
 }
 
+// ---------------------------------------------------------------------------
+// Splits of the group-of-4 stage 1 (KIVI2 with four query heads per KV head,
+// matrix-core kernel).  A (request, KV head) pair of npg pages is cut into
+// body splits of sp pages over all but its last min(npg / 8, 2 sp) pages
+// (and what rounding leaves), then tail splits of sp / 4 pages over the rest
+// (the last one shorter): the work list runs the long body splits first and
+// ends with small ones, which even out the workgroups' finishing times while
+// most pages still go in long splits.  Split r of a pair writes partial row
+// r.  Other stage-1 kernels cut every pair into splits of sp pages.
+// ---------------------------------------------------------------------------
+__host__ __device__ constexpr bool gqa4_path(int scheme, int qpk, bool generic) {
+    return scheme == KVQ_SCHEME_KIVI2 && qpk == 4 && !generic;
+}
+__host__ __device__ constexpr int gqa_tail_pages(int sp) { return sp >= 4 ? sp / 4 : 1; }
+__host__ __device__ constexpr int gqa_tail_target(int npg, int sp) {
+    return npg / 8 < 2 * sp ? npg / 8 : 2 * sp;
+}
+__host__ __device__ constexpr int gqa_body_splits(int npg, int sp) {
+    return (npg - gqa_tail_target(npg, sp)) / sp;
+}
+// splits (partial rows) of a pair of npg pages
+__host__ __device__ constexpr int gqa_splits(int npg, int sp) {
+    return gqa_body_splits(npg, sp) +
+           (npg - gqa_body_splits(npg, sp) * sp + gqa_tail_pages(sp) - 1) / gqa_tail_pages(sp);
+}
+// a bound on gqa_splits(npg, sp) over all npg <= m: the body count and the
+// tail target are each non-decreasing in npg, and the tail holds at most the
+// target plus sp - 1 pages
+__host__ __device__ constexpr int gqa_splits_bound(int m, int sp) {
+    return (m - gqa_tail_target(m, sp)) / sp +
+           (gqa_tail_target(m, sp) + sp - 1 + gqa_tail_pages(sp) - 1) / gqa_tail_pages(sp);
+}
+
 __host__ __device__ inline Geom geom(int scheme, int nb = NB) {
     Geom g{};
     if (scheme == KVQ_SCHEME_WITCERT) {

@@ -1027,77 +1027,91 @@ __device__ inline void gqa4_page(const Gqa4Page &R, Gqa4State &S, Gqa4Smem &sm, 
     }
 }
 
-// Stage-1 work list of the GQA kernel: the paged splits that hold pages,
-// full ones (split_pages pages) first in (request, KV head, split) order,
-// then each pair's shorter last split, longest first.  Workgroups are
-// dispatched in order and round-robin over the XCDs, so similar items sit
-// side by side and the shortest run last.  Item: x = b Hkv + h, y = split |
-// pages << 8 | valid tokens of its last page << 16.  One workgroup.
+// Stage-1 work list of the GQA kernel: every split of every (request, KV
+// head) pair (gqa_splits), longest first -- the body splits of split_pages
+// pages in (request, KV head, split) order, then the full tail splits in the
+// same order, then each pair's short last tail split, longest first.
+// Workgroups are dispatched in list order and round-robin over the XCDs, so
+// similar items sit side by side and the shortest run last.  One workgroup.
 constexpr int PLAN_T = 1024;
 
 __global__ __launch_bounds__(PLAN_T) void plan_kernel(KParams P, Workspace W) {
-    const int npair = P.B * P.Hkv, sp = P.split_pages, tid = threadIdx.x;
+    const int npair = P.B * P.Hkv, sp = P.split_pages, tp = gqa_tail_pages(sp), tid = threadIdx.x;
     __shared__ int cnt[65];                 // short last splits per page count
     __shared__ int cur[65];                 // their next free slot
-    __shared__ int scan[PLAN_T];
-    __shared__ int carry;
+    __shared__ int scan_b[PLAN_T];          // body splits (scan)
+    __shared__ int scan_t[PLAN_T];          // full tail splits (scan)
+    __shared__ int carry_b, carry_t, first_t;
     for (int i = tid; i < 65; i += PLAN_T) cnt[i] = 0;
-    if (tid == 0) carry = 0;
+    if (tid == 0) carry_b = carry_t = 0;
     __syncthreads();
     // quantized values of a pair, and its pages (capped by its page-table row)
     auto nvq_of = [&](int pr) { return max(0, P.state[(size_t)pr * 4] - P.sink - P.R); };
     auto pages_of = [&](int nvq) { return min((nvq + PT - 1) / PT, P.max_pages); };
-    // pass 1: the full splits (their total) and the short ones per page count
-    int nfull_tot = 0;
+    // pass 1: totals of the body and full tail splits, short ones per length
+    int nb_tot = 0, nt_tot = 0;
     for (int pr = tid; pr < npair; pr += PLAN_T) {
         const int npg = pages_of(nvq_of(pr));
-        nfull_tot += npg / sp;
-        if (npg % sp) atomicAdd(&cnt[npg % sp], 1);
+        const int nb = gqa_body_splits(npg, sp), rest = npg - nb * sp;
+        nb_tot += nb;
+        nt_tot += rest / tp;
+        if (rest % tp) atomicAdd(&cnt[rest % tp], 1);
     }
-    scan[tid] = nfull_tot;
+    scan_b[tid] = nb_tot;
+    scan_t[tid] = nt_tot;
     __syncthreads();
     for (int off = PLAN_T / 2; off > 0; off >>= 1) {
-        if (tid < off) scan[tid] += scan[tid + off];
+        if (tid < off) {
+            scan_b[tid] += scan_b[tid + off];
+            scan_t[tid] += scan_t[tid + off];
+        }
         __syncthreads();
     }
-    const int F = scan[0];
-    __syncthreads();
-    if (tid == 0) {                         // short splits after the full ones, longest first
-        int o = F;
-        for (int k = sp - 1; k >= 1; k--) {
+    if (tid == 0) {                         // then the short splits, longest first
+        first_t = scan_b[0];
+        int o = scan_b[0] + scan_t[0];
+        for (int k = tp - 1; k >= 1; k--) {
             cur[k] = o;
             o += cnt[k];
         }
         *W.n_items = (uint32_t)o;
     }
     __syncthreads();
-    // pass 2: the items, full splits at their prefix position in pair order
+    // pass 2: the items; body and full tail splits at their prefix positions
     for (int c0 = 0; c0 < npair; c0 += PLAN_T) {
         const int pr = c0 + tid;
         const int nvq = pr < npair ? nvq_of(pr) : 0;
         const int npg = pages_of(nvq);
-        const int nfull = npg / sp, rem = npg % sp;
-        const int nv_last = npg ? min(PT, nvq - (npg - 1) * PT) : 0;
-        scan[tid] = nfull;                  // inclusive scan over the chunk
+        const int nb = gqa_body_splits(npg, sp), rest = npg - nb * sp;
+        const int nt = rest / tp, rem = rest % tp;
+        const uint32_t nv_last = npg ? (uint32_t)min(PT, nvq - (npg - 1) * PT) : 0u;
+        scan_b[tid] = nb;                   // inclusive scans over the chunk
+        scan_t[tid] = nt;
         __syncthreads();
         for (int off = 1; off < PLAN_T; off <<= 1) {
-            const int v = tid >= off ? scan[tid - off] : 0;
+            const int vb = tid >= off ? scan_b[tid - off] : 0;
+            const int vt = tid >= off ? scan_t[tid - off] : 0;
             __syncthreads();
-            scan[tid] += v;
+            scan_b[tid] += vb;
+            scan_t[tid] += vt;
             __syncthreads();
         }
-        const int first = carry + scan[tid] - nfull;
-        for (int k = 0; k < nfull; k++) {
-            const bool last = rem == 0 && k == nfull - 1;
-            W.items[first + k] = make_uint2((uint32_t)pr, (uint32_t)k | (uint32_t)sp << 8 |
-                                                          (uint32_t)(last ? nv_last : PT) << 16);
-        }
-        if (rem) {
-            const int slot = atomicAdd(&cur[rem], 1);
-            W.items[slot] = make_uint2((uint32_t)pr, (uint32_t)nfull | (uint32_t)rem << 8 | (uint32_t)nv_last << 16);
-        }
+        // item of split r: pages [p0, p0 + n); the pair's last page carries
+        // its valid-token count
+        auto put = [&](int slot, int r, int p0, int n) {
+            const uint32_t last = p0 + n == npg ? nv_last : 0u;
+            W.items[slot] = make_uint4((uint32_t)pr, (uint32_t)r, (uint32_t)p0, (uint32_t)n | last << 8);
+        };
+        const int fb = carry_b + scan_b[tid] - nb;
+        for (int k = 0; k < nb; k++) put(fb + k, k, k * sp, sp);
+        const int ft = first_t + carry_t + scan_t[tid] - nt;
+        for (int k = 0; k < nt; k++) put(ft + k, nb + k, nb * sp + k * tp, tp);
+        if (rem) put(atomicAdd(&cur[rem], 1), nb + nt, nb * sp + nt * tp, rem);
         __syncthreads();
-        if (tid == PLAN_T - 1) carry += scan[tid];
+        if (tid == PLAN_T - 1) {
+            carry_b += scan_b[tid];
+            carry_t += scan_t[tid];
+        }
         __syncthreads();
     }
 }
@@ -1120,11 +1134,11 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(3, 8))) void
         return;
     }
     if (L - nw >= (int)*W.n_items) return;
-    const uint2 item = W.items[L - nw];
+    const uint4 item = W.items[L - nw];
     const int b = (int)(item.x / (uint32_t)P.Hkv), h = (int)(item.x % (uint32_t)P.Hkv);
-    const int s = item.y & 255, np = (item.y >> 8) & 127, nv_last = item.y >> 16;
+    const int s = (int)item.y, p0 = (int)item.z;           // partial row, first page
+    const int np = item.w & 255, nv_last = (item.w >> 8) ? (int)(item.w >> 8) : PT;
     Gqa4Smem &sm = U.pg;
-    const int p0 = s * P.split_pages;
     // valid tokens of the split's page i (only the prefix's last page is short)
     auto nvalid = [&](int i) { return i == np - 1 ? nv_last : PT; };
 
@@ -1981,7 +1995,10 @@ __global__ __launch_bounds__(64) void merge_kernel(KParams P, float *__restrict_
     const int npages = wit ? nkq / WPT
                        : P.scheme == KVQ_SCHEME_WITCERT_PAGED ? (l + PT - 1) / PT
                                                              : (max(0, l - P.sink - P.R) + PT - 1) / PT;
-    const int nsplit = min((npages + P.split_pages - 1) / P.split_pages, W.max_splits);
+    const int nsplit = min(gqa4_path(P.scheme, P.qpk, P.force_generic)
+                               ? gqa_splits(npages, P.split_pages)
+                               : (npages + P.split_pages - 1) / P.split_pages,
+                           W.max_splits);
     const int ne = nsplit + W.n_win;              // entries nsplit.. are the window chunks
     const size_t row0 = part_row(W, P.Hq, b, hq, 0);
     auto row_of = [&](int e) { return row0 + (size_t)(e < nsplit ? e : W.max_splits + e - nsplit); };
@@ -2079,7 +2096,7 @@ hipError_t noalloc_scratch(void **ptr, size_t *bytes) {
 hipError_t launch_decode(const KParams &P, const uint16_t *q, float *out, float *cert,
                          float sm_scale, float kappa, const Workspace &W, hipStream_t s) {
     const float qscale = sm_scale * 1.4426950408889634f;
-    const bool gqa4 = P.scheme == KVQ_SCHEME_KIVI2 && P.qpk == 4 && !P.force_generic;
+    const bool gqa4 = gqa4_path(P.scheme, P.qpk, P.force_generic);
     if (gqa4) plan_kernel<<<1, PLAN_T, 0, s>>>(P, W);
     if (W.ev_begin) {
         hipError_t e = hipEventRecord(W.ev_begin, s);

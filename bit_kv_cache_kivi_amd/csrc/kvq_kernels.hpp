@@ -34,7 +34,9 @@ struct KParams {
 struct Workspace {
     float *o;        // [B][Hq][max_splits + n_win][128]
     float2 *ml;      // [B][Hq][max_splits + n_win]  (lse in log2 units, A)
-    uint2 *items;    // [B * Hkv * max_splits] stage-1 work list (GQA kernel)
+    uint4 *items;    // [B * Hkv * max_splits] stage-1 work list (GQA kernel):
+                     // {b Hkv + h, partial row, first page, pages | valid
+                     // tokens of the pair's last page << 8 (0: none here)}
     uint32_t *n_items;  // its length
     int max_splits;
     int n_win;       // window chunks: residual / 64 (KIVI2 / KITTY) + 1 with sink tokens,

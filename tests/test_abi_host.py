@@ -55,10 +55,25 @@ def bufs(K, **over):
 
 def ws_bytes(B, Hq, Hkv, splits, n_win):
     """Workspace of kvq_decode_attention: a partial row (128 fp32 + {lse, A})
-    per query head and split or window chunk, a stage-1 work-list item (8 B)
+    per query head and split or window chunk, a stage-1 work-list item (16 B)
     per (request, KV head, split), and 256 bytes for the list's length."""
     rows = B * Hq * (splits + n_win)
-    return rows * (128 * 4 + 8) + B * Hkv * splits * 8 + 256
+    return rows * (128 * 4 + 8) + B * Hkv * splits * 16 + 256
+
+
+def gqa_splits(npg, sp):
+    """Splits of one (request, KV head) pair of npg pages in the group-of-4
+    kernel's work list: body splits of sp pages over all but the last
+    min(npg // 8, 2 sp) pages, then tail splits of sp // 4 pages (1 below 4)."""
+    tp = sp // 4 if sp >= 4 else 1
+    body = (npg - min(npg // 8, 2 * sp)) // sp
+    return body + -(-(npg - body * sp) // tp)
+
+
+def gqa_rows(max_pages, sp):
+    """Partial rows per query head the workspace holds: the most any pair of
+    at most max_pages pages needs, by brute force."""
+    return max(gqa_splits(n, sp) for n in range(max_pages + 1))
 
 
 def set_layout(K, L, B=None):
@@ -254,12 +269,13 @@ def test_null_and_alignment(K):
 
 
 def test_split_resolution_and_workspace(K):
-    # default split: 4 pages up to 128 pages of cache, above that 16 for the
-    # KIVI2 group-of-4 kernel (its work list) and 12 otherwise (1 for
-    # WITCERT's 256-token pages), raised to what keeps at most 256 splits
-    cases = (("kivi2", 8, 100, 4), ("kivi2", 8, 128, 4), ("kitty", 8, 129, 12),
-             ("kivi2", 8, 129, 16), ("kivi2", 8, 512, 16), ("kivi2", 8, 4096, 16),
-             ("kivi2", 8, 4097, 17), ("kivi2", 8, 16384, 64),
+    # default split: 4 pages up to 128 pages of cache, above that 12 (1 for
+    # WITCERT's 256-token pages); for the KIVI2 group-of-4 kernel bodies of 8
+    # and 32 pages with quarter-length tail splits; raised to what keeps at
+    # most 256 splits
+    cases = (("kivi2", 8, 100, 8), ("kivi2", 8, 128, 8), ("kitty", 8, 129, 12),
+             ("kivi2", 8, 129, 32), ("kivi2", 8, 512, 32), ("kivi2", 8, 4096, 32),
+             ("kivi2", 8, 8000, 33), ("kivi2", 8, 15807, 64),
              ("kivi2", 2, 129, 12), ("kivi2", 2, 512, 12), ("kivi2", 2, 3072, 12),
              ("kivi2", 2, 3073, 13), ("kivi2", 4, 512, 12), ("kivi4", 8, 512, 12),
              ("witcert", 8, 64, 1), ("witcert", 8, 1024, 4))
@@ -267,9 +283,18 @@ def test_split_resolution_and_workspace(K):
         L = K.make_layout(scheme, B=2, Hq=Hq, Hkv=2, max_pages=max_pages, n_pages=max_pages)
         rc, cache = set_layout(K, L)
         assert rc == K.KVQ_OK and cache.split_pages == want, (scheme, Hq, max_pages)
-        splits = -(-max_pages // want)
+        gqa = scheme == "kivi2" and Hq == 8
+        rows = gqa_rows(max_pages, want) if gqa else -(-max_pages // want)
         n_win = 4 if scheme == "witcert" else 128 // 64     # 64-token chunks of the fp16 window
-        assert K.kvq_workspace_bytes(cache) == ws_bytes(B=2, Hq=Hq, Hkv=2, splits=splits, n_win=n_win)
+        ws = K.kvq_workspace_bytes(cache)
+        if gqa:     # a closed-form bound on the rows: exact or at most two rows over
+            assert any(ws == ws_bytes(B=2, Hq=Hq, Hkv=2, splits=rows + d, n_win=n_win) for d in (0, 1, 2))
+        else:
+            assert ws == ws_bytes(B=2, Hq=Hq, Hkv=2, splits=rows, n_win=n_win)
+        assert rows <= 256
+    # past what 256 group-of-4 splits of 64-page bodies and their tails hold
+    L = K.make_layout("kivi2", B=2, Hq=8, Hkv=2, max_pages=15808, n_pages=8)
+    assert set_layout(K, L)[0] == K.KVQ_EINVAL
     # the VALU stage 1 keeps 12
     L = K.make_layout("kivi2", B=2, Hq=8, Hkv=2, max_pages=512, n_pages=512, flags=K.FLAG_GENERIC_STAGE1)
     assert set_layout(K, L)[1].split_pages == 12
@@ -361,7 +386,7 @@ def test_sink_fields_and_workspace(K):
 def test_noalloc_rejects_oversized_cache_before_device_work(K):
     # kvq_decode_attention_noalloc refuses a cache whose workspace exceeds the
     # scratch array, before any HIP call (no GPU needed to see it)
-    L = K.make_layout("kivi2", B=128, Hq=32, Hkv=8, max_pages=512, n_pages=128 * 512)
+    L = K.make_layout("kivi2", B=256, Hq=32, Hkv=8, max_pages=512, n_pages=256 * 512)
     rc, cache = set_layout(K, L)
     assert rc == K.KVQ_OK
     assert K.kvq_workspace_bytes(cache) > K.NOALLOC_SCRATCH_BYTES

@@ -64,6 +64,23 @@ def test_kivi_prefill_decode_small(Hq, Hkv, flags):
     _check_decode(case, out, cert, q)
 
 
+@pytest.mark.parametrize("split", [0, 5, 8, 12, 16])
+def test_gqa4_body_and_tail_splits(split):
+    # the group-of-4 kernel's work list: body splits of `split` pages, then
+    # tail splits of a quarter of that (the last one shorter), over requests
+    # holding 0, 9, 19, 32, 45 and 63 quantized pages; every split's partial
+    # row merged (split 0: the default for a cache this short)
+    w = inputs.workload(3, B=6, Hq=8, Hkv=2, ctx=(70, 700, 1301, 2113, 3000, 4100), steps=3)
+    case = _case(w, extra_tokens=80, split_pages=split)
+    case.check_status()
+    out, cert, q = case.decode_now(7)
+    _check_decode(case, out, cert, q)
+    for i in range(3):
+        out, cert, q = case.step(decode=True)
+        _check_decode(case, out, cert, q)
+    case.check_status()
+
+
 @pytest.mark.parametrize("Hq,Hkv", [(4, 4), (8, 2)])
 def test_kivi_streaming_crosses_flush_and_pages(Hq, Hkv):
     w = inputs.workload(2, B=2, Hq=Hq, Hkv=Hkv, ctx=(250, 383))
