@@ -21,6 +21,7 @@ import concurrent.futures as cf
 import hashlib
 import json
 import os
+import subprocess
 import sys
 import time
 
@@ -33,6 +34,8 @@ from bit_kv_cache_kivi_amd import inputs  # noqa: E402
 
 METRIC = "quantized-KV decode attn: effective KV GB/s (% of HBM peak) + tokens/s, 1 GPU"
 HBM_PEAK_GBS = 8000.0
+# host CPUs a one-GPU job is given (the oracle baseline runs on as many threads)
+BOX_CPU_SHARE = 16
 VALU_PEAK_TOPS = 256 * 64 * 2.4e9 / 1e12         # full-rate 32-bit VALU lane ops, all CUs
 PHILOX_VALU_OPS = 40                              # per Philox4x32-10 call on gfx950 (see below)
 
@@ -220,7 +223,7 @@ def setup_gpu(w: inputs.Workload, extra: int, split_pages: int):
 
 
 def run_gpu(w: inputs.Workload, steps: int, warmup: int, split_pages: int, copies: int = 1,
-            settle_s: float = 0.06):
+            settle_s: float = 0.06, latency_steps: int = 0):
     """copies > 1: that many independent caches of the workload, used in turn
     (step i on copy i mod copies), so that no cache stays resident in the
     memory-side cache between its steps (a cold-cache figure).
@@ -229,11 +232,15 @@ def run_gpu(w: inputs.Workload, steps: int, warmup: int, split_pages: int, copie
     (they read the caches and change no state) for about this long.  The GPU
     idles during the host-side prefill and needs some 20 ms of work to return
     to its working clock; without this the few timed steps of a short run
-    would measure that ramp instead of the kernels."""
+    would measure that ramp instead of the kernels.
+
+    latency_steps: after the timed steps, that many more steps one at a time,
+    each bracketed by events on the stream and followed by a host
+    synchronisation (the latency of one whole step: flush, append, decode)."""
     import torch
     from bit_kv_cache_kivi_amd import kvq
-    caches = [setup_gpu(w, extra=steps + warmup + 8, split_pages=split_pages) for _ in range(copies)]
-    n = steps + warmup
+    n = steps + warmup + latency_steps
+    caches = [setup_gpu(w, extra=n + 8, split_pages=split_pages) for _ in range(copies)]
     # every step's inputs resident in HBM before timing
     ks, vs, qs = [], [], []
     for i in range(n):
@@ -288,8 +295,30 @@ def run_gpu(w: inputs.Workload, steps: int, warmup: int, split_pages: int, copie
     if not torch.isfinite(out).all():
         raise RuntimeError("non-finite output")
     s1_ms = [a.elapsed_time(b) for a, b in ev1]
+    lat = None
+    if latency_steps:
+        dev_us, host_us = [], []
+        pairs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                 for _ in range(latency_steps)]
+        for j, (a, b) in enumerate(pairs):
+            t1 = time.perf_counter()
+            a.record()
+            one(warmup + steps + j)
+            b.record()
+            b.synchronize()
+            host_us.append((time.perf_counter() - t1) * 1e6)
+            dev_us.append(a.elapsed_time(b) * 1e3)
+        for cache in caches:
+            if cache.status_word() != 0:
+                raise RuntimeError(f"device status {cache.status_word():#x}")
+        lat = {"steps": latency_steps,
+               "device_us_median": round(float(np.median(dev_us)), 2),
+               "device_us_p90": round(float(np.percentile(dev_us, 90)), 2),
+               "device_us_min": round(float(np.min(dev_us)), 2),
+               "host_us_median": round(float(np.median(host_us)), 2),
+               "host_us_p90": round(float(np.percentile(host_us, 90)), 2)}
     del stream
-    return dt, s1_ms, settle
+    return dt, s1_ms, settle, lat
 
 
 # ---------------------------------------------------------------------------
@@ -301,14 +330,19 @@ def cpu_baseline(w: inputs.Workload, warmup: int, target_s: float = 15.0, thread
     from oracle import oracle as O
     sid = {"kivi2": O.KIVI, "kitty": O.KITTY, "witcert": O.WITCERT, "kitty_dyn": O.KITTY_DYN,
            "kivi4": O.KIVI4, "witcert_paged": O.WITCERT_TOK}[w.scheme]
+    affinity = len(os.sched_getaffinity(0))
     if threads <= 0:
-        threads = max(1, min(16, len(os.sched_getaffinity(0))))
+        # the host CPUs a one-GPU job is given (16) where the process may
+        # use more; all of them where it may use fewer
+        threads = max(1, min(BOX_CPU_SHARE, affinity))
     idx = None
     if w.scheme == "kitty":
         idx = [O.kitty_select(inputs.kitty_calibration(w, h), w.nb) for h in range(w.Hkv)]
     if w.scheme == "witcert_paged" and w.nb > 0:     # bypass masks (slots: token index)
         idx = [O.witcert_select_pairs(inputs.kitty_calibration(w, h), w.nb) for h in range(w.Hkv)]
-    pairs = [(b, b % w.Hkv) for b in range(n_pairs if n_pairs > 0 else w.B)]
+    # the whole step (every request and KV head) unless a smaller sample is asked for
+    pairs = ([(b, b % w.Hkv) for b in range(min(n_pairs, w.B))] if n_pairs > 0
+             else [(b, h) for b in range(w.B) for h in range(w.Hkv)])
     seed = 0x5EED_0000_0000_0000 | w.seed
 
     def make(pair):
@@ -328,7 +362,7 @@ def cpu_baseline(w: inputs.Workload, warmup: int, target_s: float = 15.0, thread
                  1.0 if w.scheme in ("witcert", "witcert_paged") else 0.0)
 
     # rounds of one flush/append/decode step on every sampled pair, until the
-    # timed work reaches about target_s (bounded by max_rounds)
+    # timed work reaches about target_s (at least one round; at most max_rounds)
     max_rounds = 200
     with cf.ThreadPoolExecutor(threads) as ex:
         items = list(ex.map(make, pairs))
@@ -353,11 +387,27 @@ def cpu_baseline(w: inputs.Workload, warmup: int, target_s: float = 15.0, thread
             rounds += 1
     done_pairs = len(pairs) * rounds
     gbs = done_bytes / total_t / 1e9
+    whole = len(pairs) == w.B * w.Hkv
+    what = ("every (request, KV head) pair of the workload, i.e. whole steps at full shape" if whole
+            else f"{len(pairs)} (request, KV head) pairs of the workload (one per request)")
     return {"value": gbs, "unit": "GB/s", "cores": threads, "kind": "oracle",
-            "sample": f"{len(pairs)} (request, KV head) pairs of the workload (one per request) "
-                      f"x {rounds} flush/append/decode steps ({done_bytes / 1e6:.1f} MB "
+            "sample": f"{what} x {rounds} flush/append/decode steps ({done_bytes / 1e6:.1f} MB "
                       f"algorithmic), {total_t:.1f}s on {threads} host threads",
+            "affinity_cpus": affinity, "lscpu": lscpu_counts(),
+            "step_s": round(total_t / rounds, 3) if whole else None,
             "tokens_per_s_equiv": done_pairs / w.Hkv / total_t}
+
+
+def lscpu_counts() -> dict:
+    """Sockets, cores and hardware threads of the host, as lscpu reports them."""
+    try:
+        out = subprocess.run(["lscpu", "-p=SOCKET,CORE,CPU"], capture_output=True, text=True,
+                             timeout=10).stdout
+    except (OSError, subprocess.SubprocessError):
+        return {}
+    rows = [ln.split(",") for ln in out.splitlines() if ln and not ln.startswith("#")]
+    return {"sockets": len({r[0] for r in rows}), "cores": len({(r[0], r[1]) for r in rows}),
+            "cpus": len(rows)}
 
 
 # ---------------------------------------------------------------------------
@@ -393,6 +443,9 @@ def main():
                     help="two cache copies used in turn, so the memory-side cache holds neither")
     ap.add_argument("--settle-ms", type=float, default=80.0,
                     help="decode-only passes before the warm-up steps, to bring the clock up")
+    ap.add_argument("--latency", type=int, default=-1,
+                    help="steps timed one at a time after the timed loop (default: 200 for "
+                         "workload 1, else 0)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--copy-calibration", action="store_true",
@@ -415,8 +468,9 @@ def main():
     log(f"workload {w.name}: B={w.B} Hq={w.Hq} Hkv={w.Hkv} ctx mean "
         f"{np.mean(w.ctx):.0f}, steps={args.steps} warmup={args.warmup}")
     copies = 2 if args.cold else 1
-    dt, s1_ms, settle = run_gpu(w, args.steps, args.warmup, args.split_pages, copies,
-                                args.settle_ms * 1e-3)
+    lat_steps = args.latency if args.latency >= 0 else (200 if args.workload == 1 else 0)
+    dt, s1_ms, settle, lat = run_gpu(w, args.steps, args.warmup, args.split_pages, copies,
+                                     args.settle_ms * 1e-3, lat_steps)
 
     # algorithmic bytes of the timed steps (step i advances copy i mod copies)
     cstates = [[state_after_prefill(w, l) for l in w.ctx] for _ in range(copies)]
@@ -485,6 +539,8 @@ def main():
            "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
            "settle": settle,
            "roofline": roof}
+    if lat is not None:
+        rec["latency"] = lat
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a bounded sample ...")
         rec["cpu_baseline"] = cpu_baseline(w, args.warmup, args.cpu_seconds)
