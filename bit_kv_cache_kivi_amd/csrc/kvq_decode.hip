@@ -1029,89 +1029,147 @@ __device__ inline void gqa4_page(const Gqa4Page &R, Gqa4State &S, Gqa4Smem &sm, 
 
 // Stage-1 work list of the GQA kernel: every split of every (request, KV
 // head) pair (gqa_splits), longest first -- the body splits of split_pages
-// pages in (request, KV head, split) order, then the full tail splits in the
-// same order, then each pair's short last tail split, longest first.
+// pages and then the full tail splits, each in (request, KV head, split)
+// order, then the short last tail splits by length, longest first.
 // Workgroups are dispatched in list order and round-robin over the XCDs, so
-// similar items sit side by side and the shortest run last.  One workgroup.
+// similar items sit side by side and the shortest run last.  One workgroup;
+// each pass over up to PLAN_T pairs places their items by wave-level prefix
+// sums (two barriers) and a per-length count of the short splits.
 constexpr int PLAN_T = 1024;
+constexpr int PLAN_W = PLAN_T / 64;
+
+// inclusive prefix sums over the wave's lanes of three counters
+__device__ inline void wave_scan3(int (&v)[3], int lane) {
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+#pragma unroll
+        for (int i = 0; i < 3; i++) {
+            const int t = __shfl_up(v[i], off, 64);
+            if (lane >= off) v[i] += t;
+        }
+    }
+}
 
 __global__ __launch_bounds__(PLAN_T) void plan_kernel(KParams P, Workspace W) {
-    const int npair = P.B * P.Hkv, sp = P.split_pages, tp = gqa_tail_pages(sp), tid = threadIdx.x;
-    __shared__ int cnt[65];                 // short last splits per page count
-    __shared__ int cur[65];                 // their next free slot
-    __shared__ int scan_b[PLAN_T];          // body splits (scan)
-    __shared__ int scan_t[PLAN_T];          // full tail splits (scan)
-    __shared__ int carry_b, carry_t, first_t;
-    for (int i = tid; i < 65; i += PLAN_T) cnt[i] = 0;
-    if (tid == 0) carry_b = carry_t = 0;
-    __syncthreads();
+    const int npair = P.B * P.Hkv, sp = P.split_pages, tp = gqa_tail_pages(sp);
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    __shared__ int wtot[3][PLAN_W];        // per-wave totals, then their exclusive prefixes
+    __shared__ int ctot[3];                // the pass's totals
+    __shared__ int base[3];                // each kind's region start in the list
+    __shared__ int carry[3];               // items of each kind placed by earlier passes
+    __shared__ int hist[64];               // short last splits per length (< tail length <= 16)
+    __shared__ int cur[64];                // the next free slot for each length
     // quantized values of a pair, and its pages (capped by its page-table row)
     auto nvq_of = [&](int pr) { return max(0, P.state[(size_t)pr * 4] - P.sink - P.R); };
     auto pages_of = [&](int nvq) { return min((nvq + PT - 1) / PT, P.max_pages); };
-    // pass 1: totals of the body and full tail splits, short ones per length
-    int nb_tot = 0, nt_tot = 0;
-    for (int pr = tid; pr < npair; pr += PLAN_T) {
-        const int npg = pages_of(nvq_of(pr));
+    // the wave's short last splits of each length: counted (slot false) or
+    // given slots, longest first (slot true); rem = 0: none
+    auto shorts = [&](int rem, bool slot) {
+        int got = 0;
+        for (int len = tp - 1; len >= 1; len--) {
+            const uint64_t m = __ballot(rem == len);
+            if (!m) continue;
+            const int first = __builtin_ctzll(m);
+            int b0 = 0;
+            if (lane == first) {
+                const int n = __builtin_popcountll(m);
+                b0 = slot ? atomicAdd(&cur[len], n) : (atomicAdd(&hist[len], n), 0);
+            }
+            b0 = __shfl(b0, first, 64);
+            if (rem == len) got = b0 + __builtin_popcountll(m & ((1ull << lane) - 1));
+        }
+        return got;
+    };
+    // a pass: the counts {body, full tail, short} of a pair with npg pages,
+    // their exclusive prefix over the pass (+ carry) in v, the pass totals
+    // in ctot
+    auto scan_pass = [&](int npg, int (&cnt)[3], int (&v)[3]) {
         const int nb = gqa_body_splits(npg, sp), rest = npg - nb * sp;
-        nb_tot += nb;
-        nt_tot += rest / tp;
-        if (rest % tp) atomicAdd(&cnt[rest % tp], 1);
-    }
-    scan_b[tid] = nb_tot;
-    scan_t[tid] = nt_tot;
-    __syncthreads();
-    for (int off = PLAN_T / 2; off > 0; off >>= 1) {
-        if (tid < off) {
-            scan_b[tid] += scan_b[tid + off];
-            scan_t[tid] += scan_t[tid + off];
+        cnt[0] = nb;
+        cnt[1] = rest / tp;
+        cnt[2] = rest % tp ? 1 : 0;
+#pragma unroll
+        for (int i = 0; i < 3; i++) v[i] = cnt[i];
+        wave_scan3(v, lane);
+        if (lane == 63)
+#pragma unroll
+            for (int i = 0; i < 3; i++) wtot[i][wv] = v[i];
+        __syncthreads();
+        if (wv == 0) {
+            int t[3];
+#pragma unroll
+            for (int i = 0; i < 3; i++) t[i] = lane < PLAN_W ? wtot[i][lane] : 0;
+            int u[3] = {t[0], t[1], t[2]};
+            wave_scan3(u, lane);
+            if (lane < PLAN_W)
+#pragma unroll
+                for (int i = 0; i < 3; i++) wtot[i][lane] = u[i] - t[i];
+            if (lane == PLAN_W - 1)
+#pragma unroll
+                for (int i = 0; i < 3; i++) ctot[i] = u[i];
         }
         __syncthreads();
-    }
-    if (tid == 0) {                         // then the short splits, longest first
-        first_t = scan_b[0];
-        int o = scan_b[0] + scan_t[0];
-        for (int k = tp - 1; k >= 1; k--) {
-            cur[k] = o;
-            o += cnt[k];
+#pragma unroll
+        for (int i = 0; i < 3; i++) v[i] += wtot[i][wv] - cnt[i] + carry[i];
+    };
+    // region starts: body, full tail, then the short splits by length
+    auto set_bases = [&]() {
+        base[0] = 0;
+        base[1] = ctot[0];
+        base[2] = ctot[0] + ctot[1];
+        int o = base[2];
+        for (int len = tp - 1; len >= 1; len--) {
+            cur[len] = o;
+            o += hist[len];
         }
         *W.n_items = (uint32_t)o;
-    }
+    };
+    if (tid < 3) carry[tid] = 0;
+    if (tid < 64) hist[tid] = 0;
     __syncthreads();
-    // pass 2: the items; body and full tail splits at their prefix positions
+    const bool one_pass = npair <= PLAN_T;
+    if (!one_pass) {                       // the region starts need every pair's counts first
+        int tot[3] = {0, 0, 0};
+        for (int c0 = 0; c0 < npair; c0 += PLAN_T) {
+            int cnt[3], v[3];
+            const int npg = c0 + tid < npair ? pages_of(nvq_of(c0 + tid)) : 0;
+            const int nb = gqa_body_splits(npg, sp);
+            shorts((npg - nb * sp) % tp, false);
+            scan_pass(npg, cnt, v);
+            if (tid < 3) tot[tid] += ctot[tid];
+            __syncthreads();               // ctot and wtot are reused by the next pass
+        }
+        if (tid < 3) ctot[tid] = tot[tid];
+        __syncthreads();
+        if (tid == 0) set_bases();
+        __syncthreads();
+    }
     for (int c0 = 0; c0 < npair; c0 += PLAN_T) {
         const int pr = c0 + tid;
         const int nvq = pr < npair ? nvq_of(pr) : 0;
         const int npg = pages_of(nvq);
-        const int nb = gqa_body_splits(npg, sp), rest = npg - nb * sp;
-        const int nt = rest / tp, rem = rest % tp;
-        const uint32_t nv_last = npg ? (uint32_t)min(PT, nvq - (npg - 1) * PT) : 0u;
-        scan_b[tid] = nb;                   // inclusive scans over the chunk
-        scan_t[tid] = nt;
+        const int rem = (npg - gqa_body_splits(npg, sp) * sp) % tp;
+        if (one_pass) shorts(rem, false);
+        int cnt[3], v[3];
+        scan_pass(npg, cnt, v);
+        if (one_pass && tid == 0) set_bases();  // one pass: its totals are the list's
         __syncthreads();
-        for (int off = 1; off < PLAN_T; off <<= 1) {
-            const int vb = tid >= off ? scan_b[tid - off] : 0;
-            const int vt = tid >= off ? scan_t[tid - off] : 0;
-            __syncthreads();
-            scan_b[tid] += vb;
-            scan_t[tid] += vt;
-            __syncthreads();
+        const int short_slot = shorts(rem, true);
+        if (pr < npair) {
+            const uint32_t nv_last = npg ? (uint32_t)min(PT, nvq - (npg - 1) * PT) : 0u;
+            // item of split r: pages [p0, p0 + n); the pair's last page
+            // carries its valid-token count
+            auto put = [&](int slot, int r, int p0, int n) {
+                const uint32_t last = p0 + n == npg ? nv_last : 0u;
+                W.items[slot] = make_uint4((uint32_t)pr, (uint32_t)r, (uint32_t)p0, (uint32_t)n | last << 8);
+            };
+            const int nb = cnt[0], nt = cnt[1];
+            for (int k = 0; k < nb; k++) put(base[0] + v[0] + k, k, k * sp, sp);
+            for (int k = 0; k < nt; k++) put(base[1] + v[1] + k, nb + k, nb * sp + k * tp, tp);
+            if (cnt[2]) put(short_slot, nb + nt, nb * sp + nt * tp, npg - nb * sp - nt * tp);
         }
-        // item of split r: pages [p0, p0 + n); the pair's last page carries
-        // its valid-token count
-        auto put = [&](int slot, int r, int p0, int n) {
-            const uint32_t last = p0 + n == npg ? nv_last : 0u;
-            W.items[slot] = make_uint4((uint32_t)pr, (uint32_t)r, (uint32_t)p0, (uint32_t)n | last << 8);
-        };
-        const int fb = carry_b + scan_b[tid] - nb;
-        for (int k = 0; k < nb; k++) put(fb + k, k, k * sp, sp);
-        const int ft = first_t + carry_t + scan_t[tid] - nt;
-        for (int k = 0; k < nt; k++) put(ft + k, nb + k, nb * sp + k * tp, tp);
-        if (rem) put(atomicAdd(&cur[rem], 1), nb + nt, nb * sp + nt * tp, rem);
         __syncthreads();
-        if (tid == PLAN_T - 1) {
-            carry_b += scan_b[tid];
-            carry_t += scan_t[tid];
-        }
+        if (tid < 3) carry[tid] += ctot[tid];
         __syncthreads();
     }
 }

@@ -81,6 +81,21 @@ def test_gqa4_body_and_tail_splits(split):
     case.check_status()
 
 
+def test_gqa4_work_list_over_one_plan_pass():
+    # 1040 (request, KV head) pairs, more than one pass of the plan kernel
+    # (1024): the list's regions are placed from every pair's counts first,
+    # then each pass's items after the earlier passes'
+    rng = np.random.default_rng(5)
+    ctx = tuple(int(x) for x in rng.integers(100, 1400, size=260))
+    w = inputs.workload(3, B=260, Hq=16, Hkv=4, ctx=ctx, steps=2)
+    sample = [(0, 0), (17, 3), (129, 1), (200, 2), (255, 2), (259, 3)]
+    case = _case(w, extra_tokens=64, split_pages=8, sample=sample)
+    case.check_status()
+    out, cert, q = case.decode_now(3)
+    _check_decode(case, out, cert, q)
+    case.check_status()
+
+
 @pytest.mark.parametrize("Hq,Hkv", [(4, 4), (8, 2)])
 def test_kivi_streaming_crosses_flush_and_pages(Hq, Hkv):
     w = inputs.workload(2, B=2, Hq=Hq, Hkv=Hkv, ctx=(250, 383))
