@@ -1030,13 +1030,18 @@ __device__ inline void gqa4_page(const Gqa4Page &R, Gqa4State &S, Gqa4Smem &sm, 
 // Stage-1 work list of the GQA kernel: every split of every (request, KV
 // head) pair (gqa_splits), longest first -- the body splits of split_pages
 // pages and then the full tail splits, each in (request, KV head, split)
-// order, then the short last tail splits by length, longest first.
-// Workgroups are dispatched in list order and round-robin over the XCDs, so
-// similar items sit side by side and the shortest run last.  One workgroup;
-// each pass over up to PLAN_T pairs places their items by wave-level prefix
-// sums (two barriers) and a per-length count of the short splits.
+// order, then the short last tail splits by length, longest first, each
+// length in pair order.  Workgroups are dispatched in list order and round
+// robin over the XCDs, so similar items sit side by side and the shortest run
+// last.  PLAN_G workgroups each compute every pair's place (one pass per
+// PLAN_T pairs: wave-level prefix sums of the counts and of the short splits
+// per length, two barriers) and write the items of their own share of the
+// pairs: a pair's items are scattered 16-byte stores, which one compute unit
+// issues a lane at a time.
 constexpr int PLAN_T = 1024;
 constexpr int PLAN_W = PLAN_T / 64;
+constexpr int PLAN_G = 8;
+constexpr int PLAN_L = 16;                 // short split lengths: below the tail length (<= 16)
 
 // inclusive prefix sums over the wave's lanes of three counters
 __device__ inline void wave_scan3(int (&v)[3], int lane) {
@@ -1053,47 +1058,38 @@ __device__ inline void wave_scan3(int (&v)[3], int lane) {
 __global__ __launch_bounds__(PLAN_T) void plan_kernel(KParams P, Workspace W) {
     const int npair = P.B * P.Hkv, sp = P.split_pages, tp = gqa_tail_pages(sp);
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    const int per = (npair + (int)gridDim.x - 1) / (int)gridDim.x;   // this workgroup's pairs
+    const int pr0 = (int)blockIdx.x * per, pr1 = min(npair, pr0 + per);
     __shared__ int wtot[3][PLAN_W];        // per-wave totals, then their exclusive prefixes
-    __shared__ int ctot[3];                // the pass's totals
-    __shared__ int base[3];                // each kind's region start in the list
-    __shared__ int carry[3];               // items of each kind placed by earlier passes
-    __shared__ int hist[64];               // short last splits per length (< tail length <= 16)
-    __shared__ int cur[64];                // the next free slot for each length
+    __shared__ int wlen[PLAN_L][PLAN_W];   // per-wave short splits of each length, then prefixes
+    __shared__ int ctot[3], tlen[PLAN_L];  // the pass's totals
+    __shared__ int carry[3], clen[PLAN_L]; // placed by earlier passes
+    __shared__ int base[2], blen[PLAN_L];  // region starts: body, full tail; short, by length
     // quantized values of a pair, and its pages (capped by its page-table row)
     auto nvq_of = [&](int pr) { return max(0, P.state[(size_t)pr * 4] - P.sink - P.R); };
     auto pages_of = [&](int nvq) { return min((nvq + PT - 1) / PT, P.max_pages); };
-    // the wave's short last splits of each length: counted (slot false) or
-    // given slots, longest first (slot true); rem = 0: none
-    auto shorts = [&](int rem, bool slot) {
-        int got = 0;
-        for (int len = tp - 1; len >= 1; len--) {
-            const uint64_t m = __ballot(rem == len);
-            if (!m) continue;
-            const int first = __builtin_ctzll(m);
-            int b0 = 0;
-            if (lane == first) {
-                const int n = __builtin_popcountll(m);
-                b0 = slot ? atomicAdd(&cur[len], n) : (atomicAdd(&hist[len], n), 0);
-            }
-            b0 = __shfl(b0, first, 64);
-            if (rem == len) got = b0 + __builtin_popcountll(m & ((1ull << lane) - 1));
-        }
-        return got;
-    };
-    // a pass: the counts {body, full tail, short} of a pair with npg pages,
-    // their exclusive prefix over the pass (+ carry) in v, the pass totals
-    // in ctot
-    auto scan_pass = [&](int npg, int (&cnt)[3], int (&v)[3]) {
+    // a pass: the counts {body, full tail, short} of a pair of npg pages,
+    // their exclusive prefix over the pairs so far in v, the rank of its
+    // short split among the pairs so far with one of the same length in
+    // srank; the pass's totals in ctot and tlen
+    auto pass = [&](int npg, int (&cnt)[3], int (&v)[3], int &rem, int &srank) {
         const int nb = gqa_body_splits(npg, sp), rest = npg - nb * sp;
         cnt[0] = nb;
         cnt[1] = rest / tp;
-        cnt[2] = rest % tp ? 1 : 0;
+        rem = rest % tp;
+        cnt[2] = rem ? 1 : 0;
 #pragma unroll
         for (int i = 0; i < 3; i++) v[i] = cnt[i];
         wave_scan3(v, lane);
         if (lane == 63)
 #pragma unroll
             for (int i = 0; i < 3; i++) wtot[i][wv] = v[i];
+        int rk = 0;
+        for (int len = 1; len < tp; len++) {
+            const uint64_t m = __ballot(rem == len);
+            if (lane == 0) wlen[len][wv] = __builtin_popcountll(m);
+            if (rem == len) rk = __builtin_popcountll(m & ((1ull << lane) - 1));
+        }
         __syncthreads();
         if (wv == 0) {
             int t[3];
@@ -1107,55 +1103,65 @@ __global__ __launch_bounds__(PLAN_T) void plan_kernel(KParams P, Workspace W) {
             if (lane == PLAN_W - 1)
 #pragma unroll
                 for (int i = 0; i < 3; i++) ctot[i] = u[i];
+        } else if (wv == 1 && lane < PLAN_L) {  // lane = length
+            int acc = 0;
+            for (int w = 0; w < PLAN_W; w++) {
+                const int c = lane >= 1 && lane < tp ? wlen[lane][w] : 0;
+                wlen[lane][w] = acc;
+                acc += c;
+            }
+            tlen[lane] = acc;
         }
         __syncthreads();
 #pragma unroll
         for (int i = 0; i < 3; i++) v[i] += wtot[i][wv] - cnt[i] + carry[i];
+        srank = rem ? clen[rem] + wlen[rem][wv] + rk : 0;
     };
-    // region starts: body, full tail, then the short splits by length
+    // after a pass: what it placed joins the carries
+    auto advance = [&]() {
+        __syncthreads();                   // every thread has read the carries
+        if (tid < 3) carry[tid] += ctot[tid];
+        if (tid < PLAN_L) clen[tid] += tlen[tid];
+        __syncthreads();
+    };
+    // region starts from the totals (in ctot and tlen)
     auto set_bases = [&]() {
         base[0] = 0;
         base[1] = ctot[0];
-        base[2] = ctot[0] + ctot[1];
-        int o = base[2];
+        int o = ctot[0] + ctot[1];
         for (int len = tp - 1; len >= 1; len--) {
-            cur[len] = o;
-            o += hist[len];
+            blen[len] = o;
+            o += tlen[len];
         }
-        *W.n_items = (uint32_t)o;
+        if (blockIdx.x == 0) *W.n_items = (uint32_t)o;
     };
     if (tid < 3) carry[tid] = 0;
-    if (tid < 64) hist[tid] = 0;
+    if (tid < PLAN_L) clen[tid] = 0;
     __syncthreads();
     const bool one_pass = npair <= PLAN_T;
     if (!one_pass) {                       // the region starts need every pair's counts first
-        int tot[3] = {0, 0, 0};
         for (int c0 = 0; c0 < npair; c0 += PLAN_T) {
-            int cnt[3], v[3];
-            const int npg = c0 + tid < npair ? pages_of(nvq_of(c0 + tid)) : 0;
-            const int nb = gqa_body_splits(npg, sp);
-            shorts((npg - nb * sp) % tp, false);
-            scan_pass(npg, cnt, v);
-            if (tid < 3) tot[tid] += ctot[tid];
-            __syncthreads();               // ctot and wtot are reused by the next pass
+            int cnt[3], v[3], rem, srank;
+            pass(c0 + tid < npair ? pages_of(nvq_of(c0 + tid)) : 0, cnt, v, rem, srank);
+            advance();
         }
-        if (tid < 3) ctot[tid] = tot[tid];
+        if (tid < 3) ctot[tid] = carry[tid];
+        if (tid < PLAN_L) tlen[tid] = clen[tid];
         __syncthreads();
         if (tid == 0) set_bases();
+        if (tid < 3) carry[tid] = 0;
+        if (tid < PLAN_L) clen[tid] = 0;
         __syncthreads();
     }
     for (int c0 = 0; c0 < npair; c0 += PLAN_T) {
         const int pr = c0 + tid;
         const int nvq = pr < npair ? nvq_of(pr) : 0;
         const int npg = pages_of(nvq);
-        const int rem = (npg - gqa_body_splits(npg, sp) * sp) % tp;
-        if (one_pass) shorts(rem, false);
-        int cnt[3], v[3];
-        scan_pass(npg, cnt, v);
+        int cnt[3], v[3], rem, srank;
+        pass(npg, cnt, v, rem, srank);
         if (one_pass && tid == 0) set_bases();  // one pass: its totals are the list's
         __syncthreads();
-        const int short_slot = shorts(rem, true);
-        if (pr < npair) {
+        if (pr >= pr0 && pr < pr1) {
             const uint32_t nv_last = npg ? (uint32_t)min(PT, nvq - (npg - 1) * PT) : 0u;
             // item of split r: pages [p0, p0 + n); the pair's last page
             // carries its valid-token count
@@ -1166,11 +1172,9 @@ __global__ __launch_bounds__(PLAN_T) void plan_kernel(KParams P, Workspace W) {
             const int nb = cnt[0], nt = cnt[1];
             for (int k = 0; k < nb; k++) put(base[0] + v[0] + k, k, k * sp, sp);
             for (int k = 0; k < nt; k++) put(base[1] + v[1] + k, nb + k, nb * sp + k * tp, tp);
-            if (cnt[2]) put(short_slot, nb + nt, nb * sp + nt * tp, npg - nb * sp - nt * tp);
+            if (rem) put(blen[rem] + srank, nb + nt, nb * sp + nt * tp, rem);
         }
-        __syncthreads();
-        if (tid < 3) carry[tid] += ctot[tid];
-        __syncthreads();
+        advance();
     }
 }
 
@@ -2155,7 +2159,7 @@ hipError_t launch_decode(const KParams &P, const uint16_t *q, float *out, float 
                          float sm_scale, float kappa, const Workspace &W, hipStream_t s) {
     const float qscale = sm_scale * 1.4426950408889634f;
     const bool gqa4 = gqa4_path(P.scheme, P.qpk, P.force_generic);
-    if (gqa4) plan_kernel<<<1, PLAN_T, 0, s>>>(P, W);
+    if (gqa4) plan_kernel<<<PLAN_G, PLAN_T, 0, s>>>(P, W);
     if (W.ev_begin) {
         hipError_t e = hipEventRecord(W.ev_begin, s);
         if (e != hipSuccess) return e;
