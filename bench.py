@@ -12,7 +12,7 @@ time) as `value`, with tokens/s, the stage-1 kernel's roofline (HIP events
 around it inside the timed steps) and the CPU oracle timed on a bounded
 sample of the same workload on the host cores.
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 1..5]
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 1..11]
 """
 from __future__ import annotations
 
@@ -497,7 +497,7 @@ def main():
     s1_gbs = float(np.mean(s1_bytes)) / (s1_avg_ms * 1e-3) / 1e9
     kernel = ("stage1_witcert" if w.scheme == "witcert" else
               "stage1_witcert_paged" if w.scheme == "witcert_paged" else
-              "stage1_gqa4_mfma" if (w.scheme == "kivi2" and w.group == 4) else "stage1_head_mfma")
+              "stage1_gqa4_mfma" if (w.scheme == "kivi2" and w.group in (2, 4, 8)) else "stage1_head_mfma")
     if w.scheme in ("witcert", "witcert_paged"):
         # VALU bound: Philox4x32-10 calls (one per token, channel quad and
         # side of every quantized block) x the algorithmic VALU operations per

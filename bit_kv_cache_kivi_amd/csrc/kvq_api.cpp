@@ -118,6 +118,13 @@ int splits_for(const kvq_layout_t &L, int sp) {
 
 int max_splits(const kvq_cache_t *C) { return splits_for(C->layout, C->split_pages); }
 
+// stage-1 work-list items the workspace holds: one per possible split of
+// every (request, KV head, query quad) of the group kernel
+size_t list_items(const kvq_cache_t *C) {
+    const kvq_layout_t &L = C->layout;
+    return (size_t)L.batch * L.n_kv_heads * kvq::gqa_quads(L.n_q_heads / L.n_kv_heads) * max_splits(C);
+}
+
 // 64-token chunks of the fp16 window, each a stage-1 partial of its own
 int n_win(const kvq_cache_t *C) {
     if (C->layout.scheme == KVQ_SCHEME_WITCERT_PAGED) return 0;   // no fp16 tail
@@ -197,9 +204,9 @@ size_t kvq_workspace_bytes(const kvq_cache_t *cache) {
     // fp16 window
     const size_t rows =
         (size_t)cache->layout.batch * cache->layout.n_q_heads * (max_splits(cache) + n_win(cache));
-    // and the stage-1 work list: one item per (request, KV head, split),
-    // then its length (in the last 256 bytes)
-    const size_t items = (size_t)cache->layout.batch * cache->layout.n_kv_heads * max_splits(cache);
+    // and the stage-1 work list: one item per (request, KV head, query quad,
+    // split), then its length (in the last 256 bytes)
+    const size_t items = list_items(cache);
     return rows * kvq::D * sizeof(float) + rows * sizeof(float2) + items * sizeof(uint4) + 256;
 }
 
@@ -227,7 +234,7 @@ int decode_with(const kvq_cache_t *cache, const uint16_t *q, float *out, float *
     W.max_splits = max_splits(cache);
     W.n_win = n_win(cache);
     const size_t rows = (size_t)cache->layout.batch * cache->layout.n_q_heads * (W.max_splits + W.n_win);
-    const size_t items = (size_t)cache->layout.batch * cache->layout.n_kv_heads * W.max_splits;
+    const size_t items = list_items(cache);
     W.o = (float *)workspace;
     W.ml = (float2 *)((char *)workspace + rows * kvq::D * sizeof(float));
     W.items = (uint4 *)((char *)W.ml + rows * sizeof(float2));

@@ -60,8 +60,8 @@ __host__ __device__ constexpr bool is_kitty(int scheme) {
 }
 
 // ---------------------------------------------------------------------------
-// Splits of the group-of-4 stage 1 (KIVI2 with four query heads per KV head,
-// matrix-core kernel).  A (request, KV head) pair of npg pages is cut into
+// Splits of the group-of-4 stage 1 (KIVI2 with two, four or eight query heads
+// per KV head, matrix-core kernel).  A (request, KV head) pair of npg pages is cut into
 // body splits of sp pages over all but its last min(npg / 8, 2 sp) pages
 // (and what rounding leaves), then tail splits of sp / 4 pages over the rest
 // (the last one shorter): the work list runs the long body splits first and
@@ -69,9 +69,13 @@ __host__ __device__ constexpr bool is_kitty(int scheme) {
 // most pages still go in long splits.  Split r of a pair writes partial row
 // r.  Other stage-1 kernels cut every pair into splits of sp pages.
 // ---------------------------------------------------------------------------
+// The kernel serves query heads four at a time (a quad): a group of 8 is two
+// quads per KV head, each page read once per quad; a group of 2 is one quad
+// whose last two queries are zero and not written.
 __host__ __device__ constexpr bool gqa4_path(int scheme, int qpk, bool generic) {
-    return scheme == KVQ_SCHEME_KIVI2 && qpk == 4 && !generic;
+    return scheme == KVQ_SCHEME_KIVI2 && (qpk == 2 || qpk == 4 || qpk == 8) && !generic;
 }
+__host__ __device__ constexpr int gqa_quads(int qpk) { return qpk >= 4 ? qpk / 4 : 1; }
 __host__ __device__ constexpr int gqa_tail_pages(int sp) { return sp >= 4 ? sp / 4 : 1; }
 __host__ __device__ constexpr int gqa_tail_target(int npg, int sp) {
     return npg / 8 < 2 * sp ? npg / 8 : 2 * sp;

@@ -1056,7 +1056,9 @@ __device__ inline void wave_scan3(int (&v)[3], int lane) {
 }
 
 __global__ __launch_bounds__(PLAN_T) void plan_kernel(KParams P, Workspace W) {
-    const int npair = P.B * P.Hkv, sp = P.split_pages, tp = gqa_tail_pages(sp);
+    // a unit is a (request, KV head, query quad); its pages are its pair's
+    const int nq4 = gqa_quads(P.qpk);
+    const int npair = P.B * P.Hkv * nq4, sp = P.split_pages, tp = gqa_tail_pages(sp);
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     const int per = (npair + (int)gridDim.x - 1) / (int)gridDim.x;   // this workgroup's pairs
     const int pr0 = (int)blockIdx.x * per, pr1 = min(npair, pr0 + per);
@@ -1065,8 +1067,9 @@ __global__ __launch_bounds__(PLAN_T) void plan_kernel(KParams P, Workspace W) {
     __shared__ int ctot[3], tlen[PLAN_L];  // the pass's totals
     __shared__ int carry[3], clen[PLAN_L]; // placed by earlier passes
     __shared__ int base[2], blen[PLAN_L];  // region starts: body, full tail; short, by length
-    // quantized values of a pair, and its pages (capped by its page-table row)
-    auto nvq_of = [&](int pr) { return max(0, P.state[(size_t)pr * 4] - P.sink - P.R); };
+    // quantized values of a unit's pair, and its pages (capped by its
+    // page-table row)
+    auto nvq_of = [&](int pr) { return max(0, P.state[(size_t)(pr / nq4) * 4] - P.sink - P.R); };
     auto pages_of = [&](int nvq) { return min((nvq + PT - 1) / PT, P.max_pages); };
     // a pass: the counts {body, full tail, short} of a pair of npg pages,
     // their exclusive prefix over the pairs so far in v, the rank of its
@@ -1178,8 +1181,11 @@ __global__ __launch_bounds__(PLAN_T) void plan_kernel(KParams P, Workspace W) {
     }
 }
 
+template <int QPK>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(3, 8))) void stage1_gqa4_mfma_kernel(KParams P, const uint16_t *__restrict__ q,
                                                               Workspace W, float qscale) {
+    constexpr int NQ4 = QPK >= 4 ? QPK / 4 : 1;        // query quads per KV head
+    constexpr int NQV = QPK >= 4 ? 4 : QPK;            // queries of a quad that exist
     const int lane = threadIdx.x, g = lane >> 4, r = lane & 15;
     const Geom G = geom(P.scheme, P.nb);
     __shared__ union {
@@ -1192,12 +1198,14 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(3, 8))) void
     const int nw = gridDim.y * gridDim.z * W.n_win;
     if (L < nw) {                                // the KV head's fp16 window
         const S1Item it = s1_item(W.max_splits, W.n_win);
-        window_partial<4, PT, KVQ_SCHEME_KIVI2>(P, q, W, qscale, it.b, it.hd, 4 * it.hd, it.s, lane, U.win);
+        window_partial<QPK, PT, KVQ_SCHEME_KIVI2>(P, q, W, qscale, it.b, it.hd, QPK * it.hd, it.s, lane, U.win);
         return;
     }
     if (L - nw >= (int)*W.n_items) return;
     const uint4 item = W.items[L - nw];
-    const int b = (int)(item.x / (uint32_t)P.Hkv), h = (int)(item.x % (uint32_t)P.Hkv);
+    const int pair = (int)(item.x / (uint32_t)NQ4), quad = (int)(item.x % (uint32_t)NQ4);
+    const int b = pair / P.Hkv, h = pair % P.Hkv;
+    const int hq0 = h * QPK + 4 * quad;               // the quad's first query head
     const int s = (int)item.y, p0 = (int)item.z;           // partial row, first page
     const int np = item.w & 255, nv_last = (item.w >> 8) ? (int)(item.w >> 8) : PT;
     Gqa4Smem &sm = U.pg;
@@ -1208,10 +1216,11 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(3, 8))) void
     // score-operand channels 4 (lane & 31) .. +3 (unscaled: keeps q s in the
     // range where the f16 remainder is a normal number)
     int pid_l = (lane < np && p0 + lane < P.max_pages) ? P.table[(size_t)b * P.max_pages + p0 + lane] : 0;
-    uint2 qw[4];
+    uint2 qw[4];                                 // queries past the group's end: zero
 #pragma unroll
     for (int hq = 0; hq < 4; hq++)
-        qw[hq] = *(const uint2 *)(q + ((size_t)b * P.Hq + (size_t)h * 4 + hq) * D + 4 * (lane & 31));
+        qw[hq] = hq < NQV ? *(const uint2 *)(q + ((size_t)b * P.Hq + (size_t)hq0 + hq) * D + 4 * (lane & 31))
+                          : make_uint2(0u, 0u);
 
     const bool bad = lane < np && (pid_l < 0 || pid_l >= P.n_pages);
     if (__any(bad)) {
@@ -1278,17 +1287,16 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(3, 8))) void
             S.zb[j] += shfl_xor(S.zb[j], msk);
         }
     }
-    auto query_val = [&](float va, float vb, int i) {   // value of query i, uniform
-        const float v = (i & 1) ? vb : va;
-        return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 16 * (i >> 1)));
-    };
-    float lsum[4];
-#pragma unroll
-    for (int i = 0; i < 4; i++) lsum[i] = query_val(S.la, S.lb, i);
     const int hp = r >> 2, part = (r >> 1) & 1, js = r & 1;
-    const float lh = hp == 0 ? lsum[0] : hp == 1 ? lsum[1] : hp == 2 ? lsum[2] : lsum[3];
+    // this lane's query hp: its sums sit in lane 16 (hp >> 1), slot hp & 1
+    const int src = 16 * (hp >> 1);
+    auto of_hp = [&](float va, float vb) {
+        const float a = __shfl(va, src, 64), b = __shfl(vb, src, 64);
+        return (hp & 1) ? b : a;
+    };
+    const float lh = of_hp(S.la, S.lb);
     const float il = 1.0f / lh;
-    const size_t row = part_row(W, P.Hq, b, 4 * h + hp, s);
+    const size_t row = part_row(W, P.Hq, b, hq0 + hp, s);
     bool nonfinite = !__builtin_isfinite(lh);
 #pragma unroll
     for (int nt = 0; nt < 8; nt++) {
@@ -1296,23 +1304,24 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(3, 8))) void
 #pragma unroll
         for (int i = 0; i < 4; i++) lo[i] = __shfl_down(S.acc[nt][i], 2, 16);
         const int j = nt >> 1;
-        // z sums of value group j for the four queries (uniform reads)
-        float zq[4];
-#pragma unroll
-        for (int i = 0; i < 4; i++) zq[i] = query_val(S.za[j], S.zb[j], i);
-        if (part == 0 && js == (j & 1)) {
-            const float zj = hp == 0 ? zq[0] : hp == 1 ? zq[1] : hp == 2 ? zq[2] : zq[3];
+        const float zj = of_hp(S.za[j], S.zb[j]);  // z sum of value group j, query hp
+        if (part == 0 && js == (j & 1) && hp < NQV) {
             const f4v o = (S.acc[nt] + lo + zj) * il;
 #pragma unroll
             for (int i = 0; i < 4; i++) nonfinite |= !__builtin_isfinite(o[i]);
             *(float4 *)(W.o + row * D + 16 * nt + 4 * g) = make_float4(o[0], o[1], o[2], o[3]);
         }
     }
-    flag_range(P, nonfinite, lane);
-    if (lane < 4) {
-        const float li = lane == 0 ? lsum[0] : lane == 1 ? lsum[1] : lane == 2 ? lsum[2] : lsum[3];
-        const float mi = lane == 0 ? S.m[0] : lane == 1 ? S.m[1] : lane == 2 ? S.m[2] : S.m[3];
-        const size_t row_i = part_row(W, P.Hq, b, 4 * h + lane, s);
+    flag_range(P, nonfinite && hp < NQV, lane);
+    // lane i < NQV writes query i's log-sum-exp: its l and m sit in lane
+    // 16 (i >> 1), slot i & 1 (as the maxima ma, mb)
+    const int qsrc = 16 * ((lane & 3) >> 1);
+    const float la_i = __shfl(S.la, qsrc, 64), lb_i = __shfl(S.lb, qsrc, 64);
+    const float ma_i = __shfl(S.ma, qsrc, 64), mb_i = __shfl(S.mb, qsrc, 64);
+    if (lane < NQV) {
+        const float li = (lane & 1) ? lb_i : la_i;
+        const float mi = (lane & 1) ? mb_i : ma_i;
+        const size_t row_i = part_row(W, P.Hq, b, hq0 + lane, s);
         W.ml[row_i] = make_float2(mi + log2f(li), 1.0f);
     }
 }
@@ -2183,8 +2192,14 @@ hipError_t launch_decode(const KParams &P, const uint16_t *q, float *out, float 
             default: return hipErrorInvalidValue;
         }
     } else if (gqa4) {
-        dim3 g1(W.max_splits + W.n_win, P.Hkv, P.B);
-        stage1_gqa4_mfma_kernel<<<g1, 64, 0, s>>>(P, q, W, qscale);
+        // the window chunks, then room for every split of every query quad
+        dim3 g1(gqa_quads(P.qpk) * W.max_splits + W.n_win, P.Hkv, P.B);
+        switch (P.qpk) {
+            case 2: stage1_gqa4_mfma_kernel<2><<<g1, 64, 0, s>>>(P, q, W, qscale); break;
+            case 4: stage1_gqa4_mfma_kernel<4><<<g1, 64, 0, s>>>(P, q, W, qscale); break;
+            case 8: stage1_gqa4_mfma_kernel<8><<<g1, 64, 0, s>>>(P, q, W, qscale); break;
+            default: return hipErrorInvalidValue;
+        }
     } else {
         dim3 g1(W.max_splits + W.n_win, P.Hq, P.B);   // + the window chunks of each query head
         const bool kitty = P.scheme == KVQ_SCHEME_KITTY;

@@ -119,6 +119,12 @@ def workload(wid: int, **over) -> Workload:
         w = dict(wid=10, name="witcert-paged-b32-32q8kv-ctx16384", scheme="witcert_paged", B=32,
                  Hq=32, Hkv=8, ctx=(16384,) * 32, n_outliers=4, outlier_pairs=True,
                  outlier_factor=15.0, nb=4, steps=1, seed=10)
+    elif wid == 11:
+        # a group of 8 query heads per KV head (64q/8kv), 32 requests with
+        # lengths drawn like workload 3's (uniform over 8K..32K)
+        w = dict(wid=11, name="kivi2-gqa8-b32-64q8kv-ctx8k-32k-paged", scheme="kivi2", B=32,
+                 Hq=64, Hkv=8, ctx=_lengths3(32, 8192, 32768, 11), n_outliers=4,
+                 outlier_factor=15.0, steps=1, seed=11)
     elif wid == 9:
         # KIVI-4: workload 4's shapes with 4-bit keys and values, no boosting
         w = dict(wid=9, name="kivi4-mha-b16-h32-ctx32768", scheme="kivi4", B=16, Hq=32,

@@ -56,9 +56,11 @@ def bufs(K, **over):
 def ws_bytes(B, Hq, Hkv, splits, n_win):
     """Workspace of kvq_decode_attention: a partial row (128 fp32 + {lse, A})
     per query head and split or window chunk, a stage-1 work-list item (16 B)
-    per (request, KV head, split), and 256 bytes for the list's length."""
+    per (request, KV head, query quad, split), and 256 bytes for the list's
+    length."""
     rows = B * Hq * (splits + n_win)
-    return rows * (128 * 4 + 8) + B * Hkv * splits * 16 + 256
+    quads = max(1, (Hq // Hkv) // 4)
+    return rows * (128 * 4 + 8) + B * Hkv * quads * splits * 16 + 256
 
 
 def gqa_splits(npg, sp):
@@ -277,13 +279,14 @@ def test_split_resolution_and_workspace(K):
              ("kivi2", 8, 129, 32), ("kivi2", 8, 512, 32), ("kivi2", 8, 4096, 32),
              ("kivi2", 8, 8000, 33), ("kivi2", 8, 15807, 64),
              ("kivi2", 2, 129, 12), ("kivi2", 2, 512, 12), ("kivi2", 2, 3072, 12),
-             ("kivi2", 2, 3073, 13), ("kivi2", 4, 512, 12), ("kivi4", 8, 512, 12),
+             ("kivi2", 2, 3073, 13), ("kivi2", 4, 512, 32), ("kivi2", 16, 512, 32),
+             ("kivi2", 6, 512, 12), ("kivi4", 8, 512, 12),
              ("witcert", 8, 64, 1), ("witcert", 8, 1024, 4))
     for scheme, Hq, max_pages, want in cases:
         L = K.make_layout(scheme, B=2, Hq=Hq, Hkv=2, max_pages=max_pages, n_pages=max_pages)
         rc, cache = set_layout(K, L)
         assert rc == K.KVQ_OK and cache.split_pages == want, (scheme, Hq, max_pages)
-        gqa = scheme == "kivi2" and Hq == 8
+        gqa = scheme == "kivi2" and Hq // 2 in (2, 4, 8)    # the group kernel
         rows = gqa_rows(max_pages, want) if gqa else -(-max_pages // want)
         n_win = 4 if scheme == "witcert" else 128 // 64     # 64-token chunks of the fp16 window
         ws = K.kvq_workspace_bytes(cache)

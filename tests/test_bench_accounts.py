@@ -78,7 +78,7 @@ def _stage1_mean(w, warmup=5, steps=50):
 def test_recorded_per_launch_bytes_match_the_accounting():
     with open(os.path.join(ROOT, "profiles", "traffic.json")) as f:
         rec = json.load(f)
-    names = {inputs.workload(i).name: i for i in range(1, 11)}
+    names = {inputs.workload(i).name: i for i in range(1, 12)}
     assert rec
     for key, e in rec.items():
         wname = key.split("@")[1]

@@ -97,6 +97,11 @@ def test_gqa_sink32_b64_ctx8k_32k():
     _run(inputs.workload(7))
 
 
+def test_gqa8_paged_64q8kv_b32_ctx8k_32k():
+    # a group of 8: two query quads per KV head in the group kernel
+    _run(inputs.workload(11))
+
+
 def test_witcert_paged_b32_32q8kv_ctx16384_certificate():
     _run(inputs.workload(10), kappa=2.0, cert_check=True)
 

@@ -64,13 +64,16 @@ def test_kivi_prefill_decode_small(Hq, Hkv, flags):
     _check_decode(case, out, cert, q)
 
 
-@pytest.mark.parametrize("split", [0, 5, 8, 12, 16])
-def test_gqa4_body_and_tail_splits(split):
-    # the group-of-4 kernel's work list: body splits of `split` pages, then
-    # tail splits of a quarter of that (the last one shorter), over requests
+@pytest.mark.parametrize("Hq,Hkv,split", [(8, 2, 0), (8, 2, 5), (8, 2, 8), (8, 2, 12), (8, 2, 16),
+                                           (16, 2, 0), (16, 2, 12), (4, 2, 0), (4, 2, 8), (24, 3, 5)])
+def test_gqa4_body_and_tail_splits(Hq, Hkv, split):
+    # the group kernel's work list: body splits of `split` pages, then tail
+    # splits of a quarter of that (the last one shorter), over requests
     # holding 0, 9, 19, 32, 45 and 63 quantized pages; every split's partial
-    # row merged (split 0: the default for a cache this short)
-    w = inputs.workload(3, B=6, Hq=8, Hkv=2, ctx=(70, 700, 1301, 2113, 3000, 4100), steps=3)
+    # row merged (split 0: the default for a cache this short).  Groups of 8
+    # run as two query quads per KV head, groups of 2 as one quad with two
+    # zero queries
+    w = inputs.workload(3, B=6, Hq=Hq, Hkv=Hkv, ctx=(70, 700, 1301, 2113, 3000, 4100), steps=3)
     case = _case(w, extra_tokens=80, split_pages=split)
     case.check_status()
     out, cert, q = case.decode_now(7)
