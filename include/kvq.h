@@ -153,11 +153,16 @@ typedef struct kvq_layout {
                                 m, 0 .. 4; 0 for others */
     int32_t max_pages;       /* page-table row length per request */
     int32_t n_pages;         /* pages in the pool */
-    int32_t split_pages;     /* stage-1 split size in pages; 0: 4 when max_pages
-                                <= 128, else 16 for KIVI2 with 4 query heads
-                                per KV head and 12 otherwise (1 for WITCERT,
-                                4 for WITCERT_PAGED), raised to
-                                ceil(max_pages / 256) where that is larger */
+    int32_t split_pages;     /* stage-1 split size in pages; 0: the default.
+                                KIVI2 with 2, 4 or 8 query heads per KV head
+                                (the group kernel): body splits of 8 pages when
+                                max_pages <= 128, else 32, each request's last
+                                pages in tail splits of a quarter of that
+                                (see kvq_decode_attention).  Others: 4 when
+                                max_pages <= 128, else 12 (1 for WITCERT, 4 for
+                                WITCERT_PAGED).  Raised where a request of
+                                max_pages pages would need more than 256
+                                splits */
     int32_t flags;           /* KVQ_FLAG_* */
     uint32_t layer;          /* WITCERT(_PAGED) dither counter field; < 65536 */
     uint64_t seed;           /* WITCERT(_PAGED) dither key */
@@ -264,7 +269,12 @@ int kvq_flush_key_group(const kvq_cache_t *cache, hipStream_t stream);
  * Stage 1 covers the tokens whose key and value are both quantized in splits
  * of split_pages pages, and the fp16 window (and the sink tokens) in 64-token
  * chunks, each a partial of its own; stage 2 merges all partials with
- * log-sum-exp weights ("WitCert" Key structure).  A request with no token gets a zero
+ * log-sum-exp weights ("WitCert" Key structure).  KIVI2 with 2, 4 or 8 query
+ * heads per KV head (no KVQ_FLAG_GENERIC_STAGE1) runs the group kernel, which
+ * reads each page once per four query heads: a request of npg pages is cut
+ * into splits of split_pages pages over all but its last min(npg / 8,
+ * 2 split_pages) pages and splits of split_pages / 4 over the rest, run
+ * longest first from a work list built on the device for each call.  A request with no token gets a zero
  * output row and a zero certificate.  Returns KVQ_EWORKSPACE if ws_bytes is
  * too small.
  * Range of the matrix-core stage 1 (KIVI2, KITTY, KITTY_DYN and KIVI4
@@ -290,7 +300,7 @@ int kvq_decode_attention(const kvq_cache_t *cache, const uint16_t *q, float *out
  * kvq_decode_attention with a workspace.  Allocates and frees nothing.
  * Returns KVQ_ENOSCRATCH, before any device work, when kvq_workspace_bytes()
  * of the cache exceeds KVQ_NOALLOC_SCRATCH_BYTES (for the GQA workload of 64
- * requests x 32 query heads with 32K-token page tables, 48 MB are needed);
+ * requests x 32 query heads with 32K-token page tables, 29 MB are needed);
  * KVQ_ELAUNCH if the device or the array's address cannot be obtained.
  * Every call on one GPU shares that GPU's array: calls whose execution
  * overlaps on one GPU (other streams, other threads) race on it and must be
