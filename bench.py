@@ -222,8 +222,13 @@ def setup_gpu(w: inputs.Workload, extra: int, split_pages: int):
     return cache
 
 
+def event_steps(steps: int, every: int) -> list:
+    """The timed steps whose stage-1 launch is bracketed by HIP events."""
+    return [j for j in range(steps) if j % max(1, every) == 0]
+
+
 def run_gpu(w: inputs.Workload, steps: int, warmup: int, split_pages: int, copies: int = 1,
-            settle_s: float = 0.06, latency_steps: int = 0):
+            settle_s: float = 0.06, latency_steps: int = 0, event_every: int = 4):
     """copies > 1: that many independent caches of the workload, used in turn
     (step i on copy i mod copies), so that no cache stays resident in the
     memory-side cache between its steps (a cold-cache figure).
@@ -233,6 +238,10 @@ def run_gpu(w: inputs.Workload, steps: int, warmup: int, split_pages: int, copie
     idles during the host-side prefill and needs some 20 ms of work to return
     to its working clock; without this the few timed steps of a short run
     would measure that ramp instead of the kernels.
+
+    event_every: HIP events bracket the stage-1 launch of every event_every-th
+    timed step (event_steps): recording them costs the stream about 5 us of
+    a step on this chip, so bracketing every step would slow the timed loop.
 
     latency_steps: after the timed steps, that many more steps one at a time,
     each bracketed by events on the stream and followed by a host
@@ -251,14 +260,15 @@ def run_gpu(w: inputs.Workload, steps: int, warmup: int, split_pages: int, copie
     out = torch.empty((w.B, w.Hq, 128), dtype=torch.float32, device="cuda")
     cert = torch.empty((w.B, w.Hq), dtype=torch.float32, device="cuda")
     stream = torch.cuda.current_stream()
-    ev1 = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(steps)]
+    sampled = event_steps(steps, event_every)
+    ev1 = {j: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for j in sampled}
     kappa = 1.0 if w.scheme in ("witcert", "witcert_paged") else 0.0
-    for a, b in ev1:            # torch creates the HIP event at its first record
+    for a, b in ev1.values():   # torch creates the HIP event at its first record
         a.record()
         b.record()
     torch.cuda.synchronize()
-    assert all(a.cuda_event and b.cuda_event for a, b in ev1)
+    assert all(a.cuda_event and b.cuda_event for a, b in ev1.values())
 
     def one(i, evs=None):
         cache = caches[i % copies]
@@ -284,7 +294,7 @@ def run_gpu(w: inputs.Workload, steps: int, warmup: int, split_pages: int, copie
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for j in range(steps):
-        one(warmup + j, ev1[j])
+        one(warmup + j, ev1.get(j))
     torch.cuda.synchronize()
     dt = time.perf_counter() - t0
     for cache in caches:
@@ -294,7 +304,7 @@ def run_gpu(w: inputs.Workload, steps: int, warmup: int, split_pages: int, copie
             raise RuntimeError(f"device status {st:#x}")
     if not torch.isfinite(out).all():
         raise RuntimeError("non-finite output")
-    s1_ms = [a.elapsed_time(b) for a, b in ev1]
+    s1_ms = [ev1[j][0].elapsed_time(ev1[j][1]) for j in sampled]
     lat = None
     if latency_steps:
         dev_us, host_us = [], []
@@ -443,6 +453,8 @@ def main():
                     help="two cache copies used in turn, so the memory-side cache holds neither")
     ap.add_argument("--settle-ms", type=float, default=80.0,
                     help="decode-only passes before the warm-up steps, to bring the clock up")
+    ap.add_argument("--event-every", type=int, default=4,
+                    help="bracket the stage-1 launch of every N-th timed step with HIP events")
     ap.add_argument("--latency", type=int, default=-1,
                     help="steps timed one at a time after the timed loop (default: 200 for "
                          "workload 1, else 0)")
@@ -470,7 +482,8 @@ def main():
     copies = 2 if args.cold else 1
     lat_steps = args.latency if args.latency >= 0 else (200 if args.workload == 1 else 0)
     dt, s1_ms, settle, lat = run_gpu(w, args.steps, args.warmup, args.split_pages, copies,
-                                     args.settle_ms * 1e-3, lat_steps)
+                                     args.settle_ms * 1e-3, lat_steps, args.event_every)
+    sampled = set(event_steps(args.steps, args.event_every))
 
     # algorithmic bytes of the timed steps (step i advances copy i mod copies)
     cstates = [[state_after_prefill(w, l) for l in w.ctx] for _ in range(copies)]
@@ -490,7 +503,10 @@ def main():
             s1_calls.append(0)
         b, s1, cstates[i % copies] = step_bytes(w, states)
         tot += b
-        s1_bytes.append(s1)
+        if i - args.warmup in sampled:     # the launches the events timed
+            s1_bytes.append(s1)
+        else:
+            s1_calls.pop()
     gbs = tot / dt / 1e9
     ms_step = dt / args.steps * 1e3
     s1_avg_ms = float(np.mean(s1_ms))
@@ -511,6 +527,7 @@ def main():
                 "valu_ops_per_philox_call": ops_call,
                 "traffic": traffic_entry(kernel, w.name),
                 "avg_launch_us": round(s1_avg_ms * 1e3, 2),
+                "timed_launches": len(s1_ms),
                 "median_launch_us": round(float(np.median(s1_ms)) * 1e3, 2),
                 "philox_calls_per_launch": int(calls),
                 "algorithmic_bytes_per_launch": int(np.mean(s1_bytes)),
@@ -521,6 +538,7 @@ def main():
                 "frac": round(s1_gbs / HBM_PEAK_GBS, 4),
                 "traffic": traffic_entry(kernel, w.name),
                 "avg_launch_us": round(s1_avg_ms * 1e3, 2),
+                "timed_launches": len(s1_ms),
                 "median_launch_us": round(float(np.median(s1_ms)) * 1e3, 2),
                 "algorithmic_bytes_per_launch": int(np.mean(s1_bytes))}
     rec = {"metric": METRIC, "value": round(gbs, 1), "unit": "GB/s", "n_gpus": 1,
