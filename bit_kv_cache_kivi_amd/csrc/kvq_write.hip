@@ -168,13 +168,17 @@ __global__ __launch_bounds__(64) void append_kivi_kernel(KParams P, const uint16
     const Geom G = geom(P.scheme, P.nb);
     const size_t bh = (size_t)b * P.Hkv + h;
     int32_t *st = P.state + bh * 4;
-    const int l = st[0], nkq = st[1];
+    // the new key and value and the state are loaded before anything waits
+    // for them: {l, n_kq} as one pair
+    const uint32_t knew = ((const uint32_t *)(kn + bh * D))[lane];
+    const uint32_t vnew = ((const uint32_t *)(vn + bh * D))[lane];
+    const int2 lk = *(const int2 *)st;
+    const int l = lk.x, nkq = lk.y;
+    asm volatile("" ::"s"(l), "s"(nkq));           // both halves before the branches below
     const int R = P.R, S = P.sink;
-    const uint32_t *kin = (const uint32_t *)(kn + bh * D);
-    const uint32_t *vin = (const uint32_t *)(vn + bh * D);
     if (l < S) {                                     // a sink token: kept fp16, outside the windows
-        ((uint32_t *)P.sink_k)[(bh * S + (size_t)l) * (D / 2) + lane] = kin[lane];
-        ((uint32_t *)P.sink_v)[(bh * S + (size_t)l) * (D / 2) + lane] = vin[lane];
+        ((uint32_t *)P.sink_k)[(bh * S + (size_t)l) * (D / 2) + lane] = knew;
+        ((uint32_t *)P.sink_v)[(bh * S + (size_t)l) * (D / 2) + lane] = vnew;
         if (lane == 0) {
             st[0] = l + 1;
             st[1] = l + 1;
@@ -196,12 +200,13 @@ __global__ __launch_bounds__(64) void append_kivi_kernel(KParams P, const uint16
         // quantized position t - S
         const int t = l - R - S;
         const int pid = P.table[(size_t)b * P.max_pages + t / PT];
+        const uint32_t old = rv[lane];               // channels 2*lane, 2*lane+1 (issued with the id)
+        asm volatile("" ::"v"(old));                  // loaded together with the id, not after its check
         if (!page_ok(P, pid)) {
             if (lane == 0) atomicOr(P.status, (uint32_t)KVQ_STATUS_UNMAPPED_PAGE);
             return;
         }
         uint8_t *page = page_ptr(P, pid, h);
-        const uint32_t old = rv[lane];               // channels 2*lane, 2*lane+1
         const float x0 = h2f((uint16_t)(old & 0xffffu)), x1 = h2f((uint16_t)(old >> 16));
         float mn = fminf(x0, x1), mx = fmaxf(x0, x1);
 #pragma unroll
@@ -231,8 +236,8 @@ __global__ __launch_bounds__(64) void append_kivi_kernel(KParams P, const uint16
             flag_value_scale(P, ap.s);
         }
     }
-    rk[lane] = kin[lane];
-    rv[lane] = vin[lane];
+    rk[lane] = knew;
+    rv[lane] = vnew;
     if (lane == 0) st[0] = l + 1;
 }
 
