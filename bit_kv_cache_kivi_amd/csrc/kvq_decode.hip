@@ -709,22 +709,22 @@ __device__ inline void mul_split2(float x0, _Float16 y0, float x1, _Float16 y1, 
     lo = rem_pair(a0, a1, hi);
 }
 
-// hi + lo of the two products q0 s0 and q1 s1 (q0, q1 the f16 halves of q;
-// s0, s1 the f16 in the low halves of their registers): hi = fl16(q s) and
-// lo = fl16(q s - hi), each formed from the exact product by one
-// mixed-precision fused multiply-add.
-__device__ inline void split_qs(uint32_t q, uint32_t s0, uint32_t s1, uint32_t &hi, uint32_t &lo) {
-    uint32_t h, l;
-    asm("v_fma_mixlo_f16 %0, %1, %2, 0 op_sel_hi:[1,1,0]" : "=&v"(h) : "v"(q), "v"(s0));
-    asm("v_fma_mixhi_f16 %0, %1, %2, 0 op_sel:[1,0,0] op_sel_hi:[1,1,0]" : "+v"(h) : "v"(q), "v"(s1));
-    asm("v_fma_mixlo_f16 %0, %1, %2, -%3 op_sel_hi:[1,1,1]" : "=&v"(l) : "v"(q), "v"(s0), "v"(h));
-    asm("v_fma_mixhi_f16 %0, %1, %2, -%3 op_sel:[1,0,1] op_sel_hi:[1,1,1]" : "+v"(l) : "v"(q), "v"(s1), "v"(h));
-    hi = h;
-    lo = l;
+// hi + lo of the two products q0 s0 and q1 s1, q = (q0, q1) and s2 = (s0, s1)
+// packed f16 pairs: hi = fl16(q s) by one packed f16 multiply and lo =
+// fl16(q s - hi) by one packed fused multiply-add.  An f16 x f16 product is
+// exact before its single rounding, so hi + lo is q s to within half an ulp
+// of lo.
+__device__ inline void split_qs_pk(uint32_t q, uint32_t s2, uint32_t &hi, uint32_t &lo) {
+    const h2v qv = __builtin_bit_cast(h2v, q), sv = __builtin_bit_cast(h2v, s2);
+    const h2v h = qv * sv;
+    const h2v l = __builtin_elementwise_fma(qv, sv, -h);
+    hi = __builtin_bit_cast(uint32_t, h);
+    lo = __builtin_bit_cast(uint32_t, l);
 }
 
-// The same for p s0 and p s1 with p binary32: hi = fl16(p s), lo = fl16(p s -
-// hi) from the fused products, so hi + lo is p s to within ~2^-22 of it.
+// hi + lo of p s0 and p s1 with p binary32 and s0, s1 the f16 in the low
+// halves of their registers: hi = fl16(p s), lo = fl16(p s - hi) from the
+// fused products, so hi + lo is p s to within ~2^-22 of it.
 __device__ inline void split_ps(float p, uint32_t s0, uint32_t s1, uint32_t &hi, uint32_t &lo) {
     uint32_t h, l;
     asm("v_fma_mixlo_f16 %0, %1, %2, 0 op_sel_hi:[0,1,0]" : "=&v"(h) : "v"(p), "v"(s0));
@@ -733,18 +733,6 @@ __device__ inline void split_ps(float p, uint32_t s0, uint32_t s1, uint32_t &hi,
     asm("v_fma_mixhi_f16 %0, %1, %2, -%3 op_sel:[0,0,1] op_sel_hi:[0,1,1]" : "+v"(l) : "v"(p), "v"(s1), "v"(h));
     hi = h;
     lo = l;
-}
-
-// acc + q z in binary32 (exact product): q the f16 in half QH of its
-// register, z the f16 in the high half of its own (a key group's {s, z})
-template <int QH>
-__device__ inline float fma_qz(uint32_t q, uint32_t z, float acc) {
-    float d;
-    if constexpr (QH == 0)
-        asm("v_fma_mix_f32 %0, %1, %2, %3 op_sel:[0,1,0] op_sel_hi:[1,1,0]" : "=v"(d) : "v"(q), "v"(z), "v"(acc));
-    else
-        asm("v_fma_mix_f32 %0, %1, %2, %3 op_sel:[1,1,0] op_sel_hi:[1,1,0]" : "=v"(d) : "v"(q), "v"(z), "v"(acc));
-    return d;
 }
 
 template <int CTRL>
@@ -860,18 +848,26 @@ __device__ inline void gqa4_page(const Gqa4Page &R, Gqa4State &S, Gqa4Smem &sm, 
     // queries, and the zero-point sums, added over the group's 32 lanes ----
     const int gi_p = lane >> 5;
     const uint32_t sz[4] = {R.ks.x, R.ks.y, R.ks.z, R.ks.w};
-    float bzp[4];                          // this lane's share of sum_c q_h z_c [query]
+    // the channel pairs' scales and zero points, packed (one permute each,
+    // shared by the four queries)
+    const uint32_t s01 = __builtin_amdgcn_perm(sz[1], sz[0], 0x05040100u);
+    const uint32_t s23 = __builtin_amdgcn_perm(sz[3], sz[2], 0x05040100u);
+    const uint32_t z01 = __builtin_amdgcn_perm(sz[1], sz[0], 0x07060302u);
+    const uint32_t z23 = __builtin_amdgcn_perm(sz[3], sz[2], 0x07060302u);
+    // bzp: this lane's share of sum_c q_h z_c per query, by two f16 dot
+    // products into a binary32 sum (each f16 x f16 product exact)
+    float bzp[4];
 #pragma unroll
     for (int h = 0; h < 4; h++) {
         uint32_t hv0, lv0, hv1, lv1;
-        split_qs(qw[h].x, sz[0], sz[1], hv0, lv0);
-        split_qs(qw[h].y, sz[2], sz[3], hv1, lv1);
+        split_qs_pk(qw[h].x, s01, hv0, lv0);
+        split_qs_pk(qw[h].y, s23, hv1, lv1);
         ((uint2 *)&sm.As[gi_p][2 * h][0])[lane & 31] = make_uint2(hv0, hv1);
         ((uint2 *)&sm.As[gi_p][2 * h + 1][0])[lane & 31] = make_uint2(lv0, lv1);
-        float bz = fma_qz<0>(qw[h].x, sz[0], 0.0f);
-        bz = fma_qz<1>(qw[h].x, sz[1], bz);
-        bz = fma_qz<0>(qw[h].y, sz[2], bz);
-        bzp[h] = fma_qz<1>(qw[h].y, sz[3], bz);
+        bzp[h] = __builtin_amdgcn_fdot2(__builtin_bit_cast(h2v, qw[h].y), __builtin_bit_cast(h2v, z23),
+                                        __builtin_amdgcn_fdot2(__builtin_bit_cast(h2v, qw[h].x),
+                                                               __builtin_bit_cast(h2v, z01), 0.0f, false),
+                                        false);
     }
     // Sum the shares over the 32 lanes of the key group, reduce-scatter
     // style.  With f = (L & 1) ^ (L >> 4 & 1), the first quad exchange keeps
