@@ -56,6 +56,7 @@ __device__ inline float2v cvt2(uint32_t x, int sel) {
 // ---------------------------------------------------------------------------
 typedef _Float16 h8v __attribute__((ext_vector_type(8)));
 typedef _Float16 h2v __attribute__((ext_vector_type(2)));
+typedef _Float16 h4v __attribute__((ext_vector_type(4)));
 typedef float f4v __attribute__((ext_vector_type(4)));
 typedef uint32_t u4v __attribute__((ext_vector_type(4)));
 
@@ -735,6 +736,28 @@ __device__ inline void split_ps(float p, uint32_t s0, uint32_t s1, uint32_t &hi,
     lo = l;
 }
 
+// x >> 2 for both dwords of a register pair by one 64-bit shift; the two bits
+// the high dword moves into the low one land in its top nibble's upper half,
+// which the code mask clears
+__device__ inline void shr2_pairs(const uint32_t (&x)[8], uint32_t (&y)[8]) {
+#pragma unroll
+    for (int i = 0; i < 8; i += 2) {
+        uint64_t v;
+        asm("v_lshrrev_b64 %0, 2, %1" : "=v"(v) : "v"((((uint64_t)x[i + 1] << 32) | x[i])));
+        y[i] = (uint32_t)v;
+        y[i + 1] = (uint32_t)(v >> 32);
+    }
+}
+
+// LDS read with a 4 x 4 transpose per group of four lanes (gfx950): within
+// each 16-lane group, element e of lane j is element j & 3 of the 8 bytes
+// that lane 4 e + (j >> 2) addresses
+__device__ inline h4v lds_tr16(const uint32_t *p) {
+    typedef short s4v __attribute__((ext_vector_type(4)));
+    return __builtin_bit_cast(h4v, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) s4v *)(__attribute__((address_space(3))) void *)p));
+}
+
 template <int CTRL>
 __device__ inline float dppf(float x) {
     return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0u, __builtin_bit_cast(uint32_t, x), CTRL, 0xf, 0xf, true));
@@ -798,14 +821,18 @@ struct Gqa4Page {
 
 constexpr int AS_STRIDE = 20;       // octets per score-operand row (16 + bank padding)
 
-// f16 per P.V operand column row: 64 tokens + 8, so that the 16 columns read
-// by one 16-lane group of an operand load start on 16 distinct 4-bank groups
-constexpr int BT_STRIDE = 72;
+// The P.V operand token-major: a token's 16 f16 columns in one row of
+// BT_DW dwords, so that a lane stores its token's eight columns of an operand
+// with one 16-byte write; the operand fragments are read back column-major by
+// transposing LDS reads.  12-dword rows (8 + 4 of padding): the 16-byte
+// writes of 16 lanes (16 consecutive tokens) start on 16 distinct 4-bank
+// groups of the 64 banks.
+constexpr int BT_DW = 12;
 
 struct Gqa4Smem {
     h8v As[2][8][AS_STRIDE];        // score A: [key group][row 2h = hi(q_h s), 2h + 1 = lo][channel octet]
     h8v Az[AS_STRIDE];              // a zero row (the other key group's operand rows)
-    _Float16 Bs[2][16][BT_STRIDE];  // P.V B: [operand][column (h, part, js)][token]
+    uint32_t Bt[2][PT][BT_DW];      // P.V B: [operand][token][column pair (h, part, js)]
 };
 
 // Token of this lane's first softmax score (the second is 16 later): lane
@@ -892,20 +919,21 @@ __device__ inline void gqa4_page(const Gqa4Page &R, Gqa4State &S, Gqa4Smem &sm, 
 
     // ---- scores on the matrix cores ----
     const uint32_t kd[8] = {R.ka.x, R.ka.y, R.ka.z, R.ka.w, R.kb.x, R.kb.y, R.kb.z, R.kb.w};
+    uint32_t kd2[8];                            // the same >> 2
+    shr2_pairs(kd, kd2);
     f4v sc[2] = {f4v{0.f, 0.f, 0.f, 0.f}, f4v{0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
     for (int kc = 0; kc < 4; kc++) {
         const h8v af1 = a1[4 * kc + g], af2 = a2[4 * kc + g];
+        const uint32_t *kx = (kc & 1) ? kd2 : kd;
 #pragma unroll
         for (int n2 = 0; n2 < 2; n2++) {
-            const uint32_t x = kd[2 * n2 + (kc >> 1)];
-            const h8v bf = frag8((kc & 1) ? ((x >> 2) & MSK) : (x & MSK));
+            const h8v bf = frag8(kx[2 * n2 + (kc >> 1)] & MSK);
             sc[n2] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af1, bf, sc[n2], 0, 0, 0);
         }
 #pragma unroll
         for (int n2 = 0; n2 < 2; n2++) {
-            const uint32_t x = kd[2 * (n2 + 2) + (kc >> 1)];
-            const h8v bf = frag8((kc & 1) ? ((x >> 2) & MSK) : (x & MSK));
+            const h8v bf = frag8(kx[2 * (n2 + 2) + (kc >> 1)] & MSK);
             sc[n2] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af2, bf, sc[n2], 0, 0, 0);
         }
     }
@@ -923,9 +951,17 @@ __device__ inline void gqa4_page(const Gqa4Page &R, Gqa4State &S, Gqa4Smem &sm, 
         for (int j = 0; j < 2; j++)
             if (t0 + 16 * j >= nvalid) z[j][0] = z[j][1] = -INFINITY;
     }
-    const bool exceed = z[0][0] > S.ma + LAZY_TAU || z[1][0] > S.ma + LAZY_TAU ||
-                        z[0][1] > S.mb + LAZY_TAU || z[1][1] > S.mb + LAZY_TAU;
-    if (__any(exceed)) {
+    // the exponents against the running maxima; a rescale only when one of
+    // them passes LAZY_TAU (-inf - -inf = NaN, where a first page's
+    // masked token meets a maximum not yet set, is passed over by fmaxf: the
+    // page's valid tokens give +inf)
+    float d[2][2];
+#pragma unroll
+    for (int j = 0; j < 2; j++) {
+        d[j][0] = z[j][0] - S.ma;
+        d[j][1] = z[j][1] - S.mb;
+    }
+    if (__any(fmaxf(fmaxf(d[0][0], d[1][0]), fmaxf(d[0][1], d[1][1])) > LAZY_TAU)) {
         // the new maxima: over the 32 lanes holding each query (lane bits
         // 0..3 and 5), then moved in every lane
         float mt[2] = {fmaxf(z[0][0], z[1][0]), fmaxf(z[0][1], z[1][1])};
@@ -959,12 +995,17 @@ __device__ inline void gqa4_page(const Gqa4Page &R, Gqa4State &S, Gqa4Smem &sm, 
         const float ap = hp == 0 ? alpha[0] : hp == 1 ? alpha[1] : hp == 2 ? alpha[2] : alpha[3];
 #pragma unroll
         for (int nt = 0; nt < 8; nt++) S.acc[nt] *= ap;
+#pragma unroll
+        for (int j = 0; j < 2; j++) {
+            d[j][0] = z[j][0] - S.ma;
+            d[j][1] = z[j][1] - S.mb;
+        }
     }
     float p[2][2];                              // [token][query a, a + 1]
 #pragma unroll
     for (int j = 0; j < 2; j++) {
-        p[j][0] = __builtin_amdgcn_exp2f(z[j][0] - S.ma);
-        p[j][1] = __builtin_amdgcn_exp2f(z[j][1] - S.mb);
+        p[j][0] = __builtin_amdgcn_exp2f(d[j][0]);
+        p[j][1] = __builtin_amdgcn_exp2f(d[j][1]);
     }
     S.la += p[0][0] + p[1][0];
     S.lb += p[0][1] + p[1][1];
@@ -980,25 +1021,20 @@ __device__ inline void gqa4_page(const Gqa4Page &R, Gqa4State &S, Gqa4Smem &sm, 
             const uint4 v4 = j ? R.vs1 : R.vs0;
             const uint32_t vw[4] = {v4.x, v4.y, v4.z, v4.w};
             const int t = t0 + 16 * j;
+            uint32_t h01[2], l01[2], h23[2], l23[2];
 #pragma unroll
             for (int k = 0; k < 2; k++) {
                 const float pk = p[j][k];
                 float *zk = k ? S.zb : S.za;
 #pragma unroll
                 for (int jv = 0; jv < 4; jv++) zk[jv] = fmaf(pk, (float)hi16h(vw[jv]), zk[jv]);
-                uint32_t h01, l01, h23, l23;
-                split_ps(pk, vw[0], vw[1], h01, l01);
-                split_ps(pk, vw[2], vw[3], h23, l23);
-                const int c = 4 * (ha + k);
-                sm.Bs[0][c + 0][t] = lo16h(h01);
-                sm.Bs[0][c + 1][t] = hi16h(h01);
-                sm.Bs[0][c + 2][t] = lo16h(l01);
-                sm.Bs[0][c + 3][t] = hi16h(l01);
-                sm.Bs[1][c + 0][t] = lo16h(h23);
-                sm.Bs[1][c + 1][t] = hi16h(h23);
-                sm.Bs[1][c + 2][t] = lo16h(l23);
-                sm.Bs[1][c + 3][t] = hi16h(l23);
+                split_ps(pk, vw[0], vw[1], h01[k], l01[k]);
+                split_ps(pk, vw[2], vw[3], h23[k], l23[k]);
             }
+            // columns 4 (ha + k) .. + 3 = (hi of groups 2o, 2o + 1, lo of
+            // the same) for queries ha + k, k = 0, 1: dwords 2 ha .. + 3
+            *(uint4 *)&sm.Bt[0][t][2 * ha] = make_uint4(h01[0], l01[0], h01[1], l01[1]);
+            *(uint4 *)&sm.Bt[1][t][2 * ha] = make_uint4(h23[0], l23[0], h23[1], l23[1]);
         }
     }
     lds_sync();
@@ -1007,16 +1043,23 @@ __device__ inline void gqa4_page(const Gqa4Page &R, Gqa4State &S, Gqa4Smem &sm, 
     // take operand 0, tiles 4..7 (groups 2, 3) operand 1; one product per tile
     // and 32-token step carries both halves of all four queries ----
     const uint32_t vd[8] = {R.va.x, R.va.y, R.va.z, R.va.w, R.vb.x, R.vb.y, R.vb.z, R.vb.w};
+    uint32_t vd2[8];                            // the same >> 2
+    shr2_pairs(vd, vd2);
 #pragma unroll
     for (int ks = 0; ks < 2; ks++) {
+        const uint32_t *vx = ks ? vd2 : vd;
 #pragma unroll
         for (int o = 0; o < 2; o++) {
-            const h8v bv = *(const h8v *)&sm.Bs[o][r][32 * ks + 8 * g];
+            // column r, tokens 32 ks + 8 g .. + 7: lane r of the 16-lane
+            // group addresses token row 32 ks + 8 g + (r >> 2) (+ 4), columns
+            // 4 (r & 3) .. + 3; the transposing read hands lane r column r
+            const uint32_t *rp = &sm.Bt[o][32 * ks + 8 * g + (r >> 2)][2 * (r & 3)];
+            const h4v b0 = lds_tr16(rp), b1 = lds_tr16(rp + 4 * BT_DW);
+            const h8v bv = __builtin_shufflevector(b0, b1, 0, 1, 2, 3, 4, 5, 6, 7);
 #pragma unroll
             for (int u = 0; u < 4; u++) {
                 const int nt = 4 * o + u;
-                const uint32_t x = vd[nt];
-                const h8v af = frag8(ks ? ((x >> 2) & MSK) : (x & MSK));
+                const h8v af = frag8(vx[nt] & MSK);
                 S.acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af, bv, S.acc[nt], 0, 0, 0);
             }
         }
