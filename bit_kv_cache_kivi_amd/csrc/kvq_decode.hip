@@ -1240,8 +1240,12 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(3, 8))) void
         window_partial<QPK, PT, KVQ_SCHEME_KIVI2>(P, q, W, qscale, it.b, it.hd, QPK * it.hd, it.s, lane, U.win);
         return;
     }
-    if (L - nw >= (int)*W.n_items) return;
+    // the item is read together with the list length (the grid never passes
+    // the list's capacity, so the read is in bounds either way)
     const uint4 item = W.items[L - nw];
+    const int n_items = (int)*W.n_items;
+    asm volatile("" ::"s"(item.x), "s"(n_items));
+    if (L - nw >= n_items) return;
     const int pair = (int)(item.x / (uint32_t)NQ4), quad = (int)(item.x % (uint32_t)NQ4);
     const int b = pair / P.Hkv, h = pair % P.Hkv;
     const int hq0 = h * QPK + 4 * quad;               // the quad's first query head
@@ -1314,24 +1318,32 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(3, 8))) void
 
     // ---- reduce and write the split's partial ----
     // l and the zero-point sums of query a, a + 1: over the 32 lanes holding
-    // them (lane bits 0..3 and 5); query i then sits in lane 16 (i >> 1)
+    // them (lane bits 0..3 by DPP within the row, bit 5 by a permute), which
+    // then all hold the sums; query i sits in the rows of parity i >> 1, slot
+    // i & 1
+    const int x32 = (lane ^ 32) << 2;
+    auto red = [&](float v) {
+        v += dppf<0xB1>(v);                          // quad_perm [1,0,3,2]
+        v += dppf<0x4E>(v);                          // quad_perm [2,3,0,1]
+        v += dppf<0x124>(v);                         // row_ror:4
+        v += dppf<0x128>(v);                         // row_ror:8
+        return v + __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(x32, __builtin_bit_cast(int, v)));
+    };
+    S.la = red(S.la);
+    S.lb = red(S.lb);
 #pragma unroll
-    for (int msk = 1; msk < 64; msk <<= 1) {
-        if (msk == 16) continue;
-        S.la += shfl_xor(S.la, msk);
-        S.lb += shfl_xor(S.lb, msk);
-#pragma unroll
-        for (int j = 0; j < 4; j++) {
-            S.za[j] += shfl_xor(S.za[j], msk);
-            S.zb[j] += shfl_xor(S.zb[j], msk);
-        }
+    for (int j = 0; j < 4; j++) {
+        S.za[j] = red(S.za[j]);
+        S.zb[j] = red(S.zb[j]);
     }
     const int hp = r >> 2, part = (r >> 1) & 1, js = r & 1;
-    // this lane's query hp: its sums sit in lane 16 (hp >> 1), slot hp & 1
-    const int src = 16 * (hp >> 1);
+    // this lane's query hp: slot hp & 1 of its own row where the row's
+    // parity is hp >> 1, else of lane ^ 16 (the same r, the other parity)
+    const bool own = (g & 1) == (hp >> 1);
     auto of_hp = [&](float va, float vb) {
-        const float a = __shfl(va, src, 64), b = __shfl(vb, src, 64);
-        return (hp & 1) ? b : a;
+        const float t = (hp & 1) ? vb : va;
+        const float u = __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, t), 0x401F));  // lane ^ 16
+        return own ? t : u;
     };
     const float lh = of_hp(S.la, S.lb);
     const float il = 1.0f / lh;
@@ -1339,9 +1351,9 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(3, 8))) void
     bool nonfinite = !__builtin_isfinite(lh);
 #pragma unroll
     for (int nt = 0; nt < 8; nt++) {
-        f4v lo;                                   // the lo column, two lanes up
+        f4v lo;                                   // the lo column, two lanes up (lane ^ 2)
 #pragma unroll
-        for (int i = 0; i < 4; i++) lo[i] = __shfl_down(S.acc[nt][i], 2, 16);
+        for (int i = 0; i < 4; i++) lo[i] = dppf<0x4E>(S.acc[nt][i]);
         const int j = nt >> 1;
         const float zj = of_hp(S.za[j], S.zb[j]);  // z sum of value group j, query hp
         if (part == 0 && js == (j & 1) && hp < NQV) {
@@ -1352,14 +1364,14 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(3, 8))) void
         }
     }
     flag_range(P, nonfinite && hp < NQV, lane);
-    // lane i < NQV writes query i's log-sum-exp: its l and m sit in lane
-    // 16 (i >> 1), slot i & 1 (as the maxima ma, mb)
-    const int qsrc = 16 * ((lane & 3) >> 1);
-    const float la_i = __shfl(S.la, qsrc, 64), lb_i = __shfl(S.lb, qsrc, 64);
-    const float ma_i = __shfl(S.ma, qsrc, 64), mb_i = __shfl(S.mb, qsrc, 64);
+    // lane i < NQV writes query i's log-sum-exp: its l and m sit in the rows
+    // of parity i >> 1, slot i & 1 (as the maxima ma, mb)
+    const float lt = (lane & 1) ? S.lb : S.la, mt = (lane & 1) ? S.mb : S.ma;
+    const float lu = __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, lt), 0x401F));
+    const float mu = __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, mt), 0x401F));
     if (lane < NQV) {
-        const float li = (lane & 1) ? lb_i : la_i;
-        const float mi = (lane & 1) ? mb_i : ma_i;
+        const float li = (lane & 2) ? lu : lt;
+        const float mi = (lane & 2) ? mu : mt;
         const size_t row_i = part_row(W, P.Hq, b, hq0 + lane, s);
         W.ml[row_i] = make_float2(mi + log2f(li), 1.0f);
     }
