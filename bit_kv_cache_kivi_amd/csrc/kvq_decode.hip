@@ -169,22 +169,26 @@ __device__ void window_partial(const KParams &P, const uint16_t *__restrict__ q,
             pid_l = 0;                            // read page 0 instead; the result is flagged
         }
     }
-    uint32_t vv[VPF];
-    auto load_v = [&](int tt0) {
+    // values of tokens tt0 .. tt0 + VPF - 1; with 2 VPF = PT the chunk's
+    // values come in two batches, the second loaded once the scores no longer
+    // hold the keys' registers
+    constexpr bool two = 2 * VPF == PT;
+    uint32_t vv[VPF], vv2[two ? VPF : 1];
+    auto load_v = [&](int tt0, uint32_t *v) {
         if (sinkc) {
 #pragma unroll
             for (int u = 0; u < VPF; u++)
-                vv[u] = tt0 + u < n ? *(const uint32_t *)(P.sink_v + (bh * S + (size_t)(tt0 + u)) * D + 2 * lane) : 0u;
+                v[u] = tt0 + u < n ? *(const uint32_t *)(P.sink_v + (bh * S + (size_t)(tt0 + u)) * D + 2 * lane) : 0u;
             return;
         }
         int slot = wit ? t0 + tt0 - nkq : (t0 + tt0) % P.R;
 #pragma unroll
         for (int u = 0; u < VPF; u++) {
-            vv[u] = tt0 + u < n ? *(const uint32_t *)(P.res_v + (bh * win + (size_t)slot) * D + 2 * lane) : 0u;
+            v[u] = tt0 + u < n ? *(const uint32_t *)(P.res_v + (bh * win + (size_t)slot) * D + 2 * lane) : 0u;
             if (++slot == win) slot = 0;          // the value ring wraps (KIVI2 / KITTY)
         }
     };
-    load_v(0);
+    load_v(0, vv);
     // A operand of the score product: row = query (exact in f16), k = channel
     // 32 kc + 8 g + i; rows NQ..15 are zero
     h8v aq[4];
@@ -194,6 +198,23 @@ __device__ void window_partial(const KParams &P, const uint16_t *__restrict__ q,
         if (r < NQ) raw = *(const uint4 *)(q + ((size_t)b * P.Hq + hq0 + r) * D + 32 * kc + 8 * g);
         aq[kc] = __builtin_bit_cast(h8v, raw);
     }
+    // the fp16 keys of tile nt (token t0 + 16 nt + r, channels 32 kc + 8 g
+    // ..; zero where the token has none), all four tiles loaded before the
+    // first product
+    auto load_kf16 = [&](int nt, uint4 (&k)[4]) {
+        const int tt = 16 * nt + r, t = t0 + tt;
+#pragma unroll
+        for (int kc = 0; kc < 4; kc++) k[kc] = make_uint4(0u, 0u, 0u, 0u);
+        if (tt < n && (wit || sinkc || t >= nkq)) {
+            const uint4 *kr = sinkc ? (const uint4 *)(P.sink_k + (bh * S + (size_t)t) * D)
+                                    : (const uint4 *)(P.res_k + (bh * win + (size_t)(t - nkq)) * D);
+#pragma unroll
+            for (int kc = 0; kc < 4; kc++) k[kc] = kr[4 * kc + g];
+        }
+    };
+    uint4 kf16[4][4];
+#pragma unroll
+    for (int nt = 0; nt < 4; nt++) load_kf16(nt, kf16[nt]);
     int pids[2] = {-1, -1};
     if (anyq) {
         pids[0] = __builtin_amdgcn_readlane(pid_l, 0);
@@ -225,15 +246,15 @@ __device__ void window_partial(const KParams &P, const uint16_t *__restrict__ q,
         uint4 bh4[4], bl4[4];
 #pragma unroll
         for (int kc = 0; kc < 4; kc++) {
-            bh4[kc] = make_uint4(0u, 0u, 0u, 0u);
+            bh4[kc] = kf16[0][kc];                // fp16 key (zero where none): exact in the operand
             bl4[kc] = make_uint4(0u, 0u, 0u, 0u);
         }
-        if (tt < n) {
-            if (wit || sinkc || t >= nkq) {       // fp16 key: exact in the operand
-                const uint4 *kr = sinkc ? (const uint4 *)(P.sink_k + (bh * S + (size_t)t) * D)
-                                        : (const uint4 *)(P.res_k + (bh * win + (size_t)(t - nkq)) * D);
 #pragma unroll
-                for (int kc = 0; kc < 4; kc++) bh4[kc] = kr[4 * kc + g];
+        for (int u = 0; u < 3; u++)               // the next tiles move down
+#pragma unroll
+            for (int kc = 0; kc < 4; kc++) kf16[u][kc] = kf16[u + 1][kc];
+        if (tt < n) {
+            if (wit || sinkc || t >= nkq) {
             } else {                              // quantized key: fl32(code s + z), split hi + lo
                 const int pi = (t - S) / PT - pA, tp = (t - S) % PT, gi = tp >> 5, n16 = tp >> 4;
                 const uint8_t *pg = cpage(P, pi ? pids[1] : pids[0], h);
@@ -293,6 +314,8 @@ __device__ void window_partial(const KParams &P, const uint16_t *__restrict__ q,
     }
     lds_sync();
 
+    if (two && n > VPF) load_v(VPF, vv2);      // uniform
+
     // ---- softmax over the chunk, lane = token (log2 units) ----
     float zq[8];
     {
@@ -326,14 +349,12 @@ __device__ void window_partial(const KParams &P, const uint16_t *__restrict__ q,
     float acc[NQ][2];
 #pragma unroll
     for (int j = 0; j < NQ; j++) acc[j][0] = acc[j][1] = 0.f;
-#pragma unroll 1
-    for (int tt0 = 0; tt0 < n; tt0 += VPF) {
-        if (tt0 > 0) load_v(tt0);
+    auto pv_batch = [&](const uint32_t *v, int tt0) {
 #pragma unroll
         for (int u = 0; u < VPF; u++) {
             const int tt = tt0 + u;
             if (tt < n) {
-                const float v0 = half_lo(vv[u]), v1 = half_hi(vv[u]);
+                const float v0 = half_lo(v[u]), v1 = half_hi(v[u]);
                 const float4 pa = ws.pT[tt][0];
                 float pq[8] = {pa.x, pa.y, pa.z, pa.w, 0.f, 0.f, 0.f, 0.f};
                 if (NQ > 4) {
@@ -346,6 +367,16 @@ __device__ void window_partial(const KParams &P, const uint16_t *__restrict__ q,
                     acc[j][1] = fmaf(pq[j], v1, acc[j][1]);
                 }
             }
+        }
+    };
+    if (two) {
+        pv_batch(vv, 0);
+        if (n > VPF) pv_batch(vv2, VPF);
+    } else {
+#pragma unroll 1
+        for (int tt0 = 0; tt0 < n; tt0 += VPF) {
+            if (tt0 > 0) load_v(tt0, vv);
+            pv_batch(vv, tt0);
         }
     }
 
@@ -360,9 +391,9 @@ __device__ void window_partial(const KParams &P, const uint16_t *__restrict__ q,
 }
 
 // Work item of a stage-1 workgroup.  The grid has max_splits + n_win items
-// per (head, request); the first heads x requests x n_win items of the
-// dispatch order are the window chunks, so that these start first and
-// overlap the paged splits instead of trailing them.
+// per (head, request): the paged splits of every (head, request) first in the
+// dispatch order, then the window chunks, which are shorter and fill the
+// compute units as the splits drain.
 struct S1Item {
     bool window;
     int s, hd, b;        // s: paged split, or window chunk for a window item
@@ -371,19 +402,19 @@ struct S1Item {
 __device__ inline S1Item s1_item(int max_splits, int n_win) {
     const int nh = gridDim.y, nb = gridDim.z;
     const int L = blockIdx.x + gridDim.x * (blockIdx.y + nh * blockIdx.z);
-    const int nw = nh * nb * n_win;
+    const int npg = nh * nb * max_splits;
     S1Item it;
-    if (L < nw) {
+    if (L >= npg) {
+        const int L2 = L - npg;
         it.window = true;
-        it.s = L % n_win;
-        const int rest = L / n_win;
+        it.s = L2 % n_win;
+        const int rest = L2 / n_win;
         it.hd = rest % nh;
         it.b = rest / nh;
     } else {
-        const int L2 = L - nw;
         it.window = false;
-        it.s = L2 % max_splits;
-        const int rest = L2 / max_splits;
+        it.s = L % max_splits;
+        const int rest = L / max_splits;
         it.hd = rest % nh;
         it.b = rest / nh;
     }
@@ -1231,21 +1262,24 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(3, 8))) void
         Gqa4Smem pg;
         WinSmem win;
     } U;
-    // the window chunks come first in the grid; then the paged splits, in the
-    // order of the work list (longest first), and workgroups past its end exit
+    // the paged splits first, in the order of the work list (longest first;
+    // workgroups past its end exit), then the window chunks: shorter than the
+    // body and tail splits, they fill the compute units as the list drains
     const int L = blockIdx.x + gridDim.x * (blockIdx.y + gridDim.y * blockIdx.z);
     const int nw = gridDim.y * gridDim.z * W.n_win;
-    if (L < nw) {                                // the KV head's fp16 window
-        const S1Item it = s1_item(W.max_splits, W.n_win);
-        window_partial<QPK, PT, KVQ_SCHEME_KIVI2>(P, q, W, qscale, it.b, it.hd, QPK * it.hd, it.s, lane, U.win);
+    const int Lw = L - (int)(gridDim.x * gridDim.y * gridDim.z) + nw;
+    if (Lw >= 0) {                               // the KV head's fp16 window
+        const int wc = Lw % W.n_win, rest = Lw / W.n_win;
+        const int hd = rest % (int)gridDim.y, bb = rest / (int)gridDim.y;
+        window_partial<QPK, PT / 2, KVQ_SCHEME_KIVI2>(P, q, W, qscale, bb, hd, QPK * hd, wc, lane, U.win);
         return;
     }
-    // the item is read together with the list length (the grid never passes
-    // the list's capacity, so the read is in bounds either way)
-    const uint4 item = W.items[L - nw];
+    // the item is read together with the list length (the grid's paged part
+    // is the list's capacity, so the read is in bounds either way)
+    const uint4 item = W.items[L];
     const int n_items = (int)*W.n_items;
     asm volatile("" ::"s"(item.x), "s"(n_items));
-    if (L - nw >= n_items) return;
+    if (L >= n_items) return;
     const int pair = (int)(item.x / (uint32_t)NQ4), quad = (int)(item.x % (uint32_t)NQ4);
     const int b = pair / P.Hkv, h = pair % P.Hkv;
     const int hq0 = h * QPK + 4 * quad;               // the quad's first query head
