@@ -178,17 +178,22 @@ int kvq_set_layout(kvq_cache_t *cache, const kvq_layout_t *layout, const kvq_buf
     int sp = layout->split_pages;
     if (sp == 0) {
         // default: one 256-token block per split for WITCERT; 4 pages for
-        // short caches (more splits to fill the chip), 12 for longer ones
-        // (fewer partials to merge); for the GQA kernel, whose splits run
-        // from a work list with a tail of quarter-length splits, bodies of
-        // 8 pages for short caches and 32 for longer ones; at least what
+        // the shortest caches (more splits to fill the chip), 8 up to 128
+        // pages and 32 for longer ones (fewer splits to start and merge, the
+        // window chunks filling the chip as the splits drain) -- 12 for
+        // KIVI4, whose longer splits' binary32 sums lose accuracy against the
+        // zero-point term at the 1e-5 bound; for the GQA kernel, whose splits
+        // run from a work list with a tail of quarter-length splits, bodies
+        // of 8 pages for short caches and 48 for longer ones; at least what
         // keeps <= 256 splits
         const bool g4 = gqa4(*layout);
         sp = layout->scheme == KVQ_SCHEME_WITCERT ? 1
              : wtok                                 ? 4      // 256 tokens, as one WITCERT block
-             : g4                                   ? (layout->max_pages <= 128 ? 8 : 32)
-             : layout->max_pages <= 128             ? 4
-                                                    : 12;
+             : g4                                   ? (layout->max_pages <= 128 ? 8 : 48)
+             : layout->max_pages <= 32              ? 4
+             : layout->max_pages <= 128             ? 8
+             : layout->scheme == KVQ_SCHEME_KIVI4   ? 12
+                                                    : 32;
         while (sp < 64 && splits_for(*layout, sp) > kvq::MAX_SPLITS) sp++;
     }
     // the merge takes at most MAX_SPLITS splits per query head

@@ -156,13 +156,14 @@ typedef struct kvq_layout {
     int32_t split_pages;     /* stage-1 split size in pages; 0: the default.
                                 KIVI2 with 2, 4 or 8 query heads per KV head
                                 (the group kernel): body splits of 8 pages when
-                                max_pages <= 128, else 32, each request's last
+                                max_pages <= 128, else 48, each request's last
                                 pages in tail splits of a quarter of that
                                 (see kvq_decode_attention).  Others: 4 when
-                                max_pages <= 128, else 12 (1 for WITCERT, 4 for
-                                WITCERT_PAGED).  Raised where a request of
-                                max_pages pages would need more than 256
-                                splits */
+                                max_pages <= 32, 8 when max_pages <= 128, else
+                                32 (12 for KIVI4; 1 for WITCERT, 4 for
+                                WITCERT_PAGED).
+                                Raised where a request of max_pages pages would
+                                need more than 256 splits */
     int32_t flags;           /* KVQ_FLAG_* */
     uint32_t layer;          /* WITCERT(_PAGED) dither counter field; < 65536 */
     uint64_t seed;           /* WITCERT(_PAGED) dither key */

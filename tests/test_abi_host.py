@@ -271,16 +271,16 @@ def test_null_and_alignment(K):
 
 
 def test_split_resolution_and_workspace(K):
-    # default split: 4 pages up to 128 pages of cache, above that 12 (1 for
-    # WITCERT's 256-token pages); for the KIVI2 group-of-4 kernel bodies of 8
-    # and 32 pages with quarter-length tail splits; raised to what keeps at
-    # most 256 splits
-    cases = (("kivi2", 8, 100, 8), ("kivi2", 8, 128, 8), ("kitty", 8, 129, 12),
-             ("kivi2", 8, 129, 32), ("kivi2", 8, 512, 32), ("kivi2", 8, 4096, 32),
-             ("kivi2", 8, 8000, 33), ("kivi2", 8, 15807, 64),
-             ("kivi2", 2, 129, 12), ("kivi2", 2, 512, 12), ("kivi2", 2, 3072, 12),
-             ("kivi2", 2, 3073, 13), ("kivi2", 4, 512, 32), ("kivi2", 16, 512, 32),
-             ("kivi2", 6, 512, 12), ("kivi4", 8, 512, 12),
+    # default split: 4 pages up to 32 pages of cache, 8 up to 128, above that
+    # 32 (12 for KIVI4; 1 for WITCERT's 256-token pages); for the KIVI2 group kernel bodies
+    # of 8 and 48 pages with quarter-length tail splits; raised to what keeps
+    # at most 256 splits
+    cases = (("kivi2", 8, 100, 8), ("kivi2", 8, 128, 8), ("kitty", 8, 32, 4), ("kitty", 8, 33, 8),
+             ("kitty", 8, 129, 32), ("kivi2", 8, 129, 48), ("kivi2", 8, 512, 48), ("kivi2", 8, 4096, 48),
+             ("kivi2", 8, 8000, 48), ("kivi2", 8, 15807, 64),
+             ("kivi2", 2, 16, 4), ("kivi2", 2, 100, 8), ("kivi2", 2, 129, 32), ("kivi2", 2, 512, 32),
+             ("kivi2", 2, 8192, 32), ("kivi2", 2, 8193, 33), ("kivi2", 4, 512, 48), ("kivi2", 16, 512, 48),
+             ("kivi2", 6, 512, 32), ("kivi4", 8, 512, 12), ("kivi4", 8, 100, 8),
              ("witcert", 8, 64, 1), ("witcert", 8, 1024, 4))
     for scheme, Hq, max_pages, want in cases:
         L = K.make_layout(scheme, B=2, Hq=Hq, Hkv=2, max_pages=max_pages, n_pages=max_pages)
@@ -298,9 +298,9 @@ def test_split_resolution_and_workspace(K):
     # past what 256 group-of-4 splits of 64-page bodies and their tails hold
     L = K.make_layout("kivi2", B=2, Hq=8, Hkv=2, max_pages=15808, n_pages=8)
     assert set_layout(K, L)[0] == K.KVQ_EINVAL
-    # the VALU stage 1 keeps 12
+    # the VALU stage 1 takes the one-query-head kernel's default
     L = K.make_layout("kivi2", B=2, Hq=8, Hkv=2, max_pages=512, n_pages=512, flags=K.FLAG_GENERIC_STAGE1)
-    assert set_layout(K, L)[1].split_pages == 12
+    assert set_layout(K, L)[1].split_pages == 32
     L = K.make_layout("kivi2", B=1, Hq=1, Hkv=1, max_pages=16385, n_pages=8)
     assert set_layout(K, L)[0] == K.KVQ_EINVAL          # would need splits of 128 pages
     L = K.make_layout("kivi2", B=1, Hq=1, Hkv=1, max_pages=100, n_pages=8, split_pages=3)
