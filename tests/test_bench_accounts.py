@@ -64,14 +64,18 @@ def test_kivi_window_terms_by_hand():
                            + (l - 32 - n_vq) * 256 + 32 * 512)
 
 
-def _stage1_mean(w, warmup=5, steps=50):
+def _stage1_mean(w, warmup=5, steps=50, every=4):
+    # the mean over the timed steps whose stage-1 launch the HIP events
+    # bracket (every `every`-th, bench.event_steps), as the bench line records
+    sampled = set(bench.event_steps(steps, every))
     states = [bench.state_after_prefill(w, l) for l in w.ctx]
     for _ in range(warmup):
         _, _, states = bench.step_bytes(w, states)
     s1 = []
-    for _ in range(steps):
+    for j in range(steps):
         _, b, states = bench.step_bytes(w, states)
-        s1.append(b)
+        if j in sampled:
+            s1.append(b)
     return int(np.mean(s1))
 
 
