@@ -1425,16 +1425,15 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(3, 8))) void
 //     fragment keeping the nibble half of that tile and zeroing the other.
 //   P.V, transposed: A = value codes (channel rows, token k), B column
 //     (part, j) = hi (part 0) or lo (part 1) of p_t s_{t,j}, columns 8..15
-//     zero; lane = token forms its four products and stores them as f16 rows
-//     [part][group][token] in LDS.  Channel tile nt keeps column nt/2 (hi)
-//     and 4 + nt/2 (lo).
+//     zero; lane = token forms its four products and stores them token-major
+//     in LDS, one 16-byte write a page; the fragments are read back
+//     column-major by transposing reads.  Channel tile nt keeps column nt/2
+//     (hi) and 4 + nt/2 (lo).
 // ---------------------------------------------------------------------------
-constexpr int BS_STRIDE = 72;       // f16 per P.V operand row (64 tokens + bank skew)
-
 struct HeadSmem {
     h8v As[2][3][AS_STRIDE];        // score A: [key group][row 0 hi, 1 lo, 2 zero][channel octet]
-    _Float16 Bs[2][4][BS_STRIDE];   // P.V B: [hi, lo][value group][token]
-    h8v Bz;                         // zero fragment for B columns 8..15
+    uint32_t Bt[PT][BT_DW];         // P.V B: [token][column pair]: dwords 0..3 the hi and lo
+                                    // halves of the four groups, 4..7 zero (columns 8..15)
     float zsh[PT];                  // scores, hi + lo rows [token]
     int inv[NB_MAX];                // Kitty: boosted offset -> channel
 };
@@ -1503,13 +1502,12 @@ void stage1_head_mfma_kernel(KParams P, const uint16_t *__restrict__ q, Workspac
         if (lane == 0) atomicOr(P.status, (uint32_t)KVQ_STATUS_UNMAPPED_PAGE);
         pid_l = bad ? 0 : pid_l;                 // read page 0 instead; the result is flagged
     }
-    const float qp[4] = {lo16f(qraw.x), hi16f(qraw.x), lo16f(qraw.y), hi16f(qraw.y)};
 
     if (lane < 16) {
         sm.As[0][2][lane] = h8v{0, 0, 0, 0, 0, 0, 0, 0};
         sm.As[1][2][lane] = h8v{0, 0, 0, 0, 0, 0, 0, 0};
     }
-    if (lane == 0) sm.Bz = h8v{0, 0, 0, 0, 0, 0, 0, 0};
+    *(uint4 *)&sm.Bt[lane][4] = make_uint4(0u, 0u, 0u, 0u);     // columns 8..15 stay zero
     int kc_off[8] = {0, 0, 0, 0, 0, 0, 0, 0};    // Kitty: channels of offsets 16q + 4g + i
     const int planes = P.nb >> 4;                // Kitty high planes: 1 (16 boosted) or 2 (32)
     if (KITTY && !DYN) {
@@ -1527,10 +1525,10 @@ void stage1_head_mfma_kernel(KParams P, const uint16_t *__restrict__ q, Workspac
     // operand roles
     const int gi_p = lane >> 5;                  // key group of this lane's products
     const int arow = r < 2 ? r : 2;              // score A row read by this lane
-    const _Float16 *bsrc[2];                     // P.V B fragment of this lane, per 32-token step
-#pragma unroll
-    for (int ks = 0; ks < 2; ks++)
-        bsrc[ks] = r < 8 ? &sm.Bs[r >> 2][r & 3][32 * ks + 8 * g] : (const _Float16 *)&sm.Bz;
+    // P.V B fragment of this lane (column r, tokens 32 ks + 8 g .. + 7): lane
+    // r of its 16-lane group addresses token row 32 ks + 8 g + (r >> 2) (+ 4),
+    // columns 4 (r & 3) .. + 3, and the transposing read hands it column r
+    const uint32_t *bsrc = &sm.Bt[8 * g + (r >> 2)][2 * (r & 3)];
 
     float m = -INFINITY, lsum = 0.f;             // lsum: this lane's tokens
     float zacc[4] = {0.f, 0.f, 0.f, 0.f};        // sum_t p_t z_{t,j}, this lane's tokens
@@ -1545,14 +1543,18 @@ void stage1_head_mfma_kernel(KParams P, const uint16_t *__restrict__ q, Workspac
         // ---- score operand: four products of this lane, hi and lo ----
         float bias;
         {
-            const uint32_t sz[4] = {R.ks.x, R.ks.y, R.ks.z, R.ks.w};
+            // the channel pairs' scales and zero points, packed
+            const uint32_t s01 = __builtin_amdgcn_perm(R.ks.y, R.ks.x, 0x05040100u);
+            const uint32_t s23 = __builtin_amdgcn_perm(R.ks.w, R.ks.z, 0x05040100u);
+            const uint32_t z01 = __builtin_amdgcn_perm(R.ks.y, R.ks.x, 0x07060302u);
+            const uint32_t z23 = __builtin_amdgcn_perm(R.ks.w, R.ks.z, 0x07060302u);
             uint32_t hv[2], lv[2];
-            mul_split2(qp[0], lo16h(sz[0]), qp[1], lo16h(sz[1]), hv[0], lv[0]);
-            mul_split2(qp[2], lo16h(sz[2]), qp[3], lo16h(sz[3]), hv[1], lv[1]);
-            bias = qp[0] * (float)hi16h(sz[0]);
-            bias = fmaf(qp[1], (float)hi16h(sz[1]), bias);
-            bias = fmaf(qp[2], (float)hi16h(sz[2]), bias);
-            bias = fmaf(qp[3], (float)hi16h(sz[3]), bias);
+            split_qs_pk(qraw.x, s01, hv[0], lv[0]);
+            split_qs_pk(qraw.y, s23, hv[1], lv[1]);
+            bias = __builtin_amdgcn_fdot2(__builtin_bit_cast(h2v, qraw.y), __builtin_bit_cast(h2v, z23),
+                                          __builtin_amdgcn_fdot2(__builtin_bit_cast(h2v, qraw.x),
+                                                                 __builtin_bit_cast(h2v, z01), 0.0f, false),
+                                          false);
             ((uint2 *)&sm.As[gi_p][0][0])[lane & 31] = make_uint2(hv[0], hv[1]);
             ((uint2 *)&sm.As[gi_p][1][0])[lane & 31] = make_uint2(lv[0], lv[1]);
         }
@@ -1648,14 +1650,8 @@ void stage1_head_mfma_kernel(KParams P, const uint16_t *__restrict__ q, Workspac
             uint32_t hv[2], lv[2];
             mul_split2(pt, lo16h(vw[0]), pt, lo16h(vw[1]), hv[0], lv[0]);
             mul_split2(pt, lo16h(vw[2]), pt, lo16h(vw[3]), hv[1], lv[1]);
-            sm.Bs[0][0][lane] = lo16h(hv[0]);
-            sm.Bs[0][1][lane] = hi16h(hv[0]);
-            sm.Bs[0][2][lane] = lo16h(hv[1]);
-            sm.Bs[0][3][lane] = hi16h(hv[1]);
-            sm.Bs[1][0][lane] = lo16h(lv[0]);
-            sm.Bs[1][1][lane] = hi16h(lv[0]);
-            sm.Bs[1][2][lane] = lo16h(lv[1]);
-            sm.Bs[1][3][lane] = hi16h(lv[1]);
+            // columns 0..3: hi of groups 0..3, 4..7: lo
+            *(uint4 *)&sm.Bt[lane][0] = make_uint4(hv[0], hv[1], lv[0], lv[1]);
         }
         lds_sync();
 
@@ -1666,7 +1662,9 @@ void stage1_head_mfma_kernel(KParams P, const uint16_t *__restrict__ q, Workspac
                                  HP.v2.x, HP.v2.y, HP.v2.z, HP.v2.w, HP.v3.x, HP.v3.y, HP.v3.z, HP.v3.w};
 #pragma unroll
         for (int ks = 0; ks < 2; ks++) {
-            const h8v bfr = *(const h8v *)bsrc[ks];
+            const uint32_t *rp = bsrc + 32 * ks * BT_DW;
+            const h4v b0 = lds_tr16(rp), b1 = lds_tr16(rp + 4 * BT_DW);
+            const h8v bfr = __builtin_shufflevector(b0, b1, 0, 1, 2, 3, 4, 5, 6, 7);
 #pragma unroll
             for (int nt = 0; nt < 8; nt++) {
                 const uint32_t x = vd[nt];
@@ -1713,20 +1711,28 @@ void stage1_head_mfma_kernel(KParams P, const uint16_t *__restrict__ q, Workspac
     }
 
     // ---- reduce and write the split's partial ----
+    // sums over the wave: DPP within each row, then lane ^ 16 (swizzle) and
+    // lane ^ 32 (permute)
+    const int x32 = (lane ^ 32) << 2;
+    auto wave_sum = [&](float v) {
+        v += dppf<0xB1>(v);                          // quad_perm [1,0,3,2]
+        v += dppf<0x4E>(v);                          // quad_perm [2,3,0,1]
+        v += dppf<0x124>(v);                         // row_ror:4
+        v += dppf<0x128>(v);                         // row_ror:8
+        v += __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, v), 0x401F));
+        return v + __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(x32, __builtin_bit_cast(int, v)));
+    };
+    lsum = wave_sum(lsum);
 #pragma unroll
-    for (int msk = 1; msk < 64; msk <<= 1) lsum += shfl_xor(lsum, msk);
-#pragma unroll
-    for (int j = 0; j < 4; j++)
-#pragma unroll
-        for (int msk = 1; msk < 64; msk <<= 1) zacc[j] += shfl_xor(zacc[j], msk);
+    for (int j = 0; j < 4; j++) zacc[j] = wave_sum(zacc[j]);
     const float il = 1.0f / lsum;
     const size_t row = part_row(W, P.Hq, b, hq, s);
     bool nonfinite = !__builtin_isfinite(lsum);
 #pragma unroll
     for (int nt = 0; nt < 8; nt++) {
-        f4v lo;                                   // column 4 + j, four lanes up
+        f4v lo;                                   // column 4 + j, four lanes up (row_shl:4)
 #pragma unroll
-        for (int i = 0; i < 4; i++) lo[i] = __shfl_down(acc[nt][i], 4, 16);
+        for (int i = 0; i < 4; i++) lo[i] = dppf<0x104>(acc[nt][i]);
         const int jv = nt >> 1;
         if (r == jv) {
             const float zj = jv == 0 ? zacc[0] : jv == 1 ? zacc[1] : jv == 2 ? zacc[2] : zacc[3];
