@@ -1479,7 +1479,7 @@ void stage1_head_mfma_kernel(KParams P, const uint16_t *__restrict__ q, Workspac
         WinSmem win;
     } U;
     if (it.window) {                             // this query head's fp16 window
-        window_partial<1, 16, SCHEME>(P, q, W, qscale, b, h, hq, s, lane, U.win);
+        window_partial<1, PT / 2, SCHEME>(P, q, W, qscale, b, h, hq, s, lane, U.win);
         return;
     }
     HeadSmem &sm = U.pg;
