@@ -119,10 +119,10 @@ int splits_for(const kvq_layout_t &L, int sp) {
 int max_splits(const kvq_cache_t *C) { return splits_for(C->layout, C->split_pages); }
 
 // stage-1 work-list items the workspace holds: one per possible split of
-// every (request, KV head, query quad) of the group kernel
+// every (request, KV head) of the group kernel
 size_t list_items(const kvq_cache_t *C) {
     const kvq_layout_t &L = C->layout;
-    return (size_t)L.batch * L.n_kv_heads * kvq::gqa_quads(L.n_q_heads / L.n_kv_heads) * max_splits(C);
+    return (size_t)L.batch * L.n_kv_heads * max_splits(C);
 }
 
 // 64-token chunks of the fp16 window, each a stage-1 partial of its own
@@ -209,8 +209,8 @@ size_t kvq_workspace_bytes(const kvq_cache_t *cache) {
     // fp16 window
     const size_t rows =
         (size_t)cache->layout.batch * cache->layout.n_q_heads * (max_splits(cache) + n_win(cache));
-    // and the stage-1 work list: one item per (request, KV head, query quad,
-    // split), then its length (in the last 256 bytes)
+    // and the stage-1 work list: one item per (request, KV head, split), then
+    // its length (in the last 256 bytes)
     const size_t items = list_items(cache);
     return rows * kvq::D * sizeof(float) + rows * sizeof(float2) + items * sizeof(uint4) + 256;
 }

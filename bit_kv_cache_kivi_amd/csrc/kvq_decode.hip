@@ -725,8 +725,6 @@ __device__ inline h8v frag8(uint32_t m) {
     return __builtin_bit_cast(h8v, v);
 }
 
-__device__ inline float lo16f(uint32_t v) { return h2f((uint16_t)(v & 0xffffu)); }
-__device__ inline float hi16f(uint32_t v) { return h2f((uint16_t)(v >> 16)); }
 
 constexpr float LAZY_TAU = 8.0f;
 
@@ -800,19 +798,6 @@ __device__ inline _Float16 hi16h(uint32_t v) { return __builtin_bit_cast(_Float1
 struct PageRegs {
     uint4 ka, kb, va, vb, ks, vs;
 };
-
-__device__ inline PageRegs load_page_ext(const uint8_t *page, int extent, const Geom &G, int lane) {
-    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc((void *)page, (short)0, extent, 0x00020000);
-    const int o = 16 * lane;
-    PageRegs R;
-    R.ks = bload(rs, G.ks + o);
-    R.vs = bload(rs, G.vs + o);
-    R.ka = bload(rs, G.kc + o);
-    R.kb = bload(rs, G.kc + 1024 + o);
-    R.va = bload(rs, G.vc + o);
-    R.vb = bload(rs, G.vc + 1024 + o);
-    return R;
-}
 
 __device__ inline PageRegs load_page_masked(const uint8_t *page, bool valid, const Geom &G, int lane) {
     const __amdgpu_buffer_rsrc_t rs = page_rsrc(page, valid, G);
@@ -1101,9 +1086,10 @@ __device__ inline void gqa4_page(const Gqa4Page &R, Gqa4State &S, Gqa4Smem &sm, 
 // head) pair (gqa_splits), longest first -- the body splits of split_pages
 // pages and then the full tail splits, each in (request, KV head, split)
 // order, then the short last tail splits by length, longest first, each
-// length in pair order.  Workgroups are dispatched in list order and round
-// robin over the XCDs, so similar items sit side by side and the shortest run
-// last.  PLAN_G workgroups each compute every pair's place (one pass per
+// length in pair order.  (With two query quads per KV head, an item's
+// workgroup runs one wave per quad.)  Workgroups are dispatched in list order
+// and round robin over the XCDs, so similar items sit side by side and the
+// shortest run last.  PLAN_G workgroups each compute every pair's place (one pass per
 // PLAN_T pairs: wave-level prefix sums of the counts and of the short splits
 // per length, two barriers) and write the items of their own share of the
 // pairs: a pair's items are scattered 16-byte stores, which one compute unit
@@ -1126,9 +1112,8 @@ __device__ inline void wave_scan3(int (&v)[3], int lane) {
 }
 
 __global__ __launch_bounds__(PLAN_T) void plan_kernel(KParams P, Workspace W) {
-    // a unit is a (request, KV head, query quad); its pages are its pair's
-    const int nq4 = gqa_quads(P.qpk);
-    const int npair = P.B * P.Hkv * nq4, sp = P.split_pages, tp = gqa_tail_pages(sp);
+    // pairs (request, KV head), pair index b Hkv + h
+    const int npair = P.B * P.Hkv, sp = P.split_pages, tp = gqa_tail_pages(sp);
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     const int per = (npair + (int)gridDim.x - 1) / (int)gridDim.x;   // this workgroup's pairs
     const int pr0 = (int)blockIdx.x * per, pr1 = min(npair, pr0 + per);
@@ -1139,7 +1124,7 @@ __global__ __launch_bounds__(PLAN_T) void plan_kernel(KParams P, Workspace W) {
     __shared__ int base[2], blen[PLAN_L];  // region starts: body, full tail; short, by length
     // quantized values of a unit's pair, and its pages (capped by its
     // page-table row)
-    auto nvq_of = [&](int pr) { return max(0, P.state[(size_t)(pr / nq4) * 4] - P.sink - P.R); };
+    auto nvq_of = [&](int pr) { return max(0, P.state[(size_t)pr * 4] - P.sink - P.R); };
     auto pages_of = [&](int nvq) { return min((nvq + PT - 1) / PT, P.max_pages); };
     // a pass: the counts {body, full tail, short} of a pair of npg pages,
     // their exclusive prefix over the pairs so far in v, the rank of its
@@ -1247,21 +1232,25 @@ __global__ __launch_bounds__(PLAN_T) void plan_kernel(KParams P, Workspace W) {
             for (int k = 0; k < nt; k++) put(base[1] + v[1] + k, nb + k, nb * sp + k * tp, tp);
             if (rem) put(blen[rem] + srank, nb + nt, nb * sp + nt * tp, rem);
         }
-        advance();
+        if (c0 + PLAN_T < npair) advance();   // only a later pass reads the carries
     }
 }
 
+// A workgroup is one wave per query quad of the KV head: with two quads
+// (group of 8) the two waves read the same pages at the same time, so the
+// second read is served by the cache.
 template <int QPK>
-__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(3, 8))) void stage1_gqa4_mfma_kernel(KParams P, const uint16_t *__restrict__ q,
+__global__ __launch_bounds__(QPK == 8 ? 128 : 64) __attribute__((amdgpu_waves_per_eu(3, 8))) void stage1_gqa4_mfma_kernel(KParams P, const uint16_t *__restrict__ q,
                                                               Workspace W, float qscale) {
     constexpr int NQ4 = QPK >= 4 ? QPK / 4 : 1;        // query quads per KV head
     constexpr int NQV = QPK >= 4 ? 4 : QPK;            // queries of a quad that exist
-    const int lane = threadIdx.x, g = lane >> 4, r = lane & 15;
+    const int lane = threadIdx.x & 63, g = lane >> 4, r = lane & 15;
+    const int quad = NQ4 == 1 ? 0 : (int)(threadIdx.x >> 6);
     const Geom G = geom(P.scheme, P.nb);
     __shared__ union {
         Gqa4Smem pg;
         WinSmem win;
-    } U;
+    } U[NQ4];                                    // one per wave
     // the paged splits first, in the order of the work list (longest first;
     // workgroups past its end exit), then the window chunks: shorter than the
     // body and tail splits, they fill the compute units as the list drains
@@ -1271,7 +1260,8 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(3, 8))) void
     if (Lw >= 0) {                               // the KV head's fp16 window
         const int wc = Lw % W.n_win, rest = Lw / W.n_win;
         const int hd = rest % (int)gridDim.y, bb = rest / (int)gridDim.y;
-        window_partial<QPK, PT / 2, KVQ_SCHEME_KIVI2>(P, q, W, qscale, bb, hd, QPK * hd, wc, lane, U.win);
+        window_partial<QPK / NQ4, PT / 2, KVQ_SCHEME_KIVI2>(P, q, W, qscale, bb, hd, QPK * hd + 4 * quad, wc,
+                                                            lane, U[quad].win);
         return;
     }
     // the item is read together with the list length (the grid's paged part
@@ -1280,12 +1270,11 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(3, 8))) void
     const int n_items = (int)*W.n_items;
     asm volatile("" ::"s"(item.x), "s"(n_items));
     if (L >= n_items) return;
-    const int pair = (int)(item.x / (uint32_t)NQ4), quad = (int)(item.x % (uint32_t)NQ4);
-    const int b = pair / P.Hkv, h = pair % P.Hkv;
+    const int b = (int)item.x / P.Hkv, h = (int)item.x % P.Hkv;
     const int hq0 = h * QPK + 4 * quad;               // the quad's first query head
     const int s = (int)item.y, p0 = (int)item.z;           // partial row, first page
     const int np = item.w & 255, nv_last = (item.w >> 8) ? (int)(item.w >> 8) : PT;
-    Gqa4Smem &sm = U.pg;
+    Gqa4Smem &sm = U[quad].pg;
     // valid tokens of the split's page i (only the prefix's last page is short)
     auto nvalid = [&](int i) { return i == np - 1 ? nv_last : PT; };
 
@@ -1342,6 +1331,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(3, 8))) void
     Gqa4Page ra = page_ld(0);
     __builtin_amdgcn_sched_barrier(0);
     for (int i = 0; i < np; i += 2) {
+        if (NQ4 == 2) __builtin_amdgcn_s_barrier();   // the quads' waves stay a page pair apart at most
         Gqa4Page rb = page_ld(i + 1);
         __builtin_amdgcn_sched_barrier(0);
         run_page(ra, i);
@@ -2283,12 +2273,13 @@ hipError_t launch_decode(const KParams &P, const uint16_t *q, float *out, float 
             default: return hipErrorInvalidValue;
         }
     } else if (gqa4) {
-        // the window chunks, then room for every split of every query quad
-        dim3 g1(gqa_quads(P.qpk) * W.max_splits + W.n_win, P.Hkv, P.B);
+        // room for every split of every KV head, then the window chunks; a
+        // wave per query quad
+        dim3 g1(W.max_splits + W.n_win, P.Hkv, P.B);
         switch (P.qpk) {
             case 2: stage1_gqa4_mfma_kernel<2><<<g1, 64, 0, s>>>(P, q, W, qscale); break;
             case 4: stage1_gqa4_mfma_kernel<4><<<g1, 64, 0, s>>>(P, q, W, qscale); break;
-            case 8: stage1_gqa4_mfma_kernel<8><<<g1, 64, 0, s>>>(P, q, W, qscale); break;
+            case 8: stage1_gqa4_mfma_kernel<8><<<g1, 128, 0, s>>>(P, q, W, qscale); break;
             default: return hipErrorInvalidValue;
         }
     } else {

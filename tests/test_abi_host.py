@@ -56,11 +56,9 @@ def bufs(K, **over):
 def ws_bytes(B, Hq, Hkv, splits, n_win):
     """Workspace of kvq_decode_attention: a partial row (128 fp32 + {lse, A})
     per query head and split or window chunk, a stage-1 work-list item (16 B)
-    per (request, KV head, query quad, split), and 256 bytes for the list's
-    length."""
+    per (request, KV head, split), and 256 bytes for the list's length."""
     rows = B * Hq * (splits + n_win)
-    quads = max(1, (Hq // Hkv) // 4)
-    return rows * (128 * 4 + 8) + B * Hkv * quads * splits * 16 + 256
+    return rows * (128 * 4 + 8) + B * Hkv * splits * 16 + 256
 
 
 def gqa_splits(npg, sp):
