@@ -228,7 +228,8 @@ def event_steps(steps: int, every: int) -> list:
 
 
 def run_gpu(w: inputs.Workload, steps: int, warmup: int, split_pages: int, copies: int = 1,
-            settle_s: float = 0.06, latency_steps: int = 0, event_every: int = 4):
+            settle_s: float = 0.06, latency_steps: int = 0, event_every: int = 4,
+            floor_launches: int = 0):
     """copies > 1: that many independent caches of the workload, used in turn
     (step i on copy i mod copies), so that no cache stays resident in the
     memory-side cache between its steps (a cold-cache figure).
@@ -245,7 +246,12 @@ def run_gpu(w: inputs.Workload, steps: int, warmup: int, split_pages: int, copie
 
     latency_steps: after the timed steps, that many more steps one at a time,
     each bracketed by events on the stream and followed by a host
-    synchronisation (the latency of one whole step: flush, append, decode)."""
+    synchronisation (the latency of one whole step: flush, append, decode).
+
+    floor_launches: after the timed steps (group kernel only), that many
+    launches of its load-only copy (kvq_stage1_load_floor) on the state the
+    timed steps left, each bracketed by the same stage-1 events: the floor of
+    the group kernel's access pattern."""
     import torch
     from bit_kv_cache_kivi_amd import kvq
     n = steps + warmup + latency_steps
@@ -305,6 +311,23 @@ def run_gpu(w: inputs.Workload, steps: int, warmup: int, split_pages: int, copie
     if not torch.isfinite(out).all():
         raise RuntimeError("non-finite output")
     s1_ms = [ev1[j][0].elapsed_time(ev1[j][1]) for j in sampled]
+    floor_ms = []
+    if floor_launches:
+        fev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(floor_launches + 2)]
+        for a, b in fev:
+            a.record()
+            b.record()
+        torch.cuda.synchronize()
+        cache = caches[(warmup + steps - 1) % copies]
+        for a, b in fev:                    # the first two warm the copy up, untimed
+            kvq.kvq_set_stage1_events(cache.cache, a.cuda_event, b.cuda_event)
+            cache.stage1_load_floor(qs[0], sm_scale=w.sm_scale)
+        kvq.kvq_set_stage1_events(cache.cache, None, None)
+        torch.cuda.synchronize()
+        floor_ms = [a.elapsed_time(b) for a, b in fev[2:]]
+        if cache.status_word() != 0:
+            raise RuntimeError(f"device status {cache.status_word():#x}")
     lat = None
     if latency_steps:
         dev_us, host_us = [], []
@@ -328,7 +351,7 @@ def run_gpu(w: inputs.Workload, steps: int, warmup: int, split_pages: int, copie
                "host_us_median": round(float(np.median(host_us)), 2),
                "host_us_p90": round(float(np.percentile(host_us, 90)), 2)}
     del stream
-    return dt, s1_ms, settle, lat
+    return dt, s1_ms, settle, lat, floor_ms
 
 
 # ---------------------------------------------------------------------------
@@ -458,6 +481,9 @@ def main():
     ap.add_argument("--latency", type=int, default=-1,
                     help="steps timed one at a time after the timed loop (default: 200 for "
                          "workload 1, else 0)")
+    ap.add_argument("--floor-launches", type=int, default=8,
+                    help="launches of the group kernel's load-only copy after the timed steps "
+                         "(0: none)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--copy-calibration", action="store_true",
@@ -481,8 +507,10 @@ def main():
         f"{np.mean(w.ctx):.0f}, steps={args.steps} warmup={args.warmup}")
     copies = 2 if args.cold else 1
     lat_steps = args.latency if args.latency >= 0 else (200 if args.workload == 1 else 0)
-    dt, s1_ms, settle, lat = run_gpu(w, args.steps, args.warmup, args.split_pages, copies,
-                                     args.settle_ms * 1e-3, lat_steps, args.event_every)
+    group_kernel = w.scheme == "kivi2" and w.group in (2, 4, 8)
+    dt, s1_ms, settle, lat, floor_ms = run_gpu(w, args.steps, args.warmup, args.split_pages, copies,
+                                               args.settle_ms * 1e-3, lat_steps, args.event_every,
+                                               args.floor_launches if group_kernel else 0)
     sampled = set(event_steps(args.steps, args.event_every))
 
     # algorithmic bytes of the timed steps (step i advances copy i mod copies)
@@ -513,7 +541,7 @@ def main():
     s1_gbs = float(np.mean(s1_bytes)) / (s1_avg_ms * 1e-3) / 1e9
     kernel = ("stage1_witcert" if w.scheme == "witcert" else
               "stage1_witcert_paged" if w.scheme == "witcert_paged" else
-              "stage1_gqa4_mfma" if (w.scheme == "kivi2" and w.group in (2, 4, 8)) else "stage1_head_mfma")
+              "stage1_gqa4_mfma" if group_kernel else "stage1_head_mfma")
     if w.scheme in ("witcert", "witcert_paged"):
         # VALU bound: Philox4x32-10 calls (one per token, channel quad and
         # side of every quantized block) x the algorithmic VALU operations per
@@ -541,6 +569,11 @@ def main():
                 "timed_launches": len(s1_ms),
                 "median_launch_us": round(float(np.median(s1_ms)) * 1e3, 2),
                 "algorithmic_bytes_per_launch": int(np.mean(s1_bytes))}
+        if floor_ms:
+            # the same launch with the page step's arithmetic taken out
+            # (kvq_stage1_load_floor), on the state the timed steps left
+            roof["load_floor_us"] = round(float(np.mean(floor_ms)) * 1e3, 2)
+            roof["of_load_floor"] = round(float(np.mean(floor_ms)) / s1_avg_ms, 4)
     rec = {"metric": METRIC, "value": round(gbs, 1), "unit": "GB/s", "n_gpus": 1,
            "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
            "higher_is_better": True, "scaling": "weak", "vs_baseline": None,

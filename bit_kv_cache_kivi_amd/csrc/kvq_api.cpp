@@ -232,9 +232,9 @@ int kvq_flush_key_group(const kvq_cache_t *cache, hipStream_t stream) {
 }
 
 namespace {
-// kvq_decode_attention's launch once the workspace is known good
-int decode_with(const kvq_cache_t *cache, const uint16_t *q, float *out, float *cert,
-                float sm_scale, float kappa, void *workspace, hipStream_t stream) {
+// the workspace's parts (kvq_workspace_bytes' order): partial rows, their
+// log-sum-exps, the work list and its length
+kvq::Workspace workspace_of(const kvq_cache_t *cache, void *workspace) {
     kvq::Workspace W;
     W.max_splits = max_splits(cache);
     W.n_win = n_win(cache);
@@ -246,6 +246,13 @@ int decode_with(const kvq_cache_t *cache, const uint16_t *q, float *out, float *
     W.n_items = (uint32_t *)(W.items + items);
     W.ev_begin = cache->ev_stage1_begin;
     W.ev_end = cache->ev_stage1_end;
+    return W;
+}
+
+// kvq_decode_attention's launch once the workspace is known good
+int decode_with(const kvq_cache_t *cache, const uint16_t *q, float *out, float *cert,
+                float sm_scale, float kappa, void *workspace, hipStream_t stream) {
+    const kvq::Workspace W = workspace_of(cache, workspace);
     return kvq::launch_decode(params(cache), q, out, cert, sm_scale, kappa, W, stream) == hipSuccess
                ? KVQ_OK
                : KVQ_ELAUNCH;
@@ -268,6 +275,21 @@ int kvq_decode_attention(const kvq_cache_t *cache, const uint16_t *q, float *out
     if (!aligned(workspace, 256)) return KVQ_EALIGN;
     if (ws_bytes < kvq_workspace_bytes(cache)) return KVQ_EWORKSPACE;
     return decode_with(cache, q, out, cert, sm_scale, kappa, workspace, stream);
+}
+
+int kvq_stage1_load_floor(const kvq_cache_t *cache, const uint16_t *q, float sm_scale,
+                          void *workspace, size_t ws_bytes, hipStream_t stream) {
+    int rc = check_cache(cache);
+    if (rc != KVQ_OK) return rc;
+    const kvq_layout_t &L = cache->layout;
+    if (!kvq::gqa4_path(L.scheme, L.n_q_heads / L.n_kv_heads, (L.flags & KVQ_FLAG_GENERIC_STAGE1) != 0))
+        return KVQ_EINVAL;
+    if (!q || !workspace) return KVQ_ENULL;
+    if (!aligned(q, 16) || !aligned(workspace, 256)) return KVQ_EALIGN;
+    if (ws_bytes < kvq_workspace_bytes(cache)) return KVQ_EWORKSPACE;
+    const kvq::Workspace W = workspace_of(cache, workspace);
+    return kvq::launch_stage1_floor(params(cache), q, sm_scale, W, stream) == hipSuccess ? KVQ_OK
+                                                                                         : KVQ_ELAUNCH;
 }
 
 int kvq_decode_attention_noalloc(const kvq_cache_t *cache, const uint16_t *q, float *out,

@@ -1238,10 +1238,13 @@ __global__ __launch_bounds__(PLAN_T) void plan_kernel(KParams P, Workspace W) {
 
 // A workgroup is one wave per query quad of the KV head: with two quads
 // (group of 8) the two waves read the same pages at the same time, so the
-// second read is served by the cache.
-template <int QPK>
-__global__ __launch_bounds__(QPK == 8 ? 128 : 64) __attribute__((amdgpu_waves_per_eu(3, 8))) void stage1_gqa4_mfma_kernel(KParams P, const uint16_t *__restrict__ q,
-                                                              Workspace W, float qscale) {
+// second read is served by the cache.  FLOOR: the load-only copy behind
+// kvq_stage1_load_floor -- the same work list, page loads, window chunks and
+// partial writes, with each page's words folded into one register instead of
+// gqa4_page, at the same register budget (so the same waves per SIMD).
+template <int QPK, bool FLOOR>
+__device__ __forceinline__ void gqa4_stage1(KParams P, const uint16_t *__restrict__ q,
+                                            Workspace W, float qscale) {
     constexpr int NQ4 = QPK >= 4 ? QPK / 4 : 1;        // query quads per KV head
     constexpr int NQV = QPK >= 4 ? 4 : QPK;            // queries of a quad that exist
     const int lane = threadIdx.x & 63, g = lane >> 4, r = lane & 15;
@@ -1316,8 +1319,18 @@ __global__ __launch_bounds__(QPK == 8 ? 128 : 64) __attribute__((amdgpu_waves_pe
     // is in flight.  (A deeper ring costs the registers of a third wave per
     // SIMD, which hides more latency than a second page in flight.)  Loads
     // past the split's end are issued too, with an empty extent.
+    uint32_t fold = 0;                           // FLOOR: every loaded word, folded
     auto run_page = [&](const Gqa4Page &R, int i) {
-        gqa4_page(R, S, sm, qw, a1, a2, lane, nvalid(i), qscale);
+        if constexpr (FLOOR) {
+            const uint4 w[6] = {R.ka, R.kb, R.va, R.vb, R.ks, R.vs0};
+            const uint4 w2 = R.vs1;
+#pragma unroll
+            for (int k = 0; k < 6; k++) fold ^= w[k].x ^ w[k].y ^ w[k].z ^ w[k].w;
+            fold ^= w2.x ^ w2.y ^ w2.z ^ w2.w;
+            (void)i;
+        } else {
+            gqa4_page(R, S, sm, qw, a1, a2, lane, nvalid(i), qscale);
+        }
     };
     auto page_ld = [&](int i) {
         const uint8_t *pg = base + (size_t)__builtin_amdgcn_readlane(pid_l, min(i, np - 1)) * pstride;
@@ -1340,6 +1353,19 @@ __global__ __launch_bounds__(QPK == 8 ? 128 : 64) __attribute__((amdgpu_waves_pe
         if (i + 1 < np) run_page(rb, i + 1);
     }
 
+    if constexpr (FLOOR) {
+        // the partial rows' bytes: four output rows and log-sum-exps a split
+        asm volatile("" ::: "v165");             // the group kernel's register budget
+        const float v = __builtin_bit_cast(float, fold & 0x007fffffu);   // finite
+#pragma unroll
+        for (int k = 0; k < 2; k++) {
+            const int e = lane + 64 * k, hp = e >> 5, c4 = e & 31;
+            if (hp < NQV)
+                *(float4 *)(W.o + part_row(W, P.Hq, b, hq0 + hp, s) * D + 4 * c4) = make_float4(v, v, v, v);
+        }
+        if (lane < NQV) W.ml[part_row(W, P.Hq, b, hq0 + lane, s)] = make_float2(v, 1.0f);
+        return;
+    }
     // ---- reduce and write the split's partial ----
     // l and the zero-point sums of query a, a + 1: over the 32 lanes holding
     // them (lane bits 0..3 by DPP within the row, bit 5 by a permute), which
@@ -1399,6 +1425,18 @@ __global__ __launch_bounds__(QPK == 8 ? 128 : 64) __attribute__((amdgpu_waves_pe
         const size_t row_i = part_row(W, P.Hq, b, hq0 + lane, s);
         W.ml[row_i] = make_float2(mi + log2f(li), 1.0f);
     }
+}
+
+template <int QPK>
+__global__ __launch_bounds__(QPK == 8 ? 128 : 64) __attribute__((amdgpu_waves_per_eu(3, 8))) void stage1_gqa4_mfma_kernel(KParams P, const uint16_t *__restrict__ q,
+                                                              Workspace W, float qscale) {
+    gqa4_stage1<QPK, false>(P, q, W, qscale);
+}
+
+template <int QPK>
+__global__ __launch_bounds__(QPK == 8 ? 128 : 64) __attribute__((amdgpu_waves_per_eu(3, 8))) void stage1_gqa4_floor_kernel(KParams P, const uint16_t *__restrict__ q,
+                                                               Workspace W, float qscale) {
+    gqa4_stage1<QPK, true>(P, q, W, qscale);
 }
 
 // ---------------------------------------------------------------------------
@@ -2243,6 +2281,28 @@ hipError_t noalloc_scratch(void **ptr, size_t *bytes) {
     *ptr = p;
     *bytes = sizeof(scratch);
     return hipSuccess;
+}
+
+hipError_t launch_stage1_floor(const KParams &P, const uint16_t *q, float sm_scale, const Workspace &W,
+                              hipStream_t s) {
+    if (!gqa4_path(P.scheme, P.qpk, P.force_generic)) return hipErrorInvalidValue;
+    const float qscale = sm_scale * 1.4426950408889634f;
+    plan_kernel<<<PLAN_G, PLAN_T, 0, s>>>(P, W);
+    if (W.ev_begin) {
+        hipError_t e = hipEventRecord(W.ev_begin, s);
+        if (e != hipSuccess) return e;
+    }
+    dim3 g1(W.max_splits + W.n_win, P.Hkv, P.B);   // the group kernel's grid
+    switch (P.qpk) {
+        case 2: stage1_gqa4_floor_kernel<2><<<g1, 64, 0, s>>>(P, q, W, qscale); break;
+        case 4: stage1_gqa4_floor_kernel<4><<<g1, 64, 0, s>>>(P, q, W, qscale); break;
+        case 8: stage1_gqa4_floor_kernel<8><<<g1, 128, 0, s>>>(P, q, W, qscale); break;
+        default: return hipErrorInvalidValue;
+    }
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    if (W.ev_end) e = hipEventRecord(W.ev_end, s);
+    return e;
 }
 
 hipError_t launch_decode(const KParams &P, const uint16_t *q, float *out, float *cert,

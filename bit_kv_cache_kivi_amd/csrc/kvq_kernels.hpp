@@ -65,6 +65,12 @@ hipError_t launch_witcert_calibrate(const KParams &P, const uint16_t *calib, int
 hipError_t launch_decode(const KParams &P, const uint16_t *q, float *out, float *cert,
                          float sm_scale, float kappa, const Workspace &W, hipStream_t s);
 
+// The work-list plan and the group kernel's load-only stage 1
+// (kvq_stage1_load_floor); hipErrorInvalidValue for layouts that do not run
+// the group kernel.
+hipError_t launch_stage1_floor(const KParams &P, const uint16_t *q, float sm_scale, const Workspace &W,
+                               hipStream_t s);
+
 // Device address of the fixed scratch array of the current device (resolved
 // once per device with hipGetSymbolAddress); *bytes gets its size.
 hipError_t noalloc_scratch(void **ptr, size_t *bytes);

@@ -35,7 +35,7 @@ EXPORTS = ("kvq_set_layout", "kvq_append_token", "kvq_flush_key_group",
            "kvq_decode_attention", "kvq_decode_attention_noalloc", "kvq_page_bytes",
            "kvq_page_tokens", "kvq_bytes_per_token", "kvq_workspace_bytes", "kvq_prefill",
            "kvq_kitty_calibrate", "kvq_witcert_calibrate", "kvq_set_stage1_events",
-           "kvq_strerror")
+           "kvq_stage1_load_floor", "kvq_strerror")
 
 
 class kvq_layout_t(C.Structure):
@@ -77,6 +77,7 @@ def lib():
         L.kvq_flush_key_group.argtypes = [C.POINTER(kvq_cache_t), S]
         L.kvq_decode_attention.argtypes = [C.POINTER(kvq_cache_t), P, P, P, C.c_float,
                                            C.c_float, P, C.c_size_t, S]
+        L.kvq_stage1_load_floor.argtypes = [C.POINTER(kvq_cache_t), P, C.c_float, P, C.c_size_t, S]
         L.kvq_decode_attention_noalloc.argtypes = [C.POINTER(kvq_cache_t), P, P, P, C.c_float,
                                                    C.c_float, S]
         L.kvq_page_bytes.argtypes = [C.POINTER(kvq_layout_t)]
@@ -136,6 +137,12 @@ def kvq_decode_attention_noalloc(cache: kvq_cache_t, q_ptr: int, out_ptr: int,
                                  stream: int):
     _check(lib().kvq_decode_attention_noalloc(C.byref(cache), q_ptr, out_ptr, cert_ptr, sm_scale,
                                               kappa, stream), "kvq_decode_attention_noalloc")
+
+
+def kvq_stage1_load_floor(cache: kvq_cache_t, q_ptr: int, sm_scale: float, ws_ptr: int,
+                          ws_bytes: int, stream: int):
+    _check(lib().kvq_stage1_load_floor(C.byref(cache), q_ptr, sm_scale, ws_ptr, ws_bytes, stream),
+           "kvq_stage1_load_floor")
 
 
 def kvq_prefill(cache: kvq_cache_t, req0: int, n_req: int, k_ptr: int, v_ptr: int,
@@ -267,6 +274,13 @@ class KVCache:
         kvq_decode_attention_noalloc(self.cache, q.data_ptr(), out.data_ptr(),
                                      None if cert is None else cert.data_ptr(), sm_scale, kappa,
                                      self.stream())
+
+    def stage1_load_floor(self, q, sm_scale: float = 1.0 / 128 ** 0.5):
+        """The group kernel's load-only stage 1 on the current state (a
+        measurement aid): overwrites this cache's workspace, nothing else."""
+        assert q.dtype == self.torch.float16 and q.is_contiguous()
+        kvq_stage1_load_floor(self.cache, q.data_ptr(), sm_scale, self.workspace.data_ptr(),
+                              self.ws_bytes, self.stream())
 
     def prefill(self, req0: int, K, V, lengths):
         """K, V: fp16 [n_req][Hkv][ld][128] on the device; lengths int32 [n_req]."""

@@ -311,6 +311,23 @@ int kvq_decode_attention_noalloc(const kvq_cache_t *cache, const uint16_t *q, fl
                                  float *cert, float sm_scale, float kappa,
                                  hipStream_t stream);
 
+/* Measurement aid for the group kernel (KIVI2 with 2, 4 or 8 query heads per
+ * KV head, without KVQ_FLAG_GENERIC_STAGE1): the part of kvq_decode_attention
+ * before its merge -- the work-list plan, then stage 1 with the same grid,
+ * work list, page loads (descriptors, extents, the two-page ring, the
+ * non-temporal hint), register budget, window chunks and partial-row writes
+ * -- except that each page's loaded words are folded into one register
+ * instead of entering the attention arithmetic.  Its stage-1 time is the
+ * floor of the group kernel's access pattern on the current state.  It
+ * writes meaningless partials into the workspace and nothing else: no
+ * output, no merge, the cache unchanged.  The events of
+ * kvq_set_stage1_events bracket its stage 1 as they bracket the decode's.
+ * Returns KVQ_EINVAL for a layout that does not run the group kernel,
+ * KVQ_ENULL, KVQ_EALIGN (q 16-byte, workspace 256-byte aligned) and
+ * KVQ_EWORKSPACE as kvq_decode_attention. */
+int kvq_stage1_load_floor(const kvq_cache_t *cache, const uint16_t *q, float sm_scale,
+                          void *workspace, size_t ws_bytes, hipStream_t stream);
+
 /* ---- helpers ---------------------------------------------------------- */
 
 /* Bytes of one (page, KV head) block for a layout (0 if invalid). */

@@ -333,6 +333,41 @@ def test_decode_rejects_small_workspace_before_launching(K):
     assert rc == K.KVQ_EWORKSPACE
 
 
+def test_load_floor_host_checks_launch_nothing(K):
+    # kvq_stage1_load_floor runs only the group kernel's copy: every check
+    # that fails returns before any device call (these addresses are fake)
+    lib = K.lib()
+    a = A256 + 0x10000
+    q, ws = C.c_void_p(a), C.c_void_p(a + 0x100000)
+    one = C.c_float(1.0)
+    unset = K.kvq_cache_t()
+    assert lib.kvq_stage1_load_floor(C.byref(unset), q, one, ws, C.c_size_t(1 << 30),
+                                     None) == K.KVQ_ENOLAYOUT
+    # layouts that do not run the group kernel
+    for scheme, Hq, flags in (("kivi2", 2, 0), ("kivi2", 8, K.FLAG_GENERIC_STAGE1),
+                              ("kitty", 8, 0), ("kivi4", 8, 0), ("witcert", 8, 0)):
+        L = K.make_layout(scheme, B=2, Hq=Hq, Hkv=2, max_pages=64, n_pages=128)
+        L.flags = flags
+        rc, cache = set_layout(K, L)
+        assert rc == K.KVQ_OK, scheme
+        assert lib.kvq_stage1_load_floor(C.byref(cache), q, one, ws, C.c_size_t(1 << 30),
+                                         None) == K.KVQ_EINVAL, (scheme, Hq, flags)
+    L = K.make_layout("kivi2", B=2, Hq=8, Hkv=2, max_pages=64, n_pages=128)
+    rc, cache = set_layout(K, L)
+    assert rc == K.KVQ_OK
+    need = K.kvq_workspace_bytes(cache)
+    assert lib.kvq_stage1_load_floor(C.byref(cache), None, one, ws, C.c_size_t(need),
+                                     None) == K.KVQ_ENULL
+    assert lib.kvq_stage1_load_floor(C.byref(cache), q, one, None, C.c_size_t(need),
+                                     None) == K.KVQ_ENULL
+    assert lib.kvq_stage1_load_floor(C.byref(cache), C.c_void_p(a + 8), one, ws, C.c_size_t(need),
+                                     None) == K.KVQ_EALIGN
+    assert lib.kvq_stage1_load_floor(C.byref(cache), q, one, C.c_void_p(a + 0x100040),
+                                     C.c_size_t(need), None) == K.KVQ_EALIGN
+    assert lib.kvq_stage1_load_floor(C.byref(cache), q, one, ws, C.c_size_t(need - 1),
+                                     None) == K.KVQ_EWORKSPACE
+
+
 def test_error_strings(K):
     lib = K.lib()
     lib.kvq_strerror.restype = C.c_char_p
