@@ -845,10 +845,14 @@ constexpr int AS_STRIDE = 20;       // octets per score-operand row (16 + bank p
 // groups of the 64 banks.
 constexpr int BT_DW = 12;
 
+// NQW query quads served by one wave (two for a group of 8): each quad its
+// own score operand and P.V operand; the zero row is shared.
+template <int NQW>
 struct Gqa4Smem {
-    h8v As[2][8][AS_STRIDE];        // score A: [key group][row 2h = hi(q_h s), 2h + 1 = lo][channel octet]
+    static constexpr int BTW = BT_DW;   // dwords of a P.V operand row
+    h8v As[NQW][2][8][AS_STRIDE];   // score A: [quad][key group][row 2h = hi(q_h s), 2h + 1 = lo][channel octet]
     h8v Az[AS_STRIDE];              // a zero row (the other key group's operand rows)
-    uint32_t Bt[2][PT][BT_DW];      // P.V B: [operand][token][column pair (h, part, js)]
+    uint32_t Bt[NQW][2][PT][BTW];   // P.V B: [quad][operand][token][column pair (h, part, js)]
 };
 
 // Token of this lane's first softmax score (the second is 16 later): lane
@@ -878,8 +882,14 @@ __device__ inline Gqa4Page load_gqa4_page(const uint8_t *page, int extent, const
 // token 32 (G >> 1) + r in s[0] and of the token 16 later in s[1]: the
 // softmax runs in the products' own layout, two tokens by two queries a
 // lane, and every token of a lane is in key group G >> 1.
-__device__ inline void gqa4_page(const Gqa4Page &R, Gqa4State &S, Gqa4Smem &sm, const uint2 *qw,
-                                 const h8v *a1, const h8v *a2, int lane, int nvalid, float qscale) {
+//
+// With NQW = 2 quads a wave (a group of 8), every code fragment is converted
+// once and enters the products of both quads; the rest of the step is each
+// quad's own.
+template <int NQW>
+__device__ inline void gqa4_page(const Gqa4Page &R, Gqa4State (&S)[NQW], Gqa4Smem<NQW> &sm,
+                                 const uint2 (&qw)[NQW][4], const h8v *const (&a1)[NQW],
+                                 const h8v *const (&a2)[NQW], int lane, int nvalid, float qscale) {
     const int g = lane >> 4, r = lane & 15;
     const int hp = r >> 2;
     const uint32_t MSK = 0x33333333u;
@@ -888,30 +898,16 @@ __device__ inline void gqa4_page(const Gqa4Page &R, Gqa4State &S, Gqa4Smem &sm, 
 
     // ---- score operand from the lane's own key statistics (key group
     // lane >> 5, channels 4 (lane & 31) .. +3): hi/lo of q_h s_c for the four
-    // queries, and the zero-point sums, added over the group's 32 lanes ----
+    // queries of each quad, and the zero-point sums, added over the group's
+    // 32 lanes ----
     const int gi_p = lane >> 5;
     const uint32_t sz[4] = {R.ks.x, R.ks.y, R.ks.z, R.ks.w};
     // the channel pairs' scales and zero points, packed (one permute each,
-    // shared by the four queries)
+    // shared by the queries)
     const uint32_t s01 = __builtin_amdgcn_perm(sz[1], sz[0], 0x05040100u);
     const uint32_t s23 = __builtin_amdgcn_perm(sz[3], sz[2], 0x05040100u);
     const uint32_t z01 = __builtin_amdgcn_perm(sz[1], sz[0], 0x07060302u);
     const uint32_t z23 = __builtin_amdgcn_perm(sz[3], sz[2], 0x07060302u);
-    // bzp: this lane's share of sum_c q_h z_c per query, by two f16 dot
-    // products into a binary32 sum (each f16 x f16 product exact)
-    float bzp[4];
-#pragma unroll
-    for (int h = 0; h < 4; h++) {
-        uint32_t hv0, lv0, hv1, lv1;
-        split_qs_pk(qw[h].x, s01, hv0, lv0);
-        split_qs_pk(qw[h].y, s23, hv1, lv1);
-        ((uint2 *)&sm.As[gi_p][2 * h][0])[lane & 31] = make_uint2(hv0, hv1);
-        ((uint2 *)&sm.As[gi_p][2 * h + 1][0])[lane & 31] = make_uint2(lv0, lv1);
-        bzp[h] = __builtin_amdgcn_fdot2(__builtin_bit_cast(h2v, qw[h].y), __builtin_bit_cast(h2v, z23),
-                                        __builtin_amdgcn_fdot2(__builtin_bit_cast(h2v, qw[h].x),
-                                                               __builtin_bit_cast(h2v, z01), 0.0f, false),
-                                        false);
-    }
     // Sum the shares over the 32 lanes of the key group, reduce-scatter
     // style.  With f = (L & 1) ^ (L >> 4 & 1), the first quad exchange keeps
     // queries (0, 1) where f = 0 and (2, 3) where f = 1, the second keeps the
@@ -921,116 +917,149 @@ __device__ inline void gqa4_page(const Gqa4Page &R, Gqa4State &S, Gqa4Smem &sm, 
     // add the row's quads; the two rows of the group hold a query at quad
     // positions differing in bit 0, hence the exchange with lane ^ 17.
     const bool f = ((lane ^ (lane >> 4)) & 1) != 0, b1 = (lane & 2) != 0;
-    float k0 = f ? bzp[2] : bzp[0], k1 = f ? bzp[3] : bzp[1];
-    k0 += dppf<0xB1>(f ? bzp[0] : bzp[2]);             // quad_perm [1,0,3,2]
-    k1 += dppf<0xB1>(f ? bzp[1] : bzp[3]);
-    float kq = b1 ? k1 : k0;
-    kq += dppf<0x4E>(b1 ? k0 : k1);                    // quad_perm [2,3,0,1]
-    kq += dppf<0x124>(kq);                             // row_ror:4
-    kq += dppf<0x128>(kq);                             // row_ror:8
-    kq += __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, kq), 0x441F));  // lane ^ 17
-    kq *= qscale;
-    const float bias_a = dppf<0x00>(kq), bias_b = dppf<0xAA>(kq);
+    float bias_a[NQW], bias_b[NQW];
+#pragma unroll
+    for (int qd = 0; qd < NQW; qd++) {
+        // bzp: this lane's share of sum_c q_h z_c per query, by two f16 dot
+        // products into a binary32 sum (each f16 x f16 product exact)
+        float bzp[4];
+#pragma unroll
+        for (int h = 0; h < 4; h++) {
+            uint32_t hv0, lv0, hv1, lv1;
+            split_qs_pk(qw[qd][h].x, s01, hv0, lv0);
+            split_qs_pk(qw[qd][h].y, s23, hv1, lv1);
+            ((uint2 *)&sm.As[qd][gi_p][2 * h][0])[lane & 31] = make_uint2(hv0, hv1);
+            ((uint2 *)&sm.As[qd][gi_p][2 * h + 1][0])[lane & 31] = make_uint2(lv0, lv1);
+            bzp[h] = __builtin_amdgcn_fdot2(__builtin_bit_cast(h2v, qw[qd][h].y), __builtin_bit_cast(h2v, z23),
+                                            __builtin_amdgcn_fdot2(__builtin_bit_cast(h2v, qw[qd][h].x),
+                                                                   __builtin_bit_cast(h2v, z01), 0.0f, false),
+                                            false);
+        }
+        float k0 = f ? bzp[2] : bzp[0], k1 = f ? bzp[3] : bzp[1];
+        k0 += dppf<0xB1>(f ? bzp[0] : bzp[2]);             // quad_perm [1,0,3,2]
+        k1 += dppf<0xB1>(f ? bzp[1] : bzp[3]);
+        float kq = b1 ? k1 : k0;
+        kq += dppf<0x4E>(b1 ? k0 : k1);                    // quad_perm [2,3,0,1]
+        kq += dppf<0x124>(kq);                             // row_ror:4
+        kq += dppf<0x128>(kq);                             // row_ror:8
+        kq += __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, kq), 0x441F));  // lane ^ 17
+        kq *= qscale;
+        bias_a[qd] = dppf<0x00>(kq);
+        bias_b[qd] = dppf<0xAA>(kq);
+    }
     lds_sync();
 
     // ---- scores on the matrix cores ----
     const uint32_t kd[8] = {R.ka.x, R.ka.y, R.ka.z, R.ka.w, R.kb.x, R.kb.y, R.kb.z, R.kb.w};
     uint32_t kd2[8];                            // the same >> 2
     shr2_pairs(kd, kd2);
-    f4v sc[2] = {f4v{0.f, 0.f, 0.f, 0.f}, f4v{0.f, 0.f, 0.f, 0.f}};
+    f4v sc[NQW][2];
+#pragma unroll
+    for (int qd = 0; qd < NQW; qd++) sc[qd][0] = sc[qd][1] = f4v{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int kc = 0; kc < 4; kc++) {
-        const h8v af1 = a1[4 * kc + g], af2 = a2[4 * kc + g];
+        h8v af1[NQW], af2[NQW];
+#pragma unroll
+        for (int qd = 0; qd < NQW; qd++) {
+            af1[qd] = a1[qd][4 * kc + g];
+            af2[qd] = a2[qd][4 * kc + g];
+        }
         const uint32_t *kx = (kc & 1) ? kd2 : kd;
 #pragma unroll
         for (int n2 = 0; n2 < 2; n2++) {
             const h8v bf = frag8(kx[2 * n2 + (kc >> 1)] & MSK);
-            sc[n2] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af1, bf, sc[n2], 0, 0, 0);
+#pragma unroll
+            for (int qd = 0; qd < NQW; qd++)
+                sc[qd][n2] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af1[qd], bf, sc[qd][n2], 0, 0, 0);
         }
 #pragma unroll
         for (int n2 = 0; n2 < 2; n2++) {
             const h8v bf = frag8(kx[2 * (n2 + 2) + (kc >> 1)] & MSK);
-            sc[n2] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af2, bf, sc[n2], 0, 0, 0);
+#pragma unroll
+            for (int qd = 0; qd < NQW; qd++)
+                sc[qd][n2] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af2[qd], bf, sc[qd][n2], 0, 0, 0);
         }
     }
 
-    // ---- online softmax: tokens t0 and t0 + 16, queries a and a + 1 ----
-    float z[2][2];                              // [token][query a, a + 1], log2 units
-#pragma unroll
-    for (int j = 0; j < 2; j++) {
-        z[j][0] = fmaf(sc[j][0] + sc[j][1], qscale, bias_a);
-        z[j][1] = fmaf(sc[j][2] + sc[j][3], qscale, bias_b);
-    }
     const int t0 = gqa4_token(lane);
-    if (nvalid < PT) {                          // uniform: only the prefix's last page
 #pragma unroll
-        for (int j = 0; j < 2; j++)
-            if (t0 + 16 * j >= nvalid) z[j][0] = z[j][1] = -INFINITY;
-    }
-    // the exponents against the running maxima; a rescale only when one of
-    // them passes LAZY_TAU (-inf - -inf = NaN, where a first page's
-    // masked token meets a maximum not yet set, is passed over by fmaxf: the
-    // page's valid tokens give +inf)
-    float d[2][2];
-#pragma unroll
-    for (int j = 0; j < 2; j++) {
-        d[j][0] = z[j][0] - S.ma;
-        d[j][1] = z[j][1] - S.mb;
-    }
-    if (__any(fmaxf(fmaxf(d[0][0], d[1][0]), fmaxf(d[0][1], d[1][1])) > LAZY_TAU)) {
-        // the new maxima: over the 32 lanes holding each query (lane bits
-        // 0..3 and 5), then moved in every lane
-        float mt[2] = {fmaxf(z[0][0], z[1][0]), fmaxf(z[0][1], z[1][1])};
-#pragma unroll
-        for (int k = 0; k < 2; k++) {
-#pragma unroll
-            for (int msk = 1; msk < 16; msk <<= 1) mt[k] = fmaxf(mt[k], shfl_xor(mt[k], msk));
-            mt[k] = fmaxf(mt[k], shfl_xor(mt[k], 32));
-        }
-        float alpha[4];
-#pragma unroll
-        for (int i = 0; i < 4; i++) {
-            // query i lives in lanes 16 (i >> 1) + ..: slot i & 1 of lane 16 (i >> 1)
-            const float mi = __builtin_bit_cast(float, __builtin_amdgcn_readlane(
-                                 __builtin_bit_cast(int, mt[i & 1]), 16 * (i >> 1)));
-            const float mn = fmaxf(S.m[i], mi);
-            alpha[i] = __builtin_amdgcn_exp2f(S.m[i] - mn);
-            S.m[i] = mn;
-        }
-        const bool hi2 = (g & 1) != 0;
-        S.ma = hi2 ? S.m[2] : S.m[0];
-        S.mb = hi2 ? S.m[3] : S.m[1];
-        const float aa = hi2 ? alpha[2] : alpha[0], ab = hi2 ? alpha[3] : alpha[1];
-        S.la *= aa;
-        S.lb *= ab;
-#pragma unroll
-        for (int j = 0; j < 4; j++) {
-            S.za[j] *= aa;
-            S.zb[j] *= ab;
-        }
-        const float ap = hp == 0 ? alpha[0] : hp == 1 ? alpha[1] : hp == 2 ? alpha[2] : alpha[3];
-#pragma unroll
-        for (int nt = 0; nt < 8; nt++) S.acc[nt] *= ap;
+    for (int qd = 0; qd < NQW; qd++) {
+        Gqa4State &Sq = S[qd];
+        // ---- online softmax: tokens t0 and t0 + 16, queries a and a + 1 ----
+        float z[2][2];                          // [token][query a, a + 1], log2 units
 #pragma unroll
         for (int j = 0; j < 2; j++) {
-            d[j][0] = z[j][0] - S.ma;
-            d[j][1] = z[j][1] - S.mb;
+            z[j][0] = fmaf(sc[qd][j][0] + sc[qd][j][1], qscale, bias_a[qd]);
+            z[j][1] = fmaf(sc[qd][j][2] + sc[qd][j][3], qscale, bias_b[qd]);
         }
-    }
-    float p[2][2];                              // [token][query a, a + 1]
+        if (nvalid < PT) {                      // uniform: only the prefix's last page
 #pragma unroll
-    for (int j = 0; j < 2; j++) {
-        p[j][0] = __builtin_amdgcn_exp2f(d[j][0]);
-        p[j][1] = __builtin_amdgcn_exp2f(d[j][1]);
-    }
-    S.la += p[0][0] + p[1][0];
-    S.lb += p[0][1] + p[1][1];
+            for (int j = 0; j < 2; j++)
+                if (t0 + 16 * j >= nvalid) z[j][0] = z[j][1] = -INFINITY;
+        }
+        // the exponents against the running maxima; a rescale only when one
+        // of them passes LAZY_TAU (-inf - -inf = NaN, where a first page's
+        // masked token meets a maximum not yet set, is passed over by fmaxf:
+        // the page's valid tokens give +inf)
+        float d[2][2];
+#pragma unroll
+        for (int j = 0; j < 2; j++) {
+            d[j][0] = z[j][0] - Sq.ma;
+            d[j][1] = z[j][1] - Sq.mb;
+        }
+        if (__any(fmaxf(fmaxf(d[0][0], d[1][0]), fmaxf(d[0][1], d[1][1])) > LAZY_TAU)) {
+            // the new maxima: over the 32 lanes holding each query (lane bits
+            // 0..3 and 5), then moved in every lane
+            float mt[2] = {fmaxf(z[0][0], z[1][0]), fmaxf(z[0][1], z[1][1])};
+#pragma unroll
+            for (int k = 0; k < 2; k++) {
+#pragma unroll
+                for (int msk = 1; msk < 16; msk <<= 1) mt[k] = fmaxf(mt[k], shfl_xor(mt[k], msk));
+                mt[k] = fmaxf(mt[k], shfl_xor(mt[k], 32));
+            }
+            float alpha[4];
+#pragma unroll
+            for (int i = 0; i < 4; i++) {
+                // query i lives in lanes 16 (i >> 1) + ..: slot i & 1 of lane 16 (i >> 1)
+                const float mi = __builtin_bit_cast(float, __builtin_amdgcn_readlane(
+                                     __builtin_bit_cast(int, mt[i & 1]), 16 * (i >> 1)));
+                const float mn = fmaxf(Sq.m[i], mi);
+                alpha[i] = __builtin_amdgcn_exp2f(Sq.m[i] - mn);
+                Sq.m[i] = mn;
+            }
+            const bool hi2 = (g & 1) != 0;
+            Sq.ma = hi2 ? Sq.m[2] : Sq.m[0];
+            Sq.mb = hi2 ? Sq.m[3] : Sq.m[1];
+            const float aa = hi2 ? alpha[2] : alpha[0], ab = hi2 ? alpha[3] : alpha[1];
+            Sq.la *= aa;
+            Sq.lb *= ab;
+#pragma unroll
+            for (int j = 0; j < 4; j++) {
+                Sq.za[j] *= aa;
+                Sq.zb[j] *= ab;
+            }
+            const float ap = hp == 0 ? alpha[0] : hp == 1 ? alpha[1] : hp == 2 ? alpha[2] : alpha[3];
+#pragma unroll
+            for (int nt = 0; nt < 8; nt++) Sq.acc[nt] *= ap;
+#pragma unroll
+            for (int j = 0; j < 2; j++) {
+                d[j][0] = z[j][0] - Sq.ma;
+                d[j][1] = z[j][1] - Sq.mb;
+            }
+        }
+        float p[2][2];                          // [token][query a, a + 1]
+#pragma unroll
+        for (int j = 0; j < 2; j++) {
+            p[j][0] = __builtin_amdgcn_exp2f(d[j][0]);
+            p[j][1] = __builtin_amdgcn_exp2f(d[j][1]);
+        }
+        Sq.la += p[0][0] + p[1][0];
+        Sq.lb += p[0][1] + p[1][1];
 
-    // ---- P.V operand: p_{h,t} s_{t,j} split into f16 hi and lo, stored as
-    // the B columns (h, part, js) of operand j >> 1 (js = j & 1) at token t;
-    // sum_t p_{h,t} z_{t,j} on the side.  (Statistics of tokens past nvalid
-    // read as zeros: the page's extent.) ----
-    {
+        // ---- P.V operand: p_{h,t} s_{t,j} split into f16 hi and lo, stored
+        // as the B columns (h, part, js) of operand j >> 1 (js = j & 1) at
+        // token t; sum_t p_{h,t} z_{t,j} on the side.  (Statistics of tokens
+        // past nvalid read as zeros: the page's extent.) ----
         const int ha = 2 * (g & 1);
 #pragma unroll
         for (int j = 0; j < 2; j++) {
@@ -1041,7 +1070,7 @@ __device__ inline void gqa4_page(const Gqa4Page &R, Gqa4State &S, Gqa4Smem &sm, 
 #pragma unroll
             for (int k = 0; k < 2; k++) {
                 const float pk = p[j][k];
-                float *zk = k ? S.zb : S.za;
+                float *zk = k ? Sq.zb : Sq.za;
 #pragma unroll
                 for (int jv = 0; jv < 4; jv++) zk[jv] = fmaf(pk, (float)hi16h(vw[jv]), zk[jv]);
                 split_ps(pk, vw[0], vw[1], h01[k], l01[k]);
@@ -1049,15 +1078,15 @@ __device__ inline void gqa4_page(const Gqa4Page &R, Gqa4State &S, Gqa4Smem &sm, 
             }
             // columns 4 (ha + k) .. + 3 = (hi of groups 2o, 2o + 1, lo of
             // the same) for queries ha + k, k = 0, 1: dwords 2 ha .. + 3
-            *(uint4 *)&sm.Bt[0][t][2 * ha] = make_uint4(h01[0], l01[0], h01[1], l01[1]);
-            *(uint4 *)&sm.Bt[1][t][2 * ha] = make_uint4(h23[0], l23[0], h23[1], l23[1]);
+            *(uint4 *)&sm.Bt[qd][0][t][2 * ha] = make_uint4(h01[0], l01[0], h01[1], l01[1]);
+            *(uint4 *)&sm.Bt[qd][1][t][2 * ha] = make_uint4(h23[0], l23[0], h23[1], l23[1]);
         }
     }
     lds_sync();
 
     // ---- P.V on the matrix cores: channel tiles 0..3 (value groups 0, 1)
-    // take operand 0, tiles 4..7 (groups 2, 3) operand 1; one product per tile
-    // and 32-token step carries both halves of all four queries ----
+    // take operand 0, tiles 4..7 (groups 2, 3) operand 1; one product per tile,
+    // quad and 32-token step carries both halves of the quad's four queries ----
     const uint32_t vd[8] = {R.va.x, R.va.y, R.va.z, R.va.w, R.vb.x, R.vb.y, R.vb.z, R.vb.w};
     uint32_t vd2[8];                            // the same >> 2
     shr2_pairs(vd, vd2);
@@ -1069,14 +1098,20 @@ __device__ inline void gqa4_page(const Gqa4Page &R, Gqa4State &S, Gqa4Smem &sm, 
             // column r, tokens 32 ks + 8 g .. + 7: lane r of the 16-lane
             // group addresses token row 32 ks + 8 g + (r >> 2) (+ 4), columns
             // 4 (r & 3) .. + 3; the transposing read hands lane r column r
-            const uint32_t *rp = &sm.Bt[o][32 * ks + 8 * g + (r >> 2)][2 * (r & 3)];
-            const h4v b0 = lds_tr16(rp), b1 = lds_tr16(rp + 4 * BT_DW);
-            const h8v bv = __builtin_shufflevector(b0, b1, 0, 1, 2, 3, 4, 5, 6, 7);
+            h8v bv[NQW];
+#pragma unroll
+            for (int qd = 0; qd < NQW; qd++) {
+                const uint32_t *rp = &sm.Bt[qd][o][32 * ks + 8 * g + (r >> 2)][2 * (r & 3)];
+                const h4v b0 = lds_tr16(rp), b1 = lds_tr16(rp + 4 * Gqa4Smem<NQW>::BTW);
+                bv[qd] = __builtin_shufflevector(b0, b1, 0, 1, 2, 3, 4, 5, 6, 7);
+            }
 #pragma unroll
             for (int u = 0; u < 4; u++) {
                 const int nt = 4 * o + u;
                 const h8v af = frag8(vx[nt] & MSK);
-                S.acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af, bv, S.acc[nt], 0, 0, 0);
+#pragma unroll
+                for (int qd = 0; qd < NQW; qd++)
+                    S[qd].acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af, bv[qd], S[qd].acc[nt], 0, 0, 0);
             }
         }
     }
@@ -1087,7 +1122,7 @@ __device__ inline void gqa4_page(const Gqa4Page &R, Gqa4State &S, Gqa4Smem &sm, 
 // pages and then the full tail splits, each in (request, KV head, split)
 // order, then the short last tail splits by length, longest first, each
 // length in pair order.  (With two query quads per KV head, an item's
-// workgroup runs one wave per quad.)  Workgroups are dispatched in list order
+// wave serves both.)  Workgroups are dispatched in list order
 // and round robin over the XCDs, so similar items sit side by side and the
 // shortest run last.  PLAN_G workgroups each compute every pair's place (one pass per
 // PLAN_T pairs: wave-level prefix sums of the counts and of the short splits
@@ -1236,24 +1271,24 @@ __global__ __launch_bounds__(PLAN_T) void plan_kernel(KParams P, Workspace W) {
     }
 }
 
-// A workgroup is one wave per query quad of the KV head: with two quads
-// (group of 8) the two waves read the same pages at the same time, so the
-// second read is served by the cache.  FLOOR: the load-only copy behind
+// A workgroup is one wave serving every query quad of the KV head: with two
+// quads (group of 8) each page is loaded and its codes converted once for
+// both, at two waves per SIMD (254 VGPRs) instead of three.  FLOOR: the
+// load-only copy behind
 // kvq_stage1_load_floor -- the same work list, page loads, window chunks and
 // partial writes, with each page's words folded into one register instead of
 // gqa4_page, at the same register budget (so the same waves per SIMD).
 template <int QPK, bool FLOOR>
 __device__ __forceinline__ void gqa4_stage1(KParams P, const uint16_t *__restrict__ q,
                                             Workspace W, float qscale) {
-    constexpr int NQ4 = QPK >= 4 ? QPK / 4 : 1;        // query quads per KV head
+    constexpr int NQW = QPK >= 4 ? QPK / 4 : 1;        // query quads of the KV head, all in this wave
     constexpr int NQV = QPK >= 4 ? 4 : QPK;            // queries of a quad that exist
-    const int lane = threadIdx.x & 63, g = lane >> 4, r = lane & 15;
-    const int quad = NQ4 == 1 ? 0 : (int)(threadIdx.x >> 6);
+    const int lane = threadIdx.x, g = lane >> 4, r = lane & 15;
     const Geom G = geom(P.scheme, P.nb);
     __shared__ union {
-        Gqa4Smem pg;
+        Gqa4Smem<NQW> pg;
         WinSmem win;
-    } U[NQ4];                                    // one per wave
+    } U;
     // the paged splits first, in the order of the work list (longest first;
     // workgroups past its end exit), then the window chunks: shorter than the
     // body and tail splits, they fill the compute units as the list drains
@@ -1263,8 +1298,7 @@ __device__ __forceinline__ void gqa4_stage1(KParams P, const uint16_t *__restric
     if (Lw >= 0) {                               // the KV head's fp16 window
         const int wc = Lw % W.n_win, rest = Lw / W.n_win;
         const int hd = rest % (int)gridDim.y, bb = rest / (int)gridDim.y;
-        window_partial<QPK / NQ4, PT / 2, KVQ_SCHEME_KIVI2>(P, q, W, qscale, bb, hd, QPK * hd + 4 * quad, wc,
-                                                            lane, U[quad].win);
+        window_partial<QPK, PT / 2, KVQ_SCHEME_KIVI2>(P, q, W, qscale, bb, hd, QPK * hd, wc, lane, U.win);
         return;
     }
     // the item is read together with the list length (the grid's paged part
@@ -1274,10 +1308,10 @@ __device__ __forceinline__ void gqa4_stage1(KParams P, const uint16_t *__restric
     asm volatile("" ::"s"(item.x), "s"(n_items));
     if (L >= n_items) return;
     const int b = (int)item.x / P.Hkv, h = (int)item.x % P.Hkv;
-    const int hq0 = h * QPK + 4 * quad;               // the quad's first query head
+    const int hq0 = h * QPK;                          // the KV head's first query head
     const int s = (int)item.y, p0 = (int)item.z;           // partial row, first page
     const int np = item.w & 255, nv_last = (item.w >> 8) ? (int)(item.w >> 8) : PT;
-    Gqa4Smem &sm = U[quad].pg;
+    Gqa4Smem<NQW> &sm = U.pg;
     // valid tokens of the split's page i (only the prefix's last page is short)
     auto nvalid = [&](int i) { return i == np - 1 ? nv_last : PT; };
 
@@ -1285,11 +1319,14 @@ __device__ __forceinline__ void gqa4_stage1(KParams P, const uint16_t *__restric
     // score-operand channels 4 (lane & 31) .. +3 (unscaled: keeps q s in the
     // range where the f16 remainder is a normal number)
     int pid_l = (lane < np && p0 + lane < P.max_pages) ? P.table[(size_t)b * P.max_pages + p0 + lane] : 0;
-    uint2 qw[4];                                 // queries past the group's end: zero
+    uint2 qw[NQW][4];                            // queries past the group's end: zero
 #pragma unroll
-    for (int hq = 0; hq < 4; hq++)
-        qw[hq] = hq < NQV ? *(const uint2 *)(q + ((size_t)b * P.Hq + (size_t)hq0 + hq) * D + 4 * (lane & 31))
-                          : make_uint2(0u, 0u);
+    for (int qd = 0; qd < NQW; qd++)
+#pragma unroll
+        for (int hq = 0; hq < 4; hq++)
+            qw[qd][hq] = hq < NQV ? *(const uint2 *)(q + ((size_t)b * P.Hq + (size_t)hq0 + 4 * qd + hq) * D +
+                                                     4 * (lane & 31))
+                                  : make_uint2(0u, 0u);
 
     const bool bad = lane < np && (pid_l < 0 || pid_l >= P.n_pages);
     if (__any(bad)) {
@@ -1300,18 +1337,25 @@ __device__ __forceinline__ void gqa4_stage1(KParams P, const uint16_t *__restric
     if (lane < 16) sm.Az[lane] = h8v{0, 0, 0, 0, 0, 0, 0, 0};
     // this lane's score-operand rows: row r & 7 of key group 0 (A1) or 1 (A2)
     // where its row r belongs to that group's half, else the zero row
-    const h8v *a1 = r < 8 ? &sm.As[0][r][0] : &sm.Az[0];
-    const h8v *a2 = r < 8 ? &sm.Az[0] : &sm.As[1][r - 8][0];
+    const h8v *a1[NQW], *a2[NQW];
+#pragma unroll
+    for (int qd = 0; qd < NQW; qd++) {
+        a1[qd] = r < 8 ? &sm.As[qd][0][r][0] : &sm.Az[0];
+        a2[qd] = r < 8 ? &sm.Az[0] : &sm.As[qd][1][r - 8][0];
+    }
 
-    Gqa4State S;
+    Gqa4State S[NQW];
 #pragma unroll
-    for (int i = 0; i < 4; i++) S.m[i] = -INFINITY;
-    S.ma = S.mb = -INFINITY;
-    S.la = S.lb = 0.f;
+    for (int qd = 0; qd < NQW; qd++) {
 #pragma unroll
-    for (int j = 0; j < 4; j++) S.za[j] = S.zb[j] = 0.f;
+        for (int i = 0; i < 4; i++) S[qd].m[i] = -INFINITY;
+        S[qd].ma = S[qd].mb = -INFINITY;
+        S[qd].la = S[qd].lb = 0.f;
 #pragma unroll
-    for (int nt = 0; nt < 8; nt++) S.acc[nt] = f4v{0.f, 0.f, 0.f, 0.f};
+        for (int j = 0; j < 4; j++) S[qd].za[j] = S[qd].zb[j] = 0.f;
+#pragma unroll
+        for (int nt = 0; nt < 8; nt++) S[qd].acc[nt] = f4v{0.f, 0.f, 0.f, 0.f};
+    }
 
     const uint8_t *base = P.pool + (size_t)h * P.page_bytes;
     const size_t pstride = (size_t)P.Hkv * P.page_bytes;
@@ -1344,7 +1388,6 @@ __device__ __forceinline__ void gqa4_stage1(KParams P, const uint16_t *__restric
     Gqa4Page ra = page_ld(0);
     __builtin_amdgcn_sched_barrier(0);
     for (int i = 0; i < np; i += 2) {
-        if (NQ4 == 2) __builtin_amdgcn_s_barrier();   // the quads' waves stay a page pair apart at most
         Gqa4Page rb = page_ld(i + 1);
         __builtin_amdgcn_sched_barrier(0);
         run_page(ra, i);
@@ -1355,15 +1398,22 @@ __device__ __forceinline__ void gqa4_stage1(KParams P, const uint16_t *__restric
 
     if constexpr (FLOOR) {
         // the partial rows' bytes: four output rows and log-sum-exps a split
-        asm volatile("" ::: "v165");             // the group kernel's register budget
+        if constexpr (NQW == 2)                  // the group kernel's register budget
+            asm volatile("" ::: "v255");
+        else
+            asm volatile("" ::: "v165");
         const float v = __builtin_bit_cast(float, fold & 0x007fffffu);   // finite
 #pragma unroll
-        for (int k = 0; k < 2; k++) {
-            const int e = lane + 64 * k, hp = e >> 5, c4 = e & 31;
-            if (hp < NQV)
-                *(float4 *)(W.o + part_row(W, P.Hq, b, hq0 + hp, s) * D + 4 * c4) = make_float4(v, v, v, v);
+        for (int qd = 0; qd < NQW; qd++) {
+#pragma unroll
+            for (int k = 0; k < 2; k++) {
+                const int e = lane + 64 * k, hp = e >> 5, c4 = e & 31;
+                if (hp < NQV)
+                    *(float4 *)(W.o + part_row(W, P.Hq, b, hq0 + 4 * qd + hp, s) * D + 4 * c4) =
+                        make_float4(v, v, v, v);
+            }
+            if (lane < NQV) W.ml[part_row(W, P.Hq, b, hq0 + 4 * qd + lane, s)] = make_float2(v, 1.0f);
         }
-        if (lane < NQV) W.ml[part_row(W, P.Hq, b, hq0 + lane, s)] = make_float2(v, 1.0f);
         return;
     }
     // ---- reduce and write the split's partial ----
@@ -1379,62 +1429,67 @@ __device__ __forceinline__ void gqa4_stage1(KParams P, const uint16_t *__restric
         v += dppf<0x128>(v);                         // row_ror:8
         return v + __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(x32, __builtin_bit_cast(int, v)));
     };
-    S.la = red(S.la);
-    S.lb = red(S.lb);
 #pragma unroll
-    for (int j = 0; j < 4; j++) {
-        S.za[j] = red(S.za[j]);
-        S.zb[j] = red(S.zb[j]);
-    }
-    const int hp = r >> 2, part = (r >> 1) & 1, js = r & 1;
-    // this lane's query hp: slot hp & 1 of its own row where the row's
-    // parity is hp >> 1, else of lane ^ 16 (the same r, the other parity)
-    const bool own = (g & 1) == (hp >> 1);
-    auto of_hp = [&](float va, float vb) {
-        const float t = (hp & 1) ? vb : va;
-        const float u = __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, t), 0x401F));  // lane ^ 16
-        return own ? t : u;
-    };
-    const float lh = of_hp(S.la, S.lb);
-    const float il = 1.0f / lh;
-    const size_t row = part_row(W, P.Hq, b, hq0 + hp, s);
-    bool nonfinite = !__builtin_isfinite(lh);
-#pragma unroll
-    for (int nt = 0; nt < 8; nt++) {
-        f4v lo;                                   // the lo column, two lanes up (lane ^ 2)
-#pragma unroll
-        for (int i = 0; i < 4; i++) lo[i] = dppf<0x4E>(S.acc[nt][i]);
-        const int j = nt >> 1;
-        const float zj = of_hp(S.za[j], S.zb[j]);  // z sum of value group j, query hp
-        if (part == 0 && js == (j & 1) && hp < NQV) {
-            const f4v o = (S.acc[nt] + lo + zj) * il;
-#pragma unroll
-            for (int i = 0; i < 4; i++) nonfinite |= !__builtin_isfinite(o[i]);
-            *(float4 *)(W.o + row * D + 16 * nt + 4 * g) = make_float4(o[0], o[1], o[2], o[3]);
+    for (int qd = 0; qd < NQW; qd++) {
+        Gqa4State &Sq = S[qd];
+        const int hq1 = hq0 + 4 * qd;                // the quad's first query head
+        Sq.la = red(Sq.la);
+        Sq.lb = red(Sq.lb);
+    #pragma unroll
+        for (int j = 0; j < 4; j++) {
+            Sq.za[j] = red(Sq.za[j]);
+            Sq.zb[j] = red(Sq.zb[j]);
         }
-    }
-    flag_range(P, nonfinite && hp < NQV, lane);
-    // lane i < NQV writes query i's log-sum-exp: its l and m sit in the rows
-    // of parity i >> 1, slot i & 1 (as the maxima ma, mb)
-    const float lt = (lane & 1) ? S.lb : S.la, mt = (lane & 1) ? S.mb : S.ma;
-    const float lu = __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, lt), 0x401F));
-    const float mu = __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, mt), 0x401F));
-    if (lane < NQV) {
-        const float li = (lane & 2) ? lu : lt;
-        const float mi = (lane & 2) ? mu : mt;
-        const size_t row_i = part_row(W, P.Hq, b, hq0 + lane, s);
-        W.ml[row_i] = make_float2(mi + log2f(li), 1.0f);
+        const int hp = r >> 2, part = (r >> 1) & 1, js = r & 1;
+        // this lane's query hp: slot hp & 1 of its own row where the row's
+        // parity is hp >> 1, else of lane ^ 16 (the same r, the other parity)
+        const bool own = (g & 1) == (hp >> 1);
+        auto of_hp = [&](float va, float vb) {
+            const float t = (hp & 1) ? vb : va;
+            const float u = __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, t), 0x401F));  // lane ^ 16
+            return own ? t : u;
+        };
+        const float lh = of_hp(Sq.la, Sq.lb);
+        const float il = 1.0f / lh;
+        const size_t row = part_row(W, P.Hq, b, hq1 + hp, s);
+        bool nonfinite = !__builtin_isfinite(lh);
+    #pragma unroll
+        for (int nt = 0; nt < 8; nt++) {
+            f4v lo;                                   // the lo column, two lanes up (lane ^ 2)
+    #pragma unroll
+            for (int i = 0; i < 4; i++) lo[i] = dppf<0x4E>(Sq.acc[nt][i]);
+            const int j = nt >> 1;
+            const float zj = of_hp(Sq.za[j], Sq.zb[j]);  // z sum of value group j, query hp
+            if (part == 0 && js == (j & 1) && hp < NQV) {
+                const f4v o = (Sq.acc[nt] + lo + zj) * il;
+    #pragma unroll
+                for (int i = 0; i < 4; i++) nonfinite |= !__builtin_isfinite(o[i]);
+                *(float4 *)(W.o + row * D + 16 * nt + 4 * g) = make_float4(o[0], o[1], o[2], o[3]);
+            }
+        }
+        flag_range(P, nonfinite && hp < NQV, lane);
+        // lane i < NQV writes query i's log-sum-exp: its l and m sit in the rows
+        // of parity i >> 1, slot i & 1 (as the maxima ma, mb)
+        const float lt = (lane & 1) ? Sq.lb : Sq.la, mt = (lane & 1) ? Sq.mb : Sq.ma;
+        const float lu = __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, lt), 0x401F));
+        const float mu = __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, mt), 0x401F));
+        if (lane < NQV) {
+            const float li = (lane & 2) ? lu : lt;
+            const float mi = (lane & 2) ? mu : mt;
+            const size_t row_i = part_row(W, P.Hq, b, hq1 + lane, s);
+            W.ml[row_i] = make_float2(mi + log2f(li), 1.0f);
+        }
     }
 }
 
 template <int QPK>
-__global__ __launch_bounds__(QPK == 8 ? 128 : 64) __attribute__((amdgpu_waves_per_eu(3, 8))) void stage1_gqa4_mfma_kernel(KParams P, const uint16_t *__restrict__ q,
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(QPK == 8 ? 2 : 3, 8))) void stage1_gqa4_mfma_kernel(KParams P, const uint16_t *__restrict__ q,
                                                               Workspace W, float qscale) {
     gqa4_stage1<QPK, false>(P, q, W, qscale);
 }
 
 template <int QPK>
-__global__ __launch_bounds__(QPK == 8 ? 128 : 64) __attribute__((amdgpu_waves_per_eu(3, 8))) void stage1_gqa4_floor_kernel(KParams P, const uint16_t *__restrict__ q,
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(QPK == 8 ? 2 : 3, 8))) void stage1_gqa4_floor_kernel(KParams P, const uint16_t *__restrict__ q,
                                                                Workspace W, float qscale) {
     gqa4_stage1<QPK, true>(P, q, W, qscale);
 }
@@ -2296,7 +2351,7 @@ hipError_t launch_stage1_floor(const KParams &P, const uint16_t *q, float sm_sca
     switch (P.qpk) {
         case 2: stage1_gqa4_floor_kernel<2><<<g1, 64, 0, s>>>(P, q, W, qscale); break;
         case 4: stage1_gqa4_floor_kernel<4><<<g1, 64, 0, s>>>(P, q, W, qscale); break;
-        case 8: stage1_gqa4_floor_kernel<8><<<g1, 128, 0, s>>>(P, q, W, qscale); break;
+        case 8: stage1_gqa4_floor_kernel<8><<<g1, 64, 0, s>>>(P, q, W, qscale); break;
         default: return hipErrorInvalidValue;
     }
     hipError_t e = hipGetLastError();
@@ -2339,7 +2394,7 @@ hipError_t launch_decode(const KParams &P, const uint16_t *q, float *out, float 
         switch (P.qpk) {
             case 2: stage1_gqa4_mfma_kernel<2><<<g1, 64, 0, s>>>(P, q, W, qscale); break;
             case 4: stage1_gqa4_mfma_kernel<4><<<g1, 64, 0, s>>>(P, q, W, qscale); break;
-            case 8: stage1_gqa4_mfma_kernel<8><<<g1, 128, 0, s>>>(P, q, W, qscale); break;
+            case 8: stage1_gqa4_mfma_kernel<8><<<g1, 64, 0, s>>>(P, q, W, qscale); break;
             default: return hipErrorInvalidValue;
         }
     } else {
