@@ -982,35 +982,42 @@ __device__ inline void gqa4_page(const Gqa4Page &R, Gqa4State (&S)[NQW], Gqa4Sme
     }
 
     const int t0 = gqa4_token(lane);
+    // ---- online softmax: tokens t0 and t0 + 16, queries a and a + 1 of
+    // each quad; one rescale test for all quads (a quad rescaled without
+    // need only moves its maxima up to its scores, which stays exact) ----
+    float z[NQW][2][2];                         // [quad][token][query a, a + 1], log2 units
+    float d[NQW][2][2];
+    float dmax = -INFINITY;
 #pragma unroll
     for (int qd = 0; qd < NQW; qd++) {
-        Gqa4State &Sq = S[qd];
-        // ---- online softmax: tokens t0 and t0 + 16, queries a and a + 1 ----
-        float z[2][2];                          // [token][query a, a + 1], log2 units
 #pragma unroll
         for (int j = 0; j < 2; j++) {
-            z[j][0] = fmaf(sc[qd][j][0] + sc[qd][j][1], qscale, bias_a[qd]);
-            z[j][1] = fmaf(sc[qd][j][2] + sc[qd][j][3], qscale, bias_b[qd]);
+            z[qd][j][0] = fmaf(sc[qd][j][0] + sc[qd][j][1], qscale, bias_a[qd]);
+            z[qd][j][1] = fmaf(sc[qd][j][2] + sc[qd][j][3], qscale, bias_b[qd]);
         }
         if (nvalid < PT) {                      // uniform: only the prefix's last page
 #pragma unroll
             for (int j = 0; j < 2; j++)
-                if (t0 + 16 * j >= nvalid) z[j][0] = z[j][1] = -INFINITY;
+                if (t0 + 16 * j >= nvalid) z[qd][j][0] = z[qd][j][1] = -INFINITY;
         }
         // the exponents against the running maxima; a rescale only when one
         // of them passes LAZY_TAU (-inf - -inf = NaN, where a first page's
         // masked token meets a maximum not yet set, is passed over by fmaxf:
         // the page's valid tokens give +inf)
-        float d[2][2];
 #pragma unroll
         for (int j = 0; j < 2; j++) {
-            d[j][0] = z[j][0] - Sq.ma;
-            d[j][1] = z[j][1] - Sq.mb;
+            d[qd][j][0] = z[qd][j][0] - S[qd].ma;
+            d[qd][j][1] = z[qd][j][1] - S[qd].mb;
         }
-        if (__any(fmaxf(fmaxf(d[0][0], d[1][0]), fmaxf(d[0][1], d[1][1])) > LAZY_TAU)) {
+        dmax = fmaxf(dmax, fmaxf(fmaxf(d[qd][0][0], d[qd][1][0]), fmaxf(d[qd][0][1], d[qd][1][1])));
+    }
+    if (__any(dmax > LAZY_TAU)) {
+#pragma unroll
+        for (int qd = 0; qd < NQW; qd++) {
+            Gqa4State &Sq = S[qd];
             // the new maxima: over the 32 lanes holding each query (lane bits
             // 0..3 and 5), then moved in every lane
-            float mt[2] = {fmaxf(z[0][0], z[1][0]), fmaxf(z[0][1], z[1][1])};
+            float mt[2] = {fmaxf(z[qd][0][0], z[qd][1][0]), fmaxf(z[qd][0][1], z[qd][1][1])};
 #pragma unroll
             for (int k = 0; k < 2; k++) {
 #pragma unroll
@@ -1043,15 +1050,19 @@ __device__ inline void gqa4_page(const Gqa4Page &R, Gqa4State (&S)[NQW], Gqa4Sme
             for (int nt = 0; nt < 8; nt++) Sq.acc[nt] *= ap;
 #pragma unroll
             for (int j = 0; j < 2; j++) {
-                d[j][0] = z[j][0] - Sq.ma;
-                d[j][1] = z[j][1] - Sq.mb;
+                d[qd][j][0] = z[qd][j][0] - Sq.ma;
+                d[qd][j][1] = z[qd][j][1] - Sq.mb;
             }
         }
+    }
+#pragma unroll
+    for (int qd = 0; qd < NQW; qd++) {
+        Gqa4State &Sq = S[qd];
         float p[2][2];                          // [token][query a, a + 1]
 #pragma unroll
         for (int j = 0; j < 2; j++) {
-            p[j][0] = __builtin_amdgcn_exp2f(d[j][0]);
-            p[j][1] = __builtin_amdgcn_exp2f(d[j][1]);
+            p[j][0] = __builtin_amdgcn_exp2f(d[qd][j][0]);
+            p[j][1] = __builtin_amdgcn_exp2f(d[qd][j][1]);
         }
         Sq.la += p[0][0] + p[1][0];
         Sq.lb += p[0][1] + p[1][1];
