@@ -153,7 +153,7 @@ def test_kitty_calibrate_store_decode(flags):
     case.check_store()
 
 
-@pytest.mark.parametrize("wid,Hq,Hkv", [(2, 2, 2), (3, 8, 2), (4, 2, 2), (6, 4, 1), (9, 8, 2)])
+@pytest.mark.parametrize("wid,Hq,Hkv", [(2, 2, 2), (3, 8, 2), (3, 16, 2), (4, 2, 2), (6, 4, 1), (9, 8, 2)])
 def test_sink_tokens_store_decode(wid, Hq, Hkv):
     # the first 32 tokens stay fp16: bit-exact store (sink buffers included)
     # and decode through prefill and two flushes, for KIVI-2 (one query head
@@ -247,12 +247,13 @@ def test_kivi4_store_decode(Hq, Hkv, split):
 
 
 @pytest.mark.parametrize("R", [64, 192, 256])
-@pytest.mark.parametrize("wid,Hq,Hkv", [(3, 8, 2), (2, 2, 2), (4, 4, 1), (9, 2, 1), (6, 4, 1), (8, 2, 2)])
+@pytest.mark.parametrize("wid,Hq,Hkv", [(3, 8, 2), (3, 16, 2), (2, 2, 2), (4, 4, 1), (9, 2, 1), (6, 4, 1),
+                                        (8, 2, 2)])
 def test_residual_sizes(R, wid, Hq, Hkv):
     # fp16 windows of 64, 192 and 256 tokens (one to four pages flushed at
     # once, as many window chunks): bit-exact store through prefill and
-    # flushes, decode to the tolerance, for the group-of-4 kernel, the
-    # one-query-head kernel, Kitty and KIVI-4
+    # flushes, decode to the tolerance, for the group kernel (groups of 4
+    # and 8), the one-query-head kernel, Kitty and KIVI-4
     w = inputs.workload(wid, B=2, Hq=Hq, Hkv=Hkv, ctx=(700, R + 37), R=R)
     case = _case(w, extra_tokens=2 * R + 40, split_pages=3)
     case.check_state()
@@ -268,13 +269,13 @@ def test_residual_sizes(R, wid, Hq, Hkv):
     case.check_store()
 
 
-@pytest.mark.parametrize("wid,Hq,Hkv", [(7, 8, 2), (7, 2, 2)])
+@pytest.mark.parametrize("wid,Hq,Hkv", [(7, 8, 2), (7, 16, 2), (7, 2, 2)])
 def test_merge_most_entries(wid, Hq, Hkv):
     # the largest merge a layout allows: a 256-token window plus the sink
     # chunk (five window chunks) and one-page splits over a request that
     # fills a 256-page table (252 paged splits: the window's 256 tokens and
-    # the sink occupy the rest of its capacity), for the group-of-4 kernel
-    # and the one-query-head kernel; then steps up to the capacity
+    # the sink occupy the rest of its capacity), for the group kernel (groups
+    # of 4 and 8) and the one-query-head kernel; then steps up to the capacity
     w = inputs.workload(wid, B=2, Hq=Hq, Hkv=Hkv, ctx=(16384 - 16, 900), R=256, sink=32)
     case = _case(w, extra_tokens=16, split_pages=1)
     assert case.max_pages == 256
@@ -563,8 +564,8 @@ def test_prefill_flags_bad_length():
     assert torch.equal(case.cache.pool, pool0) and torch.equal(case.cache.state, state0)
 
 
-@pytest.mark.parametrize("wid,Hq,Hkv", [(2, 2, 2), (3, 8, 2), (4, 2, 2), (5, 8, 2), (6, 4, 1), (7, 8, 2),
-                                        (9, 4, 2), (10, 8, 2)])
+@pytest.mark.parametrize("wid,Hq,Hkv", [(2, 2, 2), (3, 8, 2), (3, 16, 2), (4, 2, 2), (5, 8, 2), (6, 4, 1),
+                                        (7, 8, 2), (9, 4, 2), (10, 8, 2)])
 def test_empty_request_decodes_to_zero_then_grows(wid, Hq, Hkv):
     # request 1 holds no token: attention over an empty set is taken as a zero
     # output, a zero certificate and no effect on the other request; then it
@@ -585,7 +586,7 @@ def test_empty_request_decodes_to_zero_then_grows(wid, Hq, Hkv):
 
 
 @pytest.mark.parametrize("KS,VS", [(1.0, 60.0), (20.0, 1.0)])
-@pytest.mark.parametrize("wid,Hq,Hkv", [(3, 8, 2), (2, 2, 2), (4, 2, 2), (9, 2, 2), (6, 4, 1)])
+@pytest.mark.parametrize("wid,Hq,Hkv", [(3, 8, 2), (3, 16, 2), (2, 2, 2), (4, 2, 2), (9, 2, 2), (6, 4, 1)])
 def test_large_magnitudes_inside_the_operand_range(wid, Hq, Hkv, KS, VS):
     # values x60: value scales up to ~150, inside the P.V operands' range
     # (at most 255); keys x20: |q s| up to ~3300 and scores twenty times wider
