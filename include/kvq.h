@@ -272,7 +272,8 @@ int kvq_flush_key_group(const kvq_cache_t *cache, hipStream_t stream);
  * chunks, each a partial of its own; stage 2 merges all partials with
  * log-sum-exp weights ("WitCert" Key structure).  KIVI2 with 2, 4 or 8 query
  * heads per KV head (no KVQ_FLAG_GENERIC_STAGE1) runs the group kernel, which
- * reads each page once per four query heads: a request of npg pages is cut
+ * reads each page once for all the query heads of its KV head (one wave; up to
+ * two sets of four query heads): a request of npg pages is cut
  * into splits of split_pages pages over all but its last min(npg / 8,
  * 2 split_pages) pages and splits of split_pages / 4 over the rest, run
  * longest first from a work list built on the device for each call.  A request with no token gets a zero
