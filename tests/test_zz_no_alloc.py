@@ -62,6 +62,21 @@ def test_noalloc_matches_workspace_entry_twice_second_smaller():
             assert np.abs(o_na[b, h * g:(h + 1) * g].astype(np.float64) - ref).max() <= 1e-5
 
 
+def test_noalloc_group_of_8():
+    # the group kernel's one-wave form for two query quads per KV head through
+    # the no-allocation entry point: the same output as the workspace entry,
+    # and the oracle's for the sampled pairs
+    from gpu_harness import Case
+    w = inputs.workload(3, B=3, Hq=16, Hkv=2, ctx=(2500, 900, 4100))
+    case = Case(w, extra_tokens=64, split_pages=8, sample=[(0, 1), (2, 0)])
+    ((o_ws, _), (o_na, _)), q = _both(case, 7)
+    _same(o_ws, o_na)
+    g = case.w.group
+    for (b, h) in case.streams:
+        ref, _ = case.oracle_decode(q, b, h)
+        assert np.abs(o_na[b, h * g:(h + 1) * g].astype(np.float64) - ref).max() <= 1e-5
+
+
 def test_noalloc_witcert_certificate():
     from gpu_harness import Case
     w = inputs.workload(5, B=2, Hq=8, Hkv=2, ctx=(600, 1000))
