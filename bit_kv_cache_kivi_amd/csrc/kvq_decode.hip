@@ -1284,7 +1284,7 @@ __global__ __launch_bounds__(PLAN_T) void plan_kernel(KParams P, Workspace W) {
 
 // A workgroup is one wave serving every query quad of the KV head: with two
 // quads (group of 8) each page is loaded and its codes converted once for
-// both, at two waves per SIMD (254 VGPRs) instead of three.  FLOOR: the
+// both, at two waves per SIMD (about 250 VGPRs) instead of three.  FLOOR: the
 // load-only copy behind
 // kvq_stage1_load_floor -- the same work list, page loads, window chunks and
 // partial writes, with each page's words folded into one register instead of
